@@ -1,0 +1,242 @@
+"""CPU oracle for the weight-only mixed-bit quantized linear layer.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline leg of
+the benchmark may use this package; the product library never does.  It is a thin
+ctypes wrapper over ``qoracle.c`` (plain C, fp32 quantizer as stated by the pages,
+fp64 matmuls).  See the header of ``qoracle.c`` for the passages each routine follows.
+
+Parity pins: every routine here is pinned by tests/test_oracle_*.py against the pages'
+printed values, closed forms, invariants and brute force on tiny inputs, except the
+device byte map (``pack_device``), which is the library's own encoding: it is pinned
+only by being a bijection on the canonical bytes plus its documented locality
+properties ("parity unpinned" against the pages, which define no device layout).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+_SRC = _HERE / "qoracle.c"
+_LIB = _HERE / "liboracle.so"
+_lib = None
+
+GROUP = 128
+
+
+def build(force: bool = False) -> Path:
+    """Compile qoracle.c with gcc (IEEE fp32/fp64, no contraction, OpenMP)."""
+    if force or not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
+        tmp = _LIB.with_suffix(".so.tmp")
+        subprocess.check_call([
+            "gcc", "-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+            "-shared", "-fPIC", str(_SRC), "-o", str(tmp), "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(str(_LIB))
+        i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
+        L.or_half_value.restype = dbl
+        L.or_half_value.argtypes = [ctypes.c_uint16]
+        L.or_round_half.restype = ctypes.c_uint16
+        L.or_round_half.argtypes = [dbl]
+        L.or_quantize_group.restype = None
+        L.or_quantize_group.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.or_outlier_count.restype = i64
+        L.or_outlier_count.argtypes = [i64, i64, dbl]
+        L.or_quantize.restype = i32
+        L.or_quantize.argtypes = [i64, i64, i32, i32, vp, i64, dbl, vp, vp, vp, vp, vp, vp,
+                                  i64, ctypes.POINTER(i64)]
+        L.or_unit_values.restype = i32
+        L.or_unit_values.argtypes = [i32]
+        L.or_unit_bytes.restype = i32
+        L.or_unit_bytes.argtypes = [i32]
+        for name in ("or_pack_canonical", "or_unpack_canonical"):
+            getattr(L, name).restype = None
+            getattr(L, name).argtypes = [i64, i64, i32, vp, vp]
+        for name in ("or_pack_device", "or_unpack_device"):
+            getattr(L, name).restype = i32
+            getattr(L, name).argtypes = [i64, i64, i32, vp, vp]
+        L.or_device_offset.restype = i64
+        L.or_device_offset.argtypes = [i64, i64, i64, i32]
+        L.or_linear.restype = None
+        L.or_linear.argtypes = [i64, i64, i64, i32, vp, i64, vp, vp, vp, vp, vp, vp, vp, i64]
+        L.or_moe_ffn.restype = None
+        L.or_moe_ffn.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp] + [vp] * 9 + [vp]
+        L.or_quant_bytes.restype = dbl
+        L.or_quant_bytes.argtypes = [dbl] * 5
+        L.or_kv_bytes.restype = dbl
+        L.or_kv_bytes.argtypes = [dbl] * 5
+        L.or_num_threads.restype = i32
+        L.or_num_threads.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _bits16(a):
+    """fp16 array -> its uint16 bit patterns (a view, no arithmetic)."""
+    a = np.ascontiguousarray(a)
+    return a.view(np.uint16) if a.dtype == np.float16 else a.astype(np.uint16)
+
+
+# ---- fp16 -------------------------------------------------------------------------
+
+def half_value(h: int) -> float:
+    return lib().or_half_value(int(h))
+
+
+def round_half(x: float) -> int:
+    return lib().or_round_half(float(x))
+
+
+# ---- quantizer ----------------------------------------------------------------------
+
+def quantize_group(w_fp16, bits: int):
+    """One group -> (scale_bits uint16, zero uint8, codes uint8[n])."""
+    w = _bits16(w_fp16).ravel()
+    s = np.zeros(1, np.uint16)
+    z = np.zeros(1, np.uint8)
+    q = np.zeros(w.size, np.uint8)
+    lib().or_quantize_group(_p(w), w.size, bits, _p(s), _p(z), _p(q))
+    return int(s[0]), int(z[0]), q
+
+
+def outlier_count(n: int, k: int, frac: float) -> int:
+    return lib().or_outlier_count(n, k, frac)
+
+
+def quantize(w_fp16, bits: int, outlier_frac: float = 0.0, g: int = GROUP):
+    """W [N, K] fp16 -> dict(codes u8 [N,K], scales u16 [N,K/g], zeros u8 [N,K/g],
+    rowptr i32 [N+1], col i32 [nnz], val u16 [nnz])."""
+    w = _bits16(w_fp16)
+    N, K = w.shape
+    G = K // g
+    codes = np.zeros((N, K), np.uint8)
+    scales = np.zeros((N, G), np.uint16)
+    zeros = np.zeros((N, G), np.uint8)
+    kout = outlier_count(N, K, outlier_frac)
+    rowptr = np.zeros(N + 1, np.int32)
+    col = np.zeros(max(kout, 1), np.int32)
+    val = np.zeros(max(kout, 1), np.uint16)
+    nnz = ctypes.c_int64(0)
+    rc = lib().or_quantize(N, K, bits, g, _p(w), K, outlier_frac, _p(codes), _p(scales),
+                           _p(zeros), _p(rowptr), _p(col), _p(val), kout, ctypes.byref(nnz))
+    if rc != 0:
+        raise ValueError(f"or_quantize failed rc={rc}")
+    return dict(codes=codes, scales=scales, zeros=zeros, rowptr=rowptr,
+                col=col[:nnz.value], val=val[:nnz.value])
+
+
+# ---- packing -------------------------------------------------------------------------
+
+def unit_values(bits: int) -> int:
+    return lib().or_unit_values(bits)
+
+
+def unit_bytes(bits: int) -> int:
+    return lib().or_unit_bytes(bits)
+
+
+def pack_canonical(codes, bits: int):
+    c = _c(codes, np.uint8)
+    N, K = c.shape
+    out = np.zeros(N * K * bits // 8, np.uint8)
+    lib().or_pack_canonical(N, K, bits, _p(c), _p(out))
+    return out
+
+
+def unpack_canonical(packed, N: int, K: int, bits: int):
+    p = _c(packed, np.uint8)
+    out = np.zeros((N, K), np.uint8)
+    lib().or_unpack_canonical(N, K, bits, _p(p), _p(out))
+    return out
+
+
+def pack_device(codes, bits: int):
+    c = _c(codes, np.uint8)
+    N, K = c.shape
+    out = np.zeros(N * K * bits // 8, np.uint8)
+    if lib().or_pack_device(N, K, bits, _p(c), _p(out)) != 0:
+        raise ValueError("device layout needs N % 16 == 0 and K % 256 == 0")
+    return out
+
+
+def unpack_device(packed, N: int, K: int, bits: int):
+    p = _c(packed, np.uint8)
+    out = np.zeros((N, K), np.uint8)
+    if lib().or_unpack_device(N, K, bits, _p(p), _p(out)) != 0:
+        raise ValueError("device layout needs N % 16 == 0 and K % 256 == 0")
+    return out
+
+
+def device_offset(n: int, cb: int, K: int, bits: int) -> int:
+    return lib().or_device_offset(n, cb, K, bits)
+
+
+# ---- matmuls -------------------------------------------------------------------------
+
+def linear(x_fp16, q: dict, g: int = GROUP, outliers: bool = True):
+    """fp64 r = x * What^T (+ CSR add-back).  x [M, K] fp16; q as returned by quantize."""
+    x = _bits16(x_fp16)
+    M, K = x.shape
+    codes = _c(q["codes"], np.uint8)
+    N = codes.shape[0]
+    assert codes.shape[1] == K
+    r = np.zeros((M, N), np.float64)
+    use_csr = outliers and q.get("rowptr") is not None and len(q.get("col", [])) > 0
+    lib().or_linear(M, N, K, g, _p(x), K, _p(codes), _p(_c(q["scales"], np.uint16)),
+                    _p(_c(q["zeros"], np.uint8)),
+                    _p(_c(q["rowptr"], np.int32)) if use_csr else None,
+                    _p(_c(q["col"], np.int32)) if use_csr else None,
+                    _p(_c(q["val"], np.uint16)) if use_csr else None, _p(r), N)
+    return r
+
+
+def moe_ffn(x_fp16, ids, wts, gate: list, up: list, down: list, g: int = GROUP):
+    """fp64 routed-expert FFN.  gate/up/down: per-expert dicts from quantize()."""
+    x = _bits16(x_fp16)
+    T, D = x.shape
+    ids = _c(ids, np.int32)
+    wts = _c(wts, np.float32)
+    topk = ids.shape[1]
+    F = gate[0]["codes"].shape[0]
+    st = lambda lst, key, dt: np.ascontiguousarray(np.stack([d[key] for d in lst]), dtype=dt)
+    arrs = [st(gate, "codes", np.uint8), st(gate, "scales", np.uint16), st(gate, "zeros", np.uint8),
+            st(up, "codes", np.uint8), st(up, "scales", np.uint16), st(up, "zeros", np.uint8),
+            st(down, "codes", np.uint8), st(down, "scales", np.uint16), st(down, "zeros", np.uint8)]
+    r = np.zeros((T, D), np.float64)
+    lib().or_moe_ffn(T, D, F, topk, g, _p(ids), _p(wts), _p(x), *[_p(a) for a in arrs], _p(r))
+    return r
+
+
+# ---- byte accounting ----------------------------------------------------------------
+
+def quant_bytes(numel, bits, g, scale_bytes, zp_bits) -> float:
+    return lib().or_quant_bytes(float(numel), float(bits), float(g), float(scale_bytes),
+                                float(zp_bits))
+
+
+def kv_bytes(layers, kv_heads, head_dim, tokens, bytes_per_elem) -> float:
+    return lib().or_kv_bytes(float(layers), float(kv_heads), float(head_dim), float(tokens),
+                             float(bytes_per_elem))
+
+
+def num_threads() -> int:
+    return lib().or_num_threads()

@@ -1,0 +1,433 @@
+/*
+ * qoracle.c -- plain, slow, obviously-correct CPU reference for the weight-only
+ * mixed-bit quantized linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or load this
+ * file; only the test suite, the smoke check and the CPU-baseline leg of the benchmark
+ * use it.  It shares no code, header or table with the GPU library.
+ *
+ * Sources (pages cited by title and section):
+ *  [MB]  "二三五六" mixed 2/3/5/6-bit quantization with CPU/GPU hybrid inference
+ *        (pwwt.cn): s2.3 block size and scale overhead; s3.1 packing units (smallest n
+ *        with n*b divisible by 8); s3.2 unpack shift sequences, little-endian reads;
+ *        s4.2 fp32 scale multiply.
+ *  [IA]  inference acceleration guide (mzlw.cn): s1.1 the affine mapping
+ *        scale=(max-min)/(qmax-qmin), zero_point=qmin-round(min/scale),
+ *        q=round(x/scale)+zero_point, x_hat=(q-zero_point)*scale.
+ *  [70B] single-GPU 70B five-layer stack (bjdmk.com.cn/5414039): s2 group-wise
+ *        outlier-aware INT4 (groups of 128, top 0.1% |w| held out in fp16, added back
+ *        after the GEMM); s3 unfused reference path dequantize -> matmul(x, W^T).
+ *  [KV]  KV-cache INT8/INT4 accounting (kwkr.cn): s1.1, s3.1-s3.3 byte sums.
+ *  [MoE] on-device MoE memory wall (bjdmk.com.cn/5648983): s1.1 weight/KV byte
+ *        formulas; s4.2 routed expert tasks (hidden states + top-k expert ids).
+ *
+ * Readings where the pages are silent (each listed in the design notes):
+ *  - codes are unsigned 0..2^b-1, round() is round-half-to-even, q and zp clamp to
+ *    [0, qmax];
+ *  - the group range [lo, hi] is extended to contain 0 so zp always fits b bits;
+ *  - scale, zero point and codes are computed in IEEE fp32 (no fused multiply-add)
+ *    from the fp16-rounded scale; an all-zero group gets scale 1.0, zp 0; a scale that
+ *    rounds to zero or an fp16 subnormal is raised to 2^-14;
+ *  - "top 0.1% per group" is read as the global floor(frac*N*K) largest |w| (fp16
+ *    magnitude, ties to the lower row-major index), removed from the group range by
+ *    setting them to +0 in the dense copy and kept in an fp16 CSR over W's rows;
+ *  - bits inside a packing unit are LSB-first and units are stored little-endian.
+ *
+ * Arithmetic: quantization in fp32 exactly as stated; every matmul accumulates in
+ * fp64 over the exactly dequantized weights.  Build: gcc -O2 -ffp-contract=off
+ * -fno-fast-math -fopenmp -shared -fPIC.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------------ */
+/* IEEE 754 binary16 <-> binary64                                                  */
+/* ------------------------------------------------------------------------------ */
+
+/* Value of a binary16 bit pattern: sign, 5-bit exponent (bias 15), 10-bit fraction. */
+double or_half_value(uint16_t h)
+{
+    int s = h >> 15, e = (h >> 10) & 31, f = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);                 /* zero / subnormal */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);     /* (1 + f/1024) * 2^(e-15) */
+    return s ? -v : v;
+}
+
+/* Round a binary64 value to the nearest binary16, ties to even (one rounding). */
+uint16_t or_round_half(double x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isnan(x))
+        return 0x7E00;
+    if (a >= 65520.0)                 /* at or above the midpoint 65504..65536 */
+        return sign | 0x7C00;
+    if (a < 0x1p-14) {                /* subnormal range: integer multiples of 2^-24 */
+        double q = nearbyint(a * 0x1p24);
+        return sign | (uint16_t)q;    /* q == 1024 is the smallest normal, correctly */
+    }
+    int e;
+    double m = frexp(a, &e);          /* a = m * 2^e, m in [0.5, 1) */
+    int E = e - 1;                    /* a = (2m) * 2^E, 2m in [1, 2) */
+    double frac = nearbyint((2.0 * m - 1.0) * 1024.0);
+    if (frac == 1024.0) {
+        frac = 0.0;
+        E += 1;
+    }
+    if (E > 15)
+        return sign | 0x7C00;
+    return sign | (uint16_t)(((E + 15) << 10) | (int)frac);
+}
+
+/* ------------------------------------------------------------------------------ */
+/* Group quantizer  ([IA] s1.1; [70B] s2 groups of 128; [MB] s2.3 fp16 scale)       */
+/* ------------------------------------------------------------------------------ */
+
+static int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+/* Quantize one group of `n` fp16 weights (already with outliers set to +0). */
+void or_quantize_group(const uint16_t *w, int n, int bits,
+                       uint16_t *scale_out, uint8_t *zero_out, uint8_t *codes_out)
+{
+    const int qmin = 0, qmax = (1 << bits) - 1;
+    float lo = 0.0f, hi = 0.0f;                      /* range always contains 0 */
+    for (int i = 0; i < n; ++i) {
+        float v = (float)or_half_value(w[i]);
+        if (v < lo) lo = v;
+        if (v > hi) hi = v;
+    }
+    if (hi == lo) {                                  /* all-zero group */
+        *scale_out = 0x3C00;                         /* 1.0 */
+        *zero_out = 0;
+        for (int i = 0; i < n; ++i) codes_out[i] = 0;
+        return;
+    }
+    volatile float range = hi - lo;                  /* fp32, rounded */
+    volatile float s32 = range / (float)(qmax - qmin);
+    uint16_t sh = or_round_half((double)s32);
+    if ((sh & 0x7C00) == 0)                          /* zero or subnormal fp16 */
+        sh = 0x0400;                                 /* 2^-14 */
+    float sf = (float)or_half_value(sh);
+    volatile float lo_over_s = lo / sf;
+    int zp = clampi(qmin - (int)rintf(lo_over_s), qmin, qmax);
+    for (int i = 0; i < n; ++i) {
+        volatile float t = (float)or_half_value(w[i]) / sf;
+        codes_out[i] = (uint8_t)clampi((int)rintf(t) + zp, qmin, qmax);
+    }
+    *scale_out = sh;
+    *zero_out = (uint8_t)zp;
+}
+
+/* Number of outliers held out for a fraction `frac` of an N x K matrix. */
+int64_t or_outlier_count(int64_t n, int64_t k, double frac)
+{
+    if (!(frac > 0.0)) return 0;
+    return (int64_t)floor(frac * (double)(n * k));
+}
+
+/* qsort comparator state: rank by fp16 magnitude descending, then index ascending. */
+static const uint16_t *g_rank_w;
+static int64_t g_rank_k, g_rank_ldw;
+
+static int rank_cmp(const void *pa, const void *pb)
+{
+    int64_t a = *(const int64_t *)pa, b = *(const int64_t *)pb;
+    uint16_t ma = g_rank_w[(a / g_rank_k) * g_rank_ldw + a % g_rank_k] & 0x7FFF;
+    uint16_t mb = g_rank_w[(b / g_rank_k) * g_rank_ldw + b % g_rank_k] & 0x7FFF;
+    if (ma != mb) return ma > mb ? -1 : 1;
+    return a < b ? -1 : (a > b ? 1 : 0);
+}
+
+/*
+ * Quantize an N x K fp16 matrix (row n = output feature, groups of `g` consecutive k).
+ * With outlier_frac > 0 the floor(frac*N*K) largest |w| are held out ([70B] s2):
+ * their dense slots become +0 before the group range is taken, and the original fp16
+ * values go to a CSR over rows (cols ascending).  Returns 0 on success, 1 if the CSR
+ * capacity is too small (*nnz_out then holds the required count), 2 on bad arguments.
+ */
+int or_quantize(int64_t N, int64_t K, int bits, int g,
+                const uint16_t *w, int64_t ldw, double outlier_frac,
+                uint8_t *codes, uint16_t *scales, uint8_t *zeros,
+                int32_t *rowptr, int32_t *col, uint16_t *val, int64_t cap, int64_t *nnz_out)
+{
+    if (bits < 2 || bits > 6 || g <= 0 || K % g != 0 || ldw < K) return 2;
+    int64_t kout = or_outlier_count(N, K, outlier_frac);
+    *nnz_out = kout;
+    if (kout > 0 && kout > cap) return 1;
+
+    uint8_t *held = NULL;
+    if (kout > 0) {
+        int64_t total = N * K;
+        int64_t *idx = (int64_t *)malloc((size_t)total * sizeof(int64_t));
+        held = (uint8_t *)calloc((size_t)total, 1);
+        for (int64_t i = 0; i < total; ++i) idx[i] = i;
+        g_rank_w = w; g_rank_k = K; g_rank_ldw = ldw;
+        qsort(idx, (size_t)total, sizeof(int64_t), rank_cmp);
+        for (int64_t i = 0; i < kout; ++i) held[idx[i]] = 1;
+        free(idx);
+    }
+    if (rowptr) {
+        int64_t p = 0;
+        rowptr[0] = 0;
+        for (int64_t n = 0; n < N; ++n) {
+            for (int64_t k = 0; k < K; ++k) {
+                if (held && held[n * K + k]) {
+                    col[p] = (int32_t)k;
+                    val[p] = w[n * ldw + k];
+                    ++p;
+                }
+            }
+            rowptr[n + 1] = (int32_t)p;
+        }
+    }
+    int64_t G = K / g;
+    uint16_t *buf = (uint16_t *)malloc((size_t)g * sizeof(uint16_t));
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t gi = 0; gi < G; ++gi) {
+            for (int i = 0; i < g; ++i) {
+                int64_t k = gi * g + i;
+                buf[i] = (held && held[n * K + k]) ? 0x0000 : w[n * ldw + k];
+            }
+            or_quantize_group(buf, g, bits, &scales[n * G + gi], &zeros[n * G + gi],
+                              &codes[n * K + gi * g]);
+        }
+    }
+    free(buf);
+    free(held);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------ */
+/* Packing units  ([MB] s3.1, s3.2)                                                */
+/* ------------------------------------------------------------------------------ */
+
+/* Values per unit: smallest n with n*b divisible by 8. */
+int or_unit_values(int bits)
+{
+    int n = 1;
+    while ((n * bits) % 8 != 0) ++n;
+    return n;
+}
+
+int or_unit_bytes(int bits) { return or_unit_values(bits) * bits / 8; }
+
+/* One unit: value i sits at bits [b*i, b*i+b) of the little-endian integer formed by
+ * the unit's bytes (the shift sequences 0,3,...,21 / 0,6,12,18 / 5i of [MB] s3.2). */
+static void pack_unit(const uint8_t *codes, int bits, uint8_t *out)
+{
+    int nv = or_unit_values(bits), nb = or_unit_bytes(bits);
+    uint64_t v = 0;
+    for (int i = 0; i < nv; ++i) v |= (uint64_t)codes[i] << (bits * i);
+    for (int j = 0; j < nb; ++j) out[j] = (uint8_t)(v >> (8 * j));
+}
+
+static void unpack_unit(const uint8_t *in, int bits, uint8_t *codes)
+{
+    int nv = or_unit_values(bits), nb = or_unit_bytes(bits);
+    uint64_t v = 0;
+    for (int j = 0; j < nb; ++j) v |= (uint64_t)in[j] << (8 * j);
+    uint64_t mask = ((uint64_t)1 << bits) - 1;
+    for (int i = 0; i < nv; ++i) codes[i] = (uint8_t)((v >> (bits * i)) & mask);
+}
+
+/* Canonical layout: each row n is K*b/8 bytes of consecutive units in k order. */
+void or_pack_canonical(int64_t N, int64_t K, int bits, const uint8_t *codes, uint8_t *out)
+{
+    int nv = or_unit_values(bits), nb = or_unit_bytes(bits);
+    int64_t rowbytes = K * bits / 8;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t u = 0; u < K / nv; ++u)
+            pack_unit(&codes[n * K + u * nv], bits, &out[n * rowbytes + u * nb]);
+}
+
+void or_unpack_canonical(int64_t N, int64_t K, int bits, const uint8_t *in, uint8_t *codes)
+{
+    int nv = or_unit_values(bits), nb = or_unit_bytes(bits);
+    int64_t rowbytes = K * bits / 8;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t u = 0; u < K / nv; ++u)
+            unpack_unit(&in[n * rowbytes + u * nb], bits, &codes[n * K + u * nv]);
+}
+
+/*
+ * Device layout: a permutation of the canonical bytes (units stay whole).  It is the
+ * library's own tile order, defined here from its documented statement:
+ *  - 16-row x 256-k tiles, row-block major then k-tile; tile size 512*b bytes;
+ *  - inside a tile, "lane" l = 16*t + r (r = row in block, t = 0..3) owns a chunk of
+ *    8 blocks of 8 consecutive k (b bytes each, canonical bytes in order); block j
+ *    (0..7) covers k0 = 256*kt + 128*(j/4) + 32*(j%4) + 8*t;
+ *  - chunk byte c sits at 1024*(c/16) + 16*l + c%16 while c < F = 16*floor(b/2),
+ *    and at 64*F + 8*l + (c-F) for the 8-byte tail of odd b.
+ * Returns the byte offset of canonical byte `cb` of row `n`.
+ */
+int64_t or_device_offset(int64_t n, int64_t cb, int64_t K, int bits)
+{
+    int64_t k0 = (cb / bits) * 8;          /* first k of the 8-k block holding cb */
+    int64_t bib = cb % bits;               /* byte inside the block */
+    int64_t rb = n / 16, r = n % 16;
+    int64_t kt = k0 / 256, kk = k0 % 256;
+    int64_t gi = kk / 128, kq = kk % 128;
+    int64_t j4 = kq / 32, t = (kq % 32) / 8;
+    int64_t lane = 16 * t + r;
+    int64_t j = 4 * gi + j4;
+    int64_t c = bits * j + bib;
+    int64_t F = 16 * (bits / 2);
+    int64_t tile = rb * (K / 256) + kt;
+    int64_t off = c < F ? 1024 * (c / 16) + 16 * lane + c % 16 : 64 * F + 8 * lane + (c - F);
+    return tile * 512 * bits + off;
+}
+
+int or_pack_device(int64_t N, int64_t K, int bits, const uint8_t *codes, uint8_t *out)
+{
+    if (N % 16 != 0 || K % 256 != 0) return 2;
+    int64_t rowbytes = K * bits / 8;
+    uint8_t *canon = (uint8_t *)malloc((size_t)(N * rowbytes));
+    or_pack_canonical(N, K, bits, codes, canon);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t cb = 0; cb < rowbytes; ++cb)
+            out[or_device_offset(n, cb, K, bits)] = canon[n * rowbytes + cb];
+    free(canon);
+    return 0;
+}
+
+int or_unpack_device(int64_t N, int64_t K, int bits, const uint8_t *in, uint8_t *codes)
+{
+    if (N % 16 != 0 || K % 256 != 0) return 2;
+    int64_t rowbytes = K * bits / 8;
+    uint8_t *canon = (uint8_t *)malloc((size_t)(N * rowbytes));
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t cb = 0; cb < rowbytes; ++cb)
+            canon[n * rowbytes + cb] = in[or_device_offset(n, cb, K, bits)];
+    or_unpack_canonical(N, K, bits, canon, codes);
+    free(canon);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------ */
+/* Linear layer  ([70B] s3 unfused path; [IA] s1.1 dequantize; [70B] s2 add-back)   */
+/* ------------------------------------------------------------------------------ */
+
+/* Exact dequantized weight (q - zp) * s, in fp64. */
+static double dequant(const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+                      int64_t K, int g, int64_t n, int64_t k)
+{
+    int64_t G = K / g;
+    return ((double)codes[n * K + k] - (double)zeros[n * G + k / g]) *
+           or_half_value(scales[n * G + k / g]);
+}
+
+/*
+ * r[m, n] = sum_k x[m, k] * What[n, k] + sum_{(n, k) in CSR} x[m, k] * val,
+ * y = x * What^T with What = dequantize(codes, scales, zeros), accumulated in fp64.
+ * CSR pointers may be NULL (no outliers).
+ */
+void or_linear(int64_t M, int64_t N, int64_t K, int g,
+               const uint16_t *x, int64_t ldx,
+               const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros,
+               const int32_t *rowptr, const int32_t *col, const uint16_t *val,
+               double *r, int64_t ldr)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += or_half_value(x[m * ldx + k]) * dequant(codes, scales, zeros, K, g, n, k);
+            if (rowptr)
+                for (int32_t p = rowptr[n]; p < rowptr[n + 1]; ++p)
+                    acc += or_half_value(x[m * ldx + col[p]]) * or_half_value(val[p]);
+            r[m * ldr + n] = acc;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------------ */
+/* Routed experts  ([MoE] s4.2: hidden states + top-k expert ids per token)         */
+/* ------------------------------------------------------------------------------ */
+
+static double silu(double v) { return v / (1.0 + exp(-v)); }
+
+/*
+ * Per token t: out[t] = sum_j p[t][j] * FFN_{e}(x[t]), e = ids[t][j], with
+ * FFN_e(x) = What_down_e * fp16( silu(What_gate_e x) * (What_up_e x) ).
+ * Gate/up: codes [E][F][D], scales/zeros [E][F][D/g]; down: codes [E][D][F],
+ * scales/zeros [E][D][F/g].  Accumulation in fp64; the SwiGLU product is rounded to
+ * fp16 once (the intermediate activation is stored in fp16).  r is [T][D] fp64.
+ */
+void or_moe_ffn(int64_t T, int64_t D, int64_t F, int topk, int g,
+                const int32_t *ids, const float *wts, const uint16_t *x,
+                const uint8_t *gc, const uint16_t *gs, const uint8_t *gz,
+                const uint8_t *uc, const uint16_t *us, const uint8_t *uz,
+                const uint8_t *dc, const uint16_t *ds, const uint8_t *dz,
+                double *r)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t d = 0; d < D; ++d) r[t * D + d] = 0.0;
+        double *a = (double *)malloc((size_t)F * sizeof(double));
+        for (int j = 0; j < topk; ++j) {
+            int64_t e = ids[t * topk + j];
+            double p = (double)wts[t * topk + j];
+            const uint8_t *gce = gc + e * F * D, *uce = uc + e * F * D, *dce = dc + e * D * F;
+            const uint16_t *gse = gs + e * F * (D / g), *use = us + e * F * (D / g);
+            const uint8_t *gze = gz + e * F * (D / g), *uze = uz + e * F * (D / g);
+            const uint16_t *dse = ds + e * D * (F / g);
+            const uint8_t *dze = dz + e * D * (F / g);
+#pragma omp parallel for schedule(static)
+            for (int64_t f = 0; f < F; ++f) {
+                double gv = 0.0, uv = 0.0;
+                for (int64_t d = 0; d < D; ++d) {
+                    double xv = or_half_value(x[t * D + d]);
+                    gv += xv * dequant(gce, gse, gze, D, g, f, d);
+                    uv += xv * dequant(uce, use, uze, D, g, f, d);
+                }
+                a[f] = or_half_value(or_round_half(silu(gv) * uv));
+            }
+#pragma omp parallel for schedule(static)
+            for (int64_t d = 0; d < D; ++d) {
+                double o = 0.0;
+                for (int64_t f = 0; f < F; ++f) o += a[f] * dequant(dce, dse, dze, F, g, d, f);
+                r[t * D + d] += p * o;
+            }
+        }
+        free(a);
+    }
+}
+
+/* ------------------------------------------------------------------------------ */
+/* Byte accounting  ([MB] s1.2, s2.3; [KV] s1.1, s3.1-s3.3; [MoE] s1.1)             */
+/* ------------------------------------------------------------------------------ */
+
+/* Bytes of `numel` weights at `bits` with one scale (scale_bytes) and a zp of
+ * zp_bits per group of g: numel*b/8 + (numel/g)*(scale_bytes + zp_bits/8). */
+double or_quant_bytes(double numel, double bits, double g, double scale_bytes, double zp_bits)
+{
+    return numel * bits / 8.0 + (numel / g) * (scale_bytes + zp_bits / 8.0);
+}
+
+/* KV cache bytes: 2 (K and V) * layers * kv_heads * head_dim * tokens * bytes/elem. */
+double or_kv_bytes(double layers, double kv_heads, double head_dim, double tokens,
+                   double bytes_per_elem)
+{
+    return 2.0 * layers * kv_heads * head_dim * tokens * bytes_per_elem;
+}
+
+/* Threads the parallel loops above use. */
+int or_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

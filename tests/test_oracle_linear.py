@@ -1,0 +1,82 @@
+"""Pins for the oracle's fp64 linear layer y = x * What^T (+ fp16 outlier add-back).
+
+Definition: single-GPU 70B page, s3 (unfused path: dequantize, then matmul(x, W^T)) and
+s2 (held-out fp16 weights added back after the GEMM)."""
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+import workloads
+
+
+def dequant64(q):
+    G = q["scales"].shape[1]
+    s = q["scales"].view(np.float16).astype(np.float64)
+    z = q["zeros"].astype(np.float64)
+    return (q["codes"].astype(np.float64) - np.repeat(z, 128, axis=1)) * np.repeat(s, 128, axis=1)
+
+
+def csr_dense(q, N, K):
+    d = np.zeros((N, K))
+    rows = np.repeat(np.arange(N), np.diff(q["rowptr"]))
+    d[rows, q["col"]] = q["val"].view(np.float16).astype(np.float64)
+    return d
+
+
+def test_exact_rational_brute_force():
+    """Tiny case: the fp64 result equals the exactly-rounded rational sum to within the
+    rounding of a 256-term fp64 sum."""
+    M, N, K = 2, 3, 256
+    w = workloads.weights_fp16(N, K, 7)
+    w[1, 5] = np.float16(4.0)
+    x = workloads.activations_fp16(M, K, 7)
+    q = oracle.quantize(w, 3, 1.5 / (N * K))
+    r = oracle.linear(x, q)
+    for m in range(M):
+        for n in range(N):
+            exact = Fraction(0)
+            for k in range(K):
+                g = k // 128
+                qv = int(q["codes"][n, k]) - int(q["zeros"][n, g])
+                s = Fraction(float(np.uint16(q["scales"][n, g]).view(np.float16)))
+                exact += Fraction(float(x[m, k])) * qv * s
+            for p in range(q["rowptr"][n], q["rowptr"][n + 1]):
+                exact += Fraction(float(x[m, q["col"][p]])) * \
+                    Fraction(float(np.uint16(q["val"][p]).view(np.float16)))
+            assert abs(r[m, n] - float(exact)) <= 1e-13 * max(1.0, abs(float(exact)))
+    assert len(q["col"]) == 1 and q["col"][0] == 5
+
+
+def test_one_hot_activation_selects_a_weight():
+    N, K = 8, 512
+    q = oracle.quantize(workloads.weights_fp16(N, K, 11), 5)
+    for kstar in (0, 127, 128, 300, 511):
+        x = np.zeros((1, K), np.float16)
+        x[0, kstar] = 1.0
+        assert np.array_equal(oracle.linear(x, q)[0], dequant64(q)[:, kstar])
+
+
+def test_codes_at_zero_point_leave_only_outliers():
+    N, K = 16, 256
+    w = np.zeros((N, K), np.float16)
+    pos = np.array([3, 700, 2000, 4000])
+    w.reshape(-1)[pos] = np.float16([3.5, -4.0, 3.25, 4.75])
+    q = oracle.quantize(w, 4, len(pos) / (N * K))
+    x = workloads.activations_fp16(3, K, 2)
+    want = x.astype(np.float64) @ csr_dense(q, N, K).T
+    assert np.array_equal(oracle.linear(x, q), want)
+    assert not oracle.linear(x, q, outliers=False).any()
+
+
+def test_matches_library_matmul():
+    """Without rounding-order effects beyond fp64, r equals numpy's fp64 product of x
+    with the dequantized weight plus the dense outlier matrix."""
+    M, N, K = 4, 48, 1024
+    w = workloads.weights_fp16(N, K, 21)
+    workloads.plant_outliers(w, 0.002, 21)
+    x = workloads.activations_fp16(M, K, 21)
+    q = oracle.quantize(w, 6, 0.002)
+    want = x.astype(np.float64) @ (dequant64(q) + csr_dense(q, N, K)).T
+    got = oracle.linear(x, q)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
