@@ -1,0 +1,235 @@
+"""Benchmark: weight-only mixed-bit decode GEMV on one MI355X.
+
+Workload (one "step"): the 4096 x 4096 layer at 2, 3, 5 and 6 bits (asymmetric, groups of
+128 along K, page packing units) times decode batches M = 1, 4, 8 -- twelve qlinear_gemv
+calls.  Weights are quantized and packed once (the offline repack of the 70B page, s3) and
+the step rotates over enough identical copies (>= 1 GB in total) that every weight byte is
+read from HBM, as in a real decode pass over distinct layers, not from the 256 MB
+Infinity Cache.  Each step is one captured HIP graph, replayed.
+
+value = packed-weight bytes (codes + fp16 scales + u8 zero points) of the step / step time.
+The roofline object covers the kernel with the largest share of the step, timed live with
+HIP events around a graph of back-to-back launches on its own stream.  A secondary line
+measures the prefill dequant-GEMM (M=512, K=8192, N=28672, 4-bit + 0.1% outliers) in
+TFLOP/s.  cpu_baseline times the CPU oracle on the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "packed-weight GB/s (% HBM peak) at M=1 GEMV; TFLOP/s (% MFMA peak) at M=512"
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def quantize_pack(q, torch, w: np.ndarray, bits: int, frac: float = 0.0):
+    n, k = w.shape
+    dev = torch.device("cuda")
+    d = q.desc(bits, n, k)
+    wd = torch.from_numpy(np.ascontiguousarray(w).view(np.int16)).to(dev)
+    codes = torch.empty((n, k), dtype=torch.uint8, device=dev)
+    scales = torch.empty((n, k // 128), dtype=torch.int16, device=dev)
+    zeros = torch.empty((n, k // 128), dtype=torch.uint8, device=dev)
+    kout = q.qp_outlier_count(n, k, frac)
+    rowptr = torch.zeros(n + 1, dtype=torch.int32, device=dev)
+    col = torch.empty(max(kout, 1), dtype=torch.int32, device=dev)
+    val = torch.empty(max(kout, 1), dtype=torch.int16, device=dev)
+    wsb = q.qpack_quantize_workspace_bytes(d, frac)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    _, nnz = q.qpack_quantize(d, wd, k, frac, codes, scales, zeros, rowptr, col, val, kout, ws, wsb)
+    packed = torch.empty(q.qp_packed_bytes(d), dtype=torch.uint8, device=dev)
+    q.qpack_pack(d, codes, packed)
+    torch.cuda.synchronize()
+    del wd, codes, ws
+    return d, dict(packed=packed, scales=scales, zeros=zeros, rowptr=rowptr, col=col, val=val, nnz=nnz)
+
+
+def weight_bytes(n: int, k: int, bits: int, nnz: int = 0) -> int:
+    """Algorithmic bytes a matmul must read for the weight: packed codes, fp16 scale and u8
+    zero point per group of 128, plus the outlier CSR (int32 col + fp16 val + rowptr)."""
+    csr = (nnz * 6 + (n + 1) * 4) if nnz else 0
+    return n * k * bits // 8 + (n * k // 128) * 3 + csr
+
+
+def time_graph(torch, fn, reps: int, stream) -> float:
+    """Average ms of one fn() call: a graph of `reps` back-to-back calls, events around it."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(reps):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = float("inf")
+    for _ in range(3):
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) / reps)
+    return best
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=32, help="rotating weight copies (>= 1 GB total)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the M=512 GEMM secondary line")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part "
+              "of this build", flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import weight_only_mixed_amd as q
+    import workloads
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda")
+    K = N = 4096
+    bits_list, m_list = workloads.SWEEP_BITS, workloads.SWEEP_M
+
+    log("bench: quantize + pack 4096x4096 at 2/3/5/6 bits")
+    w = workloads.layer_weights(2)
+    W = {}
+    for b in bits_list:
+        d, wt = quantize_pack(q, torch, w, b)
+        copies = [dict(packed=wt["packed"].clone(), scales=wt["scales"].clone(), zeros=wt["zeros"].clone())
+                  for _ in range(args.copies)]
+        W[b] = (d, [q.weight(c["packed"], c["scales"], c["zeros"]) for c in copies], copies)
+    X = {m: torch.from_numpy(workloads.activations_fp16(m, K, workloads.seed_for(2)).view(np.int16)).to(dev)
+         for m in m_list}
+    Y = {(b, m): torch.empty((m, N), dtype=torch.int16, device=dev) for b in bits_list for m in m_list}
+    step_bytes = sum(weight_bytes(N, K, b) for b in bits_list) * len(m_list)
+    total_copy_bytes = sum(weight_bytes(N, K, b) for b in bits_list) * args.copies
+    log(f"bench: {args.copies} copies, {total_copy_bytes / 2**30:.2f} GiB of packed weights")
+
+    def step(c):
+        for b in bits_list:
+            d, hs, _ = W[b]
+            for m in m_list:
+                q.qlinear_gemv(d, hs[c % args.copies], X[m], K, m, Y[(b, m)], N)
+
+    stream = torch.cuda.Stream()
+    graphs = []
+    for c in range(args.copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            step(c)
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    log(f"bench: warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        graphs[i % args.copies].replay()
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for i in range(args.steps):
+            graphs[i % args.copies].replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = e0.elapsed_time(e1)
+    ms_per_step = ms_total / args.steps
+    value = step_bytes * args.steps / (ms_total * 1e-3) / 1e9
+
+    # per-kernel live timing (graphs of back-to-back launches of one (bits, M) kernel)
+    log("bench: per-kernel timing")
+    per = {}
+    for b in bits_list:
+        d, hs, _ = W[b]
+        for m in m_list:
+            fn = lambda i, d=d, hs=hs, m=m, b=b: q.qlinear_gemv(d, hs[i % args.copies], X[m], K, m, Y[(b, m)], N)
+            ms = time_graph(torch, fn, 4 * args.copies, stream)
+            per[f"b{b}_m{m}"] = dict(us=ms * 1e3, GBps=weight_bytes(N, K, b) / (ms * 1e-3) / 1e9)
+    dom = max(per, key=lambda key: per[key]["us"])
+    b_dom = int(dom.split("_")[0][1:])
+    dom_bytes = weight_bytes(N, K, b_dom)
+    achieved = dom_bytes / (per[dom]["us"] * 1e-6) / 1e9
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    kernel=f"qp::gemv_kernel<{b_dom}, 8> ({dom})", bytes_per_launch=dom_bytes,
+                    avg_launch_us=round(per[dom]["us"], 3))
+
+    extra = {}
+    if not args.no_prefill:
+        log("bench: prefill GEMM M=512 K=8192 N=28672 4-bit + 0.1% outliers")
+        wp, _ = workloads.prefill_weights()
+        dp, wt = quantize_pack(q, torch, wp, 4, workloads.PREFILL_OUTLIER_FRAC)
+        del wp
+        hp = q.weight(wt["packed"], wt["scales"], wt["zeros"], wt["rowptr"], wt["col"], wt["val"], wt["nnz"])
+        xp = torch.from_numpy(workloads.prefill_activations().view(np.int16)).to(dev)
+        Mp, Kp, Np = workloads.PREFILL_M, workloads.PREFILL_K, workloads.PREFILL_N
+        yp = torch.empty((Mp, Np), dtype=torch.int16, device=dev)
+        ms = time_graph(torch, lambda i: q.qlinear_gemm(dp, hp, xp, Kp, Mp, yp, Np), 10, stream)
+        flops = 2 * Mp * Np * Kp + 2 * Mp * wt["nnz"]
+        tf = flops / (ms * 1e-3) / 1e12
+        extra["prefill_gemm_m512"] = dict(us=round(ms * 1e3, 2), TFLOPs=round(tf, 1),
+                                          frac_mfma_f16=round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                                          flops=flops, kernel="qp::gemm_kernel<4>")
+        del hp, wt, xp, yp
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        log("bench: CPU oracle baseline")
+        refs = {b: oracle.quantize(w, b) for b in bits_list}
+        xs = {m: workloads.activations_fp16(m, K, workloads.seed_for(2)) for m in m_list}
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            for b in bits_list:
+                for m in m_list:
+                    oracle.linear(xs[m], refs[b])
+            reps += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds or reps >= 50:
+                break
+        dt = time.perf_counter() - t0
+        cpu = dict(value=round(step_bytes * reps / dt / 1e9, 4), unit="GB/s", cores=oracle.num_threads(),
+                   kind="oracle",
+                   sample=f"{reps} full steps (12 fp64 GEMVs over the oracle's own codes), {dt:.1f} s")
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "4096x4096 layer, bits {2,3,5,6} x decode M {1,4,8}, asymmetric g=128, "
+                               "page units, device tile layout",
+                   "bits": list(bits_list), "m": list(m_list), "n": N, "k": K,
+                   "weight_copies": args.copies, "step_weight_bytes": step_bytes,
+                   "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_kernel": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in per.items()},
+        **extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,241 @@
+/*
+ * qpack.h -- C ABI of the MI355X (gfx950) weight-only mixed-bit quantized linear layer.
+ *
+ * Weights W[n][k] (n = output feature, k = input feature) are quantized to b = 2..6 bits
+ * with one fp16 scale and one integer zero point per group of 128 consecutive k of a row,
+ * packed in the page units, dequantized on the GPU and multiplied by fp16 activations:
+ *     y[m][n] = sum_k x[m][k] * (q[n][k] - zp[n][k/128]) * s[n][k/128]
+ *             + sum_{(n,k) in outliers} x[m][k] * w[n][k].
+ *
+ * Passages this interface follows (page title, section):
+ *  - quantization formula scale=(max-min)/(qmax-qmin), zero_point=qmin-round(min/scale),
+ *    q=round(x/scale)+zero_point, x_hat=(q-zero_point)*scale:
+ *    "大模型推理加速实战：量化、投机采样与PD分离的工程指南", s1.1;
+ *  - groups of 128, top-0.1% |w| held out in fp16 and added back after the GEMM, fused
+ *    dequant-GEMM argument list (a, b, c, scale, zero_point, M, N, K, strides), unfused
+ *    reference dequantize -> matmul(x, W^T), one-time device repack:
+ *    "单卡运行70B大模型的五层技术栈实战", s2 and s3;
+ *  - packing units (2-bit: 4 values/1 byte, 3-bit: 8/3, 5-bit: 8/5, 6-bit: 4/3), LSB-first
+ *    values in little-endian units, fp16 scales, fp32 scale multiply, scales ordered to
+ *    match GPU tiles: 2/3/5/6-bit mixed quantization page (pwwt.cn), s2.3, s3.1-s3.3, s4.2;
+ *  - 4-bit packs two values per byte: KV-cache quantization page (kwkr.cn), s5.1;
+ *  - routed experts receive hidden states plus top-k expert ids:
+ *    "端侧MoE推理存储墙优化：显存精算、预取重叠与量化补偿实战", s4.2.
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers (hipMalloc'd memory, e.g. torch tensors), except
+ *    where a parameter says "host".  The caller owns and allocates every buffer; the library
+ *    allocates nothing and keeps no state between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = default stream).  Calls are
+ *    asynchronous on that stream; no call synchronizes the device.
+ *  - Arguments are validated on the host before anything is launched.  On any status other
+ *    than QP_OK nothing has been written, except QP_ERR_DEVICE (a launch failed; outputs are
+ *    undefined).  qp_last_error() then returns a message for the calling thread.
+ *  - No C++ exception crosses this interface.  Inputs must be finite (not checked).
+ *  - fp16 values are passed as their uint16_t bit patterns.
+ */
+#ifndef QPACK_H
+#define QPACK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QP_OK = 0,
+    QP_ERR_INVALID_ARG = 1, /* bad shape, pointer, alignment or stride */
+    QP_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. group size other than 128) */
+    QP_ERR_DEVICE = 3,      /* a HIP launch failed; message in qp_last_error() */
+    QP_ERR_WORKSPACE = 4    /* workspace or CSR capacity too small */
+} qp_status;
+
+/* Packed-byte layouts.
+ * QP_LAYOUT_CANONICAL: row n occupies k*bits/8 bytes; row n's codes in k order are cut into
+ *   page units (u values per unit: 4, 8, 2, 8, 4 for b = 2, 3, 4, 5, 6); value i of a unit is
+ *   bits [b*i, b*i+b) of the little-endian integer formed by the unit's bytes.
+ * QP_LAYOUT_DEVICE: a permutation of the canonical bytes that keeps every unit whole and
+ *   stores the matrix as 16-row x 256-k tiles (row-block major, then k-tile; 512*b bytes per
+ *   tile).  In a tile, lane l = 16*t + r (r = row in the block, t = 0..3) owns a chunk of
+ *   eight 8-k blocks of row r -- block j (0..7) starts at k0 = 256*kt + 128*(j/4) +
+ *   32*(j%4) + 8*t and is b canonical bytes -- and chunk byte c is stored at
+ *   1024*(c/16) + 16*l + c%16 while c < F = 16*floor(b/2), else at 64*F + 8*l + (c-F).
+ *   Each lane's chunk is what one wave lane feeds to eight 16x16x32 matrix-core steps.
+ *   Requires n % 16 == 0 and k % 256 == 0. */
+enum { QP_LAYOUT_CANONICAL = 0, QP_LAYOUT_DEVICE = 1 };
+
+/* Epilogues of qlinear_grouped_gemm. */
+enum {
+    QP_EPI_NONE = 0,    /* y[r][n] = fp16(acc)                                        */
+    QP_EPI_SWIGLU = 1,  /* rows are gate/up blocks interleaved by 16 (see below);
+                           y[r][j] = fp16(silu(gate_j) * up_j), j < n/2                */
+    QP_EPI_ROWS_F32 = 2 /* y is float: y[r][n] = acc (fp32), for a later combine      */
+};
+
+/* Shape and format of one quantized matrix W[n][k]. */
+typedef struct {
+    int32_t bits;       /* 2, 3, 4, 5 or 6 */
+    int32_t group_size; /* 128 (groups of consecutive k inside a row) */
+    int32_t layout;     /* QP_LAYOUT_CANONICAL or QP_LAYOUT_DEVICE */
+    int32_t reserved;   /* must be 0 */
+    int64_t n;          /* rows (output features) */
+    int64_t k;          /* columns (input features), multiple of group_size */
+} qp_weight_desc;
+
+/* Device buffers of one quantized matrix. */
+typedef struct {
+    const void *packed;         /* qp_packed_bytes(desc) bytes, 16-byte aligned */
+    const uint16_t *scales;     /* fp16 [n][k/128], row-major (planar), 4-byte aligned */
+    const uint8_t *zeros;       /* u8   [n][k/128], row-major, 2-byte aligned */
+    const int32_t *csr_rowptr;  /* [n+1] outlier CSR over rows of W, or NULL */
+    const int32_t *csr_col;     /* [nnz] column k of each outlier, ascending within a row */
+    const uint16_t *csr_val;    /* [nnz] fp16 value of each outlier */
+    int64_t nnz;                /* number of outliers (0 if csr_rowptr is NULL) */
+} qp_weight;
+
+/* ---- host-side accounting (no device work) ------------------------------------------ */
+
+/* n*k*bits/8, or 0 if desc is invalid. */
+size_t qp_packed_bytes(const qp_weight_desc *desc);
+/* n*k/group_size, or 0 if desc is invalid. */
+size_t qp_num_groups(const qp_weight_desc *desc);
+/* Bytes of `numel` weights at `bits` with one scale of `scale_bytes` and a zero point of
+ * `zp_bits` per group of `group`: numel*bits/8 + (numel/group)*(scale_bytes + zp_bits/8)
+ * (mixed-bit page s2.3; KV page s3.1). */
+double qp_quant_bytes(double numel, double bits, double group, double scale_bytes,
+                      double zp_bits);
+/* Number of held-out outliers for a fraction of an n x k matrix: floor(frac * n * k)
+ * computed in double (0 for frac <= 0). */
+int64_t qp_outlier_count(int64_t n, int64_t k, double frac);
+
+/* ---- quantize and pack -------------------------------------------------------------- */
+
+/* Scratch bytes qpack_quantize needs for this shape and outlier fraction (0 if none). */
+size_t qpack_quantize_workspace_bytes(const qp_weight_desc *desc, double outlier_frac);
+
+/*
+ * Group quantizer (inference-acceleration page s1.1; 70B page s2).
+ *  w        fp16 [n][ldw] device, ldw >= k, ldw even, 4-byte aligned.
+ *  outlier_frac  0 for none; else the floor(frac*n*k) largest |w| (fp16 magnitude, ties to
+ *           the lower row-major index) are held out: their dense slot becomes +0 before
+ *           the group range is taken, and the original values go to the CSR.
+ *  codes    u8 [n][k] device (one code per byte, unpacked).
+ *  scales   fp16 [n][k/128], zeros u8 [n][k/128] device.
+ *  csr_rowptr [n+1], csr_col [csr_cap], csr_val [csr_cap] device; may be NULL when
+ *           outlier_frac == 0 (csr_rowptr, if given, is then filled with zeros).
+ *  nnz_out  HOST pointer, receives the outlier count (also when QP_ERR_WORKSPACE is
+ *           returned because csr_cap is too small).
+ *  workspace/ws_bytes  device scratch of at least qpack_quantize_workspace_bytes().
+ * Per group: lo = min(min w, 0), hi = max(max w, 0); all-zero group -> s = 1, zp = 0;
+ * s = fp16_rne((hi-lo)/qmax) in IEEE fp32, raised to 2^-14 if it is zero or subnormal;
+ * zp = clamp(-rint(lo/s), 0, qmax); q = clamp(rint(w/s) + zp, 0, qmax) (ties to even).
+ * Layout of desc is ignored.  Bit-exact with the CPU reference.
+ */
+qp_status qpack_quantize(const qp_weight_desc *desc, const uint16_t *w, int64_t ldw,
+                         double outlier_frac, uint8_t *codes, uint16_t *scales,
+                         uint8_t *zeros, int32_t *csr_rowptr, int32_t *csr_col,
+                         uint16_t *csr_val, int64_t csr_cap, int64_t *nnz_out,
+                         void *workspace, size_t ws_bytes, void *stream);
+
+/* codes u8 [n][k] (values < 2^bits) -> packed bytes in desc->layout
+ * (qp_packed_bytes(desc) bytes, 16-byte aligned). */
+qp_status qpack_pack(const qp_weight_desc *desc, const uint8_t *codes, void *packed,
+                     void *stream);
+
+/* Inverse of qpack_pack: packed bytes in desc->layout -> codes u8 [n][k]. */
+qp_status qpack_unpack(const qp_weight_desc *desc, const void *packed, uint8_t *codes,
+                       void *stream);
+
+/* ---- matmuls ------------------------------------------------------------------------ */
+
+/*
+ * Decode GEMV, 1 <= m <= 16 (fused dequant: 70B page s3; fp32 scale: mixed-bit page s4.2).
+ *  desc->layout must be QP_LAYOUT_DEVICE.
+ *  x  fp16 [m][ldx] device, ldx >= k, ldx % 8 == 0, 16-byte aligned.
+ *  y  fp16 [m][ldy] device, ldy >= n, ldy % 4 == 0, 8-byte aligned.
+ *  The optional CSR of `w` is added in fp32 before the single fp16 rounding of y.
+ * Returns QP_ERR_UNSUPPORTED for m > 16 (use qlinear_gemm).
+ */
+qp_status qlinear_gemv(const qp_weight_desc *desc, const qp_weight *w, const uint16_t *x,
+                       int64_t ldx, int64_t m, uint16_t *y, int64_t ldy, void *stream);
+
+/*
+ * Prefill dequant-GEMM for any m >= 1 (tuned for m >= 64): same operands and result as
+ * qlinear_gemv.  Tiles of the packed weight are unpacked in registers and fed to fp16
+ * matrix cores with fp32 accumulation; scales are applied per group in fp32.
+ */
+qp_status qlinear_gemm(const qp_weight_desc *desc, const qp_weight *w, const uint16_t *x,
+                       int64_t ldx, int64_t m, uint16_t *y, int64_t ldy, void *stream);
+
+/*
+ * Grouped dequant-GEMM over routed experts (MoE page s4.2).  All experts share `desc`
+ * (layout QP_LAYOUT_DEVICE).  `experts` is a HOST array of n_experts (<= 64) weights.
+ *  row_src         int32 [rows] device: token (row of x) feeding sorted row r.
+ *  expert_offsets  int32 [n_experts+1] device: rows of expert e are
+ *                  [expert_offsets[e], expert_offsets[e+1]); offsets[n_experts] <= rows.
+ *  rows            host upper bound on expert_offsets[n_experts] (sizes nothing but
+ *                  argument checks).
+ *  epilogue        QP_EPI_NONE: y fp16 [rows][ldy];
+ *                  QP_EPI_SWIGLU: row blocks 2i and 2i+1 of each expert matrix hold gate
+ *                  rows 16i..16i+15 and up rows 16i..16i+15; y fp16 [rows][ldy] gets
+ *                  silu(gate)*up for n/2 columns (n % 32 == 0);
+ *                  QP_EPI_ROWS_F32: y is float [rows][ldy].
+ * Experts with no rows cost no weight traffic.
+ */
+qp_status qlinear_grouped_gemm(const qp_weight_desc *desc, const qp_weight *experts,
+                               int32_t n_experts, const uint16_t *x, int64_t ldx,
+                               const int32_t *row_src, const int32_t *expert_offsets,
+                               int64_t rows, int32_t epilogue, void *y, int64_t ldy,
+                               void *stream);
+
+/* ---- routed-expert plumbing (MoE page s4.2) ----------------------------------------- */
+
+/*
+ * Sort the tokens' top-k choices by expert (stable in token, then choice order).
+ *  topk_ids   int32 [tokens][topk] device, values in [0, n_experts).
+ *  topk_w     float [tokens][topk] device, combine weights.
+ *  expert_offsets int32 [n_experts+1], row_src int32 [tokens*topk],
+ *  row_weight float [tokens*topk], token_rows int32 [tokens][topk] (sorted row of each
+ *  choice) -- all device outputs.  tokens*topk <= 65536, n_experts <= 64.
+ */
+qp_status qmoe_dispatch(const int32_t *topk_ids, const float *topk_w, int64_t tokens,
+                        int32_t topk, int32_t n_experts, int32_t *expert_offsets,
+                        int32_t *row_src, float *row_weight, int32_t *token_rows,
+                        void *stream);
+
+/*
+ * out[t][j] = fp16( sum_{c < topk} row_weight[r_c] * rows_f32[r_c][j] ), r_c =
+ * token_rows[t][c], summed in fp32 in choice order (deterministic, no atomics).
+ *  rows_f32 float [*][ld_rows], out fp16 [tokens][ldo], n columns.
+ */
+qp_status qmoe_combine(const float *rows_f32, int64_t ld_rows, const int32_t *token_rows,
+                       const float *row_weight, int64_t tokens, int32_t topk, int64_t n,
+                       uint16_t *out, int64_t ldo, void *stream);
+
+/* Scratch bytes of qmoe_ffn. */
+size_t qmoe_ffn_workspace_bytes(int64_t tokens, int32_t topk, int32_t n_experts,
+                                int64_t d_model, int64_t d_ff);
+
+/*
+ * Whole routed-expert FFN on one stream: dispatch, grouped gate/up GEMM with SwiGLU
+ * (intermediate stored in fp16), grouped down GEMM (fp32 rows), weighted combine.
+ *  gate_up[e]: desc_gu = {bits, 128, DEVICE, 0, 2*d_ff, d_model}, gate/up rows interleaved
+ *              in blocks of 16 (see QP_EPI_SWIGLU);  down[e]: desc_d = {.., d_model, d_ff}.
+ *  x fp16 [tokens][ldx]; out fp16 [tokens][ldo]; HOST arrays gate_up/down.
+ */
+qp_status qmoe_ffn(const qp_weight_desc *desc_gu, const qp_weight *gate_up,
+                   const qp_weight_desc *desc_d, const qp_weight *down, int32_t n_experts,
+                   const uint16_t *x, int64_t ldx, int64_t tokens, const int32_t *topk_ids,
+                   const float *topk_w, int32_t topk, uint16_t *out, int64_t ldo,
+                   void *workspace, size_t ws_bytes, void *stream);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char *qp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QPACK_H */

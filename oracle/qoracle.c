@@ -64,6 +64,20 @@ double or_half_value(uint16_t h)
     return s ? -v : v;
 }
 
+/* Table of or_half_value over all 65536 patterns (filled once from the definition above;
+ * a speed convenience for the large sampled checks, same values). */
+static double g_half_table[65536];
+static int g_half_table_ready;
+
+static double hv(uint16_t h)
+{
+    if (!g_half_table_ready) {
+        for (int i = 0; i < 65536; ++i) g_half_table[i] = or_half_value((uint16_t)i);
+        g_half_table_ready = 1;
+    }
+    return g_half_table[h];
+}
+
 /* Round a binary64 value to the nearest binary16, ties to even (one rounding). */
 uint16_t or_round_half(double x)
 {
@@ -103,7 +117,7 @@ void or_quantize_group(const uint16_t *w, int n, int bits,
     const int qmin = 0, qmax = (1 << bits) - 1;
     float lo = 0.0f, hi = 0.0f;                      /* range always contains 0 */
     for (int i = 0; i < n; ++i) {
-        float v = (float)or_half_value(w[i]);
+        float v = (float)hv(w[i]);
         if (v < lo) lo = v;
         if (v > hi) hi = v;
     }
@@ -122,7 +136,7 @@ void or_quantize_group(const uint16_t *w, int n, int bits,
     volatile float lo_over_s = lo / sf;
     int zp = clampi(qmin - (int)rintf(lo_over_s), qmin, qmax);
     for (int i = 0; i < n; ++i) {
-        volatile float t = (float)or_half_value(w[i]) / sf;
+        volatile float t = (float)hv(w[i]) / sf;
         codes_out[i] = (uint8_t)clampi((int)rintf(t) + zp, qmin, qmax);
     }
     *scale_out = sh;
@@ -324,7 +338,7 @@ static double dequant(const uint8_t *codes, const uint16_t *scales, const uint8_
 {
     int64_t G = K / g;
     return ((double)codes[n * K + k] - (double)zeros[n * G + k / g]) *
-           or_half_value(scales[n * G + k / g]);
+           hv(scales[n * G + k / g]);
 }
 
 /*
@@ -338,15 +352,16 @@ void or_linear(int64_t M, int64_t N, int64_t K, int g,
                const int32_t *rowptr, const int32_t *col, const uint16_t *val,
                double *r, int64_t ldr)
 {
+    (void)hv(0);  /* fill the table before the parallel loop */
 #pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t m = 0; m < M; ++m) {
             double acc = 0.0;
             for (int64_t k = 0; k < K; ++k)
-                acc += or_half_value(x[m * ldx + k]) * dequant(codes, scales, zeros, K, g, n, k);
+                acc += hv(x[m * ldx + k]) * dequant(codes, scales, zeros, K, g, n, k);
             if (rowptr)
                 for (int32_t p = rowptr[n]; p < rowptr[n + 1]; ++p)
-                    acc += or_half_value(x[m * ldx + col[p]]) * or_half_value(val[p]);
+                    acc += hv(x[m * ldx + col[p]]) * hv(val[p]);
             r[m * ldr + n] = acc;
         }
     }
@@ -372,6 +387,7 @@ void or_moe_ffn(int64_t T, int64_t D, int64_t F, int topk, int g,
                 const uint8_t *dc, const uint16_t *ds, const uint8_t *dz,
                 double *r)
 {
+    (void)hv(0);
     for (int64_t t = 0; t < T; ++t) {
         for (int64_t d = 0; d < D; ++d) r[t * D + d] = 0.0;
         double *a = (double *)malloc((size_t)F * sizeof(double));
@@ -387,11 +403,11 @@ void or_moe_ffn(int64_t T, int64_t D, int64_t F, int topk, int g,
             for (int64_t f = 0; f < F; ++f) {
                 double gv = 0.0, uv = 0.0;
                 for (int64_t d = 0; d < D; ++d) {
-                    double xv = or_half_value(x[t * D + d]);
+                    double xv = hv(x[t * D + d]);
                     gv += xv * dequant(gce, gse, gze, D, g, f, d);
                     uv += xv * dequant(uce, use, uze, D, g, f, d);
                 }
-                a[f] = or_half_value(or_round_half(silu(gv) * uv));
+                a[f] = hv(or_round_half(silu(gv) * uv));
             }
 #pragma omp parallel for schedule(static)
             for (int64_t d = 0; d < D; ++d) {

@@ -1,0 +1,144 @@
+"""CPU-side checks of the C ABI: the library loads, exports every declared symbol, and the
+host-only paths (byte accounting, argument validation) behave as documented.  No call here
+launches a kernel: every device call below fails validation before any HIP work."""
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import pytest
+
+import weight_only_mixed_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qpack.h")
+GOLD = json.load(open(os.path.join(ROOT, "tests", "golden", "page_values.json")))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(q\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 14
+    out = subprocess.run(["nm", "-D", "--defined-only", q._LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(q.lib, n)
+    assert set(q.EXPORTED) == set(names)
+
+
+def test_packed_bytes_and_groups():
+    for bits in (2, 3, 4, 5, 6):
+        d = q.desc(bits, 4096, 4096)
+        assert q.qp_packed_bytes(d) == 4096 * 4096 * bits // 8
+        assert q.qp_num_groups(d) == 4096 * 32
+    assert q.qp_packed_bytes(q.desc(4, 28672, 8192)) == 117_440_512
+    assert q.qp_packed_bytes(q.desc(7, 16, 256)) == 0
+
+
+@pytest.mark.parametrize("c", GOLD["kv_quantized"] + [dict(numel=c["group"], bits=c["bits"], group=c["group"],
+                                                             scale_bytes=c["scale_bytes"], zp_bits=c["zp_bits"],
+                                                             bpw=c.get("value"))
+                                                        for c in GOLD["bits_per_weight"] if "value" in c])
+def test_quant_bytes_match_pages(c):
+    b = q.qp_quant_bytes(c["numel"], c["bits"], c["group"], c["scale_bytes"], c["zp_bits"])
+    if "bpw" in c:
+        assert b * 8 / c["group"] == c["bpw"]
+    elif "bytes" in c:
+        assert b == c["bytes"]
+    else:
+        assert b == c["bytes_approx"]
+
+
+def test_outlier_count():
+    assert q.qp_outlier_count(28672, 8192, 0.001) == 234_881
+    assert q.qp_outlier_count(64, 1024, 0.001) == 65
+    assert q.qp_outlier_count(10, 10, 0.0) == 0
+
+
+FAKE = 0x10000  # an aligned, never-dereferenced address: validation fails before any launch
+
+
+@pytest.mark.parametrize("d,expect", [
+    (q.desc(7, 16, 256), q.QP_ERR_INVALID_ARG),
+    (q.desc(1, 16, 256), q.QP_ERR_INVALID_ARG),
+    (q.desc(4, 16, 200), q.QP_ERR_INVALID_ARG),
+    (q.desc(4, 16, 256, group_size=64), q.QP_ERR_UNSUPPORTED),
+    (q.desc(4, 15, 256), q.QP_ERR_INVALID_ARG),           # device layout needs n % 16
+    (q.desc(4, 16, 384), q.QP_ERR_INVALID_ARG),           # device layout needs k % 256
+    (q.desc(4, 0, 256), q.QP_ERR_INVALID_ARG),
+])
+def test_pack_rejects_bad_descriptors(d, expect):
+    assert q.qpack_pack(d, FAKE, FAKE, stream=0, check=False) == expect
+    assert q.last_error()
+
+
+def test_pack_rejects_misaligned_pointers():
+    d = q.desc(4, 16, 256)
+    assert q.qpack_pack(d, FAKE + 1, FAKE, stream=0, check=False) == q.QP_ERR_INVALID_ARG
+    assert q.qpack_pack(d, FAKE, FAKE + 8, stream=0, check=False) == q.QP_ERR_INVALID_ARG
+    assert q.qpack_pack(d, None, FAKE, stream=0, check=False) == q.QP_ERR_INVALID_ARG
+
+
+def test_gemv_validation():
+    d = q.desc(4, 256, 512)
+    w = q.weight(FAKE, FAKE, FAKE)
+    assert q.qlinear_gemv(d, w, FAKE, 512, 17, FAKE, 256, stream=0, check=False) == q.QP_ERR_UNSUPPORTED
+    assert q.qlinear_gemv(d, w, FAKE, 512, 0, FAKE, 256, stream=0, check=False) == q.QP_ERR_INVALID_ARG
+    assert q.qlinear_gemv(d, w, FAKE, 500, 1, FAKE, 256, stream=0, check=False) == q.QP_ERR_INVALID_ARG
+    assert q.qlinear_gemv(d, w, FAKE + 2, 512, 1, FAKE, 256, stream=0, check=False) == q.QP_ERR_INVALID_ARG
+    assert q.qlinear_gemv(d, w, FAKE, 512, 1, FAKE, 100, stream=0, check=False) == q.QP_ERR_INVALID_ARG
+    canon = q.desc(4, 256, 512, layout=q.QP_LAYOUT_CANONICAL)
+    assert q.qlinear_gemv(canon, w, FAKE, 512, 1, FAKE, 256, stream=0, check=False) == q.QP_ERR_UNSUPPORTED
+    bad_csr = q.weight(FAKE, FAKE, FAKE, None, None, None, 5)
+    assert q.qlinear_gemm(d, bad_csr, FAKE, 512, 64, FAKE, 256, stream=0, check=False) == q.QP_ERR_INVALID_ARG
+    assert "csr" in q.last_error().lower()
+
+
+def test_quantize_validation():
+    d = q.desc(4, 64, 1024)
+    st, nnz = q.qpack_quantize(d, FAKE, 1024, 0.001, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, 1 << 20,
+                               stream=0, check=False)
+    assert st == q.QP_ERR_WORKSPACE and nnz == 65          # CSR capacity too small
+    st, _ = q.qpack_quantize(d, FAKE, 1024, 0.001, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 65, FAKE, 16,
+                             stream=0, check=False)
+    assert st == q.QP_ERR_WORKSPACE                         # workspace too small
+    st, _ = q.qpack_quantize(d, FAKE, 1023, 0.0, FAKE, FAKE, FAKE, stream=0, check=False)
+    assert st == q.QP_ERR_INVALID_ARG                       # odd / short ldw
+    st, _ = q.qpack_quantize(d, FAKE, 1024, 1.5, FAKE, FAKE, FAKE, stream=0, check=False)
+    assert st == q.QP_ERR_INVALID_ARG
+    assert q.qpack_quantize_workspace_bytes(d, 0.0) == 0
+    assert q.qpack_quantize_workspace_bytes(d, 0.001) > 32768 * 4
+
+
+def test_grouped_and_moe_validation():
+    d = q.desc(4, 256, 512)
+    w = q.weight(FAKE, FAKE, FAKE)
+    assert q.qlinear_grouped_gemm(d, [w] * 65, FAKE, 512, FAKE, FAKE, 10, 0, FAKE, 256, stream=0,
+                                  check=False) == q.QP_ERR_INVALID_ARG
+    assert q.qlinear_grouped_gemm(d, [w], FAKE, 512, FAKE, FAKE, 10, 9, FAKE, 256, stream=0,
+                                  check=False) == q.QP_ERR_INVALID_ARG
+    d48 = q.desc(4, 48, 512)
+    assert q.qlinear_grouped_gemm(d48, [w], FAKE, 512, FAKE, FAKE, 10, q.QP_EPI_SWIGLU, FAKE, 24, stream=0,
+                                  check=False) == q.QP_ERR_INVALID_ARG
+    assert q.qmoe_dispatch(FAKE, FAKE, 40000, 2, 16, FAKE, FAKE, FAKE, FAKE, stream=0,
+                           check=False) == q.QP_ERR_INVALID_ARG
+    assert q.qmoe_dispatch(FAKE, FAKE, 128, 2, 65, FAKE, FAKE, FAKE, FAKE, stream=0,
+                           check=False) == q.QP_ERR_INVALID_ARG
+    gu, dn = q.desc(4, 2 * 14336, 4096), q.desc(4, 4096, 14336)
+    need = q.qmoe_ffn_workspace_bytes(128, 2, 16, 4096, 14336)
+    assert need > 256 * 14336 * 2
+    assert q.qmoe_ffn(gu, [w] * 16, dn, [w] * 16, FAKE, 4096, 128, FAKE, FAKE, 2, FAKE, 4096, FAKE, need - 1,
+                      stream=0, check=False) == q.QP_ERR_WORKSPACE
+
+
+def test_status_message_is_thread_local_text():
+    q.qpack_pack(q.desc(9, 16, 256), FAKE, FAKE, stream=0, check=False)
+    assert "bits=9" in q.last_error()

@@ -1,0 +1,112 @@
+"""GPU parity: decode GEMV and prefill GEMM through the C ABI against the oracle's fp64
+accumulation of the dequantized weights (plus fp16 outlier add-back), within the floored
+relative tolerance of parity.TOL.  The oracle quantizes the same fp16 weights itself."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity import TOL, GpuWeight, from_dev_fp16, gpu, rel_err, report, to_dev_fp16
+
+pytestmark = pytest.mark.gpu
+BITS = (2, 3, 4, 5, 6)
+
+
+def run_linear(entry, g: GpuWeight, x: np.ndarray, with_csr=True):
+    torch, q = gpu()
+    m, k = x.shape
+    xd = to_dev_fp16(x)
+    y = torch.empty((m, g.n), dtype=torch.int16, device="cuda")
+    getattr(q, entry)(g.desc, g.handle(with_csr), xd, k, m, y, g.n)
+    torch.cuda.synchronize()
+    return from_dev_fp16(y)
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("m", (1, 3, 8, 16))
+def test_gemv_small_with_outliers(bits, m):
+    n, k, frac = 64, 1280, 0.002  # 5 k-tiles over 8 waves: idle waves and a ragged split
+    w = workloads.weights_fp16(n, k, 300 + bits)
+    workloads.plant_outliers(w, frac, 300 + bits)
+    x = workloads.activations_fp16(m, k, 300 + bits)
+    r = oracle.linear(x, oracle.quantize(w, bits, frac))
+    y = run_linear("qlinear_gemv", GpuWeight(w, bits, frac), x)
+    assert rel_err(y, r) <= TOL, report(y, r)
+
+
+@pytest.mark.parametrize("bits", (2, 3, 5, 6, 4))
+def test_gemv_layer_4096_full(bits):
+    """The single-layer sweep at full size (4096 x 4096), M = 1, 4, 8."""
+    w = workloads.layer_weights(1 if bits == 4 else 2)
+    ref_q = oracle.quantize(w, bits)
+    g = GpuWeight(w, bits)
+    for m in (1, 4, 8):
+        x = workloads.activations_fp16(m, 4096, workloads.seed_for(2))
+        r = oracle.linear(x, ref_q)
+        y = run_linear("qlinear_gemv", g, x)
+        assert rel_err(y, r) <= TOL, (m, report(y, r))
+
+
+def test_gemv_one_hot_exact():
+    """x = e_k returns fp16(What[:, k]) exactly (a single exact product per output)."""
+    n, k = 32, 512
+    w = workloads.weights_fp16(n, k, 7)
+    qd = oracle.quantize(w, 5)
+    g = GpuWeight(w, 5)
+    for kstar in (0, 255, 256, 511):
+        x = np.zeros((1, k), np.float16)
+        x[0, kstar] = 1.0
+        r = oracle.linear(x, qd)[0]
+        y = run_linear("qlinear_gemv", g, x)[0]
+        assert np.array_equal(y, r.astype(np.float16)), kstar
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("m", (1, 17, 200))
+def test_gemm_ragged_with_outliers(bits, m):
+    n, k, frac = 560, 1024, 0.002  # n is not a multiple of the 256-row workgroup tile
+    w = workloads.weights_fp16(n, k, 400 + bits)
+    workloads.plant_outliers(w, frac, 400 + bits)
+    x = workloads.activations_fp16(m, k, 400 + bits)
+    r = oracle.linear(x, oracle.quantize(w, bits, frac))
+    y = run_linear("qlinear_gemm", GpuWeight(w, bits, frac), x)
+    assert rel_err(y, r) <= TOL, report(y, r)
+
+
+def test_gemm_and_gemv_agree():
+    w = workloads.weights_fp16(256, 2048, 55)
+    x = workloads.activations_fp16(16, 2048, 55)
+    g = GpuWeight(w, 4)
+    a = run_linear("qlinear_gemv", g, x).astype(np.float64)
+    b = run_linear("qlinear_gemm", g, x).astype(np.float64)
+    assert rel_err(a, b) <= 2 * TOL
+
+
+def test_gemm_prefill_full_sampled():
+    """M=512, K=8192, N=28672, 4-bit + 0.1% outliers, the shape and launch the benchmark
+    times; 48 output rows x 40 activation rows recomputed by the oracle."""
+    w, pos = workloads.prefill_weights()
+    x = workloads.prefill_activations()
+    g = GpuWeight(w, 4, workloads.PREFILL_OUTLIER_FRAC)
+    y = run_linear("qlinear_gemm", g, x)
+    rng = np.random.default_rng(4)
+    ns = np.sort(rng.choice(w.shape[0], 48, replace=False))
+    ms = np.sort(rng.choice(x.shape[0], 40, replace=False))
+    w0 = w.copy()
+    w0.reshape(-1)[pos] = 0
+    sub = oracle.quantize(w0[ns], 4)
+    # the held-out values of the sampled rows, as an oracle-side CSR
+    dense = np.zeros((len(ns), w.shape[1]), np.float16)
+    flat_rows, flat_cols = np.divmod(pos, w.shape[1])
+    for i, n in enumerate(ns):
+        cols = flat_cols[flat_rows == n]
+        dense[i, cols] = w[n, cols]
+    counts = (dense != 0).sum(1)
+    sub["rowptr"] = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rr, cc = np.nonzero(dense)
+    sub["col"] = cc.astype(np.int32)
+    sub["val"] = dense[rr, cc].view(np.uint16)
+    r = oracle.linear(x[ms], sub)
+    got = y[np.ix_(ms, ns)]
+    assert rel_err(got, r) <= TOL, report(got, r)
+    assert np.isfinite(y).all()

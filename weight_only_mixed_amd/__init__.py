@@ -1,0 +1,199 @@
+"""Python binding of libqpack (include/qpack.h): MI355X weight-only mixed-bit linear layers.
+
+Argument marshalling only: every function here forwards to the C entry point of the same
+name, passing device pointers (torch tensors or raw integer addresses) and the current HIP
+stream.  All computation runs in the library's HIP kernels; there is no fallback.  Importing
+this package fails loudly if libqpack.so has not been built (``python -m
+weight_only_mixed_amd.build`` or ``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+_LIB_PATH = Path(__file__).resolve().parent / "libqpack.so"
+if not _LIB_PATH.exists():
+    raise ImportError(f"{_LIB_PATH} is missing: build the HIP library first "
+                      "(python -m weight_only_mixed_amd.build)")
+lib = ctypes.CDLL(str(_LIB_PATH))
+
+QP_OK, QP_ERR_INVALID_ARG, QP_ERR_UNSUPPORTED, QP_ERR_DEVICE, QP_ERR_WORKSPACE = range(5)
+QP_LAYOUT_CANONICAL, QP_LAYOUT_DEVICE = 0, 1
+QP_EPI_NONE, QP_EPI_SWIGLU, QP_EPI_ROWS_F32 = 0, 1, 2
+STATUS_NAMES = {0: "QP_OK", 1: "QP_ERR_INVALID_ARG", 2: "QP_ERR_UNSUPPORTED", 3: "QP_ERR_DEVICE",
+                4: "QP_ERR_WORKSPACE"}
+
+
+class qp_weight_desc(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("group_size", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("n", ctypes.c_int64), ("k", ctypes.c_int64)]
+
+
+class qp_weight(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p),
+                ("csr_rowptr", ctypes.c_void_p), ("csr_col", ctypes.c_void_p),
+                ("csr_val", ctypes.c_void_p), ("nnz", ctypes.c_int64)]
+
+
+_vp, _i64, _i32, _dbl, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_size_t
+_D = ctypes.POINTER(qp_weight_desc)
+_W = ctypes.POINTER(qp_weight)
+_SIGS = {
+    "qp_packed_bytes": (_sz, [_D]),
+    "qp_num_groups": (_sz, [_D]),
+    "qp_quant_bytes": (_dbl, [_dbl] * 5),
+    "qp_outlier_count": (_i64, [_i64, _i64, _dbl]),
+    "qpack_quantize_workspace_bytes": (_sz, [_D, _dbl]),
+    "qpack_quantize": (_i32, [_D, _vp, _i64, _dbl, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
+                              ctypes.POINTER(_i64), _vp, _sz, _vp]),
+    "qpack_pack": (_i32, [_D, _vp, _vp, _vp]),
+    "qpack_unpack": (_i32, [_D, _vp, _vp, _vp]),
+    "qlinear_gemv": (_i32, [_D, _W, _vp, _i64, _i64, _vp, _i64, _vp]),
+    "qlinear_gemm": (_i32, [_D, _W, _vp, _i64, _i64, _vp, _i64, _vp]),
+    "qlinear_grouped_gemm": (_i32, [_D, _W, _i32, _vp, _i64, _vp, _vp, _i64, _i32, _vp, _i64, _vp]),
+    "qmoe_dispatch": (_i32, [_vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "qmoe_combine": (_i32, [_vp, _i64, _vp, _vp, _i64, _i32, _i64, _vp, _i64, _vp]),
+    "qmoe_ffn_workspace_bytes": (_sz, [_i64, _i32, _i32, _i64, _i64]),
+    "qmoe_ffn": (_i32, [_D, _W, _D, _W, _i32, _vp, _i64, _i64, _vp, _vp, _i32, _vp, _i64, _vp, _sz,
+                        _vp]),
+    "qp_last_error": (ctypes.c_char_p, []),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+class QPError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} -> {STATUS_NAMES.get(status, status)}: {last_error()}")
+
+
+def last_error() -> str:
+    return lib.qp_last_error().decode()
+
+
+def _ptr(t):
+    """Device address of a torch tensor, an int address, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn, status, check):
+    if check and status != QP_OK:
+        raise QPError(fn, status)
+    return status
+
+
+def desc(bits: int, n: int, k: int, layout: int = QP_LAYOUT_DEVICE, group_size: int = 128):
+    return qp_weight_desc(bits, group_size, layout, 0, n, k)
+
+
+def weight(packed, scales, zeros, rowptr=None, col=None, val=None, nnz: int = 0):
+    return qp_weight(_ptr(packed), _ptr(scales), _ptr(zeros), _ptr(rowptr), _ptr(col), _ptr(val), nnz)
+
+
+# ---- host accounting ----------------------------------------------------------------
+
+def qp_packed_bytes(d) -> int:
+    return lib.qp_packed_bytes(ctypes.byref(d))
+
+
+def qp_num_groups(d) -> int:
+    return lib.qp_num_groups(ctypes.byref(d))
+
+
+def qp_quant_bytes(numel, bits, group, scale_bytes, zp_bits) -> float:
+    return lib.qp_quant_bytes(float(numel), float(bits), float(group), float(scale_bytes), float(zp_bits))
+
+
+def qp_outlier_count(n: int, k: int, frac: float) -> int:
+    return lib.qp_outlier_count(n, k, frac)
+
+
+def qpack_quantize_workspace_bytes(d, outlier_frac: float) -> int:
+    return lib.qpack_quantize_workspace_bytes(ctypes.byref(d), outlier_frac)
+
+
+def qmoe_ffn_workspace_bytes(tokens, topk, n_experts, d_model, d_ff) -> int:
+    return lib.qmoe_ffn_workspace_bytes(tokens, topk, n_experts, d_model, d_ff)
+
+
+# ---- device entry points -----------------------------------------------------------
+
+def qpack_quantize(d, w, ldw, outlier_frac, codes, scales, zeros, csr_rowptr=None, csr_col=None,
+                   csr_val=None, csr_cap=0, workspace=None, ws_bytes=0, stream=None, check=True):
+    """Returns (status, nnz)."""
+    nnz = _i64(0)
+    st = lib.qpack_quantize(ctypes.byref(d), _ptr(w), ldw, outlier_frac, _ptr(codes), _ptr(scales),
+                            _ptr(zeros), _ptr(csr_rowptr), _ptr(csr_col), _ptr(csr_val), csr_cap,
+                            ctypes.byref(nnz), _ptr(workspace), ws_bytes, _stream(stream))
+    _check("qpack_quantize", st, check)
+    return st, nnz.value
+
+
+def qpack_pack(d, codes, packed, stream=None, check=True):
+    return _check("qpack_pack", lib.qpack_pack(ctypes.byref(d), _ptr(codes), _ptr(packed), _stream(stream)), check)
+
+
+def qpack_unpack(d, packed, codes, stream=None, check=True):
+    return _check("qpack_unpack", lib.qpack_unpack(ctypes.byref(d), _ptr(packed), _ptr(codes), _stream(stream)),
+                  check)
+
+
+def qlinear_gemv(d, w, x, ldx, m, y, ldy, stream=None, check=True):
+    return _check("qlinear_gemv", lib.qlinear_gemv(ctypes.byref(d), ctypes.byref(w), _ptr(x), ldx, m, _ptr(y),
+                                                    ldy, _stream(stream)), check)
+
+
+def qlinear_gemm(d, w, x, ldx, m, y, ldy, stream=None, check=True):
+    return _check("qlinear_gemm", lib.qlinear_gemm(ctypes.byref(d), ctypes.byref(w), _ptr(x), ldx, m, _ptr(y),
+                                                    ldy, _stream(stream)), check)
+
+
+def qlinear_grouped_gemm(d, experts, x, ldx, row_src, expert_offsets, rows, epilogue, y, ldy, stream=None,
+                         check=True):
+    arr = (qp_weight * len(experts))(*experts)
+    return _check("qlinear_grouped_gemm",
+                  lib.qlinear_grouped_gemm(ctypes.byref(d), arr, len(experts), _ptr(x), ldx, _ptr(row_src),
+                                           _ptr(expert_offsets), rows, epilogue, _ptr(y), ldy, _stream(stream)),
+                  check)
+
+
+def qmoe_dispatch(topk_ids, topk_w, tokens, topk, n_experts, expert_offsets, row_src, row_weight, token_rows,
+                  stream=None, check=True):
+    return _check("qmoe_dispatch",
+                  lib.qmoe_dispatch(_ptr(topk_ids), _ptr(topk_w), tokens, topk, n_experts, _ptr(expert_offsets),
+                                    _ptr(row_src), _ptr(row_weight), _ptr(token_rows), _stream(stream)), check)
+
+
+def qmoe_combine(rows_f32, ld_rows, token_rows, row_weight, tokens, topk, n, out, ldo, stream=None, check=True):
+    return _check("qmoe_combine",
+                  lib.qmoe_combine(_ptr(rows_f32), ld_rows, _ptr(token_rows), _ptr(row_weight), tokens, topk, n,
+                                   _ptr(out), ldo, _stream(stream)), check)
+
+
+def qmoe_ffn(d_gu, gate_up, d_down, down, x, ldx, tokens, topk_ids, topk_w, topk, out, ldo, workspace, ws_bytes,
+             stream=None, check=True):
+    gu = (qp_weight * len(gate_up))(*gate_up)
+    dn = (qp_weight * len(down))(*down)
+    return _check("qmoe_ffn",
+                  lib.qmoe_ffn(ctypes.byref(d_gu), gu, ctypes.byref(d_down), dn, len(gate_up), _ptr(x), ldx, tokens,
+                               _ptr(topk_ids), _ptr(topk_w), topk, _ptr(out), ldo, _ptr(workspace), ws_bytes,
+                               _stream(stream)), check)
+
+
+EXPORTED = tuple(_SIGS)

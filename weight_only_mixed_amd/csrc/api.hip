@@ -1,0 +1,353 @@
+// C-ABI entry points of libqpack: argument validation on the host, then kernel launches.
+// Nothing is launched or written unless every argument passes validation.  See qpack.h for
+// the contract of each call and the passages of the pages it follows.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "qp_internal.h"
+
+namespace qp {
+
+static thread_local char g_err[512];
+
+qp_status fail(qp_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+static qp_status ok()
+{
+    g_err[0] = 0;
+    return QP_OK;
+}
+
+static qp_status device(hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return ok();
+    return fail(QP_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+static bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Shape/format checks shared by every call.  need_device: layout must be DEVICE.
+static qp_status check_desc(const qp_weight_desc *d, bool need_device)
+{
+    if (!d) return fail(QP_ERR_INVALID_ARG, "desc is NULL");
+    if (d->bits < 2 || d->bits > 6) return fail(QP_ERR_INVALID_ARG, "bits=%d not in 2..6", d->bits);
+    if (d->reserved != 0) return fail(QP_ERR_INVALID_ARG, "desc.reserved must be 0");
+    if (d->layout != QP_LAYOUT_CANONICAL && d->layout != QP_LAYOUT_DEVICE)
+        return fail(QP_ERR_INVALID_ARG, "layout=%d unknown", d->layout);
+    if (d->n <= 0 || d->k <= 0) return fail(QP_ERR_INVALID_ARG, "n=%lld k=%lld must be > 0", (long long)d->n, (long long)d->k);
+    if (d->group_size <= 0 || d->k % d->group_size != 0)
+        return fail(QP_ERR_INVALID_ARG, "k=%lld not a multiple of group_size=%d", (long long)d->k, d->group_size);
+    if (d->group_size != kGroup) return fail(QP_ERR_UNSUPPORTED, "group_size=%d (only 128 is built)", d->group_size);
+    if (d->n > (1LL << 31) - 1 || d->n * d->k > (1LL << 40))
+        return fail(QP_ERR_INVALID_ARG, "matrix too large");
+    if (d->layout == QP_LAYOUT_DEVICE && (d->n % kTileN != 0 || d->k % kTileK != 0))
+        return fail(QP_ERR_INVALID_ARG, "device layout needs n %% 16 == 0 and k %% 256 == 0 (n=%lld k=%lld)",
+                    (long long)d->n, (long long)d->k);
+    if (need_device && d->layout != QP_LAYOUT_DEVICE)
+        return fail(QP_ERR_UNSUPPORTED, "matmuls read the device layout (pack with QP_LAYOUT_DEVICE)");
+    return QP_OK;
+}
+
+static qp_status check_weight(const qp_weight_desc *d, const qp_weight *w, bool allow_csr)
+{
+    if (!w) return fail(QP_ERR_INVALID_ARG, "weight is NULL");
+    if (!w->packed || !aligned(w->packed, 16)) return fail(QP_ERR_INVALID_ARG, "packed NULL or not 16-byte aligned");
+    if (!w->scales || !aligned(w->scales, 4)) return fail(QP_ERR_INVALID_ARG, "scales NULL or not 4-byte aligned");
+    if (!w->zeros || !aligned(w->zeros, 2)) return fail(QP_ERR_INVALID_ARG, "zeros NULL or not 2-byte aligned");
+    if (w->nnz < 0) return fail(QP_ERR_INVALID_ARG, "nnz < 0");
+    if (w->csr_rowptr) {
+        if (!allow_csr && w->nnz > 0) return fail(QP_ERR_UNSUPPORTED, "outlier CSR not supported here");
+        if (w->nnz > 0 && (!w->csr_col || !w->csr_val)) return fail(QP_ERR_INVALID_ARG, "CSR col/val NULL with nnz > 0");
+    } else if (w->nnz > 0) {
+        return fail(QP_ERR_INVALID_ARG, "nnz > 0 but csr_rowptr is NULL");
+    }
+    (void)d;
+    return QP_OK;
+}
+
+static hipStream_t S(void *s) { return (hipStream_t)s; }
+
+}  // namespace qp
+
+using namespace qp;
+
+extern "C" {
+
+const char *qp_last_error(void) { return g_err; }
+
+size_t qp_packed_bytes(const qp_weight_desc *d)
+{
+    if (check_desc(d, false) != QP_OK) return 0;
+    return (size_t)(d->n * d->k * d->bits / 8);
+}
+
+size_t qp_num_groups(const qp_weight_desc *d)
+{
+    if (check_desc(d, false) != QP_OK) return 0;
+    return (size_t)(d->n * (d->k / d->group_size));
+}
+
+double qp_quant_bytes(double numel, double bits, double group, double scale_bytes, double zp_bits)
+{
+    return numel * bits / 8.0 + (numel / group) * (scale_bytes + zp_bits / 8.0);
+}
+
+int64_t qp_outlier_count(int64_t n, int64_t k, double frac)
+{
+    if (!(frac > 0.0) || n <= 0 || k <= 0) return 0;
+    return (int64_t)floor(frac * (double)(n * k));
+}
+
+size_t qpack_quantize_workspace_bytes(const qp_weight_desc *d, double outlier_frac)
+{
+    if (check_desc(d, false) != QP_OK) return 0;
+    return qp_outlier_count(d->n, d->k, outlier_frac) > 0 ? quant_ws_bytes(d->n) : 0;
+}
+
+qp_status qpack_quantize(const qp_weight_desc *d, const uint16_t *w, int64_t ldw, double outlier_frac,
+                         uint8_t *codes, uint16_t *scales, uint8_t *zeros, int32_t *csr_rowptr,
+                         int32_t *csr_col, uint16_t *csr_val, int64_t csr_cap, int64_t *nnz_out,
+                         void *workspace, size_t ws_bytes, void *stream)
+{
+    qp_status st = check_desc(d, false);
+    if (st != QP_OK) return st;
+    if (!w || !aligned(w, 4)) return fail(QP_ERR_INVALID_ARG, "w NULL or not 4-byte aligned");
+    if (ldw < d->k || ldw % 2 != 0) return fail(QP_ERR_INVALID_ARG, "ldw=%lld must be >= k and even", (long long)ldw);
+    if (!codes || !aligned(codes, 2)) return fail(QP_ERR_INVALID_ARG, "codes NULL or not 2-byte aligned");
+    if (!scales || !zeros) return fail(QP_ERR_INVALID_ARG, "scales/zeros NULL");
+    if (!nnz_out) return fail(QP_ERR_INVALID_ARG, "nnz_out NULL");
+    if (outlier_frac < 0.0 || outlier_frac > 1.0 || outlier_frac != outlier_frac)
+        return fail(QP_ERR_INVALID_ARG, "outlier_frac must be in [0, 1]");
+    const int64_t kout = qp_outlier_count(d->n, d->k, outlier_frac);
+    if (kout > 0) {
+        if (!csr_rowptr || !csr_col || !csr_val) return fail(QP_ERR_INVALID_ARG, "CSR outputs NULL with outliers requested");
+        if (d->n * d->k > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "outliers need n*k < 2^31");
+        if (csr_cap < kout) {
+            *nnz_out = kout;
+            return fail(QP_ERR_WORKSPACE, "csr_cap=%lld < %lld outliers", (long long)csr_cap, (long long)kout);
+        }
+        const size_t need = quant_ws_bytes(d->n);
+        if (!workspace || ws_bytes < need || !aligned(workspace, 16))
+            return fail(QP_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, ws_bytes);
+    }
+    *nnz_out = kout;
+    QuantWs ws{};
+    if (kout > 0) ws = quant_ws_carve(workspace, d->n);
+    return device(launch_quantize(d->bits, w, ldw, d->n, d->k, kout, codes, scales, zeros, csr_rowptr,
+                                  csr_col, csr_val, ws, S(stream)),
+                  "qpack_quantize");
+}
+
+qp_status qpack_pack(const qp_weight_desc *d, const uint8_t *codes, void *packed, void *stream)
+{
+    qp_status st = check_desc(d, false);
+    if (st != QP_OK) return st;
+    if (!codes || !aligned(codes, 8)) return fail(QP_ERR_INVALID_ARG, "codes NULL or not 8-byte aligned");
+    if (!packed || !aligned(packed, 16)) return fail(QP_ERR_INVALID_ARG, "packed NULL or not 16-byte aligned");
+    return device(launch_pack(d->bits, d->layout, codes, d->n, d->k, (uint8_t *)packed, S(stream)), "qpack_pack");
+}
+
+qp_status qpack_unpack(const qp_weight_desc *d, const void *packed, uint8_t *codes, void *stream)
+{
+    qp_status st = check_desc(d, false);
+    if (st != QP_OK) return st;
+    if (!codes || !aligned(codes, 8)) return fail(QP_ERR_INVALID_ARG, "codes NULL or not 8-byte aligned");
+    if (!packed || !aligned(packed, 16)) return fail(QP_ERR_INVALID_ARG, "packed NULL or not 16-byte aligned");
+    return device(launch_unpack(d->bits, d->layout, (const uint8_t *)packed, d->n, d->k, codes, S(stream)),
+                  "qpack_unpack");
+}
+
+static qp_status check_xy(const qp_weight_desc *d, const uint16_t *x, int64_t ldx, int64_t m, const void *y,
+                          int64_t ldy, int64_t ncols, size_t ysize)
+{
+    if (!x || !aligned(x, 16)) return fail(QP_ERR_INVALID_ARG, "x NULL or not 16-byte aligned");
+    if (ldx < d->k || ldx % 8 != 0) return fail(QP_ERR_INVALID_ARG, "ldx=%lld must be >= k and a multiple of 8", (long long)ldx);
+    if (!y || !aligned(y, 2 * ysize)) return fail(QP_ERR_INVALID_ARG, "y NULL or misaligned");
+    if (ldy < ncols || ldy % 4 != 0) return fail(QP_ERR_INVALID_ARG, "ldy=%lld must be >= %lld and a multiple of 4", (long long)ldy, (long long)ncols);
+    if (m < 1) return fail(QP_ERR_INVALID_ARG, "m=%lld must be >= 1", (long long)m);
+    return QP_OK;
+}
+
+qp_status qlinear_gemv(const qp_weight_desc *d, const qp_weight *w, const uint16_t *x, int64_t ldx, int64_t m,
+                       uint16_t *y, int64_t ldy, void *stream)
+{
+    qp_status st = check_desc(d, true);
+    if (st != QP_OK) return st;
+    if ((st = check_weight(d, w, true)) != QP_OK) return st;
+    if ((st = check_xy(d, x, ldx, m, y, ldy, d->n, 4)) != QP_OK) return st;
+    if (m > 16) return fail(QP_ERR_UNSUPPORTED, "gemv handles m <= 16 (m=%lld); use qlinear_gemm", (long long)m);
+    SmallArgs a{};
+    a.ex[0] = {(const uint8_t *)w->packed, w->scales, w->zeros};
+    if (w->nnz > 0) {
+        a.rowptr = w->csr_rowptr;
+        a.col = w->csr_col;
+        a.val = w->csr_val;
+    }
+    a.x = x;
+    a.ldx = ldx;
+    a.m = m;
+    a.n = d->n;
+    a.k = d->k;
+    a.y = y;
+    a.ldy = ldy;
+    return device(launch_gemv(d->bits, a, S(stream)), "qlinear_gemv");
+}
+
+qp_status qlinear_gemm(const qp_weight_desc *d, const qp_weight *w, const uint16_t *x, int64_t ldx, int64_t m,
+                       uint16_t *y, int64_t ldy, void *stream)
+{
+    qp_status st = check_desc(d, true);
+    if (st != QP_OK) return st;
+    if ((st = check_weight(d, w, true)) != QP_OK) return st;
+    if ((st = check_xy(d, x, ldx, m, y, ldy, d->n, 4)) != QP_OK) return st;
+    if (m > (1LL << 24)) return fail(QP_ERR_INVALID_ARG, "m too large");
+    GemmArgs a{};
+    a.packed = (const uint8_t *)w->packed;
+    a.scales = w->scales;
+    a.zeros = w->zeros;
+    if (w->nnz > 0) {
+        a.rowptr = w->csr_rowptr;
+        a.col = w->csr_col;
+        a.val = w->csr_val;
+    }
+    a.x = x;
+    a.ldx = ldx;
+    a.m = m;
+    a.n = d->n;
+    a.k = d->k;
+    a.y = y;
+    a.ldy = ldy;
+    return device(launch_gemm(d->bits, a, S(stream)), "qlinear_gemm");
+}
+
+qp_status qlinear_grouped_gemm(const qp_weight_desc *d, const qp_weight *experts, int32_t n_experts,
+                               const uint16_t *x, int64_t ldx, const int32_t *row_src,
+                               const int32_t *expert_offsets, int64_t rows, int32_t epilogue, void *y,
+                               int64_t ldy, void *stream)
+{
+    qp_status st = check_desc(d, true);
+    if (st != QP_OK) return st;
+    if (!experts) return fail(QP_ERR_INVALID_ARG, "experts NULL");
+    if (n_experts < 1 || n_experts > kMaxExperts) return fail(QP_ERR_INVALID_ARG, "n_experts=%d not in 1..64", n_experts);
+    for (int e = 0; e < n_experts; ++e)
+        if ((st = check_weight(d, &experts[e], false)) != QP_OK) return st;
+    if (epilogue != QP_EPI_NONE && epilogue != QP_EPI_SWIGLU && epilogue != QP_EPI_ROWS_F32)
+        return fail(QP_ERR_INVALID_ARG, "epilogue=%d unknown", epilogue);
+    if (epilogue == QP_EPI_SWIGLU && d->n % 32 != 0) return fail(QP_ERR_INVALID_ARG, "SwiGLU needs n %% 32 == 0");
+    const int64_t ncols = epilogue == QP_EPI_SWIGLU ? d->n / 2 : d->n;
+    if ((st = check_xy(d, x, ldx, rows < 1 ? 1 : rows, y, ldy, ncols, epilogue == QP_EPI_ROWS_F32 ? 8 : 4)) != QP_OK)
+        return st;
+    if (!expert_offsets) return fail(QP_ERR_INVALID_ARG, "expert_offsets NULL");
+    if (rows < 0) return fail(QP_ERR_INVALID_ARG, "rows < 0");
+    SmallArgs a{};
+    for (int e = 0; e < n_experts; ++e)
+        a.ex[e] = {(const uint8_t *)experts[e].packed, experts[e].scales, experts[e].zeros};
+    a.x = x;
+    a.ldx = ldx;
+    a.row_src = row_src;
+    a.offsets = expert_offsets;
+    a.m = rows;
+    a.n = d->n;
+    a.k = d->k;
+    a.y = y;
+    a.ldy = ldy;
+    return device(launch_grouped(d->bits, epilogue, n_experts, a, S(stream)), "qlinear_grouped_gemm");
+}
+
+qp_status qmoe_dispatch(const int32_t *ids, const float *w, int64_t tokens, int32_t topk, int32_t n_experts,
+                        int32_t *offsets, int32_t *row_src, float *row_weight, int32_t *token_rows, void *stream)
+{
+    if (!ids || !w || !offsets || !row_src || !row_weight || !token_rows)
+        return fail(QP_ERR_INVALID_ARG, "NULL pointer");
+    if (tokens < 1 || topk < 1 || tokens * topk > 65536)
+        return fail(QP_ERR_INVALID_ARG, "tokens*topk must be in 1..65536");
+    if (n_experts < 1 || n_experts > kMaxExperts) return fail(QP_ERR_INVALID_ARG, "n_experts not in 1..64");
+    return device(launch_moe_dispatch(ids, w, tokens, topk, n_experts, offsets, row_src, row_weight, token_rows,
+                                      S(stream)),
+                  "qmoe_dispatch");
+}
+
+qp_status qmoe_combine(const float *rows_f32, int64_t ld_rows, const int32_t *token_rows, const float *row_weight,
+                       int64_t tokens, int32_t topk, int64_t n, uint16_t *out, int64_t ldo, void *stream)
+{
+    if (!rows_f32 || !token_rows || !row_weight || !out) return fail(QP_ERR_INVALID_ARG, "NULL pointer");
+    if (tokens < 1 || topk < 1 || n < 1 || ld_rows < n || ldo < n)
+        return fail(QP_ERR_INVALID_ARG, "bad sizes");
+    if (tokens > 65535) return fail(QP_ERR_INVALID_ARG, "tokens > 65535");
+    return device(launch_moe_combine(rows_f32, ld_rows, token_rows, row_weight, tokens, topk, n, out, ldo,
+                                     S(stream)),
+                  "qmoe_combine");
+}
+
+static size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+size_t qmoe_ffn_workspace_bytes(int64_t tokens, int32_t topk, int32_t n_experts, int64_t d_model, int64_t d_ff)
+{
+    if (tokens < 1 || topk < 1 || n_experts < 1 || d_model < 1 || d_ff < 1) return 0;
+    const size_t R = (size_t)(tokens * topk);
+    return al256((n_experts + 1) * 4) + 3 * al256(R * 4) + al256(R * (size_t)d_ff * 2) +
+           al256(R * (size_t)d_model * 4);
+}
+
+qp_status qmoe_ffn(const qp_weight_desc *dgu, const qp_weight *gate_up, const qp_weight_desc *dd,
+                   const qp_weight *down, int32_t n_experts, const uint16_t *x, int64_t ldx, int64_t tokens,
+                   const int32_t *topk_ids, const float *topk_w, int32_t topk, uint16_t *out, int64_t ldo,
+                   void *workspace, size_t ws_bytes, void *stream)
+{
+    qp_status st;
+    if ((st = check_desc(dgu, true)) != QP_OK) return st;
+    if ((st = check_desc(dd, true)) != QP_OK) return st;
+    if (dgu->bits != dd->bits) return fail(QP_ERR_UNSUPPORTED, "gate/up and down must share the bit width");
+    const int64_t d_model = dgu->k, d_ff = dgu->n / 2;
+    if (dgu->n % 32 != 0 || dd->n != d_model || dd->k != d_ff)
+        return fail(QP_ERR_INVALID_ARG, "shapes: gate_up must be [2*d_ff, d_model], down [d_model, d_ff]");
+    if (d_ff % 8 != 0) return fail(QP_ERR_INVALID_ARG, "d_ff must be a multiple of 8");
+    if (!out || !aligned(out, 2) || ldo < d_model) return fail(QP_ERR_INVALID_ARG, "out NULL/misaligned or ldo < d_model");
+    const size_t need = qmoe_ffn_workspace_bytes(tokens, topk, n_experts, d_model, d_ff);
+    if (!workspace || ws_bytes < need || !aligned(workspace, 256))
+        return fail(QP_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned)", need);
+    if (tokens < 1 || topk < 1 || tokens * topk > 65536) return fail(QP_ERR_INVALID_ARG, "tokens*topk must be in 1..65536");
+    if (n_experts < 1 || n_experts > kMaxExperts) return fail(QP_ERR_INVALID_ARG, "n_experts not in 1..64");
+    for (int e = 0; e < n_experts; ++e) {
+        if ((st = check_weight(dgu, &gate_up[e], false)) != QP_OK) return st;
+        if ((st = check_weight(dd, &down[e], false)) != QP_OK) return st;
+    }
+    if (!x || !aligned(x, 16) || ldx < d_model || ldx % 8 != 0) return fail(QP_ERR_INVALID_ARG, "x NULL/misaligned or bad ldx");
+    if (!topk_ids || !topk_w) return fail(QP_ERR_INVALID_ARG, "routing NULL");
+
+    const size_t R = (size_t)(tokens * topk);
+    uint8_t *p = (uint8_t *)workspace;
+    int32_t *offsets = (int32_t *)p;
+    p += al256((n_experts + 1) * 4);
+    int32_t *row_src = (int32_t *)p;
+    p += al256(R * 4);
+    float *row_weight = (float *)p;
+    p += al256(R * 4);
+    int32_t *token_rows = (int32_t *)p;
+    p += al256(R * 4);
+    uint16_t *act = (uint16_t *)p;
+    p += al256(R * (size_t)d_ff * 2);
+    float *rows = (float *)p;
+
+    if ((st = qmoe_dispatch(topk_ids, topk_w, tokens, topk, n_experts, offsets, row_src, row_weight, token_rows,
+                            stream)) != QP_OK)
+        return st;
+    if ((st = qlinear_grouped_gemm(dgu, gate_up, n_experts, x, ldx, row_src, offsets, (int64_t)R, QP_EPI_SWIGLU,
+                                   act, d_ff, stream)) != QP_OK)
+        return st;
+    if ((st = qlinear_grouped_gemm(dd, down, n_experts, act, d_ff, nullptr, offsets, (int64_t)R, QP_EPI_ROWS_F32,
+                                   rows, d_model, stream)) != QP_OK)
+        return st;
+    return qmoe_combine(rows, d_model, token_rows, row_weight, tokens, topk, d_model, out, ldo, stream);
+}
+
+}  // extern "C"

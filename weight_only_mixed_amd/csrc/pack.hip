@@ -1,0 +1,123 @@
+// Packing of unpacked codes into the page units and the device tile order.
+//
+// Units (mixed-bit page, s3.1): the smallest n with n*b divisible by 8 -- 4 values in 1
+// byte (2-bit), 8 in 3 bytes (3-bit), 2 in 1 byte (4-bit), 8 in 5 bytes (5-bit), 4 in 3
+// bytes (6-bit).  Value i of a unit occupies bits [b*i, b*i+b) of the little-endian integer
+// formed by the unit's bytes (the shift sequences of s3.2).  Every 8 consecutive k of a row
+// therefore form b whole bytes ("a block") whose little-endian value is sum_i q_i << (b*i),
+// and both layouts move whole blocks: the canonical layout stores them in row order, the
+// device layout stores them in the tile order documented in qpack.h (a one-time repack,
+// single-GPU 70B page, s3).  One thread handles one block.
+#include "qp_internal.h"
+
+namespace qp {
+
+// Byte offset of chunk byte c (0 <= c < 8*b) of lane `lane` inside a tile.
+template <int B>
+__device__ __forceinline__ int64_t dev_chunk_offset(int c, int lane)
+{
+    constexpr int F = 16 * (B / 2);
+    return c < F ? (int64_t)(1024 * (c / 16) + 16 * lane + c % 16)
+                 : (int64_t)(64 * F + 8 * lane + (c - F));
+}
+
+// Device offset of byte `i` of the block of row n starting at k0.
+template <int B>
+__device__ __forceinline__ int64_t dev_offset(int64_t n, int64_t k0, int i, int64_t k)
+{
+    const int64_t rb = n / kTileN, kt = k0 / kTileK;
+    const int r = (int)(n % kTileN), kk = (int)(k0 % kTileK);
+    const int gi = kk / 128, kq = kk % 128;
+    const int j = 4 * gi + kq / 32, t = (kq % 32) / 8;
+    const int lane = 16 * t + r;
+    const int64_t tile = rb * (k / kTileK) + kt;
+    return tile * 512 * B + dev_chunk_offset<B>(B * j + i, lane);
+}
+
+template <int B, int LAYOUT>
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t *codes, int64_t n, int64_t k,
+                                                   uint8_t *out)
+{
+    const int64_t bpr = k / 8;
+    const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (idx >= n * bpr) return;
+    const int64_t row = idx / bpr, kb = idx % bpr;
+    const uint64_t c8 = *(const uint64_t *)(codes + row * k + kb * 8);
+    uint64_t v = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v |= ((c8 >> (8 * i)) & ((1u << B) - 1)) << (B * i);
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+        const int64_t off = LAYOUT == QP_LAYOUT_CANONICAL ? row * (k * B / 8) + kb * B + i
+                                                          : dev_offset<B>(row, kb * 8, i, k);
+        out[off] = (uint8_t)(v >> (8 * i));
+    }
+}
+
+template <int B, int LAYOUT>
+__global__ __launch_bounds__(256) void unpack_kernel(const uint8_t *in, int64_t n, int64_t k,
+                                                     uint8_t *codes)
+{
+    const int64_t bpr = k / 8;
+    const int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (idx >= n * bpr) return;
+    const int64_t row = idx / bpr, kb = idx % bpr;
+    uint64_t v = 0;
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+        const int64_t off = LAYOUT == QP_LAYOUT_CANONICAL ? row * (k * B / 8) + kb * B + i
+                                                          : dev_offset<B>(row, kb * 8, i, k);
+        v |= (uint64_t)in[off] << (8 * i);
+    }
+    uint64_t c8 = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c8 |= ((v >> (B * i)) & ((1u << B) - 1)) << (8 * i);
+    *(uint64_t *)(codes + row * k + kb * 8) = c8;
+}
+
+template <int B>
+static hipError_t pack_bits(int layout, bool unpack, const uint8_t *src, int64_t n, int64_t k,
+                            uint8_t *dst, hipStream_t st)
+{
+    const int64_t blocks = n * (k / 8);
+    const dim3 grid((unsigned)((blocks + 255) / 256)), block(256);
+    if (!unpack) {
+        if (layout == QP_LAYOUT_CANONICAL)
+            hipLaunchKernelGGL((pack_kernel<B, QP_LAYOUT_CANONICAL>), grid, block, 0, st, src, n, k, dst);
+        else
+            hipLaunchKernelGGL((pack_kernel<B, QP_LAYOUT_DEVICE>), grid, block, 0, st, src, n, k, dst);
+    } else {
+        if (layout == QP_LAYOUT_CANONICAL)
+            hipLaunchKernelGGL((unpack_kernel<B, QP_LAYOUT_CANONICAL>), grid, block, 0, st, src, n, k, dst);
+        else
+            hipLaunchKernelGGL((unpack_kernel<B, QP_LAYOUT_DEVICE>), grid, block, 0, st, src, n, k, dst);
+    }
+    return hipGetLastError();
+}
+
+static hipError_t dispatch(int bits, int layout, bool unpack, const uint8_t *src, int64_t n,
+                           int64_t k, uint8_t *dst, hipStream_t st)
+{
+    switch (bits) {
+    case 2: return pack_bits<2>(layout, unpack, src, n, k, dst, st);
+    case 3: return pack_bits<3>(layout, unpack, src, n, k, dst, st);
+    case 4: return pack_bits<4>(layout, unpack, src, n, k, dst, st);
+    case 5: return pack_bits<5>(layout, unpack, src, n, k, dst, st);
+    case 6: return pack_bits<6>(layout, unpack, src, n, k, dst, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_pack(int bits, int layout, const uint8_t *codes, int64_t n, int64_t k,
+                       uint8_t *out, hipStream_t st)
+{
+    return dispatch(bits, layout, false, codes, n, k, out, st);
+}
+
+hipError_t launch_unpack(int bits, int layout, const uint8_t *in, int64_t n, int64_t k,
+                         uint8_t *codes, hipStream_t st)
+{
+    return dispatch(bits, layout, true, in, n, k, codes, st);
+}
+
+}  // namespace qp

@@ -1,0 +1,91 @@
+// Internal declarations shared by the HIP translation units of libqpack.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qpack.h"
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+namespace qp {
+
+constexpr int kGroup = 128;      // weights per (scale, zero point)
+constexpr int kTileN = 16;       // rows per device-layout tile
+constexpr int kTileK = 256;      // k per device-layout tile (two groups)
+constexpr int kMaxExperts = 64;  // experts per grouped launch (kernel-argument table)
+
+// ---- host-side helpers (api.hip) ---------------------------------------------------
+qp_status fail(qp_status st, const char *fmt, ...);
+qp_status check_launch(const char *what);
+
+// ---- launchers -----------------------------------------------------------------------
+struct QuantWs {  // carve-up of the quantize workspace
+    uint32_t *hist;      // [32768] magnitude histogram
+    uint32_t *ctl;       // [4]: threshold bits, need_eq lo/hi, spare
+    int32_t *gt_cnt;     // [n]
+    int32_t *eq_cnt;     // [n]
+    int32_t *eq_base;    // [n]
+};
+size_t quant_ws_bytes(int64_t n);
+QuantWs quant_ws_carve(void *ws, int64_t n);
+hipError_t launch_quantize(int bits, const uint16_t *w, int64_t ldw, int64_t n, int64_t k,
+                           int64_t kout, uint8_t *codes, uint16_t *scales, uint8_t *zeros,
+                           int32_t *rowptr, int32_t *col, uint16_t *val, const QuantWs &ws,
+                           hipStream_t st);
+
+hipError_t launch_pack(int bits, int layout, const uint8_t *codes, int64_t n, int64_t k,
+                       uint8_t *out, hipStream_t st);
+hipError_t launch_unpack(int bits, int layout, const uint8_t *in, int64_t n, int64_t k,
+                         uint8_t *codes, hipStream_t st);
+
+struct ExpertPtrs {
+    const uint8_t *packed;
+    const uint16_t *scales;
+    const uint8_t *zeros;
+};
+struct SmallArgs {
+    ExpertPtrs ex[kMaxExperts];
+    const int32_t *rowptr;   // CSR of expert 0 (plain GEMV only), or null
+    const int32_t *col;
+    const uint16_t *val;
+    const uint16_t *x;
+    int64_t ldx;
+    const int32_t *row_src;  // null: row r reads x row r
+    const int32_t *offsets;  // null: rows [0, m)
+    int64_t m;
+    int64_t n, k;
+    void *y;
+    int64_t ldy;
+};
+hipError_t launch_gemv(int bits, const SmallArgs &a, hipStream_t st);
+hipError_t launch_grouped(int bits, int epilogue, int n_experts, const SmallArgs &a,
+                          hipStream_t st);
+
+struct GemmArgs {
+    const uint8_t *packed;
+    const uint16_t *scales;
+    const uint8_t *zeros;
+    const int32_t *rowptr;
+    const int32_t *col;
+    const uint16_t *val;
+    const uint16_t *x;
+    int64_t ldx;
+    int64_t m, n, k;
+    uint16_t *y;
+    int64_t ldy;
+};
+hipError_t launch_gemm(int bits, const GemmArgs &a, hipStream_t st);
+
+hipError_t launch_moe_dispatch(const int32_t *ids, const float *w, int64_t tokens, int topk,
+                               int n_experts, int32_t *offsets, int32_t *row_src,
+                               float *row_weight, int32_t *token_rows, hipStream_t st);
+hipError_t launch_moe_combine(const float *rows, int64_t ld_rows, const int32_t *token_rows,
+                              const float *row_weight, int64_t tokens, int topk, int64_t n,
+                              uint16_t *out, int64_t ldo, hipStream_t st);
+
+}  // namespace qp

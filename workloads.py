@@ -137,3 +137,36 @@ def stack_bits(layer: int, name: str) -> int:
 
 def stack_matrix_seed(layer: int, name: str) -> int:
     return seed_for(3, layer, LLAMA_MATRICES.index(name))
+
+
+def layer_weights(bits_config: int = 1) -> np.ndarray:
+    """The single 4096x4096 layer of configurations 1 and 2."""
+    return weights_fp16(LAYER_N, LAYER_K, seed_for(bits_config))
+
+
+def prefill_weights() -> tuple[np.ndarray, np.ndarray]:
+    """Configuration 4: W[28672, 8192] ~ N(0, 0.02) with 0.1% planted outliers.
+    Returns (W, sorted flat positions of the planted outliers)."""
+    w = weights_fp16(PREFILL_N, PREFILL_K, seed_for(4))
+    pos = plant_outliers(w, PREFILL_OUTLIER_FRAC, seed_for(4))
+    return w, pos
+
+
+def prefill_activations() -> np.ndarray:
+    return activations_fp16(PREFILL_M, PREFILL_K, seed_for(4))
+
+
+def moe_expert(e: int, d_model: int = MOE_DMODEL, d_ff: int = MOE_DFF, config: int = 5):
+    """(gate [d_ff, d_model], up [d_ff, d_model], down [d_model, d_ff]) of expert e."""
+    g = weights_fp16(d_ff, d_model, seed_for(config, e, LLAMA_MATRICES.index("gate")))
+    u = weights_fp16(d_ff, d_model, seed_for(config, e, LLAMA_MATRICES.index("up")))
+    d = weights_fp16(d_model, d_ff, seed_for(config, e, LLAMA_MATRICES.index("down")))
+    return g, u, d
+
+
+def moe_inputs(tokens: int = MOE_TOKENS, d_model: int = MOE_DMODEL, experts: int = MOE_EXPERTS,
+               topk: int = MOE_TOPK, config: int = 5):
+    """(x [tokens, d_model] fp16, ids int32 [tokens, topk], weights float32 [tokens, topk])."""
+    x = activations_fp16(tokens, d_model, seed_for(config))
+    ids, wts = zipf_routing(tokens, experts, topk, MOE_ZIPF, seed_for(config) + 900_000)
+    return x, ids, wts
