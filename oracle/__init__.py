@@ -72,6 +72,8 @@ def lib():
         L.or_linear.argtypes = [i64, i64, i64, i32, vp, i64, vp, vp, vp, vp, vp, vp, vp, i64]
         L.or_moe_ffn.restype = None
         L.or_moe_ffn.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp] + [vp] * 9 + [vp]
+        L.or_swiglu_act.restype = None
+        L.or_swiglu_act.argtypes = [i64, i64, i32, vp] + [vp] * 6 + [vp]
         L.or_quant_bytes.restype = dbl
         L.or_quant_bytes.argtypes = [dbl] * 5
         L.or_kv_bytes.restype = dbl
@@ -224,6 +226,17 @@ def moe_ffn(x_fp16, ids, wts, gate: list, up: list, down: list, g: int = GROUP):
     r = np.zeros((T, D), np.float64)
     lib().or_moe_ffn(T, D, F, topk, g, _p(ids), _p(wts), _p(x), *[_p(a) for a in arrs], _p(r))
     return r
+
+
+def swiglu_act(x_row_fp16, gate: dict, up: dict, g: int = GROUP):
+    """fp64 silu(What_gate x) * (What_up x) for one token row, before fp16 rounding."""
+    xt = _bits16(x_row_fp16).ravel()
+    F, D = gate["codes"].shape
+    v = np.zeros(F, np.float64)
+    lib().or_swiglu_act(D, F, g, _p(xt), _p(_c(gate["codes"], np.uint8)), _p(_c(gate["scales"], np.uint16)),
+                        _p(_c(gate["zeros"], np.uint8)), _p(_c(up["codes"], np.uint8)),
+                        _p(_c(up["scales"], np.uint16)), _p(_c(up["zeros"], np.uint8)), _p(v))
+    return v
 
 
 # ---- byte accounting ----------------------------------------------------------------

@@ -374,11 +374,33 @@ void or_linear(int64_t M, int64_t N, int64_t K, int g,
 static double silu(double v) { return v / (1.0 + exp(-v)); }
 
 /*
+ * SwiGLU intermediate of one token through one expert, before its fp16 rounding:
+ * v[f] = silu(g_f) * u_f, g = What_gate x, u = What_up x, all in fp64 ([MoE] s4.2 expert
+ * FFN gate/up; silu(v) = v / (1 + e^-v)).  Gate/up codes [F][D], scales/zeros [F][D/g].
+ */
+void or_swiglu_act(int64_t D, int64_t F, int g, const uint16_t *xt,
+                   const uint8_t *gc, const uint16_t *gs, const uint8_t *gz,
+                   const uint8_t *uc, const uint16_t *us, const uint8_t *uz, double *v)
+{
+    (void)hv(0);
+#pragma omp parallel for schedule(static)
+    for (int64_t f = 0; f < F; ++f) {
+        double gv = 0.0, uv = 0.0;
+        for (int64_t d = 0; d < D; ++d) {
+            double xv = hv(xt[d]);
+            gv += xv * dequant(gc, gs, gz, D, g, f, d);
+            uv += xv * dequant(uc, us, uz, D, g, f, d);
+        }
+        v[f] = silu(gv) * uv;
+    }
+}
+
+/*
  * Per token t: out[t] = sum_j p[t][j] * FFN_{e}(x[t]), e = ids[t][j], with
  * FFN_e(x) = What_down_e * fp16( silu(What_gate_e x) * (What_up_e x) ).
  * Gate/up: codes [E][F][D], scales/zeros [E][F][D/g]; down: codes [E][D][F],
  * scales/zeros [E][D][F/g].  Accumulation in fp64; the SwiGLU product is rounded to
- * fp16 once (the intermediate activation is stored in fp16).  r is [T][D] fp64.
+ * fp16 once (the down projection's input is an fp16 activation).  r is [T][D] fp64.
  */
 void or_moe_ffn(int64_t T, int64_t D, int64_t F, int topk, int g,
                 const int32_t *ids, const float *wts, const uint16_t *x,
@@ -388,27 +410,19 @@ void or_moe_ffn(int64_t T, int64_t D, int64_t F, int topk, int g,
                 double *r)
 {
     (void)hv(0);
+    double *v = (double *)malloc((size_t)F * sizeof(double));
+    double *a = (double *)malloc((size_t)F * sizeof(double));
     for (int64_t t = 0; t < T; ++t) {
         for (int64_t d = 0; d < D; ++d) r[t * D + d] = 0.0;
-        double *a = (double *)malloc((size_t)F * sizeof(double));
         for (int j = 0; j < topk; ++j) {
             int64_t e = ids[t * topk + j];
             double p = (double)wts[t * topk + j];
-            const uint8_t *gce = gc + e * F * D, *uce = uc + e * F * D, *dce = dc + e * D * F;
-            const uint16_t *gse = gs + e * F * (D / g), *use = us + e * F * (D / g);
-            const uint8_t *gze = gz + e * F * (D / g), *uze = uz + e * F * (D / g);
-            const uint16_t *dse = ds + e * D * (F / g);
-            const uint8_t *dze = dz + e * D * (F / g);
-#pragma omp parallel for schedule(static)
-            for (int64_t f = 0; f < F; ++f) {
-                double gv = 0.0, uv = 0.0;
-                for (int64_t d = 0; d < D; ++d) {
-                    double xv = hv(x[t * D + d]);
-                    gv += xv * dequant(gce, gse, gze, D, g, f, d);
-                    uv += xv * dequant(uce, use, uze, D, g, f, d);
-                }
-                a[f] = hv(or_round_half(silu(gv) * uv));
-            }
+            const int64_t gF = F * (D / g), gD = D * (F / g);
+            or_swiglu_act(D, F, g, x + t * D, gc + e * F * D, gs + e * gF, gz + e * gF,
+                          uc + e * F * D, us + e * gF, uz + e * gF, v);
+            for (int64_t f = 0; f < F; ++f) a[f] = hv(or_round_half(v[f]));
+            const uint8_t *dce = dc + e * D * F, *dze = dz + e * gD;
+            const uint16_t *dse = ds + e * gD;
 #pragma omp parallel for schedule(static)
             for (int64_t d = 0; d < D; ++d) {
                 double o = 0.0;
@@ -416,8 +430,9 @@ void or_moe_ffn(int64_t T, int64_t D, int64_t F, int topk, int g,
                 r[t * D + d] += p * o;
             }
         }
-        free(a);
     }
+    free(v);
+    free(a);
 }
 
 /* ------------------------------------------------------------------------------ */

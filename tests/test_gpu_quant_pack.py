@@ -98,6 +98,7 @@ def test_quantize_layer_4096_full(bits):
     assert np.array_equal(g.packed.cpu().numpy(), oracle.pack_device(ref["codes"], bits))
 
 
+@pytest.mark.timeout(600)
 def test_quantize_prefill_full_with_outliers():
     """28672 x 8192 with 234,881 planted outliers: the held-out set is exactly the planted
     set, and the dense part is bit-exact with the oracle's group quantizer."""

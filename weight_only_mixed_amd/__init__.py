@@ -11,6 +11,12 @@ from __future__ import annotations
 import ctypes
 from pathlib import Path
 
+# torch ships its own HIP runtime with the same SONAME (libamdhip64.so.7) as the system
+# one libqpack.so is linked against.  Loading torch first makes libqpack bind to the
+# runtime torch already initialised, so both share one runtime (and one view of devices,
+# streams and memory) in the process.
+import torch  # noqa: F401  (import order matters, see above)
+
 _LIB_PATH = Path(__file__).resolve().parent / "libqpack.so"
 if not _LIB_PATH.exists():
     raise ImportError(f"{_LIB_PATH} is missing: build the HIP library first "

@@ -79,35 +79,80 @@ __device__ __forceinline__ void mma_tile(const h8 *A, const h8 *X, const uint32_
 }
 
 // ---- decode GEMV: one workgroup per 16-row block, NW waves split the k-tiles ----------
+//
+// Decode is latency-bound at these sizes (a 4096 x 4096 layer is a few MB), so each wave
+// issues every global load it needs -- TPW weight tiles, their scales and zero points and
+// the activation fragments -- before its first unpack, and the next chunk of TPW tiles is in
+// flight while the current one is multiplied.  The NW partial sums of a row block are
+// reduced through LDS in a fixed order.
 
-template <int B, int NW>
+template <int B, int TPW>
+struct Chunk {
+    TileIn<B> tile[TPW];
+};
+
+template <int B, int TPW>
+__device__ __forceinline__ void load_w_chunk(const ExpertPtrs &W, int64_t rb, int64_t kt0, int64_t KT,
+                                             int64_t G, int lane, Chunk<B, TPW> &c)
+{
+#pragma unroll
+    for (int u = 0; u < TPW; ++u)
+        if (kt0 + u < KT) load_tile<B>(W, rb, kt0 + u, KT, G, lane, c.tile[u]);
+}
+
+template <int TPW>
+__device__ __forceinline__ void load_x_chunk(const uint16_t *xrow, bool act, int64_t kt0, int64_t KT, int t,
+                                             h8 (&X)[TPW][8])
+{
+#pragma unroll
+    for (int u = 0; u < TPW; ++u)
+        if (kt0 + u < KT) load_x(xrow, act, kt0 + u, t, X[u]);
+}
+
+template <int B, int TPW>
+__device__ __forceinline__ void compute_chunk(const Chunk<B, TPW> &c, const h8 (&X)[TPW][8], int64_t kt0,
+                                              int64_t KT, f4 &tot)
+{
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        if (kt0 + u < KT) {
+            GroupConst<B> g0, g1;
+            g0.set(c.tile[u].zz & 0xFF);
+            g1.set((c.tile[u].zz >> 8) & 0xFF);
+            h8 A[8];
+            unpack_chunk<B>(c.tile[u].d, g0, g1, A);
+            mma_tile(A, X[u], c.tile[u].sc, tot);
+        }
+    }
+}
+
+template <int B, int NW, int TPW>
 __global__ __launch_bounds__(NW * 64) void gemv_kernel(SmallArgs a)
 {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t = lane >> 4, r = lane & 15;
     const int64_t rb = blockIdx.x;
     const int64_t KT = a.k / kTileK, G = a.k / kGroup;
     const ExpertPtrs &W = a.ex[0];
     const bool act = r < a.m;
     const uint16_t *xrow = a.x + (act ? r : 0) * a.ldx;
+    constexpr int STRIDE = NW * TPW;
 
     f4 tot = {0.f, 0.f, 0.f, 0.f};
-    TileIn<B> cur, nxt;
-    int64_t kt = wv;
-    if (kt < KT) load_tile<B>(W, rb, kt, KT, G, lane, cur);
-    while (kt < KT) {
-        const int64_t kn = kt + NW;
-        if (kn < KT) load_tile<B>(W, rb, kn, KT, G, lane, nxt);
-        h8 X[8];
-        load_x(xrow, act, kt, t, X);
-        GroupConst<B> g0, g1;
-        g0.set(cur.zz & 0xFF);
-        g1.set((cur.zz >> 8) & 0xFF);
-        h8 A[8];
-        unpack_chunk<B>(cur.d, g0, g1, A);
-        mma_tile(A, X, cur.sc, tot);
-        cur = nxt;
-        kt = kn;
+    Chunk<B, TPW> ca, cb;  // weight tiles: two named buffers, used alternately
+    h8 X[TPW][8];          // activation fragments of the chunk being multiplied
+    int64_t k0 = (int64_t)wv * TPW;
+    if (k0 < KT) load_w_chunk<B, TPW>(W, rb, k0, KT, G, lane, ca);
+    while (k0 < KT) {
+        load_x_chunk<TPW>(xrow, act, k0, KT, t, X);
+        if (k0 + STRIDE < KT) load_w_chunk<B, TPW>(W, rb, k0 + STRIDE, KT, G, lane, cb);
+        compute_chunk<B, TPW>(ca, X, k0, KT, tot);
+        k0 += STRIDE;
+        if (k0 >= KT) break;
+        load_x_chunk<TPW>(xrow, act, k0, KT, t, X);
+        if (k0 + STRIDE < KT) load_w_chunk<B, TPW>(W, rb, k0 + STRIDE, KT, G, lane, ca);
+        compute_chunk<B, TPW>(cb, X, k0, KT, tot);
+        k0 += STRIDE;
     }
 
     __shared__ f4 red[NW][64];
@@ -138,7 +183,7 @@ template <int B, int EPI, int MT>
 __global__ __launch_bounds__(256) void grouped_kernel(SmallArgs a)
 {
     constexpr int RB = EPI == QP_EPI_SWIGLU ? 2 : 1;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t = lane >> 4, r = lane & 15;
     const int e = blockIdx.y;
     const int64_t unit = (int64_t)blockIdx.x * 4 + wv;
@@ -165,21 +210,15 @@ __global__ __launch_bounds__(256) void grouped_kernel(SmallArgs a)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) tot[u][mt] = (f4){0.f, 0.f, 0.f, 0.f};
 
-        TileIn<B> cur[RB], nxt[RB];
-#pragma unroll
-        for (int u = 0; u < RB; ++u) load_tile<B>(W, unit * RB + u, 0, KT, G, lane, cur[u]);
-        for (int64_t kt = 0; kt < KT; ++kt) {
-            if (kt + 1 < KT) {
-#pragma unroll
-                for (int u = 0; u < RB; ++u) load_tile<B>(W, unit * RB + u, kt + 1, KT, G, lane, nxt[u]);
-            }
+        TileIn<B> ta[RB], tb[RB];
+        auto compute = [&](const TileIn<B> *in, int64_t kt) {
             h8 A[RB][8];
 #pragma unroll
             for (int u = 0; u < RB; ++u) {
                 GroupConst<B> g0, g1;
-                g0.set(cur[u].zz & 0xFF);
-                g1.set((cur[u].zz >> 8) & 0xFF);
-                unpack_chunk<B>(cur[u].d, g0, g1, A[u]);
+                g0.set(in[u].zz & 0xFF);
+                g1.set((in[u].zz >> 8) & 0xFF);
+                unpack_chunk<B>(in[u].d, g0, g1, A[u]);
             }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
@@ -187,11 +226,25 @@ __global__ __launch_bounds__(256) void grouped_kernel(SmallArgs a)
                     h8 X[8];
                     load_x(xrow[mt], act[mt], kt, t, X);
 #pragma unroll
-                    for (int u = 0; u < RB; ++u) mma_tile(A[u], X, cur[u].sc, tot[u][mt]);
+                    for (int u = 0; u < RB; ++u) mma_tile(A[u], X, in[u].sc, tot[u][mt]);
                 }
             }
+        };
 #pragma unroll
-            for (int u = 0; u < RB; ++u) cur[u] = nxt[u];
+        for (int u = 0; u < RB; ++u) load_tile<B>(W, unit * RB + u, 0, KT, G, lane, ta[u]);
+        for (int64_t kt = 0; kt < KT;) {
+            if (kt + 1 < KT) {
+#pragma unroll
+                for (int u = 0; u < RB; ++u) load_tile<B>(W, unit * RB + u, kt + 1, KT, G, lane, tb[u]);
+            }
+            compute(ta, kt);
+            if (++kt >= KT) break;
+            if (kt + 1 < KT) {
+#pragma unroll
+                for (int u = 0; u < RB; ++u) load_tile<B>(W, unit * RB + u, kt + 1, KT, G, lane, ta[u]);
+            }
+            compute(tb, kt);
+            ++kt;
         }
 
 #pragma unroll
@@ -220,8 +273,8 @@ __global__ __launch_bounds__(256) void grouped_kernel(SmallArgs a)
 template <int B>
 static hipError_t gemv_bits(const SmallArgs &a, hipStream_t st)
 {
-    constexpr int NW = 8;
-    hipLaunchKernelGGL((gemv_kernel<B, NW>), dim3((unsigned)(a.n / kTileN)), dim3(NW * 64), 0, st, a);
+    constexpr int NW = 8, TPW = 1;
+    hipLaunchKernelGGL((gemv_kernel<B, NW, TPW>), dim3((unsigned)(a.n / kTileN)), dim3(NW * 64), 0, st, a);
     return hipGetLastError();
 }
 

@@ -20,10 +20,22 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
     return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// Bits [s, s+32) of the 64-bit value {hi, lo}, 0 <= s < 32.
-__device__ __forceinline__ uint32_t funnel(uint32_t hi, uint32_t lo, uint32_t s)
+// Bits [A, A+32) of the 64-bit value {hi, lo} (zeros above bit 63), A compile-time.
+// Written with v_alignbit_b32 rather than 64-bit shifts: the compiler may fuse a 64-bit
+// shift of two adjacent array elements into one 64-bit access, which keeps the register
+// array from being split into registers.
+template <int A>
+__device__ __forceinline__ uint32_t win(uint32_t hi, uint32_t lo)
 {
-    return s == 0 ? lo : (uint32_t)((((uint64_t)hi << 32) | lo) >> s);
+    static_assert(A >= 0 && A < 64, "window offset");
+    if constexpr (A == 0)
+        return lo;
+    else if constexpr (A < 32)
+        return __builtin_amdgcn_alignbit(hi, lo, A);
+    else if constexpr (A == 32)
+        return hi;
+    else
+        return hi >> (A - 32);
 }
 
 __device__ __forceinline__ uint32_t bfi_hi(uint32_t hi_src, uint32_t lo_src)
@@ -106,7 +118,7 @@ template <int J> struct BlockUnpack<3, J> {
         if constexpr ((c % 4) + 3 <= 4)
             v = d[w] >> s;                 // unit inside one dword
         else
-            v = funnel(d[w + 1], d[w], s); // unit straddles two dwords
+            v = win<s>(d[w + 1], d[w]);    // unit straddles two dwords
         const uint32_t w1 = bfi_hi(v << 13, v);          // lo: v[0:16)  hi: v[3:19)
         const uint32_t w2 = bfi_hi(v << 1, v >> 12);     // lo: v[12:28) hi: v[15:31)
         u4 r;
@@ -139,10 +151,9 @@ template <int J> struct BlockUnpack<5, J> {
     {
         constexpr int c = 5 * J, w = c / 4, o = c % 4, s = 8 * o;
         const uint32_t lo = d[w], hi = d[w + 1];
-        const uint64_t v = ((((uint64_t)hi << 32) | lo) >> s);
         constexpr uint32_t sel = o | ((o + 1) << 8) | (o << 16) | ((o + 1) << 24);
         const uint32_t x0 = perm(hi, lo, sel);           // both halves: v[0:16)
-        const uint32_t a1 = (uint32_t)(v >> 10), a2 = (uint32_t)(v >> 20), a3 = (uint32_t)(v >> 30);
+        const uint32_t a1 = win<s + 10>(hi, lo), a2 = win<s + 20>(hi, lo), a3 = win<s + 30>(hi, lo);
         const uint32_t x1 = perm(a1, a1, 0x01000100u);
         const uint32_t x2 = perm(a2, a2, 0x01000100u);
         const uint32_t x3 = perm(a3, a3, 0x01000100u);
@@ -160,12 +171,12 @@ template <int J> struct BlockUnpack<6, J> {
     static __device__ __forceinline__ h8 run(const uint32_t *d, const GroupConst<6> &gc)
     {
         constexpr int c = 6 * J, w = c / 4, s = 8 * (c % 4);
-        const uint64_t v = ((((uint64_t)d[w + 1] << 32) | d[w]) >> s);
-        const uint32_t v0 = (uint32_t)v;
-        const uint32_t w0 = bfi_hi(v0 << 10, v0);                                 // q0, q1
-        const uint32_t w1 = bfi_hi((uint32_t)(v >> 2), (uint32_t)(v >> 12));       // q2, q3
-        const uint32_t w2 = bfi_hi((uint32_t)(v >> 14), (uint32_t)(v >> 24));      // q4, q5
-        const uint32_t w3 = bfi_hi((uint32_t)(v >> 26), (uint32_t)(v >> 36));      // q6, q7
+        const uint32_t lo = d[w], hi = d[w + 1];
+        const uint32_t v0 = win<s>(hi, lo);
+        const uint32_t w0 = bfi_hi(v0 << 10, v0);                                  // q0, q1
+        const uint32_t w1 = bfi_hi(win<s + 2>(hi, lo), win<s + 12>(hi, lo));        // q2, q3
+        const uint32_t w2 = bfi_hi(win<s + 14>(hi, lo), win<s + 24>(hi, lo));       // q4, q5
+        const uint32_t w3 = bfi_hi(win<s + 26>(hi, lo), win<s + 36>(hi, lo));       // q6, q7
         u4 r;
         r[0] = magic_pair(w0, 0x003F003Fu, mul_const<0, 0>(), gc.add[0]);
         r[1] = magic_pair(w1, 0x003F003Fu, mul_const<0, 0>(), gc.add[0]);
