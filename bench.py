@@ -186,7 +186,9 @@ def main():
         xp = torch.from_numpy(workloads.prefill_activations().view(np.int16)).to(dev)
         Mp, Kp, Np = workloads.PREFILL_M, workloads.PREFILL_K, workloads.PREFILL_N
         yp = torch.empty((Mp, Np), dtype=torch.int16, device=dev)
-        ms = time_graph(torch, lambda i: q.qlinear_gemm(dp, hp, xp, Kp, Mp, yp, Np), 10, stream)
+        wsb = q.qlinear_gemm_workspace_bytes(dp, Mp, wt["nnz"])
+        wsp = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        ms = time_graph(torch, lambda i: q.qlinear_gemm(dp, hp, xp, Kp, Mp, yp, Np, wsp, wsb), 10, stream)
         flops = 2 * Mp * Np * Kp + 2 * Mp * wt["nnz"]
         tf = flops / (ms * 1e-3) / 1e12
         extra["prefill_gemm_m512"] = dict(us=round(ms * 1e3, 2), TFLOPs=round(tf, 1),

@@ -165,9 +165,16 @@ qp_status qlinear_gemv(const qp_weight_desc *desc, const qp_weight *w, const uin
  * Prefill dequant-GEMM for any m >= 1 (tuned for m >= 64): same operands and result as
  * qlinear_gemv.  Tiles of the packed weight are unpacked in registers and fed to fp16
  * matrix cores with fp32 accumulation; scales are applied per group in fp32.
+ *  workspace/ws_bytes  device scratch of at least qlinear_gemm_workspace_bytes(desc, m,
+ *           w->nnz) bytes, 16-byte aligned, only needed when w carries outliers (NULL/0
+ *           otherwise).  It holds x transposed (k * ldt fp16) and the fp32 outlier partial
+ *           (n * ldt floats), ldt = m rounded up to 128: (2k + 4n) * ldt bytes.
+ *  Limits: x, the packed weight, and each workspace part under 2 GiB.
  */
+size_t qlinear_gemm_workspace_bytes(const qp_weight_desc *desc, int64_t m, int64_t nnz);
 qp_status qlinear_gemm(const qp_weight_desc *desc, const qp_weight *w, const uint16_t *x,
-                       int64_t ldx, int64_t m, uint16_t *y, int64_t ldy, void *stream);
+                       int64_t ldx, int64_t m, uint16_t *y, int64_t ldy, void *workspace,
+                       size_t ws_bytes, void *stream);
 
 /*
  * Grouped dequant-GEMM over routed experts (MoE page s4.2).  All experts share `desc`

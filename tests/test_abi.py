@@ -100,6 +100,11 @@ def test_gemv_validation():
     bad_csr = q.weight(FAKE, FAKE, FAKE, None, None, None, 5)
     assert q.qlinear_gemm(d, bad_csr, FAKE, 512, 64, FAKE, 256, stream=0, check=False) == q.QP_ERR_INVALID_ARG
     assert "csr" in q.last_error().lower()
+    csr = q.weight(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 5)
+    need = q.qlinear_gemm_workspace_bytes(d, 64, 5)
+    assert need == (2 * 512 + 4 * 256) * 128 and q.qlinear_gemm_workspace_bytes(d, 64, 0) == 0
+    assert q.qlinear_gemm(d, csr, FAKE, 512, 64, FAKE, 256, FAKE, need - 1, stream=0,
+                          check=False) == q.QP_ERR_WORKSPACE
 
 
 def test_quantize_validation():

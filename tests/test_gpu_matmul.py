@@ -17,7 +17,13 @@ def run_linear(entry, g: GpuWeight, x: np.ndarray, with_csr=True):
     m, k = x.shape
     xd = to_dev_fp16(x)
     y = torch.empty((m, g.n), dtype=torch.int16, device="cuda")
-    getattr(q, entry)(g.desc, g.handle(with_csr), xd, k, m, y, g.n)
+    if entry == "qlinear_gemm":
+        nnz = g.nnz if with_csr else 0
+        wsb = q.qlinear_gemm_workspace_bytes(g.desc, m, nnz)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+        q.qlinear_gemm(g.desc, g.handle(with_csr), xd, k, m, y, g.n, ws, wsb)
+    else:
+        getattr(q, entry)(g.desc, g.handle(with_csr), xd, k, m, y, g.n)
     torch.cuda.synchronize()
     return from_dev_fp16(y)
 
@@ -70,6 +76,35 @@ def test_gemm_ragged_with_outliers(bits, m):
     x = workloads.activations_fp16(m, k, 400 + bits)
     r = oracle.linear(x, oracle.quantize(w, bits, frac))
     y = run_linear("qlinear_gemm", GpuWeight(w, bits, frac), x)
+    assert rel_err(y, r) <= TOL, report(y, r)
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("m", (17, 130))
+def test_gemm_ragged_dense(bits, m):
+    """No outliers: every 16-row activation tile and a partial last weight tile."""
+    n, k = 560, 1536
+    w = workloads.weights_fp16(n, k, 450 + bits)
+    x = workloads.activations_fp16(m, k, 450 + bits)
+    r = oracle.linear(x, oracle.quantize(w, bits))
+    y = run_linear("qlinear_gemm", GpuWeight(w, bits), x)
+    assert rel_err(y, r) <= TOL, report(y, r)
+
+
+def test_gemm_dense_rows_of_outliers():
+    """Rows with many outliers (60 in one row, ~20% of ten rows)."""
+    n, k, m = 256, 2048, 70
+    w = workloads.weights_fp16(n, k, 77)
+    rng = np.random.default_rng(77)
+    w[3, rng.choice(k, 60, replace=False)] = np.float16(4.0)       # 60 outliers in one row
+    w[130:140, :] = np.where(rng.random((10, k)) < 0.2, np.float16(-3.5), w[130:140, :])
+    frac = (w.astype(np.float32).__abs__() >= 3).sum() / (n * k)
+    frac = (int(round(frac * n * k)) + 0.5) / (n * k)
+    x = workloads.activations_fp16(m, k, 77)
+    ref = oracle.quantize(w, 4, frac)
+    assert len(ref["col"]) > 2048 + 60
+    r = oracle.linear(x, ref)
+    y = run_linear("qlinear_gemm", GpuWeight(w, 4, frac), x)
     assert rel_err(y, r) <= TOL, report(y, r)
 
 

@@ -55,7 +55,8 @@ _SIGS = {
     "qpack_pack": (_i32, [_D, _vp, _vp, _vp]),
     "qpack_unpack": (_i32, [_D, _vp, _vp, _vp]),
     "qlinear_gemv": (_i32, [_D, _W, _vp, _i64, _i64, _vp, _i64, _vp]),
-    "qlinear_gemm": (_i32, [_D, _W, _vp, _i64, _i64, _vp, _i64, _vp]),
+    "qlinear_gemm_workspace_bytes": (_sz, [_D, _i64, _i64]),
+    "qlinear_gemm": (_i32, [_D, _W, _vp, _i64, _i64, _vp, _i64, _vp, _sz, _vp]),
     "qlinear_grouped_gemm": (_i32, [_D, _W, _i32, _vp, _i64, _vp, _vp, _i64, _i32, _vp, _i64, _vp]),
     "qmoe_dispatch": (_i32, [_vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "qmoe_combine": (_i32, [_vp, _i64, _vp, _vp, _i64, _i32, _i64, _vp, _i64, _vp]),
@@ -165,9 +166,13 @@ def qlinear_gemv(d, w, x, ldx, m, y, ldy, stream=None, check=True):
                                                     ldy, _stream(stream)), check)
 
 
-def qlinear_gemm(d, w, x, ldx, m, y, ldy, stream=None, check=True):
+def qlinear_gemm_workspace_bytes(d, m: int, nnz: int) -> int:
+    return lib.qlinear_gemm_workspace_bytes(ctypes.byref(d), m, nnz)
+
+
+def qlinear_gemm(d, w, x, ldx, m, y, ldy, workspace=None, ws_bytes=0, stream=None, check=True):
     return _check("qlinear_gemm", lib.qlinear_gemm(ctypes.byref(d), ctypes.byref(w), _ptr(x), ldx, m, _ptr(y),
-                                                    ldy, _stream(stream)), check)
+                                                    ldy, _ptr(workspace), ws_bytes, _stream(stream)), check)
 
 
 def qlinear_grouped_gemm(d, experts, x, ldx, row_src, expert_offsets, rows, epilogue, y, ldy, stream=None,

@@ -202,22 +202,38 @@ qp_status qlinear_gemv(const qp_weight_desc *d, const qp_weight *w, const uint16
     return device(launch_gemv(d->bits, a, S(stream)), "qlinear_gemv");
 }
 
+size_t qlinear_gemm_workspace_bytes(const qp_weight_desc *d, int64_t m, int64_t nnz)
+{
+    if (check_desc(d, false) != QP_OK || m < 1 || nnz <= 0) return 0;
+    return (size_t)((d->k * 2 + d->n * 4) * gemm_xt_ld(m));
+}
+
 qp_status qlinear_gemm(const qp_weight_desc *d, const qp_weight *w, const uint16_t *x, int64_t ldx, int64_t m,
-                       uint16_t *y, int64_t ldy, void *stream)
+                       uint16_t *y, int64_t ldy, void *workspace, size_t ws_bytes, void *stream)
 {
     qp_status st = check_desc(d, true);
     if (st != QP_OK) return st;
     if ((st = check_weight(d, w, true)) != QP_OK) return st;
     if ((st = check_xy(d, x, ldx, m, y, ldy, d->n, 4)) != QP_OK) return st;
     if (m > (1LL << 24)) return fail(QP_ERR_INVALID_ARG, "m too large");
+    if (m * ldx * 2 > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "x larger than 2 GiB");
+    if ((int64_t)qp_packed_bytes(d) > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "packed weight larger than 2 GiB");
     GemmArgs a{};
     a.packed = (const uint8_t *)w->packed;
     a.scales = w->scales;
     a.zeros = w->zeros;
     if (w->nnz > 0) {
+        const size_t need = qlinear_gemm_workspace_bytes(d, m, w->nnz);
+        if (!workspace || ws_bytes < need || !aligned(workspace, 16))
+            return fail(QP_ERR_WORKSPACE, "outlier add-back needs %zu bytes of workspace (16-byte aligned)", need);
+        if (d->k * gemm_xt_ld(m) * 2 > 0x7FFFFFFFLL || d->n * gemm_xt_ld(m) * 4 > 0x7FFFFFFFLL)
+            return fail(QP_ERR_UNSUPPORTED, "m*k or m*n too large for the outlier add-back");
         a.rowptr = w->csr_rowptr;
         a.col = w->csr_col;
         a.val = w->csr_val;
+        a.ldxt = gemm_xt_ld(m);
+        a.xt = (uint16_t *)workspace;
+        a.spart = (float *)((uint8_t *)workspace + d->k * a.ldxt * 2);
     }
     a.x = x;
     a.ldx = ldx;

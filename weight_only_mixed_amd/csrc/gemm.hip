@@ -6,11 +6,19 @@
 // 16-byte loads straight into registers (double-buffered across k-tiles) and unpacks them into
 // exact fp16 (q - zp) A operands itself, so weights never pass through LDS and each weight is
 // unpacked once per 128-row activation block.  The activation tile (128 rows x one 128-k
-// group, 32 KB) is shared by the four waves through LDS, double-buffered, with the 16-byte
-// chunks of each row XOR-swizzled by the row index so that the matrix-core fragment reads
-// (16 rows, same column) hit distinct banks.  Every 128-k group is accumulated on the matrix
-// cores in fp32 and then scaled by its fp16 scale in fp32; the outlier CSR is added in the
-// epilogue before the single fp16 rounding of y.
+// group, 32 KB) is shared by the four waves through LDS: it is loaded with buffer-to-LDS DMA
+// (no registers), double-buffered, with the 16-byte chunks of each row XOR-swizzled by the row
+// index so the matrix-core fragment reads (16 rows, same column) hit distinct banks.  Every
+// 128-k group is accumulated on the matrix cores in fp32 and then scaled by its fp16 scale in
+// fp32.
+//
+// Outlier add-back (70B page, s2): the held-out fp16 weights are added in fp32 before the one
+// fp16 rounding of y.  Two small kernels run first: one writes x transposed (x^T) into the
+// caller's workspace, the other multiplies each weight row's outliers by it into an fp32
+// sparse partial S^T[n][m].  The GEMM then starts its fp32 accumulators from S^T instead of
+// zero, so the main loop is the same as without outliers.  Inside each 128-row block of m the
+// transposed layouts keep row 16*mt + r at position 8*r + mt: a lane's eight accumulator rows
+// (tiles mt = 0..7 of its row r) are 32 contiguous bytes of S^T.
 //
 // Workgroups are ordered so that the activation blocks of one weight tile run on the same XCD
 // (block b runs on XCD b % 8), where they share that XCD's L2 copy of the packed weights.
@@ -27,19 +35,20 @@ constexpr int kNT = kWaves * kRBW * kTileN;  // 128 weight rows per workgroup
 constexpr int kMRows = kMT * 16;             // 128 activation rows per workgroup
 constexpr int kRowBytes = 128 * 2;           // one 128-k group of one activation row
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
 __device__ __forceinline__ float lo_h(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFF)); }
 __device__ __forceinline__ float hi_h(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
+__device__ __forceinline__ float h_f(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)v); }
+// By value on purpose: __builtin_bit_cast applied directly to a vector element (v[i]) reads
+// element 0 with this compiler.
+__device__ __forceinline__ float as_f(uint32_t v) { return __builtin_bit_cast(float, v); }
 
 __device__ __forceinline__ uint32_t pack2(float a, float b)
 {
     const _Float16 ha = (_Float16)a, hb = (_Float16)b;
     return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
 }
-
-// LDS byte offset of 16-byte chunk c (8 k values) of activation row `row`.
-__device__ __forceinline__ int xs_off(int row, int c) { return row * kRowBytes + ((c ^ (row & 15)) << 4); }
-
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // Raw buffer resource over [base, base + bytes): loads at offsets >= bytes return zeros.
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes)
@@ -48,39 +57,61 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes)
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
 }
 
-__device__ __forceinline__ u4 ld16(rsrc_t r, uint32_t off)
+// Buffer loads at voffset (per lane) + soffset (wave-uniform: kept in a scalar register, so the
+// per-lane address registers stay few).
+__device__ __forceinline__ u4 ld16(rsrc_t r, uint32_t off, uint32_t soff = 0)
 {
-    return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
 }
-__device__ __forceinline__ u2 ld8(rsrc_t r, uint32_t off)
+__device__ __forceinline__ u2 ld8(rsrc_t r, uint32_t off, uint32_t soff = 0)
 {
-    return __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    return __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0));
 }
-__device__ __forceinline__ uint32_t ld4(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
-__device__ __forceinline__ uint32_t ld2(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0); }
+__device__ __forceinline__ uint32_t ld4(rsrc_t r, uint32_t off, uint32_t soff = 0)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
+}
+__device__ __forceinline__ uint32_t ld2(rsrc_t r, uint32_t off, uint32_t soff = 0)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0);
+}
 
-// Buffers of one workgroup: activation rows m0.. (rows past m read as zeros) and the weight
-// rows of this wave's blocks.
-struct Bufs {
-    rsrc_t x, w, sc, zr;
-    uint32_t xoff;    // this thread's first activation piece (row tid/16, chunk tid%16)
-    uint32_t xrow16;  // bytes between activation rows 16 apart
+// LDS byte offset of 16-byte chunk c (8 k values) of activation row `row`.
+__device__ __forceinline__ int xs_off(int row, int c) { return row * kRowBytes + ((c ^ (row & 15)) << 4); }
+
+// Shared memory of one workgroup: the activation tiles (double buffer).
+struct Smem {
+    uint8_t xs[2][kMRows * kRowBytes];
 };
 
-// This thread's 8 pieces of the 128 x 128-k activation tile of group `g`.
-__device__ __forceinline__ void load_x(const Bufs &bf, int64_t g, u4 *buf)
-{
-#pragma unroll
-    for (int it = 0; it < 8; ++it) buf[it] = ld16(bf.x, bf.xoff + it * bf.xrow16 + (uint32_t)g * 256);
-}
+// Buffers of one workgroup.  Every wave-uniform offset passed as soffset stays inside the
+// range the per-lane voffset was checked against (a row of x, a weight row block), so a
+// load is in bounds whether or not the hardware includes soffset in its range check.
+struct Bufs {
+    rsrc_t x;              // activation rows [m0, m)
+    rsrc_t w[kRBW];        // packed tiles of row block rb0 + u (empty past the last block)
+    rsrc_t sc[kRBW], zr[kRBW];
+    uint32_t xoff[8];      // this lane's source of LDS-DMA piece it (row offset + chunk)
+};
 
-__device__ __forceinline__ void store_x(uint8_t *lds, const u4 *buf)
+// DMA the 128 x 128-k activation tile of group g into LDS buffer `dst` (this wave's 8 KB).
+// Lane L of piece `it` fills LDS bytes [16L, 16L+16) of a 1 KB run = row 4*(8*wv+it) + L/16,
+// physical chunk L%16, which holds logical chunk (L%16) ^ (row & 15).
+__device__ __forceinline__ void dma_x(const Bufs &bf, int64_t g, uint8_t *dst, int wv)
 {
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)g * 256);  // column of group g
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
-        const int idx = it * 256 + threadIdx.x;
-        *(u4 *)(lds + xs_off(idx >> 4, idx & 15)) = buf[it];
+        uint8_t *base = dst + (wv * 8 + it) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(bf.x, (__attribute__((address_space(3))) void *)base, 16,
+                                                 bf.xoff[it], soff, 0, 0);
     }
+}
+
+__device__ __forceinline__ void wait_dma_and_sync()
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
 }
 
 template <int B>
@@ -90,30 +121,34 @@ struct WTile {
     uint32_t sc[kRBW][4];
 };
 
-// Weight tile kt of this wave's row blocks (offsets relative to the wave's first block).
+// Weight tile kt of this wave's row blocks.
 template <int B>
-__device__ __forceinline__ void load_w(const Bufs &bf, int64_t KT, int64_t G, int64_t kt, int lane, WTile<B> &w)
+__device__ __forceinline__ void load_w(const Bufs &bf, int64_t G, int64_t kt, int lane, WTile<B> &w)
 {
     const int t = lane >> 4, r = lane & 15;
+    const uint32_t vw = 16 * lane, vw8 = 8 * lane;
+    const uint32_t vz = (uint32_t)(r * G), vs = (uint32_t)(4 * t * G * 2);
+    const uint32_t tile = __builtin_amdgcn_readfirstlane((uint32_t)(kt * (512 * B)));
+    const uint32_t zo = __builtin_amdgcn_readfirstlane((uint32_t)(2 * kt));
 #pragma unroll
     for (int u = 0; u < kRBW; ++u) {
-        const uint32_t tile = (uint32_t)((u * KT + kt) * (512 * B));
 #pragma unroll
         for (int sl = 0; sl < B / 2; ++sl) {
-            const u4 v = ld16(bf.w, tile + 1024 * sl + 16 * lane);
+            const u4 v = ld16(bf.w[u], vw, tile + 1024 * sl);
             w.d[u][4 * sl + 0] = v[0];
             w.d[u][4 * sl + 1] = v[1];
             w.d[u][4 * sl + 2] = v[2];
             w.d[u][4 * sl + 3] = v[3];
         }
         if (B & 1) {
-            const u2 v = ld8(bf.w, tile + 1024 * (B / 2) + 8 * lane);
+            const u2 v = ld8(bf.w[u], vw8, tile + 1024 * (B / 2));
             w.d[u][2 * B - 2] = v[0];
             w.d[u][2 * B - 1] = v[1];
         }
-        w.zz[u] = ld2(bf.zr, (uint32_t)((u * kTileN + r) * G + 2 * kt));
+        w.zz[u] = ld2(bf.zr[u], vz, zo);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w.sc[u][i] = ld4(bf.sc, (uint32_t)(((u * kTileN + 4 * t + i) * G + 2 * kt) * 2));
+        for (int i = 0; i < 4; ++i)
+            w.sc[u][i] = ld4(bf.sc[u], vs, __builtin_amdgcn_readfirstlane((uint32_t)((i * G + 2 * kt) * 2)));
     }
 }
 
@@ -167,10 +202,10 @@ __device__ __forceinline__ void group_step(const WTile<B> &w, const uint8_t *xs,
 
 }  // namespace
 
-template <int B>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
+template <int B, bool OUTL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(GemmArgs a)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t xs[2][kMRows * kRowBytes];
+    __shared__ __attribute__((aligned(16))) Smem sm;
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t = lane >> 4, r = lane & 15;
     const int64_t KT = a.k / kTileK, G = a.k / kGroup;
@@ -187,63 +222,93 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
     }
     const int64_t m0 = mtile * kMRows;
     const int64_t NB = a.n / kTileN;
-    const int64_t rb0 = nt * (kNT / kTileN) + wv * kRBW;
-    const int64_t nrb = NB - rb0;  // row blocks from this wave's first to the end of W
+    const int64_t n0 = nt * kNT;                          // first weight row of the workgroup
+    const int64_t rb0 = nt * (kNT / kTileN) + wv * kRBW;  // first row block of this wave
 
     Bufs bf;
     bf.x = make_rsrc(a.x + m0 * a.ldx, (a.m - m0) * a.ldx * 2);
-    bf.xoff = (uint32_t)(((threadIdx.x >> 4) * a.ldx + 8 * (threadIdx.x & 15)) * 2);
-    bf.xrow16 = (uint32_t)(16 * a.ldx * 2);
-    bf.w = make_rsrc(a.packed + rb0 * KT * (512 * B), nrb * KT * (512 * B));
-    bf.sc = make_rsrc(a.scales + rb0 * kTileN * G, nrb * kTileN * G * 2);
-    bf.zr = make_rsrc(a.zeros + rb0 * kTileN * G, nrb * kTileN * G);
-
-    f4 tot[kRBW][kMT];
 #pragma unroll
-    for (int u = 0; u < kRBW; ++u)
+    for (int it = 0; it < 8; ++it) {
+        const int row = 32 * wv + 4 * it + (lane >> 4);
+        const int c = (lane & 15) ^ (row & 15);
+        bf.xoff[it] = (uint32_t)((row * a.ldx + 8 * c) * 2);
+    }
 #pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) tot[u][mt] = (f4){0.f, 0.f, 0.f, 0.f};
-
-    u4 xbuf[8];
-    load_x(bf, 0, xbuf);
-    store_x(xs[0], xbuf);
-    WTile<B> wa, wb;
-    load_w<B>(bf, KT, G, 0, lane, wa);
-    __syncthreads();
-
-    // Two k-tiles (four groups) per iteration so both weight buffers are named statically.
-    // Scheduling barriers keep each group step's unpack and fragment reads inside its step.
-    for (int64_t kt = 0; kt < KT; kt += 2) {
-        // group 2kt (buffer 0): prefetch group 2kt+1 activations and the next weight tile
-        load_x(bf, 2 * kt + 1, xbuf);
-        if (kt + 1 < KT) load_w<B>(bf, KT, G, kt + 1, lane, wb);
-        __builtin_amdgcn_sched_barrier(0);
-        group_step<B, 0>(wa, xs[0], lane, tot);
-        store_x(xs[1], xbuf);
-        __syncthreads();
-        // group 2kt+1 (buffer 1)
-        if (kt + 1 < KT) load_x(bf, 2 * kt + 2, xbuf);
-        __builtin_amdgcn_sched_barrier(0);
-        group_step<B, 1>(wa, xs[1], lane, tot);
-        if (kt + 1 < KT) store_x(xs[0], xbuf);
-        __syncthreads();
-        if (kt + 1 >= KT) break;
-        // group 2kt+2 (buffer 0)
-        load_x(bf, 2 * kt + 3, xbuf);
-        if (kt + 2 < KT) load_w<B>(bf, KT, G, kt + 2, lane, wa);
-        __builtin_amdgcn_sched_barrier(0);
-        group_step<B, 0>(wb, xs[0], lane, tot);
-        store_x(xs[1], xbuf);
-        __syncthreads();
-        // group 2kt+3 (buffer 1)
-        if (kt + 2 < KT) load_x(bf, 2 * kt + 4, xbuf);
-        __builtin_amdgcn_sched_barrier(0);
-        group_step<B, 1>(wb, xs[1], lane, tot);
-        if (kt + 2 < KT) store_x(xs[0], xbuf);
-        __syncthreads();
+    for (int u = 0; u < kRBW; ++u) {
+        const int64_t rb = rb0 + u;
+        const bool in = rb < NB;
+        bf.w[u] = make_rsrc(a.packed + rb * KT * (512 * B), in ? KT * (512 * B) : 0);
+        bf.sc[u] = make_rsrc(a.scales + rb * kTileN * G, in ? kTileN * G * 2 : 0);
+        bf.zr[u] = make_rsrc(a.zeros + rb * kTileN * G, in ? kTileN * G : 0);
     }
 
-    // epilogue: outlier add-back, fp16 store
+    f4 tot[kRBW][kMT];
+    if constexpr (OUTL) {
+        // accumulators start from the outlier partial S^T (rows past n read as zeros)
+        const rsrc_t sr = make_rsrc(a.spart, a.n * a.ldxt * 4);
+        const uint32_t ld = (uint32_t)(a.ldxt * 4);
+        const uint32_t v0 = (uint32_t)(((rb0 * kTileN + 4 * t) * a.ldxt + m0 + 8 * r) * 4);
+#pragma unroll
+        for (int u = 0; u < kRBW; ++u) {
+            u4 lo[4], hi[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t off = v0 + (uint32_t)(u * kTileN + i) * ld;
+                lo[i] = ld16(sr, off);
+                hi[i] = ld16(sr, off + 16);
+            }
+            // whole-vector construction (element-wise stores into an unset vector are avoided)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                tot[u][mt] = (f4){as_f(lo[0][mt]), as_f(lo[1][mt]), as_f(lo[2][mt]), as_f(lo[3][mt])};
+                tot[u][mt + 4] = (f4){as_f(hi[0][mt]), as_f(hi[1][mt]), as_f(hi[2][mt]), as_f(hi[3][mt])};
+            }
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kRBW; ++u)
+#pragma unroll
+            for (int mt = 0; mt < kMT; ++mt) {
+                tot[u][mt] = (f4){0.f, 0.f, 0.f, 0.f};
+                // opaque zero: a known-zero start lets the compiler specialise the first group
+                // steps, which costs registers across the whole loop
+                asm volatile("" : "+v"(tot[u][mt]));
+            }
+    }
+
+    dma_x(bf, 0, sm.xs[0], wv);
+    WTile<B> wa, wb;
+    load_w<B>(bf, G, 0, lane, wa);
+    wait_dma_and_sync();
+
+    // Two k-tiles (four groups) per iteration so both weight buffers are named statically.
+    for (int64_t kt = 0; kt < KT; kt += 2) {
+        // group 2kt (LDS buffer 0): prefetch group 2kt+1 activations and the next weight tile
+        dma_x(bf, 2 * kt + 1, sm.xs[1], wv);
+        if (kt + 1 < KT) load_w<B>(bf, G, kt + 1, lane, wb);
+        __builtin_amdgcn_sched_barrier(0);
+        group_step<B, 0>(wa, sm.xs[0], lane, tot);
+        wait_dma_and_sync();
+        // group 2kt+1 (buffer 1)
+        if (kt + 1 < KT) dma_x(bf, 2 * kt + 2, sm.xs[0], wv);
+        __builtin_amdgcn_sched_barrier(0);
+        group_step<B, 1>(wa, sm.xs[1], lane, tot);
+        wait_dma_and_sync();
+        if (kt + 1 >= KT) break;
+        // group 2kt+2 (buffer 0)
+        dma_x(bf, 2 * kt + 3, sm.xs[1], wv);
+        if (kt + 2 < KT) load_w<B>(bf, G, kt + 2, lane, wa);
+        __builtin_amdgcn_sched_barrier(0);
+        group_step<B, 0>(wb, sm.xs[0], lane, tot);
+        wait_dma_and_sync();
+        // group 2kt+3 (buffer 1)
+        if (kt + 2 < KT) dma_x(bf, 2 * kt + 4, sm.xs[0], wv);
+        __builtin_amdgcn_sched_barrier(0);
+        group_step<B, 1>(wb, sm.xs[1], lane, tot);
+        wait_dma_and_sync();
+    }
+
+    // epilogue: the fp16 store
 #pragma unroll
     for (int u = 0; u < kRBW; ++u) {
         const int64_t rb = rb0 + u;
@@ -252,30 +317,77 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a)
         for (int mt = 0; mt < kMT; ++mt) {
             const int64_t row = m0 + 16 * mt + r;
             if (row >= a.m) continue;
-            f4 s = tot[u][mt];
-            if (a.rowptr) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t n = rb * kTileN + 4 * t + i;
-                    for (int32_t p = a.rowptr[n]; p < a.rowptr[n + 1]; ++p) {
-                        const float xv = (float)__builtin_bit_cast(_Float16, a.x[row * a.ldx + a.col[p]]);
-                        s[i] = __builtin_fmaf(xv, (float)__builtin_bit_cast(_Float16, a.val[p]), s[i]);
-                    }
-                }
-            }
+            const f4 s = tot[u][mt];
             uint16_t *y = a.y + row * a.ldy + rb * kTileN + 4 * t;
             *(u2 *)y = (u2){pack2(s[0], s[1]), pack2(s[2], s[3])};
         }
     }
 }
 
+// x^T for the outlier gathers: xt[kk][128 mb + 8 r + mt] = x[128 mb + 16 mt + r][kk], zeros for
+// rows >= m.  One block per 64 k x 128 m tile, staged through LDS.
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t *x, int64_t ldx, int64_t m, int64_t k,
+                                                        uint16_t *xt, int64_t ldxt)
+{
+    __shared__ uint16_t tile[128][65];
+    const int64_t k0 = blockIdx.x * 64, m0 = blockIdx.y * 128;
+    for (int i = threadIdx.x; i < 128 * 64; i += 256) {
+        const int rm = i / 64, ck = i % 64;
+        const int64_t gm = m0 + rm, gk = k0 + ck;
+        tile[rm][ck] = (gm < m && gk < k) ? x[gm * ldx + gk] : (uint16_t)0;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 128 * 64; i += 256) {
+        const int rk = i / 128, pos = i % 128;      // pos = 8 r + mt holds row 16 mt + r
+        const int rm = 16 * (pos & 7) + (pos >> 3);
+        const int64_t gk = k0 + rk;
+        if (gk < k) xt[gk * ldxt + m0 + pos] = tile[rm][rk];
+    }
+}
+
+// Outlier partial: S^T[n][p] = sum over the outliers (n, c, v) of v * x^T[c][p], in fp32 (one
+// wave per weight row, each lane 8 consecutive positions p of a 512-position chunk).
+__global__ __launch_bounds__(256) void outlier_spmm_kernel(const int32_t *rowptr, const int32_t *col,
+                                                           const uint16_t *val, const uint16_t *xt, int64_t n,
+                                                           int64_t ldxt, float *spart)
+{
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + wv;
+    const int64_t p = (int64_t)blockIdx.y * 512 + 8 * lane;
+    if (row >= n || p >= ldxt) return;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const int64_t e0 = rowptr[row], e1 = rowptr[row + 1];
+    for (int64_t e = e0; e < e1; ++e) {
+        const float v = h_f(val[e]);
+        const u4 xv = *(const u4 *)(xt + (int64_t)col[e] * ldxt + p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc[2 * j] = __builtin_fmaf(lo_h(xv[j]), v, acc[2 * j]);
+            acc[2 * j + 1] = __builtin_fmaf(hi_h(xv[j]), v, acc[2 * j + 1]);
+        }
+    }
+    f4 *dst = (f4 *)(spart + row * ldxt + p);
+    dst[0] = (f4){acc[0], acc[1], acc[2], acc[3]};
+    dst[1] = (f4){acc[4], acc[5], acc[6], acc[7]};
+}
+
 template <int B>
 static hipError_t gemm_bits(const GemmArgs &a, hipStream_t st)
 {
     const int64_t n_tiles = (a.n + kNT - 1) / kNT, m_tiles = (a.m + kMRows - 1) / kMRows;
-    hipLaunchKernelGGL((gemm_kernel<B>), dim3((unsigned)(n_tiles * m_tiles)), dim3(256), 0, st, a);
+    if (a.rowptr) {
+        hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)((a.k + 63) / 64), (unsigned)(a.ldxt / 128)), dim3(256), 0,
+                           st, a.x, a.ldx, a.m, a.k, a.xt, a.ldxt);
+        hipLaunchKernelGGL(outlier_spmm_kernel, dim3((unsigned)((a.n + 3) / 4), (unsigned)((a.ldxt + 511) / 512)),
+                           dim3(256), 0, st, a.rowptr, a.col, a.val, a.xt, a.n, a.ldxt, a.spart);
+        hipLaunchKernelGGL((gemm_kernel<B, true>), dim3((unsigned)(n_tiles * m_tiles)), dim3(256), 0, st, a);
+    } else {
+        hipLaunchKernelGGL((gemm_kernel<B, false>), dim3((unsigned)(n_tiles * m_tiles)), dim3(256), 0, st, a);
+    }
     return hipGetLastError();
 }
+
+int64_t gemm_xt_ld(int64_t m) { return (m + kMRows - 1) / kMRows * kMRows; }
 
 hipError_t launch_gemm(int bits, const GemmArgs &a, hipStream_t st)
 {

@@ -78,7 +78,11 @@ struct GemmArgs {
     int64_t m, n, k;
     uint16_t *y;
     int64_t ldy;
+    uint16_t *xt;   // workspace (outliers only): x transposed, [k][ldxt]
+    float *spart;   // workspace (outliers only): fp32 outlier partial, [n][ldxt]
+    int64_t ldxt;
 };
+int64_t gemm_xt_ld(int64_t m);
 hipError_t launch_gemm(int bits, const GemmArgs &a, hipStream_t st);
 
 hipError_t launch_moe_dispatch(const int32_t *ids, const float *w, int64_t tokens, int topk,
