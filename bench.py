@@ -84,6 +84,83 @@ def time_graph(torch, fn, reps: int, stream) -> float:
     return best
 
 
+GEMV_SOURCES = ("weight_only_mixed_amd/csrc/qmm_small.hip", "weight_only_mixed_amd/csrc/unpack.h",
+                "weight_only_mixed_amd/csrc/qp_internal.h")
+TRAFFIC_FILE = "profiles/pmc_traffic_gemv4096_gemm_prefill.md"
+
+
+def measured_traffic(kernel: str):
+    """Per-launch HBM bytes of `kernel` from the committed FETCH_SIZE/WRITE_SIZE summary, or None
+    if there is none or the GEMV sources changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in GEMV_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    with open(path) as fh:
+        for line in fh:
+            mt = re.match(r"\s*traffic (.+) bytes=(\d+) csrc_sha256=([0-9a-f]+)\s*$", line)
+            if mt and mt.group(1) == kernel and mt.group(3) == h.hexdigest():
+                return int(mt.group(2))
+    return None
+
+
+def copy_gbps(torch, nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """Device-to-device copy bandwidth (read + write bytes / time) of torch's copy kernel."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return gbps
+
+
+def pmc_pass(q, torch, workloads):
+    """A short eager sequence for counter collection: every (bits, M) GEMV of the step on
+    four distinct weight copies, the prefill GEMM twice, and a 1 GiB copy twice (the copy is
+    the calibration kernel: its bytes are known)."""
+    dev = torch.device("cuda")
+    K = N = 4096
+    w = workloads.layer_weights(2)
+    for b in workloads.SWEEP_BITS:
+        d, wt = quantize_pack(q, torch, w, b)
+        hs = [q.weight(wt["packed"].clone(), wt["scales"].clone(), wt["zeros"].clone()) for _ in range(4)]
+        for m in workloads.SWEEP_M:
+            x = torch.from_numpy(workloads.activations_fp16(m, K, workloads.seed_for(2)).view(np.int16)).to(dev)
+            y = torch.empty((m, N), dtype=torch.int16, device=dev)
+            for h in hs:
+                q.qlinear_gemv(d, h, x, K, m, y, N)
+        torch.cuda.synchronize()
+    wp, _ = workloads.prefill_weights()
+    dp, wt = quantize_pack(q, torch, wp, 4, workloads.PREFILL_OUTLIER_FRAC)
+    hp = q.weight(wt["packed"], wt["scales"], wt["zeros"], wt["rowptr"], wt["col"], wt["val"], wt["nnz"])
+    Mp, Kp, Np = workloads.PREFILL_M, workloads.PREFILL_K, workloads.PREFILL_N
+    xp = torch.from_numpy(workloads.prefill_activations().view(np.int16)).to(dev)
+    yp = torch.empty((Mp, Np), dtype=torch.int16, device=dev)
+    wsb = q.qlinear_gemm_workspace_bytes(dp, Mp, wt["nnz"])
+    wsp = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        q.qlinear_gemm(dp, hp, xp, Kp, Mp, yp, Np, wsp, wsb)
+    torch.cuda.synchronize()
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("bench: pmc pass done")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,6 +170,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=512 GEMM secondary line")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="eager launches only (each GEMV of the step, the prefill GEMM, a 1 GiB copy) for "
+                         "hardware-counter runs; prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part "
@@ -108,6 +188,10 @@ def main():
     dev = torch.device("cuda")
     K = N = 4096
     bits_list, m_list = workloads.SWEEP_BITS, workloads.SWEEP_M
+
+    if args.pmc_pass:
+        pmc_pass(q, torch, workloads)
+        return
 
     log("bench: quantize + pack 4096x4096 at 2/3/5/6 bits")
     w = workloads.layer_weights(2)
@@ -171,9 +255,10 @@ def main():
     b_dom = int(dom.split("_")[0][1:])
     dom_bytes = weight_bytes(N, K, b_dom)
     achieved = dom_bytes / (per[dom]["us"] * 1e-6) / 1e9
+    kname = f"qp::gemv_kernel<{b_dom}, 8, 1>"
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
-                    kernel=f"qp::gemv_kernel<{b_dom}, 8> ({dom})", bytes_per_launch=dom_bytes,
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(kname),
+                    kernel=f"{kname} ({dom})", bytes_per_launch=dom_bytes,
                     avg_launch_us=round(per[dom]["us"], 3))
 
     extra = {}
@@ -195,6 +280,9 @@ def main():
                                           frac_mfma_f16=round(tf / MFMA_F16_PEAK_TFLOPS, 4),
                                           flops=flops, kernel="qp::gemm_kernel<4>")
         del hp, wt, xp, yp
+
+    log("bench: 1 GiB device copy")
+    extra["copy_GBps"] = round(copy_gbps(torch), 1)
 
     cpu = None
     if not args.no_cpu:
