@@ -89,6 +89,14 @@ GEMV_SOURCES = ("weight_only_mixed_amd/csrc/qmm_small.hip", "weight_only_mixed_a
 TRAFFIC_FILE = "profiles/pmc_traffic_gemv4096_gemm_prefill.md"
 
 
+def gemv_kernel_name(bits: int, m: int, n: int) -> str:
+    """Template instance qlinear_gemv launches for (bits, m, n): gemv_kernel<B, waves, ring
+    depth, activation row pairs> (the launcher in qmm_small.hip picks them the same way)."""
+    mx = 1 if m <= 2 else 2 if m <= 4 else 4 if m <= 8 else 8
+    nw = 4 if (n // 16 >= 512 or mx == 8) else 8
+    return f"qp::gemv_kernel<{bits}, {nw}, 2, {mx}>"
+
+
 def measured_traffic(kernel: str):
     """Per-launch HBM bytes of `kernel` from the committed FETCH_SIZE/WRITE_SIZE summary, or None
     if there is none or the GEMV sources changed since the counters were taken."""
@@ -255,7 +263,7 @@ def main():
     b_dom = int(dom.split("_")[0][1:])
     dom_bytes = weight_bytes(N, K, b_dom)
     achieved = dom_bytes / (per[dom]["us"] * 1e-6) / 1e9
-    kname = f"qp::gemv_kernel<{b_dom}, 8, 1>"
+    kname = gemv_kernel_name(b_dom, int(dom.split("_m")[1]), N)
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(kname),
                     kernel=f"{kname} ({dom})", bytes_per_launch=dom_bytes,

@@ -22,6 +22,7 @@
 //
 // Workgroups are ordered so that the activation blocks of one weight tile run on the same XCD
 // (block b runs on XCD b % 8), where they share that XCD's L2 copy of the packed weights.
+#include "bufio.h"
 #include "unpack.h"
 
 namespace qp {
@@ -34,47 +35,6 @@ constexpr int kMT = 8;                       // 16-row activation tiles per work
 constexpr int kNT = kWaves * kRBW * kTileN;  // 128 weight rows per workgroup
 constexpr int kMRows = kMT * 16;             // 128 activation rows per workgroup
 constexpr int kRowBytes = 128 * 2;           // one 128-k group of one activation row
-
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-__device__ __forceinline__ float lo_h(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFF)); }
-__device__ __forceinline__ float hi_h(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
-__device__ __forceinline__ float h_f(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)v); }
-// By value on purpose: __builtin_bit_cast applied directly to a vector element (v[i]) reads
-// element 0 with this compiler.
-__device__ __forceinline__ float as_f(uint32_t v) { return __builtin_bit_cast(float, v); }
-
-__device__ __forceinline__ uint32_t pack2(float a, float b)
-{
-    const _Float16 ha = (_Float16)a, hb = (_Float16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
-}
-
-// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes return zeros.
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes)
-{
-    const int32_t n = bytes <= 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int32_t)bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
-}
-
-// Buffer loads at voffset (per lane) + soffset (wave-uniform: kept in a scalar register, so the
-// per-lane address registers stay few).
-__device__ __forceinline__ u4 ld16(rsrc_t r, uint32_t off, uint32_t soff = 0)
-{
-    return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
-}
-__device__ __forceinline__ u2 ld8(rsrc_t r, uint32_t off, uint32_t soff = 0)
-{
-    return __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0));
-}
-__device__ __forceinline__ uint32_t ld4(rsrc_t r, uint32_t off, uint32_t soff = 0)
-{
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
-}
-__device__ __forceinline__ uint32_t ld2(rsrc_t r, uint32_t off, uint32_t soff = 0)
-{
-    return __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0);
-}
 
 // LDS byte offset of 16-byte chunk c (8 k values) of activation row `row`.
 __device__ __forceinline__ int xs_off(int row, int c) { return row * kRowBytes + ((c ^ (row & 15)) << 4); }
@@ -319,7 +279,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (row >= a.m) continue;
             const f4 s = tot[u][mt];
             uint16_t *y = a.y + row * a.ldy + rb * kTileN + 4 * t;
-            *(u2 *)y = (u2){pack2(s[0], s[1]), pack2(s[2], s[3])};
+            *(u2 *)y = (u2){pack_h2(s[0], s[1]), pack_h2(s[2], s[3])};
         }
     }
 }

@@ -14,18 +14,10 @@
 // Matrix-core fragment layout (A = 16 weight rows x 32 k, B = 32 k x 16 activation rows):
 // lane l = 16*t + r supplies row r of A and column r of B for k-slots 8t..8t+7 and receives
 // D[4t + i][r], i = 0..3 (weight row 4t+i, activation row r).
+#include "bufio.h"
 #include "unpack.h"
 
 namespace qp {
-
-__device__ __forceinline__ float lo_half(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFF)); }
-__device__ __forceinline__ float hi_half(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
-
-__device__ __forceinline__ uint32_t pack_h2(float a, float b)
-{
-    const _Float16 ha = (_Float16)a, hb = (_Float16)b;  // round to nearest even
-    return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
-}
 
 // All inputs of one k-tile for one lane: packed chunk, zero points of its A row, scales of
 // its four output rows.
@@ -73,104 +65,155 @@ __device__ __forceinline__ void mma_tile(const h8 *A, const h8 *X, const uint32_
     a1 = mfma16(A[7], X[7], a1);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        tot[i] = __builtin_fmaf(lo_half(sc[i]), a0[i], tot[i]);
-        tot[i] = __builtin_fmaf(hi_half(sc[i]), a1[i], tot[i]);
+        tot[i] = __builtin_fmaf(lo_h(sc[i]), a0[i], tot[i]);
+        tot[i] = __builtin_fmaf(hi_h(sc[i]), a1[i], tot[i]);
     }
 }
 
-// ---- decode GEMV: one workgroup per 16-row block, NW waves split the k-tiles ----------
+// ---- decode GEMV: one workgroup per 16-row block, NW waves take its k-tiles round-robin --
 //
-// Decode is latency-bound at these sizes (a 4096 x 4096 layer is a few MB), so each wave
-// issues every global load it needs -- TPW weight tiles, their scales and zero points and
-// the activation fragments -- before its first unpack, and the next chunk of TPW tiles is in
-// flight while the current one is multiplied.  The NW partial sums of a row block are
-// reduced through LDS in a fixed order.
+// Decode is latency- and VALU-bound at these sizes (a 4096 x 4096 layer is a few MB).  Every
+// operand of a k-tile -- packed codes, the activation rows, scales and zero points -- is
+// copied HBM -> LDS by buffer-to-LDS DMA into a per-wave ring of D slots, issued D-1 tiles
+// ahead, so bytes in flight cost no registers and a CU holds many waves.  Each DMA reads at
+// an offset checked by its buffer range: activation rows at or beyond m read as zeros, and
+// tiles past the end of k read zeros into a slot that is never consumed, so every tile issues
+// the same number of loads and one s_waitcnt count covers the ring.  A wave then unpacks the
+// tile from LDS and multiplies it on the matrix core; lanes of activation rows >= m keep zero
+// fragments and skip their LDS reads.  The NW partial sums of a row block are reduced
+// through LDS in a fixed order, and the outlier CSR is added in fp32 before the fp16 store.
 
-template <int B, int TPW>
-struct Chunk {
-    TileIn<B> tile[TPW];
+struct GemvBufs {
+    rsrc_t w, sc, zr, x;
+    uint32_t vw, vw8, vz, vs, vx;  // per-lane offsets
+    int64_t G;
 };
 
-template <int B, int TPW>
-__device__ __forceinline__ void load_w_chunk(const ExpertPtrs &W, int64_t rb, int64_t kt0, int64_t KT,
-                                             int64_t G, int lane, Chunk<B, TPW> &c)
+template <int B, int MX>
+struct RingSlot {
+    static constexpr int kCodes = 512 * B;           // packed tile
+    static constexpr int kX = kCodes;                 // activation rows, 512 B each, 2 per DMA
+    static constexpr int kSc = kX + 1024 * MX;        // 64 lanes x 4 B (rows >= 16 read zeros)
+    static constexpr int kZr = kSc + 256;             // 64 lanes x 4 B
+    static constexpr int kBytes = kZr + 256;
+    static constexpr int kLoads = B / 2 + 2 * (B & 1) + MX + 2;  // DMA instructions per tile
+};
+
+__device__ __forceinline__ void dma16(rsrc_t r, uint8_t *lds, uint32_t voff)
 {
-#pragma unroll
-    for (int u = 0; u < TPW; ++u)
-        if (kt0 + u < KT) load_tile<B>(W, rb, kt0 + u, KT, G, lane, c.tile[u]);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(rsrc_t r, uint8_t *lds, uint32_t voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, voff, 0, 0, 0);
 }
 
-template <int TPW>
-__device__ __forceinline__ void load_x_chunk(const uint16_t *xrow, bool act, int64_t kt0, int64_t KT, int t,
-                                             h8 (&X)[TPW][8])
+template <int B, int MX>
+__device__ __forceinline__ void ring_issue(const GemvBufs &bf, int64_t kt, int lane, int64_t ldx, uint8_t *slot)
 {
+    using S = RingSlot<B, MX>;
+    const uint32_t tw = (uint32_t)(kt * (512 * B));
 #pragma unroll
-    for (int u = 0; u < TPW; ++u)
-        if (kt0 + u < KT) load_x(xrow, act, kt0 + u, t, X[u]);
-}
-
-template <int B, int TPW>
-__device__ __forceinline__ void compute_chunk(const Chunk<B, TPW> &c, const h8 (&X)[TPW][8], int64_t kt0,
-                                              int64_t KT, f4 &tot)
-{
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-        if (kt0 + u < KT) {
-            GroupConst<B> g0, g1;
-            g0.set(c.tile[u].zz & 0xFF);
-            g1.set((c.tile[u].zz >> 8) & 0xFF);
-            h8 A[8];
-            unpack_chunk<B>(c.tile[u].d, g0, g1, A);
-            mma_tile(A, X[u], c.tile[u].sc, tot);
-        }
+    for (int sl = 0; sl < B / 2; ++sl) dma16(bf.w, slot + 1024 * sl, tw + 1024 * sl + 16 * lane);
+    if (B & 1) {
+        dma4(bf.w, slot + 1024 * (B / 2), tw + 1024 * (B / 2) + 8 * lane);
+        dma4(bf.w, slot + 1024 * (B / 2) + 256, tw + 1024 * (B / 2) + 8 * lane + 4);
     }
+    const uint32_t xk = (uint32_t)(kt * (kTileK * 2));
+#pragma unroll
+    for (int q = 0; q < MX; ++q) {
+        const uint32_t row = 2 * q + (lane >> 5);
+        dma16(bf.x, slot + S::kX + 1024 * q, (uint32_t)(row * ldx * 2) + xk + 16 * (lane & 31));
+    }
+    dma4(bf.sc, slot + S::kSc, (uint32_t)((lane * bf.G + 2 * kt) * 2));
+    dma4(bf.zr, slot + S::kZr, (uint32_t)((lane * bf.G + 2 * kt) & ~(int64_t)3));
 }
 
-template <int B, int NW, int TPW>
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int B, int NW, int D, int MX>
 __global__ __launch_bounds__(NW * 64) void gemv_kernel(SmallArgs a)
 {
+    using S = RingSlot<B, MX>;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NW][D][S::kBytes];
+    __shared__ f4 red[NW][64];
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t = lane >> 4, r = lane & 15;
     const int64_t rb = blockIdx.x;
     const int64_t KT = a.k / kTileK, G = a.k / kGroup;
     const ExpertPtrs &W = a.ex[0];
+
+    GemvBufs bf;
+    bf.G = G;
+    bf.w = make_rsrc(W.packed + rb * KT * (512 * B), KT * (512 * B));
+    bf.sc = make_rsrc(W.scales + rb * kTileN * G, kTileN * G * 2);
+    bf.zr = make_rsrc(W.zeros + rb * kTileN * G, kTileN * G);
+    bf.x = make_rsrc(a.x, a.m * a.ldx * 2);  // rows >= m read as zeros
+
+    const int64_t nt = KT > wv ? (KT - wv + NW - 1) / NW : 0;  // tiles of this wave
+#pragma unroll
+    for (int s = 0; s < D - 1; ++s) ring_issue<B, MX>(bf, wv + (int64_t)s * NW, lane, a.ldx, ring[wv][s]);
+
+    // Activation fragments: lanes of rows >= m keep zeros and never read LDS.
     const bool act = r < a.m;
-    const uint16_t *xrow = a.x + (act ? r : 0) * a.ldx;
-    constexpr int STRIDE = NW * TPW;
-
+    h8 X[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) X[j] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
     f4 tot = {0.f, 0.f, 0.f, 0.f};
-    Chunk<B, TPW> ca, cb;  // weight tiles: two named buffers, used alternately
-    h8 X[TPW][8];          // activation fragments of the chunk being multiplied
-    int64_t k0 = (int64_t)wv * TPW;
-    if (k0 < KT) load_w_chunk<B, TPW>(W, rb, k0, KT, G, lane, ca);
-    while (k0 < KT) {
-        load_x_chunk<TPW>(xrow, act, k0, KT, t, X);
-        if (k0 + STRIDE < KT) load_w_chunk<B, TPW>(W, rb, k0 + STRIDE, KT, G, lane, cb);
-        compute_chunk<B, TPW>(ca, X, k0, KT, tot);
-        k0 += STRIDE;
-        if (k0 >= KT) break;
-        load_x_chunk<TPW>(xrow, act, k0, KT, t, X);
-        if (k0 + STRIDE < KT) load_w_chunk<B, TPW>(W, rb, k0 + STRIDE, KT, G, lane, ca);
-        compute_chunk<B, TPW>(cb, X, k0, KT, tot);
-        k0 += STRIDE;
+    for (int64_t i = 0; i < nt; ++i) {
+        const int64_t kt = wv + i * NW;
+        ring_issue<B, MX>(bf, kt + (int64_t)(D - 1) * NW, lane, a.ldx, ring[wv][(i + D - 1) % D]);
+        wait_vm<S::kLoads * (D - 1)>();
+        const uint8_t *slot = ring[wv][i % D];
+        uint32_t d[2 * B];
+#pragma unroll
+        for (int sl = 0; sl < B / 2; ++sl) {
+            const u4 v = *(const u4 *)(slot + 1024 * sl + 16 * lane);
+            d[4 * sl + 0] = v[0];
+            d[4 * sl + 1] = v[1];
+            d[4 * sl + 2] = v[2];
+            d[4 * sl + 3] = v[3];
+        }
+        if (B & 1) {
+            d[2 * B - 2] = *(const uint32_t *)(slot + 1024 * (B / 2) + 4 * lane);
+            d[2 * B - 1] = *(const uint32_t *)(slot + 1024 * (B / 2) + 256 + 4 * lane);
+        }
+        if (act) {
+            const uint8_t *xb = slot + S::kX + 512 * r + 16 * t;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) X[j] = *(const h8 *)(xb + 2 * (128 * (j >> 2) + 32 * (j & 3)));
+        }
+        const u4 scv = *(const u4 *)(slot + S::kSc + 16 * t);
+        const uint32_t sc[4] = {scv[0], scv[1], scv[2], scv[3]};
+        const uint32_t zpar = (uint32_t)((r * G + 2 * kt) & 3);
+        const uint32_t zz = *(const uint16_t *)(slot + S::kZr + 4 * r + zpar);
+        GroupConst<B> g0, g1;
+        g0.set(zz & 0xFF);
+        g1.set((zz >> 8) & 0xFF);
+        h8 A[8];
+        unpack_chunk<B>(d, g0, g1, A);
+        mma_tile(A, X, sc, tot);
     }
+    wait_vm<0>();  // drain the tiles issued past the end before the workgroup's LDS is released
 
-    __shared__ f4 red[NW][64];
     red[wv][lane] = tot;
     __syncthreads();
-    if (wv != 0 || !act) return;
+    if (wv != 0 || r >= a.m) return;
     f4 s = red[0][lane];
 #pragma unroll
     for (int w = 1; w < NW; ++w) s += red[w][lane];
     if (a.rowptr) {
+        const uint16_t *xrow = a.x + r * a.ldx;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t n = rb * kTileN + 4 * t + i;
-            for (int32_t p = a.rowptr[n]; p < a.rowptr[n + 1]; ++p) {
-                const float xv = (float)__builtin_bit_cast(_Float16, xrow[a.col[p]]);
-                const float wv16 = (float)__builtin_bit_cast(_Float16, a.val[p]);
-                s[i] = __builtin_fmaf(xv, wv16, s[i]);
-            }
+            for (int32_t p = a.rowptr[n]; p < a.rowptr[n + 1]; ++p)
+                s[i] = __builtin_fmaf(h_f(xrow[a.col[p]]), h_f(a.val[p]), s[i]);
         }
     }
     uint16_t *y = (uint16_t *)a.y + r * a.ldy + rb * kTileN + 4 * t;
@@ -270,12 +313,31 @@ __global__ __launch_bounds__(256) void grouped_kernel(SmallArgs a)
     }
 }
 
+template <int B, int MX>
+static hipError_t gemv_mx(const SmallArgs &a, hipStream_t st)
+{
+    // Wide matrices have row blocks enough to fill the GPU with 4-wave workgroups (more of
+    // them fit per CU); narrow ones split each row block's k over 8 waves.
+    // (Eight waves with an 8-row-pair activation ring would exceed the 160 KB of LDS.)
+    const int64_t blocks = a.n / kTileN;
+    if constexpr (MX == 8) {
+        hipLaunchKernelGGL((gemv_kernel<B, 4, 2, MX>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    } else {
+        if (blocks >= 512)
+            hipLaunchKernelGGL((gemv_kernel<B, 4, 2, MX>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+        else
+            hipLaunchKernelGGL((gemv_kernel<B, 8, 2, MX>), dim3((unsigned)blocks), dim3(512), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
 template <int B>
 static hipError_t gemv_bits(const SmallArgs &a, hipStream_t st)
 {
-    constexpr int NW = 8, TPW = 1;
-    hipLaunchKernelGGL((gemv_kernel<B, NW, TPW>), dim3((unsigned)(a.n / kTileN)), dim3(NW * 64), 0, st, a);
-    return hipGetLastError();
+    if (a.m <= 2) return gemv_mx<B, 1>(a, st);
+    if (a.m <= 4) return gemv_mx<B, 2>(a, st);
+    if (a.m <= 8) return gemv_mx<B, 4>(a, st);
+    return gemv_mx<B, 8>(a, st);
 }
 
 hipError_t launch_gemv(int bits, const SmallArgs &a, hipStream_t st)

@@ -46,10 +46,22 @@ __device__ __forceinline__ uint32_t bfi_hi(uint32_t hi_src, uint32_t lo_src)
 __device__ __forceinline__ uint32_t h2_bits(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ h2 bits_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 
-// (word & mask) | bias(1024.0 in both halves), then * mul + add, in packed fp16.
-__device__ __forceinline__ uint32_t magic_pair(uint32_t word, uint32_t mask, h2 mul, h2 add)
+// A constant the compiler keeps in a vector register.  (word & mask) | bias is then one
+// v_and_or_b32 (the bias sits in a scalar register); with both constants as literals the
+// compiler emits a separate and and or.  The empty non-volatile asm is hoisted out of loops.
+template <uint32_t M>
+__device__ __forceinline__ uint32_t vconst()
 {
-    uint32_t t = (word & mask) | 0x64006400u;
+    uint32_t v = M;
+    asm("" : "+v"(v));
+    return v;
+}
+
+// (word & MASK) | bias(1024.0 in both halves), then * mul + add, in packed fp16.
+template <uint32_t MASK>
+__device__ __forceinline__ uint32_t magic_pair(uint32_t word, h2 mul, h2 add)
+{
+    const uint32_t t = (word & vconst<MASK>()) | 0x64006400u;
     return h2_bits(__builtin_elementwise_fma(bits_h2(t), mul, add));
 }
 
@@ -101,10 +113,10 @@ template <int J> struct BlockUnpack<2, J> {
         const uint32_t xa = perm(D, D, b0 | (b1 << 8) | (b0 << 16) | (b1 << 24));
         const uint32_t xb = perm(D, D, b1 | (b1 << 8) | (b1 << 16) | (b1 << 24));
         u4 r;
-        r[0] = magic_pair(xa, 0x000C0003u, mul_const<0, 2>(), gc.add[0]);
-        r[1] = magic_pair(xa, 0x00C00030u, mul_const<4, 6>(), gc.add[1]);
-        r[2] = magic_pair(xb, 0x000C0003u, mul_const<0, 2>(), gc.add[0]);
-        r[3] = magic_pair(xb, 0x00C00030u, mul_const<4, 6>(), gc.add[1]);
+        r[0] = magic_pair<0x000C0003u>(xa, mul_const<0, 2>(), gc.add[0]);
+        r[1] = magic_pair<0x00C00030u>(xa, mul_const<4, 6>(), gc.add[1]);
+        r[2] = magic_pair<0x000C0003u>(xb, mul_const<0, 2>(), gc.add[0]);
+        r[3] = magic_pair<0x00C00030u>(xb, mul_const<4, 6>(), gc.add[1]);
         return __builtin_bit_cast(h8, r);
     }
 };
@@ -122,10 +134,10 @@ template <int J> struct BlockUnpack<3, J> {
         const uint32_t w1 = bfi_hi(v << 13, v);          // lo: v[0:16)  hi: v[3:19)
         const uint32_t w2 = bfi_hi(v << 1, v >> 12);     // lo: v[12:28) hi: v[15:31)
         u4 r;
-        r[0] = magic_pair(w1, 0x00070007u, mul_const<0, 0>(), gc.add[0]);
-        r[1] = magic_pair(w1, 0x01C001C0u, mul_const<6, 6>(), gc.add[1]);
-        r[2] = magic_pair(w2, 0x00070007u, mul_const<0, 0>(), gc.add[0]);
-        r[3] = magic_pair(w2, 0x01C001C0u, mul_const<6, 6>(), gc.add[1]);
+        r[0] = magic_pair<0x00070007u>(w1, mul_const<0, 0>(), gc.add[0]);
+        r[1] = magic_pair<0x01C001C0u>(w1, mul_const<6, 6>(), gc.add[1]);
+        r[2] = magic_pair<0x00070007u>(w2, mul_const<0, 0>(), gc.add[0]);
+        r[3] = magic_pair<0x01C001C0u>(w2, mul_const<6, 6>(), gc.add[1]);
         return __builtin_bit_cast(h8, r);
     }
 };
@@ -139,7 +151,7 @@ template <int J> struct BlockUnpack<4, J> {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t x = perm(D, D, (uint32_t)i * 0x01010101u);
-            r[i] = magic_pair(x, 0x00F0000Fu, mul_const<0, 4>(), gc.add[0]);
+            r[i] = magic_pair<0x00F0000Fu>(x, mul_const<0, 4>(), gc.add[0]);
         }
         return __builtin_bit_cast(h8, r);
     }
@@ -158,10 +170,10 @@ template <int J> struct BlockUnpack<5, J> {
         const uint32_t x2 = perm(a2, a2, 0x01000100u);
         const uint32_t x3 = perm(a3, a3, 0x01000100u);
         u4 r;
-        r[0] = magic_pair(x0, 0x03E0001Fu, mul_const<0, 5>(), gc.add[0]);
-        r[1] = magic_pair(x1, 0x03E0001Fu, mul_const<0, 5>(), gc.add[0]);
-        r[2] = magic_pair(x2, 0x03E0001Fu, mul_const<0, 5>(), gc.add[0]);
-        r[3] = magic_pair(x3, 0x03E0001Fu, mul_const<0, 5>(), gc.add[0]);
+        r[0] = magic_pair<0x03E0001Fu>(x0, mul_const<0, 5>(), gc.add[0]);
+        r[1] = magic_pair<0x03E0001Fu>(x1, mul_const<0, 5>(), gc.add[0]);
+        r[2] = magic_pair<0x03E0001Fu>(x2, mul_const<0, 5>(), gc.add[0]);
+        r[3] = magic_pair<0x03E0001Fu>(x3, mul_const<0, 5>(), gc.add[0]);
         return __builtin_bit_cast(h8, r);
     }
 };
@@ -178,10 +190,10 @@ template <int J> struct BlockUnpack<6, J> {
         const uint32_t w2 = bfi_hi(win<s + 14>(hi, lo), win<s + 24>(hi, lo));       // q4, q5
         const uint32_t w3 = bfi_hi(win<s + 26>(hi, lo), win<s + 36>(hi, lo));       // q6, q7
         u4 r;
-        r[0] = magic_pair(w0, 0x003F003Fu, mul_const<0, 0>(), gc.add[0]);
-        r[1] = magic_pair(w1, 0x003F003Fu, mul_const<0, 0>(), gc.add[0]);
-        r[2] = magic_pair(w2, 0x003F003Fu, mul_const<0, 0>(), gc.add[0]);
-        r[3] = magic_pair(w3, 0x003F003Fu, mul_const<0, 0>(), gc.add[0]);
+        r[0] = magic_pair<0x003F003Fu>(w0, mul_const<0, 0>(), gc.add[0]);
+        r[1] = magic_pair<0x003F003Fu>(w1, mul_const<0, 0>(), gc.add[0]);
+        r[2] = magic_pair<0x003F003Fu>(w2, mul_const<0, 0>(), gc.add[0]);
+        r[3] = magic_pair<0x003F003Fu>(w3, mul_const<0, 0>(), gc.add[0]);
         return __builtin_bit_cast(h8, r);
     }
 };
