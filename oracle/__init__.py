@@ -7,9 +7,10 @@ fp64 matmuls).  See the header of ``qoracle.c`` for the passages each routine fo
 
 Parity pins: every routine here is pinned by tests/test_oracle_*.py against the pages'
 printed values, closed forms, invariants and brute force on tiny inputs, except the
-device byte map (``pack_device``), which is the library's own encoding: it is pinned
-only by being a bijection on the canonical bytes plus its documented locality
-properties ("parity unpinned" against the pages, which define no device layout).
+device layout (``pack_device``), which is the library's own encoding: it is pinned by
+round trips, by its byte map being a bijection with the documented locality, and by an
+independent decoder of the documented pair rule in the tests ("parity unpinned" against
+the pages, which define no device layout).
 """
 from __future__ import annotations
 
@@ -68,6 +69,8 @@ def lib():
             getattr(L, name).argtypes = [i64, i64, i32, vp, vp]
         L.or_device_offset.restype = i64
         L.or_device_offset.argtypes = [i64, i64, i64, i32]
+        L.or_device_reorder.restype = None
+        L.or_device_reorder.argtypes = [i64, i64, i32, vp, vp, i32]
         L.or_linear.restype = None
         L.or_linear.argtypes = [i64, i64, i64, i32, vp, i64, vp, vp, vp, vp, vp, vp, vp, i64]
         L.or_moe_ffn.restype = None
@@ -190,6 +193,15 @@ def unpack_device(packed, N: int, K: int, bits: int):
 
 def device_offset(n: int, cb: int, K: int, bits: int) -> int:
     return lib().or_device_offset(n, cb, K, bits)
+
+
+def device_reorder(codes, bits: int, inverse: bool = False):
+    """Step 1 of the device layout: codes reordered inside their packing groups."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    N, K = c.shape
+    out = np.empty_like(c)
+    lib().or_device_reorder(N, K, bits, _p(c), _p(out), 1 if inverse else 0)
+    return out
 
 
 # ---- matmuls -------------------------------------------------------------------------

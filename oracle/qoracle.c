@@ -275,16 +275,60 @@ void or_unpack_canonical(int64_t N, int64_t K, int bits, const uint8_t *in, uint
 }
 
 /*
- * Device layout: a permutation of the canonical bytes (units stay whole).  It is the
- * library's own tile order, defined here from its documented statement:
- *  - 16-row x 256-k tiles, row-block major then k-tile; tile size 512*b bytes;
- *  - inside a tile, "lane" l = 16*t + r (r = row in block, t = 0..3) owns a chunk of
- *    8 blocks of 8 consecutive k (b bytes each, canonical bytes in order); block j
- *    (0..7) covers k0 = 256*kt + 128*(j/4) + 32*(j%4) + 8*t;
- *  - chunk byte c sits at 1024*(c/16) + 16*l + c%16 while c < F = 16*floor(b/2),
- *    and at 64*F + 8*l + (c-F) for the 8-byte tail of odd b.
- * Returns the byte offset of canonical byte `cb` of row `n`.
+ * Device layout: the library's own tile order, defined here from its documented statement.
+ * Three steps, each invertible:
+ *  1. value order inside packing groups.  The GPU turns two codes into one fp16 pair with a
+ *     single mask when the two sit 16 bits apart, so inside each group of G values (pair
+ *     p = values 2p and 2p+1) packed position p < G/2 holds value 2p and position G/2 + p
+ *     holds value 2p + 1.  Groups: 4 consecutive k for 6 bits (one 3-byte unit); 8
+ *     consecutive k for 3, 4 and 5 bits (one 8-k block); for 2 bits the two 8-k blocks that
+ *     start at k0 and k0 + 32 with k0 % 64 < 32 (16 values, k0.. then k0+32..);
+ *  2. canonical unit packing (LSB first, little endian) of the reordered codes;
+ *  3. a byte map of the canonical bytes (units stay whole):
+ *     - 16-row x 256-k tiles, row-block major then k-tile; tile size 512*b bytes;
+ *     - inside a tile, "lane" l = 16*t + r (r = row in block, t = 0..3) owns a chunk of
+ *       8 blocks of 8 consecutive k (b bytes each, canonical bytes in order); block j
+ *       (0..7) covers k0 = 256*kt + 128*(j/4) + 32*(j%4) + 8*t;
+ *     - chunk byte c sits at 1024*(c/16) + 16*l + c%16 while c < F = 16*floor(b/2),
+ *       and at 64*F + 8*l + (c-F) for the 8-byte tail of odd b.
  */
+static int dev_group_size(int bits) { return bits == 2 ? 16 : bits == 6 ? 4 : 8; }
+
+/* k of value i of the group that starts at k0 (k0 is the group's first k). */
+static int64_t dev_group_k(int bits, int64_t k0, int i)
+{
+    if (bits == 2) return i < 8 ? k0 + i : k0 + 32 + (i - 8);
+    return k0 + i;
+}
+
+/* Is k0 the first k of a group? */
+static int dev_group_start(int bits, int64_t k0)
+{
+    if (bits == 2) return k0 % 8 == 0 && k0 % 64 < 32;
+    return k0 % dev_group_size(bits) == 0;
+}
+
+/* Value (index inside its group) held at packed position p. */
+static int dev_group_value(int G, int p) { return p < G / 2 ? 2 * p : 2 * (p - G / 2) + 1; }
+
+/* Step 1 on a whole row-major [N][K] code array (inverse if `inverse`). */
+static void dev_reorder(int64_t N, int64_t K, int bits, const uint8_t *in, uint8_t *out, int inverse)
+{
+    int G = dev_group_size(bits);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k0 = 0; k0 < K; ++k0) {
+            if (!dev_group_start(bits, k0)) continue;
+            for (int p = 0; p < G; ++p) {
+                int64_t kp = dev_group_k(bits, k0, p), kv = dev_group_k(bits, k0, dev_group_value(G, p));
+                if (!inverse)
+                    out[n * K + kp] = in[n * K + kv];   /* position p <- value */
+                else
+                    out[n * K + kv] = in[n * K + kp];
+            }
+        }
+}
+
+/* Step 3: byte offset of canonical byte `cb` of row `n`. */
 int64_t or_device_offset(int64_t n, int64_t cb, int64_t K, int bits)
 {
     int64_t k0 = (cb / bits) * 8;          /* first k of the 8-k block holding cb */
@@ -302,16 +346,25 @@ int64_t or_device_offset(int64_t n, int64_t cb, int64_t K, int bits)
     return tile * 512 * bits + off;
 }
 
+/* Steps 1 and 2 only: the canonical bytes that step 3 moves. */
+void or_device_reorder(int64_t N, int64_t K, int bits, const uint8_t *codes, uint8_t *out, int inverse)
+{
+    dev_reorder(N, K, bits, codes, out, inverse);
+}
+
 int or_pack_device(int64_t N, int64_t K, int bits, const uint8_t *codes, uint8_t *out)
 {
     if (N % 16 != 0 || K % 256 != 0) return 2;
     int64_t rowbytes = K * bits / 8;
+    uint8_t *perm = (uint8_t *)malloc((size_t)(N * K));
     uint8_t *canon = (uint8_t *)malloc((size_t)(N * rowbytes));
-    or_pack_canonical(N, K, bits, codes, canon);
+    dev_reorder(N, K, bits, codes, perm, 0);
+    or_pack_canonical(N, K, bits, perm, canon);
     for (int64_t n = 0; n < N; ++n)
         for (int64_t cb = 0; cb < rowbytes; ++cb)
             out[or_device_offset(n, cb, K, bits)] = canon[n * rowbytes + cb];
     free(canon);
+    free(perm);
     return 0;
 }
 
@@ -320,10 +373,13 @@ int or_unpack_device(int64_t N, int64_t K, int bits, const uint8_t *in, uint8_t 
     if (N % 16 != 0 || K % 256 != 0) return 2;
     int64_t rowbytes = K * bits / 8;
     uint8_t *canon = (uint8_t *)malloc((size_t)(N * rowbytes));
+    uint8_t *perm = (uint8_t *)malloc((size_t)(N * K));
     for (int64_t n = 0; n < N; ++n)
         for (int64_t cb = 0; cb < rowbytes; ++cb)
             canon[n * rowbytes + cb] = in[or_device_offset(n, cb, K, bits)];
-    or_unpack_canonical(N, K, bits, canon, codes);
+    or_unpack_canonical(N, K, bits, canon, perm);
+    dev_reorder(N, K, bits, perm, codes, 1);
+    free(perm);
     free(canon);
     return 0;
 }

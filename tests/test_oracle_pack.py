@@ -99,9 +99,10 @@ def test_random_forty_bit_roundtrip():
 
 
 @pytest.mark.parametrize("bits", BITS)
-def test_device_layout_is_a_byte_permutation(bits):
-    """The device layout moves whole canonical bytes (so every page unit stays intact)
-    and keeps each 16-row x 256-k tile in its own 512*b byte range."""
+def test_device_layout_byte_map(bits):
+    """The byte map of the device layout moves whole canonical bytes of the group-reordered
+    codes (so every page unit stays intact) and keeps each 16-row x 256-k tile in its own
+    512*b byte range; the reordering is a permutation inside each group."""
     N, K = 32, 512
     rowbytes = K * bits // 8
     offs = np.array([[oracle.device_offset(n, cb, K, bits) for cb in range(rowbytes)]
@@ -114,10 +115,56 @@ def test_device_layout_is_a_byte_permutation(bits):
             assert tile * 512 * bits <= offs[n, cb] < (tile + 1) * 512 * bits
     rng = np.random.default_rng(bits)
     codes = rng.integers(0, 1 << bits, (N, K)).astype(np.uint8)
+    reord = oracle.device_reorder(codes, bits)
+    assert np.array_equal(np.sort(reord, axis=1), np.sort(codes, axis=1))
+    assert np.array_equal(oracle.device_reorder(reord, bits, inverse=True), codes)
     dev = oracle.pack_device(codes, bits)
-    can = oracle.pack_canonical(codes, bits)
-    assert np.array_equal(dev[offs.reshape(-1)], can)
+    assert np.array_equal(dev[offs.reshape(-1)], oracle.pack_canonical(reord, bits))
     assert np.array_equal(oracle.unpack_device(dev, N, K, bits), codes)
+
+
+# Distance in bits between the two values of a pair (G/2 values of b bits).
+PAIR_GAP = {2: 16, 3: 12, 4: 16, 5: 20, 6: 12}
+
+
+def chunk_int(dev, bits, tile, lane):
+    """The lane's 8*b chunk bytes (documented offsets) as one little-endian integer."""
+    F = 16 * (bits // 2)
+    base = tile * 512 * bits
+    by = [dev[base + (1024 * (c // 16) + 16 * lane + c % 16 if c < F else 64 * F + 8 * lane + (c - F))]
+          for c in range(8 * bits)]
+    return int.from_bytes(bytes(by), "little")
+
+
+def pair_position(bits, j, i):
+    """Chunk bit of the low value of pair i (values 2i, 2i+1) of block j."""
+    if bits == 2:
+        return 32 * (j // 2) + 2 * (4 * (j % 2) + i)
+    if bits == 6:
+        return 48 * j + 24 * (i // 2) + 6 * (i % 2)
+    return 8 * bits * j + bits * i
+
+
+@pytest.mark.parametrize("bits", BITS)
+def test_device_layout_pair_rule(bits):
+    """Independent decoder of the documented rule the GPU unpack relies on: the values 2i and
+    2i+1 of every 8-k block sit PAIR_GAP bits apart in the lane chunk, so one mask yields an
+    fp16 pair.  Checked value by value against the codes."""
+    N, K = 16, 512
+    rng = np.random.default_rng(100 + bits)
+    codes = rng.integers(0, 1 << bits, (N, K)).astype(np.uint8)
+    dev = oracle.pack_device(codes, bits)
+    mask = (1 << bits) - 1
+    for kt in range(K // 256):
+        for lane in range(64):
+            t, r = lane // 16, lane % 16
+            v = chunk_int(dev, bits, kt, lane)
+            for j in range(8):
+                k0 = 256 * kt + 128 * (j // 4) + 32 * (j % 4) + 8 * t
+                for i in range(4):
+                    p = pair_position(bits, j, i)
+                    assert (v >> p) & mask == codes[r, k0 + 2 * i]
+                    assert (v >> (p + PAIR_GAP[bits])) & mask == codes[r, k0 + 2 * i + 1]
 
 
 def test_device_layout_lane_chunks():

@@ -1,12 +1,16 @@
 // Register-level unpack of the device layout into fp16 matrix-core operands.
 //
 // One lane of a wave holds, per 16-row x 256-k tile, a chunk of eight 8-k blocks of one
-// weight row (b bytes each; the canonical page units kept whole).  Block j feeds matrix-core
-// step j as the lane's eight A-operand values, in k order.  A value (q - zp) is produced in
-// fp16 exactly with the exponent-bias trick: OR-ing a code that sits at bit offset p < 10 of
-// a 16-bit half into the pattern of 1024.0 gives 1024 + 2^p*q exactly, and one packed fma
-// (x * 2^-p - 1024*2^-p - zp) leaves q - zp, an exact small integer.  Both halves of a
-// 32-bit word are converted by one and-or plus one packed fma; each half has its own offset.
+// weight row (b bytes each).  Block j feeds matrix-core step j as the lane's eight A-operand
+// values, in k order.  A value (q - zp) is produced in fp16 exactly with the exponent-bias
+// trick: OR-ing a code that sits at bit offset p (p + b <= 10) of a 16-bit half into the
+// pattern of 1024.0 gives 1024 + 2^p*q exactly, and one packed fma
+// (x * 2^-p - 1024*2^-p - zp) leaves q - zp, an exact small integer.  The device layout
+// orders the values inside each packing group so that the two values of every pair
+// (2i, 2i+1) of a block sit G/2*b bits apart in the chunk (16, 12, 16, 20, 12 bits for
+// b = 2..6); one 32-bit window of the chunk then puts value 2i in the low half and value
+// 2i+1 in the high half, each at an offset the bias trick accepts, and the pair costs one
+// window (shift or v_alignbit_b32, shared where possible), one and-or and one packed fma.
 // The per-group scale is applied later in fp32 (the mixed-bit page, s4.2, requires the
 // scale multiply and the accumulation in fp32).
 #pragma once
@@ -14,34 +18,6 @@
 #include "qp_internal.h"
 
 namespace qp {
-
-__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
-{
-    return __builtin_amdgcn_perm(hi, lo, sel);
-}
-
-// Bits [A, A+32) of the 64-bit value {hi, lo} (zeros above bit 63), A compile-time.
-// Written with v_alignbit_b32 rather than 64-bit shifts: the compiler may fuse a 64-bit
-// shift of two adjacent array elements into one 64-bit access, which keeps the register
-// array from being split into registers.
-template <int A>
-__device__ __forceinline__ uint32_t win(uint32_t hi, uint32_t lo)
-{
-    static_assert(A >= 0 && A < 64, "window offset");
-    if constexpr (A == 0)
-        return lo;
-    else if constexpr (A < 32)
-        return __builtin_amdgcn_alignbit(hi, lo, A);
-    else if constexpr (A == 32)
-        return hi;
-    else
-        return hi >> (A - 32);
-}
-
-__device__ __forceinline__ uint32_t bfi_hi(uint32_t hi_src, uint32_t lo_src)
-{
-    return (hi_src & 0xFFFF0000u) | (lo_src & 0x0000FFFFu);
-}
 
 __device__ __forceinline__ uint32_t h2_bits(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ h2 bits_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
@@ -71,14 +47,60 @@ __device__ __forceinline__ h2 add_const(float clo, float chi, float zp)
     return __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(clo - zp, chi - zp));
 }
 
-// Per-bitwidth pair offsets.  For each pair v (values 2v, 2v+1 of a block) the low half
-// carries value 2v at offset PLO and the high half value 2v+1 at offset PHI.
+template <int plo, int phi>
+__device__ __forceinline__ h2 mul_const()
+{
+    h2 m;
+    m[0] = (_Float16)(1.0f / (float)(1 << plo));
+    m[1] = (_Float16)(1.0f / (float)(1 << phi));
+    return m;
+}
+
+// 32 bits of a lane chunk d[0..NDW) starting at chunk bit ABS (ABS may be negative: the
+// missing low bits are zeros; bits past the chunk end are zeros).
+template <int ABS, int NDW>
+__device__ __forceinline__ uint32_t window(const uint32_t *d)
+{
+    if constexpr (ABS < 0) {
+        return d[0] << (-ABS);
+    } else {
+        constexpr int w = ABS / 32, o = ABS % 32;
+        if constexpr (o == 0)
+            return d[w];
+        else if constexpr (w + 1 < NDW)
+            return __builtin_amdgcn_alignbit(d[w + 1], d[w], o);
+        else
+            return d[w] >> o;
+    }
+}
+
+// Where pair i (values 2i, 2i+1) of block J lives: the window start ABS (chunk bit), the
+// value offsets PLO (low half) and PHI (high half) inside the window, and the index of the
+// group constant (one per distinct offset pair).
+template <int B, int J, int I> struct PairRule;
+template <int J, int I> struct PairRule<2, J, I> {   // lo at 32*(J/2) + 8*(J%2) + 2I, gap 16
+    static constexpr int ABS = 32 * (J / 2) + 8 * (J % 2), PLO = 2 * I, PHI = 2 * I, C = I;
+};
+template <int J, int I> struct PairRule<3, J, I> {   // lo at 24J + 3I, gap 12
+    static constexpr int ABS = 24 * J + 3 * I - 4, PLO = 4, PHI = 0, C = 0;
+};
+template <int J, int I> struct PairRule<4, J, I> {   // lo at 32J + 4I, gap 16
+    static constexpr int ABS = 32 * J + 8 * (I / 2), PLO = 4 * (I % 2), PHI = 4 * (I % 2), C = I % 2;
+};
+template <int J, int I> struct PairRule<5, J, I> {   // lo at 40J + 5I, gap 20
+    static constexpr int ABS = 40 * J + 5 * I, PLO = 0, PHI = 4, C = 0;
+};
+template <int J, int I> struct PairRule<6, J, I> {   // lo at 48J + 24(I/2) + 6(I%2), gap 12
+    static constexpr int ABS = 48 * J + 24 * (I / 2) + 6 * (I % 2) - 4, PLO = 4, PHI = 0, C = 0;
+};
+
+// Number of distinct (PLO, PHI) pairs per bit width, and pair c's offsets.
 template <int B> struct Offsets;
-template <> struct Offsets<2> { static constexpr int n = 2; static constexpr int plo[2] = {0, 4}; static constexpr int phi[2] = {2, 6}; };
-template <> struct Offsets<3> { static constexpr int n = 2; static constexpr int plo[2] = {0, 6}; static constexpr int phi[2] = {0, 6}; };
-template <> struct Offsets<4> { static constexpr int n = 1; static constexpr int plo[1] = {0}; static constexpr int phi[1] = {4}; };
-template <> struct Offsets<5> { static constexpr int n = 1; static constexpr int plo[1] = {0}; static constexpr int phi[1] = {5}; };
-template <> struct Offsets<6> { static constexpr int n = 1; static constexpr int plo[1] = {0}; static constexpr int phi[1] = {0}; };
+template <> struct Offsets<2> { static constexpr int n = 4; static constexpr int plo[4] = {0, 2, 4, 6}; static constexpr int phi[4] = {0, 2, 4, 6}; };
+template <> struct Offsets<3> { static constexpr int n = 1; static constexpr int plo[1] = {4}; static constexpr int phi[1] = {0}; };
+template <> struct Offsets<4> { static constexpr int n = 2; static constexpr int plo[2] = {0, 4}; static constexpr int phi[2] = {0, 4}; };
+template <> struct Offsets<5> { static constexpr int n = 1; static constexpr int plo[1] = {0}; static constexpr int phi[1] = {4}; };
+template <> struct Offsets<6> { static constexpr int n = 1; static constexpr int plo[1] = {4}; static constexpr int phi[1] = {0}; };
 
 template <int B> struct GroupConst {
     h2 add[Offsets<B>::n];
@@ -92,108 +114,25 @@ template <int B> struct GroupConst {
     }
 };
 
-template <int plo, int phi>
-__device__ __forceinline__ h2 mul_const()
+template <int B, int J, int I>
+__device__ __forceinline__ uint32_t unpack_pair(const uint32_t *d, const GroupConst<B> &gc)
 {
-    h2 m;
-    m[0] = (_Float16)(1.0f / (float)(1 << plo));
-    m[1] = (_Float16)(1.0f / (float)(1 << phi));
-    return m;
+    using R = PairRule<B, J, I>;
+    static_assert(R::PLO + B <= 10 && R::PHI + B <= 10, "field must stay inside the fp16 mantissa");
+    static_assert(Offsets<B>::plo[R::C] == R::PLO && Offsets<B>::phi[R::C] == R::PHI, "offset table");
+    constexpr uint32_t mask = (((1u << B) - 1) << R::PLO) | (((1u << B) - 1) << (16 + R::PHI));
+    return magic_pair<mask>(window<R::ABS, 2 * B>(d), mul_const<R::PLO, R::PHI>(), gc.add[R::C]);
 }
 
 // Unpack block J (0..7) of a lane chunk d[2*B] into 8 fp16 values (q - zp), k order.
-template <int B, int J> struct BlockUnpack;
-
-// 2-bit: block = bytes 2J, 2J+1 (dword J/2); value i at bit 2i of the 16-bit block.
-template <int J> struct BlockUnpack<2, J> {
-    static __device__ __forceinline__ h8 run(const uint32_t *d, const GroupConst<2> &gc)
+template <int B, int J> struct BlockUnpack {
+    static __device__ __forceinline__ h8 run(const uint32_t *d, const GroupConst<B> &gc)
     {
-        const uint32_t D = d[J / 2];
-        constexpr uint32_t b0 = 2 * (J % 2), b1 = b0 + 1;
-        const uint32_t xa = perm(D, D, b0 | (b1 << 8) | (b0 << 16) | (b1 << 24));
-        const uint32_t xb = perm(D, D, b1 | (b1 << 8) | (b1 << 16) | (b1 << 24));
         u4 r;
-        r[0] = magic_pair<0x000C0003u>(xa, mul_const<0, 2>(), gc.add[0]);
-        r[1] = magic_pair<0x00C00030u>(xa, mul_const<4, 6>(), gc.add[1]);
-        r[2] = magic_pair<0x000C0003u>(xb, mul_const<0, 2>(), gc.add[0]);
-        r[3] = magic_pair<0x00C00030u>(xb, mul_const<4, 6>(), gc.add[1]);
-        return __builtin_bit_cast(h8, r);
-    }
-};
-
-// 3-bit: block = one 3-byte unit at chunk byte 3J; value i at bit 3i.
-template <int J> struct BlockUnpack<3, J> {
-    static __device__ __forceinline__ h8 run(const uint32_t *d, const GroupConst<3> &gc)
-    {
-        constexpr int c = 3 * J, w = c / 4, s = 8 * (c % 4);
-        uint32_t v;
-        if constexpr ((c % 4) + 3 <= 4)
-            v = d[w] >> s;                 // unit inside one dword
-        else
-            v = win<s>(d[w + 1], d[w]);    // unit straddles two dwords
-        const uint32_t w1 = bfi_hi(v << 13, v);          // lo: v[0:16)  hi: v[3:19)
-        const uint32_t w2 = bfi_hi(v << 1, v >> 12);     // lo: v[12:28) hi: v[15:31)
-        u4 r;
-        r[0] = magic_pair<0x00070007u>(w1, mul_const<0, 0>(), gc.add[0]);
-        r[1] = magic_pair<0x01C001C0u>(w1, mul_const<6, 6>(), gc.add[1]);
-        r[2] = magic_pair<0x00070007u>(w2, mul_const<0, 0>(), gc.add[0]);
-        r[3] = magic_pair<0x01C001C0u>(w2, mul_const<6, 6>(), gc.add[1]);
-        return __builtin_bit_cast(h8, r);
-    }
-};
-
-// 4-bit: block = dword J; value i at bit 4i (low nibble first).
-template <int J> struct BlockUnpack<4, J> {
-    static __device__ __forceinline__ h8 run(const uint32_t *d, const GroupConst<4> &gc)
-    {
-        const uint32_t D = d[J];
-        u4 r;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t x = perm(D, D, (uint32_t)i * 0x01010101u);
-            r[i] = magic_pair<0x00F0000Fu>(x, mul_const<0, 4>(), gc.add[0]);
-        }
-        return __builtin_bit_cast(h8, r);
-    }
-};
-
-// 5-bit: block = one 5-byte unit at chunk byte 5J; value i at bit 5i of 40 bits.
-template <int J> struct BlockUnpack<5, J> {
-    static __device__ __forceinline__ h8 run(const uint32_t *d, const GroupConst<5> &gc)
-    {
-        constexpr int c = 5 * J, w = c / 4, o = c % 4, s = 8 * o;
-        const uint32_t lo = d[w], hi = d[w + 1];
-        constexpr uint32_t sel = o | ((o + 1) << 8) | (o << 16) | ((o + 1) << 24);
-        const uint32_t x0 = perm(hi, lo, sel);           // both halves: v[0:16)
-        const uint32_t a1 = win<s + 10>(hi, lo), a2 = win<s + 20>(hi, lo), a3 = win<s + 30>(hi, lo);
-        const uint32_t x1 = perm(a1, a1, 0x01000100u);
-        const uint32_t x2 = perm(a2, a2, 0x01000100u);
-        const uint32_t x3 = perm(a3, a3, 0x01000100u);
-        u4 r;
-        r[0] = magic_pair<0x03E0001Fu>(x0, mul_const<0, 5>(), gc.add[0]);
-        r[1] = magic_pair<0x03E0001Fu>(x1, mul_const<0, 5>(), gc.add[0]);
-        r[2] = magic_pair<0x03E0001Fu>(x2, mul_const<0, 5>(), gc.add[0]);
-        r[3] = magic_pair<0x03E0001Fu>(x3, mul_const<0, 5>(), gc.add[0]);
-        return __builtin_bit_cast(h8, r);
-    }
-};
-
-// 6-bit: block = two 3-byte units at chunk byte 6J; value i at bit 6i of 48 bits.
-template <int J> struct BlockUnpack<6, J> {
-    static __device__ __forceinline__ h8 run(const uint32_t *d, const GroupConst<6> &gc)
-    {
-        constexpr int c = 6 * J, w = c / 4, s = 8 * (c % 4);
-        const uint32_t lo = d[w], hi = d[w + 1];
-        const uint32_t v0 = win<s>(hi, lo);
-        const uint32_t w0 = bfi_hi(v0 << 10, v0);                                  // q0, q1
-        const uint32_t w1 = bfi_hi(win<s + 2>(hi, lo), win<s + 12>(hi, lo));        // q2, q3
-        const uint32_t w2 = bfi_hi(win<s + 14>(hi, lo), win<s + 24>(hi, lo));       // q4, q5
-        const uint32_t w3 = bfi_hi(win<s + 26>(hi, lo), win<s + 36>(hi, lo));       // q6, q7
-        u4 r;
-        r[0] = magic_pair<0x003F003Fu>(w0, mul_const<0, 0>(), gc.add[0]);
-        r[1] = magic_pair<0x003F003Fu>(w1, mul_const<0, 0>(), gc.add[0]);
-        r[2] = magic_pair<0x003F003Fu>(w2, mul_const<0, 0>(), gc.add[0]);
-        r[3] = magic_pair<0x003F003Fu>(w3, mul_const<0, 0>(), gc.add[0]);
+        r[0] = unpack_pair<B, J, 0>(d, gc);
+        r[1] = unpack_pair<B, J, 1>(d, gc);
+        r[2] = unpack_pair<B, J, 2>(d, gc);
+        r[3] = unpack_pair<B, J, 3>(d, gc);
         return __builtin_bit_cast(h8, r);
     }
 };
