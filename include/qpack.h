@@ -56,14 +56,20 @@ typedef enum {
  * QP_LAYOUT_CANONICAL: row n occupies k*bits/8 bytes; row n's codes in k order are cut into
  *   page units (u values per unit: 4, 8, 2, 8, 4 for b = 2, 3, 4, 5, 6); value i of a unit is
  *   bits [b*i, b*i+b) of the little-endian integer formed by the unit's bytes.
- * QP_LAYOUT_DEVICE: a permutation of the canonical bytes that keeps every unit whole and
- *   stores the matrix as 16-row x 256-k tiles (row-block major, then k-tile; 512*b bytes per
- *   tile).  In a tile, lane l = 16*t + r (r = row in the block, t = 0..3) owns a chunk of
- *   eight 8-k blocks of row r -- block j (0..7) starts at k0 = 256*kt + 128*(j/4) +
- *   32*(j%4) + 8*t and is b canonical bytes -- and chunk byte c is stored at
- *   1024*(c/16) + 16*l + c%16 while c < F = 16*floor(b/2), else at 64*F + 8*l + (c-F).
- *   Each lane's chunk is what one wave lane feeds to eight 16x16x32 matrix-core steps.
- *   Requires n % 16 == 0 and k % 256 == 0. */
+ * QP_LAYOUT_DEVICE: the canonical packing of reordered codes, with its bytes moved to a
+ *   tile order (units stay whole).
+ *   1. Inside each packing group of G values, packed position p < G/2 holds value 2p and
+ *      position G/2 + p holds value 2p + 1, so the two values of every pair are G/2*b bits
+ *      apart.  Groups: 4 consecutive k (6-bit), 8 consecutive k (3-, 4-, 5-bit), the two
+ *      8-k blocks at k0 and k0 + 32 with k0 % 64 < 32 (2-bit, 16 values).
+ *   2. Canonical unit packing of the reordered codes (as QP_LAYOUT_CANONICAL).
+ *   3. 16-row x 256-k tiles (row-block major, then k-tile; 512*b bytes per tile).  In a tile,
+ *      lane l = 16*t + r (r = row in the block, t = 0..3) owns a chunk of eight 8-k blocks
+ *      of row r -- block j (0..7) starts at k0 = 256*kt + 128*(j/4) + 32*(j%4) + 8*t and is
+ *      b bytes -- and chunk byte c is stored at 1024*(c/16) + 16*l + c%16 while
+ *      c < F = 16*floor(b/2), else at 64*F + 8*l + (c-F).
+ *   Each lane's chunk is what one wave lane feeds to eight 16x16x32 matrix-core steps; one
+ *   mask extracts a pair of values as an fp16 pair.  Requires n % 16 == 0, k % 256 == 0. */
 enum { QP_LAYOUT_CANONICAL = 0, QP_LAYOUT_DEVICE = 1 };
 
 /* Epilogues of qlinear_grouped_gemm. */
