@@ -169,6 +169,91 @@ def pmc_pass(q, torch, workloads):
     log("bench: pmc pass done")
 
 
+def clone_weight(torch, wt):
+    return dict(packed=wt["packed"].clone(), scales=wt["scales"].clone(), zeros=wt["zeros"].clone())
+
+
+def bench_stack(q, torch, workloads, stream, reps: int = 20):
+    """Llama-7B-shaped 32-layer decode stack at M=1 (224 GEMVs per token, mixed bit table).
+    One quantized template per (shape, bits) class, cloned so every matrix has its own HBM
+    bytes (2.96 GB in total); one token = the 224 calls in layer order, one HIP graph."""
+    dev = torch.device("cuda")
+    templates, mats, total = {}, [], 0
+    for layer in range(workloads.STACK_LAYERS):
+        for name in workloads.LLAMA_MATRICES:
+            n, k = workloads.STACK_SHAPES[name]
+            b = workloads.stack_bits(layer, name)
+            key = (n, k, b)
+            if key not in templates:
+                w = workloads.weights_fp16(n, k, workloads.stack_matrix_seed(layer, name))
+                templates[key] = quantize_pack(q, torch, w, b)
+            d, wt = templates[key]
+            c = clone_weight(torch, wt)
+            mats.append((d, q.weight(c["packed"], c["scales"], c["zeros"]), c, n, k))
+            total += weight_bytes(n, k, b)
+    xs = {k: torch.from_numpy(workloads.activations_fp16(1, k, workloads.seed_for(3)).view(np.int16)).to(dev)
+          for k in (4096, 11008)}
+    ys = {n: torch.empty((1, n), dtype=torch.int16, device=dev) for n in (4096, 11008)}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for d, h, _, n, k in mats:
+            q.qlinear_gemv(d, h, xs[k], k, 1, ys[n], n)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    gbps = total / (us * 1e-6) / 1e9
+    bits_avg = sum(workloads.stack_bits(l, nm) * workloads.STACK_SHAPES[nm][0] * workloads.STACK_SHAPES[nm][1]
+                   for l in range(workloads.STACK_LAYERS) for nm in workloads.LLAMA_MATRICES) / \
+        sum(workloads.STACK_SHAPES[nm][0] * workloads.STACK_SHAPES[nm][1]
+            for nm in workloads.LLAMA_MATRICES) / workloads.STACK_LAYERS
+    del mats, templates
+    return dict(us_per_token=round(us, 1), GBps=round(gbps, 1), frac_hbm_peak=round(gbps / HBM_PEAK_GBS, 4),
+                bytes_per_token=total, launches_per_token=7 * workloads.STACK_LAYERS, avg_bits=round(bits_avg, 3))
+
+
+def bench_moe(q, torch, workloads, stream, reps: int = 20):
+    """Routed-expert FFN: 16 experts x (gate, up 14336x4096; down 4096x14336), 4-bit, 128 tokens
+    top-2 with Zipf(1.1) routing, one qmoe_ffn call.  One quantized template per matrix kind,
+    cloned per expert (1.48 GB of expert weights); gate and up rows interleaved per 16-row block
+    for the SwiGLU epilogue."""
+    dev = torch.device("cuda")
+    E, D, F, T, K = (workloads.MOE_EXPERTS, workloads.MOE_DMODEL, workloads.MOE_DFF, workloads.MOE_TOKENS,
+                     workloads.MOE_TOPK)
+    g, u, dn = workloads.moe_expert(0)
+    gu = workloads.interleave_row_blocks(g, u, 16)
+    d_gu, t_gu = quantize_pack(q, torch, gu, 4)
+    d_dn, t_dn = quantize_pack(q, torch, dn, 4)
+    del g, u, dn, gu
+    keep, h_gu, h_dn = [], [], []
+    for _ in range(E):
+        a, b = clone_weight(torch, t_gu), clone_weight(torch, t_dn)
+        keep += [a, b]
+        h_gu.append(q.weight(a["packed"], a["scales"], a["zeros"]))
+        h_dn.append(q.weight(b["packed"], b["scales"], b["zeros"]))
+    x, ids, wts = workloads.moe_inputs()
+    xd = torch.from_numpy(x.view(np.int16)).to(dev)
+    idd = torch.from_numpy(ids.astype(np.int32)).to(dev)
+    wtd = torch.from_numpy(wts.astype(np.float32)).to(dev)
+    out = torch.empty((T, D), dtype=torch.int16, device=dev)
+    wsb = q.qmoe_ffn_workspace_bytes(T, K, E, D, F)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    fn = lambda i: q.qmoe_ffn(d_gu, h_gu, d_dn, h_dn, xd, D, T, idd, wtd, K, out, D, ws, wsb)
+    ms = time_graph(torch, fn, reps, stream)
+    active = int((np.bincount(ids.ravel(), minlength=E) > 0).sum())
+    wbytes = active * (weight_bytes(2 * F, D, 4) + weight_bytes(D, F, 4))
+    flops = 2 * T * K * (2 * F * D + D * F)
+    return dict(us=round(ms * 1e3, 1), GBps=round(wbytes / (ms * 1e-3) / 1e9, 1),
+                frac_hbm_peak=round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                TFLOPs=round(flops / (ms * 1e-3) / 1e12, 2), active_experts=active, weight_bytes=wbytes)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +262,8 @@ def main():
     ap.add_argument("--copies", type=int, default=32, help="rotating weight copies (>= 1 GB total)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=512 GEMM secondary line")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 32-layer decode stack line")
+    ap.add_argument("--no-moe", action="store_true", help="skip the routed-expert FFN line")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--pmc-pass", action="store_true",
                     help="eager launches only (each GEMV of the step, the prefill GEMM, a 1 GiB copy) for "
@@ -288,6 +375,26 @@ def main():
                                           frac_mfma_f16=round(tf / MFMA_F16_PEAK_TFLOPS, 4),
                                           flops=flops, kernel="qp::gemm_kernel<4>")
         del hp, wt, xp, yp
+
+    log("bench: 4096x4096 4-bit GEMV at M=1")
+    d4, w4 = quantize_pack(q, torch, workloads.layer_weights(1), 4)
+    c4 = [clone_weight(torch, w4) for _ in range(args.copies)]
+    h4 = [q.weight(c["packed"], c["scales"], c["zeros"]) for c in c4]
+    x1 = torch.from_numpy(workloads.activations_fp16(1, K, workloads.seed_for(1)).view(np.int16)).to(dev)
+    y1 = torch.empty((1, N), dtype=torch.int16, device=dev)
+    ms4 = time_graph(torch, lambda i: q.qlinear_gemv(d4, h4[i % args.copies], x1, K, 1, y1, N), 4 * args.copies,
+                     stream)
+    b4 = weight_bytes(N, K, 4)
+    extra["gemv_4096_4bit_m1"] = dict(us=round(ms4 * 1e3, 3), GBps=round(b4 / (ms4 * 1e-3) / 1e9, 1),
+                                      frac_hbm_peak=round(b4 / (ms4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                      kernel=gemv_kernel_name(4, 1, N))
+    del c4, h4, w4
+    if not args.no_stack:
+        log("bench: Llama-7B-shaped 32-layer decode stack at M=1")
+        extra["stack_llama7b_m1"] = bench_stack(q, torch, workloads, stream)
+    if not args.no_moe:
+        log("bench: routed-expert FFN, 16 experts, 128 tokens top-2")
+        extra["moe_16x_ffn_t128"] = bench_moe(q, torch, workloads, stream)
 
     log("bench: 1 GiB device copy")
     extra["copy_GBps"] = round(copy_gbps(torch), 1)

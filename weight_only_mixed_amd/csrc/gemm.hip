@@ -2,15 +2,15 @@
 //
 // Prior art: the fused dequant-GEMM of the single-GPU 70B page (s3) loads an INT4 tile into
 // shared memory, dequantizes it and feeds Tensor Cores.  On CDNA4 the roles are split
-// differently.  Each wave owns RBW 16-row weight blocks: it loads their packed tiles with
-// 16-byte loads straight into registers (double-buffered across k-tiles) and unpacks them into
-// exact fp16 (q - zp) A operands itself, so weights never pass through LDS and each weight is
-// unpacked once per 128-row activation block.  The activation tile (128 rows x one 128-k
-// group, 32 KB) is shared by the four waves through LDS: it is loaded with buffer-to-LDS DMA
-// (no registers), double-buffered, with the 16-byte chunks of each row XOR-swizzled by the row
-// index so the matrix-core fragment reads (16 rows, same column) hit distinct banks.  Every
-// 128-k group is accumulated on the matrix cores in fp32 and then scaled by its fp16 scale in
-// fp32.
+// differently.  Each of the eight waves of a workgroup owns two 16-row weight blocks: it loads
+// their packed tiles with 16-byte loads straight into registers (one k-tile ahead) and unpacks
+// them into exact fp16 (q - zp) A operands itself, so weights never pass through LDS and each
+// weight is unpacked once per 128-row activation block.  The activation tile (128 rows x one
+// 128-k group, 32 KB) is shared by the eight waves (256 weight rows) through a four-slot LDS
+// ring filled by buffer-to-LDS DMA three groups ahead (no registers), with the 16-byte chunks
+// of each row XOR-swizzled by the row index so the matrix-core fragment reads (16 rows, same
+// column) hit distinct banks.  Every 128-k group is accumulated on the matrix cores in fp32
+// and then scaled by its fp16 scale in fp32.
 //
 // Outlier add-back (70B page, s2): the held-out fp16 weights are added in fp32 before the one
 // fp16 rounding of y.  Two small kernels run first: one writes x transposed (x^T) into the
@@ -29,19 +29,22 @@ namespace qp {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kRBW = 2;                      // 16-row weight blocks per wave
 constexpr int kMT = 8;                       // 16-row activation tiles per workgroup
-constexpr int kNT = kWaves * kRBW * kTileN;  // 128 weight rows per workgroup
+constexpr int kNT = kWaves * kRBW * kTileN;  // 256 weight rows per workgroup
+constexpr int kRing = 4;                     // activation ring slots
+constexpr int kAhead = kRing - 1;            // groups the activation DMA runs ahead
+constexpr int kDmaOps = 4;                   // DMA instructions per wave per group
 constexpr int kMRows = kMT * 16;             // 128 activation rows per workgroup
 constexpr int kRowBytes = 128 * 2;           // one 128-k group of one activation row
 
 // LDS byte offset of 16-byte chunk c (8 k values) of activation row `row`.
 __device__ __forceinline__ int xs_off(int row, int c) { return row * kRowBytes + ((c ^ (row & 15)) << 4); }
 
-// Shared memory of one workgroup: the activation tiles (double buffer).
+// Shared memory of one workgroup: the activation ring.
 struct Smem {
-    uint8_t xs[2][kMRows * kRowBytes];
+    uint8_t xs[kRing][kMRows * kRowBytes];
 };
 
 // Buffers of one workgroup.  Every wave-uniform offset passed as soffset stays inside the
@@ -51,26 +54,35 @@ struct Bufs {
     rsrc_t x;              // activation rows [m0, m)
     rsrc_t w[kRBW];        // packed tiles of row block rb0 + u (empty past the last block)
     rsrc_t sc[kRBW], zr[kRBW];
-    uint32_t xoff[8];      // this lane's source of LDS-DMA piece it (row offset + chunk)
+    uint32_t xoff[kDmaOps];  // this lane's source of LDS-DMA piece it (row offset + chunk)
 };
 
-// DMA the 128 x 128-k activation tile of group g into LDS buffer `dst` (this wave's 8 KB).
-// Lane L of piece `it` fills LDS bytes [16L, 16L+16) of a 1 KB run = row 4*(8*wv+it) + L/16,
+// DMA the 128 x 128-k activation tile of group g into LDS slot `dst` (this wave's 4 KB).
+// Lane L of piece `it` fills LDS bytes [16L, 16L+16) of a 1 KB run = row 4*(4*wv+it) + L/16,
 // physical chunk L%16, which holds logical chunk (L%16) ^ (row & 15).
 __device__ __forceinline__ void dma_x(const Bufs &bf, int64_t g, uint8_t *dst, int wv)
 {
     const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)g * 256);  // column of group g
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        uint8_t *base = dst + (wv * 8 + it) * 1024;
+    for (int it = 0; it < kDmaOps; ++it) {
+        uint8_t *base = dst + (wv * kDmaOps + it) * 1024;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(bf.x, (__attribute__((address_space(3))) void *)base, 16,
                                                  bf.xoff[it], soff, 0, 0);
     }
 }
 
-__device__ __forceinline__ void wait_dma_and_sync()
+// Loads issued by load_w<B> (per row block: the packed pieces, one zero-point load, four
+// scale loads).
+template <int B>
+constexpr int kLoadWOps = kRBW * (B / 2 + (B & 1) + 5);
+
+// Wait until at most N of this wave's loads are outstanding (they retire in order), then
+// synchronise the workgroup.
+template <int N>
+__device__ __forceinline__ void wait_and_sync()
 {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
     __syncthreads();
 }
 
@@ -112,8 +124,11 @@ __device__ __forceinline__ void load_w(const Bufs &bf, int64_t G, int64_t kt, in
     }
 }
 
-// One 128-k group: unpack this wave's four blocks of group gi for each row block, multiply by
-// the eight activation tiles from LDS, scale and accumulate.
+// One 128-k group: unpack this wave's four blocks of group GI for each row block, then
+// multiply them by the eight 16-row activation tiles from LDS, scale and accumulate.  The
+// tile loop is software-pipelined: the fragment reads of tile mt+1 are issued before the
+// matrix-core chain of tile mt, and the fp32 scale-accumulate of tile mt-1 runs on the
+// vector ALU while that chain executes.
 template <int B, int GI>
 __device__ __forceinline__ void group_step(const WTile<B> &w, const uint8_t *xs, int lane,
                                            f4 (&tot)[kRBW][kMT])
@@ -132,38 +147,52 @@ __device__ __forceinline__ void group_step(const WTile<B> &w, const uint8_t *xs,
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[u][i] = GI == 0 ? lo_h(w.sc[u][i]) : hi_h(w.sc[u][i]);
     }
+    h8 X[2][4];
+    f4 acc[2][kRBW];
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) X[0][j4] = *(const h8 *)(xs + xs_off(r, 4 * j4 + t));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt) {
-        const int row = 16 * mt + r;
-        h8 X[4];
+        const int cur = mt & 1, nxt = cur ^ 1;
+        if (mt + 1 < kMT) {
+            const int row = 16 * (mt + 1) + r;
 #pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4) X[j4] = *(const h8 *)(xs + xs_off(row, 4 * j4 + t));
-        f4 acc[kRBW];
+            for (int j4 = 0; j4 < 4; ++j4) X[nxt][j4] = *(const h8 *)(xs + xs_off(row, 4 * j4 + t));
+        }
+        // keep the reads ahead of the chain (else they reuse the chain's fragment registers
+        // and issue too late to hide their latency)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < kRBW; ++u) acc[u] = mfma16(A[u][0], X[0], (f4){0.f, 0.f, 0.f, 0.f});
+        for (int u = 0; u < kRBW; ++u) acc[cur][u] = mfma16(A[u][0], X[cur][0], (f4){0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int j4 = 1; j4 < 4; ++j4)
 #pragma unroll
-            for (int u = 0; u < kRBW; ++u) acc[u] = mfma16(A[u][j4], X[j4], acc[u]);
+            for (int u = 0; u < kRBW; ++u) acc[cur][u] = mfma16(A[u][j4], X[cur][j4], acc[cur][u]);
+        if (mt > 0) {
 #pragma unroll
-        for (int u = 0; u < kRBW; ++u) {
+            for (int u = 0; u < kRBW; ++u) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) tot[u][mt][i] = __builtin_fmaf(s[u][i], acc[u][i], tot[u][mt][i]);
-            // Pin the update here: without it the compiler sinks these fmas below later tiles,
-            // keeping every tile's matrix-core result live at once.
-            asm volatile("" : "+v"(tot[u][mt]));
+                for (int i = 0; i < 4; ++i)
+                    tot[u][mt - 1][i] = __builtin_fmaf(s[u][i], acc[nxt][u][i], tot[u][mt - 1][i]);
+                asm volatile("" : "+v"(tot[u][mt - 1]));
+            }
         }
-        // keep the next tile's fragment reads from being hoisted above this point (register
-        // pressure); the other wave on the SIMD covers the LDS latency
         __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int u = 0; u < kRBW; ++u) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            tot[u][kMT - 1][i] = __builtin_fmaf(s[u][i], acc[(kMT - 1) & 1][u][i], tot[u][kMT - 1][i]);
+        asm volatile("" : "+v"(tot[u][kMT - 1]));
     }
 }
 
 }  // namespace
 
 template <int B, bool OUTL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(GemmArgs a)
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(GemmArgs a)
 {
     __shared__ __attribute__((aligned(16))) Smem sm;
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -188,8 +217,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     Bufs bf;
     bf.x = make_rsrc(a.x + m0 * a.ldx, (a.m - m0) * a.ldx * 2);
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int row = 32 * wv + 4 * it + (lane >> 4);
+    for (int it = 0; it < kDmaOps; ++it) {
+        const int row = 16 * wv + 4 * it + (lane >> 4);
         const int c = (lane & 15) ^ (row & 15);
         bf.xoff[it] = (uint32_t)((row * a.ldx + 8 * c) * 2);
     }
@@ -236,37 +265,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
     }
 
-    dma_x(bf, 0, sm.xs[0], wv);
+    // Activation ring: the tile of group g sits in slot g % kRing; the DMA of group g + kAhead
+    // is issued at the start of step g (groups past the end reload the last one into a slot
+    // that is never read, and weight tiles past the end reload the last tile into the idle
+    // register buffer), so every step issues the same loads and the wait counts are fixed.
+    // Order of a wave's loads: [DMA g+3] then, on even g, [weights of tile g/2 + 1].  The
+    // tile of group g+1 is needed after step g; the loads younger than its DMA (issued at
+    // step g-2) are the DMAs of g+2 and g+3 plus the weight batches of the even steps among
+    // g-2, g-1, g.
+    const int64_t GN = 2 * KT;  // groups
+    auto gclamp = [&](int64_t g) { return g < GN ? g : GN - 1; };
+    auto tclamp = [&](int64_t t) { return t < KT ? t : KT - 1; };
     WTile<B> wa, wb;
+    dma_x(bf, 0, sm.xs[0], wv);
+    dma_x(bf, gclamp(1), sm.xs[1], wv);
+    __builtin_amdgcn_sched_barrier(0);
     load_w<B>(bf, G, 0, lane, wa);
-    wait_dma_and_sync();
+    __builtin_amdgcn_sched_barrier(0);
+    dma_x(bf, gclamp(2), sm.xs[2], wv);
+    wait_and_sync<kDmaOps>();  // group 0's DMA and tile 0's weights are in
 
     // Two k-tiles (four groups) per iteration so both weight buffers are named statically.
     for (int64_t kt = 0; kt < KT; kt += 2) {
-        // group 2kt (LDS buffer 0): prefetch group 2kt+1 activations and the next weight tile
-        dma_x(bf, 2 * kt + 1, sm.xs[1], wv);
-        if (kt + 1 < KT) load_w<B>(bf, G, kt + 1, lane, wb);
+        const int64_t g = 2 * kt;
+        // group g (tile kt, first half): fetch tile kt+1's weights
+        dma_x(bf, gclamp(g + 3), sm.xs[(g + 3) % kRing], wv);
         __builtin_amdgcn_sched_barrier(0);
-        group_step<B, 0>(wa, sm.xs[0], lane, tot);
-        wait_dma_and_sync();
-        // group 2kt+1 (buffer 1)
-        if (kt + 1 < KT) dma_x(bf, 2 * kt + 2, sm.xs[0], wv);
+        load_w<B>(bf, G, tclamp(kt + 1), lane, wb);
         __builtin_amdgcn_sched_barrier(0);
-        group_step<B, 1>(wa, sm.xs[1], lane, tot);
-        wait_dma_and_sync();
+        group_step<B, 0>(wa, sm.xs[g % kRing], lane, tot);
+        wait_and_sync<2 * kDmaOps + 2 * kLoadWOps<B>>();
+        // group g+1 (tile kt, second half)
+        dma_x(bf, gclamp(g + 4), sm.xs[(g + 4) % kRing], wv);
+        __builtin_amdgcn_sched_barrier(0);
+        group_step<B, 1>(wa, sm.xs[(g + 1) % kRing], lane, tot);
+        wait_and_sync<2 * kDmaOps + kLoadWOps<B>>();
         if (kt + 1 >= KT) break;
-        // group 2kt+2 (buffer 0)
-        dma_x(bf, 2 * kt + 3, sm.xs[1], wv);
-        if (kt + 2 < KT) load_w<B>(bf, G, kt + 2, lane, wa);
+        // group g+2 (tile kt+1, first half): fetch tile kt+2's weights
+        dma_x(bf, gclamp(g + 5), sm.xs[(g + 5) % kRing], wv);
         __builtin_amdgcn_sched_barrier(0);
-        group_step<B, 0>(wb, sm.xs[0], lane, tot);
-        wait_dma_and_sync();
-        // group 2kt+3 (buffer 1)
-        if (kt + 2 < KT) dma_x(bf, 2 * kt + 4, sm.xs[0], wv);
+        load_w<B>(bf, G, tclamp(kt + 2), lane, wa);
         __builtin_amdgcn_sched_barrier(0);
-        group_step<B, 1>(wb, sm.xs[1], lane, tot);
-        wait_dma_and_sync();
+        group_step<B, 0>(wb, sm.xs[(g + 2) % kRing], lane, tot);
+        wait_and_sync<2 * kDmaOps + 2 * kLoadWOps<B>>();
+        // group g+3 (tile kt+1, second half)
+        dma_x(bf, gclamp(g + 6), sm.xs[(g + 6) % kRing], wv);
+        __builtin_amdgcn_sched_barrier(0);
+        group_step<B, 1>(wb, sm.xs[(g + 3) % kRing], lane, tot);
+        wait_and_sync<2 * kDmaOps + kLoadWOps<B>>();
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may land after the workgroup ends
 
     // epilogue: the fp16 store
 #pragma unroll
@@ -284,29 +332,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
-// x^T for the outlier gathers: xt[kk][128 mb + 8 r + mt] = x[128 mb + 16 mt + r][kk], zeros for
-// rows >= m.  One block per 64 k x 128 m tile, staged through LDS.
+// x^T for the outlier partial: xt[kk][128 mb + 8 r + mt] = x[128 mb + 16 mt + r][kk], zeros
+// for rows >= m.  One block per 64 k x 128 m tile: 16-byte loads of x rows into LDS, then
+// each thread gathers eight values (one per tile mt) for one 16-byte store of x^T.
 __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t *x, int64_t ldx, int64_t m, int64_t k,
                                                         uint16_t *xt, int64_t ldxt)
 {
-    __shared__ uint16_t tile[128][65];
+    constexpr int kPitch = 64 + 2;  // halves per LDS row (odd dword pitch: rows hit distinct banks)
+    __shared__ uint16_t tile[128 * kPitch];
     const int64_t k0 = blockIdx.x * 64, m0 = blockIdx.y * 128;
-    for (int i = threadIdx.x; i < 128 * 64; i += 256) {
-        const int rm = i / 64, ck = i % 64;
-        const int64_t gm = m0 + rm, gk = k0 + ck;
-        tile[rm][ck] = (gm < m && gk < k) ? x[gm * ldx + gk] : (uint16_t)0;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int idx = threadIdx.x + 256 * it, row = idx / 8, c = idx % 8;
+        const int64_t gm = m0 + row, gk = k0 + 8 * c;
+        u4 v = {0u, 0u, 0u, 0u};
+        if (gm < m && gk < k) v = *(const u4 *)(x + gm * ldx + gk);
+        uint32_t *dst = (uint32_t *)(tile + row * kPitch + 8 * c);  // 4-byte aligned: kPitch even
+        dst[0] = v[0];
+        dst[1] = v[1];
+        dst[2] = v[2];
+        dst[3] = v[3];
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < 128 * 64; i += 256) {
-        const int rk = i / 128, pos = i % 128;      // pos = 8 r + mt holds row 16 mt + r
-        const int rm = 16 * (pos & 7) + (pos >> 3);
-        const int64_t gk = k0 + rk;
-        if (gk < k) xt[gk * ldxt + m0 + pos] = tile[rm][rk];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int idx = threadIdx.x + 256 * it, kk = idx / 16, sgm = idx % 16;  // positions 8 sgm ..
+        uint32_t w[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+            w[h] = (uint32_t)tile[(16 * (2 * h) + sgm) * kPitch + kk] |
+                   ((uint32_t)tile[(16 * (2 * h + 1) + sgm) * kPitch + kk] << 16);
+        const int64_t gk = k0 + kk;
+        if (gk < k) *(u4 *)(xt + gk * ldxt + m0 + 8 * sgm) = (u4){w[0], w[1], w[2], w[3]};
     }
 }
 
 // Outlier partial: S^T[n][p] = sum over the outliers (n, c, v) of v * x^T[c][p], in fp32 (one
-// wave per weight row, each lane 8 consecutive positions p of a 512-position chunk).
+// wave per weight row, each lane 8 consecutive positions p of a 512-position chunk).  Eight
+// entries are gathered per step so their loads are in flight together.
 __global__ __launch_bounds__(256) void outlier_spmm_kernel(const int32_t *rowptr, const int32_t *col,
                                                            const uint16_t *val, const uint16_t *xt, int64_t n,
                                                            int64_t ldxt, float *spart)
@@ -317,14 +380,22 @@ __global__ __launch_bounds__(256) void outlier_spmm_kernel(const int32_t *rowptr
     if (row >= n || p >= ldxt) return;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const int64_t e0 = rowptr[row], e1 = rowptr[row + 1];
-    for (int64_t e = e0; e < e1; ++e) {
-        const float v = h_f(val[e]);
-        const u4 xv = *(const u4 *)(xt + (int64_t)col[e] * ldxt + p);
+    for (int64_t e = e0; e < e1; e += 8) {
+        u4 xv[8];
+        float v[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            acc[2 * j] = __builtin_fmaf(lo_h(xv[j]), v, acc[2 * j]);
-            acc[2 * j + 1] = __builtin_fmaf(hi_h(xv[j]), v, acc[2 * j + 1]);
+        for (int j = 0; j < 8; ++j) {
+            const bool ok = e + j < e1;
+            v[j] = ok ? h_f(val[e + j]) : 0.f;
+            xv[j] = ok ? *(const u4 *)(xt + (int64_t)col[e + j] * ldxt + p) : (u4){0u, 0u, 0u, 0u};
         }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] = __builtin_fmaf(lo_h(xv[j][q]), v[j], acc[2 * q]);
+                acc[2 * q + 1] = __builtin_fmaf(hi_h(xv[j][q]), v[j], acc[2 * q + 1]);
+            }
     }
     f4 *dst = (f4 *)(spart + row * ldxt + p);
     dst[0] = (f4){acc[0], acc[1], acc[2], acc[3]};
@@ -340,9 +411,9 @@ static hipError_t gemm_bits(const GemmArgs &a, hipStream_t st)
                            st, a.x, a.ldx, a.m, a.k, a.xt, a.ldxt);
         hipLaunchKernelGGL(outlier_spmm_kernel, dim3((unsigned)((a.n + 3) / 4), (unsigned)((a.ldxt + 511) / 512)),
                            dim3(256), 0, st, a.rowptr, a.col, a.val, a.xt, a.n, a.ldxt, a.spart);
-        hipLaunchKernelGGL((gemm_kernel<B, true>), dim3((unsigned)(n_tiles * m_tiles)), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((gemm_kernel<B, true>), dim3((unsigned)(n_tiles * m_tiles)), dim3(kWaves * 64), 0, st, a);
     } else {
-        hipLaunchKernelGGL((gemm_kernel<B, false>), dim3((unsigned)(n_tiles * m_tiles)), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((gemm_kernel<B, false>), dim3((unsigned)(n_tiles * m_tiles)), dim3(kWaves * 64), 0, st, a);
     }
     return hipGetLastError();
 }
