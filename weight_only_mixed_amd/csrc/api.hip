@@ -219,9 +219,7 @@ qp_status qlinear_gemm(const qp_weight_desc *d, const qp_weight *w, const uint16
     if (m * ldx * 2 > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "x larger than 2 GiB");
     if ((int64_t)qp_packed_bytes(d) > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "packed weight larger than 2 GiB");
     GemmArgs a{};
-    a.packed = (const uint8_t *)w->packed;
-    a.scales = w->scales;
-    a.zeros = w->zeros;
+    a.ex[0] = {(const uint8_t *)w->packed, w->scales, w->zeros};
     if (w->nnz > 0) {
         const size_t need = qlinear_gemm_workspace_bytes(d, m, w->nnz);
         if (!workspace || ws_bytes < need || !aligned(workspace, 16))
@@ -264,7 +262,9 @@ qp_status qlinear_grouped_gemm(const qp_weight_desc *d, const qp_weight *experts
         return st;
     if (!expert_offsets) return fail(QP_ERR_INVALID_ARG, "expert_offsets NULL");
     if (rows < 0) return fail(QP_ERR_INVALID_ARG, "rows < 0");
-    SmallArgs a{};
+    if (rows * ldx * 2 > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "x larger than 2 GiB");
+    if ((int64_t)qp_packed_bytes(d) > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "packed weight larger than 2 GiB");
+    GemmArgs a{};
     for (int e = 0; e < n_experts; ++e)
         a.ex[e] = {(const uint8_t *)experts[e].packed, experts[e].scales, experts[e].zeros};
     a.x = x;

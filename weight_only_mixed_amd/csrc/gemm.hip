@@ -129,8 +129,8 @@ __device__ __forceinline__ void load_w(const Bufs &bf, int64_t G, int64_t kt, in
 // tile loop is software-pipelined: the fragment reads of tile mt+1 are issued before the
 // matrix-core chain of tile mt, and the fp32 scale-accumulate of tile mt-1 runs on the
 // vector ALU while that chain executes.
-template <int B, int GI>
-__device__ __forceinline__ void group_step(const WTile<B> &w, const uint8_t *xs, int lane,
+template <int B, int GI, bool FULL>
+__device__ __forceinline__ void group_step(const WTile<B> &w, const uint8_t *xs, int lane, int nmt,
                                            f4 (&tot)[kRBW][kMT])
 {
     const int t = lane >> 4, r = lane & 15;
@@ -154,8 +154,9 @@ __device__ __forceinline__ void group_step(const WTile<B> &w, const uint8_t *xs,
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt) {
+        if (!FULL && mt >= nmt) break;  // uniform: tiles past the workgroup's rows are skipped
         const int cur = mt & 1, nxt = cur ^ 1;
-        if (mt + 1 < kMT) {
+        if (mt + 1 < kMT && (FULL || mt + 1 < nmt)) {
             const int row = 16 * (mt + 1) + r;
 #pragma unroll
             for (int j4 = 0; j4 < 4; ++j4) X[nxt][j4] = *(const h8 *)(xs + xs_off(row, 4 * j4 + t));
@@ -178,57 +179,144 @@ __device__ __forceinline__ void group_step(const WTile<B> &w, const uint8_t *xs,
                 asm volatile("" : "+v"(tot[u][mt - 1]));
             }
         }
+        if (FULL ? mt + 1 == kMT : mt + 1 == nmt) {  // the last tile's scale-accumulate
+#pragma unroll
+            for (int u = 0; u < kRBW; ++u) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tot[u][mt][i] = __builtin_fmaf(s[u][i], acc[cur][u][i], tot[u][mt][i]);
+                asm volatile("" : "+v"(tot[u][mt]));
+            }
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int u = 0; u < kRBW; ++u) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            tot[u][kMT - 1][i] = __builtin_fmaf(s[u][i], acc[(kMT - 1) & 1][u][i], tot[u][kMT - 1][i]);
-        asm volatile("" : "+v"(tot[u][kMT - 1]));
+}
+
+// The k loop of a workgroup.  Activation ring: the tile of group g sits in slot g % kRing; the
+// DMA of group g + kAhead is issued at the start of step g (groups past the end reload the
+// last one into a slot that is never read, and weight tiles past the end reload the last
+// tile into the idle register buffer), so every step issues the same loads and the wait
+// counts are fixed.  Order of a wave's loads: [DMA g+3] then, on even g, [weights of tile
+// g/2 + 1].  The tile of group g+1 is needed after step g; the loads younger than its DMA
+// (issued at step g-2) are the DMAs of g+2 and g+3 plus the weight batches of the even
+// steps among g-2, g-1, g.  FULL: all eight 16-row activation tiles hold rows.
+template <int B, bool FULL>
+__device__ __forceinline__ void k_loop(const Bufs &bf, Smem &sm, int64_t KT, int64_t G, int wv, int lane, int nmt,
+                                       f4 (&tot)[kRBW][kMT])
+{
+    const int64_t GN = 2 * KT;  // groups
+    auto gclamp = [&](int64_t g) { return g < GN ? g : GN - 1; };
+    auto tclamp = [&](int64_t t) { return t < KT ? t : KT - 1; };
+    WTile<B> wa, wb;
+    dma_x(bf, 0, sm.xs[0], wv);
+    dma_x(bf, gclamp(1), sm.xs[1], wv);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w<B>(bf, G, 0, lane, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_x(bf, gclamp(2), sm.xs[2], wv);
+    wait_and_sync<kDmaOps>();  // group 0's DMA and tile 0's weights are in
+
+    // Two k-tiles (four groups) per iteration so both weight buffers are named statically.
+    for (int64_t kt = 0; kt < KT; kt += 2) {
+        const int64_t g = 2 * kt;
+        // group g (tile kt, first half): fetch tile kt+1's weights
+        dma_x(bf, gclamp(g + 3), sm.xs[(g + 3) % kRing], wv);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w<B>(bf, G, tclamp(kt + 1), lane, wb);
+        __builtin_amdgcn_sched_barrier(0);
+        group_step<B, 0, FULL>(wa, sm.xs[g % kRing], lane, nmt, tot);
+        wait_and_sync<2 * kDmaOps + 2 * kLoadWOps<B>>();
+        // group g+1 (tile kt, second half)
+        dma_x(bf, gclamp(g + 4), sm.xs[(g + 4) % kRing], wv);
+        __builtin_amdgcn_sched_barrier(0);
+        group_step<B, 1, FULL>(wa, sm.xs[(g + 1) % kRing], lane, nmt, tot);
+        wait_and_sync<2 * kDmaOps + kLoadWOps<B>>();
+        if (kt + 1 >= KT) break;
+        // group g+2 (tile kt+1, first half): fetch tile kt+2's weights
+        dma_x(bf, gclamp(g + 5), sm.xs[(g + 5) % kRing], wv);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w<B>(bf, G, tclamp(kt + 2), lane, wa);
+        __builtin_amdgcn_sched_barrier(0);
+        group_step<B, 0, FULL>(wb, sm.xs[(g + 2) % kRing], lane, nmt, tot);
+        wait_and_sync<2 * kDmaOps + 2 * kLoadWOps<B>>();
+        // group g+3 (tile kt+1, second half)
+        dma_x(bf, gclamp(g + 6), sm.xs[(g + 6) % kRing], wv);
+        __builtin_amdgcn_sched_barrier(0);
+        group_step<B, 1, FULL>(wb, sm.xs[(g + 3) % kRing], lane, nmt, tot);
+        wait_and_sync<2 * kDmaOps + kLoadWOps<B>>();
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may land after the workgroup ends
 }
 
 }  // namespace
 
-template <int B, bool OUTL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(GemmArgs a)
+// Kernel modes: a plain layer, the same with outliers, or routed experts with one of the three
+// grouped epilogues.
+enum { kPlain = 0, kOutl = 1, kGroupNone = 2, kGroupSwiglu = 3, kGroupRowsF32 = 4 };
+
+// FULL: every workgroup's eight 16-row activation tiles hold rows (a launch over whole
+// 128-row tiles); otherwise tiles past the workgroup's rows are skipped.  mtile0: the first
+// 128-row tile of the launch (plain layer).
+template <int B, int MODE, bool FULL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(GemmArgs a,
+                                                                                            int64_t mtile0,
+                                                                                            int64_t m_tiles)
 {
+    constexpr bool OUTL = MODE == kOutl, GROUPED = MODE >= kGroupNone;
     __shared__ __attribute__((aligned(16))) Smem sm;
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t = lane >> 4, r = lane & 15;
     const int64_t KT = a.k / kTileK, G = a.k / kGroup;
-    const int64_t n_tiles = (a.n + kNT - 1) / kNT, m_tiles = (a.m + kMRows - 1) / kMRows;
-    int64_t nt, mtile;
-    const int64_t b = blockIdx.x;
-    if (n_tiles % 8 == 0) {  // XCD-aware: the m blocks of one n tile share an XCD
-        const int64_t xcd = b % 8, local = b / 8;
-        nt = (local / m_tiles) * 8 + xcd;
-        mtile = local % m_tiles;
+    const int64_t n_tiles = (a.n + kNT - 1) / kNT;
+    int64_t nt, m0, mend;  // weight tile; sorted rows [m0, mend) of this workgroup
+    int e = 0;
+    if constexpr (GROUPED) {
+        // blockIdx = (weight tile, expert, 128-row tile of the expert's rows)
+        e = blockIdx.y;
+        const int64_t r0 = a.offsets[e], r1 = a.offsets[e + 1];
+        nt = blockIdx.x;
+        m0 = r0 + (int64_t)blockIdx.z * kMRows;
+        if (m0 >= r1) return;  // the whole workgroup: this expert has fewer row tiles
+        mend = r1 < m0 + kMRows ? r1 : m0 + kMRows;
     } else {
-        nt = b % n_tiles;
-        mtile = b / n_tiles;
+        int64_t mtile;
+        const int64_t b = blockIdx.x;
+        if (n_tiles % 8 == 0) {  // XCD-aware: the m blocks of one n tile share an XCD
+            const int64_t xcd = b % 8, local = b / 8;
+            nt = (local / m_tiles) * 8 + xcd;
+            mtile = local % m_tiles;
+        } else {
+            nt = b % n_tiles;
+            mtile = b / n_tiles;
+        }
+        m0 = (mtile0 + mtile) * kMRows;
+        mend = a.m < m0 + kMRows ? a.m : m0 + kMRows;
     }
-    const int64_t m0 = mtile * kMRows;
+    // 16-row activation tiles holding rows (uniform; tiles past it are skipped)
+    const int nmt = (int)((mend - m0 + 15) / 16);
+    const ExpertPtrs &W = a.ex[e];
     const int64_t NB = a.n / kTileN;
-    const int64_t n0 = nt * kNT;                          // first weight row of the workgroup
     const int64_t rb0 = nt * (kNT / kTileN) + wv * kRBW;  // first row block of this wave
 
     Bufs bf;
-    bf.x = make_rsrc(a.x + m0 * a.ldx, (a.m - m0) * a.ldx * 2);
+    // Activation rows are gathered per lane: the DMA source of a row past the workgroup's
+    // rows lies past the buffer's range and reads zeros.
+    bf.x = make_rsrc(a.x, a.m * a.ldx * 2);
 #pragma unroll
     for (int it = 0; it < kDmaOps; ++it) {
         const int row = 16 * wv + 4 * it + (lane >> 4);
         const int c = (lane & 15) ^ (row & 15);
-        bf.xoff[it] = (uint32_t)((row * a.ldx + 8 * c) * 2);
+        const int64_t sr = m0 + row;
+        int64_t src = sr;
+        if constexpr (GROUPED) src = sr < mend ? (a.row_src ? a.row_src[sr] : sr) : 0;
+        bf.xoff[it] = sr < mend ? (uint32_t)((src * a.ldx + 8 * c) * 2) : 0x80000000u;
     }
 #pragma unroll
     for (int u = 0; u < kRBW; ++u) {
         const int64_t rb = rb0 + u;
         const bool in = rb < NB;
-        bf.w[u] = make_rsrc(a.packed + rb * KT * (512 * B), in ? KT * (512 * B) : 0);
-        bf.sc[u] = make_rsrc(a.scales + rb * kTileN * G, in ? kTileN * G * 2 : 0);
-        bf.zr[u] = make_rsrc(a.zeros + rb * kTileN * G, in ? kTileN * G : 0);
+        bf.w[u] = make_rsrc(W.packed + rb * KT * (512 * B), in ? KT * (512 * B) : 0);
+        bf.sc[u] = make_rsrc(W.scales + rb * kTileN * G, in ? kTileN * G * 2 : 0);
+        bf.zr[u] = make_rsrc(W.zeros + rb * kTileN * G, in ? kTileN * G : 0);
     }
 
     f4 tot[kRBW][kMT];
@@ -265,58 +353,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
     }
 
-    // Activation ring: the tile of group g sits in slot g % kRing; the DMA of group g + kAhead
-    // is issued at the start of step g (groups past the end reload the last one into a slot
-    // that is never read, and weight tiles past the end reload the last tile into the idle
-    // register buffer), so every step issues the same loads and the wait counts are fixed.
-    // Order of a wave's loads: [DMA g+3] then, on even g, [weights of tile g/2 + 1].  The
-    // tile of group g+1 is needed after step g; the loads younger than its DMA (issued at
-    // step g-2) are the DMAs of g+2 and g+3 plus the weight batches of the even steps among
-    // g-2, g-1, g.
-    const int64_t GN = 2 * KT;  // groups
-    auto gclamp = [&](int64_t g) { return g < GN ? g : GN - 1; };
-    auto tclamp = [&](int64_t t) { return t < KT ? t : KT - 1; };
-    WTile<B> wa, wb;
-    dma_x(bf, 0, sm.xs[0], wv);
-    dma_x(bf, gclamp(1), sm.xs[1], wv);
-    __builtin_amdgcn_sched_barrier(0);
-    load_w<B>(bf, G, 0, lane, wa);
-    __builtin_amdgcn_sched_barrier(0);
-    dma_x(bf, gclamp(2), sm.xs[2], wv);
-    wait_and_sync<kDmaOps>();  // group 0's DMA and tile 0's weights are in
+    k_loop<B, FULL>(bf, sm, KT, G, wv, lane, nmt, tot);
 
-    // Two k-tiles (four groups) per iteration so both weight buffers are named statically.
-    for (int64_t kt = 0; kt < KT; kt += 2) {
-        const int64_t g = 2 * kt;
-        // group g (tile kt, first half): fetch tile kt+1's weights
-        dma_x(bf, gclamp(g + 3), sm.xs[(g + 3) % kRing], wv);
-        __builtin_amdgcn_sched_barrier(0);
-        load_w<B>(bf, G, tclamp(kt + 1), lane, wb);
-        __builtin_amdgcn_sched_barrier(0);
-        group_step<B, 0>(wa, sm.xs[g % kRing], lane, tot);
-        wait_and_sync<2 * kDmaOps + 2 * kLoadWOps<B>>();
-        // group g+1 (tile kt, second half)
-        dma_x(bf, gclamp(g + 4), sm.xs[(g + 4) % kRing], wv);
-        __builtin_amdgcn_sched_barrier(0);
-        group_step<B, 1>(wa, sm.xs[(g + 1) % kRing], lane, tot);
-        wait_and_sync<2 * kDmaOps + kLoadWOps<B>>();
-        if (kt + 1 >= KT) break;
-        // group g+2 (tile kt+1, first half): fetch tile kt+2's weights
-        dma_x(bf, gclamp(g + 5), sm.xs[(g + 5) % kRing], wv);
-        __builtin_amdgcn_sched_barrier(0);
-        load_w<B>(bf, G, tclamp(kt + 2), lane, wa);
-        __builtin_amdgcn_sched_barrier(0);
-        group_step<B, 0>(wb, sm.xs[(g + 2) % kRing], lane, tot);
-        wait_and_sync<2 * kDmaOps + 2 * kLoadWOps<B>>();
-        // group g+3 (tile kt+1, second half)
-        dma_x(bf, gclamp(g + 6), sm.xs[(g + 6) % kRing], wv);
-        __builtin_amdgcn_sched_barrier(0);
-        group_step<B, 1>(wb, sm.xs[(g + 3) % kRing], lane, tot);
-        wait_and_sync<2 * kDmaOps + kLoadWOps<B>>();
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may land after the workgroup ends
-
-    // epilogue: the fp16 store
+    // epilogue
 #pragma unroll
     for (int u = 0; u < kRBW; ++u) {
         const int64_t rb = rb0 + u;
@@ -324,10 +363,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
             const int64_t row = m0 + 16 * mt + r;
-            if (row >= a.m) continue;
+            if (row >= mend) continue;
             const f4 s = tot[u][mt];
-            uint16_t *y = a.y + row * a.ldy + rb * kTileN + 4 * t;
-            *(u2 *)y = (u2){pack_h2(s[0], s[1]), pack_h2(s[2], s[3])};
+            if constexpr (MODE == kGroupRowsF32) {
+                *(f4 *)((float *)a.y + row * a.ldy + rb * kTileN + 4 * t) = s;
+            } else if constexpr (MODE == kGroupSwiglu) {
+                // row blocks 2i (gate) and 2i+1 (up) of a wave: output features 16i + 4t + j
+                if (u == 1) {
+                    const f4 gt = tot[0][mt];
+                    float o[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) o[j] = gt[j] / (1.0f + expf(-gt[j])) * s[j];
+                    uint16_t *y = (uint16_t *)a.y + row * a.ldy + (rb / 2) * kTileN + 4 * t;
+                    *(u2 *)y = (u2){pack_h2(o[0], o[1]), pack_h2(o[2], o[3])};
+                }
+            } else {
+                uint16_t *y = (uint16_t *)a.y + row * a.ldy + rb * kTileN + 4 * t;
+                *(u2 *)y = (u2){pack_h2(s[0], s[1]), pack_h2(s[2], s[3])};
+            }
         }
     }
 }
@@ -402,18 +455,30 @@ __global__ __launch_bounds__(256) void outlier_spmm_kernel(const int32_t *rowptr
     dst[1] = (f4){acc[4], acc[5], acc[6], acc[7]};
 }
 
+// Whole 128-row tiles in one launch, a ragged last tile in another.
+template <int B, int MODE>
+static void gemm_launch(const GemmArgs &a, hipStream_t st)
+{
+    const int64_t n_tiles = (a.n + kNT - 1) / kNT, full = a.m / kMRows;
+    const dim3 block(kWaves * 64);
+    if (full > 0)
+        hipLaunchKernelGGL((gemm_kernel<B, MODE, true>), dim3((unsigned)(n_tiles * full)), block, 0, st, a,
+                           (int64_t)0, full);
+    if (a.m % kMRows)
+        hipLaunchKernelGGL((gemm_kernel<B, MODE, false>), dim3((unsigned)n_tiles), block, 0, st, a, full, (int64_t)1);
+}
+
 template <int B>
 static hipError_t gemm_bits(const GemmArgs &a, hipStream_t st)
 {
-    const int64_t n_tiles = (a.n + kNT - 1) / kNT, m_tiles = (a.m + kMRows - 1) / kMRows;
     if (a.rowptr) {
         hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)((a.k + 63) / 64), (unsigned)(a.ldxt / 128)), dim3(256), 0,
                            st, a.x, a.ldx, a.m, a.k, a.xt, a.ldxt);
         hipLaunchKernelGGL(outlier_spmm_kernel, dim3((unsigned)((a.n + 3) / 4), (unsigned)((a.ldxt + 511) / 512)),
                            dim3(256), 0, st, a.rowptr, a.col, a.val, a.xt, a.n, a.ldxt, a.spart);
-        hipLaunchKernelGGL((gemm_kernel<B, true>), dim3((unsigned)(n_tiles * m_tiles)), dim3(kWaves * 64), 0, st, a);
+        gemm_launch<B, kOutl>(a, st);
     } else {
-        hipLaunchKernelGGL((gemm_kernel<B, false>), dim3((unsigned)(n_tiles * m_tiles)), dim3(kWaves * 64), 0, st, a);
+        gemm_launch<B, kPlain>(a, st);
     }
     return hipGetLastError();
 }
@@ -428,6 +493,42 @@ hipError_t launch_gemm(int bits, const GemmArgs &a, hipStream_t st)
     case 4: return gemm_bits<4>(a, st);
     case 5: return gemm_bits<5>(a, st);
     case 6: return gemm_bits<6>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+// Routed experts: one workgroup per (256-row weight tile, expert, 128-row tile of the
+// expert's sorted rows); the row tiles are sized for the worst case (all rows on one expert)
+// and the surplus workgroups return at once.
+template <int B, int MODE>
+static hipError_t grouped_mode(int n_experts, const GemmArgs &a, hipStream_t st)
+{
+    const int64_t n_tiles = (a.n + kNT - 1) / kNT, m_tiles = (a.m + kMRows - 1) / kMRows;
+    hipLaunchKernelGGL((gemm_kernel<B, MODE, false>), dim3((unsigned)n_tiles, (unsigned)n_experts, (unsigned)m_tiles),
+                       dim3(kWaves * 64), 0, st, a, (int64_t)0, m_tiles);
+    return hipGetLastError();
+}
+
+template <int B>
+static hipError_t grouped_bits(int epilogue, int n_experts, const GemmArgs &a, hipStream_t st)
+{
+    switch (epilogue) {
+    case QP_EPI_NONE: return grouped_mode<B, kGroupNone>(n_experts, a, st);
+    case QP_EPI_SWIGLU: return grouped_mode<B, kGroupSwiglu>(n_experts, a, st);
+    case QP_EPI_ROWS_F32: return grouped_mode<B, kGroupRowsF32>(n_experts, a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_grouped(int bits, int epilogue, int n_experts, const GemmArgs &a, hipStream_t st)
+{
+    if (a.m < 1) return hipSuccess;
+    switch (bits) {
+    case 2: return grouped_bits<2>(epilogue, n_experts, a, st);
+    case 3: return grouped_bits<3>(epilogue, n_experts, a, st);
+    case 4: return grouped_bits<4>(epilogue, n_experts, a, st);
+    case 5: return grouped_bits<5>(epilogue, n_experts, a, st);
+    case 6: return grouped_bits<6>(epilogue, n_experts, a, st);
     }
     return hipErrorInvalidValue;
 }

@@ -63,20 +63,20 @@ struct SmallArgs {
     int64_t ldy;
 };
 hipError_t launch_gemv(int bits, const SmallArgs &a, hipStream_t st);
-hipError_t launch_grouped(int bits, int epilogue, int n_experts, const SmallArgs &a,
-                          hipStream_t st);
 
+// Dequant-GEMM on the matrix cores: a plain layer (ex[0], optional outliers) or a group of
+// routed experts (ex[e] over the sorted rows offsets[e] .. offsets[e+1]).
 struct GemmArgs {
-    const uint8_t *packed;
-    const uint16_t *scales;
-    const uint8_t *zeros;
-    const int32_t *rowptr;
+    ExpertPtrs ex[kMaxExperts];
+    const int32_t *rowptr;   // outlier CSR (plain layer only), or null
     const int32_t *col;
     const uint16_t *val;
     const uint16_t *x;
     int64_t ldx;
-    int64_t m, n, k;
-    uint16_t *y;
+    const int32_t *row_src;  // grouped: row of x feeding sorted row r (null: row r)
+    const int32_t *offsets;  // grouped: [n_experts + 1] sorted-row ranges
+    int64_t m, n, k;         // grouped: m = upper bound of the sorted rows (and of x's rows)
+    void *y;
     int64_t ldy;
     uint16_t *xt;   // workspace (outliers only): x transposed, [k][ldxt]
     float *spart;   // workspace (outliers only): fp32 outlier partial, [n][ldxt]
@@ -84,6 +84,7 @@ struct GemmArgs {
 };
 int64_t gemm_xt_ld(int64_t m);
 hipError_t launch_gemm(int bits, const GemmArgs &a, hipStream_t st);
+hipError_t launch_grouped(int bits, int epilogue, int n_experts, const GemmArgs &a, hipStream_t st);
 
 hipError_t launch_moe_dispatch(const int32_t *ids, const float *w, int64_t tokens, int topk,
                                int n_experts, int32_t *offsets, int32_t *row_src,
