@@ -176,7 +176,9 @@ def clone_weight(torch, wt):
 def bench_stack(q, torch, workloads, stream, reps: int = 20):
     """Llama-7B-shaped 32-layer decode stack at M=1 (224 GEMVs per token, mixed bit table).
     One quantized template per (shape, bits) class, cloned so every matrix has its own HBM
-    bytes (2.96 GB in total); one token = the 224 calls in layer order, one HIP graph."""
+    bytes (2.96 GB in total).  One token = per layer the four dependent stages [q, k, v], [o],
+    [gate, up], [down], each one qlinear_gemv_batch launch (128 launches), in one HIP graph;
+    also reported with one qlinear_gemv launch per matrix (224 launches)."""
     dev = torch.device("cuda")
     templates, mats, total = {}, [], 0
     for layer in range(workloads.STACK_LAYERS):
@@ -194,20 +196,37 @@ def bench_stack(q, torch, workloads, stream, reps: int = 20):
     xs = {k: torch.from_numpy(workloads.activations_fp16(1, k, workloads.seed_for(3)).view(np.int16)).to(dev)
           for k in (4096, 11008)}
     ys = {n: torch.empty((1, n), dtype=torch.int16, device=dev) for n in (4096, 11008)}
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
+    def token_us(g):
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    # one launch per matrix
+    g1 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g1, stream=stream):
         for d, h, _, n, k in mats:
             q.qlinear_gemv(d, h, xs[k], k, 1, ys[n], n)
-    g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / reps
+    us_each = token_us(g1)
+    # one launch per dependent stage of a layer: [q, k, v], [o], [gate, up], [down]
+    ys2 = {name: torch.empty((1, workloads.STACK_SHAPES[name][0]), dtype=torch.int16, device=dev)
+           for name in workloads.LLAMA_MATRICES}
+    stages = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2, stream=stream):
+        for layer in range(workloads.STACK_LAYERS):
+            byname = dict(zip(workloads.LLAMA_MATRICES, mats[7 * layer:7 * layer + 7]))
+            for st in stages:
+                probs = [q.gemv_problem(byname[nm][0], byname[nm][1], xs[byname[nm][4]], byname[nm][4], 1, ys2[nm],
+                                        byname[nm][3]) for nm in st]
+                q.qlinear_gemv_batch(probs)
+    us = token_us(g2)
     gbps = total / (us * 1e-6) / 1e9
     bits_avg = sum(workloads.stack_bits(l, nm) * workloads.STACK_SHAPES[nm][0] * workloads.STACK_SHAPES[nm][1]
                    for l in range(workloads.STACK_LAYERS) for nm in workloads.LLAMA_MATRICES) / \
@@ -215,7 +234,9 @@ def bench_stack(q, torch, workloads, stream, reps: int = 20):
             for nm in workloads.LLAMA_MATRICES) / workloads.STACK_LAYERS
     del mats, templates
     return dict(us_per_token=round(us, 1), GBps=round(gbps, 1), frac_hbm_peak=round(gbps / HBM_PEAK_GBS, 4),
-                bytes_per_token=total, launches_per_token=7 * workloads.STACK_LAYERS, avg_bits=round(bits_avg, 3))
+                bytes_per_token=total, launches_per_token=4 * workloads.STACK_LAYERS, avg_bits=round(bits_avg, 3),
+                us_per_token_one_launch_per_matrix=round(us_each, 1),
+                GBps_one_launch_per_matrix=round(total / (us_each * 1e-6) / 1e9, 1))
 
 
 def bench_moe(q, torch, workloads, stream, reps: int = 20):

@@ -168,6 +168,24 @@ qp_status qlinear_gemv(const qp_weight_desc *desc, const qp_weight *w, const uin
                        int64_t ldx, int64_t m, uint16_t *y, int64_t ldy, void *stream);
 
 /*
+ * Independent decode GEMVs of one layer in a single launch, e.g. the q/k/v or gate/up
+ * projections that read the same activations, each at its own bit width (the mixed-bit page
+ * assigns bit widths per projection, s2.2).  Each problem has the operands and result of
+ * qlinear_gemv and is validated the same way; `problems` is a HOST array of 1..8 entries.
+ * Outputs must not overlap (not checked).  Returns the first failing problem's status.
+ */
+typedef struct {
+    qp_weight_desc desc;
+    qp_weight w;
+    const uint16_t *x;
+    int64_t ldx;
+    int64_t m;
+    uint16_t *y;
+    int64_t ldy;
+} qp_gemv_problem;
+qp_status qlinear_gemv_batch(const qp_gemv_problem *problems, int32_t count, void *stream);
+
+/*
  * Prefill dequant-GEMM for any m >= 1 (tuned for m >= 64): same operands and result as
  * qlinear_gemv.  Tiles of the packed weight are unpacked in registers and fed to fp16
  * matrix cores with fp32 accumulation; scales are applied per group in fp32.

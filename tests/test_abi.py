@@ -107,6 +107,21 @@ def test_gemv_validation():
                           check=False) == q.QP_ERR_WORKSPACE
 
 
+def test_gemv_batch_validation():
+    d = q.desc(4, 256, 512)
+    w = q.weight(FAKE, FAKE, FAKE)
+    good = q.gemv_problem(d, w, FAKE, 512, 1, FAKE, 256)
+    assert q.qlinear_gemv_batch([], stream=0, check=False) == q.QP_ERR_INVALID_ARG
+    assert q.qlinear_gemv_batch([good] * 9, stream=0, check=False) == q.QP_ERR_INVALID_ARG
+    bad_ldx = q.gemv_problem(d, w, FAKE, 500, 1, FAKE, 256)
+    assert q.qlinear_gemv_batch([good, bad_ldx], stream=0, check=False) == q.QP_ERR_INVALID_ARG
+    assert "ldx" in q.last_error()
+    big_m = q.gemv_problem(d, w, FAKE, 512, 17, FAKE, 256)
+    assert q.qlinear_gemv_batch([good, big_m], stream=0, check=False) == q.QP_ERR_UNSUPPORTED
+    canon = q.gemv_problem(q.desc(4, 256, 512, layout=q.QP_LAYOUT_CANONICAL), w, FAKE, 512, 1, FAKE, 256)
+    assert q.qlinear_gemv_batch([canon], stream=0, check=False) == q.QP_ERR_UNSUPPORTED
+
+
 def test_quantize_validation():
     d = q.desc(4, 64, 1024)
     st, nnz = q.qpack_quantize(d, FAKE, 1024, 0.001, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10, FAKE, 1 << 20,

@@ -79,6 +79,33 @@ def test_gemm_ragged_with_outliers(bits, m):
     assert rel_err(y, r) <= TOL, report(y, r)
 
 
+@pytest.mark.parametrize("ms,wide", (((1, 1, 1, 1), False), ((1, 1, 1, 1), True), ((1, 3, 8, 2), False),
+                                     ((16, 5, 1, 9), True)))
+def test_gemv_batch_mixed_bits(ms, wide):
+    """Independent problems of different bit widths, shapes and batch sizes (one with
+    outliers; `wide` makes the launch large enough for 4-wave workgroups) in one
+    qlinear_gemv_batch call."""
+    torch, q = gpu()
+    specs = [(2, 512, 1024, 0.0), (3, 256, 2048, 0.0), (6, 8192 if wide else 256, 512, 0.0), (4, 384, 1024, 0.004)]
+    gws, xs, ys, probs, refs = [], [], [], [], []
+    for i, ((bits, n, k, frac), m) in enumerate(zip(specs, ms)):
+        w = workloads.weights_fp16(n, k, 700 + i)
+        if frac:
+            workloads.plant_outliers(w, frac, 700 + i)
+        x = workloads.activations_fp16(m, k, 700 + i)
+        g = GpuWeight(w, bits, frac)
+        xd = to_dev_fp16(x)
+        y = torch.empty((m, n), dtype=torch.int16, device="cuda")
+        gws.append(g), xs.append(xd), ys.append(y)
+        probs.append(q.gemv_problem(g.desc, g.handle(True), xd, k, m, y, n))
+        refs.append(oracle.linear(x, oracle.quantize(w, bits, frac)))
+    q.qlinear_gemv_batch(probs)
+    torch.cuda.synchronize()
+    for y, r in zip(ys, refs):
+        got = from_dev_fp16(y)
+        assert rel_err(got, r) <= TOL, report(got, r)
+
+
 @pytest.mark.parametrize("bits", BITS)
 @pytest.mark.parametrize("m", (17, 130))
 def test_gemm_ragged_dense(bits, m):

@@ -41,6 +41,11 @@ class qp_weight(ctypes.Structure):
                 ("csr_val", ctypes.c_void_p), ("nnz", ctypes.c_int64)]
 
 
+class qp_gemv_problem(ctypes.Structure):
+    _fields_ = [("desc", qp_weight_desc), ("w", qp_weight), ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64),
+                ("m", ctypes.c_int64), ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64)]
+
+
 _vp, _i64, _i32, _dbl, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_size_t
 _D = ctypes.POINTER(qp_weight_desc)
 _W = ctypes.POINTER(qp_weight)
@@ -55,6 +60,7 @@ _SIGS = {
     "qpack_pack": (_i32, [_D, _vp, _vp, _vp]),
     "qpack_unpack": (_i32, [_D, _vp, _vp, _vp]),
     "qlinear_gemv": (_i32, [_D, _W, _vp, _i64, _i64, _vp, _i64, _vp]),
+    "qlinear_gemv_batch": (_i32, [ctypes.POINTER(qp_gemv_problem), _i32, _vp]),
     "qlinear_gemm_workspace_bytes": (_sz, [_D, _i64, _i64]),
     "qlinear_gemm": (_i32, [_D, _W, _vp, _i64, _i64, _vp, _i64, _vp, _sz, _vp]),
     "qlinear_grouped_gemm": (_i32, [_D, _W, _i32, _vp, _i64, _vp, _vp, _i64, _i32, _vp, _i64, _vp]),
@@ -164,6 +170,16 @@ def qpack_unpack(d, packed, codes, stream=None, check=True):
 def qlinear_gemv(d, w, x, ldx, m, y, ldy, stream=None, check=True):
     return _check("qlinear_gemv", lib.qlinear_gemv(ctypes.byref(d), ctypes.byref(w), _ptr(x), ldx, m, _ptr(y),
                                                     ldy, _stream(stream)), check)
+
+
+def gemv_problem(d, w, x, ldx, m, y, ldy):
+    """One entry of qlinear_gemv_batch (device pointers as tensors or ints)."""
+    return qp_gemv_problem(d, w, _ptr(x), ldx, m, _ptr(y), ldy)
+
+
+def qlinear_gemv_batch(problems, stream=None, check=True):
+    arr = (qp_gemv_problem * len(problems))(*problems)
+    return _check("qlinear_gemv_batch", lib.qlinear_gemv_batch(arr, len(problems), _stream(stream)), check)
 
 
 def qlinear_gemm_workspace_bytes(d, m: int, nnz: int) -> int:

@@ -177,29 +177,61 @@ static qp_status check_xy(const qp_weight_desc *d, const uint16_t *x, int64_t ld
     return QP_OK;
 }
 
-qp_status qlinear_gemv(const qp_weight_desc *d, const qp_weight *w, const uint16_t *x, int64_t ldx, int64_t m,
-                       uint16_t *y, int64_t ldy, void *stream)
+// Validated GEMV problem (shared by qlinear_gemv and qlinear_gemv_batch).
+static qp_status gemv_problem(const qp_weight_desc *d, const qp_weight *w, const uint16_t *x, int64_t ldx, int64_t m,
+                              uint16_t *y, int64_t ldy, GemvProblem *p)
 {
     qp_status st = check_desc(d, true);
     if (st != QP_OK) return st;
     if ((st = check_weight(d, w, true)) != QP_OK) return st;
     if ((st = check_xy(d, x, ldx, m, y, ldy, d->n, 4)) != QP_OK) return st;
     if (m > 16) return fail(QP_ERR_UNSUPPORTED, "gemv handles m <= 16 (m=%lld); use qlinear_gemm", (long long)m);
-    SmallArgs a{};
-    a.ex[0] = {(const uint8_t *)w->packed, w->scales, w->zeros};
+    if (m * ldx * 2 > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "x larger than 2 GiB");
+    *p = GemvProblem{};
+    p->w = {(const uint8_t *)w->packed, w->scales, w->zeros};
     if (w->nnz > 0) {
-        a.rowptr = w->csr_rowptr;
-        a.col = w->csr_col;
-        a.val = w->csr_val;
+        p->rowptr = w->csr_rowptr;
+        p->col = w->csr_col;
+        p->val = w->csr_val;
     }
-    a.x = x;
-    a.ldx = ldx;
-    a.m = m;
-    a.n = d->n;
-    a.k = d->k;
-    a.y = y;
-    a.ldy = ldy;
-    return device(launch_gemv(d->bits, a, S(stream)), "qlinear_gemv");
+    p->x = x;
+    p->ldx = ldx;
+    p->m = m;
+    p->n = d->n;
+    p->k = d->k;
+    p->y = y;
+    p->ldy = ldy;
+    p->bits = d->bits;
+    return QP_OK;
+}
+
+qp_status qlinear_gemv(const qp_weight_desc *d, const qp_weight *w, const uint16_t *x, int64_t ldx, int64_t m,
+                       uint16_t *y, int64_t ldy, void *stream)
+{
+    GemvProblem p;
+    qp_status st = gemv_problem(d, w, x, ldx, m, y, ldy, &p);
+    if (st != QP_OK) return st;
+    return device(launch_gemv(p, S(stream)), "qlinear_gemv");
+}
+
+qp_status qlinear_gemv_batch(const qp_gemv_problem *problems, int32_t count, void *stream)
+{
+    if (!problems) return fail(QP_ERR_INVALID_ARG, "problems NULL");
+    if (count < 1 || count > kMaxGemvBatch) return fail(QP_ERR_INVALID_ARG, "count=%d not in 1..%d", count, kMaxGemvBatch);
+    GemvBatch b{};
+    b.count = count;
+    int64_t blocks = 0;
+    int m_max = 1;
+    for (int i = 0; i < count; ++i) {
+        const qp_gemv_problem &q = problems[i];
+        qp_status st = gemv_problem(&q.desc, &q.w, q.x, q.ldx, q.m, q.y, q.ldy, &b.p[i]);
+        if (st != QP_OK) return st;
+        b.p[i].block0 = blocks;
+        blocks += q.desc.n / 16;
+        if (q.m > m_max) m_max = (int)q.m;
+    }
+    if (blocks > 0x7FFFFFFF) return fail(QP_ERR_UNSUPPORTED, "too many row blocks");
+    return device(launch_gemv_batch(b, blocks, m_max, S(stream)), "qlinear_gemv_batch");
 }
 
 size_t qlinear_gemm_workspace_bytes(const qp_weight_desc *d, int64_t m, int64_t nnz)

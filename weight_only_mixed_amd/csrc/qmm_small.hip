@@ -102,28 +102,27 @@ __device__ __forceinline__ void wait_vm()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// One 16-row block of problem p on this workgroup; `ring` is this wave's D slots of `pitch`
+// bytes, `red` the workgroup's reduction buffer.
 template <int B, int NW, int D, int MX>
-__global__ __launch_bounds__(NW * 64) void gemv_kernel(SmallArgs a)
+__device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uint8_t *ring, int pitch,
+                                           f4 (*red)[64])
 {
     using S = RingSlot<B, MX>;
-    __shared__ __attribute__((aligned(16))) uint8_t ring[NW][D][S::kBytes];
-    __shared__ f4 red[NW][64];
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t = lane >> 4, r = lane & 15;
-    const int64_t rb = blockIdx.x;
     const int64_t KT = a.k / kTileK, G = a.k / kGroup;
-    const ExpertPtrs &W = a.ex[0];
 
     GemvBufs bf;
     bf.G = G;
-    bf.w = make_rsrc(W.packed + rb * KT * (512 * B), KT * (512 * B));
-    bf.sc = make_rsrc(W.scales + rb * kTileN * G, kTileN * G * 2);
-    bf.zr = make_rsrc(W.zeros + rb * kTileN * G, kTileN * G);
+    bf.w = make_rsrc(a.w.packed + rb * KT * (512 * B), KT * (512 * B));
+    bf.sc = make_rsrc(a.w.scales + rb * kTileN * G, kTileN * G * 2);
+    bf.zr = make_rsrc(a.w.zeros + rb * kTileN * G, kTileN * G);
     bf.x = make_rsrc(a.x, a.m * a.ldx * 2);  // rows >= m read as zeros
 
     const int64_t nt = KT > wv ? (KT - wv + NW - 1) / NW : 0;  // tiles of this wave
 #pragma unroll
-    for (int s = 0; s < D - 1; ++s) ring_issue<B, MX>(bf, wv + (int64_t)s * NW, lane, a.ldx, ring[wv][s]);
+    for (int s = 0; s < D - 1; ++s) ring_issue<B, MX>(bf, wv + (int64_t)s * NW, lane, a.ldx, ring + s * pitch);
 
     // Activation fragments: lanes of rows >= m keep zeros and never read LDS.
     const bool act = r < a.m;
@@ -133,9 +132,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(SmallArgs a)
     f4 tot = {0.f, 0.f, 0.f, 0.f};
     for (int64_t i = 0; i < nt; ++i) {
         const int64_t kt = wv + i * NW;
-        ring_issue<B, MX>(bf, kt + (int64_t)(D - 1) * NW, lane, a.ldx, ring[wv][(i + D - 1) % D]);
+        ring_issue<B, MX>(bf, kt + (int64_t)(D - 1) * NW, lane, a.ldx, ring + ((i + D - 1) % D) * pitch);
         wait_vm<S::kLoads * (D - 1)>();
-        const uint8_t *slot = ring[wv][i % D];
+        const uint8_t *slot = ring + (i % D) * pitch;
         uint32_t d[2 * B];
 #pragma unroll
         for (int sl = 0; sl < B / 2; ++sl) {
@@ -182,12 +181,49 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(SmallArgs a)
                 s[i] = __builtin_fmaf(h_f(xrow[a.col[p]]), h_f(a.val[p]), s[i]);
         }
     }
-    uint16_t *y = (uint16_t *)a.y + r * a.ldy + rb * kTileN + 4 * t;
+    uint16_t *y = a.y + r * a.ldy + rb * kTileN + 4 * t;
     *(u2 *)y = (u2){pack_h2(s[0], s[1]), pack_h2(s[2], s[3])};
 }
 
+// One problem, one workgroup per 16-row block.
+template <int B, int NW, int D, int MX>
+__global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvProblem a)
+{
+    constexpr int pitch = RingSlot<B, MX>::kBytes;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NW][D][pitch];
+    __shared__ f4 red[NW][64];
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    gemv_block<B, NW, D, MX>(a, blockIdx.x, &ring[wv][0][0], pitch, red);
+}
+
+// Independent problems (mixed bit widths) in one launch: workgroup b serves problem p with
+// block0 <= b < block0 + n/16.  The ring slots are sized for 6-bit tiles.
+template <int NW, int D, int MX>
+__global__ __launch_bounds__(NW * 64) void gemv_batch_kernel(GemvBatch bt)
+{
+    constexpr int pitch = RingSlot<6, MX>::kBytes;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NW][D][pitch];
+    __shared__ f4 red[NW][64];
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t b = blockIdx.x;
+    int p = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxGemvBatch; ++i)
+        if (i < bt.count && b >= bt.p[i].block0) p = i;
+    const GemvProblem &a = bt.p[p];
+    const int64_t rb = b - a.block0;
+    uint8_t *rg = &ring[wv][0][0];
+    switch (a.bits) {
+    case 2: gemv_block<2, NW, D, MX>(a, rb, rg, pitch, red); break;
+    case 3: gemv_block<3, NW, D, MX>(a, rb, rg, pitch, red); break;
+    case 4: gemv_block<4, NW, D, MX>(a, rb, rg, pitch, red); break;
+    case 5: gemv_block<5, NW, D, MX>(a, rb, rg, pitch, red); break;
+    default: gemv_block<6, NW, D, MX>(a, rb, rg, pitch, red); break;
+    }
+}
+
 template <int B, int MX>
-static hipError_t gemv_mx(const SmallArgs &a, hipStream_t st)
+static hipError_t gemv_mx(const GemvProblem &a, hipStream_t st)
 {
     // Wide matrices have row blocks enough to fill the GPU with 4-wave workgroups (more of
     // them fit per CU); narrow ones split each row block's k over 8 waves.
@@ -205,7 +241,7 @@ static hipError_t gemv_mx(const SmallArgs &a, hipStream_t st)
 }
 
 template <int B>
-static hipError_t gemv_bits(const SmallArgs &a, hipStream_t st)
+static hipError_t gemv_bits(const GemvProblem &a, hipStream_t st)
 {
     if (a.m <= 2) return gemv_mx<B, 1>(a, st);
     if (a.m <= 4) return gemv_mx<B, 2>(a, st);
@@ -213,9 +249,9 @@ static hipError_t gemv_bits(const SmallArgs &a, hipStream_t st)
     return gemv_mx<B, 8>(a, st);
 }
 
-hipError_t launch_gemv(int bits, const SmallArgs &a, hipStream_t st)
+hipError_t launch_gemv(const GemvProblem &a, hipStream_t st)
 {
-    switch (bits) {
+    switch (a.bits) {
     case 2: return gemv_bits<2>(a, st);
     case 3: return gemv_bits<3>(a, st);
     case 4: return gemv_bits<4>(a, st);
@@ -223,6 +259,28 @@ hipError_t launch_gemv(int bits, const SmallArgs &a, hipStream_t st)
     case 6: return gemv_bits<6>(a, st);
     }
     return hipErrorInvalidValue;
+}
+
+template <int MX>
+static hipError_t gemv_batch_mx(const GemvBatch &b, int64_t blocks, hipStream_t st)
+{
+    if constexpr (MX >= 4) {
+        hipLaunchKernelGGL((gemv_batch_kernel<4, 2, MX>), dim3((unsigned)blocks), dim3(256), 0, st, b);
+    } else {
+        if (blocks >= 512)
+            hipLaunchKernelGGL((gemv_batch_kernel<4, 2, MX>), dim3((unsigned)blocks), dim3(256), 0, st, b);
+        else
+            hipLaunchKernelGGL((gemv_batch_kernel<8, 2, MX>), dim3((unsigned)blocks), dim3(512), 0, st, b);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_batch(const GemvBatch &b, int64_t blocks, int m_max, hipStream_t st)
+{
+    if (m_max <= 2) return gemv_batch_mx<1>(b, blocks, st);
+    if (m_max <= 4) return gemv_batch_mx<2>(b, blocks, st);
+    if (m_max <= 8) return gemv_batch_mx<4>(b, blocks, st);
+    return gemv_batch_mx<8>(b, blocks, st);
 }
 
 }  // namespace qp

@@ -48,21 +48,28 @@ struct ExpertPtrs {
     const uint16_t *scales;
     const uint8_t *zeros;
 };
-struct SmallArgs {
-    ExpertPtrs ex[kMaxExperts];
-    const int32_t *rowptr;   // CSR of expert 0 (plain GEMV only), or null
+// One decode GEMV problem, and a batch of independent ones run in a single launch.
+constexpr int kMaxGemvBatch = 8;
+struct GemvProblem {
+    ExpertPtrs w;
+    const int32_t *rowptr;  // outlier CSR, or null
     const int32_t *col;
     const uint16_t *val;
     const uint16_t *x;
     int64_t ldx;
-    const int32_t *row_src;  // null: row r reads x row r
-    const int32_t *offsets;  // null: rows [0, m)
-    int64_t m;
-    int64_t n, k;
-    void *y;
+    int64_t m, n, k;
+    uint16_t *y;
     int64_t ldy;
+    int32_t bits;
+    int32_t reserved;
+    int64_t block0;  // batch: first workgroup of this problem
 };
-hipError_t launch_gemv(int bits, const SmallArgs &a, hipStream_t st);
+struct GemvBatch {
+    GemvProblem p[kMaxGemvBatch];
+    int32_t count;
+};
+hipError_t launch_gemv(const GemvProblem &p, hipStream_t st);
+hipError_t launch_gemv_batch(const GemvBatch &b, int64_t blocks, int m_max, hipStream_t st);
 
 // Dequant-GEMM on the matrix cores: a plain layer (ex[0], optional outliers) or a group of
 // routed experts (ex[e] over the sorted rows offsets[e] .. offsets[e+1]).
