@@ -325,10 +325,12 @@ def main():
     log(f"bench: {args.copies} copies, {total_copy_bytes / 2**30:.2f} GiB of packed weights")
 
     def step(c):
+        # every GEMV of a step reads its own weight copy, so no launch finds the previous
+        # launch's bytes in the Infinity Cache
         for b in bits_list:
             d, hs, _ = W[b]
-            for m in m_list:
-                q.qlinear_gemv(d, hs[c % args.copies], X[m], K, m, Y[(b, m)], N)
+            for mi, m in enumerate(m_list):
+                q.qlinear_gemv(d, hs[(c * len(m_list) + mi) % args.copies], X[m], K, m, Y[(b, m)], N)
 
     stream = torch.cuda.Stream()
     graphs = []

@@ -1,16 +1,21 @@
 // Prefill dequant-GEMM (m >= 64) on gfx950 matrix cores.
 //
 // Prior art: the fused dequant-GEMM of the single-GPU 70B page (s3) loads an INT4 tile into
-// shared memory, dequantizes it and feeds Tensor Cores.  On CDNA4 the roles are split
-// differently.  Each of the eight waves of a workgroup owns two 16-row weight blocks: it loads
-// their packed tiles with 16-byte loads straight into registers (one k-tile ahead) and unpacks
-// them into exact fp16 (q - zp) A operands itself, so weights never pass through LDS and each
-// weight is unpacked once per 128-row activation block.  The activation tile (128 rows x one
-// 128-k group, 32 KB) is shared by the eight waves (256 weight rows) through a four-slot LDS
-// ring filled by buffer-to-LDS DMA three groups ahead (no registers), with the 16-byte chunks
-// of each row XOR-swizzled by the row index so the matrix-core fragment reads (16 rows, same
-// column) hit distinct banks.  Every 128-k group is accumulated on the matrix cores in fp32
-// and then scaled by its fp16 scale in fp32.
+// shared memory, dequantizes it and feeds Tensor Cores.  On CDNA4 the work is split
+// differently.  Each of the eight waves of a workgroup owns two 16-row weight blocks and
+// unpacks them itself into exact fp16 (q - zp) matrix-core A operands held in registers, so
+// each weight is unpacked once per 128 activation rows and no unpacked weight passes through
+// LDS.  The packed tiles are staged HBM -> LDS by buffer-to-LDS DMA two k-tiles ahead, each
+// wave into its own part of a two-slot ring (no registers, no barrier).  The activation tile
+// (128 rows x one 128-k group, 32 KB) is shared by the eight waves (256 weight rows) through
+// a two-slot LDS ring filled by DMA one group ahead, its 16-byte chunks XOR-swizzled by row so
+// the fragment reads (16 rows, same column) hit distinct banks.
+//
+// The k loop is software-pipelined across groups: while the matrix cores multiply group g,
+// the vector ALU unpacks group g+1 and applies group g's scales, tile by tile, with the
+// scheduler told to interleave one MFMA, one fragment read and two vector ops, so every wave
+// keeps both units busy.  Every 128-k group is accumulated on the matrix cores in fp32 and
+// then scaled by its fp16 scale in fp32 (mixed-bit page, s4.2).
 //
 // Outlier add-back (70B page, s2): the held-out fp16 weights are added in fp32 before the one
 // fp16 rounding of y.  Two small kernels run first: one writes x transposed (x^T) into the
@@ -22,6 +27,8 @@
 //
 // Workgroups are ordered so that the activation blocks of one weight tile run on the same XCD
 // (block b runs on XCD b % 8), where they share that XCD's L2 copy of the packed weights.
+#include <utility>
+
 #include "bufio.h"
 #include "unpack.h"
 
@@ -33,18 +40,32 @@ constexpr int kWaves = 8;
 constexpr int kRBW = 2;                      // 16-row weight blocks per wave
 constexpr int kMT = 8;                       // 16-row activation tiles per workgroup
 constexpr int kNT = kWaves * kRBW * kTileN;  // 256 weight rows per workgroup
-constexpr int kRing = 4;                     // activation ring slots
-constexpr int kAhead = kRing - 1;            // groups the activation DMA runs ahead
-constexpr int kDmaOps = 4;                   // DMA instructions per wave per group
 constexpr int kMRows = kMT * 16;             // 128 activation rows per workgroup
 constexpr int kRowBytes = 128 * 2;           // one 128-k group of one activation row
+constexpr int kXSlot = kMRows * kRowBytes;   // one activation slot: 32 KB
+constexpr int kDmaX = kXSlot / 1024 / kWaves;  // activation DMA instructions per wave per group
+
+// LDS staging of one wave's row block for one k-tile: the lane chunks as in the device layout
+// (B/2 pieces of 16 bytes per lane; for odd B the 8-byte tail as two 4-byte words 256 bytes
+// apart).
+template <int B>
+struct WStage {
+    static constexpr int kBytes = 512 * B;
+    static constexpr int kOps = B / 2 + 2 * (B & 1);  // DMA instructions per row block
+    static constexpr int kSlot = kWaves * kRBW * kBytes;
+};
+template <int B>
+constexpr int kWOps = kRBW * WStage<B>::kOps;  // weight DMA instructions per wave per k-tile
 
 // LDS byte offset of 16-byte chunk c (8 k values) of activation row `row`.
 __device__ __forceinline__ int xs_off(int row, int c) { return row * kRowBytes + ((c ^ (row & 15)) << 4); }
 
-// Shared memory of one workgroup: the activation ring.
+// Shared memory of one workgroup: a two-slot activation ring (one 128-k group per slot) and
+// a two-slot ring of packed weight tiles (one k-tile per slot; every wave owns its part).
+template <int B>
 struct Smem {
-    uint8_t xs[kRing][kMRows * kRowBytes];
+    uint8_t xs[2][kXSlot];
+    uint8_t ws[2][WStage<B>::kSlot];
 };
 
 // Buffers of one workgroup.  Every wave-uniform offset passed as soffset stays inside the
@@ -54,8 +75,17 @@ struct Bufs {
     rsrc_t x;              // activation rows [m0, m)
     rsrc_t w[kRBW];        // packed tiles of row block rb0 + u (empty past the last block)
     rsrc_t sc[kRBW], zr[kRBW];
-    uint32_t xoff[kDmaOps];  // this lane's source of LDS-DMA piece it (row offset + chunk)
+    uint32_t xoff[kDmaX];  // this lane's source of LDS-DMA piece it (row offset + chunk)
 };
+
+__device__ __forceinline__ void lds_dma16(rsrc_t r, uint8_t *lds, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(rsrc_t r, uint8_t *lds, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, voff, soff, 0, 0);
+}
 
 // DMA the 128 x 128-k activation tile of group g into LDS slot `dst` (this wave's 4 KB).
 // Lane L of piece `it` fills LDS bytes [16L, 16L+16) of a 1 KB run = row 4*(4*wv+it) + L/16,
@@ -64,20 +94,68 @@ __device__ __forceinline__ void dma_x(const Bufs &bf, int64_t g, uint8_t *dst, i
 {
     const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)g * 256);  // column of group g
 #pragma unroll
-    for (int it = 0; it < kDmaOps; ++it) {
-        uint8_t *base = dst + (wv * kDmaOps + it) * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(bf.x, (__attribute__((address_space(3))) void *)base, 16,
-                                                 bf.xoff[it], soff, 0, 0);
+    for (int it = 0; it < kDmaX; ++it) lds_dma16(bf.x, dst + (wv * kDmaX + it) * 1024, bf.xoff[it], soff);
+}
+
+// DMA this wave's packed tiles of k-tile kt into its part `dst` of a weight slot.
+template <int B>
+__device__ __forceinline__ void dma_w(const Bufs &bf, int64_t kt, uint8_t *dst, int lane)
+{
+    const uint32_t tile = __builtin_amdgcn_readfirstlane((uint32_t)(kt * (512 * B)));
+#pragma unroll
+    for (int u = 0; u < kRBW; ++u) {
+        uint8_t *base = dst + u * WStage<B>::kBytes;
+#pragma unroll
+        for (int s = 0; s < B / 2; ++s) lds_dma16(bf.w[u], base + 1024 * s, 16 * lane, tile + 1024 * s);
+        if constexpr (B & 1) {
+            lds_dma4(bf.w[u], base + 1024 * (B / 2), 8 * lane, tile + 1024 * (B / 2));
+            lds_dma4(bf.w[u], base + 1024 * (B / 2) + 256, 8 * lane + 4, tile + 1024 * (B / 2));
+        }
     }
 }
 
-// Loads issued by load_w<B> (per row block: the packed pieces, one zero-point load, four
-// scale loads).
+// This lane's chunk of one staged row block.
 template <int B>
-constexpr int kLoadWOps = kRBW * (B / 2 + (B & 1) + 5);
+__device__ __forceinline__ void read_chunk(const uint8_t *base, int lane, uint32_t *d)
+{
+#pragma unroll
+    for (int s = 0; s < B / 2; ++s) {
+        const u4 v = *(const u4 *)(base + 1024 * s + 16 * lane);
+        d[4 * s + 0] = v[0];
+        d[4 * s + 1] = v[1];
+        d[4 * s + 2] = v[2];
+        d[4 * s + 3] = v[3];
+    }
+    if constexpr (B & 1) {
+        d[2 * B - 2] = *(const uint32_t *)(base + 1024 * (B / 2) + 4 * lane);
+        d[2 * B - 1] = *(const uint32_t *)(base + 1024 * (B / 2) + 256 + 4 * lane);
+    }
+}
 
-// Wait until at most N of this wave's loads are outstanding (they retire in order), then
-// synchronise the workgroup.
+// Scales and zero points of one k-tile (both groups) for this lane: the zero points of its
+// weight row r, the scales of the accumulator rows 4t + i.
+struct SZ {
+    uint32_t zz[kRBW];
+    uint32_t sc[kRBW][4];
+};
+constexpr int kSZOps = kRBW * 5;
+
+__device__ __forceinline__ void load_sz(const Bufs &bf, int64_t G, int64_t kt, int lane, SZ &z)
+{
+    const int t = lane >> 4, r = lane & 15;
+    const uint32_t vz = (uint32_t)(r * G), vs = (uint32_t)(4 * t * G * 2);
+    const uint32_t zo = __builtin_amdgcn_readfirstlane((uint32_t)(2 * kt));
+#pragma unroll
+    for (int u = 0; u < kRBW; ++u) {
+        z.zz[u] = ld2(bf.zr[u], vz, zo);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            z.sc[u][i] = ld4(bf.sc[u], vs, __builtin_amdgcn_readfirstlane((uint32_t)((i * G + 2 * kt) * 2)));
+    }
+}
+
+// Wait until at most N of this wave's vector-memory operations are outstanding (they retire
+// in order), then synchronise the workgroup.
 template <int N>
 __device__ __forceinline__ void wait_and_sync()
 {
@@ -87,162 +165,226 @@ __device__ __forceinline__ void wait_and_sync()
 }
 
 template <int B>
-struct WTile {
-    uint32_t d[kRBW][2 * B];
-    uint32_t zz[kRBW];
-    uint32_t sc[kRBW][4];
-};
-
-// Weight tile kt of this wave's row blocks.
-template <int B>
-__device__ __forceinline__ void load_w(const Bufs &bf, int64_t G, int64_t kt, int lane, WTile<B> &w)
+__device__ __forceinline__ void set_gc(const SZ &z, int half, GroupConst<B> (&gc)[kRBW])
 {
-    const int t = lane >> 4, r = lane & 15;
-    const uint32_t vw = 16 * lane, vw8 = 8 * lane;
-    const uint32_t vz = (uint32_t)(r * G), vs = (uint32_t)(4 * t * G * 2);
-    const uint32_t tile = __builtin_amdgcn_readfirstlane((uint32_t)(kt * (512 * B)));
-    const uint32_t zo = __builtin_amdgcn_readfirstlane((uint32_t)(2 * kt));
+#pragma unroll
+    for (int u = 0; u < kRBW; ++u) gc[u].set(half == 0 ? (z.zz[u] & 0xFF) : ((z.zz[u] >> 8) & 0xFF));
+}
+
+// Unpack block J of group half H (blocks 4H .. 4H+3 of the chunk) of row block U.
+template <int B, int H, int U, int J>
+__device__ __forceinline__ void unpack_block(const uint32_t *d, const GroupConst<B> (&gc)[kRBW], h8 (&A)[kRBW][4])
+{
+    A[U][J] = BlockUnpack<B, 4 * H + J>::run(d, gc[U]);
+}
+
+// All of one group's A operands (this wave's two row blocks) from a staged weight slot part.
+template <int B, int H>
+__device__ __forceinline__ void unpack_group(const uint8_t *wpart, const SZ &z, int lane, h8 (&A)[kRBW][4])
+{
+    GroupConst<B> gc[kRBW];
+    set_gc<B>(z, H, gc);
+    uint32_t d[2 * B];
+    read_chunk<B>(wpart, lane, d);
+    unpack_block<B, H, 0, 0>(d, gc, A);
+    unpack_block<B, H, 0, 1>(d, gc, A);
+    unpack_block<B, H, 0, 2>(d, gc, A);
+    unpack_block<B, H, 0, 3>(d, gc, A);
+    read_chunk<B>(wpart + WStage<B>::kBytes, lane, d);
+    unpack_block<B, H, 1, 0>(d, gc, A);
+    unpack_block<B, H, 1, 1>(d, gc, A);
+    unpack_block<B, H, 1, 2>(d, gc, A);
+    unpack_block<B, H, 1, 3>(d, gc, A);
+}
+
+// Matrix-core chains of activation tile MT (fragments X) for both row blocks.
+__device__ __forceinline__ void tile_mma(const h8 (&A)[kRBW][4], const h8 (&X)[4], f4 (&acc)[kRBW])
+{
+#pragma unroll
+    for (int u = 0; u < kRBW; ++u) acc[u] = mfma16(A[u][0], X[0], (f4){0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int j4 = 1; j4 < 4; ++j4)
+#pragma unroll
+        for (int u = 0; u < kRBW; ++u) acc[u] = mfma16(A[u][j4], X[j4], acc[u]);
+}
+
+// tot[.][mt] += s * acc (fp32; the scale is the fp16 half SH of each packed scale word).
+template <int SH>
+__device__ __forceinline__ void scale_acc(const uint32_t (&sc)[kRBW][4], const f4 (&acc)[kRBW], f4 (&tot)[kRBW][kMT],
+                                          int mt)
+{
 #pragma unroll
     for (int u = 0; u < kRBW; ++u) {
 #pragma unroll
-        for (int sl = 0; sl < B / 2; ++sl) {
-            const u4 v = ld16(bf.w[u], vw, tile + 1024 * sl);
-            w.d[u][4 * sl + 0] = v[0];
-            w.d[u][4 * sl + 1] = v[1];
-            w.d[u][4 * sl + 2] = v[2];
-            w.d[u][4 * sl + 3] = v[3];
-        }
-        if (B & 1) {
-            const u2 v = ld8(bf.w[u], vw8, tile + 1024 * (B / 2));
-            w.d[u][2 * B - 2] = v[0];
-            w.d[u][2 * B - 1] = v[1];
-        }
-        w.zz[u] = ld2(bf.zr[u], vz, zo);
-#pragma unroll
         for (int i = 0; i < 4; ++i)
-            w.sc[u][i] = ld4(bf.sc[u], vs, __builtin_amdgcn_readfirstlane((uint32_t)((i * G + 2 * kt) * 2)));
+            tot[u][mt][i] = __builtin_fmaf(SH == 0 ? lo_h(sc[u][i]) : hi_h(sc[u][i]), acc[u][i], tot[u][mt][i]);
+        asm volatile("" : "+v"(tot[u][mt]));
     }
 }
 
-// One 128-k group: unpack this wave's four blocks of group GI for each row block, then
-// multiply them by the eight 16-row activation tiles from LDS, scale and accumulate.  The
-// tile loop is software-pipelined: the fragment reads of tile mt+1 are issued before the
-// matrix-core chain of tile mt, and the fp32 scale-accumulate of tile mt-1 runs on the
-// vector ALU while that chain executes.
-template <int B, int GI, bool FULL>
-__device__ __forceinline__ void group_step(const WTile<B> &w, const uint8_t *xs, int lane, int nmt,
+// Activation fragment reads run kXA tiles ahead of the matrix core (ring of kXR tiles).
+constexpr int kXA = 2, kXR = kXA + 1;
+
+// Unpack blocks [F, L) of the next group (block i = row block i / 4, block i % 4).
+template <int B, int NH, int F, int L>
+__device__ __forceinline__ void unpack_range(const uint32_t *d, const GroupConst<B> (&gc)[kRBW], h8 (&A)[kRBW][4])
+{
+    if constexpr (F < L) {
+        unpack_block<B, NH, F / 4, F % 4>(d, gc, A);
+        unpack_range<B, NH, F + 1, L>(d, gc, A);
+    }
+}
+
+// One activation tile of a full step of NMT tiles: fragment reads of tile MT+kXA, the
+// matrix-core chains of tile MT, the scale-accumulate of tile MT-1 and a share of the next
+// group's unpack (its eight blocks spread evenly over the NMT tiles; row block 1's chunk is
+// read at tile NMT/2), interleaved so every wave keeps its matrix core and vector ALU busy.
+template <int B, int SH, int NH, int NMT, int MT>
+__device__ __forceinline__ void full_tile(const h8 (&Acur)[kRBW][4], h8 (&Anxt)[kRBW][4], const uint32_t (&sc)[kRBW][4],
+                                          const GroupConst<B> (&gc)[kRBW], const uint8_t *xs, const uint8_t *wpart,
+                                          int lane, uint32_t (&d)[2 * B], h8 (&X)[kXR][4], f4 (&acc)[2][kRBW],
+                                          f4 (&tot)[kRBW][kMT])
+{
+    static_assert(NMT % 2 == 0 && NMT <= kMT, "even tile count");
+    constexpr int cur = MT & 1, nxt = cur ^ 1;
+    const int t = lane >> 4, r = lane & 15;
+    if constexpr (MT + kXA < NMT) {
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4)
+            X[(MT + kXA) % kXR][j4] = *(const h8 *)(xs + xs_off(16 * (MT + kXA) + r, 4 * j4 + t));
+    }
+    if constexpr (MT == 0) read_chunk<B>(wpart, lane, d);
+    if constexpr (MT == NMT / 2) read_chunk<B>(wpart + WStage<B>::kBytes, lane, d);
+    tile_mma(Acur, X[MT % kXR], acc[cur]);
+    if constexpr (MT > 0) scale_acc<SH>(sc, acc[nxt], tot, MT - 1);
+    unpack_range<B, NH, MT * 8 / NMT, (MT + 1) * 8 / NMT>(d, gc, Anxt);
+    if constexpr (MT == NMT - 1) scale_acc<SH>(sc, acc[cur], tot, MT);
+    // per matrix-core op: one fragment read and two vector ALU ops issued behind it
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int B, int SH, int NH, int NMT, int... MT>
+__device__ __forceinline__ void full_tiles(std::integer_sequence<int, MT...>, const h8 (&Acur)[kRBW][4],
+                                           h8 (&Anxt)[kRBW][4], const uint32_t (&sc)[kRBW][4],
+                                           const GroupConst<B> (&gc)[kRBW], const uint8_t *xs, const uint8_t *wpart,
+                                           int lane, uint32_t (&d)[2 * B], h8 (&X)[kXR][4], f4 (&acc)[2][kRBW],
+                                           f4 (&tot)[kRBW][kMT])
+{
+    (full_tile<B, SH, NH, NMT, MT>(Acur, Anxt, sc, gc, xs, wpart, lane, d, X, acc, tot), ...);
+}
+
+// One 128-k group step: A(g) = Acur times the activation tile of group g (slot xs), scale
+// half SH of scale words sc; meanwhile A(g+1) is unpacked into Anxt from half NH of the
+// staged tile wpart with zero points zn.  NMT > 0: the first NMT 16-row activation tiles all
+// hold rows; NMT == 0: nmt tiles hold rows (ragged), and the next group is unpacked first.
+template <int B, int SH, int NH, int NMT>
+__device__ __forceinline__ void group_step(const h8 (&Acur)[kRBW][4], h8 (&Anxt)[kRBW][4], const uint32_t (&sc)[kRBW][4],
+                                           const SZ &zn, const uint8_t *xs, const uint8_t *wpart, int lane, int nmt,
                                            f4 (&tot)[kRBW][kMT])
 {
     const int t = lane >> 4, r = lane & 15;
-    h8 A[kRBW][4];
-    float s[kRBW][4];
-#pragma unroll
-    for (int u = 0; u < kRBW; ++u) {
-        GroupConst<B> gc;
-        gc.set(GI == 0 ? (w.zz[u] & 0xFF) : ((w.zz[u] >> 8) & 0xFF));
-        A[u][0] = BlockUnpack<B, 4 * GI + 0>::run(w.d[u], gc);
-        A[u][1] = BlockUnpack<B, 4 * GI + 1>::run(w.d[u], gc);
-        A[u][2] = BlockUnpack<B, 4 * GI + 2>::run(w.d[u], gc);
-        A[u][3] = BlockUnpack<B, 4 * GI + 3>::run(w.d[u], gc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[u][i] = GI == 0 ? lo_h(w.sc[u][i]) : hi_h(w.sc[u][i]);
-    }
-    h8 X[2][4];
     f4 acc[2][kRBW];
+    if constexpr (NMT > 0) {
+        h8 X[kXR][4];
 #pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4) X[0][j4] = *(const h8 *)(xs + xs_off(r, 4 * j4 + t));
-    __builtin_amdgcn_sched_barrier(0);
+        for (int mt = 0; mt < kXA; ++mt)
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) {
-        if (!FULL && mt >= nmt) break;  // uniform: tiles past the workgroup's rows are skipped
-        const int cur = mt & 1, nxt = cur ^ 1;
-        if (mt + 1 < kMT && (FULL || mt + 1 < nmt)) {
-            const int row = 16 * (mt + 1) + r;
+            for (int j4 = 0; j4 < 4; ++j4) X[mt][j4] = *(const h8 *)(xs + xs_off(16 * mt + r, 4 * j4 + t));
+        GroupConst<B> gc[kRBW];
+        set_gc<B>(zn, NH, gc);
+        uint32_t d[2 * B];
+        __builtin_amdgcn_sched_barrier(0);
+        full_tiles<B, SH, NH, NMT>(std::make_integer_sequence<int, NMT>{}, Acur, Anxt, sc, gc, xs, wpart, lane, d, X,
+                                   acc, tot);
+    } else {
+        h8 X[2][4];
 #pragma unroll
-            for (int j4 = 0; j4 < 4; ++j4) X[nxt][j4] = *(const h8 *)(xs + xs_off(row, 4 * j4 + t));
-        }
-        // keep the reads ahead of the chain (else they reuse the chain's fragment registers
-        // and issue too late to hide their latency)
+        for (int j4 = 0; j4 < 4; ++j4) X[0][j4] = *(const h8 *)(xs + xs_off(r, 4 * j4 + t));
+        unpack_group<B, NH>(wpart, zn, lane, Anxt);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < kRBW; ++u) acc[cur][u] = mfma16(A[u][0], X[cur][0], (f4){0.f, 0.f, 0.f, 0.f});
+        for (int mt = 0; mt < kMT; ++mt) {
+            if (mt >= nmt) break;  // uniform: tiles past the workgroup's rows are skipped
+            const int cur = mt & 1, nxt = cur ^ 1;
+            if (mt + 1 < kMT && mt + 1 < nmt) {
+                const int row = 16 * (mt + 1) + r;
 #pragma unroll
-        for (int j4 = 1; j4 < 4; ++j4)
-#pragma unroll
-            for (int u = 0; u < kRBW; ++u) acc[cur][u] = mfma16(A[u][j4], X[cur][j4], acc[cur][u]);
-        if (mt > 0) {
-#pragma unroll
-            for (int u = 0; u < kRBW; ++u) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    tot[u][mt - 1][i] = __builtin_fmaf(s[u][i], acc[nxt][u][i], tot[u][mt - 1][i]);
-                asm volatile("" : "+v"(tot[u][mt - 1]));
+                for (int j4 = 0; j4 < 4; ++j4) X[nxt][j4] = *(const h8 *)(xs + xs_off(row, 4 * j4 + t));
             }
+            __builtin_amdgcn_sched_barrier(0);
+            tile_mma(Acur, X[cur], acc[cur]);
+            if (mt > 0) scale_acc<SH>(sc, acc[nxt], tot, mt - 1);
+            if (mt + 1 == nmt) scale_acc<SH>(sc, acc[cur], tot, mt);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (FULL ? mt + 1 == kMT : mt + 1 == nmt) {  // the last tile's scale-accumulate
-#pragma unroll
-            for (int u = 0; u < kRBW; ++u) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) tot[u][mt][i] = __builtin_fmaf(s[u][i], acc[cur][u][i], tot[u][mt][i]);
-                asm volatile("" : "+v"(tot[u][mt]));
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// The k loop of a workgroup.  Activation ring: the tile of group g sits in slot g % kRing; the
-// DMA of group g + kAhead is issued at the start of step g (groups past the end reload the
-// last one into a slot that is never read, and weight tiles past the end reload the last
-// tile into the idle register buffer), so every step issues the same loads and the wait
-// counts are fixed.  Order of a wave's loads: [DMA g+3] then, on even g, [weights of tile
-// g/2 + 1].  The tile of group g+1 is needed after step g; the loads younger than its DMA
-// (issued at step g-2) are the DMAs of g+2 and g+3 plus the weight batches of the even
-// steps among g-2, g-1, g.  FULL: all eight 16-row activation tiles hold rows.
-template <int B, bool FULL>
-__device__ __forceinline__ void k_loop(const Bufs &bf, Smem &sm, int64_t KT, int64_t G, int wv, int lane, int nmt,
+// The k loop of a workgroup.  Step g multiplies group g and unpacks group g+1.
+//  - Activations: slot g % 2 holds group g; the DMA of group g+1 into the other slot is
+//    issued at the start of step g (its previous contents were read in step g-1, which
+//    ended with a workgroup barrier) and waited for at the end of step g.
+//  - Weights: slot t % 2 holds k-tile t (every wave stages and reads only its own part, so
+//    no barrier is involved).  Tile t is read while unpacking groups 2t and 2t+1, in steps
+//    2t-1 and 2t; the DMA of tile t+2 into slot t % 2 is issued at the start of step 2t+1 and
+//    waited for at the end of step 2t+2.
+//  - Scales and zero points of tile t are loaded into registers at the start of step 2t-2.
+//  Each step issues its DMAs first, so the waits are: vmcnt(0) after steps 2t, and
+//  vmcnt(weight DMAs) after steps 2t+1.  Loads past the end are clamped to the last group or
+//  tile and land in slots that are not read again; the A operands unpacked from them are
+//  discarded.
+template <int B, int NMT>
+__device__ __forceinline__ void k_loop(const Bufs &bf, Smem<B> &sm, int64_t KT, int64_t G, int wv, int lane, int nmt,
                                        f4 (&tot)[kRBW][kMT])
 {
     const int64_t GN = 2 * KT;  // groups
     auto gclamp = [&](int64_t g) { return g < GN ? g : GN - 1; };
     auto tclamp = [&](int64_t t) { return t < KT ? t : KT - 1; };
-    WTile<B> wa, wb;
-    dma_x(bf, 0, sm.xs[0], wv);
-    dma_x(bf, gclamp(1), sm.xs[1], wv);
-    __builtin_amdgcn_sched_barrier(0);
-    load_w<B>(bf, G, 0, lane, wa);
-    __builtin_amdgcn_sched_barrier(0);
-    dma_x(bf, gclamp(2), sm.xs[2], wv);
-    wait_and_sync<kDmaOps>();  // group 0's DMA and tile 0's weights are in
+    uint8_t *w0 = sm.ws[0] + wv * (kRBW * WStage<B>::kBytes);  // this wave's parts of the weight slots
+    uint8_t *w1 = sm.ws[1] + wv * (kRBW * WStage<B>::kBytes);
+    SZ z0, z1;  // tiles of even / odd index
+    h8 Aa[kRBW][4], Ab[kRBW][4];
 
-    // Two k-tiles (four groups) per iteration so both weight buffers are named statically.
+    dma_x(bf, 0, sm.xs[0], wv);
+    dma_w<B>(bf, 0, w0, lane);
+    dma_w<B>(bf, tclamp(1), w1, lane);
+    load_sz(bf, G, 0, lane, z0);
+    wait_and_sync<0>();
+    unpack_group<B, 0>(w0, z0, lane, Aa);
+
     for (int64_t kt = 0; kt < KT; kt += 2) {
         const int64_t g = 2 * kt;
-        // group g (tile kt, first half): fetch tile kt+1's weights
-        dma_x(bf, gclamp(g + 3), sm.xs[(g + 3) % kRing], wv);
+        // step g: tile kt, first group; unpack tile kt's second group
+        dma_x(bf, gclamp(g + 1), sm.xs[1], wv);
+        load_sz(bf, G, tclamp(kt + 1), lane, z1);
         __builtin_amdgcn_sched_barrier(0);
-        load_w<B>(bf, G, tclamp(kt + 1), lane, wb);
+        group_step<B, 0, 1, NMT>(Aa, Ab, z0.sc, z0, sm.xs[0], w0, lane, nmt, tot);
+        wait_and_sync<0>();
+        // step g+1: tile kt, second group; unpack tile kt+1's first group
+        dma_x(bf, gclamp(g + 2), sm.xs[0], wv);
+        dma_w<B>(bf, tclamp(kt + 2), w0, lane);
         __builtin_amdgcn_sched_barrier(0);
-        group_step<B, 0, FULL>(wa, sm.xs[g % kRing], lane, nmt, tot);
-        wait_and_sync<2 * kDmaOps + 2 * kLoadWOps<B>>();
-        // group g+1 (tile kt, second half)
-        dma_x(bf, gclamp(g + 4), sm.xs[(g + 4) % kRing], wv);
-        __builtin_amdgcn_sched_barrier(0);
-        group_step<B, 1, FULL>(wa, sm.xs[(g + 1) % kRing], lane, nmt, tot);
-        wait_and_sync<2 * kDmaOps + kLoadWOps<B>>();
+        group_step<B, 1, 0, NMT>(Ab, Aa, z0.sc, z1, sm.xs[1], w1, lane, nmt, tot);
+        wait_and_sync<kWOps<B>>();
         if (kt + 1 >= KT) break;
-        // group g+2 (tile kt+1, first half): fetch tile kt+2's weights
-        dma_x(bf, gclamp(g + 5), sm.xs[(g + 5) % kRing], wv);
+        // step g+2: tile kt+1, first group; unpack its second group
+        dma_x(bf, gclamp(g + 3), sm.xs[1], wv);
+        load_sz(bf, G, tclamp(kt + 2), lane, z0);
         __builtin_amdgcn_sched_barrier(0);
-        load_w<B>(bf, G, tclamp(kt + 2), lane, wa);
+        group_step<B, 0, 1, NMT>(Aa, Ab, z1.sc, z1, sm.xs[0], w1, lane, nmt, tot);
+        wait_and_sync<0>();
+        // step g+3: tile kt+1, second group; unpack tile kt+2's first group
+        dma_x(bf, gclamp(g + 4), sm.xs[0], wv);
+        dma_w<B>(bf, tclamp(kt + 3), w1, lane);
         __builtin_amdgcn_sched_barrier(0);
-        group_step<B, 0, FULL>(wb, sm.xs[(g + 2) % kRing], lane, nmt, tot);
-        wait_and_sync<2 * kDmaOps + 2 * kLoadWOps<B>>();
-        // group g+3 (tile kt+1, second half)
-        dma_x(bf, gclamp(g + 6), sm.xs[(g + 6) % kRing], wv);
-        __builtin_amdgcn_sched_barrier(0);
-        group_step<B, 1, FULL>(wb, sm.xs[(g + 3) % kRing], lane, nmt, tot);
-        wait_and_sync<2 * kDmaOps + kLoadWOps<B>>();
+        group_step<B, 1, 0, NMT>(Ab, Aa, z1.sc, z0, sm.xs[1], w0, lane, nmt, tot);
+        wait_and_sync<kWOps<B>>();
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may land after the workgroup ends
 }
@@ -253,20 +395,48 @@ __device__ __forceinline__ void k_loop(const Bufs &bf, Smem &sm, int64_t KT, int
 // grouped epilogues.
 enum { kPlain = 0, kOutl = 1, kGroupNone = 2, kGroupSwiglu = 3, kGroupRowsF32 = 4 };
 
-// FULL: every workgroup's eight 16-row activation tiles hold rows (a launch over whole
-// 128-row tiles); otherwise tiles past the workgroup's rows are skipped.  mtile0: the first
-// 128-row tile of the launch (plain layer).
-template <int B, int MODE, bool FULL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(GemmArgs a,
-                                                                                            int64_t mtile0,
-                                                                                            int64_t m_tiles)
+// Workgroup -> (weight tile, activation rows) of a plain layer: up to two rectangles of
+// weight tiles [nt0, nt0 + nnt) x activation tiles of mh rows starting at row m0, numbered
+// from workgroup wg0 on.  Where nnt and wg0 are multiples of 8, the activation tiles of one
+// weight tile get workgroups with equal index mod 8, which the dispatcher places on the same
+// XCD, so they share its L2 copy of the packed weights.
+struct TileRect {
+    int32_t nt0, nnt, m0, mtiles, wg0;
+};
+struct TilePlan {
+    TileRect r[2];
+    int32_t nr;
+    int32_t mh;  // activation rows per tile
+};
+
+__device__ __forceinline__ void plan_tile(const TilePlan &p, int64_t b, int64_t &nt, int64_t &m0)
+{
+    const TileRect &R = (p.nr > 1 && b >= p.r[1].wg0) ? p.r[1] : p.r[0];
+    const int64_t local = b - R.wg0;
+    int64_t ntl, mt;
+    if (R.nnt % 8 == 0 && R.wg0 % 8 == 0) {
+        const int64_t xcd = local % 8, l8 = local / 8;
+        ntl = (l8 / R.mtiles) * 8 + xcd;
+        mt = l8 % R.mtiles;
+    } else {
+        ntl = local % R.nnt;
+        mt = local / R.nnt;
+    }
+    nt = R.nt0 + ntl;
+    m0 = R.m0 + mt * p.mh;
+}
+
+// NMT > 0: every workgroup's first NMT 16-row activation tiles hold rows; NMT == 0: a ragged
+// workgroup (the last activation rows of a layer, or an expert's rows), tiles past its rows
+// are skipped.
+template <int B, int MODE, int NMT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(GemmArgs a, TilePlan plan)
 {
     constexpr bool OUTL = MODE == kOutl, GROUPED = MODE >= kGroupNone;
-    __shared__ __attribute__((aligned(16))) Smem sm;
+    __shared__ __attribute__((aligned(16))) Smem<B> sm;
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t = lane >> 4, r = lane & 15;
     const int64_t KT = a.k / kTileK, G = a.k / kGroup;
-    const int64_t n_tiles = (a.n + kNT - 1) / kNT;
     int64_t nt, m0, mend;  // weight tile; sorted rows [m0, mend) of this workgroup
     int e = 0;
     if constexpr (GROUPED) {
@@ -278,18 +448,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (m0 >= r1) return;  // the whole workgroup: this expert has fewer row tiles
         mend = r1 < m0 + kMRows ? r1 : m0 + kMRows;
     } else {
-        int64_t mtile;
-        const int64_t b = blockIdx.x;
-        if (n_tiles % 8 == 0) {  // XCD-aware: the m blocks of one n tile share an XCD
-            const int64_t xcd = b % 8, local = b / 8;
-            nt = (local / m_tiles) * 8 + xcd;
-            mtile = local % m_tiles;
-        } else {
-            nt = b % n_tiles;
-            mtile = b / n_tiles;
-        }
-        m0 = (mtile0 + mtile) * kMRows;
-        mend = a.m < m0 + kMRows ? a.m : m0 + kMRows;
+        plan_tile(plan, blockIdx.x, nt, m0);
+        mend = a.m < m0 + plan.mh ? a.m : m0 + plan.mh;
     }
     // 16-row activation tiles holding rows (uniform; tiles past it are skipped)
     const int nmt = (int)((mend - m0 + 15) / 16);
@@ -302,7 +462,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // rows lies past the buffer's range and reads zeros.
     bf.x = make_rsrc(a.x, a.m * a.ldx * 2);
 #pragma unroll
-    for (int it = 0; it < kDmaOps; ++it) {
+    for (int it = 0; it < kDmaX; ++it) {
         const int row = 16 * wv + 4 * it + (lane >> 4);
         const int c = (lane & 15) ^ (row & 15);
         const int64_t sr = m0 + row;
@@ -353,7 +513,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
     }
 
-    k_loop<B, FULL>(bf, sm, KT, G, wv, lane, nmt, tot);
+    k_loop<B, NMT>(bf, sm, KT, G, wv, lane, nmt, tot);
 
     // epilogue
 #pragma unroll
@@ -455,17 +615,27 @@ __global__ __launch_bounds__(256) void outlier_spmm_kernel(const int32_t *rowptr
     dst[1] = (f4){acc[4], acc[5], acc[6], acc[7]};
 }
 
-// Whole 128-row tiles in one launch, a ragged last tile in another.
+static TilePlan one_rect(int32_t nt0, int32_t nnt, int32_t m0, int32_t mtiles, int32_t mh)
+{
+    TilePlan p{};
+    p.r[0] = {nt0, nnt, m0, mtiles, 0};
+    p.nr = 1;
+    p.mh = mh;
+    return p;
+}
+
+// Whole 128-row activation tiles in one launch, a ragged last tile in another.
 template <int B, int MODE>
 static void gemm_launch(const GemmArgs &a, hipStream_t st)
 {
-    const int64_t n_tiles = (a.n + kNT - 1) / kNT, full = a.m / kMRows;
+    const int32_t NT = (int32_t)((a.n + kNT - 1) / kNT), F = (int32_t)(a.m / kMRows);
     const dim3 block(kWaves * 64);
-    if (full > 0)
-        hipLaunchKernelGGL((gemm_kernel<B, MODE, true>), dim3((unsigned)(n_tiles * full)), block, 0, st, a,
-                           (int64_t)0, full);
+    if (F > 0)
+        hipLaunchKernelGGL((gemm_kernel<B, MODE, kMT>), dim3((unsigned)((int64_t)NT * F)), block, 0, st, a,
+                           one_rect(0, NT, 0, F, kMRows));
     if (a.m % kMRows)
-        hipLaunchKernelGGL((gemm_kernel<B, MODE, false>), dim3((unsigned)n_tiles), block, 0, st, a, full, (int64_t)1);
+        hipLaunchKernelGGL((gemm_kernel<B, MODE, 0>), dim3((unsigned)NT), block, 0, st, a,
+                           one_rect(0, NT, F * kMRows, 1, kMRows));
 }
 
 template <int B>
@@ -504,8 +674,8 @@ template <int B, int MODE>
 static hipError_t grouped_mode(int n_experts, const GemmArgs &a, hipStream_t st)
 {
     const int64_t n_tiles = (a.n + kNT - 1) / kNT, m_tiles = (a.m + kMRows - 1) / kMRows;
-    hipLaunchKernelGGL((gemm_kernel<B, MODE, false>), dim3((unsigned)n_tiles, (unsigned)n_experts, (unsigned)m_tiles),
-                       dim3(kWaves * 64), 0, st, a, (int64_t)0, m_tiles);
+    hipLaunchKernelGGL((gemm_kernel<B, MODE, 0>), dim3((unsigned)n_tiles, (unsigned)n_experts, (unsigned)m_tiles),
+                       dim3(kWaves * 64), 0, st, a, TilePlan{});
     return hipGetLastError();
 }
 
