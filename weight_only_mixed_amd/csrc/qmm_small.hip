@@ -102,12 +102,13 @@ __device__ __forceinline__ void wait_vm()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// One 16-row block of problem p on this workgroup; `ring` is this wave's D slots of `pitch`
-// bytes, `red` the workgroup's reduction buffer.
+// One 16-row block of problem p on this workgroup; slot0/slot1 are this wave's two ring slots
+// (separate LDS arrays), `red` the workgroup's reduction buffer.
 template <int B, int NW, int D, int MX>
-__device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uint8_t *ring, int pitch,
+__device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uint8_t *slot0, uint8_t *slot1,
                                            f4 (*red)[64])
 {
+    static_assert(D == 2, "two ring slots");
     using S = RingSlot<B, MX>;
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t = lane >> 4, r = lane & 15;
@@ -121,8 +122,7 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
     bf.x = make_rsrc(a.x, a.m * a.ldx * 2);  // rows >= m read as zeros
 
     const int64_t nt = KT > wv ? (KT - wv + NW - 1) / NW : 0;  // tiles of this wave
-#pragma unroll
-    for (int s = 0; s < D - 1; ++s) ring_issue<B, MX>(bf, wv + (int64_t)s * NW, lane, a.ldx, ring + s * pitch);
+    ring_issue<B, MX>(bf, wv, lane, a.ldx, slot0);
 
     // Activation fragments: lanes of rows >= m keep zeros and never read LDS.
     const bool act = r < a.m;
@@ -130,11 +130,20 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
 #pragma unroll
     for (int j = 0; j < 8; ++j) X[j] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
     f4 tot = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t i = 0; i < nt; ++i) {
+    // Tile i sits in slot i % 2 and the DMA of tile i+1 runs while tile i is consumed.  The two
+    // slots are separate LDS arrays, named statically (the loop is unrolled by two), so the
+    // compiler can tell that a slot's reads never overlap the DMA in flight into the other;
+    // with one array and computed slot addresses it waits for every outstanding DMA before
+    // each read, which serialises the loads with the arithmetic.
+    for (int64_t i0 = 0; i0 < nt; i0 += 2)
+#pragma unroll
+    for (int sd = 0; sd < 2; ++sd) {
+        const int64_t i = i0 + sd;
+        if (i >= nt) break;  // uniform
         const int64_t kt = wv + i * NW;
-        ring_issue<B, MX>(bf, kt + (int64_t)(D - 1) * NW, lane, a.ldx, ring + ((i + D - 1) % D) * pitch);
-        wait_vm<S::kLoads * (D - 1)>();
-        const uint8_t *slot = ring + (i % D) * pitch;
+        ring_issue<B, MX>(bf, kt + NW, lane, a.ldx, sd == 0 ? slot1 : slot0);
+        wait_vm<S::kLoads>();
+        const uint8_t *slot = sd == 0 ? slot0 : slot1;
         uint32_t d[2 * B];
 #pragma unroll
         for (int sl = 0; sl < B / 2; ++sl) {
@@ -190,10 +199,11 @@ template <int B, int NW, int D, int MX>
 __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvProblem a)
 {
     constexpr int pitch = RingSlot<B, MX>::kBytes;
-    __shared__ __attribute__((aligned(16))) uint8_t ring[NW][D][pitch];
+    __shared__ __attribute__((aligned(16))) uint8_t ring0[NW][pitch];
+    __shared__ __attribute__((aligned(16))) uint8_t ring1[NW][pitch];
     __shared__ f4 red[NW][64];
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    gemv_block<B, NW, D, MX>(a, blockIdx.x, &ring[wv][0][0], pitch, red);
+    gemv_block<B, NW, D, MX>(a, blockIdx.x, &ring0[wv][0], &ring1[wv][0], red);
 }
 
 // Independent problems (mixed bit widths) in one launch: workgroup b serves problem p with
@@ -202,7 +212,8 @@ template <int NW, int D, int MX>
 __global__ __launch_bounds__(NW * 64) void gemv_batch_kernel(GemvBatch bt)
 {
     constexpr int pitch = RingSlot<6, MX>::kBytes;
-    __shared__ __attribute__((aligned(16))) uint8_t ring[NW][D][pitch];
+    __shared__ __attribute__((aligned(16))) uint8_t ring0[NW][pitch];
+    __shared__ __attribute__((aligned(16))) uint8_t ring1[NW][pitch];
     __shared__ f4 red[NW][64];
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t b = blockIdx.x;
@@ -212,13 +223,13 @@ __global__ __launch_bounds__(NW * 64) void gemv_batch_kernel(GemvBatch bt)
         if (i < bt.count && b >= bt.p[i].block0) p = i;
     const GemvProblem &a = bt.p[p];
     const int64_t rb = b - a.block0;
-    uint8_t *rg = &ring[wv][0][0];
+    uint8_t *s0 = &ring0[wv][0], *s1 = &ring1[wv][0];
     switch (a.bits) {
-    case 2: gemv_block<2, NW, D, MX>(a, rb, rg, pitch, red); break;
-    case 3: gemv_block<3, NW, D, MX>(a, rb, rg, pitch, red); break;
-    case 4: gemv_block<4, NW, D, MX>(a, rb, rg, pitch, red); break;
-    case 5: gemv_block<5, NW, D, MX>(a, rb, rg, pitch, red); break;
-    default: gemv_block<6, NW, D, MX>(a, rb, rg, pitch, red); break;
+    case 2: gemv_block<2, NW, D, MX>(a, rb, s0, s1, red); break;
+    case 3: gemv_block<3, NW, D, MX>(a, rb, s0, s1, red); break;
+    case 4: gemv_block<4, NW, D, MX>(a, rb, s0, s1, red); break;
+    case 5: gemv_block<5, NW, D, MX>(a, rb, s0, s1, red); break;
+    default: gemv_block<6, NW, D, MX>(a, rb, s0, s1, red); break;
     }
 }
 
