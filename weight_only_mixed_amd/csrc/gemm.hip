@@ -155,13 +155,17 @@ __device__ __forceinline__ void load_sz(const Bufs &bf, int64_t G, int64_t kt, i
 }
 
 // Wait until at most N of this wave's vector-memory operations are outstanding (they retire
-// in order), then synchronise the workgroup.
+// in order) and its LDS reads are done, then synchronise the workgroup.  The barrier is issued
+// in the same asm statement: __syncthreads() carries a workgroup fence, for which the compiler
+// waits for every outstanding buffer-to-LDS DMA (vmcnt(0)), including the ones issued this
+// step to run ahead.  The DMA whose data the next step reads has landed once this wave's
+// vmcnt allows it, so the plain barrier is enough; the memory clobber keeps the compiler from
+// moving LDS accesses across it.
 template <int N>
 __device__ __forceinline__ void wait_and_sync()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-    __syncthreads();
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 template <int B>
