@@ -44,6 +44,7 @@ constexpr int kMRows = kMT * 16;             // 128 activation rows per workgrou
 constexpr int kRowBytes = 128 * 2;           // one 128-k group of one activation row
 constexpr int kXSlot = kMRows * kRowBytes;   // one activation slot: 32 KB
 constexpr int kDmaX = kXSlot / 1024 / kWaves;  // activation DMA instructions per wave per group
+static_assert(kDmaX * 1024 == 16 * kRowBytes, "each wave stages one 16-row activation tile");
 
 // LDS staging of one wave's row block for one k-tile: the lane chunks as in the device layout
 // (B/2 pieces of 16 bytes per lane; for odd B the 8-byte tail as two 4-byte words 256 bytes
@@ -89,9 +90,13 @@ __device__ __forceinline__ void lds_dma4(rsrc_t r, uint8_t *lds, uint32_t voff, 
 
 // DMA the 128 x 128-k activation tile of group g into LDS slot `dst` (this wave's 4 KB).
 // Lane L of piece `it` fills LDS bytes [16L, 16L+16) of a 1 KB run = row 4*(4*wv+it) + L/16,
-// physical chunk L%16, which holds logical chunk (L%16) ^ (row & 15).
-__device__ __forceinline__ void dma_x(const Bufs &bf, int64_t g, uint8_t *dst, int wv)
+// physical chunk L%16, which holds logical chunk (L%16) ^ (row & 15).  Wave wv stages rows
+// 16 wv .. 16 wv + 15, i.e. activation tile wv; when the workgroup has fewer tiles (nmt <= wv)
+// the tile is never read and the wave issues nothing (out-of-range loads read zeros but still
+// cost address-unit cycles).
+__device__ __forceinline__ void dma_x(const Bufs &bf, int64_t g, uint8_t *dst, int wv, int nmt)
 {
+    if (wv >= nmt) return;  // uniform
     const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)g * 256);  // column of group g
 #pragma unroll
     for (int it = 0; it < kDmaX; ++it) lds_dma16(bf.x, dst + (wv * kDmaX + it) * 1024, bf.xoff[it], soff);
@@ -151,6 +156,95 @@ __device__ __forceinline__ void load_sz(const Bufs &bf, int64_t G, int64_t kt, i
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             z.sc[u][i] = ld4(bf.sc[u], vs, __builtin_amdgcn_readfirstlane((uint32_t)((i * G + 2 * kt) * 2)));
+    }
+}
+
+// The loads one k-loop step issues for later steps: the activation DMA of group gx into
+// slot xdst, and on even steps (PAR 0) the scales and zero points of tile kt into z, on odd
+// steps (PAR 1) the weight DMA of tile kt into this wave's part wdst of a weight slot.
+template <int PAR>
+struct StepIO {
+    int64_t gx, kt;
+    uint8_t *xdst, *wdst;
+    SZ *z;
+};
+
+// Activation DMA piece `it` of this wave (rows 4 it + lane / 16 of its tile).
+__device__ __forceinline__ void dma_x_piece(const Bufs &bf, int64_t g, uint8_t *dst, int wv, int it)
+{
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)g * 256);
+    lds_dma16(bf.x, dst + (wv * kDmaX + it) * 1024, bf.xoff[it], soff);
+}
+
+// Scale / zero-point load p of 2 x 5: the zero pair, then the four scale words of row block p / 5.
+__device__ __forceinline__ void load_sz_piece(const Bufs &bf, int64_t G, int64_t kt, int lane, SZ &z, int p)
+{
+    const int t = lane >> 4, r = lane & 15, u = p / 5, j = p % 5;
+    if (j == 0) {
+        z.zz[u] = ld2(bf.zr[u], (uint32_t)(r * G), __builtin_amdgcn_readfirstlane((uint32_t)(2 * kt)));
+    } else {
+        const int i = j - 1;
+        z.sc[u][i] = ld4(bf.sc[u], (uint32_t)(4 * t * G * 2), __builtin_amdgcn_readfirstlane((uint32_t)((i * G + 2 * kt) * 2)));
+    }
+}
+
+// Weight DMA piece p of kWOps<B>: row block p / kOps, then its 16-byte pieces and (odd B) the
+// two 4-byte words of the tail.
+template <int B>
+__device__ __forceinline__ void dma_w_piece(const Bufs &bf, int64_t kt, uint8_t *dst, int lane, int p)
+{
+    const uint32_t tile = __builtin_amdgcn_readfirstlane((uint32_t)(kt * (512 * B)));
+    const int u = p / WStage<B>::kOps, s = p % WStage<B>::kOps;
+    uint8_t *base = dst + u * WStage<B>::kBytes;
+    if (s < B / 2) {
+        lds_dma16(bf.w[u], base + 1024 * s, 16 * lane, tile + 1024 * s);
+    } else {
+        const int h = s - B / 2;  // tail word 0 or 1
+        lds_dma4(bf.w[u], base + 1024 * (B / 2) + 256 * h, 8 * lane + 4 * h, tile + 1024 * (B / 2));
+    }
+}
+
+// The share of a step's loads issued with activation tile MT of a full step: activation
+// pieces with the first half of the tiles; scales and zero points with them too (even steps,
+// so their memory latency has most of the step), the weight pieces with the second half (odd
+// steps, after every activation piece, so the end-of-step wait can leave them in flight).
+// Issuing everything at the start of a step instead stalls all eight waves together while
+// the address unit works through about 48 KB.
+template <int B, int PAR, int NMT, int MT>
+__device__ __forceinline__ void issue_tile(const Bufs &bf, const StepIO<PAR> &io, int64_t G, int wv, int lane)
+{
+    static_assert(NMT == kMT && kDmaX == NMT / 2, "one activation piece per tile of the first half");
+    if constexpr (MT < NMT / 2) dma_x_piece(bf, io.gx, io.xdst, wv, MT);
+    if constexpr (PAR == 0 && MT < NMT / 2) {
+#pragma unroll
+        for (int p = MT * kSZOps / (NMT / 2); p < (MT + 1) * kSZOps / (NMT / 2); ++p) load_sz_piece(bf, G, io.kt, lane, *io.z, p);
+    }
+    if constexpr (PAR == 1 && MT >= NMT / 2) {
+        constexpr int q = MT - NMT / 2, h = NMT / 2;
+#pragma unroll
+        for (int p = q * kWOps<B> / h; p < (q + 1) * kWOps<B> / h; ++p) dma_w_piece<B>(bf, io.kt, io.wdst, lane, p);
+    }
+}
+
+// All of a step's loads at once (ragged steps, whose tile count is not known at compile time).
+template <int B, int PAR>
+__device__ __forceinline__ void issue_all(const Bufs &bf, const StepIO<PAR> &io, int64_t G, int wv, int lane, int nmt)
+{
+    dma_x(bf, io.gx, io.xdst, wv, nmt);
+    if constexpr (PAR == 0) load_sz(bf, G, io.kt, lane, *io.z);
+    else dma_w<B>(bf, io.kt, io.wdst, lane);
+}
+
+// After a wait that has retired this tile's scale / zero-point loads: hide their origin from
+// the compiler, which does not see the inline-asm wait and would otherwise wait for them again
+// at their first use, counting the weight DMA issued since (meant to stay in flight) as older.
+__device__ __forceinline__ void retired(SZ &z)
+{
+#pragma unroll
+    for (int u = 0; u < kRBW; ++u) {
+        asm volatile("" : "+v"(z.zz[u]));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(z.sc[u][i]));
     }
 }
 
@@ -247,11 +341,13 @@ template <int B, int SH, int NH, int NMT, int MT>
 __device__ __forceinline__ void full_tile(const h8 (&Acur)[kRBW][4], h8 (&Anxt)[kRBW][4], const uint32_t (&sc)[kRBW][4],
                                           const GroupConst<B> (&gc)[kRBW], const uint8_t *xs, const uint8_t *wpart,
                                           int lane, uint32_t (&d)[2 * B], h8 (&X)[kXR][4], f4 (&acc)[2][kRBW],
-                                          f4 (&tot)[kRBW][kMT])
+                                          f4 (&tot)[kRBW][kMT], const Bufs &bf, const StepIO<NH ^ 1> &io, int64_t G,
+                                          int wv)
 {
     static_assert(NMT % 2 == 0 && NMT <= kMT, "even tile count");
     constexpr int cur = MT & 1, nxt = cur ^ 1;
     const int t = lane >> 4, r = lane & 15;
+    issue_tile<B, NH ^ 1, NMT, MT>(bf, io, G, wv, lane);
     if constexpr (MT + kXA < NMT) {
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4)
@@ -278,19 +374,23 @@ __device__ __forceinline__ void full_tiles(std::integer_sequence<int, MT...>, co
                                            h8 (&Anxt)[kRBW][4], const uint32_t (&sc)[kRBW][4],
                                            const GroupConst<B> (&gc)[kRBW], const uint8_t *xs, const uint8_t *wpart,
                                            int lane, uint32_t (&d)[2 * B], h8 (&X)[kXR][4], f4 (&acc)[2][kRBW],
-                                           f4 (&tot)[kRBW][kMT])
+                                           f4 (&tot)[kRBW][kMT], const Bufs &bf, const StepIO<NH ^ 1> &io, int64_t G,
+                                           int wv)
 {
-    (full_tile<B, SH, NH, NMT, MT>(Acur, Anxt, sc, gc, xs, wpart, lane, d, X, acc, tot), ...);
+    (full_tile<B, SH, NH, NMT, MT>(Acur, Anxt, sc, gc, xs, wpart, lane, d, X, acc, tot, bf, io, G, wv), ...);
 }
 
 // One 128-k group step: A(g) = Acur times the activation tile of group g (slot xs), scale
 // half SH of scale words sc; meanwhile A(g+1) is unpacked into Anxt from half NH of the
-// staged tile wpart with zero points zn.  NMT > 0: the first NMT 16-row activation tiles all
-// hold rows; NMT == 0: nmt tiles hold rows (ragged), and the next group is unpacked first.
+// staged tile wpart with zero points zn, and the loads io for later steps are issued (a step
+// that unpacks a first group, NH = 0, is an odd step).  NMT > 0: the first NMT 16-row
+// activation tiles all hold rows; NMT == 0: nmt tiles hold rows (ragged), the loads are
+// issued at once and the next group is unpacked first.
 template <int B, int SH, int NH, int NMT>
 __device__ __forceinline__ void group_step(const h8 (&Acur)[kRBW][4], h8 (&Anxt)[kRBW][4], const uint32_t (&sc)[kRBW][4],
                                            const SZ &zn, const uint8_t *xs, const uint8_t *wpart, int lane, int nmt,
-                                           f4 (&tot)[kRBW][kMT])
+                                           f4 (&tot)[kRBW][kMT], const Bufs &bf, const StepIO<NH ^ 1> &io, int64_t G,
+                                           int wv)
 {
     const int t = lane >> 4, r = lane & 15;
     f4 acc[2][kRBW];
@@ -305,8 +405,10 @@ __device__ __forceinline__ void group_step(const h8 (&Acur)[kRBW][4], h8 (&Anxt)
         uint32_t d[2 * B];
         __builtin_amdgcn_sched_barrier(0);
         full_tiles<B, SH, NH, NMT>(std::make_integer_sequence<int, NMT>{}, Acur, Anxt, sc, gc, xs, wpart, lane, d, X,
-                                   acc, tot);
+                                   acc, tot, bf, io, G, wv);
     } else {
+        issue_all<B, NH ^ 1>(bf, io, G, wv, lane, nmt);
+        __builtin_amdgcn_sched_barrier(0);
         h8 X[2][4];
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4) X[0][j4] = *(const h8 *)(xs + xs_off(r, 4 * j4 + t));
@@ -332,62 +434,63 @@ __device__ __forceinline__ void group_step(const h8 (&Acur)[kRBW][4], h8 (&Anxt)
 
 // The k loop of a workgroup.  Step g multiplies group g and unpacks group g+1.
 //  - Activations: slot g % 2 holds group g; the DMA of group g+1 into the other slot is
-//    issued at the start of step g (its previous contents were read in step g-1, which
-//    ended with a workgroup barrier) and waited for at the end of step g.
+//    issued during step g (its previous contents were read in step g-1, which ended with a
+//    workgroup barrier) and waited for at the end of step g.
 //  - Weights: slot t % 2 holds k-tile t (every wave stages and reads only its own part, so
 //    no barrier is involved).  Tile t is read while unpacking groups 2t and 2t+1, in steps
-//    2t-1 and 2t; the DMA of tile t+2 into slot t % 2 is issued at the start of step 2t+1 and
-//    waited for at the end of step 2t+2.
-//  - Scales and zero points of tile t are loaded into registers at the start of step 2t-2.
-//  Each step issues its DMAs first, so the waits are: vmcnt(0) after steps 2t, and
+//    2t-1 and 2t; the DMA of tile t+2 into slot t % 2 is issued during step 2t+1, after that
+//    step's activation DMA, and waited for at the end of step 2t+2.
+//  - Scales and zero points of tile t are loaded into registers during step 2t-2.
+//  In a full step the loads are spread over its activation tiles (issue_tile); in a ragged
+//  step they are issued at its start.  The waits are: vmcnt(0) after steps 2t, and
 //  vmcnt(weight DMAs) after steps 2t+1.  Loads past the end are clamped to the last group or
 //  tile and land in slots that are not read again; the A operands unpacked from them are
 //  discarded.
 template <int B, int NMT>
-__device__ __forceinline__ void k_loop(const Bufs &bf, Smem<B> &sm, int64_t KT, int64_t G, int wv, int lane, int nmt,
+//  The four slots reach the loop as restrict pointers: that tells the compiler that reads of
+//  one slot never touch a DMA in flight into another.  Without it (slots at run-time offsets
+//  in one array) it waits for every outstanding load, the weight DMA meant to run a step and a
+//  half ahead included, before each read of the ring.
+__device__ __forceinline__ void k_loop(const Bufs &bf, uint8_t *__restrict__ xs0, uint8_t *__restrict__ xs1,
+                                       uint8_t *__restrict__ ws0, uint8_t *__restrict__ ws1, int64_t KT, int64_t G, int wv, int lane, int nmt,
                                        f4 (&tot)[kRBW][kMT])
 {
     const int64_t GN = 2 * KT;  // groups
     auto gclamp = [&](int64_t g) { return g < GN ? g : GN - 1; };
     auto tclamp = [&](int64_t t) { return t < KT ? t : KT - 1; };
-    uint8_t *w0 = sm.ws[0] + wv * (kRBW * WStage<B>::kBytes);  // this wave's parts of the weight slots
-    uint8_t *w1 = sm.ws[1] + wv * (kRBW * WStage<B>::kBytes);
+    uint8_t *w0 = ws0 + wv * (kRBW * WStage<B>::kBytes);  // this wave's parts of the weight slots
+    uint8_t *w1 = ws1 + wv * (kRBW * WStage<B>::kBytes);
     SZ z0, z1;  // tiles of even / odd index
     h8 Aa[kRBW][4], Ab[kRBW][4];
 
-    dma_x(bf, 0, sm.xs[0], wv);
+    dma_x(bf, 0, xs0, wv, nmt);
     dma_w<B>(bf, 0, w0, lane);
     dma_w<B>(bf, tclamp(1), w1, lane);
     load_sz(bf, G, 0, lane, z0);
     wait_and_sync<0>();
+    retired(z0);
     unpack_group<B, 0>(w0, z0, lane, Aa);
 
     for (int64_t kt = 0; kt < KT; kt += 2) {
         const int64_t g = 2 * kt;
         // step g: tile kt, first group; unpack tile kt's second group
-        dma_x(bf, gclamp(g + 1), sm.xs[1], wv);
-        load_sz(bf, G, tclamp(kt + 1), lane, z1);
-        __builtin_amdgcn_sched_barrier(0);
-        group_step<B, 0, 1, NMT>(Aa, Ab, z0.sc, z0, sm.xs[0], w0, lane, nmt, tot);
+        const StepIO<0> s0{gclamp(g + 1), tclamp(kt + 1), xs1, nullptr, &z1};
+        group_step<B, 0, 1, NMT>(Aa, Ab, z0.sc, z0, xs0, w0, lane, nmt, tot, bf, s0, G, wv);
         wait_and_sync<0>();
+        retired(z1);
         // step g+1: tile kt, second group; unpack tile kt+1's first group
-        dma_x(bf, gclamp(g + 2), sm.xs[0], wv);
-        dma_w<B>(bf, tclamp(kt + 2), w0, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        group_step<B, 1, 0, NMT>(Ab, Aa, z0.sc, z1, sm.xs[1], w1, lane, nmt, tot);
+        const StepIO<1> s1{gclamp(g + 2), tclamp(kt + 2), xs0, w0, nullptr};
+        group_step<B, 1, 0, NMT>(Ab, Aa, z0.sc, z1, xs1, w1, lane, nmt, tot, bf, s1, G, wv);
         wait_and_sync<kWOps<B>>();
         if (kt + 1 >= KT) break;
         // step g+2: tile kt+1, first group; unpack its second group
-        dma_x(bf, gclamp(g + 3), sm.xs[1], wv);
-        load_sz(bf, G, tclamp(kt + 2), lane, z0);
-        __builtin_amdgcn_sched_barrier(0);
-        group_step<B, 0, 1, NMT>(Aa, Ab, z1.sc, z1, sm.xs[0], w1, lane, nmt, tot);
+        const StepIO<0> s2{gclamp(g + 3), tclamp(kt + 2), xs1, nullptr, &z0};
+        group_step<B, 0, 1, NMT>(Aa, Ab, z1.sc, z1, xs0, w1, lane, nmt, tot, bf, s2, G, wv);
         wait_and_sync<0>();
+        retired(z0);
         // step g+3: tile kt+1, second group; unpack tile kt+2's first group
-        dma_x(bf, gclamp(g + 4), sm.xs[0], wv);
-        dma_w<B>(bf, tclamp(kt + 3), w1, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        group_step<B, 1, 0, NMT>(Ab, Aa, z1.sc, z0, sm.xs[1], w0, lane, nmt, tot);
+        const StepIO<1> s3{gclamp(g + 4), tclamp(kt + 3), xs0, w1, nullptr};
+        group_step<B, 1, 0, NMT>(Ab, Aa, z1.sc, z0, xs1, w0, lane, nmt, tot, bf, s3, G, wv);
         wait_and_sync<kWOps<B>>();
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may land after the workgroup ends
@@ -517,7 +620,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
     }
 
-    k_loop<B, NMT>(bf, sm, KT, G, wv, lane, nmt, tot);
+    k_loop<B, NMT>(bf, sm.xs[0], sm.xs[1], sm.ws[0], sm.ws[1], KT, G, wv, lane, nmt, tot);
 
     // epilogue
 #pragma unroll
