@@ -409,13 +409,27 @@ __device__ __forceinline__ void group_step(const h8 (&Acur)[kRBW][4], h8 (&Anxt)
     } else {
         issue_all<B, NH ^ 1>(bf, io, G, wv, lane, nmt);
         __builtin_amdgcn_sched_barrier(0);
+        // Every ragged step has a first tile: its matrix-core chains run interleaved with the
+        // unpack of the next group (few tiles leave the vector ALU the larger share), while
+        // the second tile's fragments are read (rows past the workgroup's read stale LDS
+        // bytes that are never used).
         h8 X[2][4];
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4) X[0][j4] = *(const h8 *)(xs + xs_off(r, 4 * j4 + t));
-        unpack_group<B, NH>(wpart, zn, lane, Anxt);
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
+        for (int j4 = 0; j4 < 4; ++j4) X[1][j4] = *(const h8 *)(xs + xs_off(16 + r, 4 * j4 + t));
+        tile_mma(Acur, X[0], acc[0]);
+        unpack_group<B, NH>(wpart, zn, lane, Anxt);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);  // VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (nmt == 1) scale_acc<SH>(sc, acc[0], tot, 0);
+#pragma unroll
+        for (int mt = 1; mt < kMT; ++mt) {
             if (mt >= nmt) break;  // uniform: tiles past the workgroup's rows are skipped
             const int cur = mt & 1, nxt = cur ^ 1;
             if (mt + 1 < kMT && mt + 1 < nmt) {
@@ -425,7 +439,7 @@ __device__ __forceinline__ void group_step(const h8 (&Acur)[kRBW][4], h8 (&Anxt)
             }
             __builtin_amdgcn_sched_barrier(0);
             tile_mma(Acur, X[cur], acc[cur]);
-            if (mt > 0) scale_acc<SH>(sc, acc[nxt], tot, mt - 1);
+            scale_acc<SH>(sc, acc[nxt], tot, mt - 1);
             if (mt + 1 == nmt) scale_acc<SH>(sc, acc[cur], tot, mt);
             __builtin_amdgcn_sched_barrier(0);
         }
