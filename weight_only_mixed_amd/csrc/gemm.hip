@@ -36,15 +36,30 @@ namespace qp {
 
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kRBW = 2;                      // 16-row weight blocks per wave
-constexpr int kMT = 8;                       // 16-row activation tiles per workgroup
-constexpr int kNT = kWaves * kRBW * kTileN;  // 256 weight rows per workgroup
-constexpr int kMRows = kMT * 16;             // 128 activation rows per workgroup
-constexpr int kRowBytes = 128 * 2;           // one 128-k group of one activation row
-constexpr int kXSlot = kMRows * kRowBytes;   // one activation slot: 32 KB
-constexpr int kDmaX = kXSlot / 1024 / kWaves;  // activation DMA instructions per wave per group
-static_assert(kDmaX * 1024 == 16 * kRowBytes, "each wave stages one 16-row activation tile");
+constexpr int kRBW = 2;             // 16-row weight blocks per wave
+constexpr int kRowBytes = 128 * 2;  // one 128-k group of one activation row
+
+// Workgroup geometry: W waves (2W weight row blocks) times MT 16-row activation tiles.
+//  - Geo<8, 8>: 256 weight rows x 128 activation rows, one workgroup per CU (128 KB of LDS at
+//    4 bits); the layer GEMM.
+//  - Geo<4, 2>: 128 weight rows x 32 activation rows, three workgroups per CU (48 KB); routed
+//    experts with few rows each, whose steps are too short to hide their latencies with two
+//    waves per SIMD.
+// Each wave stages kDmaX 1 KB runs of every activation slot (four rows each): rows
+// 4 kDmaX wv .. 4 kDmaX (wv + 1) - 1.
+template <int W, int MT>
+struct Geo {
+    static constexpr int kWaves = W;
+    static constexpr int kMT = MT;
+    static constexpr int kNT = W * kRBW * kTileN;    // weight rows per workgroup
+    static constexpr int kMRows = MT * 16;           // activation rows per workgroup
+    static constexpr int kXSlot = kMRows * kRowBytes;  // one activation slot
+    static constexpr int kDmaX = kXSlot / 1024 / W;  // activation DMA instructions per wave per group
+    static constexpr int kWavesPerEU = W == 8 ? 2 : 3;
+    static_assert(kDmaX * 1024 * W == kXSlot && kDmaX >= 1, "whole 1 KB runs per wave");
+};
+using GeoLayer = Geo<8, 8>;
+using GeoExperts = Geo<4, 2>;
 
 // LDS staging of one wave's row block for one k-tile: the lane chunks as in the device layout
 // (B/2 pieces of 16 bytes per lane; for odd B the 8-byte tail as two 4-byte words 256 bytes
@@ -53,7 +68,6 @@ template <int B>
 struct WStage {
     static constexpr int kBytes = 512 * B;
     static constexpr int kOps = B / 2 + 2 * (B & 1);  // DMA instructions per row block
-    static constexpr int kSlot = kWaves * kRBW * kBytes;
 };
 template <int B>
 constexpr int kWOps = kRBW * WStage<B>::kOps;  // weight DMA instructions per wave per k-tile
@@ -63,20 +77,21 @@ __device__ __forceinline__ int xs_off(int row, int c) { return row * kRowBytes +
 
 // Shared memory of one workgroup: a two-slot activation ring (one 128-k group per slot) and
 // a two-slot ring of packed weight tiles (one k-tile per slot; every wave owns its part).
-template <int B>
+template <int B, typename G>
 struct Smem {
-    uint8_t xs[2][kXSlot];
-    uint8_t ws[2][WStage<B>::kSlot];
+    uint8_t xs[2][G::kXSlot];
+    uint8_t ws[2][G::kWaves * kRBW * WStage<B>::kBytes];
 };
 
 // Buffers of one workgroup.  Every wave-uniform offset passed as soffset stays inside the
 // range the per-lane voffset was checked against (a row of x, a weight row block), so a
 // load is in bounds whether or not the hardware includes soffset in its range check.
+constexpr int kDmaXMax = GeoLayer::kDmaX;
 struct Bufs {
-    rsrc_t x;              // activation rows [m0, m)
-    rsrc_t w[kRBW];        // packed tiles of row block rb0 + u (empty past the last block)
+    rsrc_t x;                 // activation rows [m0, m)
+    rsrc_t w[kRBW];           // packed tiles of row block rb0 + u (empty past the last block)
     rsrc_t sc[kRBW], zr[kRBW];
-    uint32_t xoff[kDmaX];  // this lane's source of LDS-DMA piece it (row offset + chunk)
+    uint32_t xoff[kDmaXMax];  // this lane's source of LDS-DMA piece it (row offset + chunk)
 };
 
 __device__ __forceinline__ void lds_dma16(rsrc_t r, uint8_t *lds, uint32_t voff, uint32_t soff)
@@ -88,18 +103,23 @@ __device__ __forceinline__ void lds_dma4(rsrc_t r, uint8_t *lds, uint32_t voff, 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, voff, soff, 0, 0);
 }
 
-// DMA the 128 x 128-k activation tile of group g into LDS slot `dst` (this wave's 4 KB).
-// Lane L of piece `it` fills LDS bytes [16L, 16L+16) of a 1 KB run = row 4*(4*wv+it) + L/16,
-// physical chunk L%16, which holds logical chunk (L%16) ^ (row & 15).  Wave wv stages rows
-// 16 wv .. 16 wv + 15, i.e. activation tile wv; when the workgroup has fewer tiles (nmt <= wv)
-// the tile is never read and the wave issues nothing (out-of-range loads read zeros but still
-// cost address-unit cycles).
+// DMA the activation tile of group g (kMRows rows x 128 k) into LDS slot `dst` (this wave's
+// kDmaX KB).  Lane L of piece `it` fills LDS bytes [16L, 16L+16) of a 1 KB run = row
+// 4*(kDmaX*wv+it) + L/16, physical chunk L%16, which holds logical chunk (L%16) ^ (row & 15).
+// When the workgroup's rows end before this wave's first row, its rows are never read and the
+// wave issues nothing (out-of-range loads read zeros but still cost address-unit cycles).
+template <typename G>
+__device__ __forceinline__ bool stages_rows(int wv, int nmt)
+{
+    return 4 * G::kDmaX * wv < 16 * nmt;
+}
+template <typename G>
 __device__ __forceinline__ void dma_x(const Bufs &bf, int64_t g, uint8_t *dst, int wv, int nmt)
 {
-    if (wv >= nmt) return;  // uniform
+    if (!stages_rows<G>(wv, nmt)) return;  // uniform
     const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)g * 256);  // column of group g
 #pragma unroll
-    for (int it = 0; it < kDmaX; ++it) lds_dma16(bf.x, dst + (wv * kDmaX + it) * 1024, bf.xoff[it], soff);
+    for (int it = 0; it < G::kDmaX; ++it) lds_dma16(bf.x, dst + (wv * G::kDmaX + it) * 1024, bf.xoff[it], soff);
 }
 
 // DMA this wave's packed tiles of k-tile kt into its part `dst` of a weight slot.
@@ -169,11 +189,12 @@ struct StepIO {
     SZ *z;
 };
 
-// Activation DMA piece `it` of this wave (rows 4 it + lane / 16 of its tile).
+// Activation DMA piece `it` of this wave (four of its rows).
+template <typename G>
 __device__ __forceinline__ void dma_x_piece(const Bufs &bf, int64_t g, uint8_t *dst, int wv, int it)
 {
     const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)g * 256);
-    lds_dma16(bf.x, dst + (wv * kDmaX + it) * 1024, bf.xoff[it], soff);
+    lds_dma16(bf.x, dst + (wv * G::kDmaX + it) * 1024, bf.xoff[it], soff);
 }
 
 // Scale / zero-point load p of 2 x 5: the zero pair, then the four scale words of row block p / 5.
@@ -210,11 +231,11 @@ __device__ __forceinline__ void dma_w_piece(const Bufs &bf, int64_t kt, uint8_t 
 // steps, after every activation piece, so the end-of-step wait can leave them in flight).
 // Issuing everything at the start of a step instead stalls all eight waves together while
 // the address unit works through about 48 KB.
-template <int B, int PAR, int NMT, int MT>
+template <int B, typename GE, int PAR, int NMT, int MT>
 __device__ __forceinline__ void issue_tile(const Bufs &bf, const StepIO<PAR> &io, int64_t G, int wv, int lane)
 {
-    static_assert(NMT == kMT && kDmaX == NMT / 2, "one activation piece per tile of the first half");
-    if constexpr (MT < NMT / 2) dma_x_piece(bf, io.gx, io.xdst, wv, MT);
+    static_assert(NMT == GE::kMT && GE::kDmaX == NMT / 2, "one activation piece per tile of the first half");
+    if constexpr (MT < NMT / 2) dma_x_piece<GE>(bf, io.gx, io.xdst, wv, MT);
     if constexpr (PAR == 0 && MT < NMT / 2) {
 #pragma unroll
         for (int p = MT * kSZOps / (NMT / 2); p < (MT + 1) * kSZOps / (NMT / 2); ++p) load_sz_piece(bf, G, io.kt, lane, *io.z, p);
@@ -227,10 +248,10 @@ __device__ __forceinline__ void issue_tile(const Bufs &bf, const StepIO<PAR> &io
 }
 
 // All of a step's loads at once (ragged steps, whose tile count is not known at compile time).
-template <int B, int PAR>
+template <int B, typename GE, int PAR>
 __device__ __forceinline__ void issue_all(const Bufs &bf, const StepIO<PAR> &io, int64_t G, int wv, int lane, int nmt)
 {
-    dma_x(bf, io.gx, io.xdst, wv, nmt);
+    dma_x<GE>(bf, io.gx, io.xdst, wv, nmt);
     if constexpr (PAR == 0) load_sz(bf, G, io.kt, lane, *io.z);
     else dma_w<B>(bf, io.kt, io.wdst, lane);
 }
@@ -307,8 +328,8 @@ __device__ __forceinline__ void tile_mma(const h8 (&A)[kRBW][4], const h8 (&X)[4
 }
 
 // tot[.][mt] += s * acc (fp32; the scale is the fp16 half SH of each packed scale word).
-template <int SH>
-__device__ __forceinline__ void scale_acc(const uint32_t (&sc)[kRBW][4], const f4 (&acc)[kRBW], f4 (&tot)[kRBW][kMT],
+template <int SH, int MTS>
+__device__ __forceinline__ void scale_acc(const uint32_t (&sc)[kRBW][4], const f4 (&acc)[kRBW], f4 (&tot)[kRBW][MTS],
                                           int mt)
 {
 #pragma unroll
@@ -337,17 +358,17 @@ __device__ __forceinline__ void unpack_range(const uint32_t *d, const GroupConst
 // matrix-core chains of tile MT, the scale-accumulate of tile MT-1 and a share of the next
 // group's unpack (its eight blocks spread evenly over the NMT tiles; row block 1's chunk is
 // read at tile NMT/2), interleaved so every wave keeps its matrix core and vector ALU busy.
-template <int B, int SH, int NH, int NMT, int MT>
+template <int B, typename GE, int SH, int NH, int NMT, int MT>
 __device__ __forceinline__ void full_tile(const h8 (&Acur)[kRBW][4], h8 (&Anxt)[kRBW][4], const uint32_t (&sc)[kRBW][4],
                                           const GroupConst<B> (&gc)[kRBW], const uint8_t *xs, const uint8_t *wpart,
                                           int lane, uint32_t (&d)[2 * B], h8 (&X)[kXR][4], f4 (&acc)[2][kRBW],
-                                          f4 (&tot)[kRBW][kMT], const Bufs &bf, const StepIO<NH ^ 1> &io, int64_t G,
-                                          int wv)
+                                          f4 (&tot)[kRBW][GE::kMT], const Bufs &bf, const StepIO<NH ^ 1> &io,
+                                          int64_t G, int wv)
 {
-    static_assert(NMT % 2 == 0 && NMT <= kMT, "even tile count");
+    static_assert(NMT % 2 == 0 && NMT <= GE::kMT, "even tile count");
     constexpr int cur = MT & 1, nxt = cur ^ 1;
     const int t = lane >> 4, r = lane & 15;
-    issue_tile<B, NH ^ 1, NMT, MT>(bf, io, G, wv, lane);
+    issue_tile<B, GE, NH ^ 1, NMT, MT>(bf, io, G, wv, lane);
     if constexpr (MT + kXA < NMT) {
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4)
@@ -369,15 +390,15 @@ __device__ __forceinline__ void full_tile(const h8 (&Acur)[kRBW][4], h8 (&Anxt)[
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int B, int SH, int NH, int NMT, int... MT>
+template <int B, typename GE, int SH, int NH, int NMT, int... MT>
 __device__ __forceinline__ void full_tiles(std::integer_sequence<int, MT...>, const h8 (&Acur)[kRBW][4],
                                            h8 (&Anxt)[kRBW][4], const uint32_t (&sc)[kRBW][4],
                                            const GroupConst<B> (&gc)[kRBW], const uint8_t *xs, const uint8_t *wpart,
                                            int lane, uint32_t (&d)[2 * B], h8 (&X)[kXR][4], f4 (&acc)[2][kRBW],
-                                           f4 (&tot)[kRBW][kMT], const Bufs &bf, const StepIO<NH ^ 1> &io, int64_t G,
-                                           int wv)
+                                           f4 (&tot)[kRBW][GE::kMT], const Bufs &bf, const StepIO<NH ^ 1> &io,
+                                           int64_t G, int wv)
 {
-    (full_tile<B, SH, NH, NMT, MT>(Acur, Anxt, sc, gc, xs, wpart, lane, d, X, acc, tot, bf, io, G, wv), ...);
+    (full_tile<B, GE, SH, NH, NMT, MT>(Acur, Anxt, sc, gc, xs, wpart, lane, d, X, acc, tot, bf, io, G, wv), ...);
 }
 
 // One 128-k group step: A(g) = Acur times the activation tile of group g (slot xs), scale
@@ -386,11 +407,11 @@ __device__ __forceinline__ void full_tiles(std::integer_sequence<int, MT...>, co
 // that unpacks a first group, NH = 0, is an odd step).  NMT > 0: the first NMT 16-row
 // activation tiles all hold rows; NMT == 0: nmt tiles hold rows (ragged), the loads are
 // issued at once and the next group is unpacked first.
-template <int B, int SH, int NH, int NMT>
+template <int B, typename GE, int SH, int NH, int NMT>
 __device__ __forceinline__ void group_step(const h8 (&Acur)[kRBW][4], h8 (&Anxt)[kRBW][4], const uint32_t (&sc)[kRBW][4],
                                            const SZ &zn, const uint8_t *xs, const uint8_t *wpart, int lane, int nmt,
-                                           f4 (&tot)[kRBW][kMT], const Bufs &bf, const StepIO<NH ^ 1> &io, int64_t G,
-                                           int wv)
+                                           f4 (&tot)[kRBW][GE::kMT], const Bufs &bf, const StepIO<NH ^ 1> &io,
+                                           int64_t G, int wv)
 {
     const int t = lane >> 4, r = lane & 15;
     f4 acc[2][kRBW];
@@ -404,10 +425,10 @@ __device__ __forceinline__ void group_step(const h8 (&Acur)[kRBW][4], h8 (&Anxt)
         set_gc<B>(zn, NH, gc);
         uint32_t d[2 * B];
         __builtin_amdgcn_sched_barrier(0);
-        full_tiles<B, SH, NH, NMT>(std::make_integer_sequence<int, NMT>{}, Acur, Anxt, sc, gc, xs, wpart, lane, d, X,
-                                   acc, tot, bf, io, G, wv);
+        full_tiles<B, GE, SH, NH, NMT>(std::make_integer_sequence<int, NMT>{}, Acur, Anxt, sc, gc, xs, wpart, lane, d,
+                                       X, acc, tot, bf, io, G, wv);
     } else {
-        issue_all<B, NH ^ 1>(bf, io, G, wv, lane, nmt);
+        issue_all<B, GE, NH ^ 1>(bf, io, G, wv, lane, nmt);
         __builtin_amdgcn_sched_barrier(0);
         // Every ragged step has a first tile: its matrix-core chains run interleaved with the
         // unpack of the next group (few tiles leave the vector ALU the larger share), while
@@ -429,10 +450,10 @@ __device__ __forceinline__ void group_step(const h8 (&Acur)[kRBW][4], h8 (&Anxt)
         __builtin_amdgcn_sched_barrier(0);
         if (nmt == 1) scale_acc<SH>(sc, acc[0], tot, 0);
 #pragma unroll
-        for (int mt = 1; mt < kMT; ++mt) {
+        for (int mt = 1; mt < GE::kMT; ++mt) {
             if (mt >= nmt) break;  // uniform: tiles past the workgroup's rows are skipped
             const int cur = mt & 1, nxt = cur ^ 1;
-            if (mt + 1 < kMT && mt + 1 < nmt) {
+            if (mt + 1 < GE::kMT && mt + 1 < nmt) {
                 const int row = 16 * (mt + 1) + r;
 #pragma unroll
                 for (int j4 = 0; j4 < 4; ++j4) X[nxt][j4] = *(const h8 *)(xs + xs_off(row, 4 * j4 + t));
@@ -460,24 +481,25 @@ __device__ __forceinline__ void group_step(const h8 (&Acur)[kRBW][4], h8 (&Anxt)
 //  vmcnt(weight DMAs) after steps 2t+1.  Loads past the end are clamped to the last group or
 //  tile and land in slots that are not read again; the A operands unpacked from them are
 //  discarded.
-template <int B, int NMT>
+template <int B, typename GE, int NMT>
 //  The four slots reach the loop as restrict pointers: that tells the compiler that reads of
 //  one slot never touch a DMA in flight into another.  Without it (slots at run-time offsets
 //  in one array) it waits for every outstanding load, the weight DMA meant to run a step and a
 //  half ahead included, before each read of the ring.
 __device__ __forceinline__ void k_loop(const Bufs &bf, uint8_t *__restrict__ xs0, uint8_t *__restrict__ xs1,
                                        uint8_t *__restrict__ ws0, uint8_t *__restrict__ ws1, int64_t KT, int64_t G, int wv, int lane, int nmt,
-                                       f4 (&tot)[kRBW][kMT])
+                                       f4 (&tot)[kRBW][GE::kMT])
 {
     const int64_t GN = 2 * KT;  // groups
     auto gclamp = [&](int64_t g) { return g < GN ? g : GN - 1; };
     auto tclamp = [&](int64_t t) { return t < KT ? t : KT - 1; };
     uint8_t *w0 = ws0 + wv * (kRBW * WStage<B>::kBytes);  // this wave's parts of the weight slots
     uint8_t *w1 = ws1 + wv * (kRBW * WStage<B>::kBytes);
+    (void)sizeof(GE);
     SZ z0, z1;  // tiles of even / odd index
     h8 Aa[kRBW][4], Ab[kRBW][4];
 
-    dma_x(bf, 0, xs0, wv, nmt);
+    dma_x<GE>(bf, 0, xs0, wv, nmt);
     dma_w<B>(bf, 0, w0, lane);
     dma_w<B>(bf, tclamp(1), w1, lane);
     load_sz(bf, G, 0, lane, z0);
@@ -489,22 +511,22 @@ __device__ __forceinline__ void k_loop(const Bufs &bf, uint8_t *__restrict__ xs0
         const int64_t g = 2 * kt;
         // step g: tile kt, first group; unpack tile kt's second group
         const StepIO<0> s0{gclamp(g + 1), tclamp(kt + 1), xs1, nullptr, &z1};
-        group_step<B, 0, 1, NMT>(Aa, Ab, z0.sc, z0, xs0, w0, lane, nmt, tot, bf, s0, G, wv);
+        group_step<B, GE, 0, 1, NMT>(Aa, Ab, z0.sc, z0, xs0, w0, lane, nmt, tot, bf, s0, G, wv);
         wait_and_sync<0>();
         retired(z1);
         // step g+1: tile kt, second group; unpack tile kt+1's first group
         const StepIO<1> s1{gclamp(g + 2), tclamp(kt + 2), xs0, w0, nullptr};
-        group_step<B, 1, 0, NMT>(Ab, Aa, z0.sc, z1, xs1, w1, lane, nmt, tot, bf, s1, G, wv);
+        group_step<B, GE, 1, 0, NMT>(Ab, Aa, z0.sc, z1, xs1, w1, lane, nmt, tot, bf, s1, G, wv);
         wait_and_sync<kWOps<B>>();
         if (kt + 1 >= KT) break;
         // step g+2: tile kt+1, first group; unpack its second group
         const StepIO<0> s2{gclamp(g + 3), tclamp(kt + 2), xs1, nullptr, &z0};
-        group_step<B, 0, 1, NMT>(Aa, Ab, z1.sc, z1, xs0, w1, lane, nmt, tot, bf, s2, G, wv);
+        group_step<B, GE, 0, 1, NMT>(Aa, Ab, z1.sc, z1, xs0, w1, lane, nmt, tot, bf, s2, G, wv);
         wait_and_sync<0>();
         retired(z0);
         // step g+3: tile kt+1, second group; unpack tile kt+2's first group
         const StepIO<1> s3{gclamp(g + 4), tclamp(kt + 3), xs0, w1, nullptr};
-        group_step<B, 1, 0, NMT>(Ab, Aa, z1.sc, z0, xs1, w0, lane, nmt, tot, bf, s3, G, wv);
+        group_step<B, GE, 1, 0, NMT>(Ab, Aa, z1.sc, z0, xs1, w0, lane, nmt, tot, bf, s3, G, wv);
         wait_and_sync<kWOps<B>>();
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may land after the workgroup ends
@@ -550,18 +572,20 @@ __device__ __forceinline__ void plan_tile(const TilePlan &p, int64_t b, int64_t 
 // NMT > 0: every workgroup's first NMT 16-row activation tiles hold rows; NMT == 0: a ragged
 // workgroup (the last activation rows of a layer, or an expert's rows), tiles past its rows
 // are skipped.
-template <int B, int MODE, int NMT>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(GemmArgs a, TilePlan plan)
+template <int B, int MODE, int NMT, typename GE>
+__global__ __launch_bounds__(GE::kWaves * 64) __attribute__((amdgpu_waves_per_eu(GE::kWavesPerEU, GE::kWavesPerEU))) void gemm_kernel(
+    GemmArgs a, TilePlan plan)
 {
     constexpr bool OUTL = MODE == kOutl, GROUPED = MODE >= kGroupNone;
-    __shared__ __attribute__((aligned(16))) Smem<B> sm;
+    constexpr int kMT = GE::kMT, kMRows = GE::kMRows;
+    __shared__ __attribute__((aligned(16))) Smem<B, GE> sm;
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t = lane >> 4, r = lane & 15;
     const int64_t KT = a.k / kTileK, G = a.k / kGroup;
     int64_t nt, m0, mend;  // weight tile; sorted rows [m0, mend) of this workgroup
     int e = 0;
     if constexpr (GROUPED) {
-        // blockIdx = (weight tile, expert, 128-row tile of the expert's rows)
+        // blockIdx = (weight tile, expert, kMRows-row tile of the expert's rows)
         e = blockIdx.y;
         const int64_t r0 = a.offsets[e], r1 = a.offsets[e + 1];
         nt = blockIdx.x;
@@ -576,15 +600,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int nmt = (int)((mend - m0 + 15) / 16);
     const ExpertPtrs &W = a.ex[e];
     const int64_t NB = a.n / kTileN;
-    const int64_t rb0 = nt * (kNT / kTileN) + wv * kRBW;  // first row block of this wave
+    const int64_t rb0 = nt * (GE::kNT / kTileN) + wv * kRBW;  // first row block of this wave
 
     Bufs bf;
     // Activation rows are gathered per lane: the DMA source of a row past the workgroup's
     // rows lies past the buffer's range and reads zeros.
     bf.x = make_rsrc(a.x, a.m * a.ldx * 2);
 #pragma unroll
-    for (int it = 0; it < kDmaX; ++it) {
-        const int row = 16 * wv + 4 * it + (lane >> 4);
+    for (int it = 0; it < GE::kDmaX; ++it) {
+        const int row = 4 * (GE::kDmaX * wv + it) + (lane >> 4);
         const int c = (lane & 15) ^ (row & 15);
         const int64_t sr = m0 + row;
         int64_t src = sr;
@@ -602,6 +626,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     f4 tot[kRBW][kMT];
     if constexpr (OUTL) {
+        static_assert(kMT == 8, "the outlier partial's layout holds eight tiles per position block");
         // accumulators start from the outlier partial S^T (rows past n read as zeros)
         const rsrc_t sr = make_rsrc(a.spart, a.n * a.ldxt * 4);
         const uint32_t ld = (uint32_t)(a.ldxt * 4);
@@ -634,7 +659,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
     }
 
-    k_loop<B, NMT>(bf, sm.xs[0], sm.xs[1], sm.ws[0], sm.ws[1], KT, G, wv, lane, nmt, tot);
+    k_loop<B, GE, NMT>(bf, sm.xs[0], sm.xs[1], sm.ws[0], sm.ws[1], KT, G, wv, lane, nmt, tot);
 
     // epilogue
 #pragma unroll
@@ -749,14 +774,15 @@ static TilePlan one_rect(int32_t nt0, int32_t nnt, int32_t m0, int32_t mtiles, i
 template <int B, int MODE>
 static void gemm_launch(const GemmArgs &a, hipStream_t st)
 {
-    const int32_t NT = (int32_t)((a.n + kNT - 1) / kNT), F = (int32_t)(a.m / kMRows);
-    const dim3 block(kWaves * 64);
+    using GE = GeoLayer;
+    const int32_t NT = (int32_t)((a.n + GE::kNT - 1) / GE::kNT), F = (int32_t)(a.m / GE::kMRows);
+    const dim3 block(GE::kWaves * 64);
     if (F > 0)
-        hipLaunchKernelGGL((gemm_kernel<B, MODE, kMT>), dim3((unsigned)((int64_t)NT * F)), block, 0, st, a,
-                           one_rect(0, NT, 0, F, kMRows));
-    if (a.m % kMRows)
-        hipLaunchKernelGGL((gemm_kernel<B, MODE, 0>), dim3((unsigned)NT), block, 0, st, a,
-                           one_rect(0, NT, F * kMRows, 1, kMRows));
+        hipLaunchKernelGGL((gemm_kernel<B, MODE, GE::kMT, GE>), dim3((unsigned)((int64_t)NT * F)), block, 0, st, a,
+                           one_rect(0, NT, 0, F, GE::kMRows));
+    if (a.m % GE::kMRows)
+        hipLaunchKernelGGL((gemm_kernel<B, MODE, 0, GE>), dim3((unsigned)NT), block, 0, st, a,
+                           one_rect(0, NT, F * GE::kMRows, 1, GE::kMRows));
 }
 
 template <int B>
@@ -774,7 +800,7 @@ static hipError_t gemm_bits(const GemmArgs &a, hipStream_t st)
     return hipGetLastError();
 }
 
-int64_t gemm_xt_ld(int64_t m) { return (m + kMRows - 1) / kMRows * kMRows; }
+int64_t gemm_xt_ld(int64_t m) { return (m + GeoLayer::kMRows - 1) / GeoLayer::kMRows * GeoLayer::kMRows; }
 
 hipError_t launch_gemm(int bits, const GemmArgs &a, hipStream_t st)
 {
@@ -788,16 +814,23 @@ hipError_t launch_gemm(int bits, const GemmArgs &a, hipStream_t st)
     return hipErrorInvalidValue;
 }
 
-// Routed experts: one workgroup per (256-row weight tile, expert, 128-row tile of the
-// expert's sorted rows); the row tiles are sized for the worst case (all rows on one expert)
-// and the surplus workgroups return at once.
+// Routed experts: one workgroup per (weight tile, expert, row tile of the expert's sorted
+// rows); the row tiles are sized for the worst case (all rows on one expert) and the surplus
+// workgroups return at once.  With at most 32 rows per expert on average the small geometry
+// runs (three 4-wave workgroups per CU instead of one 8-wave one), else the layer's.
+template <int B, int MODE, typename GE>
+static hipError_t grouped_geo(int n_experts, const GemmArgs &a, hipStream_t st)
+{
+    const int64_t n_tiles = (a.n + GE::kNT - 1) / GE::kNT, m_tiles = (a.m + GE::kMRows - 1) / GE::kMRows;
+    hipLaunchKernelGGL((gemm_kernel<B, MODE, 0, GE>), dim3((unsigned)n_tiles, (unsigned)n_experts, (unsigned)m_tiles),
+                       dim3(GE::kWaves * 64), 0, st, a, TilePlan{});
+    return hipGetLastError();
+}
 template <int B, int MODE>
 static hipError_t grouped_mode(int n_experts, const GemmArgs &a, hipStream_t st)
 {
-    const int64_t n_tiles = (a.n + kNT - 1) / kNT, m_tiles = (a.m + kMRows - 1) / kMRows;
-    hipLaunchKernelGGL((gemm_kernel<B, MODE, 0>), dim3((unsigned)n_tiles, (unsigned)n_experts, (unsigned)m_tiles),
-                       dim3(kWaves * 64), 0, st, a, TilePlan{});
-    return hipGetLastError();
+    if (a.m <= (int64_t)GeoExperts::kMRows * n_experts) return grouped_geo<B, MODE, GeoExperts>(n_experts, a, st);
+    return grouped_geo<B, MODE, GeoLayer>(n_experts, a, st);
 }
 
 template <int B>
