@@ -14,8 +14,13 @@
 // The k loop is software-pipelined across groups: while the matrix cores multiply group g,
 // the vector ALU unpacks group g+1 and applies group g's scales, tile by tile, with the
 // scheduler told to interleave one MFMA, one fragment read and two vector ops, so every wave
-// keeps both units busy.  Every 128-k group is accumulated on the matrix cores in fp32 and
-// then scaled by its fp16 scale in fp32 (mixed-bit page, s4.2).
+// keeps both units busy; the step's loads for later steps are issued a few per tile.  Every
+// 128-k group is accumulated on the matrix cores in fp32 and then scaled by its fp16 scale in
+// fp32 (mixed-bit page, s4.2).
+//
+// Routed experts (on-device MoE page, s4.2) run the same kernel on their sorted token rows.
+// With few rows per expert a step is short and a wave's work in it mostly serial, so they use
+// a smaller workgroup (four waves, 32 activation rows) of which three fit on a CU.
 //
 // Outlier add-back (70B page, s2): the held-out fp16 weights are added in fp32 before the one
 // fp16 rounding of y.  Two small kernels run first: one writes x transposed (x^T) into the
@@ -437,8 +442,10 @@ __device__ __forceinline__ void group_step(const h8 (&Acur)[kRBW][4], h8 (&Anxt)
         h8 X[2][4];
 #pragma unroll
         for (int j4 = 0; j4 < 4; ++j4) X[0][j4] = *(const h8 *)(xs + xs_off(r, 4 * j4 + t));
+        if constexpr (GE::kMT > 1) {
 #pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4) X[1][j4] = *(const h8 *)(xs + xs_off(16 + r, 4 * j4 + t));
+            for (int j4 = 0; j4 < 4; ++j4) X[1][j4] = *(const h8 *)(xs + xs_off(16 + r, 4 * j4 + t));
+        }
         tile_mma(Acur, X[0], acc[0]);
         unpack_group<B, NH>(wpart, zn, lane, Anxt);
 #pragma unroll
