@@ -25,7 +25,10 @@ COMMON = [
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     "-I", str(ROOT / "include"), "-I", str(CSRC),
 ]
-PER_FILE = {"quantize.hip": ["-ffp-contract=off"]}
+# The GEMV's matrix-core results feed vector fmas right away: with the VGPR form of MFMA
+# they are written where the fmas read them, instead of accumulation registers copied over
+# one by one (eight copies per k-tile in the 4-wave kernels).
+PER_FILE = {"quantize.hip": ["-ffp-contract=off"], "qmm_small.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:
