@@ -52,10 +52,12 @@ def lib():
         L.or_round_half.argtypes = [dbl]
         L.or_quantize_group.restype = None
         L.or_quantize_group.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.or_quantize_group_sym.restype = None
+        L.or_quantize_group_sym.argtypes = [vp, i32, i32, vp, vp]
         L.or_outlier_count.restype = i64
         L.or_outlier_count.argtypes = [i64, i64, dbl]
         L.or_quantize.restype = i32
-        L.or_quantize.argtypes = [i64, i64, i32, i32, vp, i64, dbl, vp, vp, vp, vp, vp, vp,
+        L.or_quantize.argtypes = [i64, i64, i32, i32, i32, vp, i64, dbl, vp, vp, vp, vp, vp, vp,
                                   i64, ctypes.POINTER(i64)]
         L.or_unit_values.restype = i32
         L.or_unit_values.argtypes = [i32]
@@ -123,13 +125,23 @@ def quantize_group(w_fp16, bits: int):
     return int(s[0]), int(z[0]), q
 
 
+def quantize_group_sym(w_fp16, bits: int):
+    """One symmetric group -> (scale_bits uint16, codes uint8[n]); zero point 2^(bits-1)."""
+    w = _bits16(w_fp16).ravel()
+    s = np.zeros(1, np.uint16)
+    q = np.zeros(w.size, np.uint8)
+    lib().or_quantize_group_sym(_p(w), w.size, bits, _p(s), _p(q))
+    return int(s[0]), q
+
+
 def outlier_count(n: int, k: int, frac: float) -> int:
     return lib().or_outlier_count(n, k, frac)
 
 
-def quantize(w_fp16, bits: int, outlier_frac: float = 0.0, g: int = GROUP):
+def quantize(w_fp16, bits: int, outlier_frac: float = 0.0, g: int = GROUP, sym: bool = False):
     """W [N, K] fp16 -> dict(codes u8 [N,K], scales u16 [N,K/g], zeros u8 [N,K/g],
-    rowptr i32 [N+1], col i32 [nnz], val u16 [nnz])."""
+    rowptr i32 [N+1], col i32 [nnz], val u16 [nnz], sym).  With sym the groups are
+    symmetric and `zeros` holds the implied midpoint 2^(bits-1) everywhere."""
     w = _bits16(w_fp16)
     N, K = w.shape
     G = K // g
@@ -141,12 +153,14 @@ def quantize(w_fp16, bits: int, outlier_frac: float = 0.0, g: int = GROUP):
     col = np.zeros(max(kout, 1), np.int32)
     val = np.zeros(max(kout, 1), np.uint16)
     nnz = ctypes.c_int64(0)
-    rc = lib().or_quantize(N, K, bits, g, _p(w), K, outlier_frac, _p(codes), _p(scales),
-                           _p(zeros), _p(rowptr), _p(col), _p(val), kout, ctypes.byref(nnz))
+    rc = lib().or_quantize(N, K, bits, g, 1 if sym else 0, _p(w), K, outlier_frac, _p(codes), _p(scales),
+                           None if sym else _p(zeros), _p(rowptr), _p(col), _p(val), kout, ctypes.byref(nnz))
     if rc != 0:
         raise ValueError(f"or_quantize failed rc={rc}")
+    if sym:
+        zeros[:] = 1 << (bits - 1)
     return dict(codes=codes, scales=scales, zeros=zeros, rowptr=rowptr,
-                col=col[:nnz.value], val=val[:nnz.value])
+                col=col[:nnz.value], val=val[:nnz.value], sym=sym)
 
 
 # ---- packing -------------------------------------------------------------------------

@@ -31,7 +31,12 @@
  *  - "top 0.1% per group" is read as the global floor(frac*N*K) largest |w| (fp16
  *    magnitude, ties to the lower row-major index), removed from the group range by
  *    setting them to +0 in the dense copy and kept in an fp16 CSR over W's rows;
- *  - bits inside a packing unit are LSB-first and units are stored little-endian.
+ *  - bits inside a packing unit are LSB-first and units are stored little-endian;
+ *  - symmetric groups ([MB] s2.3: no zero point stored at low bit widths, the scale
+ *    absorbs the offset): the range is [-m, m] with m = max |w|, so the scale is
+ *    fp16((m + m) / qmax) and the zero point is the midpoint 2^(b-1), which the
+ *    asymmetric formula would also give for that range; it is implied, not stored, and
+ *    an all-zero group gets scale 1.0 with every code at the midpoint.
  *
  * Arithmetic: quantization in fp32 exactly as stated; every matmul accumulates in
  * fp64 over the exactly dequantized weights.  Build: gcc -O2 -ffp-contract=off
@@ -143,6 +148,33 @@ void or_quantize_group(const uint16_t *w, int n, int bits,
     *zero_out = (uint8_t)zp;
 }
 
+/* Quantize one symmetric group of `n` fp16 weights: zero point 2^(bits-1), implied. */
+void or_quantize_group_sym(const uint16_t *w, int n, int bits, uint16_t *scale_out, uint8_t *codes_out)
+{
+    const int qmax = (1 << bits) - 1, z = 1 << (bits - 1);
+    float m = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        float a = fabsf((float)hv(w[i]));
+        if (a > m) m = a;
+    }
+    if (m == 0.0f) {                                 /* all-zero group */
+        *scale_out = 0x3C00;                         /* 1.0 */
+        for (int i = 0; i < n; ++i) codes_out[i] = (uint8_t)z;
+        return;
+    }
+    volatile float two_m = m + m;                    /* exact */
+    volatile float s32 = two_m / (float)qmax;
+    uint16_t sh = or_round_half((double)s32);
+    if ((sh & 0x7C00) == 0)                          /* zero or subnormal fp16 */
+        sh = 0x0400;                                 /* 2^-14 */
+    float sf = (float)or_half_value(sh);
+    for (int i = 0; i < n; ++i) {
+        volatile float t = (float)hv(w[i]) / sf;
+        codes_out[i] = (uint8_t)clampi((int)rintf(t) + z, 0, qmax);
+    }
+    *scale_out = sh;
+}
+
 /* Number of outliers held out for a fraction `frac` of an N x K matrix. */
 int64_t or_outlier_count(int64_t n, int64_t k, double frac)
 {
@@ -169,13 +201,14 @@ static int rank_cmp(const void *pa, const void *pb)
  * their dense slots become +0 before the group range is taken, and the original fp16
  * values go to a CSR over rows (cols ascending).  Returns 0 on success, 1 if the CSR
  * capacity is too small (*nnz_out then holds the required count), 2 on bad arguments.
+ * zero_mode 1 quantizes symmetric groups (zeros is then not written and may be NULL).
  */
-int or_quantize(int64_t N, int64_t K, int bits, int g,
+int or_quantize(int64_t N, int64_t K, int bits, int g, int zero_mode,
                 const uint16_t *w, int64_t ldw, double outlier_frac,
                 uint8_t *codes, uint16_t *scales, uint8_t *zeros,
                 int32_t *rowptr, int32_t *col, uint16_t *val, int64_t cap, int64_t *nnz_out)
 {
-    if (bits < 2 || bits > 6 || g <= 0 || K % g != 0 || ldw < K) return 2;
+    if (bits < 2 || bits > 6 || g <= 0 || K % g != 0 || ldw < K || zero_mode < 0 || zero_mode > 1) return 2;
     int64_t kout = or_outlier_count(N, K, outlier_frac);
     *nnz_out = kout;
     if (kout > 0 && kout > cap) return 1;
@@ -213,8 +246,11 @@ int or_quantize(int64_t N, int64_t K, int bits, int g,
                 int64_t k = gi * g + i;
                 buf[i] = (held && held[n * K + k]) ? 0x0000 : w[n * ldw + k];
             }
-            or_quantize_group(buf, g, bits, &scales[n * G + gi], &zeros[n * G + gi],
-                              &codes[n * K + gi * g]);
+            if (zero_mode == 1)
+                or_quantize_group_sym(buf, g, bits, &scales[n * G + gi], &codes[n * K + gi * g]);
+            else
+                or_quantize_group(buf, g, bits, &scales[n * G + gi], &zeros[n * G + gi],
+                                  &codes[n * K + gi * g]);
         }
     }
     free(buf);
