@@ -80,12 +80,23 @@ enum {
     QP_EPI_ROWS_F32 = 2 /* y is float: y[r][n] = acc (fp32), for a later combine      */
 };
 
+/* Zero points of the groups.
+ *  QP_ZERO_STORED:   affine groups; one u8 zero point per group in qp_weight.zeros
+ *                    (inference acceleration guide, s1.1).
+ *  QP_ZERO_MIDPOINT: symmetric groups (mixed-bit page, s2.3: the zero point dropped at 2 and
+ *                    3 bits, the scale absorbing the offset): the group range is [-m, m] with
+ *                    m = max |w|, scale = fp16((m + m) / (2^b - 1)), and the zero point is the
+ *                    midpoint 2^(b-1), implied rather than stored (qp_weight.zeros is not read
+ *                    and may be NULL).  An all-zero group gets scale 1.0 with every code at
+ *                    the midpoint.  Allowed at every bit width. */
+enum { QP_ZERO_STORED = 0, QP_ZERO_MIDPOINT = 1 };
+
 /* Shape and format of one quantized matrix W[n][k]. */
 typedef struct {
     int32_t bits;       /* 2, 3, 4, 5 or 6 */
     int32_t group_size; /* 128 (groups of consecutive k inside a row) */
     int32_t layout;     /* QP_LAYOUT_CANONICAL or QP_LAYOUT_DEVICE */
-    int32_t reserved;   /* must be 0 */
+    int32_t zero_mode;  /* QP_ZERO_STORED or QP_ZERO_MIDPOINT */
     int64_t n;          /* rows (output features) */
     int64_t k;          /* columns (input features), multiple of group_size */
 } qp_weight_desc;
@@ -94,7 +105,7 @@ typedef struct {
 typedef struct {
     const void *packed;         /* qp_packed_bytes(desc) bytes, 16-byte aligned */
     const uint16_t *scales;     /* fp16 [n][k/128], row-major (planar), 4-byte aligned */
-    const uint8_t *zeros;       /* u8   [n][k/128], row-major, 2-byte aligned */
+    const uint8_t *zeros;       /* u8   [n][k/128], row-major, 2-byte aligned (QP_ZERO_STORED) */
     const int32_t *csr_rowptr;  /* [n+1] outlier CSR over rows of W, or NULL */
     const int32_t *csr_col;     /* [nnz] column k of each outlier, ascending within a row */
     const uint16_t *csr_val;    /* [nnz] fp16 value of each outlier */

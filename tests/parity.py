@@ -46,13 +46,14 @@ def gpu():
 class GpuWeight:
     """Quantized + packed weight on the device, built through the C ABI."""
 
-    def __init__(self, w_fp16: np.ndarray, bits: int, outlier_frac: float = 0.0, layout: int = 1):
+    def __init__(self, w_fp16: np.ndarray, bits: int, outlier_frac: float = 0.0, layout: int = 1,
+                 sym: bool = False):
         torch, q = gpu()
         n, k = w_fp16.shape
         dev = torch.device("cuda")
-        self.n, self.k, self.bits = n, k, bits
+        self.n, self.k, self.bits, self.sym = n, k, bits, sym
         w = torch.from_numpy(np.ascontiguousarray(w_fp16).view(np.int16)).to(dev)
-        d = q.desc(bits, n, k, layout)
+        d = q.desc(bits, n, k, layout, zero_mode=q.QP_ZERO_MIDPOINT if sym else q.QP_ZERO_STORED)
         self.desc = d
         G = k // 128
         self.codes = torch.empty((n, k), dtype=torch.uint8, device=dev)
@@ -64,6 +65,8 @@ class GpuWeight:
         self.val = torch.empty(max(kout, 1), dtype=torch.int16, device=dev)
         wsb = q.qpack_quantize_workspace_bytes(d, outlier_frac)
         ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        if sym:  # no zero points are written or read: pass none
+            self.zeros = None
         _, self.nnz = q.qpack_quantize(d, w, k, outlier_frac, self.codes, self.scales, self.zeros,
                                        self.rowptr, self.col, self.val, kout, ws, wsb)
         del w, ws
@@ -78,8 +81,10 @@ class GpuWeight:
 
     def host(self) -> dict:
         """Device results copied back (for comparison with the oracle's own results)."""
+        zeros = (np.full((self.n, self.k // 128), 1 << (self.bits - 1), np.uint8) if self.sym
+                 else self.zeros.cpu().numpy())
         return dict(codes=self.codes.cpu().numpy(), scales=self.scales.cpu().numpy().view(np.uint16),
-                    zeros=self.zeros.cpu().numpy(), rowptr=self.rowptr.cpu().numpy(),
+                    zeros=zeros, rowptr=self.rowptr.cpu().numpy(),
                     col=self.col.cpu().numpy()[: self.nnz], val=self.val.cpu().numpy().view(np.uint16)[: self.nnz])
 
 

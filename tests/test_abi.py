@@ -138,6 +138,24 @@ def test_quantize_validation():
     assert q.qpack_quantize_workspace_bytes(d, 0.001) > 32768 * 4
 
 
+def test_zero_mode_validation():
+    """QP_ZERO_MIDPOINT descriptors are valid at every bit width and need no zero points;
+    unknown modes are rejected; QP_ZERO_STORED still needs them (all checked before any
+    device work)."""
+    for bits in (2, 3, 4, 5, 6):
+        assert q.qp_packed_bytes(q.desc(bits, 64, 1024, zero_mode=q.QP_ZERO_MIDPOINT)) == 64 * 1024 * bits // 8
+    assert q.qp_packed_bytes(q.desc(4, 64, 1024, zero_mode=2)) == 0
+    assert q.qp_packed_bytes(q.desc(4, 64, 1024, zero_mode=-1)) == 0
+    d = q.desc(4, 64, 1024)
+    st, _ = q.qpack_quantize(d, FAKE, 1024, 0.0, FAKE, FAKE, None, stream=0, check=False)
+    assert st == q.QP_ERR_INVALID_ARG                       # stored zero points need a buffer
+    w = q.weight(FAKE, FAKE, None)
+    assert q.qlinear_gemv(d, w, FAKE, 1024, 1, FAKE, 64, stream=0, check=False) == q.QP_ERR_INVALID_ARG
+    bad = q.desc(4, 64, 1024, zero_mode=3)
+    assert q.qlinear_gemv(bad, q.weight(FAKE, FAKE, FAKE), FAKE, 1024, 1, FAKE, 64, stream=0,
+                          check=False) == q.QP_ERR_INVALID_ARG
+
+
 def test_grouped_and_moe_validation():
     d = q.desc(4, 256, 512)
     w = q.weight(FAKE, FAKE, FAKE)

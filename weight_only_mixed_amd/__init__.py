@@ -26,13 +26,14 @@ lib = ctypes.CDLL(str(_LIB_PATH))
 QP_OK, QP_ERR_INVALID_ARG, QP_ERR_UNSUPPORTED, QP_ERR_DEVICE, QP_ERR_WORKSPACE = range(5)
 QP_LAYOUT_CANONICAL, QP_LAYOUT_DEVICE = 0, 1
 QP_EPI_NONE, QP_EPI_SWIGLU, QP_EPI_ROWS_F32 = 0, 1, 2
+QP_ZERO_STORED, QP_ZERO_MIDPOINT = 0, 1
 STATUS_NAMES = {0: "QP_OK", 1: "QP_ERR_INVALID_ARG", 2: "QP_ERR_UNSUPPORTED", 3: "QP_ERR_DEVICE",
                 4: "QP_ERR_WORKSPACE"}
 
 
 class qp_weight_desc(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("group_size", ctypes.c_int32), ("layout", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("n", ctypes.c_int64), ("k", ctypes.c_int64)]
+                ("zero_mode", ctypes.c_int32), ("n", ctypes.c_int64), ("k", ctypes.c_int64)]
 
 
 class qp_weight(ctypes.Structure):
@@ -111,8 +112,9 @@ def _check(fn, status, check):
     return status
 
 
-def desc(bits: int, n: int, k: int, layout: int = QP_LAYOUT_DEVICE, group_size: int = 128):
-    return qp_weight_desc(bits, group_size, layout, 0, n, k)
+def desc(bits: int, n: int, k: int, layout: int = QP_LAYOUT_DEVICE, group_size: int = 128,
+         zero_mode: int = QP_ZERO_STORED):
+    return qp_weight_desc(bits, group_size, layout, zero_mode, n, k)
 
 
 def weight(packed, scales, zeros, rowptr=None, col=None, val=None, nnz: int = 0):

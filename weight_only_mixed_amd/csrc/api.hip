@@ -40,7 +40,8 @@ static qp_status check_desc(const qp_weight_desc *d, bool need_device)
 {
     if (!d) return fail(QP_ERR_INVALID_ARG, "desc is NULL");
     if (d->bits < 2 || d->bits > 6) return fail(QP_ERR_INVALID_ARG, "bits=%d not in 2..6", d->bits);
-    if (d->reserved != 0) return fail(QP_ERR_INVALID_ARG, "desc.reserved must be 0");
+    if (d->zero_mode != QP_ZERO_STORED && d->zero_mode != QP_ZERO_MIDPOINT)
+        return fail(QP_ERR_INVALID_ARG, "zero_mode=%d unknown", d->zero_mode);
     if (d->layout != QP_LAYOUT_CANONICAL && d->layout != QP_LAYOUT_DEVICE)
         return fail(QP_ERR_INVALID_ARG, "layout=%d unknown", d->layout);
     if (d->n <= 0 || d->k <= 0) return fail(QP_ERR_INVALID_ARG, "n=%lld k=%lld must be > 0", (long long)d->n, (long long)d->k);
@@ -62,7 +63,8 @@ static qp_status check_weight(const qp_weight_desc *d, const qp_weight *w, bool 
     if (!w) return fail(QP_ERR_INVALID_ARG, "weight is NULL");
     if (!w->packed || !aligned(w->packed, 16)) return fail(QP_ERR_INVALID_ARG, "packed NULL or not 16-byte aligned");
     if (!w->scales || !aligned(w->scales, 4)) return fail(QP_ERR_INVALID_ARG, "scales NULL or not 4-byte aligned");
-    if (!w->zeros || !aligned(w->zeros, 2)) return fail(QP_ERR_INVALID_ARG, "zeros NULL or not 2-byte aligned");
+    if (d->zero_mode == QP_ZERO_STORED && (!w->zeros || !aligned(w->zeros, 2)))
+        return fail(QP_ERR_INVALID_ARG, "zeros NULL or not 2-byte aligned");
     if (w->nnz < 0) return fail(QP_ERR_INVALID_ARG, "nnz < 0");
     if (w->csr_rowptr) {
         if (!allow_csr && w->nnz > 0) return fail(QP_ERR_UNSUPPORTED, "outlier CSR not supported here");
@@ -70,8 +72,14 @@ static qp_status check_weight(const qp_weight_desc *d, const qp_weight *w, bool 
     } else if (w->nnz > 0) {
         return fail(QP_ERR_INVALID_ARG, "nnz > 0 but csr_rowptr is NULL");
     }
-    (void)d;
     return QP_OK;
+}
+
+// Zero-point pair the kernels use in place of the stored ones: 0 = read them; for implied
+// midpoints, 2^(b-1) in both bytes (a row's two groups of one k-tile).
+static uint32_t zero_pair(const qp_weight_desc *d)
+{
+    return d->zero_mode == QP_ZERO_MIDPOINT ? 0x101u << (d->bits - 1) : 0u;
 }
 
 static hipStream_t S(void *s) { return (hipStream_t)s; }
@@ -123,7 +131,7 @@ qp_status qpack_quantize(const qp_weight_desc *d, const uint16_t *w, int64_t ldw
     if (!w || !aligned(w, 4)) return fail(QP_ERR_INVALID_ARG, "w NULL or not 4-byte aligned");
     if (ldw < d->k || ldw % 2 != 0) return fail(QP_ERR_INVALID_ARG, "ldw=%lld must be >= k and even", (long long)ldw);
     if (!codes || !aligned(codes, 2)) return fail(QP_ERR_INVALID_ARG, "codes NULL or not 2-byte aligned");
-    if (!scales || !zeros) return fail(QP_ERR_INVALID_ARG, "scales/zeros NULL");
+    if (!scales || (!zeros && d->zero_mode == QP_ZERO_STORED)) return fail(QP_ERR_INVALID_ARG, "scales/zeros NULL");
     if (!nnz_out) return fail(QP_ERR_INVALID_ARG, "nnz_out NULL");
     if (outlier_frac < 0.0 || outlier_frac > 1.0 || outlier_frac != outlier_frac)
         return fail(QP_ERR_INVALID_ARG, "outlier_frac must be in [0, 1]");
@@ -142,8 +150,8 @@ qp_status qpack_quantize(const qp_weight_desc *d, const uint16_t *w, int64_t ldw
     *nnz_out = kout;
     QuantWs ws{};
     if (kout > 0) ws = quant_ws_carve(workspace, d->n);
-    return device(launch_quantize(d->bits, w, ldw, d->n, d->k, kout, codes, scales, zeros, csr_rowptr,
-                                  csr_col, csr_val, ws, S(stream)),
+    return device(launch_quantize(d->bits, d->zero_mode == QP_ZERO_MIDPOINT, w, ldw, d->n, d->k, kout, codes, scales,
+                                  zeros, csr_rowptr, csr_col, csr_val, ws, S(stream)),
                   "qpack_quantize");
 }
 
@@ -189,6 +197,7 @@ static qp_status gemv_problem(const qp_weight_desc *d, const qp_weight *w, const
     if (m * ldx * 2 > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "x larger than 2 GiB");
     *p = GemvProblem{};
     p->w = {(const uint8_t *)w->packed, w->scales, w->zeros};
+    p->zmid = zero_pair(d);
     if (w->nnz > 0) {
         p->rowptr = w->csr_rowptr;
         p->col = w->csr_col;
@@ -252,6 +261,7 @@ qp_status qlinear_gemm(const qp_weight_desc *d, const qp_weight *w, const uint16
     if ((int64_t)qp_packed_bytes(d) > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "packed weight larger than 2 GiB");
     GemmArgs a{};
     a.ex[0] = {(const uint8_t *)w->packed, w->scales, w->zeros};
+    a.zmid = zero_pair(d);
     if (w->nnz > 0) {
         const size_t need = qlinear_gemm_workspace_bytes(d, m, w->nnz);
         if (!workspace || ws_bytes < need || !aligned(workspace, 16))
@@ -299,6 +309,7 @@ qp_status qlinear_grouped_gemm(const qp_weight_desc *d, const qp_weight *experts
     GemmArgs a{};
     for (int e = 0; e < n_experts; ++e)
         a.ex[e] = {(const uint8_t *)experts[e].packed, experts[e].scales, experts[e].zeros};
+    a.zmid = zero_pair(d);
     a.x = x;
     a.ldx = ldx;
     a.row_src = row_src;

@@ -97,6 +97,7 @@ struct Bufs {
     rsrc_t w[kRBW];           // packed tiles of row block rb0 + u (empty past the last block)
     rsrc_t sc[kRBW], zr[kRBW];
     uint32_t xoff[kDmaXMax];  // this lane's source of LDS-DMA piece it (row offset + chunk)
+    uint32_t zmid;            // 0: stored zero points; else the implied pair used instead
 };
 
 __device__ __forceinline__ void lds_dma16(rsrc_t r, uint8_t *lds, uint32_t voff, uint32_t soff)
@@ -264,8 +265,13 @@ __device__ __forceinline__ void issue_all(const Bufs &bf, const StepIO<PAR> &io,
 // After a wait that has retired this tile's scale / zero-point loads: hide their origin from
 // the compiler, which does not see the inline-asm wait and would otherwise wait for them again
 // at their first use, counting the weight DMA issued since (meant to stay in flight) as older.
-__device__ __forceinline__ void retired(SZ &z)
+// Implied zero points (zmid != 0) replace the loaded ones (those loads read out of range).
+__device__ __forceinline__ void retired(SZ &z, uint32_t zmid)
 {
+    if (zmid) {  // uniform
+#pragma unroll
+        for (int u = 0; u < kRBW; ++u) z.zz[u] = zmid;
+    }
 #pragma unroll
     for (int u = 0; u < kRBW; ++u) {
         asm volatile("" : "+v"(z.zz[u]));
@@ -511,7 +517,7 @@ __device__ __forceinline__ void k_loop(const Bufs &bf, uint8_t *__restrict__ xs0
     dma_w<B>(bf, tclamp(1), w1, lane);
     load_sz(bf, G, 0, lane, z0);
     wait_and_sync<0>();
-    retired(z0);
+    retired(z0, bf.zmid);
     unpack_group<B, 0>(w0, z0, lane, Aa);
 
     for (int64_t kt = 0; kt < KT; kt += 2) {
@@ -520,7 +526,7 @@ __device__ __forceinline__ void k_loop(const Bufs &bf, uint8_t *__restrict__ xs0
         const StepIO<0> s0{gclamp(g + 1), tclamp(kt + 1), xs1, nullptr, &z1};
         group_step<B, GE, 0, 1, NMT>(Aa, Ab, z0.sc, z0, xs0, w0, lane, nmt, tot, bf, s0, G, wv);
         wait_and_sync<0>();
-        retired(z1);
+        retired(z1, bf.zmid);
         // step g+1: tile kt, second group; unpack tile kt+1's first group
         const StepIO<1> s1{gclamp(g + 2), tclamp(kt + 2), xs0, w0, nullptr};
         group_step<B, GE, 1, 0, NMT>(Ab, Aa, z0.sc, z1, xs1, w1, lane, nmt, tot, bf, s1, G, wv);
@@ -530,7 +536,7 @@ __device__ __forceinline__ void k_loop(const Bufs &bf, uint8_t *__restrict__ xs0
         const StepIO<0> s2{gclamp(g + 3), tclamp(kt + 2), xs1, nullptr, &z0};
         group_step<B, GE, 0, 1, NMT>(Aa, Ab, z1.sc, z1, xs0, w1, lane, nmt, tot, bf, s2, G, wv);
         wait_and_sync<0>();
-        retired(z0);
+        retired(z0, bf.zmid);
         // step g+3: tile kt+1, second group; unpack tile kt+2's first group
         const StepIO<1> s3{gclamp(g + 4), tclamp(kt + 3), xs0, w1, nullptr};
         group_step<B, GE, 1, 0, NMT>(Ab, Aa, z1.sc, z0, xs1, w0, lane, nmt, tot, bf, s3, G, wv);
@@ -610,6 +616,7 @@ __global__ __launch_bounds__(GE::kWaves * 64) __attribute__((amdgpu_waves_per_eu
     const int64_t rb0 = nt * (GE::kNT / kTileN) + wv * kRBW;  // first row block of this wave
 
     Bufs bf;
+    bf.zmid = a.zmid;
     // Activation rows are gathered per lane: the DMA source of a row past the workgroup's
     // rows lies past the buffer's range and reads zeros.
     bf.x = make_rsrc(a.x, a.m * a.ldx * 2);
@@ -628,7 +635,7 @@ __global__ __launch_bounds__(GE::kWaves * 64) __attribute__((amdgpu_waves_per_eu
         const bool in = rb < NB;
         bf.w[u] = make_rsrc(W.packed + rb * KT * (512 * B), in ? KT * (512 * B) : 0);
         bf.sc[u] = make_rsrc(W.scales + rb * kTileN * G, in ? kTileN * G * 2 : 0);
-        bf.zr[u] = make_rsrc(W.zeros + rb * kTileN * G, in ? kTileN * G : 0);
+        bf.zr[u] = make_rsrc(W.zeros + rb * kTileN * G, in && !a.zmid ? kTileN * G : 0);
     }
 
     f4 tot[kRBW][kMT];

@@ -118,7 +118,7 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
     bf.G = G;
     bf.w = make_rsrc(a.w.packed + rb * KT * (512 * B), KT * (512 * B));
     bf.sc = make_rsrc(a.w.scales + rb * kTileN * G, kTileN * G * 2);
-    bf.zr = make_rsrc(a.w.zeros + rb * kTileN * G, kTileN * G);
+    bf.zr = make_rsrc(a.w.zeros + rb * kTileN * G, a.zmid ? 0 : kTileN * G);  // implied: none read
     bf.x = make_rsrc(a.x, a.m * a.ldx * 2);  // rows >= m read as zeros
 
     const int64_t nt = KT > wv ? (KT - wv + NW - 1) / NW : 0;  // tiles of this wave
@@ -165,7 +165,7 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
         const u4 scv = *(const u4 *)(slot + S::kSc + 16 * t);
         const uint32_t sc[4] = {scv[0], scv[1], scv[2], scv[3]};
         const uint32_t zpar = (uint32_t)((r * G + 2 * kt) & 3);
-        const uint32_t zz = *(const uint16_t *)(slot + S::kZr + 4 * r + zpar);
+        const uint32_t zz = a.zmid ? a.zmid : *(const uint16_t *)(slot + S::kZr + 4 * r + zpar);
         GroupConst<B> g0, g1;
         g0.set(zz & 0xFF);
         g1.set((zz >> 8) & 0xFF);

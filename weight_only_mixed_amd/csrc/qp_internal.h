@@ -33,7 +33,7 @@ struct QuantWs {  // carve-up of the quantize workspace
 };
 size_t quant_ws_bytes(int64_t n);
 QuantWs quant_ws_carve(void *ws, int64_t n);
-hipError_t launch_quantize(int bits, const uint16_t *w, int64_t ldw, int64_t n, int64_t k,
+hipError_t launch_quantize(int bits, bool sym, const uint16_t *w, int64_t ldw, int64_t n, int64_t k,
                            int64_t kout, uint8_t *codes, uint16_t *scales, uint8_t *zeros,
                            int32_t *rowptr, int32_t *col, uint16_t *val, const QuantWs &ws,
                            hipStream_t st);
@@ -61,7 +61,7 @@ struct GemvProblem {
     uint16_t *y;
     int64_t ldy;
     int32_t bits;
-    int32_t reserved;
+    uint32_t zmid;   // 0: stored zero points; else the implied pair (2^(b-1) in both bytes)
     int64_t block0;  // batch: first workgroup of this problem
 };
 struct GemvBatch {
@@ -85,6 +85,7 @@ struct GemmArgs {
     int64_t m, n, k;         // grouped: m = upper bound of the sorted rows (and of x's rows)
     void *y;
     int64_t ldy;
+    uint32_t zmid;  // 0: stored zero points; else the implied pair (2^(b-1) in both bytes)
     uint16_t *xt;   // workspace (outliers only): x transposed, [k][ldxt]
     float *spart;   // workspace (outliers only): fp32 outlier partial, [n][ldxt]
     int64_t ldxt;

@@ -216,6 +216,38 @@ __device__ int block_scan_excl_256(int v, int *lds)
     return base + x - v;
 }
 
+// Quantize one symmetric group of 128 held in a wave (two values per lane): range [-m, m]
+// with m = max |w|, scale fp16((m + m) / qmax), codes around the implied midpoint 2^(b-1).
+template <int BITS>
+__device__ __forceinline__ void quantize_group_wave_sym(float v0, float v1, int lane, uint8_t *codes_out,
+                                                        uint16_t *scale_out)
+{
+    constexpr int qmax = (1 << BITS) - 1, z = 1 << (BITS - 1);
+    float m = __builtin_fabsf(v0);
+    if (__builtin_fabsf(v1) > m) m = __builtin_fabsf(v1);
+    for (int off = 32; off > 0; off >>= 1) {
+        const float om = __shfl_xor(m, off);
+        if (om > m) m = om;
+    }
+    uint16_t sbits;
+    uint32_t q0, q1;
+    if (m == 0.0f) {
+        sbits = 0x3C00;  // 1.0
+        q0 = q1 = z;
+    } else {
+        const float s32 = __fdiv_rn(__fadd_rn(m, m), (float)qmax);
+        sbits = __builtin_bit_cast(uint16_t, (_Float16)s32);
+        if ((sbits & 0x7C00) == 0) sbits = 0x0400;  // zero / subnormal -> 2^-14
+        const float sf = (float)__builtin_bit_cast(_Float16, sbits);
+        int a = (int)__builtin_rintf(__fdiv_rn(v0, sf)) + z;
+        int b = (int)__builtin_rintf(__fdiv_rn(v1, sf)) + z;
+        q0 = a < 0 ? 0 : (a > qmax ? qmax : a);
+        q1 = b < 0 ? 0 : (b > qmax ? qmax : b);
+    }
+    *(uint16_t *)(codes_out + 2 * lane) = (uint16_t)(q0 | (q1 << 8));
+    if (lane == 0) *scale_out = sbits;
+}
+
 // Quantize one group of 128 held in a wave: two values per lane.
 template <int BITS>
 __device__ __forceinline__ void quantize_group_wave(float v0, float v1, int lane,
@@ -266,8 +298,9 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t b)
 }
 
 // One block per row.  With outliers: mark held-out elements in LDS (ordered scan), write
-// their CSR entries, then quantize each group with held-out slots read as +0.
-template <int BITS, bool OUTL>
+// their CSR entries, then quantize each group with held-out slots read as +0.  SYM: symmetric
+// groups, no zero points written.
+template <int BITS, bool OUTL, bool SYM>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(
     const uint16_t *w, int64_t ldw, int64_t k, const uint32_t *ctl, const int32_t *eq_base,
     const int32_t *rowptr, uint8_t *codes, uint16_t *scales, uint8_t *zeros, int32_t *col,
@@ -323,12 +356,15 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
             if (held[c]) v0 = 0.0f;
             if (held[c + 1]) v1 = 0.0f;
         }
-        quantize_group_wave<BITS>(v0, v1, lane, codes + r * k + g * kGroup, scales + r * G + g,
-                                  zeros + r * G + g);
+        if constexpr (SYM)
+            quantize_group_wave_sym<BITS>(v0, v1, lane, codes + r * k + g * kGroup, scales + r * G + g);
+        else
+            quantize_group_wave<BITS>(v0, v1, lane, codes + r * k + g * kGroup, scales + r * G + g,
+                                      zeros + r * G + g);
     }
 }
 
-template <int BITS>
+template <int BITS, bool SYM>
 static hipError_t quantize_bits(const uint16_t *w, int64_t ldw, int64_t n, int64_t k,
                                 int64_t kout, uint8_t *codes, uint16_t *scales, uint8_t *zeros,
                                 int32_t *rowptr, int32_t *col, uint16_t *val, const QuantWs &ws,
@@ -344,14 +380,14 @@ static hipError_t quantize_bits(const uint16_t *w, int64_t ldw, int64_t n, int64
                            ws.gt_cnt, ws.eq_cnt);
         hipLaunchKernelGGL(rowscan_kernel, dim3(1), dim3(1024), 0, st, n, ws.ctl, ws.gt_cnt,
                            ws.eq_cnt, ws.eq_base, rowptr);
-        hipLaunchKernelGGL((quantize_rows_kernel<BITS, true>), dim3(n), dim3(256), (size_t)k, st,
+        hipLaunchKernelGGL((quantize_rows_kernel<BITS, true, SYM>), dim3(n), dim3(256), (size_t)k, st,
                            w, ldw, k, ws.ctl, ws.eq_base, rowptr, codes, scales, zeros, col, val);
     } else {
         if (rowptr)
             hipLaunchKernelGGL(rowscan_kernel, dim3(1), dim3(1024), 0, st, n,
                                (const uint32_t *)nullptr, (const int32_t *)nullptr,
                                (const int32_t *)nullptr, (int32_t *)nullptr, rowptr);
-        hipLaunchKernelGGL((quantize_rows_kernel<BITS, false>), dim3(n), dim3(256), 0, st, w, ldw,
+        hipLaunchKernelGGL((quantize_rows_kernel<BITS, false, SYM>), dim3(n), dim3(256), 0, st, w, ldw,
                            k, (const uint32_t *)nullptr, (const int32_t *)nullptr,
                            (const int32_t *)nullptr, codes, scales, zeros, (int32_t *)nullptr,
                            (uint16_t *)nullptr);
@@ -359,19 +395,29 @@ static hipError_t quantize_bits(const uint16_t *w, int64_t ldw, int64_t n, int64
     return hipGetLastError();
 }
 
-hipError_t launch_quantize(int bits, const uint16_t *w, int64_t ldw, int64_t n, int64_t k,
+template <bool SYM>
+static hipError_t quantize_mode(int bits, const uint16_t *w, int64_t ldw, int64_t n, int64_t k,
+                                int64_t kout, uint8_t *codes, uint16_t *scales, uint8_t *zeros,
+                                int32_t *rowptr, int32_t *col, uint16_t *val, const QuantWs &ws,
+                                hipStream_t st)
+{
+    switch (bits) {
+    case 2: return quantize_bits<2, SYM>(w, ldw, n, k, kout, codes, scales, zeros, rowptr, col, val, ws, st);
+    case 3: return quantize_bits<3, SYM>(w, ldw, n, k, kout, codes, scales, zeros, rowptr, col, val, ws, st);
+    case 4: return quantize_bits<4, SYM>(w, ldw, n, k, kout, codes, scales, zeros, rowptr, col, val, ws, st);
+    case 5: return quantize_bits<5, SYM>(w, ldw, n, k, kout, codes, scales, zeros, rowptr, col, val, ws, st);
+    case 6: return quantize_bits<6, SYM>(w, ldw, n, k, kout, codes, scales, zeros, rowptr, col, val, ws, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_quantize(int bits, bool sym, const uint16_t *w, int64_t ldw, int64_t n, int64_t k,
                            int64_t kout, uint8_t *codes, uint16_t *scales, uint8_t *zeros,
                            int32_t *rowptr, int32_t *col, uint16_t *val, const QuantWs &ws,
                            hipStream_t st)
 {
-    switch (bits) {
-    case 2: return quantize_bits<2>(w, ldw, n, k, kout, codes, scales, zeros, rowptr, col, val, ws, st);
-    case 3: return quantize_bits<3>(w, ldw, n, k, kout, codes, scales, zeros, rowptr, col, val, ws, st);
-    case 4: return quantize_bits<4>(w, ldw, n, k, kout, codes, scales, zeros, rowptr, col, val, ws, st);
-    case 5: return quantize_bits<5>(w, ldw, n, k, kout, codes, scales, zeros, rowptr, col, val, ws, st);
-    case 6: return quantize_bits<6>(w, ldw, n, k, kout, codes, scales, zeros, rowptr, col, val, ws, st);
-    }
-    return hipErrorInvalidValue;
+    if (sym) return quantize_mode<true>(bits, w, ldw, n, k, kout, codes, scales, zeros, rowptr, col, val, ws, st);
+    return quantize_mode<false>(bits, w, ldw, n, k, kout, codes, scales, zeros, rowptr, col, val, ws, st);
 }
 
 }  // namespace qp
