@@ -41,11 +41,12 @@ __device__ __forceinline__ uint32_t magic_pair(uint32_t word, h2 mul, h2 add)
     return h2_bits(__builtin_elementwise_fma(bits_h2(t), mul, add));
 }
 
-// Packed (lo, hi) constants -1024*2^-p - zp for one group's zero point.
-__device__ __forceinline__ h2 add_const(float clo, float chi, float zp)
-{
-    return __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(clo - zp, chi - zp));
-}
+// fp16 bits of -(1024*2^-p + zp) for a zero point zp < 2^(10-p): 1024*2^-p + zp has exponent
+// 10 - p and mantissa zp*2^p, so the value is the sign and exponent bits of -1024*2^-p with
+// zp*2^p in the mantissa.  The packed (lo, hi) pair for offsets (plo, phi) is therefore one
+// integer multiply-add, zp * (2^plo + 2^(16+phi)) + bits(-1024*2^-plo, -1024*2^-phi), instead
+// of two fp32 subtractions and a conversion.
+__host__ __device__ constexpr uint32_t neg_bias_bits(int p) { return 0x8000u | ((uint32_t)(25 - p) << 10); }
 
 template <int plo, int phi>
 __device__ __forceinline__ h2 mul_const()
@@ -102,15 +103,18 @@ template <> struct Offsets<4> { static constexpr int n = 2; static constexpr int
 template <> struct Offsets<5> { static constexpr int n = 1; static constexpr int plo[1] = {0}; static constexpr int phi[1] = {4}; };
 template <> struct Offsets<6> { static constexpr int n = 1; static constexpr int plo[1] = {4}; static constexpr int phi[1] = {0}; };
 
+// Per-group constants of the bias trick: add[c] = (-1024*2^-plo - zp, -1024*2^-phi - zp) for
+// offset pair c, zp in [0, 2^B) (so zp < 2^(10-p) for every offset p with p + B <= 10).
 template <int B> struct GroupConst {
     h2 add[Offsets<B>::n];
     __device__ __forceinline__ void set(uint32_t zp)
     {
-        float z = (float)zp;
 #pragma unroll
-        for (int i = 0; i < Offsets<B>::n; ++i)
-            add[i] = add_const(-1024.0f / (float)(1 << Offsets<B>::plo[i]),
-                               -1024.0f / (float)(1 << Offsets<B>::phi[i]), z);
+        for (int i = 0; i < Offsets<B>::n; ++i) {
+            const uint32_t c = neg_bias_bits(Offsets<B>::plo[i]) | (neg_bias_bits(Offsets<B>::phi[i]) << 16);
+            const uint32_t mult = (1u << Offsets<B>::plo[i]) | (1u << (16 + Offsets<B>::phi[i]));
+            add[i] = bits_h2((zp & ((1u << B) - 1)) * mult + c);
+        }
     }
 };
 
