@@ -160,7 +160,7 @@ def quantize(w_fp16, bits: int, outlier_frac: float = 0.0, g: int = GROUP, sym: 
     if sym:
         zeros[:] = 1 << (bits - 1)
     return dict(codes=codes, scales=scales, zeros=zeros, rowptr=rowptr,
-                col=col[:nnz.value], val=val[:nnz.value], sym=sym)
+                col=col[:nnz.value], val=val[:nnz.value], sym=sym, g=g)
 
 
 # ---- packing -------------------------------------------------------------------------
@@ -220,13 +220,21 @@ def device_reorder(codes, bits: int, inverse: bool = False):
 
 # ---- matmuls -------------------------------------------------------------------------
 
-def linear(x_fp16, q: dict, g: int = GROUP, outliers: bool = True):
+def _group_of(q: dict, K: int) -> int:
+    """Group size of a quantized matrix (recorded by quantize, else from the scale shape)."""
+    g = q.get("g") or K // np.asarray(q["scales"]).shape[1]
+    assert K % g == 0 and np.asarray(q["scales"]).shape[1] == K // g
+    return g
+
+
+def linear(x_fp16, q: dict, outliers: bool = True):
     """fp64 r = x * What^T (+ CSR add-back).  x [M, K] fp16; q as returned by quantize."""
     x = _bits16(x_fp16)
     M, K = x.shape
     codes = _c(q["codes"], np.uint8)
     N = codes.shape[0]
     assert codes.shape[1] == K
+    g = _group_of(q, K)
     r = np.zeros((M, N), np.float64)
     use_csr = outliers and q.get("rowptr") is not None and len(q.get("col", [])) > 0
     lib().or_linear(M, N, K, g, _p(x), K, _p(codes), _p(_c(q["scales"], np.uint16)),
@@ -237,14 +245,16 @@ def linear(x_fp16, q: dict, g: int = GROUP, outliers: bool = True):
     return r
 
 
-def moe_ffn(x_fp16, ids, wts, gate: list, up: list, down: list, g: int = GROUP):
-    """fp64 routed-expert FFN.  gate/up/down: per-expert dicts from quantize()."""
+def moe_ffn(x_fp16, ids, wts, gate: list, up: list, down: list):
+    """fp64 routed-expert FFN.  gate/up/down: per-expert dicts from quantize() (one group size)."""
     x = _bits16(x_fp16)
     T, D = x.shape
     ids = _c(ids, np.int32)
     wts = _c(wts, np.float32)
     topk = ids.shape[1]
     F = gate[0]["codes"].shape[0]
+    g = _group_of(gate[0], D)
+    assert _group_of(down[0], F) == g
     st = lambda lst, key, dt: np.ascontiguousarray(np.stack([d[key] for d in lst]), dtype=dt)
     arrs = [st(gate, "codes", np.uint8), st(gate, "scales", np.uint16), st(gate, "zeros", np.uint8),
             st(up, "codes", np.uint8), st(up, "scales", np.uint16), st(up, "zeros", np.uint8),
@@ -254,10 +264,11 @@ def moe_ffn(x_fp16, ids, wts, gate: list, up: list, down: list, g: int = GROUP):
     return r
 
 
-def swiglu_act(x_row_fp16, gate: dict, up: dict, g: int = GROUP):
+def swiglu_act(x_row_fp16, gate: dict, up: dict):
     """fp64 silu(What_gate x) * (What_up x) for one token row, before fp16 rounding."""
     xt = _bits16(x_row_fp16).ravel()
     F, D = gate["codes"].shape
+    g = _group_of(gate, D)
     v = np.zeros(F, np.float64)
     lib().or_swiglu_act(D, F, g, _p(xt), _p(_c(gate["codes"], np.uint8)), _p(_c(gate["scales"], np.uint16)),
                         _p(_c(gate["zeros"], np.uint8)), _p(_c(up["codes"], np.uint8)),

@@ -5,6 +5,7 @@ s2 (held-out fp16 weights added back after the GEMM)."""
 from fractions import Fraction
 
 import numpy as np
+import pytest
 
 import oracle
 import workloads
@@ -80,3 +81,30 @@ def test_matches_library_matmul():
     want = x.astype(np.float64) @ (dequant64(q) + csr_dense(q, N, K)).T
     got = oracle.linear(x, q)
     assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("g", (32, 64))
+def test_small_groups_match_group_routine_and_brute_force(g):
+    """Groups of 32 and 64 (mixed-bit page, s2.3: small blocks for the lowest bit widths):
+    the matrix quantizer equals the group routine on each g-value group, and the linear
+    layer equals a brute-force fp64 product of the dequantized weights."""
+    w = workloads.weights_fp16(6, 256, 81)
+    for bits, sym in ((2, False), (2, True), (5, False)):
+        d = oracle.quantize(w, bits, g=g, sym=sym)
+        assert d["scales"].shape == (6, 256 // g) and d["g"] == g
+        for n in range(6):
+            for j in range(256 // g):
+                grp = w[n, g * j: g * (j + 1)]
+                if sym:
+                    s, q = oracle.quantize_group_sym(grp, bits)
+                else:
+                    s, z, q = oracle.quantize_group(grp, bits)
+                    assert d["zeros"][n, j] == z
+                assert d["scales"][n, j] == s
+                assert np.array_equal(d["codes"][n, g * j: g * (j + 1)], q)
+        x = workloads.activations_fp16(3, 256, 82)
+        sc = np.repeat(d["scales"].view(np.float16).astype(np.float64), g, axis=1)
+        zp = np.repeat(d["zeros"].astype(np.float64), g, axis=1)
+        what = (d["codes"].astype(np.float64) - zp) * sc
+        want = x.astype(np.float64) @ what.T
+        assert np.allclose(oracle.linear(x, d), want, rtol=1e-12, atol=1e-12)
