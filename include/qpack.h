@@ -2,9 +2,10 @@
  * qpack.h -- C ABI of the MI355X (gfx950) weight-only mixed-bit quantized linear layer.
  *
  * Weights W[n][k] (n = output feature, k = input feature) are quantized to b = 2..6 bits
- * with one fp16 scale and one integer zero point per group of 128 consecutive k of a row,
- * packed in the page units, dequantized on the GPU and multiplied by fp16 activations:
- *     y[m][n] = sum_k x[m][k] * (q[n][k] - zp[n][k/128]) * s[n][k/128]
+ * with one fp16 scale and one integer zero point per group of g = 128 (or 64, 32)
+ * consecutive k of a row, packed in the page units, dequantized on the GPU and multiplied by
+ * fp16 activations:
+ *     y[m][n] = sum_k x[m][k] * (q[n][k] - zp[n][k/g]) * s[n][k/g]
  *             + sum_{(n,k) in outliers} x[m][k] * w[n][k].
  *
  * Passages this interface follows (page title, section):
@@ -94,18 +95,22 @@ enum { QP_ZERO_STORED = 0, QP_ZERO_MIDPOINT = 1 };
 /* Shape and format of one quantized matrix W[n][k]. */
 typedef struct {
     int32_t bits;       /* 2, 3, 4, 5 or 6 */
-    int32_t group_size; /* 128 (groups of consecutive k inside a row) */
+    int32_t group_size; /* 32, 64 or 128 weights of consecutive k inside a row share a scale and
+                           zero point (mixed-bit page, s2.3: small groups for the lowest bit
+                           widths).  32 and 64: qpack_quantize, qpack_pack/unpack, qlinear_gemv
+                           and qlinear_gemv_batch (one group size per batch); the GEMM, grouped
+                           GEMM and MoE FFN return QP_ERR_UNSUPPORTED for them. */
     int32_t layout;     /* QP_LAYOUT_CANONICAL or QP_LAYOUT_DEVICE */
     int32_t zero_mode;  /* QP_ZERO_STORED or QP_ZERO_MIDPOINT */
     int64_t n;          /* rows (output features) */
-    int64_t k;          /* columns (input features), multiple of group_size */
+    int64_t k;          /* columns (input features), multiple of 128 */
 } qp_weight_desc;
 
 /* Device buffers of one quantized matrix. */
 typedef struct {
     const void *packed;         /* qp_packed_bytes(desc) bytes, 16-byte aligned */
-    const uint16_t *scales;     /* fp16 [n][k/128], row-major (planar), 4-byte aligned */
-    const uint8_t *zeros;       /* u8   [n][k/128], row-major, 2-byte aligned (QP_ZERO_STORED) */
+    const uint16_t *scales;     /* fp16 [n][k/group_size], row-major (planar), 4-byte aligned */
+    const uint8_t *zeros;       /* u8   [n][k/group_size], row-major, 2-byte aligned (QP_ZERO_STORED) */
     const int32_t *csr_rowptr;  /* [n+1] outlier CSR over rows of W, or NULL */
     const int32_t *csr_col;     /* [nnz] column k of each outlier, ascending within a row */
     const uint16_t *csr_val;    /* [nnz] fp16 value of each outlier */
@@ -139,7 +144,8 @@ size_t qpack_quantize_workspace_bytes(const qp_weight_desc *desc, double outlier
  *           the lower row-major index) are held out: their dense slot becomes +0 before
  *           the group range is taken, and the original values go to the CSR.
  *  codes    u8 [n][k] device (one code per byte, unpacked).
- *  scales   fp16 [n][k/128], zeros u8 [n][k/128] device.
+ *  scales   fp16 [n][k/g], zeros u8 [n][k/g] device (zeros unused, may be NULL, with
+ *           QP_ZERO_MIDPOINT); g = desc->group_size.
  *  csr_rowptr [n+1], csr_col [csr_cap], csr_val [csr_cap] device; may be NULL when
  *           outlier_frac == 0 (csr_rowptr, if given, is then filled with zeros).
  *  nnz_out  HOST pointer, receives the outlier count (also when QP_ERR_WORKSPACE is

@@ -47,15 +47,15 @@ class GpuWeight:
     """Quantized + packed weight on the device, built through the C ABI."""
 
     def __init__(self, w_fp16: np.ndarray, bits: int, outlier_frac: float = 0.0, layout: int = 1,
-                 sym: bool = False):
+                 sym: bool = False, g: int = 128):
         torch, q = gpu()
         n, k = w_fp16.shape
         dev = torch.device("cuda")
-        self.n, self.k, self.bits, self.sym = n, k, bits, sym
+        self.n, self.k, self.bits, self.sym, self.g = n, k, bits, sym, g
         w = torch.from_numpy(np.ascontiguousarray(w_fp16).view(np.int16)).to(dev)
-        d = q.desc(bits, n, k, layout, zero_mode=q.QP_ZERO_MIDPOINT if sym else q.QP_ZERO_STORED)
+        d = q.desc(bits, n, k, layout, group_size=g, zero_mode=q.QP_ZERO_MIDPOINT if sym else q.QP_ZERO_STORED)
         self.desc = d
-        G = k // 128
+        G = k // g
         self.codes = torch.empty((n, k), dtype=torch.uint8, device=dev)
         self.scales = torch.empty((n, G), dtype=torch.int16, device=dev)
         self.zeros = torch.empty((n, G), dtype=torch.uint8, device=dev)
@@ -81,7 +81,7 @@ class GpuWeight:
 
     def host(self) -> dict:
         """Device results copied back (for comparison with the oracle's own results)."""
-        zeros = (np.full((self.n, self.k // 128), 1 << (self.bits - 1), np.uint8) if self.sym
+        zeros = (np.full((self.n, self.k // self.g), 1 << (self.bits - 1), np.uint8) if self.sym
                  else self.zeros.cpu().numpy())
         return dict(codes=self.codes.cpu().numpy(), scales=self.scales.cpu().numpy().view(np.uint16),
                     zeros=zeros, rowptr=self.rowptr.cpu().numpy(),

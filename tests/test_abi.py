@@ -70,7 +70,8 @@ FAKE = 0x10000  # an aligned, never-dereferenced address: validation fails befor
     (q.desc(7, 16, 256), q.QP_ERR_INVALID_ARG),
     (q.desc(1, 16, 256), q.QP_ERR_INVALID_ARG),
     (q.desc(4, 16, 200), q.QP_ERR_INVALID_ARG),
-    (q.desc(4, 16, 256, group_size=64), q.QP_ERR_UNSUPPORTED),
+    (q.desc(4, 16, 256, group_size=256), q.QP_ERR_UNSUPPORTED),
+    (q.desc(4, 16, 256, group_size=16), q.QP_ERR_UNSUPPORTED),
     (q.desc(4, 15, 256), q.QP_ERR_INVALID_ARG),           # device layout needs n % 16
     (q.desc(4, 16, 384), q.QP_ERR_INVALID_ARG),           # device layout needs k % 256
     (q.desc(4, 0, 256), q.QP_ERR_INVALID_ARG),
@@ -154,6 +155,24 @@ def test_zero_mode_validation():
     bad = q.desc(4, 64, 1024, zero_mode=3)
     assert q.qlinear_gemv(bad, q.weight(FAKE, FAKE, FAKE), FAKE, 1024, 1, FAKE, 64, stream=0,
                           check=False) == q.QP_ERR_INVALID_ARG
+
+
+def test_group_size_validation():
+    """Groups of 32, 64 and 128 are valid descriptors (k a multiple of 128); other sizes are
+    not built; the GEMM and grouped GEMM take only 128; a GEMV batch takes one group size."""
+    for g in (32, 64, 128):
+        assert q.qp_num_groups(q.desc(2, 64, 1024, group_size=g)) == 64 * 1024 // g
+    assert q.qp_num_groups(q.desc(2, 64, 1024, group_size=256)) == 0
+    assert q.qp_num_groups(q.desc(2, 64, 1088, group_size=32)) == 0     # k not a multiple of 128
+    d32 = q.desc(2, 256, 512, group_size=32)
+    w = q.weight(FAKE, FAKE, FAKE)
+    assert q.qlinear_gemm(d32, w, FAKE, 512, 64, FAKE, 256, FAKE, 1 << 20, stream=0,
+                          check=False) == q.QP_ERR_UNSUPPORTED
+    assert q.qlinear_grouped_gemm(d32, [w], FAKE, 512, None, FAKE, 4, q.QP_EPI_NONE, FAKE, 256, stream=0,
+                                  check=False) == q.QP_ERR_UNSUPPORTED
+    p32 = q.gemv_problem(d32, w, FAKE, 512, 1, FAKE, 256)
+    p128 = q.gemv_problem(q.desc(2, 256, 512), w, FAKE, 512, 1, FAKE, 256)
+    assert q.qlinear_gemv_batch([p32, p128], stream=0, check=False) == q.QP_ERR_UNSUPPORTED
 
 
 def test_grouped_and_moe_validation():

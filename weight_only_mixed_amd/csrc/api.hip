@@ -47,7 +47,9 @@ static qp_status check_desc(const qp_weight_desc *d, bool need_device)
     if (d->n <= 0 || d->k <= 0) return fail(QP_ERR_INVALID_ARG, "n=%lld k=%lld must be > 0", (long long)d->n, (long long)d->k);
     if (d->group_size <= 0 || d->k % d->group_size != 0)
         return fail(QP_ERR_INVALID_ARG, "k=%lld not a multiple of group_size=%d", (long long)d->k, d->group_size);
-    if (d->group_size != kGroup) return fail(QP_ERR_UNSUPPORTED, "group_size=%d (only 128 is built)", d->group_size);
+    if (d->group_size != 32 && d->group_size != 64 && d->group_size != 128)
+        return fail(QP_ERR_UNSUPPORTED, "group_size=%d (32, 64 and 128 are built)", d->group_size);
+    if (d->k % 128 != 0) return fail(QP_ERR_UNSUPPORTED, "k=%lld must be a multiple of 128", (long long)d->k);
     if (d->n > (1LL << 31) - 1 || d->n * d->k > (1LL << 40))
         return fail(QP_ERR_INVALID_ARG, "matrix too large");
     if (d->layout == QP_LAYOUT_DEVICE && (d->n % kTileN != 0 || d->k % kTileK != 0))
@@ -150,7 +152,7 @@ qp_status qpack_quantize(const qp_weight_desc *d, const uint16_t *w, int64_t ldw
     *nnz_out = kout;
     QuantWs ws{};
     if (kout > 0) ws = quant_ws_carve(workspace, d->n);
-    return device(launch_quantize(d->bits, d->zero_mode == QP_ZERO_MIDPOINT, w, ldw, d->n, d->k, kout, codes, scales,
+    return device(launch_quantize(d->bits, d->zero_mode == QP_ZERO_MIDPOINT, w, ldw, d->n, d->k, d->group_size, kout, codes, scales,
                                   zeros, csr_rowptr, csr_col, csr_val, ws, S(stream)),
                   "qpack_quantize");
 }
@@ -198,6 +200,7 @@ static qp_status gemv_problem(const qp_weight_desc *d, const qp_weight *w, const
     *p = GemvProblem{};
     p->w = {(const uint8_t *)w->packed, w->scales, w->zeros};
     p->zmid = zero_pair(d);
+    p->gs = d->group_size;
     if (w->nnz > 0) {
         p->rowptr = w->csr_rowptr;
         p->col = w->csr_col;
@@ -235,6 +238,7 @@ qp_status qlinear_gemv_batch(const qp_gemv_problem *problems, int32_t count, voi
         const qp_gemv_problem &q = problems[i];
         qp_status st = gemv_problem(&q.desc, &q.w, q.x, q.ldx, q.m, q.y, q.ldy, &b.p[i]);
         if (st != QP_OK) return st;
+        if (b.p[i].gs != b.p[0].gs) return fail(QP_ERR_UNSUPPORTED, "one group size per batch");
         b.p[i].block0 = blocks;
         blocks += q.desc.n / 16;
         if (q.m > m_max) m_max = (int)q.m;
@@ -254,6 +258,7 @@ qp_status qlinear_gemm(const qp_weight_desc *d, const qp_weight *w, const uint16
 {
     qp_status st = check_desc(d, true);
     if (st != QP_OK) return st;
+    if (d->group_size != kGroup) return fail(QP_ERR_UNSUPPORTED, "the GEMM is built for groups of 128");
     if ((st = check_weight(d, w, true)) != QP_OK) return st;
     if ((st = check_xy(d, x, ldx, m, y, ldy, d->n, 4)) != QP_OK) return st;
     if (m > (1LL << 24)) return fail(QP_ERR_INVALID_ARG, "m too large");
@@ -292,6 +297,7 @@ qp_status qlinear_grouped_gemm(const qp_weight_desc *d, const qp_weight *experts
 {
     qp_status st = check_desc(d, true);
     if (st != QP_OK) return st;
+    if (d->group_size != kGroup) return fail(QP_ERR_UNSUPPORTED, "the grouped GEMM is built for groups of 128");
     if (!experts) return fail(QP_ERR_INVALID_ARG, "experts NULL");
     if (n_experts < 1 || n_experts > kMaxExperts) return fail(QP_ERR_INVALID_ARG, "n_experts=%d not in 1..64", n_experts);
     for (int e = 0; e < n_experts; ++e)

@@ -17,23 +17,26 @@
 
 namespace qp {
 
-// tot += s0 * (A[0..3] . X[0..3]) + s1 * (A[4..7] . X[4..7]), groups kept apart.
-__device__ __forceinline__ void mma_tile(const h8 *A, const h8 *X, const uint32_t *sc, f4 &tot)
+// tot += sum over the tile's NG groups c of s_c * (A[j] . X[j] for the 8/NG blocks j of c),
+// groups kept apart and added in group order.  sc[i][c / 2] holds the fp16 scales of groups
+// c and c+1 (low, high half) for accumulator row 4t + i.
+template <int NG>
+__device__ __forceinline__ void mma_tile(const h8 *A, const h8 *X, const uint32_t (&sc)[4][NG / 2], f4 &tot)
 {
+    constexpr int JB = 8 / NG;  // blocks per group
     const f4 z = {0.f, 0.f, 0.f, 0.f};
-    f4 a0 = mfma16(A[0], X[0], z);
-    f4 a1 = mfma16(A[4], X[4], z);
-    a0 = mfma16(A[1], X[1], a0);
-    a1 = mfma16(A[5], X[5], a1);
-    a0 = mfma16(A[2], X[2], a0);
-    a1 = mfma16(A[6], X[6], a1);
-    a0 = mfma16(A[3], X[3], a0);
-    a1 = mfma16(A[7], X[7], a1);
+    f4 acc[NG];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        tot[i] = __builtin_fmaf(lo_h(sc[i]), a0[i], tot[i]);
-        tot[i] = __builtin_fmaf(hi_h(sc[i]), a1[i], tot[i]);
-    }
+    for (int c = 0; c < NG; ++c) acc[c] = mfma16(A[c * JB], X[c * JB], z);
+#pragma unroll
+    for (int jj = 1; jj < JB; ++jj)
+#pragma unroll
+        for (int c = 0; c < NG; ++c) acc[c] = mfma16(A[c * JB + jj], X[c * JB + jj], acc[c]);
+#pragma unroll
+    for (int c = 0; c < NG; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            tot[i] = __builtin_fmaf((c & 1) ? hi_h(sc[i][c / 2]) : lo_h(sc[i][c / 2]), acc[c][i], tot[i]);
 }
 
 // ---- decode GEMV: one workgroup per 16-row block, NW waves take its k-tiles round-robin --
@@ -55,14 +58,22 @@ struct GemvBufs {
     int64_t G;
 };
 
-template <int B, int MX>
+// One ring slot: a k-tile's packed codes, activation rows, and the scales and zero points of
+// its NG = 256 / GS groups for the block's 16 rows (lane l < 16 stages row l; lanes >= 16 read
+// zeros).  Scales: NG = 2 one 4-byte DMA, NG = 4 two (region A groups 0-1, B groups 2-3),
+// NG = 8 one 16-byte DMA.  Zero points: NG = 2 the aligned 4-byte word holding the pair,
+// NG = 4 one 4-byte DMA, NG = 8 two (groups 0-3, 4-7).
+template <int B, int MX, int GS>
 struct RingSlot {
+    static constexpr int NG = kTileK / GS;
+    static constexpr int kScOps = NG == 4 ? 2 : 1, kZrOps = NG == 8 ? 2 : 1;
     static constexpr int kCodes = 512 * B;           // packed tile
     static constexpr int kX = kCodes;                 // activation rows, 512 B each, 2 per DMA
-    static constexpr int kSc = kX + 1024 * MX;        // 64 lanes x 4 B (rows >= 16 read zeros)
-    static constexpr int kZr = kSc + 256;             // 64 lanes x 4 B
-    static constexpr int kBytes = kZr + 256;
-    static constexpr int kLoads = B / 2 + 2 * (B & 1) + MX + 2;  // DMA instructions per tile
+    static constexpr int kSc = kX + 1024 * MX;
+    static constexpr int kZr = kSc + (NG == 8 ? 1024 : 256 * kScOps);
+    static constexpr int kBytes = kZr + 256 * kZrOps;
+    static constexpr int kLoads = B / 2 + 2 * (B & 1) + MX + kScOps + kZrOps;  // DMA instructions per tile
+    static_assert(NG == 2 || NG == 4 || NG == 8, "groups of 128, 64 or 32");
 };
 
 __device__ __forceinline__ void dma16(rsrc_t r, uint8_t *lds, uint32_t voff)
@@ -74,10 +85,11 @@ __device__ __forceinline__ void dma4(rsrc_t r, uint8_t *lds, uint32_t voff)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, voff, 0, 0, 0);
 }
 
-template <int B, int MX>
+template <int B, int MX, int GS>
 __device__ __forceinline__ void ring_issue(const GemvBufs &bf, int64_t kt, int lane, int64_t ldx, uint8_t *slot)
 {
-    using S = RingSlot<B, MX>;
+    using S = RingSlot<B, MX, GS>;
+    constexpr int NG = S::NG;
     const uint32_t tw = (uint32_t)(kt * (512 * B));
 #pragma unroll
     for (int sl = 0; sl < B / 2; ++sl) dma16(bf.w, slot + 1024 * sl, tw + 1024 * sl + 16 * lane);
@@ -91,8 +103,19 @@ __device__ __forceinline__ void ring_issue(const GemvBufs &bf, int64_t kt, int l
         const uint32_t row = 2 * q + (lane >> 5);
         dma16(bf.x, slot + S::kX + 1024 * q, (uint32_t)(row * ldx * 2) + xk + 16 * (lane & 31));
     }
-    dma4(bf.sc, slot + S::kSc, (uint32_t)((lane * bf.G + 2 * kt) * 2));
-    dma4(bf.zr, slot + S::kZr, (uint32_t)((lane * bf.G + 2 * kt) & ~(int64_t)3));
+    const uint32_t g0 = (uint32_t)(lane * bf.G + NG * kt);  // this lane's row, the tile's first group
+    if constexpr (NG == 2) {
+        dma4(bf.sc, slot + S::kSc, 2 * g0);
+        dma4(bf.zr, slot + S::kZr, g0 & ~3u);
+    } else if constexpr (NG == 4) {
+        dma4(bf.sc, slot + S::kSc, 2 * g0);
+        dma4(bf.sc, slot + S::kSc + 256, 2 * g0 + 4);
+        dma4(bf.zr, slot + S::kZr, g0);
+    } else {
+        dma16(bf.sc, slot + S::kSc, 2 * g0);
+        dma4(bf.zr, slot + S::kZr, g0);
+        dma4(bf.zr, slot + S::kZr + 256, g0 + 4);
+    }
 }
 
 template <int N>
@@ -104,15 +127,16 @@ __device__ __forceinline__ void wait_vm()
 
 // One 16-row block of problem p on this workgroup; slot0/slot1 are this wave's two ring slots
 // (separate LDS arrays), `red` the workgroup's reduction buffer.
-template <int B, int NW, int D, int MX>
+template <int B, int NW, int D, int MX, int GS>
 __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uint8_t *slot0, uint8_t *slot1,
                                            f4 (*red)[64])
 {
     static_assert(D == 2, "two ring slots");
-    using S = RingSlot<B, MX>;
+    using S = RingSlot<B, MX, GS>;
+    constexpr int NG = S::NG;
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t = lane >> 4, r = lane & 15;
-    const int64_t KT = a.k / kTileK, G = a.k / kGroup;
+    const int64_t KT = a.k / kTileK, G = a.k / GS;
 
     GemvBufs bf;
     bf.G = G;
@@ -122,7 +146,7 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
     bf.x = make_rsrc(a.x, a.m * a.ldx * 2);  // rows >= m read as zeros
 
     const int64_t nt = KT > wv ? (KT - wv + NW - 1) / NW : 0;  // tiles of this wave
-    ring_issue<B, MX>(bf, wv, lane, a.ldx, slot0);
+    ring_issue<B, MX, GS>(bf, wv, lane, a.ldx, slot0);
 
     // Activation fragments: lanes of rows >= m keep zeros and never read LDS.
     const bool act = r < a.m;
@@ -141,7 +165,7 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
         const int64_t i = i0 + sd;
         if (i >= nt) break;  // uniform
         const int64_t kt = wv + i * NW;
-        ring_issue<B, MX>(bf, kt + NW, lane, a.ldx, sd == 0 ? slot1 : slot0);
+        ring_issue<B, MX, GS>(bf, kt + NW, lane, a.ldx, sd == 0 ? slot1 : slot0);
         wait_vm<S::kLoads>();
         const uint8_t *slot = sd == 0 ? slot0 : slot1;
         uint32_t d[2 * B];
@@ -162,16 +186,41 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
 #pragma unroll
             for (int j = 0; j < 8; ++j) X[j] = *(const h8 *)(xb + 2 * (128 * (j >> 2) + 32 * (j & 3)));
         }
-        const u4 scv = *(const u4 *)(slot + S::kSc + 16 * t);
-        const uint32_t sc[4] = {scv[0], scv[1], scv[2], scv[3]};
-        const uint32_t zpar = (uint32_t)((r * G + 2 * kt) & 3);
-        const uint32_t zz = a.zmid ? a.zmid : *(const uint16_t *)(slot + S::kZr + 4 * r + zpar);
-        GroupConst<B> g0, g1;
-        g0.set(zz & 0xFF);
-        g1.set((zz >> 8) & 0xFF);
+        // scales of rows 4t..4t+3 (two groups per word) and zero points of row r
+        uint32_t sc[4][NG / 2];
+        uint32_t zw[NG == 8 ? 2 : 1];
+        if constexpr (NG == 2) {
+            const u4 v = *(const u4 *)(slot + S::kSc + 16 * t);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[i][0] = v[i];
+            const uint32_t zpar = (uint32_t)((r * G + 2 * kt) & 3);
+            zw[0] = *(const uint16_t *)(slot + S::kZr + 4 * r + zpar);
+        } else if constexpr (NG == 4) {
+            const u4 v0 = *(const u4 *)(slot + S::kSc + 16 * t), v1 = *(const u4 *)(slot + S::kSc + 256 + 16 * t);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sc[i][0] = v0[i];
+                sc[i][1] = v1[i];
+            }
+            zw[0] = *(const uint32_t *)(slot + S::kZr + 4 * r);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u4 v = *(const u4 *)(slot + S::kSc + 16 * (4 * t + i));
+                sc[i][0] = v[0];
+                sc[i][1] = v[1];
+                sc[i][2] = v[2];
+                sc[i][3] = v[3];
+            }
+            zw[0] = *(const uint32_t *)(slot + S::kZr + 4 * r);
+            zw[1] = *(const uint32_t *)(slot + S::kZr + 256 + 4 * r);
+        }
+        GroupConst<B> gc[NG];
+#pragma unroll
+        for (int c = 0; c < NG; ++c) gc[c].set(a.zmid ? (a.zmid & 0xFF) : (zw[c / 4] >> (8 * (c % 4))) & 0xFF);
         h8 A[8];
-        unpack_chunk<B>(d, g0, g1, A);
-        mma_tile(A, X, sc, tot);
+        unpack_chunk_groups<B, NG>(d, gc, A);
+        mma_tile<NG>(A, X, sc, tot);
     }
     wait_vm<0>();  // drain the tiles issued past the end before the workgroup's LDS is released
 
@@ -195,23 +244,23 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
 }
 
 // One problem, one workgroup per 16-row block.
-template <int B, int NW, int D, int MX>
+template <int B, int NW, int D, int MX, int GS>
 __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvProblem a)
 {
-    constexpr int pitch = RingSlot<B, MX>::kBytes;
+    constexpr int pitch = RingSlot<B, MX, GS>::kBytes;
     __shared__ __attribute__((aligned(16))) uint8_t ring0[NW][pitch];
     __shared__ __attribute__((aligned(16))) uint8_t ring1[NW][pitch];
     __shared__ f4 red[NW][64];
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    gemv_block<B, NW, D, MX>(a, blockIdx.x, &ring0[wv][0], &ring1[wv][0], red);
+    gemv_block<B, NW, D, MX, GS>(a, blockIdx.x, &ring0[wv][0], &ring1[wv][0], red);
 }
 
-// Independent problems (mixed bit widths) in one launch: workgroup b serves problem p with
-// block0 <= b < block0 + n/16.  The ring slots are sized for 6-bit tiles.
-template <int NW, int D, int MX>
+// Independent problems (mixed bit widths, one group size) in one launch: workgroup b serves
+// problem p with block0 <= b < block0 + n/16.  The ring slots are sized for 6-bit tiles.
+template <int NW, int D, int MX, int GS>
 __global__ __launch_bounds__(NW * 64) void gemv_batch_kernel(GemvBatch bt)
 {
-    constexpr int pitch = RingSlot<6, MX>::kBytes;
+    constexpr int pitch = RingSlot<6, MX, GS>::kBytes;
     __shared__ __attribute__((aligned(16))) uint8_t ring0[NW][pitch];
     __shared__ __attribute__((aligned(16))) uint8_t ring1[NW][pitch];
     __shared__ f4 red[NW][64];
@@ -225,15 +274,15 @@ __global__ __launch_bounds__(NW * 64) void gemv_batch_kernel(GemvBatch bt)
     const int64_t rb = b - a.block0;
     uint8_t *s0 = &ring0[wv][0], *s1 = &ring1[wv][0];
     switch (a.bits) {
-    case 2: gemv_block<2, NW, D, MX>(a, rb, s0, s1, red); break;
-    case 3: gemv_block<3, NW, D, MX>(a, rb, s0, s1, red); break;
-    case 4: gemv_block<4, NW, D, MX>(a, rb, s0, s1, red); break;
-    case 5: gemv_block<5, NW, D, MX>(a, rb, s0, s1, red); break;
-    default: gemv_block<6, NW, D, MX>(a, rb, s0, s1, red); break;
+    case 2: gemv_block<2, NW, D, MX, GS>(a, rb, s0, s1, red); break;
+    case 3: gemv_block<3, NW, D, MX, GS>(a, rb, s0, s1, red); break;
+    case 4: gemv_block<4, NW, D, MX, GS>(a, rb, s0, s1, red); break;
+    case 5: gemv_block<5, NW, D, MX, GS>(a, rb, s0, s1, red); break;
+    default: gemv_block<6, NW, D, MX, GS>(a, rb, s0, s1, red); break;
     }
 }
 
-template <int B, int MX>
+template <int B, int MX, int GS>
 static hipError_t gemv_mx(const GemvProblem &a, hipStream_t st)
 {
     // Wide matrices have row blocks enough to fill the GPU with 4-wave workgroups (more of
@@ -241,23 +290,30 @@ static hipError_t gemv_mx(const GemvProblem &a, hipStream_t st)
     // (Eight waves with an 8-row-pair activation ring would exceed the 160 KB of LDS.)
     const int64_t blocks = a.n / kTileN;
     if constexpr (MX == 8) {
-        hipLaunchKernelGGL((gemv_kernel<B, 4, 2, MX>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((gemv_kernel<B, 4, 2, MX, GS>), dim3((unsigned)blocks), dim3(256), 0, st, a);
     } else {
         if (blocks >= 512)
-            hipLaunchKernelGGL((gemv_kernel<B, 4, 2, MX>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+            hipLaunchKernelGGL((gemv_kernel<B, 4, 2, MX, GS>), dim3((unsigned)blocks), dim3(256), 0, st, a);
         else
-            hipLaunchKernelGGL((gemv_kernel<B, 8, 2, MX>), dim3((unsigned)blocks), dim3(512), 0, st, a);
+            hipLaunchKernelGGL((gemv_kernel<B, 8, 2, MX, GS>), dim3((unsigned)blocks), dim3(512), 0, st, a);
     }
     return hipGetLastError();
 }
 
+template <int B, int GS>
+static hipError_t gemv_bits_gs(const GemvProblem &a, hipStream_t st)
+{
+    if (a.m <= 2) return gemv_mx<B, 1, GS>(a, st);
+    if (a.m <= 4) return gemv_mx<B, 2, GS>(a, st);
+    if (a.m <= 8) return gemv_mx<B, 4, GS>(a, st);
+    return gemv_mx<B, 8, GS>(a, st);
+}
 template <int B>
 static hipError_t gemv_bits(const GemvProblem &a, hipStream_t st)
 {
-    if (a.m <= 2) return gemv_mx<B, 1>(a, st);
-    if (a.m <= 4) return gemv_mx<B, 2>(a, st);
-    if (a.m <= 8) return gemv_mx<B, 4>(a, st);
-    return gemv_mx<B, 8>(a, st);
+    if (a.gs == 32) return gemv_bits_gs<B, 32>(a, st);
+    if (a.gs == 64) return gemv_bits_gs<B, 64>(a, st);
+    return gemv_bits_gs<B, 128>(a, st);
 }
 
 hipError_t launch_gemv(const GemvProblem &a, hipStream_t st)
@@ -272,26 +328,34 @@ hipError_t launch_gemv(const GemvProblem &a, hipStream_t st)
     return hipErrorInvalidValue;
 }
 
-template <int MX>
+template <int MX, int GS>
 static hipError_t gemv_batch_mx(const GemvBatch &b, int64_t blocks, hipStream_t st)
 {
     if constexpr (MX >= 4) {
-        hipLaunchKernelGGL((gemv_batch_kernel<4, 2, MX>), dim3((unsigned)blocks), dim3(256), 0, st, b);
+        hipLaunchKernelGGL((gemv_batch_kernel<4, 2, MX, GS>), dim3((unsigned)blocks), dim3(256), 0, st, b);
     } else {
         if (blocks >= 512)
-            hipLaunchKernelGGL((gemv_batch_kernel<4, 2, MX>), dim3((unsigned)blocks), dim3(256), 0, st, b);
+            hipLaunchKernelGGL((gemv_batch_kernel<4, 2, MX, GS>), dim3((unsigned)blocks), dim3(256), 0, st, b);
         else
-            hipLaunchKernelGGL((gemv_batch_kernel<8, 2, MX>), dim3((unsigned)blocks), dim3(512), 0, st, b);
+            hipLaunchKernelGGL((gemv_batch_kernel<8, 2, MX, GS>), dim3((unsigned)blocks), dim3(512), 0, st, b);
     }
     return hipGetLastError();
 }
 
+template <int GS>
+static hipError_t gemv_batch_gs(const GemvBatch &b, int64_t blocks, int m_max, hipStream_t st)
+{
+    if (m_max <= 2) return gemv_batch_mx<1, GS>(b, blocks, st);
+    if (m_max <= 4) return gemv_batch_mx<2, GS>(b, blocks, st);
+    if (m_max <= 8) return gemv_batch_mx<4, GS>(b, blocks, st);
+    return gemv_batch_mx<8, GS>(b, blocks, st);
+}
+
 hipError_t launch_gemv_batch(const GemvBatch &b, int64_t blocks, int m_max, hipStream_t st)
 {
-    if (m_max <= 2) return gemv_batch_mx<1>(b, blocks, st);
-    if (m_max <= 4) return gemv_batch_mx<2>(b, blocks, st);
-    if (m_max <= 8) return gemv_batch_mx<4>(b, blocks, st);
-    return gemv_batch_mx<8>(b, blocks, st);
+    if (b.p[0].gs == 32) return gemv_batch_gs<32>(b, blocks, m_max, st);
+    if (b.p[0].gs == 64) return gemv_batch_gs<64>(b, blocks, m_max, st);
+    return gemv_batch_gs<128>(b, blocks, m_max, st);
 }
 
 }  // namespace qp

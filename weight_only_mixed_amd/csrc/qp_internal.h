@@ -33,7 +33,7 @@ struct QuantWs {  // carve-up of the quantize workspace
 };
 size_t quant_ws_bytes(int64_t n);
 QuantWs quant_ws_carve(void *ws, int64_t n);
-hipError_t launch_quantize(int bits, bool sym, const uint16_t *w, int64_t ldw, int64_t n, int64_t k,
+hipError_t launch_quantize(int bits, bool sym, const uint16_t *w, int64_t ldw, int64_t n, int64_t k, int gs,
                            int64_t kout, uint8_t *codes, uint16_t *scales, uint8_t *zeros,
                            int32_t *rowptr, int32_t *col, uint16_t *val, const QuantWs &ws,
                            hipStream_t st);
@@ -62,6 +62,8 @@ struct GemvProblem {
     int64_t ldy;
     int32_t bits;
     uint32_t zmid;   // 0: stored zero points; else the implied pair (2^(b-1) in both bytes)
+    int32_t gs;      // group size: 32, 64 or 128
+    int32_t pad;
     int64_t block0;  // batch: first workgroup of this problem
 };
 struct GemvBatch {

@@ -216,16 +216,20 @@ __device__ int block_scan_excl_256(int v, int *lds)
     return base + x - v;
 }
 
-// Quantize one symmetric group of 128 held in a wave (two values per lane): range [-m, m]
-// with m = max |w|, scale fp16((m + m) / qmax), codes around the implied midpoint 2^(b-1).
+constexpr int kChunk = 128;  // weights of a row one wave quantizes at a time (groups of 32, 64 or 128)
+
+// Quantize the symmetric groups of `gs` values (32, 64 or 128) in a wave's 128 values (two
+// per lane, lanes [j gs/2, (j+1) gs/2) hold group j): range [-m, m] with m = max |w|, scale
+// fp16((m + m) / qmax), codes around the implied midpoint 2^(b-1).  scale_out points at the
+// chunk's first group.
 template <int BITS>
-__device__ __forceinline__ void quantize_group_wave_sym(float v0, float v1, int lane, uint8_t *codes_out,
+__device__ __forceinline__ void quantize_group_wave_sym(float v0, float v1, int lane, int gs, uint8_t *codes_out,
                                                         uint16_t *scale_out)
 {
     constexpr int qmax = (1 << BITS) - 1, z = 1 << (BITS - 1);
     float m = __builtin_fabsf(v0);
     if (__builtin_fabsf(v1) > m) m = __builtin_fabsf(v1);
-    for (int off = 32; off > 0; off >>= 1) {
+    for (int off = gs / 4; off > 0; off >>= 1) {
         const float om = __shfl_xor(m, off);
         if (om > m) m = om;
     }
@@ -245,12 +249,14 @@ __device__ __forceinline__ void quantize_group_wave_sym(float v0, float v1, int 
         q1 = b < 0 ? 0 : (b > qmax ? qmax : b);
     }
     *(uint16_t *)(codes_out + 2 * lane) = (uint16_t)(q0 | (q1 << 8));
-    if (lane == 0) *scale_out = sbits;
+    if (lane % (gs / 2) == 0) scale_out[lane / (gs / 2)] = sbits;
 }
 
-// Quantize one group of 128 held in a wave: two values per lane.
+// Quantize the groups of `gs` values (32, 64 or 128) in a wave's 128 values: two values per
+// lane, lanes [j gs/2, (j+1) gs/2) hold group j; scale_out / zero_out point at the chunk's
+// first group.
 template <int BITS>
-__device__ __forceinline__ void quantize_group_wave(float v0, float v1, int lane,
+__device__ __forceinline__ void quantize_group_wave(float v0, float v1, int lane, int gs,
                                                     uint8_t *codes_out, uint16_t *scale_out,
                                                     uint8_t *zero_out)
 {
@@ -260,7 +266,7 @@ __device__ __forceinline__ void quantize_group_wave(float v0, float v1, int lane
     if (v0 > hi) hi = v0;
     if (v1 < lo) lo = v1;
     if (v1 > hi) hi = v1;
-    for (int off = 32; off > 0; off >>= 1) {
+    for (int off = gs / 4; off > 0; off >>= 1) {
         const float olo = __shfl_xor(lo, off), ohi = __shfl_xor(hi, off);
         if (olo < lo) lo = olo;
         if (ohi > hi) hi = ohi;
@@ -286,9 +292,9 @@ __device__ __forceinline__ void quantize_group_wave(float v0, float v1, int lane
         q1 = b < 0 ? 0 : (b > qmax ? qmax : b);
     }
     *(uint16_t *)(codes_out + 2 * lane) = (uint16_t)(q0 | (q1 << 8));
-    if (lane == 0) {
-        *scale_out = sbits;
-        *zero_out = (uint8_t)zp;
+    if (lane % (gs / 2) == 0) {
+        scale_out[lane / (gs / 2)] = sbits;
+        zero_out[lane / (gs / 2)] = (uint8_t)zp;
     }
 }
 
@@ -304,14 +310,14 @@ template <int BITS, bool OUTL, bool SYM>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(
     const uint16_t *w, int64_t ldw, int64_t k, const uint32_t *ctl, const int32_t *eq_base,
     const int32_t *rowptr, uint8_t *codes, uint16_t *scales, uint8_t *zeros, int32_t *col,
-    uint16_t *val)
+    uint16_t *val, int gs)
 {
     extern __shared__ uint8_t held[];  // k bytes (OUTL only)
     __shared__ int scan_lds[4];
     const int64_t r = blockIdx.x;
     const uint16_t *row = w + r * ldw;
     const int t = threadIdx.x;
-    const int64_t G = k / kGroup;
+    const int64_t G = k / gs, per = kChunk / gs;  // groups per row, per 128-value chunk
 
     if constexpr (OUTL) {
         const uint32_t T = ctl[0];
@@ -348,8 +354,8 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
     }
 
     const int lane = t & 63, wv = t >> 6;
-    for (int64_t g = wv; g < G; g += 4) {
-        const int64_t c = g * kGroup + 2 * lane;
+    for (int64_t ch = wv; ch < k / kChunk; ch += 4) {
+        const int64_t c = ch * kChunk + 2 * lane;
         const uint32_t pair = *(const uint32_t *)(row + c);
         float v0 = half_bits_to_float(pair & 0xFFFF), v1 = half_bits_to_float(pair >> 16);
         if constexpr (OUTL) {
@@ -357,15 +363,15 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
             if (held[c + 1]) v1 = 0.0f;
         }
         if constexpr (SYM)
-            quantize_group_wave_sym<BITS>(v0, v1, lane, codes + r * k + g * kGroup, scales + r * G + g);
+            quantize_group_wave_sym<BITS>(v0, v1, lane, gs, codes + r * k + ch * kChunk, scales + r * G + ch * per);
         else
-            quantize_group_wave<BITS>(v0, v1, lane, codes + r * k + g * kGroup, scales + r * G + g,
-                                      zeros + r * G + g);
+            quantize_group_wave<BITS>(v0, v1, lane, gs, codes + r * k + ch * kChunk, scales + r * G + ch * per,
+                                      zeros + r * G + ch * per);
     }
 }
 
 template <int BITS, bool SYM>
-static hipError_t quantize_bits(const uint16_t *w, int64_t ldw, int64_t n, int64_t k,
+static hipError_t quantize_bits(const uint16_t *w, int64_t ldw, int64_t n, int64_t k, int gs,
                                 int64_t kout, uint8_t *codes, uint16_t *scales, uint8_t *zeros,
                                 int32_t *rowptr, int32_t *col, uint16_t *val, const QuantWs &ws,
                                 hipStream_t st)
@@ -381,7 +387,7 @@ static hipError_t quantize_bits(const uint16_t *w, int64_t ldw, int64_t n, int64
         hipLaunchKernelGGL(rowscan_kernel, dim3(1), dim3(1024), 0, st, n, ws.ctl, ws.gt_cnt,
                            ws.eq_cnt, ws.eq_base, rowptr);
         hipLaunchKernelGGL((quantize_rows_kernel<BITS, true, SYM>), dim3(n), dim3(256), (size_t)k, st,
-                           w, ldw, k, ws.ctl, ws.eq_base, rowptr, codes, scales, zeros, col, val);
+                           w, ldw, k, ws.ctl, ws.eq_base, rowptr, codes, scales, zeros, col, val, gs);
     } else {
         if (rowptr)
             hipLaunchKernelGGL(rowscan_kernel, dim3(1), dim3(1024), 0, st, n,
@@ -390,34 +396,34 @@ static hipError_t quantize_bits(const uint16_t *w, int64_t ldw, int64_t n, int64
         hipLaunchKernelGGL((quantize_rows_kernel<BITS, false, SYM>), dim3(n), dim3(256), 0, st, w, ldw,
                            k, (const uint32_t *)nullptr, (const int32_t *)nullptr,
                            (const int32_t *)nullptr, codes, scales, zeros, (int32_t *)nullptr,
-                           (uint16_t *)nullptr);
+                           (uint16_t *)nullptr, gs);
     }
     return hipGetLastError();
 }
 
 template <bool SYM>
-static hipError_t quantize_mode(int bits, const uint16_t *w, int64_t ldw, int64_t n, int64_t k,
+static hipError_t quantize_mode(int bits, const uint16_t *w, int64_t ldw, int64_t n, int64_t k, int gs,
                                 int64_t kout, uint8_t *codes, uint16_t *scales, uint8_t *zeros,
                                 int32_t *rowptr, int32_t *col, uint16_t *val, const QuantWs &ws,
                                 hipStream_t st)
 {
     switch (bits) {
-    case 2: return quantize_bits<2, SYM>(w, ldw, n, k, kout, codes, scales, zeros, rowptr, col, val, ws, st);
-    case 3: return quantize_bits<3, SYM>(w, ldw, n, k, kout, codes, scales, zeros, rowptr, col, val, ws, st);
-    case 4: return quantize_bits<4, SYM>(w, ldw, n, k, kout, codes, scales, zeros, rowptr, col, val, ws, st);
-    case 5: return quantize_bits<5, SYM>(w, ldw, n, k, kout, codes, scales, zeros, rowptr, col, val, ws, st);
-    case 6: return quantize_bits<6, SYM>(w, ldw, n, k, kout, codes, scales, zeros, rowptr, col, val, ws, st);
+    case 2: return quantize_bits<2, SYM>(w, ldw, n, k, gs, kout, codes, scales, zeros, rowptr, col, val, ws, st);
+    case 3: return quantize_bits<3, SYM>(w, ldw, n, k, gs, kout, codes, scales, zeros, rowptr, col, val, ws, st);
+    case 4: return quantize_bits<4, SYM>(w, ldw, n, k, gs, kout, codes, scales, zeros, rowptr, col, val, ws, st);
+    case 5: return quantize_bits<5, SYM>(w, ldw, n, k, gs, kout, codes, scales, zeros, rowptr, col, val, ws, st);
+    case 6: return quantize_bits<6, SYM>(w, ldw, n, k, gs, kout, codes, scales, zeros, rowptr, col, val, ws, st);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_quantize(int bits, bool sym, const uint16_t *w, int64_t ldw, int64_t n, int64_t k,
+hipError_t launch_quantize(int bits, bool sym, const uint16_t *w, int64_t ldw, int64_t n, int64_t k, int gs,
                            int64_t kout, uint8_t *codes, uint16_t *scales, uint8_t *zeros,
                            int32_t *rowptr, int32_t *col, uint16_t *val, const QuantWs &ws,
                            hipStream_t st)
 {
-    if (sym) return quantize_mode<true>(bits, w, ldw, n, k, kout, codes, scales, zeros, rowptr, col, val, ws, st);
-    return quantize_mode<false>(bits, w, ldw, n, k, kout, codes, scales, zeros, rowptr, col, val, ws, st);
+    if (sym) return quantize_mode<true>(bits, w, ldw, n, k, gs, kout, codes, scales, zeros, rowptr, col, val, ws, st);
+    return quantize_mode<false>(bits, w, ldw, n, k, gs, kout, codes, scales, zeros, rowptr, col, val, ws, st);
 }
 
 }  // namespace qp

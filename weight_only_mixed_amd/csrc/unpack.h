@@ -160,6 +160,21 @@ __device__ __forceinline__ void load_chunk(const uint8_t *tile, int lane, uint32
     }
 }
 
+// Unpack all eight blocks of a chunk with NG groups per k-tile: block j belongs to group
+// j * NG / 8 (NG = 2: blocks 0-3 and 4-7; NG = 8: one group per block).
+template <int B, int NG>
+__device__ __forceinline__ void unpack_chunk_groups(const uint32_t *d, const GroupConst<B> (&gc)[NG], h8 *a)
+{
+    a[0] = BlockUnpack<B, 0>::run(d, gc[0 * NG / 8]);
+    a[1] = BlockUnpack<B, 1>::run(d, gc[1 * NG / 8]);
+    a[2] = BlockUnpack<B, 2>::run(d, gc[2 * NG / 8]);
+    a[3] = BlockUnpack<B, 3>::run(d, gc[3 * NG / 8]);
+    a[4] = BlockUnpack<B, 4>::run(d, gc[4 * NG / 8]);
+    a[5] = BlockUnpack<B, 5>::run(d, gc[5 * NG / 8]);
+    a[6] = BlockUnpack<B, 6>::run(d, gc[6 * NG / 8]);
+    a[7] = BlockUnpack<B, 7>::run(d, gc[7 * NG / 8]);
+}
+
 // Unpack all eight blocks of a chunk; blocks 0..3 use group 0's zero point, 4..7 group 1's.
 template <int B>
 __device__ __forceinline__ void unpack_chunk(const uint32_t *d, const GroupConst<B> &g0,
