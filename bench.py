@@ -12,7 +12,8 @@ The roofline object covers the kernel with the largest share of the step, timed 
 HIP events around a graph of back-to-back launches on its own stream.  A secondary line
 measures the prefill dequant-GEMM (M=512, K=8192, N=28672, 4-bit + 0.1% outliers) in
 TFLOP/s.  Further lines: the 4-bit 4096 x 4096 GEMV at M=1, the same layer at 2 and 3 bits
-with symmetric groups (no zero points), a Llama-7B-shaped decode stack and a 16-expert FFN.
+with symmetric groups (no zero points) and with groups of 32 and 64, a Llama-7B-shaped decode
+stack and a 16-expert FFN.
 cpu_baseline times the CPU oracle on the same step.
 """
 from __future__ import annotations
@@ -37,14 +38,14 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def quantize_pack(q, torch, w: np.ndarray, bits: int, frac: float = 0.0, sym: bool = False):
+def quantize_pack(q, torch, w: np.ndarray, bits: int, frac: float = 0.0, sym: bool = False, g: int = 128):
     n, k = w.shape
     dev = torch.device("cuda")
-    d = q.desc(bits, n, k, zero_mode=q.QP_ZERO_MIDPOINT if sym else q.QP_ZERO_STORED)
+    d = q.desc(bits, n, k, group_size=g, zero_mode=q.QP_ZERO_MIDPOINT if sym else q.QP_ZERO_STORED)
     wd = torch.from_numpy(np.ascontiguousarray(w).view(np.int16)).to(dev)
     codes = torch.empty((n, k), dtype=torch.uint8, device=dev)
-    scales = torch.empty((n, k // 128), dtype=torch.int16, device=dev)
-    zeros = None if sym else torch.empty((n, k // 128), dtype=torch.uint8, device=dev)
+    scales = torch.empty((n, k // g), dtype=torch.int16, device=dev)
+    zeros = None if sym else torch.empty((n, k // g), dtype=torch.uint8, device=dev)
     kout = q.qp_outlier_count(n, k, frac)
     rowptr = torch.zeros(n + 1, dtype=torch.int32, device=dev)
     col = torch.empty(max(kout, 1), dtype=torch.int32, device=dev)
@@ -59,12 +60,12 @@ def quantize_pack(q, torch, w: np.ndarray, bits: int, frac: float = 0.0, sym: bo
     return d, dict(packed=packed, scales=scales, zeros=zeros, rowptr=rowptr, col=col, val=val, nnz=nnz)
 
 
-def weight_bytes(n: int, k: int, bits: int, nnz: int = 0, sym: bool = False) -> int:
+def weight_bytes(n: int, k: int, bits: int, nnz: int = 0, sym: bool = False, g: int = 128) -> int:
     """Algorithmic bytes a matmul must read for the weight: packed codes, fp16 scale and u8
-    zero point per group of 128 (no zero point for symmetric groups), plus the outlier CSR
+    zero point per group of g (no zero point for symmetric groups), plus the outlier CSR
     (int32 col + fp16 val + rowptr)."""
     csr = (nnz * 6 + (n + 1) * 4) if nnz else 0
-    return n * k * bits // 8 + (n * k // 128) * (2 if sym else 3) + csr
+    return n * k * bits // 8 + (n * k // g) * (2 if sym else 3) + csr
 
 
 def time_graph(torch, fn, reps: int, stream) -> float:
@@ -428,6 +429,19 @@ def main():
         sym[f"b{b}_m1"] = dict(us=round(ms * 1e3, 3), GBps=round(bs / (ms * 1e-3) / 1e9, 1), bytes=bs)
         del cs, hs, wsy
     extra["gemv_4096_sym_m1"] = sym
+    log("bench: 4096x4096 GEMV at M=1 with groups of 32 and 64")
+    small = {}
+    for b, g, sy in ((2, 32, True), (2, 64, True), (2, 32, False), (5, 64, False), (6, 64, False)):
+        ds, wsy = quantize_pack(q, torch, workloads.layer_weights(2), b, sym=sy, g=g)
+        cs = [clone_weight(torch, wsy) for _ in range(args.copies)]
+        hs = [q.weight(c["packed"], c["scales"], c["zeros"]) for c in cs]
+        ms = time_graph(torch, lambda i: q.qlinear_gemv(ds, hs[i % args.copies], x1, K, 1, y1, N), 4 * args.copies,
+                        stream)
+        bs = weight_bytes(N, K, b, sym=sy, g=g)
+        small[f"b{b}_g{g}{'_sym' if sy else ''}"] = dict(us=round(ms * 1e3, 3), GBps=round(bs / (ms * 1e-3) / 1e9, 1),
+                                                         bytes=bs, bits_per_weight=round(8 * bs / (N * K), 4))
+        del cs, hs, wsy
+    extra["gemv_4096_small_groups_m1"] = small
     if not args.no_stack:
         log("bench: Llama-7B-shaped 32-layer decode stack at M=1")
         extra["stack_llama7b_m1"] = bench_stack(q, torch, workloads, stream)
