@@ -98,7 +98,7 @@ def gemv_kernel_name(bits: int, m: int, n: int) -> str:
     depth, activation row pairs> (the launcher in qmm_small.hip picks them the same way)."""
     mx = 1 if m <= 2 else 2 if m <= 4 else 4 if m <= 8 else 8
     nw = 4 if (n // 16 >= 512 or mx == 8) else 8
-    return f"qp::gemv_kernel<{bits}, {nw}, 2, {mx}>"
+    return f"qp::gemv_kernel<{bits}, {nw}, 2, {mx}, 128>"
 
 
 def measured_traffic(kernel: str):
