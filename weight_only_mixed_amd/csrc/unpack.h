@@ -141,25 +141,6 @@ template <int B, int J> struct BlockUnpack {
     }
 };
 
-// Load lane `lane`'s chunk of one device-layout tile (512*B bytes at `tile`).
-template <int B>
-__device__ __forceinline__ void load_chunk(const uint8_t *tile, int lane, uint32_t *d)
-{
-#pragma unroll
-    for (int s = 0; s < B / 2; ++s) {
-        const u4 v = *(const u4 *)(tile + 1024 * s + 16 * lane);
-        d[4 * s + 0] = v[0];
-        d[4 * s + 1] = v[1];
-        d[4 * s + 2] = v[2];
-        d[4 * s + 3] = v[3];
-    }
-    if (B & 1) {
-        const u2 v = *(const u2 *)(tile + 1024 * (B / 2) + 8 * lane);
-        d[2 * B - 2] = v[0];
-        d[2 * B - 1] = v[1];
-    }
-}
-
 // Unpack all eight blocks of a chunk with NG groups per k-tile: block j belongs to group
 // j * NG / 8 (NG = 2: blocks 0-3 and 4-7; NG = 8: one group per block).
 template <int B, int NG>
@@ -175,30 +156,9 @@ __device__ __forceinline__ void unpack_chunk_groups(const uint32_t *d, const Gro
     a[7] = BlockUnpack<B, 7>::run(d, gc[7 * NG / 8]);
 }
 
-// Unpack all eight blocks of a chunk; blocks 0..3 use group 0's zero point, 4..7 group 1's.
-template <int B>
-__device__ __forceinline__ void unpack_chunk(const uint32_t *d, const GroupConst<B> &g0,
-                                             const GroupConst<B> &g1, h8 *a)
-{
-    a[0] = BlockUnpack<B, 0>::run(d, g0);
-    a[1] = BlockUnpack<B, 1>::run(d, g0);
-    a[2] = BlockUnpack<B, 2>::run(d, g0);
-    a[3] = BlockUnpack<B, 3>::run(d, g0);
-    a[4] = BlockUnpack<B, 4>::run(d, g1);
-    a[5] = BlockUnpack<B, 5>::run(d, g1);
-    a[6] = BlockUnpack<B, 6>::run(d, g1);
-    a[7] = BlockUnpack<B, 7>::run(d, g1);
-}
-
 __device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-// First k of block j of lane group t inside k-tile kt.
-__device__ __forceinline__ int block_k0(int kt, int j, int t)
-{
-    return kTileK * kt + 128 * (j >> 2) + 32 * (j & 3) + 8 * t;
 }
 
 }  // namespace qp
