@@ -77,6 +77,18 @@ def lib():
         L.or_linear.argtypes = [i64, i64, i64, i32, vp, i64, vp, vp, vp, vp, vp, vp, vp, i64]
         L.or_moe_ffn.restype = None
         L.or_moe_ffn.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp] + [vp] * 9 + [vp]
+        L.or_kv_quantize_row.restype = None
+        L.or_kv_quantize_row.argtypes = [vp, i32, i32, i32, vp, vp]
+        L.or_kv_k_pos.restype = i64
+        L.or_kv_k_pos.argtypes = [i32, i32]
+        L.or_kv_v_pos.restype = i64
+        L.or_kv_v_pos.argtypes = [i32, i32, i32]
+        for name in ("or_kv_layout", "or_kv_unlayout"):
+            getattr(L, name).restype = None
+            getattr(L, name).argtypes = [i32, i32, i64, i64, vp, vp, vp]
+        L.or_attn_decode.restype = None
+        L.or_attn_decode.argtypes = [i64, i64, i64, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, dbl,
+                                     vp, vp]
         L.or_swiglu_act.restype = None
         L.or_swiglu_act.argtypes = [i64, i64, i32, vp] + [vp] * 6 + [vp]
         L.or_quant_bytes.restype = dbl
@@ -274,6 +286,71 @@ def swiglu_act(x_row_fp16, gate: dict, up: dict):
                         _p(_c(gate["zeros"], np.uint8)), _p(_c(up["codes"], np.uint8)),
                         _p(_c(up["scales"], np.uint16)), _p(_c(up["zeros"], np.uint8)), _p(v))
     return v
+
+
+# ---- quantized KV cache and decode attention ------------------------------------------
+
+KV_DIM = 128
+
+
+def kv_quantize(x_fp16, bits: int, g: int):
+    """Rows of fp16 head vectors [n][128] -> (offset codes u8 [n][128], fp32 scales [n][128/g])."""
+    x = _bits16(x_fp16).reshape(-1, KV_DIM)
+    n = x.shape[0]
+    codes = np.zeros((n, KV_DIM), np.uint8)
+    scales = np.zeros((n, KV_DIM // g), np.float32)
+    L = lib()
+    for i in range(n):
+        row = np.ascontiguousarray(x[i])
+        L.or_kv_quantize_row(_p(row), KV_DIM, g, bits, _p(codes[i]), _p(scales[i]))
+    return codes, scales
+
+
+def kv_k_pos(bits: int, d: int) -> int:
+    return lib().or_kv_k_pos(bits, d)
+
+
+def kv_v_pos(bits: int, w: int, d: int) -> int:
+    return lib().or_kv_v_pos(bits, w, d)
+
+
+def kv_cache_bytes(rows: int, bits: int) -> int:
+    return rows * KV_DIM * bits // 8
+
+
+def kv_layout(codes, slots, which: int, bits: int, cap: int, total_rows: int, cache=None):
+    """Scatter offset codes [n][128] to cache rows `slots` (which: 0 = K, 1 = V layout)."""
+    codes = _c(codes, np.uint8)
+    slots = _c(slots, np.int64)
+    if cache is None:
+        cache = np.zeros(kv_cache_bytes(total_rows, bits), np.uint8)
+    lib().or_kv_layout(which, bits, cap, len(slots), _p(slots), _p(codes), _p(cache))
+    return cache
+
+
+def kv_unlayout(cache, slots, which: int, bits: int, cap: int):
+    cache = _c(cache, np.uint8)
+    slots = _c(slots, np.int64)
+    codes = np.zeros((len(slots), KV_DIM), np.uint8)
+    lib().or_kv_unlayout(which, bits, cap, len(slots), _p(slots), _p(cache), _p(codes))
+    return codes
+
+
+def attn_decode(q_fp16, kc, ks, vc, vs, lens, kv_heads: int, cap: int, kbits: int, vbits: int,
+                sm_scale: float):
+    """fp64 decode attention over offset codes [B*Hkv*cap][128] and fp32 scales.
+    Returns (o [B][Hq][128], a [B][Hq][128]) with a = sum_t p_t |v_t|."""
+    q = _bits16(q_fp16)
+    B, Hq = q.shape[0], q.shape[1]
+    kc, vc = _c(kc, np.uint8), _c(vc, np.uint8)
+    ks, vs = _c(ks, np.float32), _c(vs, np.float32)
+    kg, vg = KV_DIM // ks.shape[1], KV_DIM // vs.shape[1]
+    lens = _c(lens, np.int32)
+    o = np.zeros((B, Hq, KV_DIM), np.float64)
+    a = np.zeros((B, Hq, KV_DIM), np.float64)
+    lib().or_attn_decode(B, Hq, kv_heads, cap, kbits, kg, vbits, vg, _p(np.ascontiguousarray(q)), _p(kc), _p(ks),
+                         _p(vc), _p(vs), _p(lens), float(sm_scale), _p(o), _p(a))
+    return o, a
 
 
 # ---- byte accounting ----------------------------------------------------------------

@@ -17,7 +17,10 @@
  *  [70B] single-GPU 70B five-layer stack (bjdmk.com.cn/5414039): s2 group-wise
  *        outlier-aware INT4 (groups of 128, top 0.1% |w| held out in fp16, added back
  *        after the GEMM); s3 unfused reference path dequantize -> matmul(x, W^T).
- *  [KV]  KV-cache INT8/INT4 accounting (kwkr.cn): s1.1, s3.1-s3.3 byte sums.
+ *  [KV]  KV-cache INT8/INT4 quantization (kwkr.cn): s1.1, s3.1-s3.3 byte sums; s2.1
+ *        symmetric absmax scale; s2.2 per-group along the head dimension; s2.3 K at
+ *        INT4 with V at INT8; s3.1 FP32 scales; s5.1 4-bit packing, the operator
+ *        consuming the quantized cache directly.
  *  [MoE] on-device MoE memory wall (bjdmk.com.cn/5648983): s1.1 weight/KV byte
  *        formulas; s4.2 routed expert tasks (hidden states + top-k expert ids).
  *
@@ -36,7 +39,11 @@
  *    absorbs the offset): the range is [-m, m] with m = max |w|, so the scale is
  *    fp16((m + m) / qmax) and the zero point is the midpoint 2^(b-1), which the
  *    asymmetric formula would also give for that range; it is implied, not stored, and
- *    an all-zero group gets scale 1.0 with every code at the midpoint.
+ *    an all-zero group gets scale 1.0 with every code at the midpoint;
+ *  - KV cache ([KV] s2.1-s2.2, s3.1): symmetric groups along the head dimension with
+ *    qmax = 2^(b-1) - 1, an fp32 scale m / qmax, codes rint(x / s) clamped to
+ *    [-qmax, qmax] and stored offset by 2^(b-1); an all-zero group stores scale 0;
+ *    attention over an empty sequence returns 0.
  *
  * Arithmetic: quantization in fp32 exactly as stated; every matmul accumulates in
  * fp64 over the exactly dequantized weights.  Build: gcc -O2 -ffp-contract=off
@@ -525,6 +532,160 @@ void or_moe_ffn(int64_t T, int64_t D, int64_t F, int topk, int g,
     }
     free(v);
     free(a);
+}
+
+/* ------------------------------------------------------------------------------ */
+/* Quantized KV cache and decode attention  ([KV] s2.1-s2.3, s3.1, s5.1)             */
+/* ------------------------------------------------------------------------------ */
+
+/* Symmetric per-group quantization of one cached row ([KV] s2.1: the scale comes from
+ * the absolute maximum, every element is divided by it and rounded; s2.2: adjacent
+ * elements of the head dimension share one scale per group; s3.1: the scale is FP32).
+ * Readings: qmax = 2^(b-1) - 1 (127 at 8 bits, the [-127, 127] range of the inference
+ * guide's INT8 example; 7 at 4 bits); s = m / qmax in IEEE fp32; q = rint(x / s) with
+ * ties to even, clamped to [-qmax, qmax]; an all-zero group stores s = 0 and q = 0.
+ * Codes are stored offset by 2^(b-1) (so 1 .. 2^b - 1; 2^(b-1) means 0). */
+void or_kv_quantize_row(const uint16_t *x, int n, int g, int bits, uint8_t *codes, float *scales)
+{
+    const int qmax = (1 << (bits - 1)) - 1, mid = 1 << (bits - 1);
+    for (int g0 = 0; g0 < n; g0 += g) {
+        float m = 0.0f;
+        for (int i = 0; i < g; ++i) {
+            const float a = fabsf((float)hv(x[g0 + i]));
+            if (a > m) m = a;
+        }
+        const float s = m / (float)qmax;
+        scales[g0 / g] = m == 0.0f ? 0.0f : s;
+        for (int i = 0; i < g; ++i) {
+            int q = 0;
+            if (m != 0.0f) {
+                const float v = (float)hv(x[g0 + i]) / s;
+                q = clampi((int)rintf(v), -qmax, qmax);
+            }
+            codes[g0 + i] = (uint8_t)(q + mid);
+        }
+    }
+}
+
+/* Storage of the quantized cache (the library's own encoding; the page fixes only that
+ * 4-bit values pack two per byte, [KV] s5.1).  Positions are in values: value p of a
+ * 4-bit stream is the low nibble of byte p/2 when p is even, the high nibble otherwise.
+ *  sigma(s): slot s = 0..7 of an 8-value piece sits at s (8-bit) or s/2 + 4*(s%2)
+ *  (4-bit: the two values of a pair are four nibbles apart).
+ *  K row (one token, head_dim 128): value d = 32j + 8t + s sits at 32t + 8j + sigma(s).
+ *  V tile (32 tokens x 128, tile u holds tokens 32u .. 32u+31 of one head): token
+ *  tau = 32u + w and value d = 16c + r sit at 1024t + 64r + 8c + sigma(s), where
+ *  w = 4t + s (s < 4) or 16 + 4t + (s - 4) (s >= 4). */
+static int kv_sigma(int bits, int s) { return bits == 8 ? s : s / 2 + 4 * (s % 2); }
+
+int64_t or_kv_k_pos(int bits, int d)
+{
+    const int j = d / 32, t = (d % 32) / 8, s = d % 8;
+    return 32 * t + 8 * j + kv_sigma(bits, s);
+}
+
+int64_t or_kv_v_pos(int bits, int w, int d)
+{
+    const int hi = w >= 16, t = ((w % 16) / 4), s = (w % 4) + 4 * hi;
+    const int c = d / 16, r = d % 16;
+    return 1024 * t + 64 * r + 8 * c + kv_sigma(bits, s);
+}
+
+static void put_value(uint8_t *base, int bits, int64_t pos, uint8_t v)
+{
+    if (bits == 8) {
+        base[pos] = v;
+    } else {
+        uint8_t *b = base + pos / 2;
+        *b = (pos % 2) ? (uint8_t)((*b & 0x0F) | (v << 4)) : (uint8_t)((*b & 0xF0) | (v & 0x0F));
+    }
+}
+
+static uint8_t get_value(const uint8_t *base, int bits, int64_t pos)
+{
+    if (bits == 8) return base[pos];
+    return (pos % 2) ? (uint8_t)(base[pos / 2] >> 4) : (uint8_t)(base[pos / 2] & 0x0F);
+}
+
+/* Value position of (row R = (b*heads + h)*cap + tau, d) in the cache of one tensor,
+ * counted from the cache base (which: 0 = K rows, 1 = V tiles; cap % 32 == 0). */
+static int64_t kv_pos(int which, int bits, int64_t cap, int64_t R, int d)
+{
+    if (which == 0) return R * 128 + or_kv_k_pos(bits, d);
+    const int64_t region = R / cap, tau = R % cap;
+    return region * cap * 128 + (tau / 32) * 32 * 128 + or_kv_v_pos(bits, (int)(tau % 32), d);
+}
+
+/* Scatter offset codes [rows][128] into the cache bytes at rows slot[i] (K or V layout). */
+void or_kv_layout(int which, int bits, int64_t cap, int64_t rows, const int64_t *slot,
+                  const uint8_t *codes, uint8_t *cache)
+{
+    for (int64_t i = 0; i < rows; ++i)
+        for (int d = 0; d < 128; ++d)
+            put_value(cache, bits, kv_pos(which, bits, cap, slot[i], d), codes[i * 128 + d]);
+}
+
+/* Gather: the inverse of or_kv_layout for rows slot[i]. */
+void or_kv_unlayout(int which, int bits, int64_t cap, int64_t rows, const int64_t *slot,
+                    const uint8_t *cache, uint8_t *codes)
+{
+    for (int64_t i = 0; i < rows; ++i)
+        for (int d = 0; d < 128; ++d)
+            codes[i * 128 + d] = get_value(cache, bits, kv_pos(which, bits, cap, slot[i], d));
+}
+
+/* Decode attention over the quantized cache ([KV] s5.1: the operator reads the quantized
+ * K/V and their scales directly).  For batch b and query head h (kv head h / (Hq/Hkv)),
+ * over the first len[b] tokens of that kv head:
+ *   z_t = sm_scale * sum_d q[h][d] * kq_t[d]*ks_t[d/kg],  p = softmax(z),
+ *   o[h][d] = sum_t p_t * vq_t[d]*vs_t[d/vg]                      (all in fp64),
+ * with kq, vq the signed codes (stored code - 2^(b-1)).  Also a[h][d] = sum_t p_t |v_t[d]|,
+ * the weighted magnitude that bounds rounding errors of a computed o.  len[b] == 0
+ * gives o = 0, a = 0.  kc/vc: offset codes [B*Hkv*cap][128] (unpacked), ks/vs:
+ * [B*Hkv*cap][128/g] fp32; q fp16 [B][Hq][128]. */
+void or_attn_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t cap, int kbits, int kg, int vbits,
+                    int vg, const uint16_t *q, const uint8_t *kc, const float *ks,
+                    const uint8_t *vc, const float *vs, const int32_t *len, double sm_scale,
+                    double *o, double *a)
+{
+    const int kmid = 1 << (kbits - 1), vmid = 1 << (vbits - 1);
+    const int64_t grp = Hq / Hkv;
+    (void)hv(0); /* fill the half table before the threads read it */
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < Hq; ++h) {
+            const int64_t hk = h / grp, base = (b * Hkv + hk) * cap;
+            const int64_t L = len[b];
+            double *oh = o + (b * Hq + h) * 128, *ah = a + (b * Hq + h) * 128;
+            for (int d = 0; d < 128; ++d) oh[d] = ah[d] = 0.0;
+            if (L <= 0) continue;
+            double *z = (double *)malloc((size_t)L * sizeof(double));
+            double zmax = -INFINITY;
+            for (int64_t t = 0; t < L; ++t) {
+                const int64_t R = base + t;
+                double acc = 0.0;
+                for (int d = 0; d < 128; ++d)
+                    acc += hv(q[(b * Hq + h) * 128 + d]) *
+                           ((double)((int)kc[R * 128 + d] - kmid) * (double)ks[R * (128 / kg) + d / kg]);
+                z[t] = sm_scale * acc;
+                if (z[t] > zmax) zmax = z[t];
+            }
+            double sum = 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                z[t] = exp(z[t] - zmax);
+                sum += z[t];
+            }
+            for (int64_t t = 0; t < L; ++t) {
+                const int64_t R = base + t;
+                const double p = z[t] / sum;
+                for (int d = 0; d < 128; ++d) {
+                    const double v = (double)((int)vc[R * 128 + d] - vmid) * (double)vs[R * (128 / vg) + d / vg];
+                    oh[d] += p * v;
+                    ah[d] += p * fabs(v);
+                }
+            }
+            free(z);
+        }
 }
 
 /* ------------------------------------------------------------------------------ */
