@@ -567,6 +567,13 @@ void or_kv_quantize_row(const uint16_t *x, int n, int g, int bits, uint8_t *code
     }
 }
 
+/* or_kv_quantize_row over `rows` consecutive rows of 128 values. */
+void or_kv_quantize_rows(const uint16_t *x, int64_t rows, int g, int bits, uint8_t *codes, float *scales)
+{
+    for (int64_t i = 0; i < rows; ++i)
+        or_kv_quantize_row(x + i * 128, 128, g, bits, codes + i * 128, scales + i * (128 / g));
+}
+
 /* Storage of the quantized cache (the library's own encoding; the page fixes only that
  * 4-bit values pack two per byte, [KV] s5.1).  Positions are in values: value p of a
  * 4-bit stream is the low nibble of byte p/2 when p is even, the high nibble otherwise.
@@ -640,9 +647,10 @@ void or_kv_unlayout(int which, int bits, int64_t cap, int64_t rows, const int64_
  *   z_t = sm_scale * sum_d q[h][d] * kq_t[d]*ks_t[d/kg],  p = softmax(z),
  *   o[h][d] = sum_t p_t * vq_t[d]*vs_t[d/vg]                      (all in fp64),
  * with kq, vq the signed codes (stored code - 2^(b-1)).  Also a[h][d] = sum_t p_t |v_t[d]|,
- * the weighted magnitude that bounds rounding errors of a computed o.  len[b] == 0
- * gives o = 0, a = 0.  kc/vc: offset codes [B*Hkv*cap][128] (unpacked), ks/vs:
- * [B*Hkv*cap][128/g] fp32; q fp16 [B][Hq][128]. */
+ * the weighted magnitude that bounds rounding errors of a computed o.  len[b] <= 0
+ * gives o = 0, a = 0; a length above cap counts as cap (a sequence holds cap slots).
+ * kc/vc: offset codes [B*Hkv*cap][128] (unpacked), ks/vs: [B*Hkv*cap][128/g] fp32;
+ * q fp16 [B][Hq][128]. */
 void or_attn_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t cap, int kbits, int kg, int vbits,
                     int vg, const uint16_t *q, const uint8_t *kc, const float *ks,
                     const uint8_t *vc, const float *vs, const int32_t *len, double sm_scale,
@@ -655,7 +663,7 @@ void or_attn_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t cap, int kbits, 
     for (int64_t b = 0; b < B; ++b)
         for (int64_t h = 0; h < Hq; ++h) {
             const int64_t hk = h / grp, base = (b * Hkv + hk) * cap;
-            const int64_t L = len[b];
+            const int64_t L = len[b] > cap ? cap : len[b];
             double *oh = o + (b * Hq + h) * 128, *ah = a + (b * Hq + h) * 128;
             for (int d = 0; d < 128; ++d) oh[d] = ah[d] = 0.0;
             if (L <= 0) continue;

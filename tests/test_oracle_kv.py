@@ -246,3 +246,12 @@ def test_attention_token_order_and_empty():
     o2, _ = oracle.attn_decode(q, kc[perm], ks[perm], vc[perm], vs[perm], lens, Hkv, cap, 4, 8, 0.1)
     assert np.allclose(o[0], o2[0], rtol=1e-13, atol=1e-15)
     assert (o[1] == 0).all() and (a[1] == 0).all()
+
+
+def test_attention_length_clamped_to_capacity():
+    B, Hkv, cap = 2, 1, 32
+    kc, ks, vc, vs = _cache(B, Hkv, cap, 4, 64, 8, 64, 10)
+    q = _rows(2, 14).reshape(2, 1, D)
+    o1, _ = oracle.attn_decode(q, kc, ks, vc, vs, np.array([cap, 5], np.int32), Hkv, cap, 4, 8, 0.1)
+    o2, _ = oracle.attn_decode(q, kc, ks, vc, vs, np.array([cap + 100, 5], np.int32), Hkv, cap, 4, 8, 0.1)
+    assert (o1 == o2).all()
