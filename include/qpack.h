@@ -21,7 +21,9 @@
  *    match GPU tiles: 2/3/5/6-bit mixed quantization page (pwwt.cn), s2.3, s3.1-s3.3, s4.2;
  *  - 4-bit packs two values per byte: KV-cache quantization page (kwkr.cn), s5.1;
  *  - routed experts receive hidden states plus top-k expert ids:
- *    "端侧MoE推理存储墙优化：显存精算、预取重叠与量化补偿实战", s4.2.
+ *    "端侧MoE推理存储墙优化：显存精算、预取重叠与量化补偿实战", s4.2;
+ *  - quantized KV cache read directly by decode attention: KV-cache quantization page
+ *    (kwkr.cn), s2.1-s2.3, s3.1, s5.1.
  *
  * Conventions for every entry point:
  *  - All array pointers are DEVICE pointers (hipMalloc'd memory, e.g. torch tensors), except
@@ -278,6 +280,83 @@ qp_status qmoe_ffn(const qp_weight_desc *desc_gu, const qp_weight *gate_up,
                    const uint16_t *x, int64_t ldx, int64_t tokens, const int32_t *topk_ids,
                    const float *topk_w, int32_t topk, uint16_t *out, int64_t ldo,
                    void *workspace, size_t ws_bytes, void *stream);
+
+/* ---- quantized KV cache and decode attention (KV-cache quantization page, kwkr.cn) ---- */
+
+/*
+ * Geometry and format of a quantized KV cache.  Each (sequence b, kv head h) owns
+ * `capacity` token slots; cache row R = (b*kv_heads + h)*capacity + token.  K and V are
+ * quantized per row in symmetric groups of adjacent head-dimension values (s2.1, s2.2) at
+ * their own bit widths (s2.3: INT4 K with INT8 V is the page's middle ground) with one fp32
+ * scale per group (s3.1):
+ *     m = max |x| over the group, qmax = 2^(bits-1) - 1, s = m / qmax (IEEE fp32),
+ *     q = clamp(rint(x / s), -qmax, qmax) (ties to even), stored as q + 2^(bits-1);
+ *     an all-zero group stores s = 0 and q = 0.
+ * Code bytes (4-bit values two per byte, s5.1; value p is the low nibble of byte p/2 when p
+ * is even; sigma(s) = s at 8 bits, s/2 + 4*(s%2) at 4 bits):
+ *   K  row R holds 128*k_bits/8 bytes; value d = 32j + 8t + s sits at 32t + 8j + sigma(s).
+ *   V  each (b, h) holds capacity/32 tiles of 32 tokens (32*128*v_bits/8 bytes each); token
+ *      w of a tile, w = 4t + s (s < 4) or 16 + 4t + s - 4 (s >= 4), value d = 16c + r, sits
+ *      at 1024t + 64r + 8c + sigma(s).
+ *   Scales: fp32 [rows][128/group].
+ * These orders put every operand of the attention's 16x16x32 matrix-core steps in one
+ * contiguous 16-64 byte piece per lane.
+ */
+typedef struct {
+    int32_t batch;      /* sequences */
+    int32_t q_heads;    /* query heads, a multiple of kv_heads with q_heads/kv_heads <= 16 */
+    int32_t kv_heads;
+    int32_t head_dim;   /* 128 */
+    int32_t k_bits;     /* 4 or 8 */
+    int32_t v_bits;     /* 4 or 8 */
+    int32_t k_group;    /* 32, 64 or 128 */
+    int32_t v_group;    /* 32, 64 or 128 */
+    int64_t capacity;   /* token slots per (sequence, kv head): a multiple of 32, < 2^24 */
+} qkv_desc;
+enum { QKV_K = 0, QKV_V = 1 };
+
+/* Code bytes of the whole K (which = QKV_K) or V cache: batch*kv_heads*capacity*128*bits/8,
+ * or 0 if desc is invalid. */
+size_t qkv_cache_bytes(const qkv_desc *desc, int32_t which);
+/* fp32 scales of the whole K or V cache: batch*kv_heads*capacity*128/group (0 if invalid). */
+size_t qkv_scale_count(const qkv_desc *desc, int32_t which);
+
+/*
+ * Quantize `rows` new K (or V) head vectors into the cache (the write path of a decode or
+ * prefill step).
+ *  x       fp16 [rows][ldx] device, ldx >= 128, ldx % 8 == 0, 16-byte aligned.
+ *  slots   int64 [rows] device: cache row R of each input row.  Rows whose slot is outside
+ *          [0, batch*kv_heads*capacity) are skipped (the device cannot report them).
+ *          Slots must be distinct within one call.
+ *  codes   the cache's code bytes (qkv_cache_bytes), 16-byte aligned; scales fp32
+ *          (qkv_scale_count), 16-byte aligned.  Only the addressed rows change.
+ * Bit-exact with the CPU reference.
+ */
+qp_status qkv_quantize(const qkv_desc *desc, int32_t which, const uint16_t *x, int64_t ldx,
+                       const int64_t *slots, int64_t rows, void *codes, float *scales,
+                       void *stream);
+
+/* Scratch bytes of qattn_decode (0 when one chunk per (sequence, kv head) suffices). */
+size_t qattn_decode_workspace_bytes(const qkv_desc *desc);
+
+/*
+ * Decode attention over the quantized cache, one query token per sequence (s5.1: the
+ * operator reads the packed codes and scales and dequantizes in registers).  For sequence
+ * b and query head h (kv head h / (q_heads/kv_heads)), over its first seq_lens[b] tokens:
+ *     z_t = sm_scale * q[b][h] . K_t,   p = softmax(z),   o[b][h] = sum_t p_t V_t
+ * with K_t, V_t the dequantized rows (code - 2^(bits-1)) * scale.  Scores accumulate in
+ * fp32 (each K group scaled in fp32); V values are dequantized to fp16 and the softmax
+ * weights (at most 2^14 times their share) are rounded to fp16 for the matrix cores; o is
+ * rounded once to fp16.  seq_lens[b] <= 0 gives o = 0; lengths above capacity are clamped.
+ *  q        fp16 [batch][q_heads][128] device, 16-byte aligned.
+ *  seq_lens int32 [batch] device.
+ *  o        fp16 [batch][q_heads][128] device.
+ *  workspace/ws_bytes  at least qattn_decode_workspace_bytes(desc) bytes, 16-byte aligned.
+ */
+qp_status qattn_decode(const qkv_desc *desc, const uint16_t *q, const void *k_codes,
+                       const float *k_scales, const void *v_codes, const float *v_scales,
+                       const int32_t *seq_lens, float sm_scale, uint16_t *o, void *workspace,
+                       size_t ws_bytes, void *stream);
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char *qp_last_error(void);

@@ -199,3 +199,69 @@ def test_grouped_and_moe_validation():
 def test_status_message_is_thread_local_text():
     q.qpack_pack(q.desc(9, 16, 256), FAKE, FAKE, stream=0, check=False)
     assert "bits=9" in q.last_error()
+
+
+# ---- quantized KV cache ----------------------------------------------------------------
+
+def _kv_layer_bytes(d):
+    return sum(q.qkv_cache_bytes(d, w) + 4 * q.qkv_scale_count(d, w) for w in (q.QKV_K, q.QKV_V))
+
+
+@pytest.mark.parametrize("heads,group,mib", [(32, 64, 288), (32, 128, 272), (4, 64, 36)])
+def test_kv_cache_sizes_match_page(heads, group, mib):
+    """KV page s3.1-s3.2: 32 layers, 2048 tokens, INT4 K and V with FP32 scales."""
+    d = q.kv_desc(1, heads, heads, 2048, 4, 4, group, group)
+    assert 32 * _kv_layer_bytes(d) == mib * 2 ** 20
+
+
+def test_kv_mixed_precision_size():
+    """KV page s2.3: INT4 K with INT8 V leaves 0.375 GB of the 1 GB fp16 cache."""
+    c = GOLD["kv_mixed_k4_v8"]
+    d = q.kv_desc(1, c["kv_heads"], c["kv_heads"], c["tokens"], c["k_bits"], c["v_bits"])
+    assert c["layers"] * (q.qkv_cache_bytes(d, q.QKV_K) + q.qkv_cache_bytes(d, q.QKV_V)) == c["bytes"]
+
+
+def test_kv_workspace():
+    assert q.qattn_decode_workspace_bytes(q.kv_desc(64, 32, 32, 128)) == 0     # one chunk each
+    d = q.kv_desc(1, 32, 8, 32768)
+    ws = q.qattn_decode_workspace_bytes(d)
+    assert ws > 0 and ws % (32 * (128 * 4 + 8)) == 0
+
+
+FAKE = 1 << 20  # a 16-byte aligned address; never dereferenced (validation fails first)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, q.QP_ERR_UNSUPPORTED), ("k_bits", 2, q.QP_ERR_UNSUPPORTED), ("v_bits", 6, q.QP_ERR_UNSUPPORTED),
+    ("k_group", 16, q.QP_ERR_UNSUPPORTED), ("v_group", 256, q.QP_ERR_UNSUPPORTED),
+    ("q_heads", 12, q.QP_ERR_INVALID_ARG), ("q_heads", 8 * 17, q.QP_ERR_UNSUPPORTED),
+    ("capacity", 48, q.QP_ERR_INVALID_ARG), ("capacity", 0, q.QP_ERR_INVALID_ARG), ("batch", 0, q.QP_ERR_INVALID_ARG)])
+def test_kv_desc_validation(field, value, status):
+    d = q.kv_desc(2, 16, 8, 256)
+    setattr(d, field, value)
+    assert q.qkv_cache_bytes(d, q.QKV_K) == 0 and q.qkv_scale_count(d, q.QKV_V) == 0
+    assert q.qkv_quantize(d, q.QKV_K, FAKE, 128, FAKE, 4, FAKE, FAKE, check=False) == status
+    assert q.qattn_decode(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, 1 << 30, check=False) == status
+    assert q.last_error()
+
+
+def test_kv_call_validation():
+    d = q.kv_desc(2, 16, 8, 256)
+    E = q.QP_ERR_INVALID_ARG
+    assert q.qkv_quantize(d, 2, FAKE, 128, FAKE, 4, FAKE, FAKE, check=False) == E
+    assert q.qkv_quantize(d, q.QKV_V, FAKE + 2, 128, FAKE, 4, FAKE, FAKE, check=False) == E   # x misaligned
+    assert q.qkv_quantize(d, q.QKV_V, FAKE, 120, FAKE, 4, FAKE, FAKE, check=False) == E       # ldx < 128
+    assert q.qkv_quantize(d, q.QKV_V, FAKE, 128, None, 4, FAKE, FAKE, check=False) == E       # slots NULL
+    assert q.qkv_quantize(d, q.QKV_V, FAKE, 128, FAKE, -1, FAKE, FAKE, check=False) == E
+    assert q.qkv_quantize(d, q.QKV_V, FAKE, 128, FAKE, 4, FAKE + 8, FAKE, check=False) == E   # codes misaligned
+    assert q.qattn_decode(d, FAKE + 2, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, check=False) == E
+    assert q.qattn_decode(d, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, check=False) == E
+    assert q.qattn_decode(d, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0.1, FAKE, check=False) == E
+    assert q.qattn_decode(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, float("nan"), FAKE, check=False) == E
+    big = q.kv_desc(1, 8, 8, 32768)
+    need = q.qattn_decode_workspace_bytes(big)
+    assert need > 0
+    assert q.qattn_decode(big, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, need - 1,
+                          check=False) == q.QP_ERR_WORKSPACE
+    assert q.qattn_decode(big, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, None, 0,
+                          check=False) == q.QP_ERR_WORKSPACE

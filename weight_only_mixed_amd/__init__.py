@@ -42,6 +42,15 @@ class qp_weight(ctypes.Structure):
                 ("csr_val", ctypes.c_void_p), ("nnz", ctypes.c_int64)]
 
 
+class qkv_desc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("q_heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32),
+                ("k_group", ctypes.c_int32), ("v_group", ctypes.c_int32), ("capacity", ctypes.c_int64)]
+
+
+QKV_K, QKV_V = 0, 1
+
+
 class qp_gemv_problem(ctypes.Structure):
     _fields_ = [("desc", qp_weight_desc), ("w", qp_weight), ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64),
                 ("m", ctypes.c_int64), ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64)]
@@ -50,6 +59,7 @@ class qp_gemv_problem(ctypes.Structure):
 _vp, _i64, _i32, _dbl, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_size_t
 _D = ctypes.POINTER(qp_weight_desc)
 _W = ctypes.POINTER(qp_weight)
+_KD = ctypes.POINTER(qkv_desc)
 _SIGS = {
     "qp_packed_bytes": (_sz, [_D]),
     "qp_num_groups": (_sz, [_D]),
@@ -70,6 +80,11 @@ _SIGS = {
     "qmoe_ffn_workspace_bytes": (_sz, [_i64, _i32, _i32, _i64, _i64]),
     "qmoe_ffn": (_i32, [_D, _W, _D, _W, _i32, _vp, _i64, _i64, _vp, _vp, _i32, _vp, _i64, _vp, _sz,
                         _vp]),
+    "qkv_cache_bytes": (_sz, [_KD, _i32]),
+    "qkv_scale_count": (_sz, [_KD, _i32]),
+    "qkv_quantize": (_i32, [_KD, _i32, _vp, _i64, _vp, _i64, _vp, _vp, _vp]),
+    "qattn_decode_workspace_bytes": (_sz, [_KD]),
+    "qattn_decode": (_i32, [_KD, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _sz, _vp]),
     "qp_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -223,6 +238,38 @@ def qmoe_ffn(d_gu, gate_up, d_down, down, x, ldx, tokens, topk_ids, topk_w, topk
                   lib.qmoe_ffn(ctypes.byref(d_gu), gu, ctypes.byref(d_down), dn, len(gate_up), _ptr(x), ldx, tokens,
                                _ptr(topk_ids), _ptr(topk_w), topk, _ptr(out), ldo, _ptr(workspace), ws_bytes,
                                _stream(stream)), check)
+
+
+# ---- quantized KV cache and decode attention --------------------------------------------
+
+def kv_desc(batch: int, q_heads: int, kv_heads: int, capacity: int, k_bits: int = 4, v_bits: int = 8,
+            k_group: int = 64, v_group: int = 64, head_dim: int = 128):
+    return qkv_desc(batch, q_heads, kv_heads, head_dim, k_bits, v_bits, k_group, v_group, capacity)
+
+
+def qkv_cache_bytes(d, which: int) -> int:
+    return lib.qkv_cache_bytes(ctypes.byref(d), which)
+
+
+def qkv_scale_count(d, which: int) -> int:
+    return lib.qkv_scale_count(ctypes.byref(d), which)
+
+
+def qattn_decode_workspace_bytes(d) -> int:
+    return lib.qattn_decode_workspace_bytes(ctypes.byref(d))
+
+
+def qkv_quantize(d, which, x, ldx, slots, rows, codes, scales, stream=None, check=True):
+    return _check("qkv_quantize", lib.qkv_quantize(ctypes.byref(d), which, _ptr(x), ldx, _ptr(slots), rows,
+                                                    _ptr(codes), _ptr(scales), _stream(stream)), check)
+
+
+def qattn_decode(d, q, k_codes, k_scales, v_codes, v_scales, seq_lens, sm_scale, o, workspace=None, ws_bytes=0,
+                 stream=None, check=True):
+    return _check("qattn_decode",
+                  lib.qattn_decode(ctypes.byref(d), _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
+                                   _ptr(v_scales), _ptr(seq_lens), float(sm_scale), _ptr(o), _ptr(workspace),
+                                   ws_bytes, _stream(stream)), check)
 
 
 EXPORTED = tuple(_SIGS)

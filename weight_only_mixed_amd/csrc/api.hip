@@ -86,6 +86,27 @@ static uint32_t zero_pair(const qp_weight_desc *d)
 
 static hipStream_t S(void *s) { return (hipStream_t)s; }
 
+// Geometry of a quantized KV cache (qkv_desc).
+static qp_status check_kv(const qkv_desc *d)
+{
+    if (!d) return fail(QP_ERR_INVALID_ARG, "desc is NULL");
+    if (d->head_dim != 128) return fail(QP_ERR_UNSUPPORTED, "head_dim=%d (128 is built)", d->head_dim);
+    if ((d->k_bits != 4 && d->k_bits != 8) || (d->v_bits != 4 && d->v_bits != 8))
+        return fail(QP_ERR_UNSUPPORTED, "k_bits=%d v_bits=%d (4 and 8 are built)", d->k_bits, d->v_bits);
+    for (int g : {d->k_group, d->v_group})
+        if (g != 32 && g != 64 && g != 128) return fail(QP_ERR_UNSUPPORTED, "group %d (32, 64, 128 are built)", g);
+    if (d->batch < 1 || d->kv_heads < 1 || d->q_heads < 1)
+        return fail(QP_ERR_INVALID_ARG, "batch, q_heads and kv_heads must be >= 1");
+    if (d->q_heads % d->kv_heads != 0) return fail(QP_ERR_INVALID_ARG, "q_heads must be a multiple of kv_heads");
+    if (d->q_heads / d->kv_heads > 16) return fail(QP_ERR_UNSUPPORTED, "more than 16 query heads per kv head");
+    if (d->capacity < 32 || d->capacity % 32 != 0 || d->capacity >= (1LL << 24))
+        return fail(QP_ERR_INVALID_ARG, "capacity=%lld must be a multiple of 32 below 2^24", (long long)d->capacity);
+    if ((int64_t)d->batch * d->kv_heads > (1LL << 16)) return fail(QP_ERR_INVALID_ARG, "batch*kv_heads above 65536");
+    return QP_OK;
+}
+
+static int64_t kv_rows(const qkv_desc *d) { return (int64_t)d->batch * d->kv_heads * d->capacity; }
+
 }  // namespace qp
 
 using namespace qp;
@@ -413,6 +434,93 @@ qp_status qmoe_ffn(const qp_weight_desc *dgu, const qp_weight *gate_up, const qp
                                    rows, d_model, stream)) != QP_OK)
         return st;
     return qmoe_combine(rows, d_model, token_rows, row_weight, tokens, topk, d_model, out, ldo, stream);
+}
+
+size_t qkv_cache_bytes(const qkv_desc *d, int32_t which)
+{
+    if (check_kv(d) != QP_OK || (which != QKV_K && which != QKV_V)) return 0;
+    return (size_t)kv_rows(d) * 128 * (which == QKV_K ? d->k_bits : d->v_bits) / 8;
+}
+
+size_t qkv_scale_count(const qkv_desc *d, int32_t which)
+{
+    if (check_kv(d) != QP_OK || (which != QKV_K && which != QKV_V)) return 0;
+    return (size_t)kv_rows(d) * (128 / (which == QKV_K ? d->k_group : d->v_group));
+}
+
+qp_status qkv_quantize(const qkv_desc *d, int32_t which, const uint16_t *x, int64_t ldx, const int64_t *slots,
+                       int64_t rows, void *codes, float *scales, void *stream)
+{
+    qp_status st;
+    if ((st = check_kv(d)) != QP_OK) return st;
+    if (which != QKV_K && which != QKV_V) return fail(QP_ERR_INVALID_ARG, "which=%d (QKV_K or QKV_V)", which);
+    if (rows < 0) return fail(QP_ERR_INVALID_ARG, "rows < 0");
+    if (rows > 0 && (!x || !aligned(x, 16) || ldx < 128 || ldx % 8 != 0))
+        return fail(QP_ERR_INVALID_ARG, "x NULL/misaligned or bad ldx");
+    if (rows > 0 && !slots) return fail(QP_ERR_INVALID_ARG, "slots NULL");
+    if (!codes || !aligned(codes, 16) || !scales || !aligned(scales, 16))
+        return fail(QP_ERR_INVALID_ARG, "codes/scales NULL or not 16-byte aligned");
+    if (rows > (1LL << 31) - 4) return fail(QP_ERR_INVALID_ARG, "too many rows");
+    KvQuantArgs a{};
+    a.x = x;
+    a.ldx = ldx;
+    a.slots = slots;
+    a.rows = rows;
+    a.total_rows = kv_rows(d);
+    a.cap = d->capacity;
+    a.codes = (uint8_t *)codes;
+    a.scales = scales;
+    const int bits = which == QKV_K ? d->k_bits : d->v_bits, g = which == QKV_K ? d->k_group : d->v_group;
+    return device(launch_kv_quantize(bits, which, g, a, S(stream)), "kv quantize");
+}
+
+size_t qattn_decode_workspace_bytes(const qkv_desc *d)
+{
+    if (check_kv(d) != QP_OK) return 0;
+    int32_t ns, ch;
+    kv_split(d->batch, d->kv_heads, d->capacity, &ns, &ch);
+    if (ns == 1) return 0;
+    const size_t parts = (size_t)d->batch * d->q_heads * ns;
+    return parts * 128 * 4 + parts * 2 * 4;
+}
+
+qp_status qattn_decode(const qkv_desc *d, const uint16_t *q, const void *k_codes, const float *k_scales,
+                       const void *v_codes, const float *v_scales, const int32_t *seq_lens, float sm_scale,
+                       uint16_t *o, void *workspace, size_t ws_bytes, void *stream)
+{
+    qp_status st;
+    if ((st = check_kv(d)) != QP_OK) return st;
+    if (!q || !aligned(q, 16) || !o || !aligned(o, 16)) return fail(QP_ERR_INVALID_ARG, "q/o NULL or not 16-byte aligned");
+    if (!k_codes || !aligned(k_codes, 16) || !v_codes || !aligned(v_codes, 16) || !k_scales ||
+        !aligned(k_scales, 16) || !v_scales || !aligned(v_scales, 16))
+        return fail(QP_ERR_INVALID_ARG, "cache codes/scales NULL or not 16-byte aligned");
+    if (!seq_lens) return fail(QP_ERR_INVALID_ARG, "seq_lens NULL");
+    if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY)
+        return fail(QP_ERR_INVALID_ARG, "sm_scale not finite");
+    const size_t need = qattn_decode_workspace_bytes(d);
+    if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 16)))
+        return fail(QP_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned)", need);
+    KvAttnArgs a{};
+    a.q = q;
+    a.kc = (const uint8_t *)k_codes;
+    a.ks = k_scales;
+    a.vc = (const uint8_t *)v_codes;
+    a.vs = v_scales;
+    a.lens = seq_lens;
+    a.o = o;
+    a.cap = d->capacity;
+    a.hq = d->q_heads;
+    a.hkv = d->kv_heads;
+    a.grp = d->q_heads / d->kv_heads;
+    kv_split(d->batch, d->kv_heads, d->capacity, &a.nsplit, &a.chunk);
+    if (a.nsplit > 1) {
+        const size_t parts = (size_t)d->batch * d->q_heads * a.nsplit;
+        a.part_o = (float *)workspace;
+        a.part_ml = (float *)((uint8_t *)workspace + parts * 128 * 4);
+    }
+    a.c = (float)((double)sm_scale * 1.4426950408889634);
+    return device(launch_kv_attn(d->k_bits, d->v_bits, d->k_group, d->v_group, d->batch, a, S(stream)),
+                  "kv attention");
 }
 
 }  // extern "C"

@@ -1,0 +1,431 @@
+// Quantized KV cache on gfx950: the write path (new K/V rows quantized into the cache) and
+// decode attention that reads the packed codes and their scales directly.
+//
+// KV-cache quantization page (kwkr.cn): s2.1 symmetric groups, scale from the absolute
+// maximum; s2.2 groups of adjacent head-dimension elements (32, 64 or 128); s2.3 K and V at
+// their own bit widths (INT4 K with INT8 V); s3.1 one FP32 scale per group; s5.1 4-bit values
+// two per byte and an attention operator that dequantizes in registers instead of writing an
+// fp16 copy of the cache.  Head dimension 128.  This file is compiled without floating-point
+// contraction so the write path is bit-identical to the CPU reference; the attention writes
+// its fused multiply-adds explicitly.
+//
+// Cache storage (values counted in the tensor's own width; a 4-bit value p is the low nibble
+// of byte p/2 when p is even):
+//   sigma(s) = s (8-bit) or s/2 + 4*(s%2) (4-bit) places slot s = 0..7 of an 8-value piece.
+//   K: row R = (b*Hkv + h)*cap + token, 128*kb/8 bytes; value d = 32j + 8t + s at
+//      32t + 8j + sigma(s).  Lane l = 16t + r of a wave reads token r's 16 (32) contiguous
+//      bytes at 16t (32t): the A operands of the four 16x16x32 matrix-core steps j.
+//   V: per (b, h), tiles of 32 tokens (32*128*vb/8 bytes); token w of a tile with
+//      w = 4t + s (s < 4) or 16 + 4t + s - 4 (s >= 4) and value d = 16c + r sit at
+//      1024t + 64r + 8c + sigma(s).  Lane (t, r) reads 64 (32) contiguous bytes: for each
+//      16-value slice c, its eight tokens at one d, the A operand of V^T.
+//   Scales: fp32 [R][128/g].
+//
+// Attention (one query token per sequence, GQA: query head h reads kv head h / (Hq/Hkv)):
+// a workgroup of four waves takes one (sequence, kv head, token chunk); each wave walks its
+// 32-token tiles with an online softmax for all query heads of the kv head at once (up to 16,
+// the matrix-core N dimension; missing heads are zero columns).
+//   scores:  S^T[token][head] = K codes (exact fp16 integers) x Q^T per group of the head
+//            dimension, each group scaled by its fp32 K scale in fp32.  Lane (t, r) receives
+//            the scores of tokens 4t+i and 16+4t+i (i = 0..3) for head r -- exactly the eight
+//            tokens it supplies to the V product below, so no value crosses lanes except the
+//            row maximum.
+//   softmax: base-2 exponent with the log2(e) factor folded into the score scale; weights
+//            exp2(z - m + 14) <= 2^14 so fp16 keeps them normal far below the maximum; the
+//            2^14 cancels in o / l.
+//   values:  O^T[d][head] += (V codes * V scale, rounded to fp16) x P^T on the matrix core.
+// The four waves' (m, l, O) are merged through LDS; with several chunks per (sequence, kv
+// head) the partial results go to the workspace and a second kernel merges them.
+#include "bufio.h"
+#include "unpack.h"
+
+namespace qp {
+
+constexpr int kD = 128;
+
+// ---- storage maps ------------------------------------------------------------------------
+
+__device__ __forceinline__ int kv_sigma(int bits, int s) { return bits == 8 ? s : s / 2 + 4 * (s % 2); }
+
+__device__ __forceinline__ int kv_k_pos(int bits, int d)
+{
+    return 32 * ((d % 32) / 8) + 8 * (d / 32) + kv_sigma(bits, d % 8);
+}
+
+__device__ __forceinline__ int kv_v_pos(int bits, int w, int d)
+{
+    const int hi = w >= 16, t = (w % 16) / 4, s = (w % 4) + 4 * hi;
+    return 1024 * t + 64 * (d % 16) + 8 * (d / 16) + kv_sigma(bits, s);
+}
+
+// ---- write path: one wave per row, lane l holds d = l and d = 64 + l ---------------------
+
+template <int BITS, int WHICH, int G>
+__global__ __launch_bounds__(256) void kv_quantize_kernel(KvQuantArgs a)
+{
+    constexpr int qmax = (1 << (BITS - 1)) - 1, mid = 1 << (BITS - 1), NG = kD / G;
+    constexpr int span = G < 64 ? G : 64;
+    __shared__ uint8_t stage[4][kD];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t row = (int64_t)blockIdx.x * 4 + wv;
+    const bool in = row < a.rows;
+    const int64_t slot = in ? a.slots[row] : -1;
+    const bool ok = in && slot >= 0 && slot < a.total_rows;
+    float v[2] = {0.f, 0.f};
+    if (ok) {
+        const uint16_t *x = a.x + row * a.ldx;
+        v[0] = h_f(x[lane]);
+        v[1] = h_f(x[64 + lane]);
+    }
+    float m[2] = {__builtin_fabsf(v[0]), __builtin_fabsf(v[1])};
+#pragma unroll
+    for (int off = span / 2; off >= 1; off >>= 1) {
+        m[0] = __builtin_fmaxf(m[0], __shfl_xor(m[0], off));
+        m[1] = __builtin_fmaxf(m[1], __shfl_xor(m[1], off));
+    }
+    if constexpr (G == 128) m[0] = m[1] = __builtin_fmaxf(m[0], m[1]);
+    uint8_t c[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const float s = m[e] / (float)qmax;
+        int q = 0;
+        if (m[e] != 0.f) {
+            q = (int)__builtin_rintf(v[e] / s);
+            q = q < -qmax ? -qmax : (q > qmax ? qmax : q);
+        }
+        c[e] = (uint8_t)(q + mid);
+        const int d = 64 * e + lane;
+        if (ok && d % G == 0) a.scales[slot * NG + d / G] = m[e] == 0.f ? 0.f : s;
+    }
+    if constexpr (WHICH == 0 && BITS == 4) {
+        // A K row's nibbles all belong to this row: gather whole bytes through LDS.
+        stage[wv][lane] = c[0];
+        stage[wv][64 + lane] = c[1];
+        __syncthreads();
+        if (ok) {
+            // byte l holds nibble positions 2l, 2l + 1; position p = 32t + 8j + sigma(s)
+            uint32_t byte = 0;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int p = 2 * lane + h, t = p / 32, j = (p % 32) / 8, sg = p % 8;
+                const int s = sg < 4 ? 2 * sg : 2 * (sg - 4) + 1;
+                byte |= (uint32_t)stage[wv][32 * j + 8 * t + s] << (4 * h);
+            }
+            a.codes[slot * (kD / 2) + lane] = (uint8_t)byte;
+        }
+    } else if (ok) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int d = 64 * e + lane;
+            int64_t pos;
+            if constexpr (WHICH == 0) {
+                pos = slot * kD + kv_k_pos(BITS, d);
+            } else {
+                const int64_t region = slot / a.cap, tau = slot % a.cap;
+                pos = (region * a.cap + (tau / 32) * 32) * kD + kv_v_pos(BITS, (int)(tau % 32), d);
+            }
+            if constexpr (BITS == 8) {
+                a.codes[pos] = c[e];
+            } else {
+                // Two tokens share each byte of a V tile: replace only this nibble.
+                uint32_t *wd = (uint32_t *)a.codes + pos / 8;
+                const int sh = 4 * (int)(pos % 8);
+                atomicAnd(wd, ~(0xFu << sh));
+                atomicOr(wd, (uint32_t)c[e] << sh);
+            }
+        }
+    }
+}
+
+template <int BITS, int WHICH>
+static hipError_t quant_g(const KvQuantArgs &a, int g, hipStream_t st)
+{
+    const dim3 grid((unsigned)((a.rows + 3) / 4)), block(256);
+    if (g == 32) hipLaunchKernelGGL((kv_quantize_kernel<BITS, WHICH, 32>), grid, block, 0, st, a);
+    else if (g == 64) hipLaunchKernelGGL((kv_quantize_kernel<BITS, WHICH, 64>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((kv_quantize_kernel<BITS, WHICH, 128>), grid, block, 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_quantize(int bits, int which, int g, const KvQuantArgs &a, hipStream_t st)
+{
+    if (a.rows == 0) return hipSuccess;
+    if (bits == 4) return which == 0 ? quant_g<4, 0>(a, g, st) : quant_g<4, 1>(a, g, st);
+    return which == 0 ? quant_g<8, 0>(a, g, st) : quant_g<8, 1>(a, g, st);
+}
+
+// ---- decode attention ---------------------------------------------------------------------
+
+// Eight offset 4-bit codes of one piece (sigma order) -> the eight signed values, slot order.
+__device__ __forceinline__ h8 unpack_nib8(uint32_t w)
+{
+    const h2 one = {(_Float16)1.0f, (_Float16)1.0f}, sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const h2 a0 = {(_Float16)-1032.0f, (_Float16)-1032.0f}, a1 = {(_Float16)-72.0f, (_Float16)-72.0f};
+    const uint32_t p0 = magic_pair<0x000F000Fu>(w, one, a0);        // slots 0, 1
+    const uint32_t p1 = magic_pair<0x00F000F0u>(w, sixteenth, a1);  // slots 2, 3
+    const uint32_t w8 = w >> 8;
+    const uint32_t p2 = magic_pair<0x000F000Fu>(w8, one, a0);       // slots 4, 5
+    const uint32_t p3 = magic_pair<0x00F000F0u>(w8, sixteenth, a1); // slots 6, 7
+    const u4 r = {p0, p1, p2, p3};
+    return __builtin_bit_cast(h8, r);
+}
+
+// Eight offset 8-bit codes (slot order) -> the eight signed values.
+__device__ __forceinline__ h8 unpack_byte8(uint32_t w0, uint32_t w1)
+{
+    const h2 a = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    const uint32_t bias = 0x64006400u;
+    u4 r;
+    r[0] = h2_bits(bits_h2((w0 & 0xFFu) | ((w0 << 8) & 0xFF0000u) | bias) + a);
+    r[1] = h2_bits(bits_h2(((w0 >> 16) & 0xFFu) | ((w0 >> 8) & 0xFF0000u) | bias) + a);
+    r[2] = h2_bits(bits_h2((w1 & 0xFFu) | ((w1 << 8) & 0xFF0000u) | bias) + a);
+    r[3] = h2_bits(bits_h2(((w1 >> 16) & 0xFFu) | ((w1 >> 8) & 0xFF0000u) | bias) + a);
+    return __builtin_bit_cast(h8, r);
+}
+
+// One 32-token tile's operands for lane (t, r).
+template <int KB, int VB, int GK, int GV>
+struct KvTile {
+    u4 k[2][KB / 4];     // token 16u + r: its 16 (32) bytes at 16t (32t)
+    u4 v[VB / 2];        // 64 (32) bytes of the V tile at 1024t + 64r (512t + 32r)
+    float ks[2][4 * GK]; // K scales of tokens 16u + 4t + i, i = 0..3 (row-major [token][group])
+    float vs[2][4 * GV]; // V scales of the same tokens
+};
+
+template <int KB, int VB, int GK, int GV>
+__device__ __forceinline__ void load_tile(KvTile<KB, VB, GK, GV> &x, rsrc_t kr, rsrc_t ksr, rsrc_t vr, rsrc_t vsr,
+                                          int T, int t, int r)
+{
+    constexpr int KRB = kD * KB / 8, VTB = 32 * kD * VB / 8;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const uint32_t ko = (uint32_t)((32 * T + 16 * u + r) * KRB + (KRB / 4) * t);
+#pragma unroll
+        for (int e = 0; e < KB / 4; ++e) x.k[u][e] = ld16(kr, ko + 16 * e);
+        const uint32_t so = (uint32_t)((32 * T + 16 * u + 4 * t) * 4);
+#pragma unroll
+        for (int e = 0; e < GK; ++e) {
+            const u4 s = ld16(ksr, so * GK + 16 * e);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x.ks[u][4 * e + i] = as_f(s[i]);
+        }
+#pragma unroll
+        for (int e = 0; e < GV; ++e) {
+            const u4 s = ld16(vsr, so * GV + 16 * e);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x.vs[u][4 * e + i] = as_f(s[i]);
+        }
+    }
+    const uint32_t vo = (uint32_t)(T * VTB + (VTB / 4) * t + (VTB / 64) * r);
+#pragma unroll
+    for (int e = 0; e < VB / 2; ++e) x.v[e] = ld16(vr, vo + 16 * e);
+}
+
+template <int KB>
+__device__ __forceinline__ h8 k_frag(const u4 (&k)[KB / 4], int j)
+{
+    if constexpr (KB == 4) return unpack_nib8(k[0][j]);
+    else return unpack_byte8(k[j / 2][(2 * j) % 4], k[j / 2][(2 * j) % 4 + 1]);
+}
+
+template <int VB>
+__device__ __forceinline__ h8 v_frag(const u4 (&v)[VB / 2], int c)
+{
+    if constexpr (VB == 4) return unpack_nib8(v[c / 4][c % 4]);
+    else return unpack_byte8(v[c / 2][(2 * c) % 4], v[c / 2][(2 * c) % 4 + 1]);
+}
+
+template <int KB, int VB, int KG, int VG>
+__global__ __launch_bounds__(256) void kv_attn_kernel(KvAttnArgs a)
+{
+    constexpr int GK = kD / KG, GV = kD / VG, KSTEP = KG / 32;
+    constexpr int KRB = kD * KB / 8, VTB = 32 * kD * VB / 8;
+    __shared__ float sm_o[4][16][kD + 1];
+    __shared__ float sm_m[4][16], sm_l[4][16];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int t = lane >> 4, r = lane & 15;
+    const int b = blockIdx.z, hk = blockIdx.y, sp = blockIdx.x;
+    int L = a.lens[b];
+    L = L < 0 ? 0 : (L > a.cap ? (int)a.cap : L);
+    const int t0 = sp * a.chunk, t1 = t0 + a.chunk < L ? t0 + a.chunk : L;
+    const int64_t R0 = ((int64_t)b * a.hkv + hk) * a.cap;
+    const rsrc_t kr = make_rsrc(a.kc + R0 * KRB, (int64_t)L * KRB);
+    const rsrc_t ksr = make_rsrc(a.ks + R0 * GK, (int64_t)L * GK * 4);
+    const rsrc_t vr = make_rsrc(a.vc + R0 * (kD * VB / 8), (int64_t)((L + 31) / 32) * VTB);
+    const rsrc_t vsr = make_rsrc(a.vs + R0 * GV, (int64_t)L * GV * 4);
+
+    // B operand of the score product: head r's values d = 32j + 8t + s (zero past the group)
+    h8 Q[4];
+    const int64_t qrow = (int64_t)b * a.hq + (int64_t)hk * a.grp + r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (r < a.grp) Q[j] = *(const h8 *)(a.q + qrow * kD + 32 * j + 8 * t);
+        else Q[j] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
+    }
+
+    float m = -__builtin_inff(), l = 0.f;
+    f4 O[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) O[c] = (f4){0.f, 0.f, 0.f, 0.f};
+
+    int T = t0 / 32 + wv;
+    KvTile<KB, VB, GK, GV> cur, nxt;
+    if (32 * T < t1) load_tile(cur, kr, ksr, vr, vsr, T, t, r);
+    for (; 32 * T < t1; T += 4) {
+        if (32 * (T + 4) < t1) load_tile(nxt, kr, ksr, vr, vsr, T + 4, t, r);
+        // scores of tokens 32T + 16u + 4t + i for head r, already in base-2 units
+        float z[2][4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            f4 zt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int gi = 0; gi < GK; ++gi) {
+                f4 acc = mfma16(k_frag<KB>(cur.k[u], KSTEP * gi), Q[KSTEP * gi], (f4){0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                for (int jj = 1; jj < KSTEP; ++jj)
+                    acc = mfma16(k_frag<KB>(cur.k[u], KSTEP * gi + jj), Q[KSTEP * gi + jj], acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) zt[i] = __builtin_fmaf(cur.ks[u][GK * i + gi], acc[i], zt[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tok = 32 * T + 16 * u + 4 * t + i;
+                z[u][i] = tok < t1 ? zt[i] * a.c : -__builtin_inff();
+            }
+        }
+        float mt = z[0][0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mt = __builtin_fmaxf(mt, z[e / 4][e % 4]);
+        mt = __builtin_fmaxf(mt, __shfl_xor(mt, 16));
+        mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32));
+        const float mn = __builtin_fmaxf(m, mt);  // finite: token 32T < t1 is in every tile
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        m = mn;
+        const float base = mn - 14.0f;
+        float p[8], ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(z[e / 4][e % 4] - base);
+            ps += p[e];
+        }
+        l = __builtin_fmaf(l, alpha, ps);
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) O[c] *= alpha;
+        }
+        const u4 pw = {pack_h2(p[0], p[1]), pack_h2(p[2], p[3]), pack_h2(p[4], p[5]), pack_h2(p[6], p[7])};
+        const h8 P = __builtin_bit_cast(h8, pw);
+        // V scales per slot as fp16, one set per V group
+        h8 vsh[GV];
+#pragma unroll
+        for (int gi = 0; gi < GV; ++gi) {
+            const u4 w = {pack_h2(cur.vs[0][GV * 0 + gi], cur.vs[0][GV * 1 + gi]),
+                          pack_h2(cur.vs[0][GV * 2 + gi], cur.vs[0][GV * 3 + gi]),
+                          pack_h2(cur.vs[1][GV * 0 + gi], cur.vs[1][GV * 1 + gi]),
+                          pack_h2(cur.vs[1][GV * 2 + gi], cur.vs[1][GV * 3 + gi])};
+            vsh[gi] = __builtin_bit_cast(h8, w);
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const h8 vq = v_frag<VB>(cur.v, c) * vsh[(16 * c) / VG];
+            O[c] = mfma16(vq, P, O[c]);
+        }
+        if (32 * (T + 4) < t1) cur = nxt;
+    }
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm_o[wv][r][16 * c + 4 * t + i] = O[c][i];
+    if (t == 0) {
+        sm_m[wv][r] = m;
+        sm_l[wv][r] = l;
+    }
+    __syncthreads();
+    const int64_t bh0 = (int64_t)b * a.hq + (int64_t)hk * a.grp;
+    for (int idx = threadIdx.x; idx < a.grp * kD; idx += 256) {
+        const int h = idx / kD, d = idx % kD;
+        float M = sm_m[0][h];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) M = __builtin_fmaxf(M, sm_m[w][h]);
+        float o = 0.f, S = 0.f;
+        if (M != -__builtin_inff()) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float e = __builtin_amdgcn_exp2f(sm_m[w][h] - M);
+                o = __builtin_fmaf(e, sm_o[w][h][d], o);
+                S = __builtin_fmaf(e, sm_l[w][h], S);
+            }
+        }
+        if (a.nsplit == 1) {
+            const float y = S > 0.f ? o / S : 0.f;
+            a.o[(bh0 + h) * kD + d] = __builtin_bit_cast(uint16_t, (_Float16)y);
+        } else {
+            const int64_t pi = (bh0 + h) * a.nsplit + sp;
+            a.part_o[pi * kD + d] = o;
+            if (d == 0) {
+                a.part_ml[2 * pi] = M;
+                a.part_ml[2 * pi + 1] = S;
+            }
+        }
+    }
+}
+
+// Merge the chunks of one (sequence, query head): one thread per d.
+__global__ __launch_bounds__(128) void kv_combine_kernel(KvAttnArgs a)
+{
+    const int64_t bh = blockIdx.x;
+    const int d = threadIdx.x;
+    float M = -__builtin_inff();
+    for (int s = 0; s < a.nsplit; ++s) M = __builtin_fmaxf(M, a.part_ml[2 * (bh * a.nsplit + s)]);
+    float o = 0.f, S = 0.f;
+    if (M != -__builtin_inff()) {
+        for (int s = 0; s < a.nsplit; ++s) {
+            const int64_t pi = bh * a.nsplit + s;
+            const float e = __builtin_amdgcn_exp2f(a.part_ml[2 * pi] - M);
+            o = __builtin_fmaf(e, a.part_o[pi * kD + d], o);
+            S = __builtin_fmaf(e, a.part_ml[2 * pi + 1], S);
+        }
+    }
+    const float y = S > 0.f ? o / S : 0.f;
+    a.o[bh * kD + d] = __builtin_bit_cast(uint16_t, (_Float16)y);
+}
+
+template <int KB, int VB>
+static hipError_t attn_kv(const KvAttnArgs &a, int kg, int vg, dim3 grid, hipStream_t st)
+{
+#define QP_KV_ATTN(KG, VG) \
+    if (kg == KG && vg == VG) { hipLaunchKernelGGL((kv_attn_kernel<KB, VB, KG, VG>), grid, dim3(256), 0, st, a); return hipGetLastError(); }
+    QP_KV_ATTN(32, 32) QP_KV_ATTN(32, 64) QP_KV_ATTN(32, 128)
+    QP_KV_ATTN(64, 32) QP_KV_ATTN(64, 64) QP_KV_ATTN(64, 128)
+    QP_KV_ATTN(128, 32) QP_KV_ATTN(128, 64) QP_KV_ATTN(128, 128)
+#undef QP_KV_ATTN
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_kv_attn(int kb, int vb, int kg, int vg, int64_t batch, const KvAttnArgs &a, hipStream_t st)
+{
+    const dim3 grid((unsigned)a.nsplit, (unsigned)a.hkv, (unsigned)batch);
+    hipError_t e;
+    if (kb == 4) e = vb == 4 ? attn_kv<4, 4>(a, kg, vg, grid, st) : attn_kv<4, 8>(a, kg, vg, grid, st);
+    else e = vb == 4 ? attn_kv<8, 4>(a, kg, vg, grid, st) : attn_kv<8, 8>(a, kg, vg, grid, st);
+    if (e != hipSuccess || a.nsplit == 1) return e;
+    hipLaunchKernelGGL(kv_combine_kernel, dim3((unsigned)(batch * a.hq)), dim3(kD), 0, st, a);
+    return hipGetLastError();
+}
+
+// Chunks per (sequence, kv head): enough workgroups to fill the GPU about four times over,
+// each chunk a multiple of 128 tokens (one tile per wave at least).
+void kv_split(int64_t batch, int64_t hkv, int64_t cap, int32_t *nsplit, int32_t *chunk)
+{
+    const int64_t want = (1024 + batch * hkv - 1) / (batch * hkv);
+    const int64_t maxs = (cap + 127) / 128;
+    int64_t ns = want < 1 ? 1 : (want > maxs ? maxs : want);
+    int64_t ch = ((cap + ns - 1) / ns + 127) / 128 * 128;
+    ns = (cap + ch - 1) / ch;
+    *nsplit = (int32_t)ns;
+    *chunk = (int32_t)ch;
+}
+
+}  // namespace qp

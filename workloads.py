@@ -13,7 +13,11 @@ Recipe (numpy PCG64 via ``numpy.random.default_rng``):
   * MoE routing: expert popularity p_r proportional to r^-s (Zipf), router logits
     log(p) + Gumbel(0, 1) per token, top-k by logit, combine weights = softmax of the
     logits taken at the chosen experts (not renormalised).
-Seeds: 1000*config + 16*layer + matrix_index; activations use seed + 500000.
+  * KV cache: K and V head vectors (head_dim 128) ~ N(0, 1) rounded to fp16 -- the KV page
+    (s1.2) describes projected K/V as concentrated without extreme outliers; queries ~ N(0, 1);
+    sequence lengths uniform in [lo, hi] for ragged batches.
+Seeds: 1000*config + 16*layer + matrix_index; activations use seed + 500000.  The KV cache
+is config 6 (matrix 0 = K, 1 = V; queries and lengths use the activation offset).
 """
 from __future__ import annotations
 
@@ -119,6 +123,28 @@ PREFILL_OUTLIER_FRAC = 0.001
 
 # MoE grouped experts (configuration 5).
 MOE_EXPERTS, MOE_DMODEL, MOE_DFF, MOE_TOKENS, MOE_TOPK, MOE_ZIPF = 16, 4096, 14336, 128, 2, 1.1
+
+
+# Quantized KV-cache decode (config 6): the KV page's 7B MHA layer (32 heads x 128) at a 32K
+# context, and a GQA layer (8 KV heads, 8 query heads each) with four sequences of 8K.
+KV_HEAD_DIM = 128
+KV_MHA = dict(batch=1, q_heads=32, kv_heads=32, capacity=32768)
+KV_GQA = dict(batch=4, q_heads=64, kv_heads=8, capacity=8192)
+
+
+def kv_rows(rows: int, seed: int) -> np.ndarray:
+    """rows head vectors [rows, 128] ~ N(0, 1), fp16 (K or V of cache rows 0 .. rows-1)."""
+    return normal_fp16((rows, KV_HEAD_DIM), seed)
+
+
+def kv_queries(batch: int, q_heads: int, seed: int) -> np.ndarray:
+    return normal_fp16((batch, q_heads, KV_HEAD_DIM), seed + ACT_SEED_OFFSET)
+
+
+def kv_lengths(batch: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """Ragged sequence lengths, uniform integers in [lo, hi]."""
+    rng = np.random.default_rng(seed + ACT_SEED_OFFSET + 1)
+    return rng.integers(lo, hi + 1, size=batch).astype(np.int32)
 
 
 def stack_bits(layer: int, name: str) -> int:
