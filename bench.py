@@ -20,6 +20,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -280,6 +281,64 @@ def bench_moe(q, torch, workloads, stream, reps: int = 20):
                 TFLOPs=round(flops / (ms * 1e-3) / 1e12, 2), active_experts=active, weight_bytes=wbytes)
 
 
+def kv_call_bytes(q, d, lens) -> int:
+    """Algorithmic bytes of one decode-attention call: the K and V codes and fp32 scales of the
+    first lens[b] tokens of every (sequence, kv head); queries and outputs (a few KB) left out."""
+    per_tok = (128 * d.k_bits // 8 + 4 * (128 // d.k_group) + 128 * d.v_bits // 8 + 4 * (128 // d.v_group))
+    return int(sum(int(L) for L in lens)) * d.kv_heads * per_tok
+
+
+def bench_kv(q, torch, workloads, stream, min_bytes: int = 1 << 30):
+    """Decode attention over the quantized KV cache (INT4 K, INT8 V, groups of 64, fp32
+    scales): the KV page's 7B MHA layer at a 32K context and a GQA layer with four 8K
+    sequences.  Each layer's cache is quantized once through qkv_quantize; the timed graph
+    rotates over enough distinct layer caches (>= 1 GiB) that the cache streams from HBM."""
+    out = {}
+    for name in ("KV_MHA", "KV_GQA"):
+        cfg = getattr(workloads, name)
+        d = q.kv_desc(cfg["batch"], cfg["q_heads"], cfg["kv_heads"], cfg["capacity"], 4, 8, 64, 64)
+        rows = cfg["batch"] * cfg["kv_heads"] * cfg["capacity"]
+        lens = np.full(cfg["batch"], cfg["capacity"], np.int32)
+        nbytes = kv_call_bytes(q, d, lens)
+        layers = max(2, -(-min_bytes // nbytes))
+        slots = torch.arange(rows, dtype=torch.int64, device="cuda")
+        caches = []
+        for layer in range(layers):
+            c = {}
+            for w in (q.QKV_K, q.QKV_V):
+                if layer == 0:
+                    x = torch.from_numpy(workloads.kv_rows(rows, workloads.seed_for(6, 0, w)).view(np.int16)).cuda()
+                    c[w] = (torch.empty(q.qkv_cache_bytes(d, w), dtype=torch.uint8, device="cuda"),
+                            torch.empty(q.qkv_scale_count(d, w), dtype=torch.float32, device="cuda"))
+                    q.qkv_quantize(d, w, x, 128, slots, rows, c[w][0], c[w][1])
+                    del x
+                else:
+                    c[w] = (caches[0][w][0].clone(), caches[0][w][1].clone())
+            caches.append(c)
+        qv = torch.from_numpy(workloads.kv_queries(cfg["batch"], cfg["q_heads"], workloads.seed_for(6) + 2)
+                              .view(np.int16)).cuda()
+        ln = torch.from_numpy(lens).cuda()
+        o = torch.empty((cfg["batch"], cfg["q_heads"], 128), dtype=torch.int16, device="cuda")
+        wsb = q.qattn_decode_workspace_bytes(d)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+        sm = 1.0 / math.sqrt(128)
+
+        def call(i):
+            c = caches[i % layers]
+            q.qattn_decode(d, qv, c[q.QKV_K][0], c[q.QKV_K][1], c[q.QKV_V][0], c[q.QKV_V][1], ln, sm, o, ws, wsb)
+
+        ms = time_graph(torch, call, 2 * layers, stream)
+        flops = 4 * int(lens.sum()) * cfg["q_heads"] * 128
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out[name.lower()] = dict(us=round(ms * 1e3, 2), GBps=round(gbps, 1), frac_hbm_peak=round(gbps / HBM_PEAK_GBS, 4),
+                                 TFLOPs=round(flops / (ms * 1e-3) / 1e12, 2), bytes=nbytes, layers_rotated=layers,
+                                 shape=dict(batch=cfg["batch"], q_heads=cfg["q_heads"], kv_heads=cfg["kv_heads"],
+                                            tokens=cfg["capacity"], k_bits=4, v_bits=8, group=64),
+                                 kernel=f"qp::kv_attn_kernel<4, 8, 64, 64>")
+        del caches, o, ws
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,6 +349,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=512 GEMM secondary line")
     ap.add_argument("--no-stack", action="store_true", help="skip the 32-layer decode stack line")
     ap.add_argument("--no-moe", action="store_true", help="skip the routed-expert FFN line")
+    ap.add_argument("--no-kv", action="store_true", help="skip the quantized-KV decode attention line")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--pmc-pass", action="store_true",
                     help="eager launches only (each GEMV of the step, the prefill GEMM, a 1 GiB copy) for "
@@ -448,6 +508,9 @@ def main():
     if not args.no_moe:
         log("bench: routed-expert FFN, 16 experts, 128 tokens top-2")
         extra["moe_16x_ffn_t128"] = bench_moe(q, torch, workloads, stream)
+    if not args.no_kv:
+        log("bench: decode attention over an INT4-K / INT8-V cache (32K MHA, 4 x 8K GQA)")
+        extra["kv_decode_attention"] = bench_kv(q, torch, workloads, stream)
 
     log("bench: 1 GiB device copy")
     extra["copy_GBps"] = round(copy_gbps(torch), 1)
