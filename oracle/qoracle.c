@@ -581,8 +581,10 @@ void or_kv_quantize_rows(const uint16_t *x, int64_t rows, int g, int bits, uint8
  *  (4-bit: the two values of a pair are four nibbles apart).
  *  K row (one token, head_dim 128): value d = 32j + 8t + s sits at 32t + 8j + sigma(s).
  *  V tile (32 tokens x 128, tile u holds tokens 32u .. 32u+31 of one head): token
- *  tau = 32u + w and value d = 16c + r sit at 1024t + 64r + 8c + sigma(s), where
- *  w = 4t + s (s < 4) or 16 + 4t + (s - 4) (s >= 4). */
+ *  tau = 32u + w and value d = 16c + r, with w = 4t + s (s < 4) or 16 + 4t + (s - 4)
+ *  (s >= 4), belong to lane l = 16t + r, slice c, slot s.  A lane's eight 8-value slices
+ *  fill its pieces of P = 128/b values (P/8 slices each), and piece e of lane l sits at
+ *  64*P*e + P*l: value position 64*P*(c / (P/8)) + P*l + 8*(c % (P/8)) + sigma(s). */
 static int kv_sigma(int bits, int s) { return bits == 8 ? s : s / 2 + 4 * (s % 2); }
 
 int64_t or_kv_k_pos(int bits, int d)
@@ -594,8 +596,9 @@ int64_t or_kv_k_pos(int bits, int d)
 int64_t or_kv_v_pos(int bits, int w, int d)
 {
     const int hi = w >= 16, t = ((w % 16) / 4), s = (w % 4) + 4 * hi;
-    const int c = d / 16, r = d % 16;
-    return 1024 * t + 64 * r + 8 * c + kv_sigma(bits, s);
+    const int c = d / 16, r = d % 16, l = 16 * t + r;
+    const int P = 128 / bits, spp = P / 8;
+    return 64 * P * (c / spp) + P * l + 8 * (c % spp) + kv_sigma(bits, s);
 }
 
 static void put_value(uint8_t *base, int bits, int64_t pos, uint8_t v)

@@ -135,12 +135,21 @@ def test_v_layout_bijection_and_locality(bits):
     pos = {(w, d): oracle.kv_v_pos(bits, w, d) for w in range(32) for d in range(D)}
     assert sorted(pos.values()) == list(range(32 * D))
     tau = lambda t, s: 4 * t + s if s < 4 else 16 + 4 * t + (s - 4)
+    P = 128 // bits  # values per 16-byte piece
     for t in range(4):
         for r in range(16):
+            lane = 16 * t + r
             for c in range(8):
+                # lane (t, r), slice c: its eight tokens at d = 16c + r fill 8 consecutive slots
                 got = sorted(pos[(tau(t, s), 16 * c + r)] for s in range(8))
-                base = 1024 * t + 64 * r + 8 * c
+                e = c // (P // 8)
+                base = 64 * P * e + P * lane + 8 * (c % (P // 8))
                 assert got == list(range(base, base + 8))
+    # piece e of every lane: the 64 lanes' pieces tile one contiguous 1 KB block
+    for e in range(bits // 2):
+        lanes = sorted(min(pos[(tau(t, s), 16 * c + r)] for s in range(8) for c in range(8)
+                           if c // (P // 8) == e) for t in range(4) for r in range(16))
+        assert lanes == [64 * P * e + P * l for l in range(64)]
 
 
 @pytest.mark.parametrize("which", [0, 1])
