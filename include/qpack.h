@@ -297,7 +297,7 @@ qp_status qmoe_ffn(const qp_weight_desc *desc_gu, const qp_weight *gate_up,
  *   K  row R holds 128*k_bits/8 bytes; value d = 32j + 8t + s sits at 32t + 8j + sigma(s).
  *   V  each (b, h) holds capacity/32 tiles of 32 tokens (32*128*v_bits/8 bytes each); token
  *      w of a tile, w = 4t + s (s < 4) or 16 + 4t + s - 4 (s >= 4), value d = 16c + r, sits
- *      at 1024t + 64r + 8c + sigma(s).
+ *      at 64*P*(c/(P/8)) + P*(16t + r) + 8*(c%(P/8)) + sigma(s), P = 128/v_bits.
  *   Scales: fp32 [rows][128/group].
  * These orders put every operand of the attention's 16x16x32 matrix-core steps in one
  * contiguous 16-64 byte piece per lane.

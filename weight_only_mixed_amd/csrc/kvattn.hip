@@ -16,9 +16,10 @@
 //      32t + 8j + sigma(s).  Lane l = 16t + r of a wave reads token r's 16 (32) contiguous
 //      bytes at 16t (32t): the A operands of the four 16x16x32 matrix-core steps j.
 //   V: per (b, h), tiles of 32 tokens (32*128*vb/8 bytes); token w of a tile with
-//      w = 4t + s (s < 4) or 16 + 4t + s - 4 (s >= 4) and value d = 16c + r sit at
-//      1024t + 64r + 8c + sigma(s).  Lane (t, r) reads 64 (32) contiguous bytes: for each
-//      16-value slice c, its eight tokens at one d, the A operand of V^T.
+//      w = 4t + s (s < 4) or 16 + 4t + s - 4 (s >= 4) and value d = 16c + r belong to lane
+//      l = 16t + r, slice c (its eight tokens at one d: the A operand of V^T), slot s.  The
+//      lane's slices fill 16-byte pieces of P = 128/vb values, and piece e of lane l sits at
+//      64*P*e + P*l, so each of the tile's 16-byte fetches reads 1 KB contiguous.
 //   Scales: fp32 [R][128/g].
 //
 // Attention (one query token per sequence, GQA: query head h reads kv head h / (Hq/Hkv)):
@@ -55,7 +56,8 @@ __device__ __forceinline__ int kv_k_pos(int bits, int d)
 __device__ __forceinline__ int kv_v_pos(int bits, int w, int d)
 {
     const int hi = w >= 16, t = (w % 16) / 4, s = (w % 4) + 4 * hi;
-    return 1024 * t + 64 * (d % 16) + 8 * (d / 16) + kv_sigma(bits, s);
+    const int c = d / 16, l = 16 * t + d % 16, P = 128 / bits, spp = P / 8;
+    return 64 * P * (c / spp) + P * l + 8 * (c % spp) + kv_sigma(bits, s);
 }
 
 // ---- write path: one wave per row, lane l holds d = l and d = 64 + l ---------------------
@@ -170,55 +172,81 @@ __device__ __forceinline__ h8 unpack_nib8(uint32_t w)
     return __builtin_bit_cast(h8, r);
 }
 
-// Eight offset 8-bit codes (slot order) -> the eight signed values.
+// Eight offset 8-bit codes (slot order) -> the eight signed values.  v_perm_b32 places code
+// bytes under the 0x64 exponent byte (1024 + code in each half) in one step per pair.
 __device__ __forceinline__ h8 unpack_byte8(uint32_t w0, uint32_t w1)
 {
     const h2 a = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-    const uint32_t bias = 0x64006400u;
+    const uint32_t hi = 0x64646464u;
     u4 r;
-    r[0] = h2_bits(bits_h2((w0 & 0xFFu) | ((w0 << 8) & 0xFF0000u) | bias) + a);
-    r[1] = h2_bits(bits_h2(((w0 >> 16) & 0xFFu) | ((w0 >> 8) & 0xFF0000u) | bias) + a);
-    r[2] = h2_bits(bits_h2((w1 & 0xFFu) | ((w1 << 8) & 0xFF0000u) | bias) + a);
-    r[3] = h2_bits(bits_h2(((w1 >> 16) & 0xFFu) | ((w1 >> 8) & 0xFF0000u) | bias) + a);
+    r[0] = h2_bits(bits_h2(__builtin_amdgcn_perm(hi, w0, 0x04010400u)) + a);  // bytes 0, 1
+    r[1] = h2_bits(bits_h2(__builtin_amdgcn_perm(hi, w0, 0x04030402u)) + a);  // bytes 2, 3
+    r[2] = h2_bits(bits_h2(__builtin_amdgcn_perm(hi, w1, 0x04010400u)) + a);
+    r[3] = h2_bits(bits_h2(__builtin_amdgcn_perm(hi, w1, 0x04030402u)) + a);
     return __builtin_bit_cast(h8, r);
 }
 
-// One 32-token tile's operands for lane (t, r).
+// A wave's ring slot: one 32-token tile.  Code pieces are fetched by 16-byte buffer-to-LDS
+// DMA, lane l's piece landing at 16*l of a 1 KB block, so each lane later reads back exactly
+// the bytes it fetched; the tile's fp32 K and V scales (token-major, 32*G floats) come by
+// 4-byte DMA.  Bytes in flight cost no registers, so a wave keeps D-1 tiles in flight.
 template <int KB, int VB, int GK, int GV>
-struct KvTile {
-    u4 k[2][KB / 4];     // token 16u + r: its 16 (32) bytes at 16t (32t)
-    u4 v[VB / 2];        // 64 (32) bytes of the V tile at 1024t + 64r (512t + 32r)
-    float ks[2][4 * GK]; // K scales of tokens 16u + 4t + i, i = 0..3 (row-major [token][group])
-    float vs[2][4 * GV]; // V scales of the same tokens
+struct KvSlot {
+    static constexpr int kK = 0;                        // K: u = 0, 1 (16 tokens each) x KB/4 blocks
+    static constexpr int kV = kK + 1024 * (KB / 2);     // V: VB/2 blocks
+    static constexpr int kKsOps = GK > 2 ? GK / 2 : 1;  // 256-byte DMAs of K scales
+    static constexpr int kVsOps = GV > 2 ? GV / 2 : 1;
+    static constexpr int kKs = kV + 1024 * (VB / 2);
+    static constexpr int kVs = kKs + 256 * kKsOps;
+    static constexpr int kBytes = kVs + 256 * kVsOps;
+    static constexpr int kLoads = KB / 2 + VB / 2 + kKsOps + kVsOps;  // DMA instructions per tile
 };
 
-template <int KB, int VB, int GK, int GV>
-__device__ __forceinline__ void load_tile(KvTile<KB, VB, GK, GV> &x, rsrc_t kr, rsrc_t ksr, rsrc_t vr, rsrc_t vsr,
-                                          int T, int t, int r)
+constexpr int kKvWaves = 4, kKvDepth = 3;
+
+struct KvBufs {
+    rsrc_t k, ks, v, vs;
+};
+
+__device__ __forceinline__ void kv_dma16(rsrc_t r, uint8_t *lds, uint32_t voff)
 {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void kv_dma4(rsrc_t r, uint8_t *lds, uint32_t voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, voff, 0, 0, 0);
+}
+
+// Fetch tile T into a slot.  Tiles past the sequence read zeros (buffer range) and tiles past
+// the wave's share are fetched but never read, so every step issues the same DMA count.
+template <int KB, int VB, int GK, int GV>
+__device__ __forceinline__ void kv_issue(const KvBufs &bf, int T, int lane, uint8_t *slot)
+{
+    using S = KvSlot<KB, VB, GK, GV>;
     constexpr int KRB = kD * KB / 8, VTB = 32 * kD * VB / 8;
+    const int t = lane >> 4, r = lane & 15;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const uint32_t ko = (uint32_t)((32 * T + 16 * u + r) * KRB + (KRB / 4) * t);
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int e = 0; e < KB / 4; ++e) x.k[u][e] = ld16(kr, ko + 16 * e);
-        const uint32_t so = (uint32_t)((32 * T + 16 * u + 4 * t) * 4);
+        for (int e = 0; e < KB / 4; ++e)
+            kv_dma16(bf.k, slot + S::kK + 1024 * (u * (KB / 4) + e),
+                     (uint32_t)((32 * T + 16 * u + r) * KRB + (KRB / 4) * t + 16 * e));
 #pragma unroll
-        for (int e = 0; e < GK; ++e) {
-            const u4 s = ld16(ksr, so * GK + 16 * e);
+    for (int e = 0; e < VB / 2; ++e)
+        kv_dma16(bf.v, slot + S::kV + 1024 * e, (uint32_t)(T * VTB + 1024 * e + 16 * lane));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x.ks[u][4 * e + i] = as_f(s[i]);
-        }
+    for (int e = 0; e < S::kKsOps; ++e)
+        kv_dma4(bf.ks, slot + S::kKs + 256 * e, (uint32_t)(32 * T * GK * 4 + 256 * e + 4 * lane));
 #pragma unroll
-        for (int e = 0; e < GV; ++e) {
-            const u4 s = ld16(vsr, so * GV + 16 * e);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x.vs[u][4 * e + i] = as_f(s[i]);
-        }
-    }
-    const uint32_t vo = (uint32_t)(T * VTB + (VTB / 4) * t + (VTB / 64) * r);
-#pragma unroll
-    for (int e = 0; e < VB / 2; ++e) x.v[e] = ld16(vr, vo + 16 * e);
+    for (int e = 0; e < S::kVsOps; ++e)
+        kv_dma4(bf.vs, slot + S::kVs + 256 * e, (uint32_t)(32 * T * GV * 4 + 256 * e + 4 * lane));
+}
+
+template <int N>
+__device__ __forceinline__ void kv_wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 template <int KB>
@@ -235,24 +263,151 @@ __device__ __forceinline__ h8 v_frag(const u4 (&v)[VB / 2], int c)
     else return unpack_byte8(v[c / 2][(2 * c) % 4], v[c / 2][(2 * c) % 4 + 1]);
 }
 
+// Online-softmax state of a wave: running maximum m (base 2, shared by the four lanes of a
+// head), the lane's share l of the weight sum, and O^T (lane (t, r): d = 16c + 4t + i, head r).
+struct KvState {
+    float m, l;
+    f4 O[8];
+};
+
+// Consume tile T from a slot: scores, softmax update, values.
 template <int KB, int VB, int KG, int VG>
-__global__ __launch_bounds__(256) void kv_attn_kernel(KvAttnArgs a)
+__device__ __forceinline__ void kv_tile(const uint8_t *slot, int T, int t1, const h8 (&Q)[4], float c, int lane,
+                                        KvState &st)
 {
     constexpr int GK = kD / KG, GV = kD / VG, KSTEP = KG / 32;
+    using S = KvSlot<KB, VB, GK, GV>;
+    const int t = lane >> 4;
+    u4 kd[2][KB / 4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < KB / 4; ++e) kd[u][e] = *(const u4 *)(slot + S::kK + 1024 * (u * (KB / 4) + e) + 16 * lane);
+    u4 vd[VB / 2];
+#pragma unroll
+    for (int e = 0; e < VB / 2; ++e) vd[e] = *(const u4 *)(slot + S::kV + 1024 * e + 16 * lane);
+    float ks[2][4 * GK], vs[2][4 * GV];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int e = 0; e < GK; ++e) {
+            const u4 v = *(const u4 *)(slot + S::kKs + ((16 * u + 4 * t) * GK + 4 * e) * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ks[u][4 * e + i] = as_f(v[i]);
+        }
+#pragma unroll
+        for (int e = 0; e < GV; ++e) {
+            const u4 v = *(const u4 *)(slot + S::kVs + ((16 * u + 4 * t) * GV + 4 * e) * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vs[u][4 * e + i] = as_f(v[i]);
+        }
+    }
+    // scores of tokens 32T + 16u + 4t + i for head r, in base-2 units
+    float z[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        f4 zt = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int gi = 0; gi < GK; ++gi) {
+            f4 acc = mfma16(k_frag<KB>(kd[u], KSTEP * gi), Q[KSTEP * gi], (f4){0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int jj = 1; jj < KSTEP; ++jj) acc = mfma16(k_frag<KB>(kd[u], KSTEP * gi + jj), Q[KSTEP * gi + jj], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) zt[i] = __builtin_fmaf(ks[u][GK * i + gi], acc[i], zt[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[u][i] = zt[i] * c;
+    }
+    if (32 * T + 32 > t1) {  // the sequence or chunk ends inside this tile (wave-uniform)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (32 * T + 16 * (e / 4) + 4 * t + e % 4 >= t1) z[e / 4][e % 4] = -__builtin_inff();
+    }
+    float mt = z[0][0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mt = __builtin_fmaxf(mt, z[e / 4][e % 4]);
+    mt = __builtin_fmaxf(mt, __shfl_xor(mt, 16));
+    mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = __builtin_fmaxf(st.m, mt);  // finite: token 32T < t1 is in every tile
+    const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
+    st.m = mn;
+    const float base = mn - 14.0f;
+    float p[8], ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(z[e / 4][e % 4] - base);
+        ps += p[e];
+    }
+    st.l = __builtin_fmaf(st.l, alpha, ps);
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) st.O[cc] *= alpha;
+    }
+    const u4 pw = {pack_h2(p[0], p[1]), pack_h2(p[2], p[3]), pack_h2(p[4], p[5]), pack_h2(p[6], p[7])};
+    const h8 P = __builtin_bit_cast(h8, pw);
+    h8 vsh[GV];
+#pragma unroll
+    for (int gi = 0; gi < GV; ++gi) {
+        const u4 w = {pack_h2(vs[0][GV * 0 + gi], vs[0][GV * 1 + gi]), pack_h2(vs[0][GV * 2 + gi], vs[0][GV * 3 + gi]),
+                      pack_h2(vs[1][GV * 0 + gi], vs[1][GV * 1 + gi]), pack_h2(vs[1][GV * 2 + gi], vs[1][GV * 3 + gi])};
+        vsh[gi] = __builtin_bit_cast(h8, w);
+    }
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+        const h8 vq = v_frag<VB>(vd, cc) * vsh[(16 * cc) / VG];
+        st.O[cc] = mfma16(vq, P, st.O[cc]);
+    }
+}
+
+// A wave's tiles i = 0 .. nt-1 (tile T0 + i*kKvWaves) through its three ring slots.  The
+// slots are restrict pointers and the loop is unrolled by three, so every slot access names a
+// slot statically and the compiler never waits for a DMA in flight into another slot.
+template <int KB, int VB, int KG, int VG>
+__device__ __forceinline__ void kv_loop(const KvBufs &bf, uint8_t *__restrict__ s0, uint8_t *__restrict__ s1,
+                                        uint8_t *__restrict__ s2, int T0, int nt, int t1, const h8 (&Q)[4], float c,
+                                        int lane, KvState &st)
+{
+    constexpr int GK = kD / KG, GV = kD / VG, W = kKvWaves;
+    using S = KvSlot<KB, VB, GK, GV>;
+    kv_issue<KB, VB, GK, GV>(bf, T0, lane, s0);
+    kv_issue<KB, VB, GK, GV>(bf, T0 + W, lane, s1);
+    for (int i = 0; i < nt; i += 3) {
+        kv_issue<KB, VB, GK, GV>(bf, T0 + W * (i + 2), lane, s2);
+        kv_wait_vm<2 * S::kLoads>();
+        kv_tile<KB, VB, KG, VG>(s0, T0 + W * i, t1, Q, c, lane, st);
+        if (i + 1 >= nt) break;
+        kv_issue<KB, VB, GK, GV>(bf, T0 + W * (i + 3), lane, s0);
+        kv_wait_vm<2 * S::kLoads>();
+        kv_tile<KB, VB, KG, VG>(s1, T0 + W * (i + 1), t1, Q, c, lane, st);
+        if (i + 2 >= nt) break;
+        kv_issue<KB, VB, GK, GV>(bf, T0 + W * (i + 4), lane, s1);
+        kv_wait_vm<2 * S::kLoads>();
+        kv_tile<KB, VB, KG, VG>(s2, T0 + W * (i + 2), t1, Q, c, lane, st);
+    }
+    kv_wait_vm<0>();  // drain the fetches past the end before the LDS is reused
+}
+
+template <int KB, int VB, int KG, int VG>
+__global__ __launch_bounds__(kKvWaves * 64) void kv_attn_kernel(KvAttnArgs a)
+{
+    constexpr int GK = kD / KG, GV = kD / VG, W = kKvWaves;
     constexpr int KRB = kD * KB / 8, VTB = 32 * kD * VB / 8;
-    __shared__ float sm_o[4][16][kD + 1];
-    __shared__ float sm_m[4][16], sm_l[4][16];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    constexpr int pitch = KvSlot<KB, VB, GK, GV>::kBytes;
+    constexpr int ring_bytes = kKvDepth * W * pitch, merge_bytes = W * 16 * (kD + 1) * 4;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[ring_bytes > merge_bytes ? ring_bytes : merge_bytes];
+    __shared__ float sm_m[W][16], sm_l[W][16];
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t = lane >> 4, r = lane & 15;
     const int b = blockIdx.z, hk = blockIdx.y, sp = blockIdx.x;
     int L = a.lens[b];
     L = L < 0 ? 0 : (L > a.cap ? (int)a.cap : L);
     const int t0 = sp * a.chunk, t1 = t0 + a.chunk < L ? t0 + a.chunk : L;
     const int64_t R0 = ((int64_t)b * a.hkv + hk) * a.cap;
-    const rsrc_t kr = make_rsrc(a.kc + R0 * KRB, (int64_t)L * KRB);
-    const rsrc_t ksr = make_rsrc(a.ks + R0 * GK, (int64_t)L * GK * 4);
-    const rsrc_t vr = make_rsrc(a.vc + R0 * (kD * VB / 8), (int64_t)((L + 31) / 32) * VTB);
-    const rsrc_t vsr = make_rsrc(a.vs + R0 * GV, (int64_t)L * GV * 4);
+    KvBufs bf;
+    bf.k = make_rsrc(a.kc + R0 * KRB, (int64_t)L * KRB);
+    bf.ks = make_rsrc(a.ks + R0 * GK, (int64_t)L * GK * 4);
+    bf.v = make_rsrc(a.vc + R0 * (kD * VB / 8), (int64_t)((L + 31) / 32) * VTB);
+    bf.vs = make_rsrc(a.vs + R0 * GV, (int64_t)L * GV * 4);
 
     // B operand of the score product: head r's values d = 32j + 8t + s (zero past the group)
     h8 Q[4];
@@ -263,96 +418,40 @@ __global__ __launch_bounds__(256) void kv_attn_kernel(KvAttnArgs a)
         else Q[j] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
     }
 
-    float m = -__builtin_inff(), l = 0.f;
-    f4 O[8];
+    KvState st;
+    st.m = -__builtin_inff();
+    st.l = 0.f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) O[c] = (f4){0.f, 0.f, 0.f, 0.f};
-
-    int T = t0 / 32 + wv;
-    KvTile<KB, VB, GK, GV> cur, nxt;
-    if (32 * T < t1) load_tile(cur, kr, ksr, vr, vsr, T, t, r);
-    for (; 32 * T < t1; T += 4) {
-        if (32 * (T + 4) < t1) load_tile(nxt, kr, ksr, vr, vsr, T + 4, t, r);
-        // scores of tokens 32T + 16u + 4t + i for head r, already in base-2 units
-        float z[2][4];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            f4 zt = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int gi = 0; gi < GK; ++gi) {
-                f4 acc = mfma16(k_frag<KB>(cur.k[u], KSTEP * gi), Q[KSTEP * gi], (f4){0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                for (int jj = 1; jj < KSTEP; ++jj)
-                    acc = mfma16(k_frag<KB>(cur.k[u], KSTEP * gi + jj), Q[KSTEP * gi + jj], acc);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) zt[i] = __builtin_fmaf(cur.ks[u][GK * i + gi], acc[i], zt[i]);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = 32 * T + 16 * u + 4 * t + i;
-                z[u][i] = tok < t1 ? zt[i] * a.c : -__builtin_inff();
-            }
-        }
-        float mt = z[0][0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) mt = __builtin_fmaxf(mt, z[e / 4][e % 4]);
-        mt = __builtin_fmaxf(mt, __shfl_xor(mt, 16));
-        mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32));
-        const float mn = __builtin_fmaxf(m, mt);  // finite: token 32T < t1 is in every tile
-        const float alpha = __builtin_amdgcn_exp2f(m - mn);
-        m = mn;
-        const float base = mn - 14.0f;
-        float p[8], ps = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(z[e / 4][e % 4] - base);
-            ps += p[e];
-        }
-        l = __builtin_fmaf(l, alpha, ps);
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) O[c] *= alpha;
-        }
-        const u4 pw = {pack_h2(p[0], p[1]), pack_h2(p[2], p[3]), pack_h2(p[4], p[5]), pack_h2(p[6], p[7])};
-        const h8 P = __builtin_bit_cast(h8, pw);
-        // V scales per slot as fp16, one set per V group
-        h8 vsh[GV];
-#pragma unroll
-        for (int gi = 0; gi < GV; ++gi) {
-            const u4 w = {pack_h2(cur.vs[0][GV * 0 + gi], cur.vs[0][GV * 1 + gi]),
-                          pack_h2(cur.vs[0][GV * 2 + gi], cur.vs[0][GV * 3 + gi]),
-                          pack_h2(cur.vs[1][GV * 0 + gi], cur.vs[1][GV * 1 + gi]),
-                          pack_h2(cur.vs[1][GV * 2 + gi], cur.vs[1][GV * 3 + gi])};
-            vsh[gi] = __builtin_bit_cast(h8, w);
-        }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const h8 vq = v_frag<VB>(cur.v, c) * vsh[(16 * c) / VG];
-            O[c] = mfma16(vq, P, O[c]);
-        }
-        if (32 * (T + 4) < t1) cur = nxt;
+    for (int cc = 0; cc < 8; ++cc) st.O[cc] = (f4){0.f, 0.f, 0.f, 0.f};
+    const int T0 = t0 / 32, ntiles = t1 > t0 ? (t1 + 31) / 32 - T0 : 0;
+    const int nt = ntiles > wv ? (ntiles - wv + W - 1) / W : 0;
+    if (nt > 0) {
+        uint8_t *base = ring + (size_t)wv * kKvDepth * pitch;
+        kv_loop<KB, VB, KG, VG>(bf, base, base + pitch, base + 2 * pitch, T0 + wv, nt, t1, Q, a.c, lane, st);
     }
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    st.l += __shfl_xor(st.l, 16);
+    st.l += __shfl_xor(st.l, 32);
+    __syncthreads();  // every wave is done with its ring: the merge buffer overlays it
+    float(*sm_o)[16][kD + 1] = reinterpret_cast<float(*)[16][kD + 1]>(ring);
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+    for (int cc = 0; cc < 8; ++cc)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sm_o[wv][r][16 * c + 4 * t + i] = O[c][i];
+        for (int i = 0; i < 4; ++i) sm_o[wv][r][16 * cc + 4 * t + i] = st.O[cc][i];
     if (t == 0) {
-        sm_m[wv][r] = m;
-        sm_l[wv][r] = l;
+        sm_m[wv][r] = st.m;
+        sm_l[wv][r] = st.l;
     }
     __syncthreads();
     const int64_t bh0 = (int64_t)b * a.hq + (int64_t)hk * a.grp;
-    for (int idx = threadIdx.x; idx < a.grp * kD; idx += 256) {
+    for (int idx = threadIdx.x; idx < a.grp * kD; idx += W * 64) {
         const int h = idx / kD, d = idx % kD;
         float M = sm_m[0][h];
 #pragma unroll
-        for (int w = 1; w < 4; ++w) M = __builtin_fmaxf(M, sm_m[w][h]);
+        for (int w = 1; w < W; ++w) M = __builtin_fmaxf(M, sm_m[w][h]);
         float o = 0.f, S = 0.f;
         if (M != -__builtin_inff()) {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
+            for (int w = 0; w < W; ++w) {
                 const float e = __builtin_amdgcn_exp2f(sm_m[w][h] - M);
                 o = __builtin_fmaf(e, sm_o[w][h][d], o);
                 S = __builtin_fmaf(e, sm_l[w][h], S);
@@ -396,7 +495,7 @@ template <int KB, int VB>
 static hipError_t attn_kv(const KvAttnArgs &a, int kg, int vg, dim3 grid, hipStream_t st)
 {
 #define QP_KV_ATTN(KG, VG) \
-    if (kg == KG && vg == VG) { hipLaunchKernelGGL((kv_attn_kernel<KB, VB, KG, VG>), grid, dim3(256), 0, st, a); return hipGetLastError(); }
+    if (kg == KG && vg == VG) { hipLaunchKernelGGL((kv_attn_kernel<KB, VB, KG, VG>), grid, dim3(kKvWaves * 64), 0, st, a); return hipGetLastError(); }
     QP_KV_ATTN(32, 32) QP_KV_ATTN(32, 64) QP_KV_ATTN(32, 128)
     QP_KV_ATTN(64, 32) QP_KV_ATTN(64, 64) QP_KV_ATTN(64, 128)
     QP_KV_ATTN(128, 32) QP_KV_ATTN(128, 64) QP_KV_ATTN(128, 128)
@@ -419,7 +518,7 @@ hipError_t launch_kv_attn(int kb, int vb, int kg, int vg, int64_t batch, const K
 // each chunk a multiple of 128 tokens (one tile per wave at least).
 void kv_split(int64_t batch, int64_t hkv, int64_t cap, int32_t *nsplit, int32_t *chunk)
 {
-    const int64_t want = (1024 + batch * hkv - 1) / (batch * hkv);
+    const int64_t want = (512 + batch * hkv - 1) / (batch * hkv);
     const int64_t maxs = (cap + 127) / 128;
     int64_t ns = want < 1 ? 1 : (want > maxs ? maxs : want);
     int64_t ch = ((cap + ns - 1) / ns + 127) / 128 * 128;
