@@ -202,7 +202,7 @@ struct KvSlot {
     static constexpr int kLoads = KB / 2 + VB / 2 + kKsOps + kVsOps;  // DMA instructions per tile
 };
 
-constexpr int kKvWaves = 4, kKvDepth = 3;
+constexpr int kKvWaves = 4, kKvDepth = 2;
 
 struct KvBufs {
     rsrc_t k, ks, v, vs;
@@ -359,30 +359,44 @@ __device__ __forceinline__ void kv_tile(const uint8_t *slot, int T, int t1, cons
     }
 }
 
-// A wave's tiles i = 0 .. nt-1 (tile T0 + i*kKvWaves) through its three ring slots.  The
-// slots are restrict pointers and the loop is unrolled by three, so every slot access names a
-// slot statically and the compiler never waits for a DMA in flight into another slot.
+// A wave's tiles i = 0 .. nt-1 (tile T0 + i*kKvWaves) through its ring of kKvDepth slots.
+// The slots are restrict pointers and the loop is unrolled by the depth, so every slot access
+// names a slot statically and the compiler never waits for a DMA in flight into another slot.
 template <int KB, int VB, int KG, int VG>
 __device__ __forceinline__ void kv_loop(const KvBufs &bf, uint8_t *__restrict__ s0, uint8_t *__restrict__ s1,
                                         uint8_t *__restrict__ s2, int T0, int nt, int t1, const h8 (&Q)[4], float c,
                                         int lane, KvState &st)
 {
-    constexpr int GK = kD / KG, GV = kD / VG, W = kKvWaves;
+    constexpr int GK = kD / KG, GV = kD / VG, W = kKvWaves, D = kKvDepth;
     using S = KvSlot<KB, VB, GK, GV>;
+    static_assert(D == 2 || D == 3, "two or three slots");
     kv_issue<KB, VB, GK, GV>(bf, T0, lane, s0);
-    kv_issue<KB, VB, GK, GV>(bf, T0 + W, lane, s1);
-    for (int i = 0; i < nt; i += 3) {
-        kv_issue<KB, VB, GK, GV>(bf, T0 + W * (i + 2), lane, s2);
-        kv_wait_vm<2 * S::kLoads>();
-        kv_tile<KB, VB, KG, VG>(s0, T0 + W * i, t1, Q, c, lane, st);
-        if (i + 1 >= nt) break;
-        kv_issue<KB, VB, GK, GV>(bf, T0 + W * (i + 3), lane, s0);
-        kv_wait_vm<2 * S::kLoads>();
-        kv_tile<KB, VB, KG, VG>(s1, T0 + W * (i + 1), t1, Q, c, lane, st);
-        if (i + 2 >= nt) break;
-        kv_issue<KB, VB, GK, GV>(bf, T0 + W * (i + 4), lane, s1);
-        kv_wait_vm<2 * S::kLoads>();
-        kv_tile<KB, VB, KG, VG>(s2, T0 + W * (i + 2), t1, Q, c, lane, st);
+    if constexpr (D == 3) {
+        kv_issue<KB, VB, GK, GV>(bf, T0 + W, lane, s1);
+        for (int i = 0; i < nt; i += 3) {
+            kv_issue<KB, VB, GK, GV>(bf, T0 + W * (i + 2), lane, s2);
+            kv_wait_vm<2 * S::kLoads>();
+            kv_tile<KB, VB, KG, VG>(s0, T0 + W * i, t1, Q, c, lane, st);
+            if (i + 1 >= nt) break;
+            kv_issue<KB, VB, GK, GV>(bf, T0 + W * (i + 3), lane, s0);
+            kv_wait_vm<2 * S::kLoads>();
+            kv_tile<KB, VB, KG, VG>(s1, T0 + W * (i + 1), t1, Q, c, lane, st);
+            if (i + 2 >= nt) break;
+            kv_issue<KB, VB, GK, GV>(bf, T0 + W * (i + 4), lane, s1);
+            kv_wait_vm<2 * S::kLoads>();
+            kv_tile<KB, VB, KG, VG>(s2, T0 + W * (i + 2), t1, Q, c, lane, st);
+        }
+    } else {
+        (void)s2;
+        for (int i = 0; i < nt; i += 2) {
+            kv_issue<KB, VB, GK, GV>(bf, T0 + W * (i + 1), lane, s1);
+            kv_wait_vm<S::kLoads>();
+            kv_tile<KB, VB, KG, VG>(s0, T0 + W * i, t1, Q, c, lane, st);
+            if (i + 1 >= nt) break;
+            kv_issue<KB, VB, GK, GV>(bf, T0 + W * (i + 2), lane, s0);
+            kv_wait_vm<S::kLoads>();
+            kv_tile<KB, VB, KG, VG>(s1, T0 + W * (i + 1), t1, Q, c, lane, st);
+        }
     }
     kv_wait_vm<0>();  // drain the fetches past the end before the LDS is reused
 }
@@ -427,7 +441,8 @@ __global__ __launch_bounds__(kKvWaves * 64) void kv_attn_kernel(KvAttnArgs a)
     const int nt = ntiles > wv ? (ntiles - wv + W - 1) / W : 0;
     if (nt > 0) {
         uint8_t *base = ring + (size_t)wv * kKvDepth * pitch;
-        kv_loop<KB, VB, KG, VG>(bf, base, base + pitch, base + 2 * pitch, T0 + wv, nt, t1, Q, a.c, lane, st);
+        kv_loop<KB, VB, KG, VG>(bf, base, base + pitch, base + (kKvDepth - 1) * pitch, T0 + wv, nt, t1, Q, a.c,
+                                lane, st);
     }
     st.l += __shfl_xor(st.l, 16);
     st.l += __shfl_xor(st.l, 32);
