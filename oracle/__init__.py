@@ -79,6 +79,8 @@ def lib():
         L.or_moe_ffn.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp] + [vp] * 9 + [vp]
         L.or_kv_quantize_row.restype = None
         L.or_kv_quantize_row.argtypes = [vp, i32, i32, i32, vp, vp]
+        L.or_kv_quantize_rows.restype = None
+        L.or_kv_quantize_rows.argtypes = [vp, i64, i32, i32, vp, vp]
         L.or_kv_k_pos.restype = i64
         L.or_kv_k_pos.argtypes = [i32, i32]
         L.or_kv_v_pos.restype = i64
@@ -295,14 +297,11 @@ KV_DIM = 128
 
 def kv_quantize(x_fp16, bits: int, g: int):
     """Rows of fp16 head vectors [n][128] -> (offset codes u8 [n][128], fp32 scales [n][128/g])."""
-    x = _bits16(x_fp16).reshape(-1, KV_DIM)
+    x = np.ascontiguousarray(_bits16(x_fp16).reshape(-1, KV_DIM))
     n = x.shape[0]
     codes = np.zeros((n, KV_DIM), np.uint8)
     scales = np.zeros((n, KV_DIM // g), np.float32)
-    L = lib()
-    for i in range(n):
-        row = np.ascontiguousarray(x[i])
-        L.or_kv_quantize_row(_p(row), KV_DIM, g, bits, _p(codes[i]), _p(scales[i]))
+    lib().or_kv_quantize_rows(_p(x), n, g, bits, _p(codes), _p(scales))
     return codes, scales
 
 
