@@ -263,6 +263,26 @@ __device__ __forceinline__ h8 v_frag(const u4 (&v)[VB / 2], int c)
     else return unpack_byte8(v[c / 2][(2 * c) % 4], v[c / 2][(2 * c) % 4 + 1]);
 }
 
+// max(v[l], v[l ^ X]) for X = 16 or 32 without a trip through LDS: the gfx950 permlane swaps
+// exchange 16-lane rows (odd with even) or the two 32-lane halves, so the pair of results
+// holds both values at every lane.
+template <int X>
+__device__ __forceinline__ float max_pair(float v)
+{
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    uint32_t a, b;
+    if constexpr (X == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        a = r[0];
+        b = r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        a = r[0];
+        b = r[1];
+    }
+    return __builtin_fmaxf(as_f(a), as_f(b));
+}
+
 // Online-softmax state of a wave: running maximum m (base 2, shared by the four lanes of a
 // head), the lane's share l of the weight sum, and O^T (lane (t, r): d = 16c + 4t + i, head r).
 struct KvState {
@@ -326,8 +346,8 @@ __device__ __forceinline__ void kv_tile(const uint8_t *slot, int T, int t1, cons
     float mt = z[0][0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) mt = __builtin_fmaxf(mt, z[e / 4][e % 4]);
-    mt = __builtin_fmaxf(mt, __shfl_xor(mt, 16));
-    mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32));
+    mt = max_pair<16>(mt);
+    mt = max_pair<32>(mt);
     const float mn = __builtin_fmaxf(st.m, mt);  // finite: token 32T < t1 is in every tile
     const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
     st.m = mn;
