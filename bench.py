@@ -141,8 +141,9 @@ def copy_gbps(torch, nbytes: int = 1 << 30, reps: int = 10) -> float:
 
 def pmc_pass(q, torch, workloads):
     """A short eager sequence for counter collection: every (bits, M) GEMV of the step on
-    four distinct weight copies, the prefill GEMM twice, and a 1 GiB copy twice (the copy is
-    the calibration kernel: its bytes are known)."""
+    four distinct weight copies, the prefill GEMM twice, decode attention over two copies of
+    the 32K MHA quantized cache, and a 1 GiB copy twice (the copy is the calibration kernel:
+    its bytes are known)."""
     dev = torch.device("cuda")
     K = N = 4096
     w = workloads.layer_weights(2)
@@ -166,6 +167,30 @@ def pmc_pass(q, torch, workloads):
     for _ in range(2):
         q.qlinear_gemm(dp, hp, xp, Kp, Mp, yp, Np, wsp, wsb)
     torch.cuda.synchronize()
+    del hp, wt, xp, yp, wsp
+    cfg = workloads.KV_MHA
+    d = q.kv_desc(cfg["batch"], cfg["q_heads"], cfg["kv_heads"], cfg["capacity"], 4, 8, 64, 64)
+    rows = cfg["batch"] * cfg["kv_heads"] * cfg["capacity"]
+    slots = torch.arange(rows, dtype=torch.int64, device=dev)
+    cache = {}
+    for w in (q.QKV_K, q.QKV_V):
+        x = torch.from_numpy(workloads.kv_rows(rows, workloads.seed_for(6, 0, w)).view(np.int16)).to(dev)
+        cache[w] = (torch.empty(q.qkv_cache_bytes(d, w), dtype=torch.uint8, device=dev),
+                    torch.empty(q.qkv_scale_count(d, w), dtype=torch.float32, device=dev))
+        q.qkv_quantize(d, w, x, 128, slots, rows, cache[w][0], cache[w][1])
+        del x
+    copies = [cache, {w: (c[0].clone(), c[1].clone()) for w, c in cache.items()}]
+    qv = torch.from_numpy(workloads.kv_queries(cfg["batch"], cfg["q_heads"], workloads.seed_for(6) + 2)
+                          .view(np.int16)).to(dev)
+    ln = torch.full((cfg["batch"],), cfg["capacity"], dtype=torch.int32, device=dev)
+    o = torch.empty((cfg["batch"], cfg["q_heads"], 128), dtype=torch.int16, device=dev)
+    wsb = q.qattn_decode_workspace_bytes(d)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    for c in copies:
+        q.qattn_decode(d, qv, c[q.QKV_K][0], c[q.QKV_K][1], c[q.QKV_V][0], c[q.QKV_V][1], ln, 1.0 / math.sqrt(128),
+                       o, ws, wsb)
+    torch.cuda.synchronize()
+    del copies, cache
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     for _ in range(2):
