@@ -506,23 +506,55 @@ __global__ __launch_bounds__(kKvWaves * 64) void kv_attn_kernel(KvAttnArgs a)
     }
 }
 
-// Merge the chunks of one (sequence, query head): one thread per d.
-__global__ __launch_bounds__(128) void kv_combine_kernel(KvAttnArgs a)
+// Merge the chunks of one (sequence, query head): one thread per d.  The chunk maxima and
+// sums are read once into LDS by all threads together, and the partial outputs are read eight
+// chunks at a time so their loads are in flight together (the merge is latency-bound).
+constexpr int kKvMaxSplit = 1024;
+
+__global__ __launch_bounds__(kD) void kv_combine_kernel(KvAttnArgs a)
 {
+    __shared__ float sm_e[kKvMaxSplit], sm_s[kKvMaxSplit], red[kD];
     const int64_t bh = blockIdx.x;
-    const int d = threadIdx.x;
+    const int d = threadIdx.x, ns = a.nsplit;
+    const float *ml = a.part_ml + 2 * bh * ns;
     float M = -__builtin_inff();
-    for (int s = 0; s < a.nsplit; ++s) M = __builtin_fmaxf(M, a.part_ml[2 * (bh * a.nsplit + s)]);
-    float o = 0.f, S = 0.f;
-    if (M != -__builtin_inff()) {
-        for (int s = 0; s < a.nsplit; ++s) {
-            const int64_t pi = bh * a.nsplit + s;
-            const float e = __builtin_amdgcn_exp2f(a.part_ml[2 * pi] - M);
-            o = __builtin_fmaf(e, a.part_o[pi * kD + d], o);
-            S = __builtin_fmaf(e, a.part_ml[2 * pi + 1], S);
-        }
+    for (int s = d; s < ns; s += kD) {
+        const float m = ml[2 * s];
+        sm_e[s] = m;
+        sm_s[s] = ml[2 * s + 1];
+        M = __builtin_fmaxf(M, m);
     }
-    const float y = S > 0.f ? o / S : 0.f;
+    red[d] = M;
+    __syncthreads();
+#pragma unroll
+    for (int w = kD / 2; w >= 1; w >>= 1) {
+        if (d < w) red[d] = __builtin_fmaxf(red[d], red[d + w]);
+        __syncthreads();
+    }
+    M = red[0];
+    float y = 0.f;
+    if (M != -__builtin_inff()) {
+        for (int s = d; s < ns; s += kD) sm_e[s] = __builtin_amdgcn_exp2f(sm_e[s] - M);
+        __syncthreads();
+        const float *po = a.part_o + bh * ns * kD + d;
+        float o = 0.f, S = 0.f;
+        int s = 0;
+        for (; s + 8 <= ns; s += 8) {
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = po[(int64_t)(s + i) * kD];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                o = __builtin_fmaf(sm_e[s + i], v[i], o);
+                S = __builtin_fmaf(sm_e[s + i], sm_s[s + i], S);
+            }
+        }
+        for (; s < ns; ++s) {
+            o = __builtin_fmaf(sm_e[s], po[(int64_t)s * kD], o);
+            S = __builtin_fmaf(sm_e[s], sm_s[s], S);
+        }
+        y = S > 0.f ? o / S : 0.f;
+    }
     a.o[bh * kD + d] = __builtin_bit_cast(uint16_t, (_Float16)y);
 }
 
@@ -556,6 +588,7 @@ void kv_split(int64_t batch, int64_t hkv, int64_t cap, int32_t *nsplit, int32_t 
     const int64_t want = (512 + batch * hkv - 1) / (batch * hkv);
     const int64_t maxs = (cap + 127) / 128;
     int64_t ns = want < 1 ? 1 : (want > maxs ? maxs : want);
+    if (ns > kKvMaxSplit) ns = kKvMaxSplit;
     int64_t ch = ((cap + ns - 1) / ns + 127) / 128 * 128;
     ns = (cap + ch - 1) / ch;
     *nsplit = (int32_t)ns;
