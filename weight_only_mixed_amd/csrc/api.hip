@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include "kv_internal.h"
 #include "qp_internal.h"
 
 namespace qp {

@@ -38,6 +38,7 @@
 // The four waves' (m, l, O) are merged through LDS; with several chunks per (sequence, kv
 // head) the partial results go to the workspace and a second kernel merges them.
 #include "bufio.h"
+#include "kv_internal.h"
 #include "unpack.h"
 
 namespace qp {
