@@ -77,6 +77,11 @@ def lib():
         L.or_linear.argtypes = [i64, i64, i64, i32, vp, i64, vp, vp, vp, vp, vp, vp, vp, i64]
         L.or_moe_ffn.restype = None
         L.or_moe_ffn.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp] + [vp] * 9 + [vp]
+        L.or_zero_row_bytes.restype = i64
+        L.or_zero_row_bytes.argtypes = [i64, i32]
+        for name in ("or_pack_zeros", "or_unpack_zeros"):
+            getattr(L, name).restype = None
+            getattr(L, name).argtypes = [i64, i64, i32, vp, vp]
         L.or_kv_quantize_row.restype = None
         L.or_kv_quantize_row.argtypes = [vp, i32, i32, i32, vp, vp]
         L.or_kv_quantize_rows.restype = None
@@ -288,6 +293,28 @@ def swiglu_act(x_row_fp16, gate: dict, up: dict):
                         _p(_c(gate["zeros"], np.uint8)), _p(_c(up["codes"], np.uint8)),
                         _p(_c(up["scales"], np.uint16)), _p(_c(up["zeros"], np.uint8)), _p(v))
     return v
+
+
+# ---- zero points stored in b bits -----------------------------------------------------
+
+def zero_row_bytes(G: int, bits: int) -> int:
+    return lib().or_zero_row_bytes(G, bits)
+
+
+def pack_zeros(zeros, bits: int):
+    """u8 zero points [N][G] -> rows of b-bit fields (LSB-first), zero_row_bytes(G, bits) each."""
+    z = _c(zeros, np.uint8)
+    N, G = z.shape
+    out = np.zeros((N, zero_row_bytes(G, bits)), np.uint8)
+    lib().or_pack_zeros(N, G, bits, _p(z), _p(out))
+    return out
+
+
+def unpack_zeros(packed, N: int, G: int, bits: int):
+    p = _c(packed, np.uint8)
+    z = np.zeros((N, G), np.uint8)
+    lib().or_unpack_zeros(N, G, bits, _p(p), _p(z))
+    return z
 
 
 # ---- quantized KV cache and decode attention ------------------------------------------

@@ -40,6 +40,8 @@
  *    fp16((m + m) / qmax) and the zero point is the midpoint 2^(b-1), which the
  *    asymmetric formula would also give for that range; it is implied, not stored, and
  *    an all-zero group gets scale 1.0 with every code at the midpoint;
+ *  - zero points stored in b bits ([MB] s2.3): the same zero points as the affine groups,
+ *    row n a little-endian stream of b-bit fields (LSB-first), rows padded to 32-bit words;
  *  - KV cache ([KV] s2.1-s2.2, s3.1): symmetric groups along the head dimension with
  *    qmax = 2^(b-1) - 1, an fp32 scale m / qmax, codes rint(x / s) clamped to
  *    [-qmax, qmax] and stored offset by 2^(b-1); an all-zero group stores scale 0;
@@ -532,6 +534,42 @@ void or_moe_ffn(int64_t T, int64_t D, int64_t F, int topk, int g,
     }
     free(v);
     free(a);
+}
+
+/* ------------------------------------------------------------------------------ */
+/* Zero points stored in b bits  ([MB] s2.3)                                        */
+/* ------------------------------------------------------------------------------ */
+
+/* Bytes of one row of b-bit zero points: G fields, rounded up to whole 32-bit words. */
+int64_t or_zero_row_bytes(int64_t G, int bits) { return 4 * ((G * bits + 31) / 32); }
+
+/* [MB] s2.3 counts an asymmetric group's zero point at b bits.  Row n of the packed array
+ * is a little-endian bit stream: zero point gi of the row occupies bits [gi*b, gi*b + b)
+ * (LSB-first, as the page's units store codes), the rest of the row's last word is zero. */
+void or_pack_zeros(int64_t N, int64_t G, int bits, const uint8_t *zeros, uint8_t *out)
+{
+    const int64_t rb = or_zero_row_bytes(G, bits);
+    memset(out, 0, (size_t)(N * rb));
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t gi = 0; gi < G; ++gi)
+            for (int i = 0; i < bits; ++i) {
+                const int64_t bit = gi * bits + i;
+                if ((zeros[n * G + gi] >> i) & 1) out[n * rb + bit / 8] |= (uint8_t)(1u << (bit % 8));
+            }
+}
+
+void or_unpack_zeros(int64_t N, int64_t G, int bits, const uint8_t *in, uint8_t *zeros)
+{
+    const int64_t rb = or_zero_row_bytes(G, bits);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t gi = 0; gi < G; ++gi) {
+            unsigned v = 0;
+            for (int i = 0; i < bits; ++i) {
+                const int64_t bit = gi * bits + i;
+                v |= (unsigned)((in[n * rb + bit / 8] >> (bit % 8)) & 1) << i;
+            }
+            zeros[n * G + gi] = (uint8_t)v;
+        }
 }
 
 /* ------------------------------------------------------------------------------ */

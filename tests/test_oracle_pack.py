@@ -185,3 +185,39 @@ def test_device_layout_lane_chunks():
             want = [1024 * (c // 16) + 16 * lane + c % 16 if c < F else 64 * F + 8 * lane + (c - F)
                     for c in range(8 * bits)]
             assert chunk == want
+
+
+# ---- zero points stored in b bits (mixed-bit page, s2.3) --------------------------------
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6])
+@pytest.mark.parametrize("G", [1, 5, 32, 86, 128])
+def test_packed_zeros_round_trip_and_size(bits, G):
+    rng = np.random.default_rng(bits * 100 + G)
+    z = rng.integers(0, 1 << bits, (7, G), dtype=np.uint8)
+    p = oracle.pack_zeros(z, bits)
+    assert p.shape == (7, 4 * ((G * bits + 31) // 32))
+    assert (oracle.unpack_zeros(p, 7, G, bits) == z).all()
+
+
+@pytest.mark.parametrize("bits", [2, 3, 5, 6])
+def test_packed_zeros_bit_positions(bits):
+    """Field g of a row is bits [g*b, g*b + b) of the little-endian row stream: a single
+    all-ones field lands exactly there, every other bit of the row stays zero."""
+    G = 40
+    for g in (0, 1, 7, 10, 31, 39):
+        z = np.zeros((1, G), np.uint8)
+        z[0, g] = (1 << bits) - 1
+        p = oracle.pack_zeros(z, bits)[0]
+        stream = int.from_bytes(p.tobytes(), "little")
+        assert stream == ((1 << bits) - 1) << (g * bits)
+
+
+def test_packed_zeros_bits_per_weight():
+    """The page's 2-bit, 32-weight block with an fp16 scale and a 2-bit zero point (about 2.56
+    bits per weight): the zero-point bytes this layout stores for a 4096-wide row are exactly
+    b bits per group, so codes + scales + packed zero points give that figure."""
+    c = [c for c in GOLD["bits_per_weight"] if c["zp_bits"] == 2][0]
+    G = 4096 // c["group"]
+    row_bytes = 4096 * c["bits"] / 8 + G * c["scale_bytes"] + oracle.zero_row_bytes(G, c["zp_bits"])
+    assert oracle.zero_row_bytes(G, c["zp_bits"]) == G * c["zp_bits"] // 8
+    assert abs(row_bytes * 8 / 4096 - c["value_approx"]) <= c["tol"]
