@@ -91,8 +91,16 @@ enum {
  *                    m = max |w|, scale = fp16((m + m) / (2^b - 1)), and the zero point is the
  *                    midpoint 2^(b-1), implied rather than stored (qp_weight.zeros is not read
  *                    and may be NULL).  An all-zero group gets scale 1.0 with every code at
- *                    the midpoint.  Allowed at every bit width. */
-enum { QP_ZERO_STORED = 0, QP_ZERO_MIDPOINT = 1 };
+ *                    the midpoint.  Allowed at every bit width.
+ *  QP_ZERO_PACKED:   affine groups as QP_ZERO_STORED, with the zero points kept in b bits
+ *                    (mixed-bit page, s2.3: a b-bit group's zero point costs b bits): row n of
+ *                    qp_weight.zeros is a little-endian bit stream in which group g's zero point
+ *                    occupies bits [g*b, g*b + b), padded to whole 32-bit words
+ *                    (qp_zero_bytes(desc) bytes in all).  qpack_quantize writes u8 zero points
+ *                    in this mode too; qpack_pack_zeros turns them into the packed form.  Read by
+ *                    qlinear_gemv and qlinear_gemv_batch; the GEMM, grouped GEMM and MoE FFN
+ *                    return QP_ERR_UNSUPPORTED. */
+enum { QP_ZERO_STORED = 0, QP_ZERO_MIDPOINT = 1, QP_ZERO_PACKED = 2 };
 
 /* Shape and format of one quantized matrix W[n][k]. */
 typedef struct {
@@ -103,7 +111,7 @@ typedef struct {
                            and qlinear_gemv_batch (one group size per batch); the GEMM, grouped
                            GEMM and MoE FFN return QP_ERR_UNSUPPORTED for them. */
     int32_t layout;     /* QP_LAYOUT_CANONICAL or QP_LAYOUT_DEVICE */
-    int32_t zero_mode;  /* QP_ZERO_STORED or QP_ZERO_MIDPOINT */
+    int32_t zero_mode;  /* QP_ZERO_STORED, QP_ZERO_MIDPOINT or QP_ZERO_PACKED */
     int64_t n;          /* rows (output features) */
     int64_t k;          /* columns (input features), multiple of 128 */
 } qp_weight_desc;
@@ -112,7 +120,9 @@ typedef struct {
 typedef struct {
     const void *packed;         /* qp_packed_bytes(desc) bytes, 16-byte aligned */
     const uint16_t *scales;     /* fp16 [n][k/group_size], row-major (planar), 4-byte aligned */
-    const uint8_t *zeros;       /* u8   [n][k/group_size], row-major, 2-byte aligned (QP_ZERO_STORED) */
+    const uint8_t *zeros;       /* u8   [n][k/group_size], row-major, 2-byte aligned (QP_ZERO_STORED);
+                                   b-bit rows of qp_zero_bytes(desc)/n bytes, 4-byte aligned
+                                   (QP_ZERO_PACKED); unused (QP_ZERO_MIDPOINT) */
     const int32_t *csr_rowptr;  /* [n+1] outlier CSR over rows of W, or NULL */
     const int32_t *csr_col;     /* [nnz] column k of each outlier, ascending within a row */
     const uint16_t *csr_val;    /* [nnz] fp16 value of each outlier */
@@ -125,6 +135,9 @@ typedef struct {
 size_t qp_packed_bytes(const qp_weight_desc *desc);
 /* n*k/group_size, or 0 if desc is invalid. */
 size_t qp_num_groups(const qp_weight_desc *desc);
+/* Bytes of qp_weight.zeros for desc->zero_mode: n*k/g (stored), n*4*ceil((k/g)*bits/32)
+ * (packed), 0 (midpoint); 0 if desc is invalid. */
+size_t qp_zero_bytes(const qp_weight_desc *desc);
 /* Bytes of `numel` weights at `bits` with one scale of `scale_bytes` and a zero point of
  * `zp_bits` per group of `group`: numel*bits/8 + (numel/group)*(scale_bytes + zp_bits/8)
  * (mixed-bit page s2.3; KV page s3.1). */
@@ -168,6 +181,12 @@ qp_status qpack_quantize(const qp_weight_desc *desc, const uint16_t *w, int64_t 
  * (qp_packed_bytes(desc) bytes, 16-byte aligned). */
 qp_status qpack_pack(const qp_weight_desc *desc, const uint8_t *codes, void *packed,
                      void *stream);
+
+/* u8 zero points [n][k/g] (as qpack_quantize writes them, 2-byte aligned) -> the b-bit rows
+ * of QP_ZERO_PACKED (qp_zero_bytes(desc) bytes, 4-byte aligned).  desc->zero_mode must be
+ * QP_ZERO_PACKED; values must be below 2^bits (they are, from qpack_quantize). */
+qp_status qpack_pack_zeros(const qp_weight_desc *desc, const uint8_t *zeros, void *packed_zeros,
+                           void *stream);
 
 /* Inverse of qpack_pack: packed bytes in desc->layout -> codes u8 [n][k]. */
 qp_status qpack_unpack(const qp_weight_desc *desc, const void *packed, uint8_t *codes,

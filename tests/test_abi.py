@@ -145,7 +145,7 @@ def test_zero_mode_validation():
     device work)."""
     for bits in (2, 3, 4, 5, 6):
         assert q.qp_packed_bytes(q.desc(bits, 64, 1024, zero_mode=q.QP_ZERO_MIDPOINT)) == 64 * 1024 * bits // 8
-    assert q.qp_packed_bytes(q.desc(4, 64, 1024, zero_mode=2)) == 0
+    assert q.qp_packed_bytes(q.desc(4, 64, 1024, zero_mode=3)) == 0
     assert q.qp_packed_bytes(q.desc(4, 64, 1024, zero_mode=-1)) == 0
     d = q.desc(4, 64, 1024)
     st, _ = q.qpack_quantize(d, FAKE, 1024, 0.0, FAKE, FAKE, None, stream=0, check=False)
@@ -265,3 +265,32 @@ def test_kv_call_validation():
                           check=False) == q.QP_ERR_WORKSPACE
     assert q.qattn_decode(big, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, None, 0,
                           check=False) == q.QP_ERR_WORKSPACE
+
+
+def test_packed_zero_points():
+    """QP_ZERO_PACKED: zero points in b bits per group, rows padded to 32-bit words; the GEMV
+    takes them, the matrix-core GEMMs and the expert FFN do not, a GEMV batch does not mix
+    them with byte zero points; qpack_pack_zeros checks its mode and pointers (all before any
+    device work)."""
+    for bits in (2, 3, 4, 5, 6):
+        for g in (32, 64, 128):
+            for k in (1024, 1280, 11008 // 128 * 128):
+                G = k // g
+                d = q.desc(bits, 64, k, group_size=g, zero_mode=q.QP_ZERO_PACKED)
+                assert q.qp_zero_bytes(d) == 64 * 4 * ((G * bits + 31) // 32)
+                assert q.qp_zero_bytes(q.desc(bits, 64, k, group_size=g)) == 64 * G
+                assert q.qp_zero_bytes(q.desc(bits, 64, k, group_size=g, zero_mode=q.QP_ZERO_MIDPOINT)) == 0
+    d = q.desc(2, 256, 1024, group_size=128, zero_mode=q.QP_ZERO_PACKED)
+    w = q.weight(FAKE, FAKE, FAKE)
+    U, E = q.QP_ERR_UNSUPPORTED, q.QP_ERR_INVALID_ARG
+    assert q.qlinear_gemm(d, w, FAKE, 1024, 64, FAKE, 256, stream=0, check=False) == U
+    assert q.qlinear_grouped_gemm(d, [w], FAKE, 1024, FAKE, FAKE, 64, q.QP_EPI_NONE, FAKE, 256, stream=0,
+                                  check=False) == U
+    assert q.qlinear_gemv(d, q.weight(FAKE, FAKE, FAKE + 2), FAKE, 1024, 1, FAKE, 256, stream=0,
+                          check=False) == E                       # packed zeros need 4-byte alignment
+    ds = q.desc(2, 256, 1024, group_size=128)
+    probs = [q.gemv_problem(d, w, FAKE, 1024, 1, FAKE, 256), q.gemv_problem(ds, w, FAKE, 1024, 1, FAKE, 256)]
+    assert q.qlinear_gemv_batch(probs, stream=0, check=False) == U
+    assert q.qpack_pack_zeros(ds, FAKE, FAKE, stream=0, check=False) == E      # mode must be packed
+    assert q.qpack_pack_zeros(d, FAKE + 1, FAKE, stream=0, check=False) == E
+    assert q.qpack_pack_zeros(d, FAKE, FAKE + 2, stream=0, check=False) == E

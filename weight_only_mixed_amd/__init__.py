@@ -26,7 +26,7 @@ lib = ctypes.CDLL(str(_LIB_PATH))
 QP_OK, QP_ERR_INVALID_ARG, QP_ERR_UNSUPPORTED, QP_ERR_DEVICE, QP_ERR_WORKSPACE = range(5)
 QP_LAYOUT_CANONICAL, QP_LAYOUT_DEVICE = 0, 1
 QP_EPI_NONE, QP_EPI_SWIGLU, QP_EPI_ROWS_F32 = 0, 1, 2
-QP_ZERO_STORED, QP_ZERO_MIDPOINT = 0, 1
+QP_ZERO_STORED, QP_ZERO_MIDPOINT, QP_ZERO_PACKED = 0, 1, 2
 STATUS_NAMES = {0: "QP_OK", 1: "QP_ERR_INVALID_ARG", 2: "QP_ERR_UNSUPPORTED", 3: "QP_ERR_DEVICE",
                 4: "QP_ERR_WORKSPACE"}
 
@@ -63,6 +63,7 @@ _KD = ctypes.POINTER(qkv_desc)
 _SIGS = {
     "qp_packed_bytes": (_sz, [_D]),
     "qp_num_groups": (_sz, [_D]),
+    "qp_zero_bytes": (_sz, [_D]),
     "qp_quant_bytes": (_dbl, [_dbl] * 5),
     "qp_outlier_count": (_i64, [_i64, _i64, _dbl]),
     "qpack_quantize_workspace_bytes": (_sz, [_D, _dbl]),
@@ -70,6 +71,7 @@ _SIGS = {
                               ctypes.POINTER(_i64), _vp, _sz, _vp]),
     "qpack_pack": (_i32, [_D, _vp, _vp, _vp]),
     "qpack_unpack": (_i32, [_D, _vp, _vp, _vp]),
+    "qpack_pack_zeros": (_i32, [_D, _vp, _vp, _vp]),
     "qlinear_gemv": (_i32, [_D, _W, _vp, _i64, _i64, _vp, _i64, _vp]),
     "qlinear_gemv_batch": (_i32, [ctypes.POINTER(qp_gemv_problem), _i32, _vp]),
     "qlinear_gemm_workspace_bytes": (_sz, [_D, _i64, _i64]),
@@ -146,6 +148,10 @@ def qp_num_groups(d) -> int:
     return lib.qp_num_groups(ctypes.byref(d))
 
 
+def qp_zero_bytes(d) -> int:
+    return lib.qp_zero_bytes(ctypes.byref(d))
+
+
 def qp_quant_bytes(numel, bits, group, scale_bytes, zp_bits) -> float:
     return lib.qp_quant_bytes(float(numel), float(bits), float(group), float(scale_bytes), float(zp_bits))
 
@@ -177,6 +183,11 @@ def qpack_quantize(d, w, ldw, outlier_frac, codes, scales, zeros, csr_rowptr=Non
 
 def qpack_pack(d, codes, packed, stream=None, check=True):
     return _check("qpack_pack", lib.qpack_pack(ctypes.byref(d), _ptr(codes), _ptr(packed), _stream(stream)), check)
+
+
+def qpack_pack_zeros(d, zeros, packed_zeros, stream=None, check=True):
+    return _check("qpack_pack_zeros", lib.qpack_pack_zeros(ctypes.byref(d), _ptr(zeros), _ptr(packed_zeros),
+                                                            _stream(stream)), check)
 
 
 def qpack_unpack(d, packed, codes, stream=None, check=True):

@@ -41,7 +41,7 @@ static qp_status check_desc(const qp_weight_desc *d, bool need_device)
 {
     if (!d) return fail(QP_ERR_INVALID_ARG, "desc is NULL");
     if (d->bits < 2 || d->bits > 6) return fail(QP_ERR_INVALID_ARG, "bits=%d not in 2..6", d->bits);
-    if (d->zero_mode != QP_ZERO_STORED && d->zero_mode != QP_ZERO_MIDPOINT)
+    if (d->zero_mode != QP_ZERO_STORED && d->zero_mode != QP_ZERO_MIDPOINT && d->zero_mode != QP_ZERO_PACKED)
         return fail(QP_ERR_INVALID_ARG, "zero_mode=%d unknown", d->zero_mode);
     if (d->layout != QP_LAYOUT_CANONICAL && d->layout != QP_LAYOUT_DEVICE)
         return fail(QP_ERR_INVALID_ARG, "layout=%d unknown", d->layout);
@@ -68,6 +68,8 @@ static qp_status check_weight(const qp_weight_desc *d, const qp_weight *w, bool 
     if (!w->scales || !aligned(w->scales, 4)) return fail(QP_ERR_INVALID_ARG, "scales NULL or not 4-byte aligned");
     if (d->zero_mode == QP_ZERO_STORED && (!w->zeros || !aligned(w->zeros, 2)))
         return fail(QP_ERR_INVALID_ARG, "zeros NULL or not 2-byte aligned");
+    if (d->zero_mode == QP_ZERO_PACKED && (!w->zeros || !aligned(w->zeros, 4)))
+        return fail(QP_ERR_INVALID_ARG, "packed zeros NULL or not 4-byte aligned");
     if (w->nnz < 0) return fail(QP_ERR_INVALID_ARG, "nnz < 0");
     if (w->csr_rowptr) {
         if (!allow_csr && w->nnz > 0) return fail(QP_ERR_UNSUPPORTED, "outlier CSR not supported here");
@@ -86,6 +88,12 @@ static uint32_t zero_pair(const qp_weight_desc *d)
 }
 
 static hipStream_t S(void *s) { return (hipStream_t)s; }
+
+// Bytes of one row of b-bit zero points (QP_ZERO_PACKED): whole 32-bit words.
+static int64_t zero_row_bytes(const qp_weight_desc *d)
+{
+    return 4 * ((d->k / d->group_size * d->bits + 31) / 32);
+}
 
 // Geometry of a quantized KV cache (qkv_desc).
 static qp_status check_kv(const qkv_desc *d)
@@ -128,6 +136,14 @@ size_t qp_num_groups(const qp_weight_desc *d)
     return (size_t)(d->n * (d->k / d->group_size));
 }
 
+size_t qp_zero_bytes(const qp_weight_desc *d)
+{
+    if (check_desc(d, false) != QP_OK) return 0;
+    if (d->zero_mode == QP_ZERO_MIDPOINT) return 0;
+    if (d->zero_mode == QP_ZERO_PACKED) return (size_t)(d->n * zero_row_bytes(d));
+    return (size_t)(d->n * (d->k / d->group_size));
+}
+
 double qp_quant_bytes(double numel, double bits, double group, double scale_bytes, double zp_bits)
 {
     return numel * bits / 8.0 + (numel / group) * (scale_bytes + zp_bits / 8.0);
@@ -155,7 +171,7 @@ qp_status qpack_quantize(const qp_weight_desc *d, const uint16_t *w, int64_t ldw
     if (!w || !aligned(w, 4)) return fail(QP_ERR_INVALID_ARG, "w NULL or not 4-byte aligned");
     if (ldw < d->k || ldw % 2 != 0) return fail(QP_ERR_INVALID_ARG, "ldw=%lld must be >= k and even", (long long)ldw);
     if (!codes || !aligned(codes, 2)) return fail(QP_ERR_INVALID_ARG, "codes NULL or not 2-byte aligned");
-    if (!scales || (!zeros && d->zero_mode == QP_ZERO_STORED)) return fail(QP_ERR_INVALID_ARG, "scales/zeros NULL");
+    if (!scales || (!zeros && d->zero_mode != QP_ZERO_MIDPOINT)) return fail(QP_ERR_INVALID_ARG, "scales/zeros NULL");
     if (!nnz_out) return fail(QP_ERR_INVALID_ARG, "nnz_out NULL");
     if (outlier_frac < 0.0 || outlier_frac > 1.0 || outlier_frac != outlier_frac)
         return fail(QP_ERR_INVALID_ARG, "outlier_frac must be in [0, 1]");
@@ -186,6 +202,18 @@ qp_status qpack_pack(const qp_weight_desc *d, const uint8_t *codes, void *packed
     if (!codes || !aligned(codes, 8)) return fail(QP_ERR_INVALID_ARG, "codes NULL or not 8-byte aligned");
     if (!packed || !aligned(packed, 16)) return fail(QP_ERR_INVALID_ARG, "packed NULL or not 16-byte aligned");
     return device(launch_pack(d->bits, d->layout, codes, d->n, d->k, (uint8_t *)packed, S(stream)), "qpack_pack");
+}
+
+qp_status qpack_pack_zeros(const qp_weight_desc *d, const uint8_t *zeros, void *packed_zeros, void *stream)
+{
+    qp_status st = check_desc(d, false);
+    if (st != QP_OK) return st;
+    if (d->zero_mode != QP_ZERO_PACKED) return fail(QP_ERR_INVALID_ARG, "zero_mode must be QP_ZERO_PACKED");
+    if (!zeros || !aligned(zeros, 2)) return fail(QP_ERR_INVALID_ARG, "zeros NULL or not 2-byte aligned");
+    if (!packed_zeros || !aligned(packed_zeros, 4)) return fail(QP_ERR_INVALID_ARG, "packed_zeros NULL or not 4-byte aligned");
+    return device(launch_pack_zeros(d->bits, zeros, d->n, d->k / d->group_size, zero_row_bytes(d),
+                                    (uint8_t *)packed_zeros, S(stream)),
+                  "qpack_pack_zeros");
 }
 
 qp_status qpack_unpack(const qp_weight_desc *d, const void *packed, uint8_t *codes, void *stream)
@@ -223,6 +251,7 @@ static qp_status gemv_problem(const qp_weight_desc *d, const qp_weight *w, const
     p->w = {(const uint8_t *)w->packed, w->scales, w->zeros};
     p->zmid = zero_pair(d);
     p->gs = d->group_size;
+    p->zrow = d->zero_mode == QP_ZERO_PACKED ? (int32_t)zero_row_bytes(d) : 0;
     if (w->nnz > 0) {
         p->rowptr = w->csr_rowptr;
         p->col = w->csr_col;
@@ -261,6 +290,8 @@ qp_status qlinear_gemv_batch(const qp_gemv_problem *problems, int32_t count, voi
         qp_status st = gemv_problem(&q.desc, &q.w, q.x, q.ldx, q.m, q.y, q.ldy, &b.p[i]);
         if (st != QP_OK) return st;
         if (b.p[i].gs != b.p[0].gs) return fail(QP_ERR_UNSUPPORTED, "one group size per batch");
+        if ((b.p[i].zrow != 0) != (b.p[0].zrow != 0))
+            return fail(QP_ERR_UNSUPPORTED, "packed and byte zero points in one batch");
         b.p[i].block0 = blocks;
         blocks += q.desc.n / 16;
         if (q.m > m_max) m_max = (int)q.m;
@@ -281,6 +312,7 @@ qp_status qlinear_gemm(const qp_weight_desc *d, const qp_weight *w, const uint16
     qp_status st = check_desc(d, true);
     if (st != QP_OK) return st;
     if (d->group_size != kGroup) return fail(QP_ERR_UNSUPPORTED, "the GEMM is built for groups of 128");
+    if (d->zero_mode == QP_ZERO_PACKED) return fail(QP_ERR_UNSUPPORTED, "the GEMM reads byte zero points");
     if ((st = check_weight(d, w, true)) != QP_OK) return st;
     if ((st = check_xy(d, x, ldx, m, y, ldy, d->n, 4)) != QP_OK) return st;
     if (m > (1LL << 24)) return fail(QP_ERR_INVALID_ARG, "m too large");
@@ -320,6 +352,7 @@ qp_status qlinear_grouped_gemm(const qp_weight_desc *d, const qp_weight *experts
     qp_status st = check_desc(d, true);
     if (st != QP_OK) return st;
     if (d->group_size != kGroup) return fail(QP_ERR_UNSUPPORTED, "the grouped GEMM is built for groups of 128");
+    if (d->zero_mode == QP_ZERO_PACKED) return fail(QP_ERR_UNSUPPORTED, "the grouped GEMM reads byte zero points");
     if (!experts) return fail(QP_ERR_INVALID_ARG, "experts NULL");
     if (n_experts < 1 || n_experts > kMaxExperts) return fail(QP_ERR_INVALID_ARG, "n_experts=%d not in 1..64", n_experts);
     for (int e = 0; e < n_experts; ++e)
@@ -394,6 +427,9 @@ qp_status qmoe_ffn(const qp_weight_desc *dgu, const qp_weight *gate_up, const qp
     if ((st = check_desc(dgu, true)) != QP_OK) return st;
     if ((st = check_desc(dd, true)) != QP_OK) return st;
     if (dgu->bits != dd->bits) return fail(QP_ERR_UNSUPPORTED, "gate/up and down must share the bit width");
+    if (dgu->group_size != kGroup || dd->group_size != kGroup || dgu->zero_mode == QP_ZERO_PACKED ||
+        dd->zero_mode == QP_ZERO_PACKED)
+        return fail(QP_ERR_UNSUPPORTED, "the expert FFN is built for groups of 128 with byte or implied zero points");
     const int64_t d_model = dgu->k, d_ff = dgu->n / 2;
     if (dgu->n % 32 != 0 || dd->n != d_model || dd->k != d_ff)
         return fail(QP_ERR_INVALID_ARG, "shapes: gate_up must be [2*d_ff, d_model], down [d_model, d_ff]");

@@ -190,4 +190,33 @@ hipError_t launch_unpack(int bits, int layout, const uint8_t *in, int64_t n, int
     return dispatch(bits, layout, true, in, n, k, codes, st);
 }
 
+// Zero points in b bits (mixed-bit page, s2.3): one thread per 32-bit word of a row's
+// little-endian stream, gathering the (at most 17) fields that overlap the word; group g's
+// field is bits [g*b, g*b + b) of the row, bits past the last field are zero.
+__global__ __launch_bounds__(256) void pack_zeros_kernel(const uint8_t *zeros, int64_t n, int64_t G, int bits,
+                                                         int64_t words, uint32_t *out)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n * words) return;
+    const int64_t r = i / words, w = i % words;
+    const int64_t lo = 32 * w, hi = lo + 32;  // this word's bit range in the row stream
+    uint32_t v = 0;
+    for (int64_t g = lo / bits; g < G && g * bits < hi; ++g) {
+        const uint64_t f = (uint64_t)(zeros[r * G + g] & ((1u << bits) - 1));
+        const int64_t p = g * bits - lo;  // field position relative to the word (may be < 0)
+        v |= (uint32_t)(p >= 0 ? f << p : f >> -p);
+    }
+    out[i] = v;
+}
+
+hipError_t launch_pack_zeros(int bits, const uint8_t *zeros, int64_t n, int64_t G, int64_t row_bytes,
+                             uint8_t *out, hipStream_t st)
+{
+    const int64_t words = row_bytes / 4, total = n * words;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(pack_zeros_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, zeros, n, G, bits,
+                       words, (uint32_t *)out);
+    return hipGetLastError();
+}
+
 }  // namespace qp

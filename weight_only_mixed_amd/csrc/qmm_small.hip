@@ -54,6 +54,7 @@ __device__ __forceinline__ void mma_tile(const h8 *A, const h8 *X, const uint32_
 
 struct GemvBufs {
     rsrc_t w, sc, zr, x;
+    uint32_t zrow;  // bytes per row of b-bit zero points (ZP); 0 for byte zero points
     uint32_t vw, vw8, vz, vs, vx;  // per-lane offsets
     int64_t G;
 };
@@ -62,11 +63,14 @@ struct GemvBufs {
 // its NG = 256 / GS groups for the block's 16 rows (lane l < 16 stages row l; lanes >= 16 read
 // zeros).  Scales: NG = 2 one 4-byte DMA, NG = 4 two (region A groups 0-1, B groups 2-3),
 // NG = 8 one 16-byte DMA.  Zero points: NG = 2 the aligned 4-byte word holding the pair,
-// NG = 4 one 4-byte DMA, NG = 8 two (groups 0-3, 4-7).
-template <int B, int MX, int GS>
+// NG = 4 one 4-byte DMA, NG = 8 two (groups 0-3, 4-7); b-bit zero points (ZP) the 32-bit
+// words of the row's bit stream that cover the tile's NG fields (two, or three when
+// NG*B + 31 > 64).
+template <int B, int MX, int GS, int ZP = 0>
 struct RingSlot {
     static constexpr int NG = kTileK / GS;
-    static constexpr int kScOps = NG == 4 ? 2 : 1, kZrOps = NG == 8 ? 2 : 1;
+    static constexpr int kScOps = NG == 4 ? 2 : 1;
+    static constexpr int kZrOps = ZP ? (NG * B + 62) / 32 : (NG == 8 ? 2 : 1);
     static constexpr int kCodes = 512 * B;           // packed tile
     static constexpr int kX = kCodes;                 // activation rows, 512 B each, 2 per DMA
     static constexpr int kSc = kX + 1024 * MX;
@@ -85,10 +89,10 @@ __device__ __forceinline__ void dma4(rsrc_t r, uint8_t *lds, uint32_t voff)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, voff, 0, 0, 0);
 }
 
-template <int B, int MX, int GS>
+template <int B, int MX, int GS, int ZP>
 __device__ __forceinline__ void ring_issue(const GemvBufs &bf, int64_t kt, int lane, int64_t ldx, uint8_t *slot)
 {
-    using S = RingSlot<B, MX, GS>;
+    using S = RingSlot<B, MX, GS, ZP>;
     constexpr int NG = S::NG;
     const uint32_t tw = (uint32_t)(kt * (512 * B));
 #pragma unroll
@@ -104,7 +108,20 @@ __device__ __forceinline__ void ring_issue(const GemvBufs &bf, int64_t kt, int l
         dma16(bf.x, slot + S::kX + 1024 * q, (uint32_t)(row * ldx * 2) + xk + 16 * (lane & 31));
     }
     const uint32_t g0 = (uint32_t)(lane * bf.G + NG * kt);  // this lane's row, the tile's first group
-    if constexpr (NG == 2) {
+    if constexpr (ZP) {
+        // the words of this lane's row stream from the one holding bit NG*kt*B on
+        const uint32_t zo = lane * bf.zrow + 4 * (uint32_t)((NG * kt * B) >> 5);
+#pragma unroll
+        for (int e = 0; e < S::kZrOps; ++e) dma4(bf.zr, slot + S::kZr + 256 * e, zo + 4 * e);
+        if constexpr (NG == 2) {
+            dma4(bf.sc, slot + S::kSc, 2 * g0);
+        } else if constexpr (NG == 4) {
+            dma4(bf.sc, slot + S::kSc, 2 * g0);
+            dma4(bf.sc, slot + S::kSc + 256, 2 * g0 + 4);
+        } else {
+            dma16(bf.sc, slot + S::kSc, 2 * g0);
+        }
+    } else if constexpr (NG == 2) {
         dma4(bf.sc, slot + S::kSc, 2 * g0);
         dma4(bf.zr, slot + S::kZr, g0 & ~3u);
     } else if constexpr (NG == 4) {
@@ -127,12 +144,12 @@ __device__ __forceinline__ void wait_vm()
 
 // One 16-row block of problem p on this workgroup; slot0/slot1 are this wave's two ring slots
 // (separate LDS arrays), `red` the workgroup's reduction buffer.
-template <int B, int NW, int D, int MX, int GS>
+template <int B, int NW, int D, int MX, int GS, int ZP>
 __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uint8_t *slot0, uint8_t *slot1,
                                            f4 (*red)[64])
 {
     static_assert(D == 2, "two ring slots");
-    using S = RingSlot<B, MX, GS>;
+    using S = RingSlot<B, MX, GS, ZP>;
     constexpr int NG = S::NG;
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t = lane >> 4, r = lane & 15;
@@ -142,11 +159,17 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
     bf.G = G;
     bf.w = make_rsrc(a.w.packed + rb * KT * (512 * B), KT * (512 * B));
     bf.sc = make_rsrc(a.w.scales + rb * kTileN * G, kTileN * G * 2);
-    bf.zr = make_rsrc(a.w.zeros + rb * kTileN * G, a.zmid ? 0 : kTileN * G);  // implied: none read
+    if constexpr (ZP) {
+        bf.zrow = (uint32_t)a.zrow;
+        bf.zr = make_rsrc(a.w.zeros + rb * kTileN * a.zrow, kTileN * a.zrow);
+    } else {
+        bf.zrow = 0;
+        bf.zr = make_rsrc(a.w.zeros + rb * kTileN * G, a.zmid ? 0 : kTileN * G);  // implied: none read
+    }
     bf.x = make_rsrc(a.x, a.m * a.ldx * 2);  // rows >= m read as zeros
 
     const int64_t nt = KT > wv ? (KT - wv + NW - 1) / NW : 0;  // tiles of this wave
-    ring_issue<B, MX, GS>(bf, wv, lane, a.ldx, slot0);
+    ring_issue<B, MX, GS, ZP>(bf, wv, lane, a.ldx, slot0);
 
     // Activation fragments: lanes of rows >= m keep zeros and never read LDS.
     const bool act = r < a.m;
@@ -165,7 +188,7 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
         const int64_t i = i0 + sd;
         if (i >= nt) break;  // uniform
         const int64_t kt = wv + i * NW;
-        ring_issue<B, MX, GS>(bf, kt + NW, lane, a.ldx, sd == 0 ? slot1 : slot0);
+        ring_issue<B, MX, GS, ZP>(bf, kt + NW, lane, a.ldx, sd == 0 ? slot1 : slot0);
         wait_vm<S::kLoads>();
         const uint8_t *slot = sd == 0 ? slot0 : slot1;
         uint32_t d[2 * B];
@@ -193,8 +216,10 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
             const u4 v = *(const u4 *)(slot + S::kSc + 16 * t);
 #pragma unroll
             for (int i = 0; i < 4; ++i) sc[i][0] = v[i];
-            const uint32_t zpar = (uint32_t)((r * G + 2 * kt) & 3);
-            zw[0] = *(const uint16_t *)(slot + S::kZr + 4 * r + zpar);
+            if constexpr (!ZP) {
+                const uint32_t zpar = (uint32_t)((r * G + 2 * kt) & 3);
+                zw[0] = *(const uint16_t *)(slot + S::kZr + 4 * r + zpar);
+            }
         } else if constexpr (NG == 4) {
             const u4 v0 = *(const u4 *)(slot + S::kSc + 16 * t), v1 = *(const u4 *)(slot + S::kSc + 256 + 16 * t);
 #pragma unroll
@@ -202,7 +227,7 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
                 sc[i][0] = v0[i];
                 sc[i][1] = v1[i];
             }
-            zw[0] = *(const uint32_t *)(slot + S::kZr + 4 * r);
+            if constexpr (!ZP) zw[0] = *(const uint32_t *)(slot + S::kZr + 4 * r);
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -212,12 +237,29 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
                 sc[i][2] = v[2];
                 sc[i][3] = v[3];
             }
-            zw[0] = *(const uint32_t *)(slot + S::kZr + 4 * r);
-            zw[1] = *(const uint32_t *)(slot + S::kZr + 256 + 4 * r);
+            if constexpr (!ZP) {
+                zw[0] = *(const uint32_t *)(slot + S::kZr + 4 * r);
+                zw[1] = *(const uint32_t *)(slot + S::kZr + 256 + 4 * r);
+            }
         }
         GroupConst<B> gc[NG];
+        if constexpr (ZP) {
+            // fields c = 0 .. NG-1 at bits sh + c*B of the words fetched from the row stream
+            uint32_t zp[3] = {0u, 0u, 0u};
 #pragma unroll
-        for (int c = 0; c < NG; ++c) gc[c].set(a.zmid ? (a.zmid & 0xFF) : (zw[c / 4] >> (8 * (c % 4))) & 0xFF);
+            for (int e = 0; e < S::kZrOps; ++e) zp[e] = *(const uint32_t *)(slot + S::kZr + 256 * e + 4 * r);
+            const uint64_t lo = zp[0] | ((uint64_t)zp[1] << 32), hi = zp[1] | ((uint64_t)zp[2] << 32);
+            const int sh = (int)((NG * kt * B) & 31);
+#pragma unroll
+            for (int c = 0; c < NG; ++c) {
+                const int p = sh + c * B;
+                const uint32_t v = p < 32 ? (uint32_t)(lo >> p) : (uint32_t)(hi >> (p - 32));
+                gc[c].set(v & ((1u << B) - 1));
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < NG; ++c) gc[c].set(a.zmid ? (a.zmid & 0xFF) : (zw[c / 4] >> (8 * (c % 4))) & 0xFF);
+        }
         h8 A[8];
         unpack_chunk_groups<B, NG>(d, gc, A);
         mma_tile<NG>(A, X, sc, tot);
@@ -244,23 +286,23 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
 }
 
 // One problem, one workgroup per 16-row block.
-template <int B, int NW, int D, int MX, int GS>
+template <int B, int NW, int D, int MX, int GS, int ZP>
 __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvProblem a)
 {
-    constexpr int pitch = RingSlot<B, MX, GS>::kBytes;
+    constexpr int pitch = RingSlot<B, MX, GS, ZP>::kBytes;
     __shared__ __attribute__((aligned(16))) uint8_t ring0[NW][pitch];
     __shared__ __attribute__((aligned(16))) uint8_t ring1[NW][pitch];
     __shared__ f4 red[NW][64];
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    gemv_block<B, NW, D, MX, GS>(a, blockIdx.x, &ring0[wv][0], &ring1[wv][0], red);
+    gemv_block<B, NW, D, MX, GS, ZP>(a, blockIdx.x, &ring0[wv][0], &ring1[wv][0], red);
 }
 
 // Independent problems (mixed bit widths, one group size) in one launch: workgroup b serves
 // problem p with block0 <= b < block0 + n/16.  The ring slots are sized for 6-bit tiles.
-template <int NW, int D, int MX, int GS>
+template <int NW, int D, int MX, int GS, int ZP>
 __global__ __launch_bounds__(NW * 64) void gemv_batch_kernel(GemvBatch bt)
 {
-    constexpr int pitch = RingSlot<6, MX, GS>::kBytes;
+    constexpr int pitch = RingSlot<6, MX, GS, ZP>::kBytes;
     __shared__ __attribute__((aligned(16))) uint8_t ring0[NW][pitch];
     __shared__ __attribute__((aligned(16))) uint8_t ring1[NW][pitch];
     __shared__ f4 red[NW][64];
@@ -274,15 +316,15 @@ __global__ __launch_bounds__(NW * 64) void gemv_batch_kernel(GemvBatch bt)
     const int64_t rb = b - a.block0;
     uint8_t *s0 = &ring0[wv][0], *s1 = &ring1[wv][0];
     switch (a.bits) {
-    case 2: gemv_block<2, NW, D, MX, GS>(a, rb, s0, s1, red); break;
-    case 3: gemv_block<3, NW, D, MX, GS>(a, rb, s0, s1, red); break;
-    case 4: gemv_block<4, NW, D, MX, GS>(a, rb, s0, s1, red); break;
-    case 5: gemv_block<5, NW, D, MX, GS>(a, rb, s0, s1, red); break;
-    default: gemv_block<6, NW, D, MX, GS>(a, rb, s0, s1, red); break;
+    case 2: gemv_block<2, NW, D, MX, GS, ZP>(a, rb, s0, s1, red); break;
+    case 3: gemv_block<3, NW, D, MX, GS, ZP>(a, rb, s0, s1, red); break;
+    case 4: gemv_block<4, NW, D, MX, GS, ZP>(a, rb, s0, s1, red); break;
+    case 5: gemv_block<5, NW, D, MX, GS, ZP>(a, rb, s0, s1, red); break;
+    default: gemv_block<6, NW, D, MX, GS, ZP>(a, rb, s0, s1, red); break;
     }
 }
 
-template <int B, int MX, int GS>
+template <int B, int MX, int GS, int ZP>
 static hipError_t gemv_mx(const GemvProblem &a, hipStream_t st)
 {
     // Wide matrices have row blocks enough to fill the GPU with 4-wave workgroups (more of
@@ -290,72 +332,84 @@ static hipError_t gemv_mx(const GemvProblem &a, hipStream_t st)
     // (Eight waves with an 8-row-pair activation ring would exceed the 160 KB of LDS.)
     const int64_t blocks = a.n / kTileN;
     if constexpr (MX == 8) {
-        hipLaunchKernelGGL((gemv_kernel<B, 4, 2, MX, GS>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((gemv_kernel<B, 4, 2, MX, GS, ZP>), dim3((unsigned)blocks), dim3(256), 0, st, a);
     } else {
         if (blocks >= 512)
-            hipLaunchKernelGGL((gemv_kernel<B, 4, 2, MX, GS>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+            hipLaunchKernelGGL((gemv_kernel<B, 4, 2, MX, GS, ZP>), dim3((unsigned)blocks), dim3(256), 0, st, a);
         else
-            hipLaunchKernelGGL((gemv_kernel<B, 8, 2, MX, GS>), dim3((unsigned)blocks), dim3(512), 0, st, a);
+            hipLaunchKernelGGL((gemv_kernel<B, 8, 2, MX, GS, ZP>), dim3((unsigned)blocks), dim3(512), 0, st, a);
     }
     return hipGetLastError();
 }
 
-template <int B, int GS>
+template <int B, int GS, int ZP>
 static hipError_t gemv_bits_gs(const GemvProblem &a, hipStream_t st)
 {
-    if (a.m <= 2) return gemv_mx<B, 1, GS>(a, st);
-    if (a.m <= 4) return gemv_mx<B, 2, GS>(a, st);
-    if (a.m <= 8) return gemv_mx<B, 4, GS>(a, st);
-    return gemv_mx<B, 8, GS>(a, st);
+    if (a.m <= 2) return gemv_mx<B, 1, GS, ZP>(a, st);
+    if (a.m <= 4) return gemv_mx<B, 2, GS, ZP>(a, st);
+    if (a.m <= 8) return gemv_mx<B, 4, GS, ZP>(a, st);
+    return gemv_mx<B, 8, GS, ZP>(a, st);
 }
-template <int B>
+template <int B, int ZP>
 static hipError_t gemv_bits(const GemvProblem &a, hipStream_t st)
 {
-    if (a.gs == 32) return gemv_bits_gs<B, 32>(a, st);
-    if (a.gs == 64) return gemv_bits_gs<B, 64>(a, st);
-    return gemv_bits_gs<B, 128>(a, st);
+    if (a.gs == 32) return gemv_bits_gs<B, 32, ZP>(a, st);
+    if (a.gs == 64) return gemv_bits_gs<B, 64, ZP>(a, st);
+    return gemv_bits_gs<B, 128, ZP>(a, st);
 }
 
-hipError_t launch_gemv(const GemvProblem &a, hipStream_t st)
+template <int ZP>
+static hipError_t gemv_zp(const GemvProblem &a, hipStream_t st)
 {
     switch (a.bits) {
-    case 2: return gemv_bits<2>(a, st);
-    case 3: return gemv_bits<3>(a, st);
-    case 4: return gemv_bits<4>(a, st);
-    case 5: return gemv_bits<5>(a, st);
-    case 6: return gemv_bits<6>(a, st);
+    case 2: return gemv_bits<2, ZP>(a, st);
+    case 3: return gemv_bits<3, ZP>(a, st);
+    case 4: return gemv_bits<4, ZP>(a, st);
+    case 5: return gemv_bits<5, ZP>(a, st);
+    case 6: return gemv_bits<6, ZP>(a, st);
     }
     return hipErrorInvalidValue;
 }
 
-template <int MX, int GS>
+hipError_t launch_gemv(const GemvProblem &a, hipStream_t st)
+{
+    return a.zrow ? gemv_zp<1>(a, st) : gemv_zp<0>(a, st);
+}
+
+template <int MX, int GS, int ZP>
 static hipError_t gemv_batch_mx(const GemvBatch &b, int64_t blocks, hipStream_t st)
 {
     if constexpr (MX >= 4) {
-        hipLaunchKernelGGL((gemv_batch_kernel<4, 2, MX, GS>), dim3((unsigned)blocks), dim3(256), 0, st, b);
+        hipLaunchKernelGGL((gemv_batch_kernel<4, 2, MX, GS, ZP>), dim3((unsigned)blocks), dim3(256), 0, st, b);
     } else {
         if (blocks >= 512)
-            hipLaunchKernelGGL((gemv_batch_kernel<4, 2, MX, GS>), dim3((unsigned)blocks), dim3(256), 0, st, b);
+            hipLaunchKernelGGL((gemv_batch_kernel<4, 2, MX, GS, ZP>), dim3((unsigned)blocks), dim3(256), 0, st, b);
         else
-            hipLaunchKernelGGL((gemv_batch_kernel<8, 2, MX, GS>), dim3((unsigned)blocks), dim3(512), 0, st, b);
+            hipLaunchKernelGGL((gemv_batch_kernel<8, 2, MX, GS, ZP>), dim3((unsigned)blocks), dim3(512), 0, st, b);
     }
     return hipGetLastError();
 }
 
-template <int GS>
+template <int GS, int ZP>
 static hipError_t gemv_batch_gs(const GemvBatch &b, int64_t blocks, int m_max, hipStream_t st)
 {
-    if (m_max <= 2) return gemv_batch_mx<1, GS>(b, blocks, st);
-    if (m_max <= 4) return gemv_batch_mx<2, GS>(b, blocks, st);
-    if (m_max <= 8) return gemv_batch_mx<4, GS>(b, blocks, st);
-    return gemv_batch_mx<8, GS>(b, blocks, st);
+    if (m_max <= 2) return gemv_batch_mx<1, GS, ZP>(b, blocks, st);
+    if (m_max <= 4) return gemv_batch_mx<2, GS, ZP>(b, blocks, st);
+    if (m_max <= 8) return gemv_batch_mx<4, GS, ZP>(b, blocks, st);
+    return gemv_batch_mx<8, GS, ZP>(b, blocks, st);
+}
+
+template <int ZP>
+static hipError_t gemv_batch_zp(const GemvBatch &b, int64_t blocks, int m_max, hipStream_t st)
+{
+    if (b.p[0].gs == 32) return gemv_batch_gs<32, ZP>(b, blocks, m_max, st);
+    if (b.p[0].gs == 64) return gemv_batch_gs<64, ZP>(b, blocks, m_max, st);
+    return gemv_batch_gs<128, ZP>(b, blocks, m_max, st);
 }
 
 hipError_t launch_gemv_batch(const GemvBatch &b, int64_t blocks, int m_max, hipStream_t st)
 {
-    if (b.p[0].gs == 32) return gemv_batch_gs<32>(b, blocks, m_max, st);
-    if (b.p[0].gs == 64) return gemv_batch_gs<64>(b, blocks, m_max, st);
-    return gemv_batch_gs<128>(b, blocks, m_max, st);
+    return b.p[0].zrow ? gemv_batch_zp<1>(b, blocks, m_max, st) : gemv_batch_zp<0>(b, blocks, m_max, st);
 }
 
 }  // namespace qp

@@ -42,6 +42,8 @@ hipError_t launch_pack(int bits, int layout, const uint8_t *codes, int64_t n, in
                        uint8_t *out, hipStream_t st);
 hipError_t launch_unpack(int bits, int layout, const uint8_t *in, int64_t n, int64_t k,
                          uint8_t *codes, hipStream_t st);
+hipError_t launch_pack_zeros(int bits, const uint8_t *zeros, int64_t n, int64_t G, int64_t row_bytes,
+                             uint8_t *out, hipStream_t st);
 
 struct ExpertPtrs {
     const uint8_t *packed;
@@ -63,7 +65,7 @@ struct GemvProblem {
     int32_t bits;
     uint32_t zmid;   // 0: stored zero points; else the implied pair (2^(b-1) in both bytes)
     int32_t gs;      // group size: 32, 64 or 128
-    int32_t pad;
+    int32_t zrow;    // bytes per row of b-bit zero points (0: one byte per group)
     int64_t block0;  // batch: first workgroup of this problem
 };
 struct GemvBatch {
