@@ -12,8 +12,9 @@ The roofline object covers the kernel with the largest share of the step, timed 
 HIP events around a graph of back-to-back launches on its own stream.  A secondary line
 measures the prefill dequant-GEMM (M=512, K=8192, N=28672, 4-bit + 0.1% outliers) in
 TFLOP/s.  Further lines: the 4-bit 4096 x 4096 GEMV at M=1, the same layer at 2 and 3 bits
-with symmetric groups (no zero points) and with groups of 32 and 64, a Llama-7B-shaped decode
-stack and a 16-expert FFN.
+with symmetric groups (no zero points), with groups of 32 and 64, and with zero points kept in
+b bits, a Llama-7B-shaped decode stack, a 16-expert FFN, and decode attention over a quantized
+KV cache.
 cpu_baseline times the CPU oracle on the same step.
 """
 from __future__ import annotations
@@ -527,6 +528,23 @@ def main():
                                                          bytes=bs, bits_per_weight=round(8 * bs / (N * K), 4))
         del cs, hs, wsy
     extra["gemv_4096_small_groups_m1"] = small
+    log("bench: 4096x4096 GEMV at M=1 with zero points in b bits")
+    pz = {}
+    for b, g in ((2, 32), (3, 64), (5, 64), (6, 128)):
+        dz = q.desc(b, N, K, group_size=g, zero_mode=q.QP_ZERO_PACKED)
+        _, wz = quantize_pack(q, torch, workloads.layer_weights(2), b, g=g)
+        zp = torch.empty(q.qp_zero_bytes(dz), dtype=torch.uint8, device=dev)
+        q.qpack_pack_zeros(dz, wz["zeros"], zp)
+        cs = [dict(packed=wz["packed"].clone(), scales=wz["scales"].clone(), zeros=zp.clone())
+              for _ in range(args.copies)]
+        hs = [q.weight(c["packed"], c["scales"], c["zeros"]) for c in cs]
+        ms = time_graph(torch, lambda i: q.qlinear_gemv(dz, hs[i % args.copies], x1, K, 1, y1, N), 4 * args.copies,
+                        stream)
+        bz = N * K * b // 8 + (N * K // g) * 2 + q.qp_zero_bytes(dz)
+        pz[f"b{b}_g{g}"] = dict(us=round(ms * 1e3, 3), GBps=round(bz / (ms * 1e-3) / 1e9, 1), bytes=bz,
+                                bits_per_weight=round(8 * bz / (N * K), 4))
+        del cs, hs, wz, zp
+    extra["gemv_4096_packed_zeros_m1"] = pz
     if not args.no_stack:
         log("bench: Llama-7B-shaped 32-layer decode stack at M=1")
         extra["stack_llama7b_m1"] = bench_stack(q, torch, workloads, stream)
