@@ -96,11 +96,12 @@ TRAFFIC_FILE = "profiles/pmc_traffic_gemv4096_gemm_prefill.md"
 
 
 def gemv_kernel_name(bits: int, m: int, n: int) -> str:
-    """Template instance qlinear_gemv launches for (bits, m, n): gemv_kernel<B, waves, ring
-    depth, activation row pairs> (the launcher in qmm_small.hip picks them the same way)."""
+    """Template instance qlinear_gemv launches for (bits, m, n) with groups of 128 and byte
+    zero points: gemv_kernel<B, waves, ring depth, activation row pairs, group size, b-bit
+    zero points> (the launcher in qmm_small.hip picks them the same way)."""
     mx = 1 if m <= 2 else 2 if m <= 4 else 4 if m <= 8 else 8
     nw = 4 if (n // 16 >= 512 or mx == 8) else 8
-    return f"qp::gemv_kernel<{bits}, {nw}, 2, {mx}, 128>"
+    return f"qp::gemv_kernel<{bits}, {nw}, 2, {mx}, 128, 0>"
 
 
 def measured_traffic(kernel: str):
