@@ -110,7 +110,8 @@ static qp_status check_kv(const qkv_desc *d)
     if (d->q_heads / d->kv_heads > 16) return fail(QP_ERR_UNSUPPORTED, "more than 16 query heads per kv head");
     if (d->capacity < 32 || d->capacity % 32 != 0 || d->capacity >= (1LL << 24))
         return fail(QP_ERR_INVALID_ARG, "capacity=%lld must be a multiple of 32 below 2^24", (long long)d->capacity);
-    if ((int64_t)d->batch * d->kv_heads > (1LL << 16)) return fail(QP_ERR_INVALID_ARG, "batch*kv_heads above 65536");
+    if ((int64_t)d->batch * d->kv_heads > (1LL << 16) || d->batch > 65535 || d->kv_heads > 65535)
+        return fail(QP_ERR_INVALID_ARG, "batch*kv_heads above 65536 (or batch or kv_heads above 65535)");
     return QP_OK;
 }
 
