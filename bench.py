@@ -316,14 +316,15 @@ def kv_call_bytes(q, d, lens) -> int:
 
 
 def bench_kv(q, torch, workloads, stream, min_bytes: int = 1 << 30):
-    """Decode attention over the quantized KV cache (INT4 K, INT8 V, groups of 64, fp32
-    scales): the KV page's 7B MHA layer at a 32K context and a GQA layer with four 8K
-    sequences.  Each layer's cache is quantized once through qkv_quantize; the timed graph
+    """Decode attention over the quantized KV cache (groups of 64, fp32 scales): INT4 K with
+    INT8 V on the KV page's 7B MHA layer at a 32K context and on a GQA layer with four 8K
+    sequences, and the MHA layer all INT8 and all INT4.  Each layer's cache is quantized once through qkv_quantize; the timed graph
     rotates over enough distinct layer caches (>= 1 GiB) that the cache streams from HBM."""
     out = {}
-    for name in ("KV_MHA", "KV_GQA"):
+    for key, name, kb, vb in (("kv_mha", "KV_MHA", 4, 8), ("kv_gqa", "KV_GQA", 4, 8), ("kv_mha_k8v8", "KV_MHA", 8, 8),
+                              ("kv_mha_k4v4", "KV_MHA", 4, 4)):
         cfg = getattr(workloads, name)
-        d = q.kv_desc(cfg["batch"], cfg["q_heads"], cfg["kv_heads"], cfg["capacity"], 4, 8, 64, 64)
+        d = q.kv_desc(cfg["batch"], cfg["q_heads"], cfg["kv_heads"], cfg["capacity"], kb, vb, 64, 64)
         rows = cfg["batch"] * cfg["kv_heads"] * cfg["capacity"]
         lens = np.full(cfg["batch"], cfg["capacity"], np.int32)
         nbytes = kv_call_bytes(q, d, lens)
@@ -357,11 +358,11 @@ def bench_kv(q, torch, workloads, stream, min_bytes: int = 1 << 30):
         ms = time_graph(torch, call, 2 * layers, stream)
         flops = 4 * int(lens.sum()) * cfg["q_heads"] * 128
         gbps = nbytes / (ms * 1e-3) / 1e9
-        out[name.lower()] = dict(us=round(ms * 1e3, 2), GBps=round(gbps, 1), frac_hbm_peak=round(gbps / HBM_PEAK_GBS, 4),
-                                 TFLOPs=round(flops / (ms * 1e-3) / 1e12, 2), bytes=nbytes, layers_rotated=layers,
-                                 shape=dict(batch=cfg["batch"], q_heads=cfg["q_heads"], kv_heads=cfg["kv_heads"],
-                                            tokens=cfg["capacity"], k_bits=4, v_bits=8, group=64),
-                                 kernel=f"qp::kv_attn_kernel<4, 8, 64, 64>")
+        out[key] = dict(us=round(ms * 1e3, 2), GBps=round(gbps, 1), frac_hbm_peak=round(gbps / HBM_PEAK_GBS, 4),
+                        TFLOPs=round(flops / (ms * 1e-3) / 1e12, 2), bytes=nbytes, layers_rotated=layers,
+                        shape=dict(batch=cfg["batch"], q_heads=cfg["q_heads"], kv_heads=cfg["kv_heads"],
+                                   tokens=cfg["capacity"], k_bits=kb, v_bits=vb, group=64),
+                        kernel=f"qp::kv_attn_kernel<{kb}, {vb}, 64, 64>")
         del caches, o, ws
     return out
 
