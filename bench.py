@@ -15,7 +15,8 @@ TFLOP/s.  Further lines: the 4-bit 4096 x 4096 GEMV at M=1, the same layer at 2 
 with symmetric groups (no zero points), with groups of 32 and 64, and with zero points kept in
 b bits, a Llama-7B-shaped decode stack, a 16-expert FFN, and decode attention over a quantized
 KV cache.
-cpu_baseline times the CPU oracle on the same step.
+cpu_baseline times the CPU oracle on the same step; cpu_baseline_1thread times one step of it on
+one thread.
 """
 from __future__ import annotations
 
@@ -560,7 +561,7 @@ def main():
     log("bench: 1 GiB device copy")
     extra["copy_GBps"] = round(copy_gbps(torch), 1)
 
-    cpu = None
+    cpu = cpu1 = None
     if not args.no_cpu:
         import oracle
         log("bench: CPU oracle baseline")
@@ -579,6 +580,17 @@ def main():
         cpu = dict(value=round(step_bytes * reps / dt / 1e9, 4), unit="GB/s", cores=oracle.num_threads(),
                    kind="oracle",
                    sample=f"{reps} full steps (12 fp64 GEMVs over the oracle's own codes), {dt:.1f} s")
+        # the same oracle on one thread, over one step
+        threads = oracle.num_threads()
+        oracle.set_num_threads(1)
+        t0 = time.perf_counter()
+        for b in bits_list:
+            for m in m_list:
+                oracle.linear(xs[m], refs[b])
+        dt1 = time.perf_counter() - t0
+        oracle.set_num_threads(threads)
+        cpu1 = dict(value=round(step_bytes / dt1 / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                    sample=f"1 full step (12 fp64 GEMVs over the oracle's own codes) on one thread, {dt1:.1f} s")
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -591,6 +603,7 @@ def main():
                    "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "cpu_baseline_1thread": cpu1,
         "per_kernel": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in per.items()},
         **extra,
     }

@@ -104,6 +104,8 @@ def lib():
         L.or_kv_bytes.argtypes = [dbl] * 5
         L.or_num_threads.restype = i32
         L.or_num_threads.argtypes = []
+        L.or_set_num_threads.restype = None
+        L.or_set_num_threads.argtypes = [i32]
         _lib = L
     return _lib
 
@@ -393,3 +395,7 @@ def kv_bytes(layers, kv_heads, head_dim, tokens, bytes_per_elem) -> float:
 
 def num_threads() -> int:
     return lib().or_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    lib().or_set_num_threads(int(n))

@@ -755,6 +755,16 @@ double or_kv_bytes(double layers, double kv_heads, double head_dim, double token
     return 2.0 * layers * kv_heads * head_dim * tokens * bytes_per_elem;
 }
 
+/* Threads the parallel loops above use from now on (n >= 1). */
+void or_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Threads the parallel loops above use. */
 int or_num_threads(void)
 {
