@@ -242,10 +242,12 @@ qp_status qlinear_gemm(const qp_weight_desc *desc, const qp_weight *w, const uin
  * Grouped dequant-GEMM over routed experts (MoE page s4.2).  All experts share `desc`
  * (layout QP_LAYOUT_DEVICE).  `experts` is a HOST array of n_experts (<= 64) weights.
  *  row_src         int32 [rows] device: token (row of x) feeding sorted row r.
- *  expert_offsets  int32 [n_experts+1] device: rows of expert e are
- *                  [expert_offsets[e], expert_offsets[e+1]); offsets[n_experts] <= rows.
- *  rows            host upper bound on expert_offsets[n_experts] (sizes nothing but
- *                  argument checks).
+ *  expert_offsets  int32 [n_experts+1] device, non-decreasing, from >= 0 to <= rows: rows
+ *                  of expert e are [expert_offsets[e], expert_offsets[e+1]).
+ *  rows            host upper bound on expert_offsets[n_experts].  It sizes the launch:
+ *                  one workgroup per weight tile and per row tile that some routing of
+ *                  `rows` rows could occupy; the tiles the routing leaves empty return
+ *                  at once.
  *  epilogue        QP_EPI_NONE: y fp16 [rows][ldy];
  *                  QP_EPI_SWIGLU: row blocks 2i and 2i+1 of each expert matrix hold gate
  *                  rows 16i..16i+15 and up rows 16i..16i+15; y fp16 [rows][ldy] gets

@@ -211,19 +211,24 @@ def test_grouped_projections_parity(bits):
             assert rel_err(yd[rows], r) <= TOL, (e, report(yd[rows], r))
 
 
-@pytest.mark.parametrize("sizes", ([70, 33, 32, 1, 0, 15, 16, 17], [150, 129, 0, 5]),
-                         ids=("small-geometry", "layer-geometry"))
-def test_grouped_row_tiles(sizes):
+@pytest.mark.parametrize("sizes,base,slack", (([70, 33, 32, 1, 0, 15, 16, 17], 0, 0),
+                                                ([150, 129, 0, 5], 0, 0),
+                                                ([0, 0, 0, 0, 0, 0, 0, 97], 0, 0),
+                                                ([40, 0, 31, 9], 7, 50)),
+                         ids=("small-geometry", "layer-geometry", "last-expert-only", "offset-base-and-slack"))
+def test_grouped_row_tiles(sizes, base, slack):
     """Expert row counts at and around the 32- and 128-row tile edges, on both workgroup
-    geometries (at most 32 rows per expert on average selects the 4-wave, 32-row one)."""
+    geometries (at most 32 rows per expert on average selects the 4-wave, 32-row one); all
+    rows on the last expert; and a routing that starts at sorted row `base` under a row
+    bound `slack` rows above its end (rows outside the routing stay untouched)."""
     torch, q = gpu()
     E, D, N = len(sizes), 256, 512
-    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
-    R = int(offsets[-1])
+    offsets = (base + np.concatenate([[0], np.cumsum(sizes)])).astype(np.int32)
+    R = int(offsets[-1]) + slack
     x = workloads.activations_fp16(R, D, 71)
     raw = [workloads.weights_fp16(N, D, 700 + e) for e in range(E)]
     ws = [GpuWeight(w, 4) for w in raw]
-    y = torch.empty((R, N), dtype=torch.float32, device="cuda")
+    y = torch.full((R, N), 7.0, dtype=torch.float32, device="cuda")
     q.qlinear_grouped_gemm(ws[0].desc, [w.handle() for w in ws], to_dev_fp16(x), D, None, dev(offsets), R,
                            q.QP_EPI_ROWS_F32, y, N)
     torch.cuda.synchronize()
@@ -233,6 +238,8 @@ def test_grouped_row_tiles(sizes):
         if len(rows):
             r = oracle.linear(x[rows], oracle.quantize(raw[e], 4))
             assert rel_err(y[rows], r) <= TOL, (e, report(y[rows], r))
+    outside = np.r_[0:offsets[0], offsets[-1]:R]
+    assert np.all(y[outside] == 7.0)
 
 
 @pytest.mark.parametrize("bits", (4, 2))

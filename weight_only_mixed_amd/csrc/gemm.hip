@@ -32,6 +32,7 @@
 //
 // Workgroups are ordered so that the activation blocks of one weight tile run on the same XCD
 // (block b runs on XCD b % 8), where they share that XCD's L2 copy of the packed weights.
+#include <algorithm>
 #include <utility>
 
 #include "bufio.h"
@@ -562,7 +563,8 @@ struct TileRect {
 struct TilePlan {
     TileRect r[2];
     int32_t nr;
-    int32_t mh;  // activation rows per tile
+    int32_t mh;       // activation rows per tile
+    int32_t experts;  // grouped: entries of the offsets table, minus one
 };
 
 __device__ __forceinline__ void plan_tile(const TilePlan &p, int64_t b, int64_t &nt, int64_t &m0)
@@ -598,12 +600,29 @@ __global__ __launch_bounds__(GE::kWaves * 64) __attribute__((amdgpu_waves_per_eu
     int64_t nt, m0, mend;  // weight tile; sorted rows [m0, mend) of this workgroup
     int e = 0;
     if constexpr (GROUPED) {
-        // blockIdx = (weight tile, expert, kMRows-row tile of the expert's rows)
-        e = blockIdx.y;
-        const int64_t r0 = a.offsets[e], r1 = a.offsets[e + 1];
+        // blockIdx = (weight tile, work item).  Work items number the occupied kMRows-row
+        // tiles of all experts in expert order; lane i of every wave takes expert i's tile
+        // count, a wave scan gives each expert its first work item, and the expert whose
+        // range holds blockIdx.y serves this workgroup.  Surplus items return at once.
+        const int32_t w = (int32_t)blockIdx.y;
+        int32_t tiles = 0;
+        if (lane < plan.experts) {
+            const int32_t c = a.offsets[lane + 1] - a.offsets[lane];
+            tiles = c > 0 ? (c + kMRows - 1) / kMRows : 0;
+        }
+        int32_t incl = tiles;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int32_t y = __shfl_up(incl, off);
+            if (lane >= off) incl += y;
+        }
+        const uint64_t hit = __ballot(lane < plan.experts && w >= incl - tiles && w < incl);
+        if (!hit) return;  // the whole workgroup
+        e = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+        const int32_t first = __shfl(incl - tiles, e);
+        const int64_t r1 = a.offsets[e + 1];
         nt = blockIdx.x;
-        m0 = r0 + (int64_t)blockIdx.z * kMRows;
-        if (m0 >= r1) return;  // the whole workgroup: this expert has fewer row tiles
+        m0 = a.offsets[e] + (int64_t)(w - first) * kMRows;
         mend = r1 < m0 + kMRows ? r1 : m0 + kMRows;
     } else {
         plan_tile(plan, blockIdx.x, nt, m0);
@@ -828,16 +847,22 @@ hipError_t launch_gemm(int bits, const GemmArgs &a, hipStream_t st)
     return hipErrorInvalidValue;
 }
 
-// Routed experts: one workgroup per (weight tile, expert, row tile of the expert's sorted
-// rows); the row tiles are sized for the worst case (all rows on one expert) and the surplus
-// workgroups return at once.  With at most 32 rows per expert on average the small geometry
-// runs (three 4-wave workgroups per CU instead of one 8-wave one), else the layer's.
+// Routed experts: one workgroup per (weight tile, occupied row tile of an expert's sorted
+// rows).  The row counts live on the device, so the grid holds the most row tiles any routing
+// of a.m rows over the experts can occupy, sum over e of ceil(c_e / T) <= (a.m + E (T - 1)) / T,
+// and the surplus workgroups return at once.  With at most 32 rows per expert on average the
+// small geometry runs (three 4-wave workgroups per CU instead of one 8-wave one), else the
+// layer's.
 template <int B, int MODE, typename GE>
 static hipError_t grouped_geo(int n_experts, const GemmArgs &a, hipStream_t st)
 {
-    const int64_t n_tiles = (a.n + GE::kNT - 1) / GE::kNT, m_tiles = (a.m + GE::kMRows - 1) / GE::kMRows;
-    hipLaunchKernelGGL((gemm_kernel<B, MODE, 0, GE>), dim3((unsigned)n_tiles, (unsigned)n_experts, (unsigned)m_tiles),
-                       dim3(GE::kWaves * 64), 0, st, a, TilePlan{});
+    constexpr int64_t T = GE::kMRows;
+    const int64_t n_tiles = (a.n + GE::kNT - 1) / GE::kNT;
+    const int64_t items = std::min<int64_t>((a.m + n_experts * (T - 1)) / T, n_experts * ((a.m + T - 1) / T));
+    TilePlan plan{};
+    plan.experts = n_experts;
+    hipLaunchKernelGGL((gemm_kernel<B, MODE, 0, GE>), dim3((unsigned)n_tiles, (unsigned)items), dim3(GE::kWaves * 64),
+                       0, st, a, plan);
     return hipGetLastError();
 }
 template <int B, int MODE>
