@@ -507,17 +507,24 @@ __global__ __launch_bounds__(kKvWaves * 64) void kv_attn_kernel(KvAttnArgs a)
     }
 }
 
-// Merge the chunks of one (sequence, query head): one thread per d.  The chunk maxima and
-// sums are read once into LDS by all threads together, and the partial outputs are read eight
-// chunks at a time so their loads are in flight together (the merge is latency-bound).
+// Merge the chunks of one (sequence, query head): one thread per d.  The merge is bound by
+// memory latency, so the partial outputs of the first kKvPre chunks are loaded together with
+// the chunk maxima and sums, before anything depends on them; the maxima and sums are read
+// once into LDS by all threads together, the maximum is reduced by wave shuffles, and the
+// partial outputs of further chunks are read eight at a time.
 constexpr int kKvMaxSplit = 1024;
+constexpr int kKvPre = 16;
 
 __global__ __launch_bounds__(kD) void kv_combine_kernel(KvAttnArgs a)
 {
-    __shared__ float sm_e[kKvMaxSplit], sm_s[kKvMaxSplit], red[kD];
+    __shared__ float sm_e[kKvMaxSplit], sm_s[kKvMaxSplit], red[kD / 64];
     const int64_t bh = blockIdx.x;
     const int d = threadIdx.x, ns = a.nsplit;
     const float *ml = a.part_ml + 2 * bh * ns;
+    const float *po = a.part_o + bh * ns * kD + d;
+    float pre[kKvPre];
+#pragma unroll
+    for (int i = 0; i < kKvPre; ++i) pre[i] = i < ns ? po[(int64_t)i * kD] : 0.f;
     float M = -__builtin_inff();
     for (int s = d; s < ns; s += kD) {
         const float m = ml[2 * s];
@@ -525,21 +532,26 @@ __global__ __launch_bounds__(kD) void kv_combine_kernel(KvAttnArgs a)
         sm_s[s] = ml[2 * s + 1];
         M = __builtin_fmaxf(M, m);
     }
-    red[d] = M;
-    __syncthreads();
 #pragma unroll
-    for (int w = kD / 2; w >= 1; w >>= 1) {
-        if (d < w) red[d] = __builtin_fmaxf(red[d], red[d + w]);
-        __syncthreads();
-    }
+    for (int off = 32; off >= 1; off >>= 1) M = __builtin_fmaxf(M, __shfl_xor(M, off));
+    if ((d & 63) == 0) red[d >> 6] = M;
+    __syncthreads();
     M = red[0];
+#pragma unroll
+    for (int w = 1; w < kD / 64; ++w) M = __builtin_fmaxf(M, red[w]);
     float y = 0.f;
     if (M != -__builtin_inff()) {
         for (int s = d; s < ns; s += kD) sm_e[s] = __builtin_amdgcn_exp2f(sm_e[s] - M);
         __syncthreads();
-        const float *po = a.part_o + bh * ns * kD + d;
         float o = 0.f, S = 0.f;
-        int s = 0;
+#pragma unroll
+        for (int i = 0; i < kKvPre; ++i) {
+            if (i < ns) {
+                o = __builtin_fmaf(sm_e[i], pre[i], o);
+                S = __builtin_fmaf(sm_e[i], sm_s[i], S);
+            }
+        }
+        int s = kKvPre;
         for (; s + 8 <= ns; s += 8) {
             float v[8];
 #pragma unroll
