@@ -385,8 +385,8 @@ def main():
                          "hardware-counter runs; prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part "
-              "of this build", flush=True)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
+              "multi-GPU path", flush=True)
         sys.exit(2)
 
     import torch

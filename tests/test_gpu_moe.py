@@ -59,11 +59,11 @@ def test_dispatch_exact():
 class Experts:
     """Gate/up interleaved by 16-row blocks, and down, quantized and packed on the GPU."""
 
-    def __init__(self, E, D, F, bits, config):
+    def __init__(self, E, D, F, bits, stream):
         self.bits, self.D, self.F = bits, D, F
         self.gate_up, self.down, self.raw = [], [], []
         for e in range(E):
-            g, u, d = workloads.moe_expert(e, D, F, config)
+            g, u, d = workloads.moe_expert(e, D, F, stream)
             self.raw.append((g, u, d))
             self.gate_up.append(GpuWeight(workloads.interleave_row_blocks(g, u), bits))
             self.down.append(GpuWeight(d, bits))
@@ -170,7 +170,7 @@ def test_grouped_projections_parity(bits):
     on gathered token rows, down on the oracle's fp16 intermediate."""
     torch, q = gpu()
     E, D, F, T = 5, 512, 768, 37
-    ex = Experts(E, D, F, bits, config=50 + bits)
+    ex = Experts(E, D, F, bits, stream=50 + bits)
     x = workloads.activations_fp16(T, D, 51)
     ids, wts = small_routing(T, E, 52)
     order, offsets, row_src, _ = expected_dispatch(ids, E)
@@ -248,7 +248,7 @@ def test_swiglu_epilogue_rounding(bits):
     at near-ties, where it may be the other neighbour (never more than one ulp)."""
     torch, q = gpu()
     E, D, F, T = 4, 512, 512, 40
-    ex = Experts(E, D, F, bits, config=70 + bits)
+    ex = Experts(E, D, F, bits, stream=70 + bits)
     x = workloads.activations_fp16(T, D, 71)
     ids, _ = workloads.zipf_routing(T, E, 2, 1.1, 72)
     order, offsets, row_src, _ = expected_dispatch(ids, E)
@@ -274,7 +274,7 @@ def test_swiglu_epilogue_rounding(bits):
 @pytest.mark.parametrize("bits", (4, 2, 6))
 def test_moe_ffn_small(bits):
     E, D, F, T = 5, 512, 768, 37
-    ex = Experts(E, D, F, bits, config=50 + bits)
+    ex = Experts(E, D, F, bits, stream=50 + bits)
     x = workloads.activations_fp16(T, D, 51)
     ids, wts = small_routing(T, E, 52)
     y = run_ffn(ex, x, ids, wts)
@@ -285,7 +285,7 @@ def test_moe_ffn_small(bits):
 def test_moe_all_tokens_one_expert_many_tiles():
     """130 rows on one expert: more than the 128-row pass of the grouped kernel."""
     E, D, F, T = 2, 256, 512, 130
-    ex = Experts(E, D, F, 4, config=60)
+    ex = Experts(E, D, F, 4, stream=60)
     x = workloads.activations_fp16(T, D, 61)
     ids = np.zeros((T, 1), np.int32)
     wts = np.ones((T, 1), np.float32)
@@ -295,12 +295,12 @@ def test_moe_all_tokens_one_expert_many_tiles():
 
 
 @pytest.mark.timeout(900)
-def test_moe_config_full_sampled():
+def test_moe_ffn_full_sampled():
     """16 experts, d_model 4096, d_ff 14336, 128 tokens top-2 Zipf(1.1): the whole FFN on the
     GPU in the launch sequence the benchmark uses; 4 tokens recomputed by the oracle."""
     E, D, F = workloads.MOE_EXPERTS, workloads.MOE_DMODEL, workloads.MOE_DFF
     x, ids, wts = workloads.moe_inputs()
-    ex = Experts(E, D, F, 4, config=5)
+    ex = Experts(E, D, F, 4, stream=5)
     y = run_ffn(ex, x, ids, wts)
     assert np.isfinite(y).all()
     pick = np.array([0, 5, 77, 127])

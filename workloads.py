@@ -16,8 +16,11 @@ Recipe (numpy PCG64 via ``numpy.random.default_rng``):
   * KV cache: K and V head vectors (head_dim 128) ~ N(0, 1) rounded to fp16 -- the KV page
     (s1.2) describes projected K/V as concentrated without extreme outliers; queries ~ N(0, 1);
     sequence lengths uniform in [lo, hi] for ragged batches.
-Seeds: 1000*config + 16*layer + matrix_index; activations use seed + 500000.  The KV cache
-is config 6 (matrix 0 = K, 1 = V; queries and lengths use the activation offset).
+Seeds: 1000*w + 16*layer + matrix_index, where w numbers the seed stream of a workload:
+1 the 4096 x 4096 layer at 4 bits, 2 the same layer swept over 2/3/5/6 bits and M = 1/4/8,
+3 the 32-layer Llama-7B-shaped stack, 4 the M = 512 prefill GEMM, 5 the 16-expert FFN, 6 the
+quantized KV cache (matrix 0 = K, 1 = V; queries and lengths use the activation offset).
+Activations use seed + 500000.
 """
 from __future__ import annotations
 
@@ -29,8 +32,8 @@ ACT_SEED_OFFSET = 500_000
 LLAMA_MATRICES = ("q", "k", "v", "o", "gate", "up", "down")
 
 
-def seed_for(config: int, layer: int = 0, matrix: int = 0) -> int:
-    return 1000 * config + 16 * layer + matrix
+def seed_for(stream: int, layer: int = 0, matrix: int = 0) -> int:
+    return 1000 * stream + 16 * layer + matrix
 
 
 def normal_fp16(shape, seed: int, std: float = 1.0) -> np.ndarray:
@@ -104,28 +107,28 @@ def interleave_row_blocks(a: np.ndarray, b: np.ndarray, block: int = 16) -> np.n
 # Named workloads
 # ---------------------------------------------------------------------------------
 
-# Single 4096x4096 layer (configurations 1 and 2).
+# Single 4096x4096 layer (seed streams 1 and 2).
 LAYER_N = 4096
 LAYER_K = 4096
 SWEEP_BITS = (2, 3, 5, 6)
 SWEEP_M = (1, 4, 8)
 
-# Llama-7B-shaped decode stack (configuration 3).
+# Llama-7B-shaped decode stack (seed stream 3).
 STACK_LAYERS = 32
 STACK_SHAPES = {  # (N, K) per matrix
     "q": (4096, 4096), "k": (4096, 4096), "v": (4096, 4096), "o": (4096, 4096),
     "gate": (11008, 4096), "up": (11008, 4096), "down": (4096, 11008),
 }
 
-# Prefill-shaped dequant-GEMM with outliers (configuration 4).
+# Prefill-shaped dequant-GEMM with outliers (seed stream 4).
 PREFILL_M, PREFILL_K, PREFILL_N = 512, 8192, 28672
 PREFILL_OUTLIER_FRAC = 0.001
 
-# MoE grouped experts (configuration 5).
+# MoE grouped experts (seed stream 5).
 MOE_EXPERTS, MOE_DMODEL, MOE_DFF, MOE_TOKENS, MOE_TOPK, MOE_ZIPF = 16, 4096, 14336, 128, 2, 1.1
 
 
-# Quantized KV-cache decode (config 6): the KV page's 7B MHA layer (32 heads x 128) at a 32K
+# Quantized KV-cache decode (seed stream 6): the KV page's 7B MHA layer (32 heads x 128) at a 32K
 # context, and a GQA layer (8 KV heads, 8 query heads each) with four sequences of 8K.
 KV_HEAD_DIM = 128
 KV_MHA = dict(batch=1, q_heads=32, kv_heads=32, capacity=32768)
@@ -165,9 +168,9 @@ def stack_matrix_seed(layer: int, name: str) -> int:
     return seed_for(3, layer, LLAMA_MATRICES.index(name))
 
 
-def layer_weights(bits_config: int = 1) -> np.ndarray:
-    """The single 4096x4096 layer of configurations 1 and 2."""
-    return weights_fp16(LAYER_N, LAYER_K, seed_for(bits_config))
+def layer_weights(stream: int = 1) -> np.ndarray:
+    """The single 4096x4096 layer (seed stream 1: the 4-bit layer, 2: the bit sweep)."""
+    return weights_fp16(LAYER_N, LAYER_K, seed_for(stream))
 
 
 def prefill_weights() -> tuple[np.ndarray, np.ndarray]:
@@ -182,17 +185,17 @@ def prefill_activations() -> np.ndarray:
     return activations_fp16(PREFILL_M, PREFILL_K, seed_for(4))
 
 
-def moe_expert(e: int, d_model: int = MOE_DMODEL, d_ff: int = MOE_DFF, config: int = 5):
+def moe_expert(e: int, d_model: int = MOE_DMODEL, d_ff: int = MOE_DFF, stream: int = 5):
     """(gate [d_ff, d_model], up [d_ff, d_model], down [d_model, d_ff]) of expert e."""
-    g = weights_fp16(d_ff, d_model, seed_for(config, e, LLAMA_MATRICES.index("gate")))
-    u = weights_fp16(d_ff, d_model, seed_for(config, e, LLAMA_MATRICES.index("up")))
-    d = weights_fp16(d_model, d_ff, seed_for(config, e, LLAMA_MATRICES.index("down")))
+    g = weights_fp16(d_ff, d_model, seed_for(stream, e, LLAMA_MATRICES.index("gate")))
+    u = weights_fp16(d_ff, d_model, seed_for(stream, e, LLAMA_MATRICES.index("up")))
+    d = weights_fp16(d_model, d_ff, seed_for(stream, e, LLAMA_MATRICES.index("down")))
     return g, u, d
 
 
 def moe_inputs(tokens: int = MOE_TOKENS, d_model: int = MOE_DMODEL, experts: int = MOE_EXPERTS,
-               topk: int = MOE_TOPK, config: int = 5):
+               topk: int = MOE_TOPK, stream: int = 5):
     """(x [tokens, d_model] fp16, ids int32 [tokens, topk], weights float32 [tokens, topk])."""
-    x = activations_fp16(tokens, d_model, seed_for(config))
-    ids, wts = zipf_routing(tokens, experts, topk, MOE_ZIPF, seed_for(config) + 900_000)
+    x = activations_fp16(tokens, d_model, seed_for(stream))
+    ids, wts = zipf_routing(tokens, experts, topk, MOE_ZIPF, seed_for(stream) + 900_000)
     return x, ids, wts
