@@ -242,6 +242,32 @@ def test_grouped_row_tiles(sizes, base, slack):
     assert np.all(y[outside] == 7.0)
 
 
+def test_grouped_64_experts():
+    """The most experts one launch takes: every lane of the work-item scan holds an expert,
+    with empty experts, a large one and single rows spread over the table."""
+    torch, q = gpu()
+    E, D, N = 64, 256, 256
+    rng = np.random.default_rng(7300)
+    sizes = rng.integers(0, 6, E)
+    sizes[[0, 13, 63]] = [0, 75, 33]
+    sizes[rng.choice(E, 8, replace=False)] = 0
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    R = int(offsets[-1])
+    x = workloads.activations_fp16(R, D, 73)
+    raw = [workloads.weights_fp16(N, D, 7300 + e) for e in range(E)]
+    ws = [GpuWeight(w, 3) for w in raw]
+    y = torch.full((R, N), 7.0, dtype=torch.float32, device="cuda")
+    q.qlinear_grouped_gemm(ws[0].desc, [w.handle() for w in ws], to_dev_fp16(x), D, None, dev(offsets), R,
+                           q.QP_EPI_ROWS_F32, y, N)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    for e in range(E):
+        rows = np.arange(offsets[e], offsets[e + 1])
+        if len(rows):
+            r = oracle.linear(x[rows], oracle.quantize(raw[e], 3))
+            assert rel_err(y[rows], r) <= TOL, (e, report(y[rows], r))
+
+
 @pytest.mark.parametrize("bits", (4, 2))
 def test_swiglu_epilogue_rounding(bits):
     """The SwiGLU epilogue's fp16 result equals the oracle's rounding of silu(g)*u except
