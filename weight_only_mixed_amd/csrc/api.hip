@@ -345,6 +345,31 @@ qp_status qlinear_gemm(const qp_weight_desc *d, const qp_weight *w, const uint16
     return device(launch_gemm(d->bits, a, S(stream)), "qlinear_gemm");
 }
 
+// The grouped launch after validation.  ksplit > 1 (fp32 rows only): k in ksplit equal parts,
+// part p writing its partial rows at y + p * ysplit floats.
+static qp_status grouped_launch(const qp_weight_desc *d, const qp_weight *experts, int32_t n_experts,
+                                const uint16_t *x, int64_t ldx, const int32_t *row_src,
+                                const int32_t *expert_offsets, int64_t rows, int32_t epilogue, void *y,
+                                int64_t ldy, int32_t ksplit, int64_t ysplit, void *stream)
+{
+    GemmArgs a{};
+    for (int e = 0; e < n_experts; ++e)
+        a.ex[e] = {(const uint8_t *)experts[e].packed, experts[e].scales, experts[e].zeros};
+    a.zmid = zero_pair(d);
+    a.x = x;
+    a.ldx = ldx;
+    a.row_src = row_src;
+    a.offsets = expert_offsets;
+    a.m = rows;
+    a.n = d->n;
+    a.k = d->k;
+    a.y = y;
+    a.ldy = ldy;
+    a.ksplit = ksplit;
+    a.ysplit = ysplit;
+    return device(launch_grouped(d->bits, epilogue, n_experts, a, S(stream)), "qlinear_grouped_gemm");
+}
+
 qp_status qlinear_grouped_gemm(const qp_weight_desc *d, const qp_weight *experts, int32_t n_experts,
                                const uint16_t *x, int64_t ldx, const int32_t *row_src,
                                const int32_t *expert_offsets, int64_t rows, int32_t epilogue, void *y,
@@ -368,20 +393,7 @@ qp_status qlinear_grouped_gemm(const qp_weight_desc *d, const qp_weight *experts
     if (rows < 0) return fail(QP_ERR_INVALID_ARG, "rows < 0");
     if (rows * ldx * 2 > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "x larger than 2 GiB");
     if ((int64_t)qp_packed_bytes(d) > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "packed weight larger than 2 GiB");
-    GemmArgs a{};
-    for (int e = 0; e < n_experts; ++e)
-        a.ex[e] = {(const uint8_t *)experts[e].packed, experts[e].scales, experts[e].zeros};
-    a.zmid = zero_pair(d);
-    a.x = x;
-    a.ldx = ldx;
-    a.row_src = row_src;
-    a.offsets = expert_offsets;
-    a.m = rows;
-    a.n = d->n;
-    a.k = d->k;
-    a.y = y;
-    a.ldy = ldy;
-    return device(launch_grouped(d->bits, epilogue, n_experts, a, S(stream)), "qlinear_grouped_gemm");
+    return grouped_launch(d, experts, n_experts, x, ldx, row_src, expert_offsets, rows, epilogue, y, ldy, 1, 0, stream);
 }
 
 qp_status qmoe_dispatch(const int32_t *ids, const float *w, int64_t tokens, int32_t topk, int32_t n_experts,
@@ -404,19 +416,24 @@ qp_status qmoe_combine(const float *rows_f32, int64_t ld_rows, const int32_t *to
     if (tokens < 1 || topk < 1 || n < 1 || ld_rows < n || ldo < n)
         return fail(QP_ERR_INVALID_ARG, "bad sizes");
     if (tokens > 65535) return fail(QP_ERR_INVALID_ARG, "tokens > 65535");
-    return device(launch_moe_combine(rows_f32, ld_rows, token_rows, row_weight, tokens, topk, n, out, ldo,
+    return device(launch_moe_combine(rows_f32, ld_rows, token_rows, row_weight, tokens, topk, n, out, ldo, 1, 0,
                                      S(stream)),
                   "qmoe_combine");
 }
 
 static size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// The expert FFN computes the down projection in two k halves (each half a whole number of
+// 512-k tile pairs): its grid then holds twice the workgroups of the one-pass launch, which
+// fills the CUs' workgroup slots better; the halves' fp32 rows are summed by the combine.
+static int32_t ffn_down_split(int64_t d_ff) { return d_ff % 512 == 0 ? 2 : 1; }
+
 size_t qmoe_ffn_workspace_bytes(int64_t tokens, int32_t topk, int32_t n_experts, int64_t d_model, int64_t d_ff)
 {
     if (tokens < 1 || topk < 1 || n_experts < 1 || d_model < 1 || d_ff < 1) return 0;
     const size_t R = (size_t)(tokens * topk);
     return al256((n_experts + 1) * 4) + 3 * al256(R * 4) + al256(R * (size_t)d_ff * 2) +
-           al256(R * (size_t)d_model * 4);
+           ffn_down_split(d_ff) * al256(R * (size_t)d_model * 4);
 }
 
 qp_status qmoe_ffn(const qp_weight_desc *dgu, const qp_weight *gate_up, const qp_weight_desc *dd,
@@ -468,10 +485,14 @@ qp_status qmoe_ffn(const qp_weight_desc *dgu, const qp_weight *gate_up, const qp
     if ((st = qlinear_grouped_gemm(dgu, gate_up, n_experts, x, ldx, row_src, offsets, (int64_t)R, QP_EPI_SWIGLU,
                                    act, d_ff, stream)) != QP_OK)
         return st;
-    if ((st = qlinear_grouped_gemm(dd, down, n_experts, act, d_ff, nullptr, offsets, (int64_t)R, QP_EPI_ROWS_F32,
-                                   rows, d_model, stream)) != QP_OK)
+    const int32_t ks = ffn_down_split(d_ff);
+    const int64_t ystride = (int64_t)(al256(R * (size_t)d_model * 4) / 4);
+    if ((st = grouped_launch(dd, down, n_experts, act, d_ff, nullptr, offsets, (int64_t)R, QP_EPI_ROWS_F32, rows,
+                             d_model, ks, ystride, stream)) != QP_OK)
         return st;
-    return qmoe_combine(rows, d_model, token_rows, row_weight, tokens, topk, d_model, out, ldo, stream);
+    return device(launch_moe_combine(rows, d_model, token_rows, row_weight, tokens, topk, d_model, out, ldo, ks,
+                                     ystride, S(stream)),
+                  "qmoe_combine");
 }
 
 size_t qkv_cache_bytes(const qkv_desc *d, int32_t which)

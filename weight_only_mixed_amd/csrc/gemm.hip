@@ -597,6 +597,14 @@ __global__ __launch_bounds__(GE::kWaves * 64) __attribute__((amdgpu_waves_per_eu
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t = lane >> 4, r = lane & 15;
     const int64_t KT = a.k / kTileK, G = a.k / kGroup;
+    // k range: all of k, or part blockIdx.z of a.ksplit equal parts (grouped fp32 rows)
+    int64_t kt0 = 0, KTp = KT;
+    if constexpr (MODE == kGroupRowsF32) {
+        if (a.ksplit > 1) {
+            KTp = KT / a.ksplit;
+            kt0 = (int64_t)blockIdx.z * KTp;
+        }
+    }
     int64_t nt, m0, mend;  // weight tile; sorted rows [m0, mend) of this workgroup
     int e = 0;
     if constexpr (GROUPED) {
@@ -638,7 +646,7 @@ __global__ __launch_bounds__(GE::kWaves * 64) __attribute__((amdgpu_waves_per_eu
     bf.zmid = a.zmid;
     // Activation rows are gathered per lane: the DMA source of a row past the workgroup's
     // rows lies past the buffer's range and reads zeros.
-    bf.x = make_rsrc(a.x, a.m * a.ldx * 2);
+    bf.x = make_rsrc(a.x + kt0 * kTileK, (a.m * a.ldx - kt0 * kTileK) * 2);
 #pragma unroll
     for (int it = 0; it < GE::kDmaX; ++it) {
         const int row = 4 * (GE::kDmaX * wv + it) + (lane >> 4);
@@ -652,9 +660,10 @@ __global__ __launch_bounds__(GE::kWaves * 64) __attribute__((amdgpu_waves_per_eu
     for (int u = 0; u < kRBW; ++u) {
         const int64_t rb = rb0 + u;
         const bool in = rb < NB;
-        bf.w[u] = make_rsrc(W.packed + rb * KT * (512 * B), in ? KT * (512 * B) : 0);
-        bf.sc[u] = make_rsrc(W.scales + rb * kTileN * G, in ? kTileN * G * 2 : 0);
-        bf.zr[u] = make_rsrc(W.zeros + rb * kTileN * G, in && !a.zmid ? kTileN * G : 0);
+        // tiles kt0 .. kt0 + KTp - 1 of the block; scale / zero point rows keep their stride G
+        bf.w[u] = make_rsrc(W.packed + (rb * KT + kt0) * (512 * B), in ? KTp * (512 * B) : 0);
+        bf.sc[u] = make_rsrc(W.scales + rb * kTileN * G + 2 * kt0, in ? (kTileN * G - 2 * kt0) * 2 : 0);
+        bf.zr[u] = make_rsrc(W.zeros + rb * kTileN * G + 2 * kt0, in && !a.zmid ? kTileN * G - 2 * kt0 : 0);
     }
 
     f4 tot[kRBW][kMT];
@@ -692,7 +701,7 @@ __global__ __launch_bounds__(GE::kWaves * 64) __attribute__((amdgpu_waves_per_eu
             }
     }
 
-    k_loop<B, GE, NMT>(bf, sm.xs[0], sm.xs[1], sm.ws[0], sm.ws[1], KT, G, wv, lane, nmt, tot);
+    k_loop<B, GE, NMT>(bf, sm.xs[0], sm.xs[1], sm.ws[0], sm.ws[1], KTp, G, wv, lane, nmt, tot);
 
     // epilogue
 #pragma unroll
@@ -705,7 +714,7 @@ __global__ __launch_bounds__(GE::kWaves * 64) __attribute__((amdgpu_waves_per_eu
             if (row >= mend) continue;
             const f4 s = tot[u][mt];
             if constexpr (MODE == kGroupRowsF32) {
-                *(f4 *)((float *)a.y + row * a.ldy + rb * kTileN + 4 * t) = s;
+                *(f4 *)((float *)a.y + (int64_t)blockIdx.z * a.ysplit + row * a.ldy + rb * kTileN + 4 * t) = s;
             } else if constexpr (MODE == kGroupSwiglu) {
                 // row blocks 2i (gate) and 2i+1 (up) of a wave: output features 16i + 4t + j
                 if (u == 1) {
@@ -861,8 +870,9 @@ static hipError_t grouped_geo(int n_experts, const GemmArgs &a, hipStream_t st)
     const int64_t items = std::min<int64_t>((a.m + n_experts * (T - 1)) / T, n_experts * ((a.m + T - 1) / T));
     TilePlan plan{};
     plan.experts = n_experts;
-    hipLaunchKernelGGL((gemm_kernel<B, MODE, 0, GE>), dim3((unsigned)n_tiles, (unsigned)items), dim3(GE::kWaves * 64),
-                       0, st, a, plan);
+    const unsigned parts = MODE == kGroupRowsF32 && a.ksplit > 1 ? (unsigned)a.ksplit : 1u;
+    hipLaunchKernelGGL((gemm_kernel<B, MODE, 0, GE>), dim3((unsigned)n_tiles, (unsigned)items, parts),
+                       dim3(GE::kWaves * 64), 0, st, a, plan);
     return hipGetLastError();
 }
 template <int B, int MODE>

@@ -86,7 +86,8 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t *ids, cons
 __global__ __launch_bounds__(256) void combine_kernel(const float *rows, int64_t ld_rows,
                                                       const int32_t *token_rows,
                                                       const float *row_weight, int topk,
-                                                      int64_t n, uint16_t *out, int64_t ldo)
+                                                      int64_t n, uint16_t *out, int64_t ldo,
+                                                      int nsplit, int64_t split_stride)
 {
     const int64_t tok = blockIdx.y;
     const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -95,7 +96,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *rows, int64_t
     for (int j = 0; j < topk; ++j) {
         const int32_t r = token_rows[tok * topk + j];
         if (r < 0) continue;
-        s = __builtin_fmaf(row_weight[r], rows[r * ld_rows + c], s);
+        // a row computed in k parts: its partial rows summed in part order first
+        float v = rows[r * ld_rows + c];
+        for (int p = 1; p < nsplit; ++p) v += rows[p * split_stride + r * ld_rows + c];
+        s = __builtin_fmaf(row_weight[r], v, s);
     }
     out[tok * ldo + c] = __builtin_bit_cast(uint16_t, (_Float16)s);
 }
@@ -111,10 +115,11 @@ hipError_t launch_moe_dispatch(const int32_t *ids, const float *w, int64_t token
 
 hipError_t launch_moe_combine(const float *rows, int64_t ld_rows, const int32_t *token_rows,
                               const float *row_weight, int64_t tokens, int topk, int64_t n,
-                              uint16_t *out, int64_t ldo, hipStream_t st)
+                              uint16_t *out, int64_t ldo, int nsplit, int64_t split_stride,
+                              hipStream_t st)
 {
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256), (unsigned)tokens), dim3(256),
-                       0, st, rows, ld_rows, token_rows, row_weight, topk, n, out, ldo);
+                       0, st, rows, ld_rows, token_rows, row_weight, topk, n, out, ldo, nsplit, split_stride);
     return hipGetLastError();
 }
 

@@ -90,6 +90,8 @@ struct GemmArgs {
     void *y;
     int64_t ldy;
     uint32_t zmid;  // 0: stored zero points; else the implied pair (2^(b-1) in both bytes)
+    int32_t ksplit;  // grouped fp32 rows: k in ksplit equal parts (0 or 1: whole k); part s
+    int64_t ysplit;  //   writes its partial rows at y + s * ysplit floats
     uint16_t *xt;   // workspace (outliers only): x transposed, [k][ldxt]
     float *spart;   // workspace (outliers only): fp32 outlier partial, [n][ldxt]
     int64_t ldxt;
@@ -103,6 +105,7 @@ hipError_t launch_moe_dispatch(const int32_t *ids, const float *w, int64_t token
                                float *row_weight, int32_t *token_rows, hipStream_t st);
 hipError_t launch_moe_combine(const float *rows, int64_t ld_rows, const int32_t *token_rows,
                               const float *row_weight, int64_t tokens, int topk, int64_t n,
-                              uint16_t *out, int64_t ldo, hipStream_t st);
+                              uint16_t *out, int64_t ldo, int nsplit, int64_t split_stride,
+                              hipStream_t st);
 
 }  // namespace qp
