@@ -298,8 +298,11 @@ def test_swiglu_epilogue_rounding(bits):
 
 
 @pytest.mark.parametrize("bits", (4, 2, 6))
-def test_moe_ffn_small(bits):
-    E, D, F, T = 5, 512, 768, 37
+@pytest.mark.parametrize("F", (768, 1024), ids=("down-one-pass", "down-two-k-halves"))
+def test_moe_ffn_small(bits, F):
+    """d_ff = 768 runs the down projection in one pass, 1024 in two k halves summed by the
+    combine."""
+    E, D, T = 5, 512, 37
     ex = Experts(E, D, F, bits, stream=50 + bits)
     x = workloads.activations_fp16(T, D, 51)
     ids, wts = small_routing(T, E, 52)
