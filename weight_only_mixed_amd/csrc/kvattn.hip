@@ -594,13 +594,13 @@ hipError_t launch_kv_attn(int kb, int vb, int kg, int vg, int64_t batch, const K
     return hipGetLastError();
 }
 
-// Chunks per (sequence, kv head): about one workgroup per CU (256 of them), each chunk a
-// multiple of 128 tokens (one tile per wave at least).  Workgroup counts that are not a
-// multiple of the CU count leave some CUs a second chunk while others idle, and two per CU
-// cost more merges and shorter per-wave streams.
+// Chunks per (sequence, kv head): at most one workgroup per CU (256 of them), each chunk a
+// multiple of 128 tokens (one tile per wave at least).  A workgroup count a little above a
+// multiple of the CU count gives a few CUs a second chunk while the rest idle, so the split
+// rounds down; two per CU cost more merges and shorter per-wave streams.
 void kv_split(int64_t batch, int64_t hkv, int64_t cap, int32_t *nsplit, int32_t *chunk)
 {
-    const int64_t want = (256 + batch * hkv - 1) / (batch * hkv);
+    const int64_t want = 256 / (batch * hkv);
     const int64_t maxs = (cap + 127) / 128;
     int64_t ns = want < 1 ? 1 : (want > maxs ? maxs : want);
     if (ns > kKvMaxSplit) ns = kKvMaxSplit;
