@@ -201,6 +201,13 @@ def test_attention_many_chunks():
     check_attention(c, np.array([4000], np.int32), 1 / math.sqrt(128), 6701, "chunks")
 
 
+def test_attention_split_rounds_down():
+    """24 (sequence, kv head) rows at 1280 tokens: ten chunks of 128 each (240 workgroups)."""
+    c = Cache(3, 16, 8, 1280, 4, 8, 64, 64, 6750)
+    c.write_all()
+    check_attention(c, np.array([1280, 700, 5], np.int32), 1 / math.sqrt(128), 6751, "split10")
+
+
 def test_attention_large_scores():
     """Sharp softmax (scores of order 100): the running maximum and rescaling carry it."""
     c = Cache(2, 4, 4, 256, 8, 8, 64, 64, 6800)
