@@ -196,6 +196,17 @@ def test_grouped_and_moe_validation():
                       stream=0, check=False) == q.QP_ERR_WORKSPACE
 
 
+def test_moe_ffn_rejects_intermediate_beyond_2gib():
+    """The fp16 intermediate [tokens*topk][d_ff] is read through one 2 GiB buffer range: 65536
+    routed rows at d_ff = 16384 (2 GiB exactly) must be refused before any launch."""
+    w = q.weight(FAKE, FAKE, FAKE)
+    gu, dn = q.desc(4, 2 * 16384, 4096), q.desc(4, 4096, 16384)
+    need = q.qmoe_ffn_workspace_bytes(32768, 2, 16, 4096, 16384)
+    assert q.qmoe_ffn(gu, [w] * 16, dn, [w] * 16, FAKE, 4096, 32768, FAKE, FAKE, 2, FAKE, 4096, FAKE, need,
+                      stream=0, check=False) == q.QP_ERR_UNSUPPORTED
+    assert "2 GiB" in q.last_error()
+
+
 def test_status_message_is_thread_local_text():
     q.qpack_pack(q.desc(9, 16, 256), FAKE, FAKE, stream=0, check=False)
     assert "bits=9" in q.last_error()

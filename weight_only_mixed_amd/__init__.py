@@ -3,8 +3,8 @@
 Argument marshalling only: every function here forwards to the C entry point of the same
 name, passing device pointers (torch tensors or raw integer addresses) and the current HIP
 stream.  All computation runs in the library's HIP kernels; there is no fallback.  Importing
-this package fails loudly if libqpack.so has not been built (``python -m
-weight_only_mixed_amd.build`` or ``__graft_entry__.build()``).
+this package fails loudly if libqpack.so has not been built (``python
+weight_only_mixed_amd/build.py`` or ``__graft_entry__.build()``).
 """
 from __future__ import annotations
 
@@ -20,7 +20,7 @@ import torch  # noqa: F401  (import order matters, see above)
 _LIB_PATH = Path(__file__).resolve().parent / "libqpack.so"
 if not _LIB_PATH.exists():
     raise ImportError(f"{_LIB_PATH} is missing: build the HIP library first "
-                      "(python -m weight_only_mixed_amd.build)")
+                      "(python weight_only_mixed_amd/build.py)")
 lib = ctypes.CDLL(str(_LIB_PATH))
 
 QP_OK, QP_ERR_INVALID_ARG, QP_ERR_UNSUPPORTED, QP_ERR_DEVICE, QP_ERR_WORKSPACE = range(5)

@@ -464,6 +464,12 @@ qp_status qmoe_ffn(const qp_weight_desc *dgu, const qp_weight *gate_up, const qp
     }
     if (!x || !aligned(x, 16) || ldx < d_model || ldx % 8 != 0) return fail(QP_ERR_INVALID_ARG, "x NULL/misaligned or bad ldx");
     if (!topk_ids || !topk_w) return fail(QP_ERR_INVALID_ARG, "routing NULL");
+    // The down projection reads the fp16 intermediate [tokens*topk][d_ff] through one buffer
+    // resource, as qlinear_grouped_gemm reads x: it must stay within 2 GiB.
+    if (tokens * topk * d_ff * 2 > 0x7FFFFFFFLL)
+        return fail(QP_ERR_UNSUPPORTED, "tokens*topk*d_ff*2 = %lld bytes of intermediate exceed 2 GiB",
+                    (long long)(tokens * topk * d_ff * 2));
+    if (tokens * ldx * 2 > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "x larger than 2 GiB");
 
     const size_t R = (size_t)(tokens * topk);
     uint8_t *p = (uint8_t *)workspace;
