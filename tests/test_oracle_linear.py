@@ -108,3 +108,37 @@ def test_small_groups_match_group_routine_and_brute_force(g):
         what = (d["codes"].astype(np.float64) - zp) * sc
         want = x.astype(np.float64) @ what.T
         assert np.allclose(oracle.linear(x, d), want, rtol=1e-12, atol=1e-12)
+
+
+def test_small_integer_inputs_give_exact_integers():
+    """Codes, zero points, power-of-two scales and small-integer activations make every
+    dequantized weight and every product a small dyadic number, so the fp64 result must equal
+    the integer sum computed in Python's exact integers (no floating point at all), CSR
+    outlier terms included."""
+    rng = np.random.default_rng(31)
+    M, N, K, bits = 3, 32, 512, 5
+    G = K // 128
+    codes = rng.integers(0, 32, (N, K)).astype(np.uint8)
+    zeros = rng.integers(0, 32, (N, G)).astype(np.uint8)
+    exps = rng.integers(-2, 3, (N, G))                       # scales 1/4 .. 4
+    scales = np.float16(2.0) ** exps.astype(np.float16)
+    x = rng.integers(-9, 10, (M, K)).astype(np.float16)
+    # three outliers, integer valued, in rows 0, 0 and 17
+    rowptr = np.zeros(N + 1, np.int32)
+    cols, vals = [5, 400, 77], [3.0, -4.0, 5.0]
+    rowptr[1:] = 2
+    rowptr[18:] = 3
+    q = dict(codes=codes, scales=scales.view(np.uint16), zeros=zeros, rowptr=rowptr,
+             col=np.array(cols, np.int32), val=np.array(vals, np.float16).view(np.uint16), g=128)
+    r = oracle.linear(x, q)
+    xi = x.astype(np.int64)
+    for m in range(M):
+        for n in range(N):
+            acc4 = 0                                       # the sum times 4 (scales >= 1/4)
+            for k in range(K):
+                g = k // 128
+                acc4 += int(xi[m, k]) * (int(codes[n, k]) - int(zeros[n, g])) * (1 << (int(exps[n, g]) + 2))
+            for p in range(rowptr[n], rowptr[n + 1]):
+                acc4 += 4 * int(xi[m, cols[p]]) * int(vals[p])
+            assert r[m, n] * 4 == acc4, (m, n)
+    assert np.array_equal(r, np.round(r * 4) / 4)

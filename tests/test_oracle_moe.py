@@ -61,3 +61,60 @@ def test_zipf_routing_skew():
     assert 0.75 < share < 0.88
     assert (wts > 0).all() and (wts.sum(1) <= 1.0 + 1e-6).all()
     assert (ids[:, 0] != ids[:, 1]).all()
+
+
+def _expert(entries, n, k, zp=8):
+    """A 4-bit expert matrix [n, k] whose dequantized weights are 0 except `entries`
+    {(row, col): small integer}: scale 1.0, zero point 8, so code = value + 8."""
+    codes = np.full((n, k), zp, np.uint8)
+    for (i, j), v in entries.items():
+        codes[i, j] = zp + v
+    G = k // 128
+    return dict(codes=codes, scales=np.full((n, G), np.float16(1.0)).view(np.uint16),
+                zeros=np.full((n, G), zp, np.uint8), g=128)
+
+
+def test_hand_worked_two_expert_swiglu():
+    """One token x = e_0 routed to two experts with combine weights 0.75 and 0.125 (not
+    summing to 1: the oracle must use the weights it is given, not renormalise them).
+
+    Expert 0: gate[0,0] = 2, up[0,0] = 3  -> a_0 = fp16(silu(2) * 3)
+      silu(2) * 3 = 6 / (1 + e^-2) = 6 / 1.1353352832... = 5.2847824678...
+      fp16 spacing on [4, 8) is 2^-8: 5.28478... * 256 = 1352.90 -> 1353 / 256 = 5.28515625
+      down[0,0] = 1, down[1,0] = -2   -> o = (5.28515625, -10.5703125, 0, ...)
+    Expert 1: gate[0,0] = -1, up[0,0] = 4 -> a_0 = fp16(silu(-1) * 4)
+      silu(-1) * 4 = -4 / (1 + e) = -4 / 3.7182818284... = -1.0757656854...
+      fp16 spacing on [1, 2) is 2^-10: -1101.58 -> -1102 / 1024 = -1.076171875
+      down[0,0] = 3, down[1,0] = 1    -> o = (-3.228515625, -1.076171875, 0, ...)
+    out[0] = 0.75 * 5.28515625 + 0.125 * -3.228515625 = 3.9638671875 - 0.403564453125 = 3.560302734375
+    out[1] = 0.75 * -10.5703125 + 0.125 * -1.076171875 = -7.927734375 - 0.134521484375 = -8.062255859375
+    Every other output is 0.  All these values are dyadic, so the fp64 result is exact."""
+    D = F = 128
+    gate = [_expert({(0, 0): 2}, F, D), _expert({(0, 0): -1}, F, D)]
+    up = [_expert({(0, 0): 3}, F, D), _expert({(0, 0): 4}, F, D)]
+    down = [_expert({(0, 0): 1, (1, 0): -2}, D, F), _expert({(0, 0): 3, (1, 0): 1}, D, F)]
+    x = np.zeros((1, D), np.float16)
+    x[0, 0] = 1.0
+    ids = np.array([[0, 1]], np.int32)
+    wts = np.array([[0.75, 0.125]], np.float32)
+    r = oracle.moe_ffn(x, ids, wts, gate, up, down)
+    want = np.zeros(D)
+    want[0], want[1] = 3.560302734375, -8.062255859375
+    assert np.array_equal(r[0], want)
+    # the SwiGLU intermediate before its fp16 rounding
+    v = oracle.swiglu_act(x[0], gate[0], up[0])
+    assert abs(v[0] - 5.2847824678672947) < 1e-12 and not v[1:].any()
+
+
+def test_all_rows_to_one_expert_equals_dense_ffn_from_linear():
+    """Every token routed to expert 1 with weight 1 (top-1): the FFN equals the dense
+    chain built from the oracle's linear layer, down(fp16(silu(gate x) * (up x)))."""
+    g, u, d = experts(4)
+    x = workloads.activations_fp16(5, D, 4)
+    ids = np.ones((5, 1), np.int32)
+    wts = np.ones((5, 1), np.float32)
+    got = oracle.moe_ffn(x, ids, wts, g, u, d)
+    gv, uv = oracle.linear(x, g[1]), oracle.linear(x, u[1])
+    a = (gv / (1.0 + np.exp(-gv)) * uv).astype(np.float16)
+    want = oracle.linear(a, d[1])
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-13)

@@ -140,3 +140,138 @@ def test_outlier_ties_go_to_lower_index():
     r = oracle.quantize(w, 3, frac)
     rows = np.repeat(np.arange(n), np.diff(r["rowptr"]))
     assert np.array_equal(rows * k + r["col"], cand[:40])
+
+
+# ---- independent restatement in numpy float32 ---------------------------------------------
+#
+# The formula of the inference acceleration guide, s1.1, restated with numpy's float32 and
+# float16 types under the same readings (range extended to contain 0, RNE via np.rint,
+# clamping to [0, qmax], scale stored in fp16 and raised to 2^-14 when it would be zero or
+# subnormal, an all-zero group stored as scale 1, zero point 0).  Each numpy float32
+# operation is one correctly rounded IEEE operation, and float32 -> float16 is one RNE
+# rounding, so this fixes the exact sequence the oracle must follow.  It shares nothing with
+# the oracle but the readings.
+
+def np_quantize_groups(w16, bits):
+    """[G, n] fp16 groups -> (scale fp16 [G], zero point [G], codes [G, n]) as float arrays."""
+    qmax = np.float32((1 << bits) - 1)
+    w = w16.astype(np.float32)
+    lo = np.minimum(w.min(axis=1), np.float32(0))
+    hi = np.maximum(w.max(axis=1), np.float32(0))
+    empty = hi == lo
+    s32 = (hi - lo) / qmax
+    s16 = s32.astype(np.float16)
+    s16 = np.where(np.abs(s16) < np.float16(2.0 ** -14), np.float16(2.0 ** -14), s16)
+    s16 = np.where(empty, np.float16(1.0), s16)
+    sf = s16.astype(np.float32)
+    zp = np.clip(np.float32(0) - np.rint(lo / sf), np.float32(0), qmax)
+    q = np.clip(np.rint(w / sf[:, None]) + zp[:, None], np.float32(0), qmax)
+    zp = np.where(empty, np.float32(0), zp)
+    q = np.where(empty[:, None], np.float32(0), q)
+    return s16, zp, q
+
+
+def np_quantize_groups_sym(w16, bits):
+    """Symmetric groups (mixed-bit page, s2.3): range [-m, m], implied midpoint zero point."""
+    qmax = np.float32((1 << bits) - 1)
+    z = np.float32(1 << (bits - 1))
+    w = w16.astype(np.float32)
+    m = np.abs(w).max(axis=1)
+    empty = m == np.float32(0)
+    s16 = ((m + m) / qmax).astype(np.float16)
+    s16 = np.where(np.abs(s16) < np.float16(2.0 ** -14), np.float16(2.0 ** -14), s16)
+    s16 = np.where(empty, np.float16(1.0), s16)
+    sf = s16.astype(np.float32)
+    q = np.clip(np.rint(w / sf[:, None]) + z, np.float32(0), qmax)
+    return s16, q
+
+
+def random_groups(count, seed):
+    """fp16 groups of 128 at three scales, a third of them shifted so the group is one-signed
+    or lopsided (the range-contains-zero reading then matters)."""
+    rng = np.random.default_rng(seed)
+    std = np.array([1e-3, 0.02, 1.0])[rng.integers(0, 3, count)]
+    shift = rng.choice([0.0, 0.0, 0.0, 3.0, -3.0, 0.7], count)
+    w = rng.standard_normal((count, 128)) * std[:, None] + (shift * std)[:, None]
+    return w.astype(np.float16)
+
+
+def half_step_groups(bits, count, seed):
+    """Groups whose values sit exactly on half steps of an exactly representable scale:
+    scale 2^e, range [-a*2^e, (qmax-a)*2^e], values (j + 1/2) * 2^e.  Every code is a tie."""
+    rng = np.random.default_rng(seed)
+    qmax = (1 << bits) - 1
+    out = np.zeros((count, 128), np.float16)
+    for i in range(count):
+        e = int(rng.integers(-12, 2))
+        a = int(rng.integers(0, qmax + 1))
+        j = rng.integers(-a, qmax - a, 126)
+        vals = np.concatenate([[-a, qmax - a], j + 0.5]) * 2.0 ** e
+        out[i] = rng.permutation(vals).astype(np.float16)
+    return out
+
+
+@pytest.mark.parametrize("bits", (2, 3, 4, 5, 6))
+def test_numpy_float32_restatement_bit_exact(bits):
+    """The oracle's quantizer equals the numpy float32 restatement on 10^5 random groups and on
+    groups built from exact half steps."""
+    w = np.concatenate([random_groups(100_000, 500 + bits), half_step_groups(bits, 2000, 600 + bits)])
+    r = oracle.quantize(w, bits)
+    s16, zp, q = np_quantize_groups(w, bits)
+    assert np.array_equal(r["scales"][:, 0], s16.view(np.uint16))
+    assert np.array_equal(r["zeros"][:, 0], zp.astype(np.uint8))
+    assert np.array_equal(r["codes"], q.astype(np.uint8))
+
+
+@pytest.mark.parametrize("bits", (2, 3, 4, 5, 6))
+def test_numpy_float32_restatement_symmetric(bits):
+    w = np.concatenate([random_groups(50_000, 700 + bits), half_step_groups(bits, 1000, 800 + bits)])
+    r = oracle.quantize(w, bits, sym=True)
+    s16, q = np_quantize_groups_sym(w, bits)
+    assert np.array_equal(r["scales"][:, 0], s16.view(np.uint16))
+    assert np.array_equal(r["codes"], q.astype(np.uint8))
+
+
+def test_half_step_groups_are_ties():
+    """The tie groups above really put every non-extreme value on a half step of its scale."""
+    for bits in (2, 4, 6):
+        w = half_step_groups(bits, 50, 900 + bits)
+        s16, zp, _ = np_quantize_groups(w, bits)
+        t = w.astype(np.float64) / s16.astype(np.float64)[:, None]
+        frac = np.abs(t - np.floor(t))
+        assert (np.sum(frac == 0.5, axis=1) >= 100).all()
+
+
+def test_restatement_has_power_against_nearby_mistakes():
+    """Three plausible slips in the quantizer each change results on this sample, so the
+    bit-exact pins above would catch them: dividing by the fp32 quotient instead of the stored
+    fp16 scale, rounding half away from zero instead of to even, and a plain [min, max] range
+    instead of one extended to contain 0.  (Forming the scale quotient in double instead of
+    fp32 does not change it: a quotient by 2^b - 1 has a repeating bit pattern that cannot
+    fall exactly on a binary16 midpoint, so it is not among the slips.)"""
+    bits = 3
+    w = np.concatenate([random_groups(20_000, 503), half_step_groups(bits, 500, 603)])
+    r = oracle.quantize(w, bits)
+    qmax = np.float32(7)
+    wf = w.astype(np.float32)
+    lo = np.minimum(wf.min(axis=1), np.float32(0))
+    hi = np.maximum(wf.max(axis=1), np.float32(0))
+    s32 = (hi - lo) / qmax
+    s32 = np.where(s32 == 0, np.float32(1), s32)
+    zp = np.clip(-np.rint(lo / s32), 0, qmax)
+    q_unrounded_scale = np.clip(np.rint(wf / s32[:, None]) + zp[:, None], 0, qmax).astype(np.uint8)
+    assert np.count_nonzero(q_unrounded_scale != r["codes"]) > 0
+
+    s16, zp16, q16 = np_quantize_groups(w, bits)
+    sf = s16.astype(np.float32)[:, None]
+    t = wf / sf
+    away = np.trunc(t + np.copysign(np.float32(0.5), t))
+    q_away = np.clip(away + zp16[:, None], 0, qmax).astype(np.uint8)
+    assert np.count_nonzero(q_away != r["codes"]) > 0
+
+    plo, phi = wf.min(axis=1), wf.max(axis=1)
+    ps = ((phi - plo) / qmax).astype(np.float16).astype(np.float32)
+    ps = np.where(ps == 0, np.float32(1), ps)
+    pz = np.clip(-np.rint(plo / ps), 0, qmax)
+    q_plain = np.clip(np.rint(wf / ps[:, None]) + pz[:, None], 0, qmax).astype(np.uint8)
+    assert np.count_nonzero(q_plain != r["codes"]) > 0
