@@ -1,22 +1,22 @@
-"""Benchmark: weight-only mixed-bit decode GEMV on one MI355X.
+"""Benchmark: weight-only mixed-bit quantized linear layers on one MI355X.
 
-Workload (one "step"): the 4096 x 4096 layer at 2, 3, 5 and 6 bits (asymmetric, groups of
-128 along K, page packing units) times decode batches M = 1, 4, 8 -- twelve qlinear_gemv
-calls.  Weights are quantized and packed once (the offline repack of the 70B page, s3) and
-the step rotates over enough identical copies (>= 1 GB in total) that every weight byte is
-read from HBM, as in a real decode pass over distinct layers, not from the 256 MB
-Infinity Cache.  Each step is one captured HIP graph, replayed.
+Headline step: the 4096 x 4096 layer at 4 bits (asymmetric, groups of 128 along K, page packing
+units, device tile layout) times one fp16 activation row (M = 1): one qlinear_gemv call.
+Weights are quantized and packed once (the offline repack of the 70B page, s3) and the steps
+rotate over enough identical copies (>= 1 GiB in total) that every weight byte is read from
+HBM, as in a decode pass over distinct layers, not from the 256 MB Infinity Cache.  The timed
+steps run as captured HIP graphs of back-to-back launches on one stream.
 
-value = packed-weight bytes (codes + fp16 scales + u8 zero points) of the step / step time.
-The roofline object covers the kernel with the largest share of the step, timed live with
-HIP events around a graph of back-to-back launches on its own stream.  A secondary line
-measures the prefill dequant-GEMM (M=512, K=8192, N=28672, 4-bit + 0.1% outliers) in
-TFLOP/s.  Further lines: the 4-bit 4096 x 4096 GEMV at M=1, the same layer at 2 and 3 bits
-with symmetric groups (no zero points), with groups of 32 and 64, and with zero points kept in
-b bits, a Llama-7B-shaped decode stack, a 16-expert FFN, and decode attention over a quantized
-KV cache.
-cpu_baseline times the CPU oracle on the same step; cpu_baseline_1thread times one step of it on
-one thread.
+value = packed-weight bytes (codes + fp16 scales + u8 zero points) per step / step time.  The
+step is one launch of the GEMV, so the roofline object (bound: HBM) is that kernel's average
+launch duration over the timed region.  roofline_prefill (bound: MFMA) is the prefill
+dequant-GEMM (M=512, K=8192, N=28672, 4-bit + 0.1% fp16 CSR outliers), end to end and with the
+dense kernel alone.  Further lines: the 2/3/5/6-bit sweep at M = 1, 4, 8, symmetric groups,
+groups of 32 and 64, zero points in b bits, a Llama-7B-shaped decode stack, a 16-expert FFN and
+decode attention over a quantized KV cache.  Per-kernel lines take the median of five timed
+graph replays.
+cpu_baseline times the CPU oracle on the headline step (all host cores); cpu_baseline_1thread
+the same on one thread; cpu_baseline_prefill the oracle on a sample of the prefill GEMM.
 """
 from __future__ import annotations
 
@@ -71,24 +71,35 @@ def weight_bytes(n: int, k: int, bits: int, nnz: int = 0, sym: bool = False, g: 
     return n * k * bits // 8 + (n * k // g) * (2 if sym else 3) + csr
 
 
-def time_graph(torch, fn, reps: int, stream) -> float:
-    """Average ms of one fn() call: a graph of `reps` back-to-back calls, events around it."""
+def time_graph(torch, fn, reps: int, stream, trials: int = 5) -> float:
+    """Average ms of one fn(i) call: a graph of `reps` back-to-back calls (i = 0..reps-1), HIP
+    events around each replay on the graph's stream; the median over `trials` replays."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         for i in range(reps):
             fn(i)
     g.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    best = float("inf")
-    for _ in range(3):
+    times = []
+    for _ in range(trials):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):
             e0.record(stream)
             g.replay()
             e1.record(stream)
         torch.cuda.synchronize()
-        best = min(best, e0.elapsed_time(e1) / reps)
-    return best
+        times.append(e0.elapsed_time(e1) / reps)
+    del g
+    return float(np.median(times))
+
+
+ROTATION_BYTES = 1 << 30
+
+
+def copies_for(nbytes: int, min_bytes: int = ROTATION_BYTES) -> int:
+    """Distinct weight copies a memory-bound line rotates over: at least `min_bytes` in total
+    (four times the 256 MB Infinity Cache), so each launch reads its weight from HBM."""
+    return max(2, -(-min_bytes // nbytes))
 
 
 GEMV_SOURCES = ("weight_only_mixed_amd/csrc/qmm_small.hip", "weight_only_mixed_amd/csrc/unpack.h",
@@ -143,12 +154,20 @@ def copy_gbps(torch, nbytes: int = 1 << 30, reps: int = 10) -> float:
 
 
 def pmc_pass(q, torch, workloads):
-    """A short eager sequence for counter collection: every (bits, M) GEMV of the step on
-    four distinct weight copies, the prefill GEMM twice, decode attention over two copies of
+    """A short eager sequence for counter collection: the headline 4-bit M=1 GEMV and every
+    (bits, M) GEMV of the sweep on four distinct weight copies each, the prefill GEMM twice, decode attention over two copies of
     the 32K MHA quantized cache, and a 1 GiB copy twice (the copy is the calibration kernel:
     its bytes are known)."""
     dev = torch.device("cuda")
     K = N = 4096
+    d4, w4 = quantize_pack(q, torch, workloads.layer_weights(1), 4)
+    h4 = [q.weight(w4["packed"].clone(), w4["scales"].clone(), w4["zeros"].clone()) for _ in range(4)]
+    x1 = torch.from_numpy(workloads.activations_fp16(1, K, workloads.seed_for(1)).view(np.int16)).to(dev)
+    y1 = torch.empty((1, N), dtype=torch.int16, device=dev)
+    for h in h4:
+        q.qlinear_gemv(d4, h, x1, K, 1, y1, N)
+    torch.cuda.synchronize()
+    del h4, w4
     w = workloads.layer_weights(2)
     for b in workloads.SWEEP_BITS:
         d, wt = quantize_pack(q, torch, w, b)
@@ -368,21 +387,122 @@ def bench_kv(q, torch, workloads, stream, min_bytes: int = 1 << 30):
     return out
 
 
+def rotated_gemv(q, torch, d, wt, nbytes):
+    """Handles of enough clones of one packed weight for a >= 1 GiB rotation (the clones are
+    kept alive by the returned list)."""
+    n = copies_for(nbytes)
+    keep = [clone_weight(torch, wt) for _ in range(n)]
+    return [q.weight(c["packed"], c["scales"], c["zeros"]) for c in keep], keep
+
+
+def gemv_line(q, torch, stream, d, wt, nbytes, x, m, y, ldy):
+    """Median-of-5 time of one qlinear_gemv launch over a >= 1 GiB rotation."""
+    hs, keep = rotated_gemv(q, torch, d, wt, nbytes)
+    k = d.k
+    ms = time_graph(torch, lambda i: q.qlinear_gemv(d, hs[i % len(hs)], x, k, m, y, ldy), 2 * len(hs), stream)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    del hs, keep
+    return dict(us=round(ms * 1e3, 3), GBps=round(gbps, 1), frac_hbm_peak=round(gbps / HBM_PEAK_GBS, 4),
+                bytes=nbytes)
+
+
+def bench_prefill(q, torch, workloads, stream):
+    """Prefill dequant-GEMM (M=512, K=8192, N=28672, 4-bit g=128, 0.1% fp16 CSR outliers), end to
+    end through qlinear_gemm, and the same weight without its outliers (the dense kernel
+    alone).  The weight (123 MB) is read once per launch; its reuse across the 512 rows makes
+    the call MFMA-bound, so no rotation is needed."""
+    dev = torch.device("cuda")
+    wp, _ = workloads.prefill_weights()
+    dp, wt = quantize_pack(q, torch, wp, 4, workloads.PREFILL_OUTLIER_FRAC)
+    del wp
+    Mp, Kp, Np = workloads.PREFILL_M, workloads.PREFILL_K, workloads.PREFILL_N
+    hp = q.weight(wt["packed"], wt["scales"], wt["zeros"], wt["rowptr"], wt["col"], wt["val"], wt["nnz"])
+    hd = q.weight(wt["packed"], wt["scales"], wt["zeros"])
+    xp = torch.from_numpy(workloads.prefill_activations().view(np.int16)).to(dev)
+    yp = torch.empty((Mp, Np), dtype=torch.int16, device=dev)
+    wsb = q.qlinear_gemm_workspace_bytes(dp, Mp, wt["nnz"])
+    wsp = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    ms = time_graph(torch, lambda i: q.qlinear_gemm(dp, hp, xp, Kp, Mp, yp, Np, wsp, wsb), 10, stream)
+    ms_dense = time_graph(torch, lambda i: q.qlinear_gemm(dp, hd, xp, Kp, Mp, yp, Np, None, 0), 10, stream)
+    dense_flops = 2 * Mp * Np * Kp
+    flops = dense_flops + 2 * Mp * wt["nnz"]
+    tf = flops / (ms * 1e-3) / 1e12
+    tf_dense = dense_flops / (ms_dense * 1e-3) / 1e12
+    wbytes = weight_bytes(Np, Kp, 4, wt["nnz"])
+    del hp, hd, wt, xp, yp, wsp
+    roof = dict(bound="mfma", achieved=round(tf, 1), peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s",
+                frac=round(tf / MFMA_F16_PEAK_TFLOPS, 4), traffic=None,
+                kernel="qlinear_gemm end to end (config M=512 K=8192 N=28672, 4-bit + outliers)",
+                flops_per_launch=flops, avg_launch_us=round(ms * 1e3, 2),
+                dense_kernel_alone=dict(achieved=round(tf_dense, 1), frac=round(tf_dense / MFMA_F16_PEAK_TFLOPS, 4),
+                                        avg_launch_us=round(ms_dense * 1e3, 2), flops_per_launch=dense_flops,
+                                        kernel="qp::gemm_kernel<4, 0, 8> (no outliers)"),
+                weight_bytes=wbytes)
+    return roof
+
+
+def cpu_baselines(workloads, K, N, headline_bytes, seconds):
+    """The oracle (as it stands) on the host cores: the headline GEMV repeated for about
+    `seconds`, the same on one thread, and a column sample of the prefill GEMM in fp64."""
+    import oracle
+    w = workloads.layer_weights(1)
+    ref = oracle.quantize(w, 4)
+    x = workloads.activations_fp16(1, K, workloads.seed_for(1))
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.linear(x, ref)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    cores = oracle.num_threads()
+    cpu = dict(value=round(headline_bytes * reps / dt / 1e9, 4), unit="GB/s", cores=cores, kind="oracle",
+               sample=f"{reps} headline steps (fp64 GEMV, 4096x4096 4-bit, M=1, over the oracle's own codes), "
+                      f"{dt:.1f} s")
+    oracle.set_num_threads(1)
+    t0 = time.perf_counter()
+    reps1 = 0
+    while time.perf_counter() - t0 < seconds / 4:
+        oracle.linear(x, ref)
+        reps1 += 1
+    dt1 = time.perf_counter() - t0
+    oracle.set_num_threads(cores)
+    cpu1 = dict(value=round(headline_bytes * reps1 / dt1 / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                sample=f"{reps1} headline steps on one thread, {dt1:.1f} s")
+    # prefill: every activation row against a sample of weight rows (columns of y)
+    wp, _ = workloads.prefill_weights()
+    ncols = 512
+    refp = oracle.quantize(np.ascontiguousarray(wp[:ncols]), 4)
+    del wp
+    xp = workloads.prefill_activations()
+    t0 = time.perf_counter()
+    oracle.linear(xp, refp)
+    dtp = time.perf_counter() - t0
+    flops = 2 * xp.shape[0] * ncols * xp.shape[1]
+    cpup = dict(value=round(flops / dtp / 1e12, 6), unit="TFLOP/s", cores=cores, kind="oracle",
+                sample=f"all {xp.shape[0]} activation rows x {ncols} of the 28672 weight rows of the prefill "
+                       f"GEMM (K={xp.shape[1]}, fp64, outliers not held out in the sample), {dtp:.1f} s")
+    return cpu, cpu1, cpup
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--copies", type=int, default=32, help="rotating weight copies (>= 1 GB total)")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    ap.add_argument("--no-prefill", action="store_true", help="skip the M=512 GEMM secondary line")
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baselines")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the M=512 GEMM line")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the 2/3/5/6-bit x M=1,4,8 sweep lines")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the symmetric / small-group / b-bit zero point GEMV lines")
     ap.add_argument("--no-stack", action="store_true", help="skip the 32-layer decode stack line")
     ap.add_argument("--no-moe", action="store_true", help="skip the routed-expert FFN line")
     ap.add_argument("--no-kv", action="store_true", help="skip the quantized-KV decode attention line")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--pmc-pass", action="store_true",
-                    help="eager launches only (each GEMV of the step, the prefill GEMM, a 1 GiB copy) for "
-                         "hardware-counter runs; prints no JSON")
+                    help="eager launches only (the headline GEMV, each GEMV of the sweep, the prefill GEMM, "
+                         "decode attention, a 1 GiB copy) for hardware-counter runs; prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no "
@@ -397,157 +517,110 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda")
     K = N = 4096
-    bits_list, m_list = workloads.SWEEP_BITS, workloads.SWEEP_M
 
     if args.pmc_pass:
         pmc_pass(q, torch, workloads)
         return
 
-    log("bench: quantize + pack 4096x4096 at 2/3/5/6 bits")
-    w = workloads.layer_weights(2)
-    W = {}
-    for b in bits_list:
-        d, wt = quantize_pack(q, torch, w, b)
-        copies = [dict(packed=wt["packed"].clone(), scales=wt["scales"].clone(), zeros=wt["zeros"].clone())
-                  for _ in range(args.copies)]
-        W[b] = (d, [q.weight(c["packed"], c["scales"], c["zeros"]) for c in copies], copies)
-    X = {m: torch.from_numpy(workloads.activations_fp16(m, K, workloads.seed_for(2)).view(np.int16)).to(dev)
-         for m in m_list}
-    Y = {(b, m): torch.empty((m, N), dtype=torch.int16, device=dev) for b in bits_list for m in m_list}
-    step_bytes = sum(weight_bytes(N, K, b) for b in bits_list) * len(m_list)
-    total_copy_bytes = sum(weight_bytes(N, K, b) for b in bits_list) * args.copies
-    log(f"bench: {args.copies} copies, {total_copy_bytes / 2**30:.2f} GiB of packed weights")
-
-    def step(c):
-        # every GEMV of a step reads its own weight copy, so no launch finds the previous
-        # launch's bytes in the Infinity Cache
-        for b in bits_list:
-            d, hs, _ = W[b]
-            for mi, m in enumerate(m_list):
-                q.qlinear_gemv(d, hs[(c * len(m_list) + mi) % args.copies], X[m], K, m, Y[(b, m)], N)
-
+    # ---- headline: 4096 x 4096, 4-bit, M = 1 ------------------------------------------------
+    log("bench: quantize + pack the 4096x4096 4-bit layer")
+    d4, w4 = quantize_pack(q, torch, workloads.layer_weights(1), 4)
+    step_bytes = weight_bytes(N, K, 4)
+    h4, keep4 = rotated_gemv(q, torch, d4, w4, step_bytes)
+    ncopies = len(h4)
+    x1 = torch.from_numpy(workloads.activations_fp16(1, K, workloads.seed_for(1)).view(np.int16)).to(dev)
+    y1 = torch.empty((1, N), dtype=torch.int16, device=dev)
+    log(f"bench: {ncopies} copies, {ncopies * step_bytes / 2**30:.2f} GiB of packed weights")
     stream = torch.cuda.Stream()
-    graphs = []
-    for c in range(args.copies):
+
+    def capture(count):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            step(c)
-        graphs.append(g)
+            for i in range(count):
+                q.qlinear_gemv(d4, h4[i % ncopies], x1, K, 1, y1, N)
+        return g
+
+    g_full = capture(ncopies)
+    rem = args.steps % ncopies
+    g_rem = capture(rem) if rem else None
     torch.cuda.synchronize()
 
     log(f"bench: warmup {args.warmup} steps")
-    for i in range(args.warmup):
-        graphs[i % args.copies].replay()
+    for _ in range(-(-args.warmup // ncopies)):
+        g_full.replay()
     torch.cuda.synchronize()
     log(f"bench: timing {args.steps} steps")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_wall = time.perf_counter()
     with torch.cuda.stream(stream):
         e0.record(stream)
-        for i in range(args.steps):
-            graphs[i % args.copies].replay()
+        for _ in range(args.steps // ncopies):
+            g_full.replay()
+        if g_rem is not None:
+            g_rem.replay()
         e1.record(stream)
     torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
     ms_total = e0.elapsed_time(e1)
     ms_per_step = ms_total / args.steps
     value = step_bytes * args.steps / (ms_total * 1e-3) / 1e9
+    kname = gemv_kernel_name(4, 1, N)
+    roofline = dict(bound="hbm", achieved=round(value, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(value / HBM_PEAK_GBS, 4), traffic=measured_traffic(kname),
+                    kernel=kname, bytes_per_launch=step_bytes, avg_launch_us=round(ms_per_step * 1e3, 3))
+    del g_full, g_rem
+    extra = {"gemv_4096_4bit_m1_median5": gemv_line(q, torch, stream, d4, w4, step_bytes, x1, 1, y1, N)}
+    del h4, keep4
 
-    # per-kernel live timing (graphs of back-to-back launches of one (bits, M) kernel)
-    log("bench: per-kernel timing")
-    per = {}
-    for b in bits_list:
-        d, hs, _ = W[b]
-        for m in m_list:
-            fn = lambda i, d=d, hs=hs, m=m, b=b: q.qlinear_gemv(d, hs[i % args.copies], X[m], K, m, Y[(b, m)], N)
-            ms = time_graph(torch, fn, 4 * args.copies, stream)
-            per[f"b{b}_m{m}"] = dict(us=ms * 1e3, GBps=weight_bytes(N, K, b) / (ms * 1e-3) / 1e9)
-    dom = max(per, key=lambda key: per[key]["us"])
-    b_dom = int(dom.split("_")[0][1:])
-    dom_bytes = weight_bytes(N, K, b_dom)
-    achieved = dom_bytes / (per[dom]["us"] * 1e-6) / 1e9
-    kname = gemv_kernel_name(b_dom, int(dom.split("_m")[1]), N)
-    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(kname),
-                    kernel=f"{kname} ({dom})", bytes_per_launch=dom_bytes,
-                    avg_launch_us=round(per[dom]["us"], 3))
-
-    extra = {}
     if not args.no_prefill:
         log("bench: prefill GEMM M=512 K=8192 N=28672 4-bit + 0.1% outliers")
-        wp, _ = workloads.prefill_weights()
-        dp, wt = quantize_pack(q, torch, wp, 4, workloads.PREFILL_OUTLIER_FRAC)
-        del wp
-        hp = q.weight(wt["packed"], wt["scales"], wt["zeros"], wt["rowptr"], wt["col"], wt["val"], wt["nnz"])
-        xp = torch.from_numpy(workloads.prefill_activations().view(np.int16)).to(dev)
-        Mp, Kp, Np = workloads.PREFILL_M, workloads.PREFILL_K, workloads.PREFILL_N
-        yp = torch.empty((Mp, Np), dtype=torch.int16, device=dev)
-        wsb = q.qlinear_gemm_workspace_bytes(dp, Mp, wt["nnz"])
-        wsp = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
-        ms = time_graph(torch, lambda i: q.qlinear_gemm(dp, hp, xp, Kp, Mp, yp, Np, wsp, wsb), 10, stream)
-        flops = 2 * Mp * Np * Kp + 2 * Mp * wt["nnz"]
-        tf = flops / (ms * 1e-3) / 1e12
-        extra["prefill_gemm_m512"] = dict(us=round(ms * 1e3, 2), TFLOPs=round(tf, 1),
-                                          frac_mfma_f16=round(tf / MFMA_F16_PEAK_TFLOPS, 4),
-                                          flops=flops, kernel="qp::gemm_kernel<4>")
-        del hp, wt, xp, yp
+        extra["roofline_prefill"] = bench_prefill(q, torch, workloads, stream)
 
-    log("bench: 4096x4096 4-bit GEMV at M=1")
-    d4, w4 = quantize_pack(q, torch, workloads.layer_weights(1), 4)
-    c4 = [clone_weight(torch, w4) for _ in range(args.copies)]
-    h4 = [q.weight(c["packed"], c["scales"], c["zeros"]) for c in c4]
-    x1 = torch.from_numpy(workloads.activations_fp16(1, K, workloads.seed_for(1)).view(np.int16)).to(dev)
-    y1 = torch.empty((1, N), dtype=torch.int16, device=dev)
-    ms4 = time_graph(torch, lambda i: q.qlinear_gemv(d4, h4[i % args.copies], x1, K, 1, y1, N), 4 * args.copies,
-                     stream)
-    b4 = weight_bytes(N, K, 4)
-    extra["gemv_4096_4bit_m1"] = dict(us=round(ms4 * 1e3, 3), GBps=round(b4 / (ms4 * 1e-3) / 1e9, 1),
-                                      frac_hbm_peak=round(b4 / (ms4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                      kernel=gemv_kernel_name(4, 1, N))
-    del c4, h4, w4
-    log("bench: 4096x4096 symmetric 2- and 3-bit GEMV at M=1 (no zero points)")
-    sym = {}
-    for b in (2, 3):
-        ds, wsy = quantize_pack(q, torch, workloads.layer_weights(2), b, sym=True)
-        cs = [clone_weight(torch, wsy) for _ in range(args.copies)]
-        hs = [q.weight(c["packed"], c["scales"], None) for c in cs]
-        ms = time_graph(torch, lambda i: q.qlinear_gemv(ds, hs[i % args.copies], x1, K, 1, y1, N), 4 * args.copies,
-                        stream)
-        bs = weight_bytes(N, K, b, sym=True)
-        sym[f"b{b}_m1"] = dict(us=round(ms * 1e3, 3), GBps=round(bs / (ms * 1e-3) / 1e9, 1), bytes=bs)
-        del cs, hs, wsy
-    extra["gemv_4096_sym_m1"] = sym
-    log("bench: 4096x4096 GEMV at M=1 with groups of 32 and 64")
-    small = {}
-    for b, g, sy in ((2, 32, True), (2, 64, True), (2, 32, False), (5, 64, False), (6, 64, False)):
-        ds, wsy = quantize_pack(q, torch, workloads.layer_weights(2), b, sym=sy, g=g)
-        cs = [clone_weight(torch, wsy) for _ in range(args.copies)]
-        hs = [q.weight(c["packed"], c["scales"], c["zeros"]) for c in cs]
-        ms = time_graph(torch, lambda i: q.qlinear_gemv(ds, hs[i % args.copies], x1, K, 1, y1, N), 4 * args.copies,
-                        stream)
-        bs = weight_bytes(N, K, b, sym=sy, g=g)
-        small[f"b{b}_g{g}{'_sym' if sy else ''}"] = dict(us=round(ms * 1e3, 3), GBps=round(bs / (ms * 1e-3) / 1e9, 1),
-                                                         bytes=bs, bits_per_weight=round(8 * bs / (N * K), 4))
-        del cs, hs, wsy
-    extra["gemv_4096_small_groups_m1"] = small
-    log("bench: 4096x4096 GEMV at M=1 with zero points in b bits")
-    pz = {}
-    for b, g in ((2, 32), (3, 64), (5, 64), (6, 128)):
-        dz = q.desc(b, N, K, group_size=g, zero_mode=q.QP_ZERO_PACKED)
-        _, wz = quantize_pack(q, torch, workloads.layer_weights(2), b, g=g)
-        zp = torch.empty(q.qp_zero_bytes(dz), dtype=torch.uint8, device=dev)
-        q.qpack_pack_zeros(dz, wz["zeros"], zp)
-        cs = [dict(packed=wz["packed"].clone(), scales=wz["scales"].clone(), zeros=zp.clone())
-              for _ in range(args.copies)]
-        hs = [q.weight(c["packed"], c["scales"], c["zeros"]) for c in cs]
-        ms = time_graph(torch, lambda i: q.qlinear_gemv(dz, hs[i % args.copies], x1, K, 1, y1, N), 4 * args.copies,
-                        stream)
-        bz = N * K * b // 8 + (N * K // g) * 2 + q.qp_zero_bytes(dz)
-        pz[f"b{b}_g{g}"] = dict(us=round(ms * 1e3, 3), GBps=round(bz / (ms * 1e-3) / 1e9, 1), bytes=bz,
-                                bits_per_weight=round(8 * bz / (N * K), 4))
-        del cs, hs, wz, zp
-    extra["gemv_4096_packed_zeros_m1"] = pz
+    if not args.no_sweep:
+        log("bench: 4096x4096 sweep, bits 2/3/5/6 x M 1/4/8")
+        sweep = {}
+        w2 = workloads.layer_weights(2)
+        for b in workloads.SWEEP_BITS:
+            d, wt = quantize_pack(q, torch, w2, b)
+            for m in workloads.SWEEP_M:
+                x = torch.from_numpy(workloads.activations_fp16(m, K, workloads.seed_for(2)).view(np.int16)).to(dev)
+                y = torch.empty((m, N), dtype=torch.int16, device=dev)
+                line = gemv_line(q, torch, stream, d, wt, weight_bytes(N, K, b), x, m, y, N)
+                line["kernel"] = gemv_kernel_name(b, m, N)
+                sweep[f"b{b}_m{m}"] = line
+            del wt
+        extra["sweep_4096"] = sweep
+
+    if not args.no_variants:
+        log("bench: 4096x4096 GEMV at M=1: symmetric groups, groups of 32/64, b-bit zero points")
+        w2 = workloads.layer_weights(2)
+        sym = {}
+        for b in (2, 3):
+            ds, wsy = quantize_pack(q, torch, w2, b, sym=True)
+            sym[f"b{b}_m1"] = gemv_line(q, torch, stream, ds, wsy, weight_bytes(N, K, b, sym=True), x1, 1, y1, N)
+            del wsy
+        extra["gemv_4096_sym_m1"] = sym
+        small = {}
+        for b, g, sy in ((2, 32, True), (2, 64, True), (2, 32, False), (5, 64, False), (6, 64, False)):
+            ds, wsy = quantize_pack(q, torch, w2, b, sym=sy, g=g)
+            bs = weight_bytes(N, K, b, sym=sy, g=g)
+            line = gemv_line(q, torch, stream, ds, wsy, bs, x1, 1, y1, N)
+            line["bits_per_weight"] = round(8 * bs / (N * K), 4)
+            small[f"b{b}_g{g}{'_sym' if sy else ''}"] = line
+            del wsy
+        extra["gemv_4096_small_groups_m1"] = small
+        pz = {}
+        for b, g in ((2, 32), (3, 64), (5, 64), (6, 128)):
+            dz = q.desc(b, N, K, group_size=g, zero_mode=q.QP_ZERO_PACKED)
+            _, wz = quantize_pack(q, torch, w2, b, g=g)
+            zp = torch.empty(q.qp_zero_bytes(dz), dtype=torch.uint8, device=dev)
+            q.qpack_pack_zeros(dz, wz["zeros"], zp)
+            wz["zeros"] = zp
+            bz = N * K * b // 8 + (N * K // g) * 2 + q.qp_zero_bytes(dz)
+            line = gemv_line(q, torch, stream, dz, wz, bz, x1, 1, y1, N)
+            line["bits_per_weight"] = round(8 * bz / (N * K), 4)
+            pz[f"b{b}_g{g}"] = line
+            del wz, zp
+        extra["gemv_4096_packed_zeros_m1"] = pz
     if not args.no_stack:
         log("bench: Llama-7B-shaped 32-layer decode stack at M=1")
         extra["stack_llama7b_m1"] = bench_stack(q, torch, workloads, stream)
@@ -561,50 +634,24 @@ def main():
     log("bench: 1 GiB device copy")
     extra["copy_GBps"] = round(copy_gbps(torch), 1)
 
-    cpu = cpu1 = None
+    cpu = cpu1 = cpup = None
     if not args.no_cpu:
-        import oracle
-        log("bench: CPU oracle baseline")
-        refs = {b: oracle.quantize(w, b) for b in bits_list}
-        xs = {m: workloads.activations_fp16(m, K, workloads.seed_for(2)) for m in m_list}
-        t0 = time.perf_counter()
-        reps = 0
-        while True:
-            for b in bits_list:
-                for m in m_list:
-                    oracle.linear(xs[m], refs[b])
-            reps += 1
-            if time.perf_counter() - t0 >= args.cpu_seconds or reps >= 50:
-                break
-        dt = time.perf_counter() - t0
-        cpu = dict(value=round(step_bytes * reps / dt / 1e9, 4), unit="GB/s", cores=oracle.num_threads(),
-                   kind="oracle",
-                   sample=f"{reps} full steps (12 fp64 GEMVs over the oracle's own codes), {dt:.1f} s")
-        # the same oracle on one thread, over one step
-        threads = oracle.num_threads()
-        oracle.set_num_threads(1)
-        t0 = time.perf_counter()
-        for b in bits_list:
-            for m in m_list:
-                oracle.linear(xs[m], refs[b])
-        dt1 = time.perf_counter() - t0
-        oracle.set_num_threads(threads)
-        cpu1 = dict(value=round(step_bytes / dt1 / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                    sample=f"1 full step (12 fp64 GEMVs over the oracle's own codes) on one thread, {dt1:.1f} s")
+        log("bench: CPU oracle baselines")
+        cpu, cpu1, cpup = cpu_baselines(workloads, K, N, step_bytes, args.cpu_seconds)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-        "config": {"workload": "4096x4096 layer, bits {2,3,5,6} x decode M {1,4,8}, asymmetric g=128, "
-                               "page units, device tile layout",
-                   "bits": list(bits_list), "m": list(m_list), "n": N, "k": K,
-                   "weight_copies": args.copies, "step_weight_bytes": step_bytes,
+        "config": {"workload": "4096x4096 layer, 4-bit asymmetric g=128, decode M=1 GEMV (page units, "
+                               "device tile layout)",
+                   "bits": 4, "m": 1, "n": N, "k": K, "group": 128,
+                   "weight_copies": ncopies, "step_weight_bytes": step_bytes,
                    "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "cpu_baseline_1thread": cpu1,
-        "per_kernel": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in per.items()},
+        "cpu_baseline_prefill": cpup,
         **extra,
     }
     print(json.dumps(out), flush=True)

@@ -147,14 +147,15 @@ def test_gemm_and_gemv_agree():
 @pytest.mark.timeout(600)
 def test_gemm_prefill_full_sampled():
     """M=512, K=8192, N=28672, 4-bit + 0.1% outliers, the shape and launch the benchmark
-    times; 48 output rows x 40 activation rows recomputed by the oracle."""
+    times; 512 weight rows (spread over the 112 row tiles) x all 512 activation rows
+    recomputed by the oracle."""
     w, pos = workloads.prefill_weights()
     x = workloads.prefill_activations()
     g = GpuWeight(w, 4, workloads.PREFILL_OUTLIER_FRAC)
     y = run_linear("qlinear_gemm", g, x)
     rng = np.random.default_rng(4)
-    ns = np.sort(rng.choice(w.shape[0], 48, replace=False))
-    ms = np.sort(rng.choice(x.shape[0], 40, replace=False))
+    ns = np.sort(rng.choice(w.shape[0], 512, replace=False))
+    ms = np.arange(x.shape[0])
     w0 = w.copy()
     w0.reshape(-1)[pos] = 0
     sub = oracle.quantize(w0[ns], 4)

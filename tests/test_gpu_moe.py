@@ -326,13 +326,25 @@ def test_moe_all_tokens_one_expert_many_tiles():
 @pytest.mark.timeout(900)
 def test_moe_ffn_full_sampled():
     """16 experts, d_model 4096, d_ff 14336, 128 tokens top-2 Zipf(1.1): the whole FFN on the
-    GPU in the launch sequence the benchmark uses; 4 tokens recomputed by the oracle."""
+    GPU in the launch sequence the benchmark uses; at least 16 tokens, chosen so that together
+    they route to every active expert, recomputed by the oracle."""
     E, D, F = workloads.MOE_EXPERTS, workloads.MOE_DMODEL, workloads.MOE_DFF
     x, ids, wts = workloads.moe_inputs()
     ex = Experts(E, D, F, 4, stream=5)
     y = run_ffn(ex, x, ids, wts)
     assert np.isfinite(y).all()
-    pick = np.array([0, 5, 77, 127])
+    chosen = [0, 5, 77, 127]
+    for e in np.unique(ids):
+        if e not in ids[chosen]:
+            chosen.append(int(np.nonzero((ids == e).any(axis=1))[0][0]))
+    for t in np.linspace(0, len(ids) - 1, 16).astype(int):
+        if len(chosen) >= 16:
+            break
+        if t not in chosen:
+            chosen.append(int(t))
+    pick = np.array(sorted(chosen))
+    assert len(pick) >= 16 and set(ids[pick].ravel()) == set(np.unique(ids))
+    print(f"moe full: {len(pick)} tokens cover {len(np.unique(ids))} active experts", flush=True)
     used = set(ids[pick].ravel().tolist())
     r = oracle.moe_ffn(x[pick], ids[pick], wts[pick], *ex.oracle_sets(used))
     check_ffn(y[pick], r, flip_bound(ex, x[pick], ids[pick], wts[pick]))
