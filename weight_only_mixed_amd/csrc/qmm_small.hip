@@ -188,8 +188,15 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
         const int64_t i = i0 + sd;
         if (i >= nt) break;  // uniform
         const int64_t kt = wv + i * NW;
-        ring_issue<B, MX, GS, ZP>(bf, kt + NW, lane, a.ldx, sd == 0 ? slot1 : slot0);
-        wait_vm<S::kLoads>();
+        // At 2 and 4 bits nothing is fetched past the wave's last tile (2-2.5% faster at
+        // 4096 x 4096); at 3, 5 and 6 bits the same branch measured 5-9% slower, so those widths
+        // keep issuing the (out-of-range, zero-filled) fetch for the tile after the last.
+        if ((B != 2 && B != 4) || i + 1 < nt) {  // uniform
+            ring_issue<B, MX, GS, ZP>(bf, kt + NW, lane, a.ldx, sd == 0 ? slot1 : slot0);
+            wait_vm<S::kLoads>();
+        } else {
+            wait_vm<0>();
+        }
         const uint8_t *slot = sd == 0 ? slot0 : slot1;
         uint32_t d[2 * B];
 #pragma unroll
