@@ -379,6 +379,25 @@ qp_status qattn_decode(const qkv_desc *desc, const uint16_t *q, const void *k_co
                        const int32_t *seq_lens, float sm_scale, uint16_t *o, void *workspace,
                        size_t ws_bytes, void *stream);
 
+/*
+ * qattn_decode for callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, kernels and
+ * results as qattn_decode, without the workspace: the chunk partials live in a fixed array
+ * inside the library, QATTN_NOALLOC_SCRATCH_BYTES bytes per GPU, created with the library and
+ * held by each GPU it runs on until the process ends.  Its address on a GPU is looked up once,
+ * on the first call with that GPU current.  No call allocates anything.
+ *  Limit: qattn_decode_workspace_bytes(desc) must not exceed QATTN_NOALLOC_SCRATCH_BYTES
+ *  (2 MiB covers every shape with up to 8 query heads per kv head, and more whenever the
+ *  cache is split into fewer chunks); otherwise QP_ERR_WORKSPACE and nothing is launched.
+ *  All calls on one GPU share the array: calls that overlap on one GPU (different streams,
+ *  or host threads without ordering) race and give wrong results.  The array is written
+ *  before it is read within a call, so nothing needs clearing between calls.
+ */
+#define QATTN_NOALLOC_SCRATCH_BYTES (2u * 1024u * 1024u)
+qp_status qattn_decode_noalloc(const qkv_desc *desc, const uint16_t *q, const void *k_codes,
+                               const float *k_scales, const void *v_codes, const float *v_scales,
+                               const int32_t *seq_lens, float sm_scale, uint16_t *o, void *stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char *qp_last_error(void);
 

@@ -305,3 +305,15 @@ def test_packed_zero_points():
     assert q.qpack_pack_zeros(ds, FAKE, FAKE, stream=0, check=False) == E      # mode must be packed
     assert q.qpack_pack_zeros(d, FAKE + 1, FAKE, stream=0, check=False) == E
     assert q.qpack_pack_zeros(d, FAKE, FAKE + 2, stream=0, check=False) == E
+
+
+def test_attention_noalloc_rejects_scratch_beyond_its_limit():
+    """16 query heads per kv head over 16 kv heads split into 16 chunks needs 4096 partials
+    (2,129,920 bytes), above the fixed 2 MiB: refused before any device call."""
+    d = q.kv_desc(1, 256, 16, 32768, 4, 8, 64, 64)
+    need = q.qattn_decode_workspace_bytes(d)
+    assert need == 4096 * (128 * 4 + 8) > q.QATTN_NOALLOC_SCRATCH_BYTES
+    st = q.qattn_decode_noalloc(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, stream=0, check=False)
+    assert st == q.QP_ERR_WORKSPACE and "2097152" in q.last_error()
+    # within the limit: the benchmarked 4 x 8K GQA layer (2048 partials)
+    assert 0 < q.qattn_decode_workspace_bytes(q.kv_desc(4, 64, 8, 8192)) <= q.QATTN_NOALLOC_SCRATCH_BYTES

@@ -87,6 +87,7 @@ _SIGS = {
     "qkv_quantize": (_i32, [_KD, _i32, _vp, _i64, _vp, _i64, _vp, _vp, _vp]),
     "qattn_decode_workspace_bytes": (_sz, [_KD]),
     "qattn_decode": (_i32, [_KD, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _sz, _vp]),
+    "qattn_decode_noalloc": (_i32, [_KD, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp]),
     "qp_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -281,6 +282,17 @@ def qattn_decode(d, q, k_codes, k_scales, v_codes, v_scales, seq_lens, sm_scale,
                   lib.qattn_decode(ctypes.byref(d), _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
                                    _ptr(v_scales), _ptr(seq_lens), float(sm_scale), _ptr(o), _ptr(workspace),
                                    ws_bytes, _stream(stream)), check)
+
+
+QATTN_NOALLOC_SCRATCH_BYTES = 2 * 1024 * 1024
+
+
+def qattn_decode_noalloc(d, q, k_codes, k_scales, v_codes, v_scales, seq_lens, sm_scale, o, stream=None,
+                         check=True):
+    return _check("qattn_decode_noalloc",
+                  lib.qattn_decode_noalloc(ctypes.byref(d), _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
+                                           _ptr(v_scales), _ptr(seq_lens), float(sm_scale), _ptr(o),
+                                           _stream(stream)), check)
 
 
 EXPORTED = tuple(_SIGS)

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kv_internal.h"
 #include "qp_internal.h"
 
@@ -116,6 +118,33 @@ static qp_status check_kv(const qkv_desc *d)
 }
 
 static int64_t kv_rows(const qkv_desc *d) { return (int64_t)d->batch * d->kv_heads * d->capacity; }
+
+// Scratch of qattn_decode_noalloc: one copy per GPU.  In host code `scratch` names a host-side
+// stand-in, not device memory, so its device address is looked up per device (with that device
+// current) and only that address is ever passed to kernels.
+__device__ __align__(256) uint8_t scratch[QATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_dev[kMaxDevices];
+
+static qp_status scratch_address(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(QP_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(QP_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(QP_ERR_DEVICE, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return QP_OK;
+}
 
 }  // namespace qp
 
@@ -586,6 +615,23 @@ qp_status qattn_decode(const qkv_desc *d, const uint16_t *q, const void *k_codes
     a.c = (float)((double)sm_scale * 1.4426950408889634);
     return device(launch_kv_attn(d->k_bits, d->v_bits, d->k_group, d->v_group, d->batch, a, S(stream)),
                   "kv attention");
+}
+
+qp_status qattn_decode_noalloc(const qkv_desc *d, const uint16_t *q, const void *k_codes, const float *k_scales,
+                               const void *v_codes, const float *v_scales, const int32_t *seq_lens, float sm_scale,
+                               uint16_t *o, void *stream)
+{
+    qp_status st;
+    if ((st = check_kv(d)) != QP_OK) return st;
+    const size_t need = qattn_decode_workspace_bytes(d);
+    if (need > QATTN_NOALLOC_SCRATCH_BYTES)
+        return fail(QP_ERR_WORKSPACE,
+                    "qattn_decode_noalloc: this shape needs %zu bytes of scratch, above its fixed %u bytes; "
+                    "use qattn_decode with a workspace",
+                    need, (unsigned)QATTN_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if (need > 0 && (st = scratch_address(&ws)) != QP_OK) return st;
+    return qattn_decode(d, q, k_codes, k_scales, v_codes, v_scales, seq_lens, sm_scale, o, ws, need, stream);
 }
 
 }  // extern "C"
