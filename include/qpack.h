@@ -398,6 +398,31 @@ qp_status qattn_decode_noalloc(const qkv_desc *desc, const uint16_t *q, const vo
                                const float *k_scales, const void *v_codes, const float *v_scales,
                                const int32_t *seq_lens, float sm_scale, uint16_t *o, void *stream);
 
+/*
+ * Serialized packed weight (HOST memory): a self-describing little-endian byte string holding
+ * one quantized, packed weight -- codes (either layout), scales, zero points and the outlier
+ * CSR -- so a repacked model can be stored and reloaded without repacking (the one-time repack
+ * of the single-GPU 70B page, s3; every field little-endian as the mixed-bit page, s3.2, reads
+ * its units).  Layout: a 64-byte header -- "QPKW", u32 version 1, u32 header size 64, i32 bits,
+ * i32 group size, i32 layout, i32 zero mode, u32 flags 0, i64 n, i64 k, i64 nnz, u32 CRC-32
+ * (IEEE) of the whole blob with this field counted as zeros, u32 0 -- then sections at
+ * multiples of 64 bytes:
+ * packed codes, scales (u16 each), zero points (absent for implied ones), and with nnz > 0 the
+ * CSR row pointers (i32, n+1), columns (i32) and values (u16).
+ */
+/* Bytes of the blob of a weight with `nnz` outliers (0 if desc is invalid). */
+size_t qp_blob_bytes(const qp_weight_desc *desc, int64_t nnz);
+/* Serialize.  w holds HOST pointers (sizes as for the device arrays; CSR arrays only when
+ * w->nnz > 0).  blob: host, at least qp_blob_bytes(desc, w->nnz) bytes (else QP_ERR_WORKSPACE). */
+qp_status qp_blob_write(const qp_weight_desc *desc, const qp_weight *w, void *blob, size_t blob_bytes);
+/* Check a blob (magic, version, sizes, checksum, CSR row pointers and columns) and return its
+ * descriptor, its nnz and, if offsets is not NULL, the byte offsets of its six sections
+ * (packed, scales, zeros, rowptr, col, val; 0 for an absent section).  The sections hold
+ * little-endian integers and can be used in place on a little-endian host.  A blob that
+ * fails any check returns QP_ERR_INVALID_ARG (QP_ERR_UNSUPPORTED for an unknown version). */
+qp_status qp_blob_parse(const void *blob, size_t blob_bytes, qp_weight_desc *desc_out, int64_t *nnz_out,
+                        size_t *offsets);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char *qp_last_error(void);
 

@@ -88,6 +88,9 @@ _SIGS = {
     "qattn_decode_workspace_bytes": (_sz, [_KD]),
     "qattn_decode": (_i32, [_KD, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _sz, _vp]),
     "qattn_decode_noalloc": (_i32, [_KD, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp]),
+    "qp_blob_bytes": (_sz, [_D, _i64]),
+    "qp_blob_write": (_i32, [_D, _W, _vp, _sz]),
+    "qp_blob_parse": (_i32, [_vp, _sz, _D, ctypes.POINTER(_i64), ctypes.POINTER(_sz)]),
     "qp_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -282,6 +285,30 @@ def qattn_decode(d, q, k_codes, k_scales, v_codes, v_scales, seq_lens, sm_scale,
                   lib.qattn_decode(ctypes.byref(d), _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
                                    _ptr(v_scales), _ptr(seq_lens), float(sm_scale), _ptr(o), _ptr(workspace),
                                    ws_bytes, _stream(stream)), check)
+
+
+def qp_blob_bytes(d, nnz: int = 0) -> int:
+    return lib.qp_blob_bytes(ctypes.byref(d), nnz)
+
+
+def qp_blob_write(d, w, blob, check=True):
+    """w: a qp_weight of HOST addresses; blob: a writable host buffer (e.g. a numpy uint8 array)."""
+    import numpy as np
+    b = np.ascontiguousarray(blob)
+    return _check("qp_blob_write", lib.qp_blob_write(ctypes.byref(d), ctypes.byref(w), b.ctypes.data, b.nbytes),
+                  check)
+
+
+def qp_blob_parse(blob, check=True):
+    """-> (status, desc, nnz, section offsets (6))."""
+    import numpy as np
+    b = np.ascontiguousarray(blob)
+    d = qp_weight_desc()
+    nnz = _i64(0)
+    offs = (_sz * 6)()
+    st = _check("qp_blob_parse", lib.qp_blob_parse(b.ctypes.data, b.nbytes, ctypes.byref(d), ctypes.byref(nnz), offs),
+                check)
+    return st, d, nnz.value, list(offs)
 
 
 QATTN_NOALLOC_SCRATCH_BYTES = 2 * 1024 * 1024

@@ -1,7 +1,7 @@
 """Build libqpack.so (the HIP library behind include/qpack.h) for gfx950, in-tree.
 
-Every .hip under csrc/ is compiled to an object with hipcc, then linked into one shared
-library next to this file.  The quantizer is compiled without floating-point contraction so
+Every .hip under csrc/ is compiled to an object with hipcc (and every host-only .cpp with g++),
+then linked into one shared library next to this file.  The quantizer is compiled without floating-point contraction so
 its fp32 arithmetic is exactly the stated sequence of IEEE operations.
 """
 from __future__ import annotations
@@ -36,9 +36,16 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
+# Host-only sources (.cpp): plain C++ (g++), no device code.
+HOST = ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-I", str(ROOT / "include"), "-I", str(CSRC)]
+
+
 def _compile(src: Path) -> Path:
     obj = OBJ / (src.stem + ".o")
-    cmd = [hipcc(), *COMMON, *PER_FILE.get(src.name, []), "-c", str(src), "-o", str(obj)]
+    if src.suffix == ".cpp":
+        cmd = [*HOST, "-c", str(src), "-o", str(obj)]
+    else:
+        cmd = [hipcc(), *COMMON, *PER_FILE.get(src.name, []), "-c", str(src), "-o", str(obj)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src.name}:\n{r.stdout}\n{r.stderr}")
@@ -47,7 +54,7 @@ def _compile(src: Path) -> Path:
 
 def build(verbose: bool = False) -> Path:
     OBJ.mkdir(exist_ok=True)
-    srcs = sorted(CSRC.glob("*.hip"))
+    srcs = sorted(CSRC.glob("*.hip")) + sorted(CSRC.glob("*.cpp"))
     jobs = min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
     with ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, srcs))

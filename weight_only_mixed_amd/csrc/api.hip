@@ -38,6 +38,14 @@ static qp_status device(hipError_t e, const char *what)
 
 static bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// a * b * c > lim, for non-negative factors, without overflowing.
+static bool prod_over(int64_t a, int64_t b, int64_t c, int64_t lim)
+{
+    int64_t ab, abc;
+    if (__builtin_mul_overflow(a, b, &ab) || __builtin_mul_overflow(ab, c, &abc)) return true;
+    return abc > lim;
+}
+
 // Shape/format checks shared by every call.  need_device: layout must be DEVICE.
 static qp_status check_desc(const qp_weight_desc *d, bool need_device)
 {
@@ -53,7 +61,7 @@ static qp_status check_desc(const qp_weight_desc *d, bool need_device)
     if (d->group_size != 32 && d->group_size != 64 && d->group_size != 128)
         return fail(QP_ERR_UNSUPPORTED, "group_size=%d (32, 64 and 128 are built)", d->group_size);
     if (d->k % 128 != 0) return fail(QP_ERR_UNSUPPORTED, "k=%lld must be a multiple of 128", (long long)d->k);
-    if (d->n > (1LL << 31) - 1 || d->n * d->k > (1LL << 40))
+    if (d->n > (1LL << 31) - 1 || prod_over(d->n, d->k, 1, 1LL << 40))
         return fail(QP_ERR_INVALID_ARG, "matrix too large");
     if (d->layout == QP_LAYOUT_DEVICE && (d->n % kTileN != 0 || d->k % kTileK != 0))
         return fail(QP_ERR_INVALID_ARG, "device layout needs n %% 16 == 0 and k %% 256 == 0 (n=%lld k=%lld)",
@@ -276,7 +284,7 @@ static qp_status gemv_problem(const qp_weight_desc *d, const qp_weight *w, const
     if ((st = check_weight(d, w, true)) != QP_OK) return st;
     if ((st = check_xy(d, x, ldx, m, y, ldy, d->n, 4)) != QP_OK) return st;
     if (m > 16) return fail(QP_ERR_UNSUPPORTED, "gemv handles m <= 16 (m=%lld); use qlinear_gemm", (long long)m);
-    if (m * ldx * 2 > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "x larger than 2 GiB");
+    if (prod_over(m, ldx, 2, 0x7FFFFFFFLL)) return fail(QP_ERR_UNSUPPORTED, "x larger than 2 GiB");
     *p = GemvProblem{};
     p->w = {(const uint8_t *)w->packed, w->scales, w->zeros};
     p->zmid = zero_pair(d);
@@ -332,8 +340,10 @@ qp_status qlinear_gemv_batch(const qp_gemv_problem *problems, int32_t count, voi
 
 size_t qlinear_gemm_workspace_bytes(const qp_weight_desc *d, int64_t m, int64_t nnz)
 {
-    if (check_desc(d, false) != QP_OK || m < 1 || nnz <= 0) return 0;
-    return (size_t)((d->k * 2 + d->n * 4) * gemm_xt_ld(m));
+    if (check_desc(d, false) != QP_OK || m < 1 || m > (1LL << 24) || nnz <= 0) return 0;
+    const int64_t per = d->k * 2 + d->n * 4;  // n*k <= 2^40 keeps this far from overflow
+    if (prod_over(per, gemm_xt_ld(m), 1, 1LL << 62)) return 0;
+    return (size_t)(per * gemm_xt_ld(m));
 }
 
 qp_status qlinear_gemm(const qp_weight_desc *d, const qp_weight *w, const uint16_t *x, int64_t ldx, int64_t m,
@@ -346,17 +356,17 @@ qp_status qlinear_gemm(const qp_weight_desc *d, const qp_weight *w, const uint16
     if ((st = check_weight(d, w, true)) != QP_OK) return st;
     if ((st = check_xy(d, x, ldx, m, y, ldy, d->n, 4)) != QP_OK) return st;
     if (m > (1LL << 24)) return fail(QP_ERR_INVALID_ARG, "m too large");
-    if (m * ldx * 2 > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "x larger than 2 GiB");
+    if (prod_over(m, ldx, 2, 0x7FFFFFFFLL)) return fail(QP_ERR_UNSUPPORTED, "x larger than 2 GiB");
     if ((int64_t)qp_packed_bytes(d) > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "packed weight larger than 2 GiB");
     GemmArgs a{};
     a.ex[0] = {(const uint8_t *)w->packed, w->scales, w->zeros};
     a.zmid = zero_pair(d);
     if (w->nnz > 0) {
+        if (prod_over(d->k, gemm_xt_ld(m), 2, 0x7FFFFFFFLL) || prod_over(d->n, gemm_xt_ld(m), 4, 0x7FFFFFFFLL))
+            return fail(QP_ERR_UNSUPPORTED, "m*k or m*n too large for the outlier add-back");
         const size_t need = qlinear_gemm_workspace_bytes(d, m, w->nnz);
         if (!workspace || ws_bytes < need || !aligned(workspace, 16))
             return fail(QP_ERR_WORKSPACE, "outlier add-back needs %zu bytes of workspace (16-byte aligned)", need);
-        if (d->k * gemm_xt_ld(m) * 2 > 0x7FFFFFFFLL || d->n * gemm_xt_ld(m) * 4 > 0x7FFFFFFFLL)
-            return fail(QP_ERR_UNSUPPORTED, "m*k or m*n too large for the outlier add-back");
         a.rowptr = w->csr_rowptr;
         a.col = w->csr_col;
         a.val = w->csr_val;
@@ -420,7 +430,7 @@ qp_status qlinear_grouped_gemm(const qp_weight_desc *d, const qp_weight *experts
         return st;
     if (!expert_offsets) return fail(QP_ERR_INVALID_ARG, "expert_offsets NULL");
     if (rows < 0) return fail(QP_ERR_INVALID_ARG, "rows < 0");
-    if (rows * ldx * 2 > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "x larger than 2 GiB");
+    if (prod_over(rows, ldx, 2, 0x7FFFFFFFLL)) return fail(QP_ERR_UNSUPPORTED, "x larger than 2 GiB");
     if ((int64_t)qp_packed_bytes(d) > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "packed weight larger than 2 GiB");
     return grouped_launch(d, experts, n_experts, x, ldx, row_src, expert_offsets, rows, epilogue, y, ldy, 1, 0, stream);
 }
@@ -498,7 +508,7 @@ qp_status qmoe_ffn(const qp_weight_desc *dgu, const qp_weight *gate_up, const qp
     if (tokens * topk * d_ff * 2 > 0x7FFFFFFFLL)
         return fail(QP_ERR_UNSUPPORTED, "tokens*topk*d_ff*2 = %lld bytes of intermediate exceed 2 GiB",
                     (long long)(tokens * topk * d_ff * 2));
-    if (tokens * ldx * 2 > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "x larger than 2 GiB");
+    if (prod_over(tokens, ldx, 2, 0x7FFFFFFFLL)) return fail(QP_ERR_UNSUPPORTED, "x larger than 2 GiB");
 
     const size_t R = (size_t)(tokens * topk);
     uint8_t *p = (uint8_t *)workspace;
