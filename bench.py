@@ -441,6 +441,54 @@ def bench_prefill(q, torch, workloads, stream):
     return roof
 
 
+def host_read_gbps(nbytes: int = 1 << 30, threads: int = 0) -> float:
+    """Host memory read bandwidth: numpy sums over slices of a 1 GiB array in parallel threads
+    (the reductions release the GIL), the reference for the host GEMV's GB/s."""
+    from concurrent.futures import ThreadPoolExecutor
+    n = threads or max(1, (os.cpu_count() or 2) - 1)
+    a = np.ones(nbytes // 8, np.uint64)
+    parts = np.array_split(a, n)
+    with ThreadPoolExecutor(n) as ex:
+        list(ex.map(lambda p: int(p.sum()), parts))
+        t = time.perf_counter()
+        for _ in range(3):
+            list(ex.map(lambda p: int(p.sum()), parts))
+        dt = (time.perf_counter() - t) / 3
+    return nbytes / dt / 1e9
+
+
+def bench_host_gemv(q, workloads, K, N):
+    """Host fused unpack-MAC GEMV (canonical layout, the CPU half of a layer split) on the 4096 x
+    4096 layer at M = 1, rotating over >= 1 GiB of weight copies; GB/s of packed bytes."""
+    import oracle  # the oracle only quantizes and packs the inputs here
+    out = {}
+    w = workloads.layer_weights(1)
+    x = np.ascontiguousarray(workloads.activations_fp16(1, K, workloads.seed_for(1))).view(np.uint16)
+    y = np.zeros((1, N), np.uint16)
+    for bits in (2, 4, 6):
+        r = oracle.quantize(w, bits)
+        packed = np.ascontiguousarray(oracle.pack_canonical(r["codes"], bits))
+        sc, z = np.ascontiguousarray(r["scales"]), np.ascontiguousarray(r["zeros"])
+        nb = weight_bytes(N, K, bits)
+        copies = [(packed.copy(), sc.copy(), z.copy()) for _ in range(copies_for(nb))]
+        hs = [q.qp_weight(p.ctypes.data, s_.ctypes.data, z_.ctypes.data, None, None, None, 0) for p, s_, z_ in copies]
+        d = q.desc(bits, N, K, q.QP_LAYOUT_CANONICAL)
+        for h in hs[:4]:
+            q.qlinear_gemv_host(d, h, x, K, 1, y, N)
+        times = []
+        for _ in range(3):
+            t = time.perf_counter()
+            for h in hs:
+                q.qlinear_gemv_host(d, h, x, K, 1, y, N)
+            times.append((time.perf_counter() - t) / len(hs))
+        dt = float(np.median(times))
+        out[f"b{bits}_m1"] = dict(us=round(dt * 1e6, 1), GBps=round(nb / dt / 1e9, 2), bytes=nb, copies=len(hs))
+        del copies, hs
+    out["threads"] = max(1, (os.cpu_count() or 2) - 1)
+    out["host_read_GBps"] = round(host_read_gbps(), 2)
+    return out
+
+
 def cpu_baselines(workloads, K, N, headline_bytes, seconds):
     """The oracle (as it stands) on the host cores: the headline GEMV repeated for about
     `seconds`, the same on one thread, and a column sample of the prefill GEMM in fp64."""
@@ -499,6 +547,7 @@ def main():
     ap.add_argument("--no-stack", action="store_true", help="skip the 32-layer decode stack line")
     ap.add_argument("--no-moe", action="store_true", help="skip the routed-expert FFN line")
     ap.add_argument("--no-kv", action="store_true", help="skip the quantized-KV decode attention line")
+    ap.add_argument("--no-host", action="store_true", help="skip the host (CPU) fused GEMV line")
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--pmc-pass", action="store_true",
                     help="eager launches only (the headline GEMV, each GEMV of the sweep, the prefill GEMM, "
@@ -630,6 +679,10 @@ def main():
     if not args.no_kv:
         log("bench: decode attention over an INT4-K / INT8-V cache (32K MHA, 4 x 8K GQA)")
         extra["kv_decode_attention"] = bench_kv(q, torch, workloads, stream)
+
+    if not args.no_host:
+        log("bench: host fused unpack-MAC GEMV, 4096x4096, M=1")
+        extra["host_gemv_4096_m1"] = bench_host_gemv(q, workloads, K, N)
 
     log("bench: 1 GiB device copy")
     extra["copy_GBps"] = round(copy_gbps(torch), 1)

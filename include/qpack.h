@@ -399,6 +399,25 @@ qp_status qattn_decode_noalloc(const qkv_desc *desc, const uint16_t *q, const vo
                                const int32_t *seq_lens, float sm_scale, uint16_t *o, void *stream);
 
 /*
+ * Decode GEMV on the HOST CPU for a CPU/GPU layer split (the CPU half of the 2/3/5/6-bit mixed
+ * quantization page: s4.1 fused unpack and multiply-accumulate ordered by output, no buffer of
+ * unpacked weights, byte-permute unpacking on 256-bit vectors; s4.3 prefetch distance 4; s5.2
+ * one core left to the scheduling side).  Same result definition as qlinear_gemv:
+ *     y[m][n] = fp16( sum_g s[n][g] * sum_{k in g} x[m][k] * (q[n][k] - zp[n][g])
+ *                     + sum_{CSR row n} x[m][k] * val )
+ * accumulated in fp32 (each group's partial, then its scale, then the outliers, in fp32).
+ *  desc     canonical layout (QP_LAYOUT_CANONICAL), groups of 32/64/128, byte or implied zero
+ *           points (QP_ZERO_STORED / QP_ZERO_MIDPOINT).
+ *  w        HOST pointers: packed canonical rows, scales, zeros, optional CSR.
+ *  x, y     HOST fp16 [m][ldx] and [m][ldy]; 1 <= m <= 8.
+ *  threads  worker threads (OpenMP); 0 = the machine's processors minus one.
+ * Uses AVX2/FMA/F16C when the CPU has them, else a portable loop with the same arithmetic.
+ * Synchronous; allocates nothing.
+ */
+qp_status qlinear_gemv_host(const qp_weight_desc *desc, const qp_weight *w, const uint16_t *x, int64_t ldx,
+                            int64_t m, uint16_t *y, int64_t ldy, int32_t threads);
+
+/*
  * Serialized packed weight (HOST memory): a self-describing little-endian byte string holding
  * one quantized, packed weight -- codes (either layout), scales, zero points and the outlier
  * CSR -- so a repacked model can be stored and reloaded without repacking (the one-time repack

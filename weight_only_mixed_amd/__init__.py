@@ -88,6 +88,7 @@ _SIGS = {
     "qattn_decode_workspace_bytes": (_sz, [_KD]),
     "qattn_decode": (_i32, [_KD, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _sz, _vp]),
     "qattn_decode_noalloc": (_i32, [_KD, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp]),
+    "qlinear_gemv_host": (_i32, [_D, _W, _vp, _i64, _i64, _vp, _i64, _i32]),
     "qp_blob_bytes": (_sz, [_D, _i64]),
     "qp_blob_write": (_i32, [_D, _W, _vp, _sz]),
     "qp_blob_parse": (_i32, [_vp, _sz, _D, ctypes.POINTER(_i64), ctypes.POINTER(_sz)]),
@@ -285,6 +286,14 @@ def qattn_decode(d, q, k_codes, k_scales, v_codes, v_scales, seq_lens, sm_scale,
                   lib.qattn_decode(ctypes.byref(d), _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
                                    _ptr(v_scales), _ptr(seq_lens), float(sm_scale), _ptr(o), _ptr(workspace),
                                    ws_bytes, _stream(stream)), check)
+
+
+def qlinear_gemv_host(d, w, x, ldx, m, y, ldy, threads: int = 0, check=True):
+    """Host GEMV: w a qp_weight of HOST addresses; x, y host buffers (numpy fp16 / uint16 arrays or
+    integer addresses)."""
+    addr = lambda a: a if isinstance(a, int) else a.ctypes.data
+    return _check("qlinear_gemv_host", lib.qlinear_gemv_host(ctypes.byref(d), ctypes.byref(w), addr(x), ldx, m,
+                                                             addr(y), ldy, threads), check)
 
 
 def qp_blob_bytes(d, nnz: int = 0) -> int:

@@ -36,8 +36,9 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-# Host-only sources (.cpp): plain C++ (g++), no device code.
-HOST = ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-I", str(ROOT / "include"), "-I", str(CSRC)]
+# Host-only sources (.cpp): plain C++ (g++, OpenMP), no device code.  Vector code is selected
+# per function with target attributes, so the objects run on any x86-64 host.
+HOST = ["g++", "-O3", "-std=c++17", "-fPIC", "-Wall", "-fopenmp", "-I", str(ROOT / "include"), "-I", str(CSRC)]
 
 
 def _compile(src: Path) -> Path:
@@ -59,7 +60,7 @@ def build(verbose: bool = False) -> Path:
     with ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB.with_suffix(".so.tmp")
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *map(str, objs), "-o", str(tmp)]
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *map(str, objs), "-lgomp", "-o", str(tmp)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")

@@ -1,0 +1,342 @@
+// Host-side fused unpack + multiply-accumulate GEMV (the CPU half of a CPU/GPU layer split,
+// 2/3/5/6-bit mixed quantization page, s4.1 and s4.3).  Host memory only.
+//
+// What the page asks of the CPU kernel, and how it is met here:
+//  * unpacking fused into the multiply-accumulate loop, no intermediate buffer of unpacked
+//    weights, the loop ordered by output so unpacked values are used at once (s4.1): each
+//    thread takes R output rows at a time and walks k once, its unpacked codes living only in
+//    vector registers;
+//  * byte-permute unpacking on 256-bit vectors (s4.1): the 8 codes of an 8-k block (b bytes,
+//    canonical page units) come from one 16-byte broadcast load, one byte shuffle that puts
+//    the 4 bytes holding code i into 32-bit lane i, one per-lane variable shift and one mask --
+//    the same four instructions for every width, straddling 3- and 5-bit fields included;
+//  * fp32 accumulation with the scale applied in fp32 (s4.2);
+//  * software prefetch four cache lines ahead on every row stream (s4.3: distance 4);
+//  * worker threads one fewer than the cores by default, leaving one for the scheduling side
+//    (s5.2).
+// The zero point is not subtracted per weight: per group, sum_k x_k (q_k - zp) = sum_k x_k q_k
+// - zp * sum_k x_k, and the lane-wise sums of x are accumulated beside the products, so the
+// inner loop is shuffle, shift, and, convert, and one fma per activation row.
+#include <immintrin.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#include "qpack.h"
+
+namespace qp {
+qp_status fail(qp_status st, const char *fmt, ...);
+}
+
+namespace {
+
+// IEEE binary16 -> binary32 (exact), for the portable path and the outlier values.
+float half_to_float(uint16_t h)
+{
+    const uint32_t s = (uint32_t)(h >> 15) << 31, e = (h >> 10) & 31, f = h & 1023;
+    uint32_t bits;
+    if (e == 0) {
+        if (f == 0) {
+            bits = s;
+        } else {  // subnormal: renormalise
+            int sh = 0;
+            uint32_t m = f;
+            while (!(m & 1024)) {
+                m <<= 1;
+                ++sh;
+            }
+            bits = s | ((uint32_t)(113 - sh) << 23) | ((m & 1023) << 13);
+        }
+    } else if (e == 31) {
+        bits = s | 0x7F800000u | (f << 13);
+    } else {
+        bits = s | ((e + 112) << 23) | (f << 13);
+    }
+    float v;
+    memcpy(&v, &bits, 4);
+    return v;
+}
+
+// binary32 -> binary16, round to nearest even (one rounding).
+uint16_t float_to_half(float v)
+{
+    uint32_t x;
+    memcpy(&x, &v, 4);
+    const uint32_t s = (x >> 16) & 0x8000u;
+    const int32_t e = (int32_t)((x >> 23) & 255) - 127;
+    uint32_t m = x & 0x7FFFFFu;
+    if (e == 128) return (uint16_t)(s | 0x7C00u | (m ? 0x200u : 0u));
+    if (e > 15) return (uint16_t)(s | 0x7C00u);
+    if (e >= -14) {  // normal range: keep 10 bits, round on the 13 dropped
+        uint32_t h = ((uint32_t)(e + 15) << 10) | (m >> 13);
+        const uint32_t rem = m & 0x1FFFu;
+        if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) ++h;  // may carry into the exponent
+        return (uint16_t)(s | h);
+    }
+    if (e < -25) return (uint16_t)s;
+    // subnormal result: value = (m | 2^23) * 2^(e-23), in units of 2^-24
+    m |= 0x800000u;
+    const int sh = -e - 1;  // 14..24
+    uint32_t h = m >> sh;
+    const uint32_t rem = m & ((1u << sh) - 1), half = 1u << (sh - 1);
+    if (rem > half || (rem == half && (h & 1u))) ++h;
+    return (uint16_t)(s | h);
+}
+
+struct HostArgs {
+    const uint8_t *w;        // canonical packed rows, k*b/8 bytes each
+    const uint16_t *scales;  // [n][G]
+    const uint8_t *zeros;    // [n][G], or null (implied midpoint zmid)
+    uint32_t zmid;
+    const int32_t *rowptr;
+    const int32_t *col;
+    const uint16_t *val;
+    const uint16_t *x;
+    int64_t ldx, m, n, k, G, gs;
+    uint16_t *y;
+    int64_t ldy;
+    int bits;
+    int64_t total_bytes;  // n * k * b / 8
+};
+
+// Outliers of row r added in fp32, then the one fp16 rounding.
+void finish_row(const HostArgs &a, int64_t r, const float *acc)
+{
+    for (int64_t mm = 0; mm < a.m; ++mm) {
+        float s = acc[mm];
+        if (a.rowptr)
+            for (int32_t p = a.rowptr[r]; p < a.rowptr[r + 1]; ++p)
+                s = __builtin_fmaf(half_to_float(a.x[mm * a.ldx + a.col[p]]), half_to_float(a.val[p]), s);
+        a.y[mm * a.ldy + r] = float_to_half(s);
+    }
+}
+
+// Portable path: the same fused loop (per group: sum x*q and sum x, then scale), scalar.
+void rows_scalar(const HostArgs &a, int64_t r0, int64_t r1)
+{
+    const int b = a.bits;
+    const int64_t rb = a.k * b / 8;
+    float acc[8];
+    for (int64_t r = r0; r < r1; ++r) {
+        for (int64_t mm = 0; mm < a.m; ++mm) acc[mm] = 0.f;
+        const uint8_t *row = a.w + r * rb;
+        for (int64_t g = 0; g < a.G; ++g) {
+            const float s = half_to_float(a.scales[r * a.G + g]);
+            const float zp = (float)(a.zeros ? a.zeros[r * a.G + g] : a.zmid);
+            for (int64_t mm = 0; mm < a.m; ++mm) {
+                float sq = 0.f, sx = 0.f;
+                for (int64_t kk = g * a.gs; kk < (g + 1) * a.gs; ++kk) {
+                    const int64_t bit = kk * b;
+                    uint32_t v = row[bit >> 3] | ((uint32_t)(((bit >> 3) + 1 < rb) ? row[(bit >> 3) + 1] : 0) << 8);
+                    const uint32_t q = (v >> (bit & 7)) & ((1u << b) - 1);
+                    const float xv = half_to_float(a.x[mm * a.ldx + kk]);
+                    sq = __builtin_fmaf(xv, (float)q, sq);
+                    sx += xv;
+                }
+                acc[mm] = __builtin_fmaf(s, __builtin_fmaf(-zp, sx, sq), acc[mm]);
+            }
+        }
+        finish_row(a, r, acc);
+    }
+}
+
+// ---- AVX2 path ---------------------------------------------------------------------------
+#define QP_AVX2 __attribute__((target("avx2,fma,f16c")))
+
+// Byte shuffle and shifts that turn a block's b bytes into its 8 codes in 32-bit lanes:
+// lane i takes bytes floor(b*i/8) .. +3 and shifts right by (b*i) % 8.
+struct Unpacker {
+    __m256i shuf, shift, mask;
+};
+
+QP_AVX2 Unpacker make_unpacker(int b)
+{
+    alignas(32) int8_t sh[32];
+    alignas(32) int32_t sv[8];
+    for (int i = 0; i < 8; ++i) {
+        const int byte0 = (b * i) / 8;
+        for (int j = 0; j < 4; ++j) {
+            const int src = byte0 + j;
+            sh[4 * i + j] = (int8_t)(src < 16 ? src : -128);  // 16-byte lanes: both halves see the block
+        }
+        sv[i] = (b * i) % 8;
+    }
+    Unpacker u;
+    u.shuf = _mm256_load_si256((const __m256i *)sh);
+    u.shift = _mm256_load_si256((const __m256i *)sv);
+    u.mask = _mm256_set1_epi32((1 << b) - 1);
+    return u;
+}
+
+QP_AVX2 inline __m256 unpack8(const uint8_t *p, const Unpacker &u)
+{
+    const __m256i v = _mm256_broadcastsi128_si256(_mm_loadu_si128((const __m128i *)p));
+    const __m256i c = _mm256_and_si256(_mm256_srlv_epi32(_mm256_shuffle_epi8(v, u.shuf), u.shift), u.mask);
+    return _mm256_cvtepi32_ps(c);
+}
+
+// A block read that cannot run past the end of the packed buffer (the last row's tail).
+QP_AVX2 inline __m256 unpack8_safe(const HostArgs &a, const uint8_t *p, const Unpacker &u)
+{
+    alignas(16) uint8_t tmp[16] = {0};
+    const int64_t off = p - a.w, left = a.total_bytes - off;
+    memcpy(tmp, p, (size_t)(left < 16 ? left : 16));
+    return unpack8(tmp, u);
+}
+
+QP_AVX2 inline float hsum(__m256 v)
+{
+    __m128 s = _mm_add_ps(_mm256_castps256_ps128(v), _mm256_extractf128_ps(v, 1));
+    s = _mm_add_ps(s, _mm_movehl_ps(s, s));
+    s = _mm_add_ss(s, _mm_movehdup_ps(s));
+    return _mm_cvtss_f32(s);
+}
+
+// R rows [r0, r0+R) with M activation rows.
+template <int R, int M>
+QP_AVX2 void rows_avx2_tile(const HostArgs &a, int64_t r0, const Unpacker &u)
+{
+    const int b = a.bits;
+    const int64_t rb = a.k * b / 8, bpg = a.gs / 8;  // bytes per row, blocks per group
+    const uint8_t *rows[R];
+    bool tail[R];
+    for (int i = 0; i < R; ++i) {
+        rows[i] = a.w + (r0 + i) * rb;
+        tail[i] = (r0 + i) * rb + rb + 16 > a.total_bytes;
+    }
+    __m256 tot[R][M];
+    for (int i = 0; i < R; ++i)
+        for (int mm = 0; mm < M; ++mm) tot[i][mm] = _mm256_setzero_ps();
+    for (int64_t g = 0; g < a.G; ++g) {
+        __m256 acc[R][M], xs[M];
+        for (int mm = 0; mm < M; ++mm) xs[mm] = _mm256_setzero_ps();
+        for (int i = 0; i < R; ++i)
+            for (int mm = 0; mm < M; ++mm) acc[i][mm] = _mm256_setzero_ps();
+        for (int64_t j = 0; j < bpg; ++j) {
+            const int64_t blk = g * bpg + j, k0 = 8 * blk;
+            __m256 xv[M];
+            for (int mm = 0; mm < M; ++mm) {
+                xv[mm] = _mm256_cvtph_ps(_mm_loadu_si128((const __m128i *)(a.x + mm * a.ldx + k0)));
+                xs[mm] = _mm256_add_ps(xs[mm], xv[mm]);
+            }
+            for (int i = 0; i < R; ++i) {
+                const uint8_t *p = rows[i] + blk * b;
+                if ((blk & 7) == 0) _mm_prefetch((const char *)(p + 4 * 64), _MM_HINT_T0);
+                const __m256 wq = (tail[i] && p + 16 > rows[i] + rb) ? unpack8_safe(a, p, u) : unpack8(p, u);
+                for (int mm = 0; mm < M; ++mm) acc[i][mm] = _mm256_fmadd_ps(xv[mm], wq, acc[i][mm]);
+            }
+        }
+        for (int i = 0; i < R; ++i) {
+            const int64_t r = r0 + i;
+            const float s = half_to_float(a.scales[r * a.G + g]);
+            const float zp = (float)(a.zeros ? a.zeros[r * a.G + g] : a.zmid);
+            const __m256 vs = _mm256_set1_ps(s), vnz = _mm256_set1_ps(-zp);
+            for (int mm = 0; mm < M; ++mm)
+                tot[i][mm] = _mm256_fmadd_ps(vs, _mm256_fmadd_ps(vnz, xs[mm], acc[i][mm]), tot[i][mm]);
+        }
+    }
+    for (int i = 0; i < R; ++i) {
+        float acc1[8];
+        for (int mm = 0; mm < M; ++mm) acc1[mm] = hsum(tot[i][mm]);
+        finish_row(a, r0 + i, acc1);
+    }
+}
+
+template <int M>
+QP_AVX2 void rows_avx2_m(const HostArgs &a, int64_t r0, int64_t r1, const Unpacker &u)
+{
+    constexpr int R = M == 1 ? 4 : M == 2 ? 2 : 1;
+    int64_t r = r0;
+    for (; r + R <= r1; r += R) rows_avx2_tile<R, M>(a, r, u);
+    for (; r < r1; ++r) rows_avx2_tile<1, M>(a, r, u);
+}
+
+QP_AVX2 void rows_avx2(const HostArgs &a, int64_t r0, int64_t r1)
+{
+    const Unpacker u = make_unpacker(a.bits);
+    switch (a.m) {
+    case 1: rows_avx2_m<1>(a, r0, r1, u); break;
+    case 2: rows_avx2_m<2>(a, r0, r1, u); break;
+    case 3: rows_avx2_m<3>(a, r0, r1, u); break;
+    case 4: rows_avx2_m<4>(a, r0, r1, u); break;
+    case 5: rows_avx2_m<5>(a, r0, r1, u); break;
+    case 6: rows_avx2_m<6>(a, r0, r1, u); break;
+    case 7: rows_avx2_m<7>(a, r0, r1, u); break;
+    default: rows_avx2_m<8>(a, r0, r1, u); break;
+    }
+}
+
+// The vector path when the CPU has AVX2, FMA and F16C, unless QPACK_HOST_PORTABLE is set in the
+// environment (which selects the portable loop, e.g. to test it on a vector-capable host).
+bool use_avx2()
+{
+    static const bool cpu = __builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma") &&
+                            __builtin_cpu_supports("f16c");
+    return cpu && !getenv("QPACK_HOST_PORTABLE");
+}
+
+int default_threads()
+{
+#ifdef _OPENMP
+    const int p = omp_get_num_procs();
+    return p > 2 ? p - 1 : 1;
+#else
+    return 1;
+#endif
+}
+
+}  // namespace
+
+extern "C" qp_status qlinear_gemv_host(const qp_weight_desc *d, const qp_weight *w, const uint16_t *x, int64_t ldx,
+                                       int64_t m, uint16_t *y, int64_t ldy, int32_t threads)
+{
+    if (!d || !w || !x || !y) return qp::fail(QP_ERR_INVALID_ARG, "qlinear_gemv_host: NULL argument");
+    if (qp_packed_bytes(d) == 0) return qp::fail(QP_ERR_INVALID_ARG, "qlinear_gemv_host: invalid weight description");
+    if (d->layout != QP_LAYOUT_CANONICAL)
+        return qp::fail(QP_ERR_UNSUPPORTED, "qlinear_gemv_host reads the canonical layout");
+    if (d->zero_mode == QP_ZERO_PACKED)
+        return qp::fail(QP_ERR_UNSUPPORTED, "qlinear_gemv_host reads byte or implied zero points");
+    if (m < 1 || m > 8) return qp::fail(QP_ERR_UNSUPPORTED, "qlinear_gemv_host handles 1 <= m <= 8 (m=%lld)", (long long)m);
+    if (ldx < d->k || ldy < d->n) return qp::fail(QP_ERR_INVALID_ARG, "qlinear_gemv_host: ldx < k or ldy < n");
+    if (!w->packed || !w->scales || (d->zero_mode == QP_ZERO_STORED && !w->zeros))
+        return qp::fail(QP_ERR_INVALID_ARG, "qlinear_gemv_host: packed/scales/zeros NULL");
+    if (w->nnz < 0 || (w->nnz > 0 && (!w->csr_rowptr || !w->csr_col || !w->csr_val)))
+        return qp::fail(QP_ERR_INVALID_ARG, "qlinear_gemv_host: bad outlier CSR");
+    if (threads < 0) return qp::fail(QP_ERR_INVALID_ARG, "qlinear_gemv_host: threads < 0");
+    HostArgs a;
+    a.w = (const uint8_t *)w->packed;
+    a.scales = w->scales;
+    a.zeros = d->zero_mode == QP_ZERO_STORED ? w->zeros : nullptr;
+    a.zmid = 1u << (d->bits - 1);
+    a.rowptr = w->nnz > 0 ? w->csr_rowptr : nullptr;
+    a.col = w->csr_col;
+    a.val = w->csr_val;
+    a.x = x;
+    a.ldx = ldx;
+    a.m = m;
+    a.n = d->n;
+    a.k = d->k;
+    a.gs = d->group_size;
+    a.G = d->k / d->group_size;
+    a.y = y;
+    a.ldy = ldy;
+    a.bits = d->bits;
+    a.total_bytes = (int64_t)qp_packed_bytes(d);
+    const int nt = threads > 0 ? threads : default_threads();
+    const bool avx = use_avx2();
+    // Rows in chunks of 16 (a multiple of every row tile), spread over the threads.
+    const int64_t chunks = (a.n + 15) / 16;
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t c = 0; c < chunks; ++c) {
+        const int64_t r0 = 16 * c, r1 = r0 + 16 < a.n ? r0 + 16 : a.n;
+        if (avx)
+            rows_avx2(a, r0, r1);
+        else
+            rows_scalar(a, r0, r1);
+    }
+    return QP_OK;
+}
