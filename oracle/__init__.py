@@ -77,6 +77,14 @@ def lib():
         L.or_linear.argtypes = [i64, i64, i64, i32, vp, i64, vp, vp, vp, vp, vp, vp, vp, i64]
         L.or_moe_ffn.restype = None
         L.or_moe_ffn.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp] + [vp] * 9 + [vp]
+        L.or_act_quantize.restype = None
+        L.or_act_quantize.argtypes = [i64, i64, vp, i64, vp, vp]
+        L.or_act_pos.restype = i64
+        L.or_act_pos.argtypes = [i64]
+        L.or_act_layout.restype = None
+        L.or_act_layout.argtypes = [i64, i64, vp, vp, i32]
+        L.or_linear_a8.restype = None
+        L.or_linear_a8.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp]
         L.or_zero_row_bytes.restype = i64
         L.or_zero_row_bytes.argtypes = [i64, i32]
         for name in ("or_pack_zeros", "or_unpack_zeros"):
@@ -282,6 +290,42 @@ def moe_ffn(x_fp16, ids, wts, gate: list, up: list, down: list):
             st(down, "codes", np.uint8), st(down, "scales", np.uint16), st(down, "zeros", np.uint8)]
     r = np.zeros((T, D), np.float64)
     lib().or_moe_ffn(T, D, F, topk, g, _p(ids), _p(wts), _p(x), *[_p(a) for a in arrs], _p(r))
+    return r
+
+
+def act_quantize(x_fp16):
+    """Per-token int8 activations: x [M, K] fp16 -> (xq int8 [M, K] row-major, scales fp32 [M])."""
+    x = _bits16(x_fp16)
+    M, K = x.shape
+    xq = np.zeros((M, K), np.int8)
+    sc = np.zeros(M, np.float32)
+    lib().or_act_quantize(M, K, _p(x), K, _p(xq), _p(sc))
+    return xq, sc
+
+
+def act_pos(k: int) -> int:
+    return lib().or_act_pos(k)
+
+
+def act_layout(xq, inverse: bool = False):
+    """Row-major int8 activations <-> the library's storage order (within 128-k groups)."""
+    a = np.ascontiguousarray(xq, dtype=np.int8)
+    M, K = a.shape
+    out = np.zeros_like(a)
+    lib().or_act_layout(M, K, _p(a), _p(out), 1 if inverse else 0)
+    return out
+
+
+def linear_a8(xq, sx, q: dict):
+    """fp64 r = s_x * sum_g s_w * (integer group dot products of xq with q - zp)."""
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    M, K = xq.shape
+    codes = _c(q["codes"], np.uint8)
+    N = codes.shape[0]
+    g = _group_of(q, K)
+    r = np.zeros((M, N), np.float64)
+    lib().or_linear_a8(M, N, K, g, _p(xq), _p(_c(sx, np.float32)), _p(codes), _p(_c(q["scales"], np.uint16)),
+                       _p(_c(q["zeros"], np.uint8)), _p(r))
     return r
 
 

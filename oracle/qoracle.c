@@ -23,6 +23,9 @@
  *        consuming the quantized cache directly.
  *  [MoE] on-device MoE memory wall (bjdmk.com.cn/5648983): s1.1 weight/KV byte
  *        formulas; s4.2 routed expert tasks (hidden states + top-k expert ids).
+ *  [IA]  also s1.2: W8A8 (weights and activations in INT8 on the integer matrix units, with
+ *        dynamic per-token activation quantization); [MB] s4.2: unpack to 8-bit integers,
+ *        integer dot-product accumulate, scale in floating point.
  *
  * Readings where the pages are silent (each listed in the design notes):
  *  - codes are unsigned 0..2^b-1, round() is round-half-to-even, q and zp clamp to
@@ -734,6 +737,81 @@ void or_attn_decode(int64_t B, int64_t Hq, int64_t Hkv, int64_t cap, int kbits, 
                 }
             }
             free(z);
+        }
+}
+
+/* ------------------------------------------------------------------------------ */
+/* Integer-dot path: int8 activations x b-bit weights  ([IA] s1.2; [MB] s4.2)       */
+/* ------------------------------------------------------------------------------ */
+
+/* Dynamic per-token activation quantization ([IA] s1.2: W8A8 quantizes activations to INT8
+ * dynamically, per token).  Reading, as the symmetric INT8 form of [IA] s1.1 ([-127, 127]):
+ * for row m, a = max_k |x[m][k]| in fp32, s = a / 127 in IEEE fp32, xq = clamp(rint(x / s),
+ * -127, 127) (fp32 division, ties to even); an all-zero row stores s = 0 and xq = 0.
+ * xq is row-major [M][K] here (the library's own k order inside each group is a storage
+ * map, or_act_layout). */
+void or_act_quantize(int64_t M, int64_t K, const uint16_t *x, int64_t ldx, int8_t *xq, float *scales)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t *row = x + m * ldx;
+        float a = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            const float v = fabsf((float)hv(row[k]));
+            if (v > a) a = v;
+        }
+        volatile float s = a / 127.0f;
+        scales[m] = a == 0.0f ? 0.0f : s;
+        for (int64_t k = 0; k < K; ++k) {
+            int q = 0;
+            if (a != 0.0f) {
+                volatile float t = (float)hv(row[k]) / s;
+                q = clampi((int)rintf(t), -127, 127);
+            }
+            xq[m * K + k] = (int8_t)q;
+        }
+    }
+}
+
+/* Position of k inside its 128-k group in the library's int8 activation rows: 16-byte pieces
+ * (64-k step s, lane quarter t) holding k = 64s + 8t + [0, 8) then 64s + 32 + 8t + [0, 8), so
+ * one 16-byte read gives a lane the 16 k values it multiplies on the integer matrix core. */
+int64_t or_act_pos(int64_t k)
+{
+    const int64_t g = k / 128, kk = k % 128, st = kk / 64, rem = kk % 64;
+    const int64_t p = rem / 32, t = (rem % 32) / 8, e = rem % 8;
+    return g * 128 + 16 * (4 * st + t) + 8 * p + e;
+}
+
+/* Row-major xq [M][K] -> the library's storage order (inverse = 1: back). */
+void or_act_layout(int64_t M, int64_t K, const int8_t *in, int8_t *out, int inverse)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            if (inverse) out[m * K + k] = in[m * K + or_act_pos(k)];
+            else out[m * K + or_act_pos(k)] = in[m * K + k];
+        }
+}
+
+/* r[m][n] = s_x[m] * sum_g s_w[n][g] * sum_{k in g} xq[m][k] * (q[n][k] - zp[n][g]) ([MB] s4.2:
+ * integer dot products per group, the scale multiply in floating point), in fp64; every
+ * group's integer sum is exact. */
+void or_linear_a8(int64_t M, int64_t N, int64_t K, int g, const int8_t *xq, const float *sx,
+                  const uint8_t *codes, const uint16_t *scales, const uint8_t *zeros, double *r)
+{
+    const int64_t G = K / g;
+    (void)hv(0);
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t gi = 0; gi < G; ++gi) {
+                int64_t isum = 0;
+                const int zp = zeros[n * G + gi];
+                for (int64_t k = gi * g; k < (gi + 1) * g; ++k)
+                    isum += (int64_t)xq[m * K + k] * ((int64_t)codes[n * K + k] - zp);
+                acc += hv(scales[n * G + gi]) * (double)isum;
+            }
+            r[m * N + n] = (double)sx[m] * acc;
         }
 }
 
