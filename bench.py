@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 METRIC = "packed-weight GB/s (% HBM peak) at M=1 GEMV; TFLOP/s (% MFMA peak) at M=512"
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
+MFMA_I8_PEAK_TOPS = 5000.0
 
 
 def log(msg):
@@ -441,6 +442,45 @@ def bench_prefill(q, torch, workloads, stream):
     return roof
 
 
+def bench_prefill_a8(q, torch, workloads, stream):
+    """Integer-dot prefill (the W8A8 path): the prefill shape M=512, K=8192, N=28672 at 4 bits,
+    g=128, on int8 activations (no outlier add-back: the held-out weights stay in their groups
+    here).  Timed as the GEMM alone (qlinear_gemm_a8 on int8 activations already resident) and
+    end to end (qact_quantize of the fp16 activations, then the GEMM); ops = 2 M N K against
+    the dense int8 matrix-core peak."""
+    dev = torch.device("cuda")
+    wp, _ = workloads.prefill_weights()
+    dp, wt = quantize_pack(q, torch, wp, 4)
+    del wp
+    Mp, Kp, Np = workloads.PREFILL_M, workloads.PREFILL_K, workloads.PREFILL_N
+    h = q.weight(wt["packed"], wt["scales"], wt["zeros"])
+    xp = torch.from_numpy(workloads.prefill_activations().view(np.int16)).to(dev)
+    xq = torch.empty((Mp, Kp), dtype=torch.int8, device=dev)
+    sx = torch.empty(Mp, dtype=torch.float32, device=dev)
+    yp = torch.empty((Mp, Np), dtype=torch.int16, device=dev)
+    q.qact_quantize(xp, Kp, Mp, Kp, xq, sx)
+    ms_gemm = time_graph(torch, lambda i: q.qlinear_gemm_a8(dp, h, xq, sx, Mp, yp, Np), 10, stream)
+
+    def e2e(i):
+        q.qact_quantize(xp, Kp, Mp, Kp, xq, sx)
+        q.qlinear_gemm_a8(dp, h, xq, sx, Mp, yp, Np)
+
+    ms_e2e = time_graph(torch, e2e, 10, stream)
+    ms_act = time_graph(torch, lambda i: q.qact_quantize(xp, Kp, Mp, Kp, xq, sx), 50, stream)
+    ops = 2 * Mp * Np * Kp
+    tops = ops / (ms_gemm * 1e-3) / 1e12
+    tops_e2e = ops / (ms_e2e * 1e-3) / 1e12
+    del h, wt, xp, xq, sx, yp
+    return dict(bound="mfma", achieved=round(tops, 1), peak=MFMA_I8_PEAK_TOPS, unit="TOP/s",
+                frac=round(tops / MFMA_I8_PEAK_TOPS, 4), traffic=None,
+                kernel="qp::gemm_a8_kernel<4> (M=512 K=8192 N=28672, 4-bit g=128, int8 activations)",
+                ops_per_launch=ops, avg_launch_us=round(ms_gemm * 1e3, 2),
+                end_to_end=dict(achieved=round(tops_e2e, 1), frac=round(tops_e2e / MFMA_I8_PEAK_TOPS, 4),
+                                avg_us=round(ms_e2e * 1e3, 2), kernels="qact_quantize + qlinear_gemm_a8"),
+                act_quantize_us=round(ms_act * 1e3, 2),
+                act_quantize_GBps=round((Mp * Kp * 3 + Mp * 4) / (ms_act * 1e-3) / 1e9, 1))
+
+
 def host_read_gbps(nbytes: int = 1 << 30, threads: int = 0) -> float:
     """Host memory read bandwidth: numpy sums over slices of a 1 GiB array in parallel threads
     (the reductions release the GIL), the reference for the host GEMV's GB/s."""
@@ -623,6 +663,8 @@ def main():
     if not args.no_prefill:
         log("bench: prefill GEMM M=512 K=8192 N=28672 4-bit + 0.1% outliers")
         extra["roofline_prefill"] = bench_prefill(q, torch, workloads, stream)
+        log("bench: integer-dot prefill (int8 activations) M=512 K=8192 N=28672 4-bit")
+        extra["roofline_prefill_a8"] = bench_prefill_a8(q, torch, workloads, stream)
 
     if not args.no_sweep:
         log("bench: 4096x4096 sweep, bits 2/3/5/6 x M 1/4/8")

@@ -239,6 +239,41 @@ qp_status qlinear_gemm(const qp_weight_desc *desc, const qp_weight *w, const uin
                        size_t ws_bytes, void *stream);
 
 /*
+ * Dynamic per-token int8 activations for the integer-dot path (W8A8 on the integer matrix
+ * units with per-token activation quantization: "大模型推理加速实战：量化、投机采样与PD分离的工程
+ * 指南", s1.2 and s3.5).  Row m of x: a = max_k |x[m][k]|, s = a / 127, and
+ * xq[m][k] = clamp(rint(x[m][k] / s), -127, 127), every step one IEEE fp32 operation (correctly
+ * rounded division, round half to even); an all-zero row gets s = 0 and xq = 0.
+ *  x        fp16 [m][ldx] device, ldx >= k, ldx % 8 == 0, 16-byte aligned; finite.
+ *  k        multiple of 128.
+ *  xq       int8 [m][k] device (row stride k), 8-byte aligned, in the int8 storage map: inside
+ *           each 128-k group of a row, 16-byte piece 4s + t (s = 0, 1; t = 0..3) holds
+ *           k = 64s + 8t .. 64s + 8t + 7 followed by k = 64s + 32 + 8t .. 64s + 32 + 8t + 7
+ *           (one piece is the 16 k one lane feeds to one int8 matrix-core step).
+ *  x_scales float [m] device: s per row.
+ * m >= 1.
+ */
+qp_status qact_quantize(const uint16_t *x, int64_t ldx, int64_t m, int64_t k, int8_t *xq,
+                        float *x_scales, void *stream);
+
+/*
+ * Integer-dot dequant-GEMM on int8 activations (the W8A8 path above; mixed-bit page s4.2:
+ * codes unpacked to 8-bit integers, integer dot products, the scale applied in fp32):
+ *     y[m][n] = fp16( x_scales[m] * sum_g s[n][g] * sum_{k in g} xq[m][k] * (q[n][k] - zp[n][g]) )
+ * with each group's integer sum exact (int32) and the sum over groups in fp32.
+ *  desc     QP_LAYOUT_DEVICE, group_size 128, QP_ZERO_STORED or QP_ZERO_MIDPOINT.
+ *  w        no outliers (w->nnz must be 0: the held-out weights are defined against the fp16
+ *           activations; use qlinear_gemm for them).
+ *  xq, x_scales  from qact_quantize (xq 16-byte aligned, m * k < 2^31).
+ *  y        fp16 [m][ldy] device, ldy >= n, ldy % 4 == 0, 8-byte aligned.
+ * m >= 1 (as every matmul here).  Returns QP_ERR_UNSUPPORTED for other group sizes, packed
+ * zero points and outliers.
+ */
+qp_status qlinear_gemm_a8(const qp_weight_desc *desc, const qp_weight *w, const int8_t *xq,
+                          const float *x_scales, int64_t m, uint16_t *y, int64_t ldy,
+                          void *stream);
+
+/*
  * Grouped dequant-GEMM over routed experts (MoE page s4.2).  All experts share `desc`
  * (layout QP_LAYOUT_DEVICE).  `experts` is a HOST array of n_experts (<= 64) weights.
  *  row_src         int32 [rows] device: token (row of x) feeding sorted row r.

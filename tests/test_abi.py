@@ -317,3 +317,28 @@ def test_attention_noalloc_rejects_scratch_beyond_its_limit():
     assert st == q.QP_ERR_WORKSPACE and "2097152" in q.last_error()
     # within the limit: the benchmarked 4 x 8K GQA layer (2048 partials)
     assert 0 < q.qattn_decode_workspace_bytes(q.kv_desc(4, 64, 8, 8192)) <= q.QATTN_NOALLOC_SCRATCH_BYTES
+
+
+def test_int8_path_validation():
+    """qact_quantize / qlinear_gemm_a8 reject what the kernels do not handle, before any launch."""
+    assert q.qact_quantize(FAKE, 256, 4, 200, FAKE, FAKE, stream=0, check=False) == q.QP_ERR_INVALID_ARG  # k % 128
+    assert q.qact_quantize(FAKE, 100, 4, 128, FAKE, FAKE, stream=0, check=False) == q.QP_ERR_INVALID_ARG  # ldx < k
+    assert q.qact_quantize(FAKE + 8, 128, 4, 128, FAKE, FAKE, stream=0, check=False) == q.QP_ERR_INVALID_ARG
+    assert q.qact_quantize(FAKE, 128, 0, 128, FAKE, FAKE, stream=0, check=False) == q.QP_ERR_INVALID_ARG
+    assert q.qact_quantize(FAKE, 128, 4, 128, FAKE + 4, FAKE, stream=0, check=False) == q.QP_ERR_INVALID_ARG
+    d = q.desc(4, 256, 512)
+    w = q.weight(FAKE, FAKE, FAKE)
+    ok = dict(stream=0, check=False)
+    assert q.qlinear_gemm_a8(d, w, FAKE, FAKE, 0, FAKE, 256, **ok) == q.QP_ERR_INVALID_ARG
+    assert q.qlinear_gemm_a8(d, w, FAKE + 8, FAKE, 4, FAKE, 256, **ok) == q.QP_ERR_INVALID_ARG
+    assert q.qlinear_gemm_a8(d, w, FAKE, FAKE, 4, FAKE, 100, **ok) == q.QP_ERR_INVALID_ARG
+    assert q.qlinear_gemm_a8(d, w, FAKE, FAKE, (1 << 31) // 512, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
+    csr = q.weight(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 5)
+    assert q.qlinear_gemm_a8(d, csr, FAKE, FAKE, 4, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
+    assert "outlier" in q.last_error()
+    d64 = q.desc(4, 256, 512, group_size=64)
+    assert q.qlinear_gemm_a8(d64, w, FAKE, FAKE, 4, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
+    dpk = q.desc(4, 256, 512, zero_mode=q.QP_ZERO_PACKED)
+    assert q.qlinear_gemm_a8(dpk, w, FAKE, FAKE, 4, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
+    canon = q.desc(4, 256, 512, layout=q.QP_LAYOUT_CANONICAL)
+    assert q.qlinear_gemm_a8(canon, w, FAKE, FAKE, 4, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED

@@ -76,6 +76,8 @@ _SIGS = {
     "qlinear_gemv_batch": (_i32, [ctypes.POINTER(qp_gemv_problem), _i32, _vp]),
     "qlinear_gemm_workspace_bytes": (_sz, [_D, _i64, _i64]),
     "qlinear_gemm": (_i32, [_D, _W, _vp, _i64, _i64, _vp, _i64, _vp, _sz, _vp]),
+    "qact_quantize": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "qlinear_gemm_a8": (_i32, [_D, _W, _vp, _vp, _i64, _vp, _i64, _vp]),
     "qlinear_grouped_gemm": (_i32, [_D, _W, _i32, _vp, _i64, _vp, _vp, _i64, _i32, _vp, _i64, _vp]),
     "qmoe_dispatch": (_i32, [_vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "qmoe_combine": (_i32, [_vp, _i64, _vp, _vp, _i64, _i32, _i64, _vp, _i64, _vp]),
@@ -222,6 +224,16 @@ def qlinear_gemm_workspace_bytes(d, m: int, nnz: int) -> int:
 def qlinear_gemm(d, w, x, ldx, m, y, ldy, workspace=None, ws_bytes=0, stream=None, check=True):
     return _check("qlinear_gemm", lib.qlinear_gemm(ctypes.byref(d), ctypes.byref(w), _ptr(x), ldx, m, _ptr(y),
                                                     ldy, _ptr(workspace), ws_bytes, _stream(stream)), check)
+
+
+def qact_quantize(x, ldx, m, k, xq, x_scales, stream=None, check=True):
+    return _check("qact_quantize", lib.qact_quantize(_ptr(x), ldx, m, k, _ptr(xq), _ptr(x_scales), _stream(stream)),
+                  check)
+
+
+def qlinear_gemm_a8(d, w, xq, x_scales, m, y, ldy, stream=None, check=True):
+    return _check("qlinear_gemm_a8", lib.qlinear_gemm_a8(ctypes.byref(d), ctypes.byref(w), _ptr(xq), _ptr(x_scales),
+                                                          m, _ptr(y), ldy, _stream(stream)), check)
 
 
 def qlinear_grouped_gemm(d, experts, x, ldx, row_src, expert_offsets, rows, epilogue, y, ldy, stream=None,

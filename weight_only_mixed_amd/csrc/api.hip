@@ -644,4 +644,38 @@ qp_status qattn_decode_noalloc(const qkv_desc *d, const uint16_t *q, const void 
     return qattn_decode(d, q, k_codes, k_scales, v_codes, v_scales, seq_lens, sm_scale, o, ws, need, stream);
 }
 
+qp_status qact_quantize(const uint16_t *x, int64_t ldx, int64_t m, int64_t k, int8_t *xq, float *x_scales,
+                        void *stream)
+{
+    if (!x || !aligned(x, 16)) return fail(QP_ERR_INVALID_ARG, "x NULL or not 16-byte aligned");
+    if (!xq || !aligned(xq, 8)) return fail(QP_ERR_INVALID_ARG, "xq NULL or not 8-byte aligned");
+    if (!x_scales || !aligned(x_scales, 4)) return fail(QP_ERR_INVALID_ARG, "x_scales NULL or misaligned");
+    if (k <= 0 || k % kGroup != 0) return fail(QP_ERR_INVALID_ARG, "k=%lld must be a positive multiple of 128", (long long)k);
+    if (ldx < k || ldx % 8 != 0) return fail(QP_ERR_INVALID_ARG, "ldx=%lld must be >= k and a multiple of 8", (long long)ldx);
+    if (m < 1 || m > 0x7FFFFFFFLL) return fail(QP_ERR_INVALID_ARG, "m=%lld not in 1..2^31-1", (long long)m);
+    if (prod_over(m, ldx, 2, 1LL << 62) || prod_over(m, k, 1, 1LL << 62)) return fail(QP_ERR_INVALID_ARG, "x or xq too large");
+    return device(launch_act_quantize(x, ldx, m, k, xq, x_scales, S(stream)), "qact_quantize");
+}
+
+qp_status qlinear_gemm_a8(const qp_weight_desc *d, const qp_weight *w, const int8_t *xq, const float *x_scales,
+                          int64_t m, uint16_t *y, int64_t ldy, void *stream)
+{
+    qp_status st = check_desc(d, true);
+    if (st != QP_OK) return st;
+    if (d->group_size != kGroup) return fail(QP_ERR_UNSUPPORTED, "the int8 GEMM is built for groups of 128");
+    if (d->zero_mode == QP_ZERO_PACKED) return fail(QP_ERR_UNSUPPORTED, "the int8 GEMM reads byte zero points");
+    if ((st = check_weight(d, w, false)) != QP_OK) return st;
+    if (w->nnz > 0) return fail(QP_ERR_UNSUPPORTED, "outliers are not applied on int8 activations");
+    if (!xq || !aligned(xq, 16)) return fail(QP_ERR_INVALID_ARG, "xq NULL or not 16-byte aligned");
+    if (!x_scales || !aligned(x_scales, 4)) return fail(QP_ERR_INVALID_ARG, "x_scales NULL or misaligned");
+    if (!y || !aligned(y, 8)) return fail(QP_ERR_INVALID_ARG, "y NULL or misaligned");
+    if (ldy < d->n || ldy % 4 != 0) return fail(QP_ERR_INVALID_ARG, "ldy=%lld must be >= %lld and a multiple of 4", (long long)ldy, (long long)d->n);
+    if (m < 1) return fail(QP_ERR_INVALID_ARG, "m=%lld must be >= 1", (long long)m);
+    if (prod_over(m, d->k, 1, 0x7FFFFFFFLL)) return fail(QP_ERR_UNSUPPORTED, "xq larger than 2 GiB");
+    if ((int64_t)qp_packed_bytes(d) > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "packed weight larger than 2 GiB");
+    const ExpertPtrs ep{(const uint8_t *)w->packed, w->scales, w->zeros};
+    return device(launch_gemm_a8(d->bits, ep, xq, x_scales, m, d->n, d->k, zero_pair(d), y, ldy, S(stream)),
+                  "qlinear_gemm_a8");
+}
+
 }  // extern "C"
