@@ -56,9 +56,10 @@ def test_act_quantize_bit_exact(m, k):
 
 
 @pytest.mark.parametrize("bits", BITS)
-@pytest.mark.parametrize("m", (1, 17, 130))
+@pytest.mark.parametrize("m", (1, 17, 130, 300))
 def test_gemm_a8_ragged(bits, m):
-    """Every bit width; a partial last weight tile (n = 560) and a partial activation block."""
+    """Every bit width; a partial last weight tile (n = 560); one partial 256-row activation
+    block, or a full one and a partial one (m = 300)."""
     n, k = 560, 1536
     w = workloads.weights_fp16(n, k, 950 + bits)
     x = workloads.activations_fp16(m, k, 950 + bits)

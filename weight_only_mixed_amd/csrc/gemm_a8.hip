@@ -8,9 +8,13 @@
 //     acc[m][n] += s_w[n][g] * isum                                   (fp32)
 // and y[m][n] = fp16(acc * s_x[m]) once at the end.
 //
-// The workgroup is the fp16 GEMM's: eight waves of two 16-row weight blocks (256 rows) times
-// 128 activation rows, the same two-slot LDS rings filled by buffer-to-LDS DMA, the same
-// weight staging, scale and zero-point loads and waits.  What changes is the operand:
+// The workgroup has the fp16 GEMM's structure: eight waves of two 16-row weight blocks (256
+// rows), the same two-slot LDS rings filled by buffer-to-LDS DMA, the same weight staging, scale
+// and zero-point loads and waits.  It covers 256 activation rows instead of 128: every output
+// costs two vector ops per group here (conversion and fma) against one matrix-core op per 64 k,
+// so the vector ALU sets the pace, and sixteen 16-row tiles per wave halve the unpack work per
+// output (measured 17-25% faster than eight tiles at 2-6 bits; 241-250 VGPRs, no spills).
+// What changes is the operand:
 //  - Weights become the A operand of v_mfma_i32_16x16x64_i8 as bytes (q - zp).  A lane's
 //    chunk holds, per 128-k group, four 8-k blocks (k = 32s + 8t + [0, 8) for lane quarter t);
 //    blocks 2p and 2p+1 form its 16 bytes for matrix-core step p (p = 0, 1).  The codes are
@@ -39,7 +43,7 @@ using namespace mm;
 
 typedef int32_t i4v __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 8, kMT = 8;
+constexpr int kWaves = 8, kMT = 16;
 constexpr int kNT = kWaves * kRBW * kTileN;     // weight rows per workgroup
 constexpr int kMRows = kMT * 16;                // activation rows per workgroup
 constexpr int kXRow = 128;                      // bytes of one activation row per group
@@ -159,17 +163,49 @@ __device__ __forceinline__ void unpack_pair8_2(const uint32_t *d, uint32_t zb, i
     Wn[S / 2][3] = (int32_t)o1[1];
 }
 
-// The unpack share of activation tile MT: block MT % 4 of row block MT / 4 (2 bits: both blocks
-// of a word on even tiles).
-template <int B, int NH, int MT>
-__device__ __forceinline__ void unpack_share(const uint32_t *d, const uint32_t (&zb)[kRBW], i4v (&Wn)[kRBW][2])
+// Unpack schedule over the activation tiles of a step: both row blocks' chunks are read at tile 0
+// and unpacked from tile 1 on, when the reads have landed behind tile 0's matrix-core work.  The
+// units (eight blocks, block / 4 = row block; 2 bits: four words of two blocks each) are spread
+// evenly: unit j on tile 1 + j (kMT - 1) / units.
+template <int B>
+constexpr int kUnits = B == 2 ? 4 : 8;
+template <int B>
+constexpr int unit_tile(int j) { return 1 + j * (kMT - 1) / kUnits<B>; }
+
+template <int B, int NH, int J>
+__device__ __forceinline__ void unpack_unit(const uint32_t (&d)[kRBW][2 * B], const uint32_t (&zb)[kRBW],
+                                            i4v (&Wn)[kRBW][2])
 {
-    constexpr int u = MT / 4, s = MT % 4;
-    if constexpr (B == 2) {
-        if constexpr (s % 2 == 0) unpack_pair8_2<NH, s>(d, zb[u], Wn[u]);
-    } else {
-        unpack_block8<B, NH, s>(d, zb[u], Wn[u]);
-    }
+    constexpr int blk = B == 2 ? 2 * J : J, u = blk / 4, s = blk % 4;
+    if constexpr (B == 2)
+        unpack_pair8_2<NH, s>(d[u], zb[u], Wn[u]);
+    else
+        unpack_block8<B, NH, s>(d[u], zb[u], Wn[u]);
+}
+template <int B, int NH, int MT, int J>
+__device__ __forceinline__ void unpack_if(const uint32_t (&d)[kRBW][2 * B], const uint32_t (&zb)[kRBW],
+                                          i4v (&Wn)[kRBW][2])
+{
+    if constexpr (unit_tile<B>(J) == MT) unpack_unit<B, NH, J>(d, zb, Wn);
+}
+template <int B, int NH, int MT, int... J>
+__device__ __forceinline__ void unpack_units(std::integer_sequence<int, J...>, const uint32_t (&d)[kRBW][2 * B],
+                                             const uint32_t (&zb)[kRBW], i4v (&Wn)[kRBW][2])
+{
+    (unpack_if<B, NH, MT, J>(d, zb, Wn), ...);
+}
+template <int B, int NH, int MT>
+__device__ __forceinline__ void unpack_share(const uint32_t (&d)[kRBW][2 * B], const uint32_t (&zb)[kRBW],
+                                             i4v (&Wn)[kRBW][2])
+{
+    unpack_units<B, NH, MT>(std::make_integer_sequence<int, kUnits<B>>{}, d, zb, Wn);
+}
+
+template <int B, int NH, int... J>
+__device__ __forceinline__ void unpack_all(std::integer_sequence<int, J...>, const uint32_t (&d)[kRBW][2 * B],
+                                           const uint32_t (&zb)[kRBW], i4v (&Wn)[kRBW][2])
+{
+    (unpack_unit<B, NH, J>(d, zb, Wn), ...);
 }
 
 // Whole group (before the loop): both row blocks from a staged weight slot part.
@@ -179,17 +215,10 @@ __device__ __forceinline__ void unpack_group8(const uint8_t *wpart, const SZ &z,
     uint32_t zb[kRBW];
 #pragma unroll
     for (int u = 0; u < kRBW; ++u) zb[u] = zbias((z.zz[u] >> (8 * NH)) & 0xFF);
-    uint32_t d[2 * B];
-    read_chunk<B>(wpart, lane, d);
-    unpack_share<B, NH, 0>(d, zb, W);
-    unpack_share<B, NH, 1>(d, zb, W);
-    unpack_share<B, NH, 2>(d, zb, W);
-    unpack_share<B, NH, 3>(d, zb, W);
-    read_chunk<B>(wpart + WStage<B>::kBytes, lane, d);
-    unpack_share<B, NH, 4>(d, zb, W);
-    unpack_share<B, NH, 5>(d, zb, W);
-    unpack_share<B, NH, 6>(d, zb, W);
-    unpack_share<B, NH, 7>(d, zb, W);
+    uint32_t d[kRBW][2 * B];
+    read_chunk<B>(wpart, lane, d[0]);
+    read_chunk<B>(wpart + WStage<B>::kBytes, lane, d[1]);
+    unpack_all<B, NH>(std::make_integer_sequence<int, kUnits<B>>{}, d, zb, W);
 }
 
 // ---- k loop --------------------------------------------------------------------------------
@@ -227,33 +256,37 @@ __device__ __forceinline__ void issue_tile8(const Bufs &bf, const StepIO<PAR> &i
     }
 }
 
-constexpr int kXA = 2, kXR = kXA + 1;  // fragment reads run two tiles ahead (ring of three)
+constexpr int kXA = 1, kXR = kXA + 1;  // fragment reads run one tile ahead (ring of two)
+constexpr int kLag = 1, kAR = kLag + 1;  // integer sums are scaled one tile later (ring of two)
 
 // Activation tile MT of a step: its fragment reads for tile MT + 2, the matrix-core chains of
-// tile MT (two K = 64 steps per row block, from zero), the scaling of tile MT - 1's integer
-// sums and a share of the next group's unpack.
+// tile MT (two K = 64 steps per row block, from zero), the scaling of tile MT - 2's integer
+// sums (their matrix-core ops finished a tile ago) and a share of the next group's unpack.
 template <int B, int SH, int NH, int MT>
 __device__ __forceinline__ void tile8(const i4v (&Wc)[kRBW][2], i4v (&Wn)[kRBW][2], const uint32_t (&sc)[kRBW][4],
                                       const uint32_t (&zb)[kRBW], const uint8_t *xs, const uint8_t *wpart, int lane,
-                                      uint32_t (&d)[2 * B], i4v (&X)[kXR][2], i4v (&acc)[2][kRBW],
+                                      uint32_t (&d)[kRBW][2 * B], i4v (&X)[kXR][2], i4v (&acc)[kAR][kRBW],
                                       f4 (&tot)[kRBW][kMT], const Bufs &bf, const StepIO<NH ^ 1> &io, int64_t G, int wv)
 {
-    constexpr int cur = MT & 1, prv = cur ^ 1;
+    constexpr int cur = MT % kAR;
     const int t = lane >> 4, r = lane & 15;
     issue_tile8<B, NH ^ 1, MT>(bf, io, G, wv, lane);
     if constexpr (MT + kXA < kMT) {
 #pragma unroll
         for (int p = 0; p < 2; ++p) X[(MT + kXA) % kXR][p] = *(const i4v *)(xs + xs_off8(16 * (MT + kXA) + r, 4 * p + t));
     }
-    if constexpr (MT == 0) read_chunk<B>(wpart, lane, d);
-    if constexpr (MT == kMT / 2) read_chunk<B>(wpart + WStage<B>::kBytes, lane, d);
+    if constexpr (MT == 0) read_chunk<B>(wpart, lane, d[0]);
+    if constexpr (MT == 0) read_chunk<B>(wpart + WStage<B>::kBytes, lane, d[1]);
 #pragma unroll
     for (int u = 0; u < kRBW; ++u) acc[cur][u] = mfma8(Wc[u][0], X[MT % kXR][0], (i4v){0, 0, 0, 0});
 #pragma unroll
     for (int u = 0; u < kRBW; ++u) acc[cur][u] = mfma8(Wc[u][1], X[MT % kXR][1], acc[cur][u]);
-    if constexpr (MT > 0) scale8<SH>(sc, acc[prv], tot, MT - 1);
     unpack_share<B, NH, MT>(d, zb, Wn);
-    if constexpr (MT == kMT - 1) scale8<SH>(sc, acc[cur], tot, MT);
+    if constexpr (MT >= kLag) scale8<SH>(sc, acc[(MT - kLag) % kAR], tot, MT - kLag);
+    if constexpr (MT == kMT - 1) {
+#pragma unroll
+        for (int j = kMT - kLag; j < kMT; ++j) scale8<SH>(sc, acc[j % kAR], tot, j);
+    }
     // per matrix-core op: a fragment read and a few vector ops issued behind it
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -267,8 +300,8 @@ __device__ __forceinline__ void tile8(const i4v (&Wc)[kRBW][2], i4v (&Wn)[kRBW][
 template <int B, int SH, int NH, int... MT>
 __device__ __forceinline__ void tiles8(std::integer_sequence<int, MT...>, const i4v (&Wc)[kRBW][2], i4v (&Wn)[kRBW][2],
                                        const uint32_t (&sc)[kRBW][4], const uint32_t (&zb)[kRBW], const uint8_t *xs,
-                                       const uint8_t *wpart, int lane, uint32_t (&d)[2 * B], i4v (&X)[kXR][2],
-                                       i4v (&acc)[2][kRBW], f4 (&tot)[kRBW][kMT], const Bufs &bf,
+                                       const uint8_t *wpart, int lane, uint32_t (&d)[kRBW][2 * B], i4v (&X)[kXR][2],
+                                       i4v (&acc)[kAR][kRBW], f4 (&tot)[kRBW][kMT], const Bufs &bf,
                                        const StepIO<NH ^ 1> &io, int64_t G, int wv)
 {
     (tile8<B, SH, NH, MT>(Wc, Wn, sc, zb, xs, wpart, lane, d, X, acc, tot, bf, io, G, wv), ...);
@@ -291,8 +324,8 @@ __device__ __forceinline__ void step8(const i4v (&Wc)[kRBW][2], i4v (&Wn)[kRBW][
     uint32_t zb[kRBW];
 #pragma unroll
     for (int u = 0; u < kRBW; ++u) zb[u] = zbias((zn.zz[u] >> (8 * NH)) & 0xFF);
-    uint32_t d[2 * B];
-    i4v acc[2][kRBW];
+    uint32_t d[kRBW][2 * B];
+    i4v acc[kAR][kRBW];
     __builtin_amdgcn_sched_barrier(0);
     tiles8<B, SH, NH>(std::make_integer_sequence<int, kMT>{}, Wc, Wn, sc, zb, xs, wpart, lane, d, X, acc, tot, bf, io,
                       G, wv);
