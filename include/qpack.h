@@ -225,8 +225,9 @@ qp_status qlinear_gemv_batch(const qp_gemv_problem *problems, int32_t count, voi
 
 /*
  * Prefill dequant-GEMM for any m >= 1 (tuned for m >= 64): same operands and result as
- * qlinear_gemv.  Tiles of the packed weight are unpacked in registers and fed to fp16
- * matrix cores with fp32 accumulation; scales are applied per group in fp32.
+ * qlinear_gemv, for every group size (32, 64, 128) and zero mode.  Tiles of the packed
+ * weight are unpacked in registers and fed to fp16 matrix cores with fp32 accumulation;
+ * scales are applied per group in fp32.
  *  workspace/ws_bytes  device scratch of at least qlinear_gemm_workspace_bytes(desc, m,
  *           w->nnz) bytes, 16-byte aligned, only needed when w carries outliers (NULL/0
  *           otherwise).  It holds x transposed (k * ldt fp16) and the fp32 outlier partial
@@ -261,13 +262,13 @@ qp_status qact_quantize(const uint16_t *x, int64_t ldx, int64_t m, int64_t k, in
  * codes unpacked to 8-bit integers, integer dot products, the scale applied in fp32):
  *     y[m][n] = fp16( x_scales[m] * sum_g s[n][g] * sum_{k in g} xq[m][k] * (q[n][k] - zp[n][g]) )
  * with each group's integer sum exact (int32) and the sum over groups in fp32.
- *  desc     QP_LAYOUT_DEVICE, group_size 128, QP_ZERO_STORED or QP_ZERO_MIDPOINT.
+ *  desc     QP_LAYOUT_DEVICE, group_size 128, any zero mode (stored, implied midpoint, b-bit).
  *  w        no outliers (w->nnz must be 0: the held-out weights are defined against the fp16
  *           activations; use qlinear_gemm for them).
  *  xq, x_scales  from qact_quantize (xq 16-byte aligned, m * k < 2^31).
  *  y        fp16 [m][ldy] device, ldy >= n, ldy % 4 == 0, 8-byte aligned.
- * m >= 1 (as every matmul here).  Returns QP_ERR_UNSUPPORTED for other group sizes, packed
- * zero points and outliers.
+ * m >= 1 (as every matmul here).  Returns QP_ERR_UNSUPPORTED for groups of 32 or 64 and for
+ * outliers.
  */
 qp_status qlinear_gemm_a8(const qp_weight_desc *desc, const qp_weight *w, const int8_t *xq,
                           const float *x_scales, int64_t m, uint16_t *y, int64_t ldy,
@@ -275,7 +276,8 @@ qp_status qlinear_gemm_a8(const qp_weight_desc *desc, const qp_weight *w, const 
 
 /*
  * Grouped dequant-GEMM over routed experts (MoE page s4.2).  All experts share `desc`
- * (layout QP_LAYOUT_DEVICE).  `experts` is a HOST array of n_experts (<= 64) weights.
+ * (layout QP_LAYOUT_DEVICE; any group size and zero mode).  `experts` is a HOST array of
+ * n_experts (<= 64) weights.
  *  row_src         int32 [rows] device: token (row of x) feeding sorted row r.
  *  expert_offsets  int32 [n_experts+1] device, non-decreasing, from >= 0 to <= rows: rows
  *                  of expert e are [expert_offsets[e], expert_offsets[e+1]).
@@ -327,8 +329,9 @@ size_t qmoe_ffn_workspace_bytes(int64_t tokens, int32_t topk, int32_t n_experts,
 /*
  * Whole routed-expert FFN on one stream: dispatch, grouped gate/up GEMM with SwiGLU
  * (intermediate stored in fp16), grouped down GEMM (fp32 rows), weighted combine.
- *  gate_up[e]: desc_gu = {bits, 128, DEVICE, 0, 2*d_ff, d_model}, gate/up rows interleaved
- *              in blocks of 16 (see QP_EPI_SWIGLU);  down[e]: desc_d = {.., d_model, d_ff}.
+ *  gate_up[e]: desc_gu = {bits, g, DEVICE, zero mode, 2*d_ff, d_model}, gate/up rows
+ *              interleaved in blocks of 16 (see QP_EPI_SWIGLU);  down[e]: desc_d = {.., d_model,
+ *              d_ff}, with the same bit width (group size and zero mode may differ).
  *  x fp16 [tokens][ldx]; out fp16 [tokens][ldo]; HOST arrays gate_up/down.
  */
 qp_status qmoe_ffn(const qp_weight_desc *desc_gu, const qp_weight *gate_up,

@@ -47,13 +47,16 @@ class GpuWeight:
     """Quantized + packed weight on the device, built through the C ABI."""
 
     def __init__(self, w_fp16: np.ndarray, bits: int, outlier_frac: float = 0.0, layout: int = 1,
-                 sym: bool = False, g: int = 128):
+                 sym: bool = False, g: int = 128, packed_zeros: bool = False):
+        """packed_zeros: affine zero points kept in b bits (QP_ZERO_PACKED, packed on the GPU
+        from qpack_quantize's bytes by qpack_pack_zeros); the bytes stay in zeros_u8."""
         torch, q = gpu()
         n, k = w_fp16.shape
         dev = torch.device("cuda")
         self.n, self.k, self.bits, self.sym, self.g = n, k, bits, sym, g
         w = torch.from_numpy(np.ascontiguousarray(w_fp16).view(np.int16)).to(dev)
-        d = q.desc(bits, n, k, layout, group_size=g, zero_mode=q.QP_ZERO_MIDPOINT if sym else q.QP_ZERO_STORED)
+        mode = q.QP_ZERO_MIDPOINT if sym else (q.QP_ZERO_PACKED if packed_zeros else q.QP_ZERO_STORED)
+        d = q.desc(bits, n, k, layout, group_size=g, zero_mode=mode)
         self.desc = d
         G = k // g
         self.codes = torch.empty((n, k), dtype=torch.uint8, device=dev)
@@ -72,6 +75,10 @@ class GpuWeight:
         del w, ws
         self.packed = torch.empty(q.qp_packed_bytes(d), dtype=torch.uint8, device=dev)
         q.qpack_pack(d, self.codes, self.packed)
+        if packed_zeros:
+            self.zeros_u8 = self.zeros
+            self.zeros = torch.full((q.qp_zero_bytes(d),), 0xA5, dtype=torch.uint8, device=dev)
+            q.qpack_pack_zeros(d, self.zeros_u8, self.zeros)
 
     def handle(self, with_csr: bool = True):
         _, q = gpu()

@@ -159,17 +159,14 @@ def test_zero_mode_validation():
 
 def test_group_size_validation():
     """Groups of 32, 64 and 128 are valid descriptors (k a multiple of 128); other sizes are
-    not built; the GEMM and grouped GEMM take only 128; a GEMV batch takes one group size."""
+    not built; the int8-activation GEMM takes only 128; a GEMV batch takes one group size."""
     for g in (32, 64, 128):
         assert q.qp_num_groups(q.desc(2, 64, 1024, group_size=g)) == 64 * 1024 // g
     assert q.qp_num_groups(q.desc(2, 64, 1024, group_size=256)) == 0
     assert q.qp_num_groups(q.desc(2, 64, 1088, group_size=32)) == 0     # k not a multiple of 128
     d32 = q.desc(2, 256, 512, group_size=32)
     w = q.weight(FAKE, FAKE, FAKE)
-    assert q.qlinear_gemm(d32, w, FAKE, 512, 64, FAKE, 256, FAKE, 1 << 20, stream=0,
-                          check=False) == q.QP_ERR_UNSUPPORTED
-    assert q.qlinear_grouped_gemm(d32, [w], FAKE, 512, None, FAKE, 4, q.QP_EPI_NONE, FAKE, 256, stream=0,
-                                  check=False) == q.QP_ERR_UNSUPPORTED
+    assert q.qlinear_gemm_a8(d32, w, FAKE, FAKE, 64, FAKE, 256, stream=0, check=False) == q.QP_ERR_UNSUPPORTED
     p32 = q.gemv_problem(d32, w, FAKE, 512, 1, FAKE, 256)
     p128 = q.gemv_problem(q.desc(2, 256, 512), w, FAKE, 512, 1, FAKE, 256)
     assert q.qlinear_gemv_batch([p32, p128], stream=0, check=False) == q.QP_ERR_UNSUPPORTED
@@ -279,10 +276,9 @@ def test_kv_call_validation():
 
 
 def test_packed_zero_points():
-    """QP_ZERO_PACKED: zero points in b bits per group, rows padded to 32-bit words; the GEMV
-    takes them, the matrix-core GEMMs and the expert FFN do not, a GEMV batch does not mix
-    them with byte zero points; qpack_pack_zeros checks its mode and pointers (all before any
-    device work)."""
+    """QP_ZERO_PACKED: zero points in b bits per group, rows padded to 32-bit words; every
+    matmul checks their alignment, a GEMV batch does not mix them with byte zero points;
+    qpack_pack_zeros checks its mode and pointers (all before any device work)."""
     for bits in (2, 3, 4, 5, 6):
         for g in (32, 64, 128):
             for k in (1024, 1280, 11008 // 128 * 128):
@@ -294,11 +290,12 @@ def test_packed_zero_points():
     d = q.desc(2, 256, 1024, group_size=128, zero_mode=q.QP_ZERO_PACKED)
     w = q.weight(FAKE, FAKE, FAKE)
     U, E = q.QP_ERR_UNSUPPORTED, q.QP_ERR_INVALID_ARG
-    assert q.qlinear_gemm(d, w, FAKE, 1024, 64, FAKE, 256, stream=0, check=False) == U
-    assert q.qlinear_grouped_gemm(d, [w], FAKE, 1024, FAKE, FAKE, 64, q.QP_EPI_NONE, FAKE, 256, stream=0,
-                                  check=False) == U
-    assert q.qlinear_gemv(d, q.weight(FAKE, FAKE, FAKE + 2), FAKE, 1024, 1, FAKE, 256, stream=0,
-                          check=False) == E                       # packed zeros need 4-byte alignment
+    misaligned = q.weight(FAKE, FAKE, FAKE + 2)                  # packed zeros need 4-byte alignment
+    assert q.qlinear_gemv(d, misaligned, FAKE, 1024, 1, FAKE, 256, stream=0, check=False) == E
+    assert q.qlinear_gemm(d, misaligned, FAKE, 1024, 64, FAKE, 256, stream=0, check=False) == E
+    assert q.qlinear_grouped_gemm(d, [misaligned], FAKE, 1024, FAKE, FAKE, 64, q.QP_EPI_NONE, FAKE, 256, stream=0,
+                                  check=False) == E
+    assert q.qlinear_gemm_a8(d, misaligned, FAKE, FAKE, 64, FAKE, 256, stream=0, check=False) == E
     ds = q.desc(2, 256, 1024, group_size=128)
     probs = [q.gemv_problem(d, w, FAKE, 1024, 1, FAKE, 256), q.gemv_problem(ds, w, FAKE, 1024, 1, FAKE, 256)]
     assert q.qlinear_gemv_batch(probs, stream=0, check=False) == U
@@ -338,7 +335,5 @@ def test_int8_path_validation():
     assert "outlier" in q.last_error()
     d64 = q.desc(4, 256, 512, group_size=64)
     assert q.qlinear_gemm_a8(d64, w, FAKE, FAKE, 4, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
-    dpk = q.desc(4, 256, 512, zero_mode=q.QP_ZERO_PACKED)
-    assert q.qlinear_gemm_a8(dpk, w, FAKE, FAKE, 4, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
     canon = q.desc(4, 256, 512, layout=q.QP_LAYOUT_CANONICAL)
     assert q.qlinear_gemm_a8(canon, w, FAKE, FAKE, 4, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED

@@ -59,20 +59,20 @@ def test_dispatch_exact():
 class Experts:
     """Gate/up interleaved by 16-row blocks, and down, quantized and packed on the GPU."""
 
-    def __init__(self, E, D, F, bits, stream):
-        self.bits, self.D, self.F = bits, D, F
+    def __init__(self, E, D, F, bits, stream, g: int = 128, packed_zeros: bool = False):
+        self.bits, self.D, self.F, self.g = bits, D, F, g
         self.gate_up, self.down, self.raw = [], [], []
         for e in range(E):
-            g, u, d = workloads.moe_expert(e, D, F, stream)
-            self.raw.append((g, u, d))
-            self.gate_up.append(GpuWeight(workloads.interleave_row_blocks(g, u), bits))
-            self.down.append(GpuWeight(d, bits))
+            gt, u, d = workloads.moe_expert(e, D, F, stream)
+            self.raw.append((gt, u, d))
+            self.gate_up.append(GpuWeight(workloads.interleave_row_blocks(gt, u), bits, g=g, packed_zeros=packed_zeros))
+            self.down.append(GpuWeight(d, bits, g=g, packed_zeros=packed_zeros))
         self._oracle = {}
 
     def oracle_expert(self, e):
         """The oracle's own quantization of expert e: (gate, up, down) dicts."""
         if e not in self._oracle:
-            self._oracle[e] = tuple(oracle.quantize(m, self.bits) for m in self.raw[e])
+            self._oracle[e] = tuple(oracle.quantize(m, self.bits, g=self.g) for m in self.raw[e])
         return self._oracle[e]
 
     def oracle_sets(self, used):
@@ -81,8 +81,8 @@ class Experts:
             if e in used:
                 a, b, c = self.oracle_expert(e)
             else:  # never referenced by the tokens passed to the oracle
-                z = lambda n, k: dict(codes=np.zeros((n, k), np.uint8), scales=np.zeros((n, k // 128), np.uint16),
-                                      zeros=np.zeros((n, k // 128), np.uint8))
+                z = lambda n, k: dict(codes=np.zeros((n, k), np.uint8), scales=np.zeros((n, k // self.g), np.uint16),
+                                      zeros=np.zeros((n, k // self.g), np.uint8), g=self.g)
                 a, b, c = z(*g.shape), z(*u.shape), z(*d.shape)
             gs.append(a)
             us.append(b)
@@ -91,9 +91,10 @@ class Experts:
 
 
 def dequant(qd):
+    g = qd.get("g", 128)
     s = qd["scales"].view(np.float16).astype(np.float64)
     z = qd["zeros"].astype(np.float64)
-    return (qd["codes"] - np.repeat(z, 128, 1)) * np.repeat(s, 128, 1)
+    return (qd["codes"] - np.repeat(z, g, 1)) * np.repeat(s, g, 1)
 
 
 def near_tie(v, abs_err=0.0):
@@ -128,8 +129,9 @@ def flip_bound(ex: Experts, x, ids, wts):
             _, ulp, near = near_tie(v)
             if near.any():
                 cols = np.nonzero(near)[0]
-                wd = (d["codes"][:, cols].astype(np.float64) - d["zeros"][:, cols // 128]) * \
-                    d["scales"][:, cols // 128].view(np.float16).astype(np.float64)
+                gd = d.get("g", 128)
+                wd = (d["codes"][:, cols].astype(np.float64) - d["zeros"][:, cols // gd]) * \
+                    d["scales"][:, cols // gd].view(np.float16).astype(np.float64)
                 bound[t] += float(wts[t, j]) * (np.abs(wd) * ulp[cols]).sum(axis=1)
     return bound
 

@@ -351,8 +351,6 @@ qp_status qlinear_gemm(const qp_weight_desc *d, const qp_weight *w, const uint16
 {
     qp_status st = check_desc(d, true);
     if (st != QP_OK) return st;
-    if (d->group_size != kGroup) return fail(QP_ERR_UNSUPPORTED, "the GEMM is built for groups of 128");
-    if (d->zero_mode == QP_ZERO_PACKED) return fail(QP_ERR_UNSUPPORTED, "the GEMM reads byte zero points");
     if ((st = check_weight(d, w, true)) != QP_OK) return st;
     if ((st = check_xy(d, x, ldx, m, y, ldy, d->n, 4)) != QP_OK) return st;
     if (m > (1LL << 24)) return fail(QP_ERR_INVALID_ARG, "m too large");
@@ -361,6 +359,8 @@ qp_status qlinear_gemm(const qp_weight_desc *d, const qp_weight *w, const uint16
     GemmArgs a{};
     a.ex[0] = {(const uint8_t *)w->packed, w->scales, w->zeros};
     a.zmid = zero_pair(d);
+    a.gs = d->group_size;
+    a.zrow = d->zero_mode == QP_ZERO_PACKED ? (uint32_t)zero_row_bytes(d) : 0u;
     if (w->nnz > 0) {
         if (prod_over(d->k, gemm_xt_ld(m), 2, 0x7FFFFFFFLL) || prod_over(d->n, gemm_xt_ld(m), 4, 0x7FFFFFFFLL))
             return fail(QP_ERR_UNSUPPORTED, "m*k or m*n too large for the outlier add-back");
@@ -395,6 +395,8 @@ static qp_status grouped_launch(const qp_weight_desc *d, const qp_weight *expert
     for (int e = 0; e < n_experts; ++e)
         a.ex[e] = {(const uint8_t *)experts[e].packed, experts[e].scales, experts[e].zeros};
     a.zmid = zero_pair(d);
+    a.gs = d->group_size;
+    a.zrow = d->zero_mode == QP_ZERO_PACKED ? (uint32_t)zero_row_bytes(d) : 0u;
     a.x = x;
     a.ldx = ldx;
     a.row_src = row_src;
@@ -416,8 +418,6 @@ qp_status qlinear_grouped_gemm(const qp_weight_desc *d, const qp_weight *experts
 {
     qp_status st = check_desc(d, true);
     if (st != QP_OK) return st;
-    if (d->group_size != kGroup) return fail(QP_ERR_UNSUPPORTED, "the grouped GEMM is built for groups of 128");
-    if (d->zero_mode == QP_ZERO_PACKED) return fail(QP_ERR_UNSUPPORTED, "the grouped GEMM reads byte zero points");
     if (!experts) return fail(QP_ERR_INVALID_ARG, "experts NULL");
     if (n_experts < 1 || n_experts > kMaxExperts) return fail(QP_ERR_INVALID_ARG, "n_experts=%d not in 1..64", n_experts);
     for (int e = 0; e < n_experts; ++e)
@@ -484,9 +484,6 @@ qp_status qmoe_ffn(const qp_weight_desc *dgu, const qp_weight *gate_up, const qp
     if ((st = check_desc(dgu, true)) != QP_OK) return st;
     if ((st = check_desc(dd, true)) != QP_OK) return st;
     if (dgu->bits != dd->bits) return fail(QP_ERR_UNSUPPORTED, "gate/up and down must share the bit width");
-    if (dgu->group_size != kGroup || dd->group_size != kGroup || dgu->zero_mode == QP_ZERO_PACKED ||
-        dd->zero_mode == QP_ZERO_PACKED)
-        return fail(QP_ERR_UNSUPPORTED, "the expert FFN is built for groups of 128 with byte or implied zero points");
     const int64_t d_model = dgu->k, d_ff = dgu->n / 2;
     if (dgu->n % 32 != 0 || dd->n != d_model || dd->k != d_ff)
         return fail(QP_ERR_INVALID_ARG, "shapes: gate_up must be [2*d_ff, d_model], down [d_model, d_ff]");
@@ -663,7 +660,6 @@ qp_status qlinear_gemm_a8(const qp_weight_desc *d, const qp_weight *w, const int
     qp_status st = check_desc(d, true);
     if (st != QP_OK) return st;
     if (d->group_size != kGroup) return fail(QP_ERR_UNSUPPORTED, "the int8 GEMM is built for groups of 128");
-    if (d->zero_mode == QP_ZERO_PACKED) return fail(QP_ERR_UNSUPPORTED, "the int8 GEMM reads byte zero points");
     if ((st = check_weight(d, w, false)) != QP_OK) return st;
     if (w->nnz > 0) return fail(QP_ERR_UNSUPPORTED, "outliers are not applied on int8 activations");
     if (!xq || !aligned(xq, 16)) return fail(QP_ERR_INVALID_ARG, "xq NULL or not 16-byte aligned");
@@ -674,7 +670,8 @@ qp_status qlinear_gemm_a8(const qp_weight_desc *d, const qp_weight *w, const int
     if (prod_over(m, d->k, 1, 0x7FFFFFFFLL)) return fail(QP_ERR_UNSUPPORTED, "xq larger than 2 GiB");
     if ((int64_t)qp_packed_bytes(d) > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "packed weight larger than 2 GiB");
     const ExpertPtrs ep{(const uint8_t *)w->packed, w->scales, w->zeros};
-    return device(launch_gemm_a8(d->bits, ep, xq, x_scales, m, d->n, d->k, zero_pair(d), y, ldy, S(stream)),
+    const uint32_t zrow = d->zero_mode == QP_ZERO_PACKED ? (uint32_t)zero_row_bytes(d) : 0u;
+    return device(launch_gemm_a8(d->bits, ep, xq, x_scales, m, d->n, d->k, zero_pair(d), zrow, y, ldy, S(stream)),
                   "qlinear_gemm_a8");
 }
 

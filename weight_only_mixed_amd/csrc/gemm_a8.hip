@@ -210,11 +210,11 @@ __device__ __forceinline__ void unpack_all(std::integer_sequence<int, J...>, con
 
 // Whole group (before the loop): both row blocks from a staged weight slot part.
 template <int B, int NH>
-__device__ __forceinline__ void unpack_group8(const uint8_t *wpart, const SZ &z, int lane, i4v (&W)[kRBW][2])
+__device__ __forceinline__ void unpack_group8(const uint8_t *wpart, const SZ<kGroup> &z, int lane, i4v (&W)[kRBW][2])
 {
     uint32_t zb[kRBW];
 #pragma unroll
-    for (int u = 0; u < kRBW; ++u) zb[u] = zbias((z.zz[u] >> (8 * NH)) & 0xFF);
+    for (int u = 0; u < kRBW; ++u) zb[u] = zbias(zp_of(z, u, NH));
     uint32_t d[kRBW][2 * B];
     read_chunk<B>(wpart, lane, d[0]);
     read_chunk<B>(wpart + WStage<B>::kBytes, lane, d[1]);
@@ -223,16 +223,15 @@ __device__ __forceinline__ void unpack_group8(const uint8_t *wpart, const SZ &z,
 
 // ---- k loop --------------------------------------------------------------------------------
 
-// tot[.][mt] += s * float(isum) for scale half SH of each packed scale word.
+// tot[.][mt] += s * float(isum), s the scale of group SH of the tile for the lane's weight row.
 template <int SH>
-__device__ __forceinline__ void scale8(const uint32_t (&sc)[kRBW][4], const i4v (&acc)[kRBW], f4 (&tot)[kRBW][kMT],
-                                       int mt)
+__device__ __forceinline__ void scale8(const SZ<kGroup> &zs, const i4v (&acc)[kRBW], f4 (&tot)[kRBW][kMT], int mt)
 {
 #pragma unroll
     for (int u = 0; u < kRBW; ++u) {
+        const float s = sc_of(zs, u, SH);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            tot[u][mt][i] = __builtin_fmaf(SH == 0 ? lo_h(sc[u][i]) : hi_h(sc[u][i]), (float)acc[u][i], tot[u][mt][i]);
+        for (int i = 0; i < 4; ++i) tot[u][mt][i] = __builtin_fmaf(s, (float)acc[u][i], tot[u][mt][i]);
         asm volatile("" : "+v"(tot[u][mt]));
     }
 }
@@ -241,13 +240,13 @@ __device__ __forceinline__ void scale8(const uint32_t (&sc)[kRBW][4], const i4v 
 // tiles; scales and zero points (even steps) with the first half; the weight DMA (odd steps)
 // with the second half, after every activation piece, so the end-of-step wait can leave it in
 // flight.
-template <int B, int PAR, int MT>
-__device__ __forceinline__ void issue_tile8(const Bufs &bf, const StepIO<PAR> &io, int64_t G, int wv, int lane)
+template <int B, bool ZPK, int PAR, int MT>
+__device__ __forceinline__ void issue_tile8(const Bufs &bf, const StepIO<PAR, kGroup> &io, int64_t G, int wv, int lane)
 {
     if constexpr (MT < kDmaX) dma_x8(bf, io.gx, io.xdst, wv, MT);
     if constexpr (PAR == 0 && MT < kMT / 2) {
 #pragma unroll
-        for (int p = MT * kSZOps / (kMT / 2); p < (MT + 1) * kSZOps / (kMT / 2); ++p) load_sz_piece(bf, G, io.kt, lane, *io.z, p);
+        for (int p = MT * kSZOps / (kMT / 2); p < (MT + 1) * kSZOps / (kMT / 2); ++p) load_sz_piece<B, kGroup, ZPK>(bf, G, io.kt, lane, *io.z, p);
     }
     if constexpr (PAR == 1 && MT >= kMT / 2) {
         constexpr int q = MT - kMT / 2, h = kMT / 2;
@@ -262,15 +261,15 @@ constexpr int kLag = 1, kAR = kLag + 1;  // integer sums are scaled one tile lat
 // Activation tile MT of a step: its fragment reads for tile MT + 2, the matrix-core chains of
 // tile MT (two K = 64 steps per row block, from zero), the scaling of tile MT - 2's integer
 // sums (their matrix-core ops finished a tile ago) and a share of the next group's unpack.
-template <int B, int SH, int NH, int MT>
-__device__ __forceinline__ void tile8(const i4v (&Wc)[kRBW][2], i4v (&Wn)[kRBW][2], const uint32_t (&sc)[kRBW][4],
+template <int B, bool ZPK, int SH, int NH, int MT>
+__device__ __forceinline__ void tile8(const i4v (&Wc)[kRBW][2], i4v (&Wn)[kRBW][2], const SZ<kGroup> &zs,
                                       const uint32_t (&zb)[kRBW], const uint8_t *xs, const uint8_t *wpart, int lane,
                                       uint32_t (&d)[kRBW][2 * B], i4v (&X)[kXR][2], i4v (&acc)[kAR][kRBW],
-                                      f4 (&tot)[kRBW][kMT], const Bufs &bf, const StepIO<NH ^ 1> &io, int64_t G, int wv)
+                                      f4 (&tot)[kRBW][kMT], const Bufs &bf, const StepIO<NH ^ 1, kGroup> &io, int64_t G, int wv)
 {
     constexpr int cur = MT % kAR;
     const int t = lane >> 4, r = lane & 15;
-    issue_tile8<B, NH ^ 1, MT>(bf, io, G, wv, lane);
+    issue_tile8<B, ZPK, NH ^ 1, MT>(bf, io, G, wv, lane);
     if constexpr (MT + kXA < kMT) {
 #pragma unroll
         for (int p = 0; p < 2; ++p) X[(MT + kXA) % kXR][p] = *(const i4v *)(xs + xs_off8(16 * (MT + kXA) + r, 4 * p + t));
@@ -278,14 +277,14 @@ __device__ __forceinline__ void tile8(const i4v (&Wc)[kRBW][2], i4v (&Wn)[kRBW][
     if constexpr (MT == 0) read_chunk<B>(wpart, lane, d[0]);
     if constexpr (MT == 0) read_chunk<B>(wpart + WStage<B>::kBytes, lane, d[1]);
 #pragma unroll
-    for (int u = 0; u < kRBW; ++u) acc[cur][u] = mfma8(Wc[u][0], X[MT % kXR][0], (i4v){0, 0, 0, 0});
+    for (int u = 0; u < kRBW; ++u) acc[cur][u] = mfma8(X[MT % kXR][0], Wc[u][0], (i4v){0, 0, 0, 0});
 #pragma unroll
-    for (int u = 0; u < kRBW; ++u) acc[cur][u] = mfma8(Wc[u][1], X[MT % kXR][1], acc[cur][u]);
+    for (int u = 0; u < kRBW; ++u) acc[cur][u] = mfma8(X[MT % kXR][1], Wc[u][1], acc[cur][u]);
     unpack_share<B, NH, MT>(d, zb, Wn);
-    if constexpr (MT >= kLag) scale8<SH>(sc, acc[(MT - kLag) % kAR], tot, MT - kLag);
+    if constexpr (MT >= kLag) scale8<SH>(zs, acc[(MT - kLag) % kAR], tot, MT - kLag);
     if constexpr (MT == kMT - 1) {
 #pragma unroll
-        for (int j = kMT - kLag; j < kMT; ++j) scale8<SH>(sc, acc[j % kAR], tot, j);
+        for (int j = kMT - kLag; j < kMT; ++j) scale8<SH>(zs, acc[j % kAR], tot, j);
     }
     // per matrix-core op: a fragment read and a few vector ops issued behind it
 #pragma unroll
@@ -297,23 +296,23 @@ __device__ __forceinline__ void tile8(const i4v (&Wc)[kRBW][2], i4v (&Wn)[kRBW][
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int B, int SH, int NH, int... MT>
+template <int B, bool ZPK, int SH, int NH, int... MT>
 __device__ __forceinline__ void tiles8(std::integer_sequence<int, MT...>, const i4v (&Wc)[kRBW][2], i4v (&Wn)[kRBW][2],
-                                       const uint32_t (&sc)[kRBW][4], const uint32_t (&zb)[kRBW], const uint8_t *xs,
+                                       const SZ<kGroup> &zs, const uint32_t (&zb)[kRBW], const uint8_t *xs,
                                        const uint8_t *wpart, int lane, uint32_t (&d)[kRBW][2 * B], i4v (&X)[kXR][2],
                                        i4v (&acc)[kAR][kRBW], f4 (&tot)[kRBW][kMT], const Bufs &bf,
-                                       const StepIO<NH ^ 1> &io, int64_t G, int wv)
+                                       const StepIO<NH ^ 1, kGroup> &io, int64_t G, int wv)
 {
-    (tile8<B, SH, NH, MT>(Wc, Wn, sc, zb, xs, wpart, lane, d, X, acc, tot, bf, io, G, wv), ...);
+    (tile8<B, ZPK, SH, NH, MT>(Wc, Wn, zs, zb, xs, wpart, lane, d, X, acc, tot, bf, io, G, wv), ...);
 }
 
 // One 128-k group step: Wc times the activation tile of this group (slot xs), scale half SH;
 // meanwhile the next group (half NH of staged tile wpart, zero points zn) is unpacked into Wn
 // and the loads io are issued.
-template <int B, int SH, int NH>
-__device__ __forceinline__ void step8(const i4v (&Wc)[kRBW][2], i4v (&Wn)[kRBW][2], const uint32_t (&sc)[kRBW][4],
-                                      const SZ &zn, const uint8_t *xs, const uint8_t *wpart, int lane,
-                                      f4 (&tot)[kRBW][kMT], const Bufs &bf, const StepIO<NH ^ 1> &io, int64_t G, int wv)
+template <int B, bool ZPK, int SH, int NH>
+__device__ __forceinline__ void step8(const i4v (&Wc)[kRBW][2], i4v (&Wn)[kRBW][2], const SZ<kGroup> &zs,
+                                      const SZ<kGroup> &zn, const uint8_t *xs, const uint8_t *wpart, int lane,
+                                      f4 (&tot)[kRBW][kMT], const Bufs &bf, const StepIO<NH ^ 1, kGroup> &io, int64_t G, int wv)
 {
     const int t = lane >> 4, r = lane & 15;
     i4v X[kXR][2];
@@ -323,11 +322,11 @@ __device__ __forceinline__ void step8(const i4v (&Wc)[kRBW][2], i4v (&Wn)[kRBW][
         for (int p = 0; p < 2; ++p) X[mt][p] = *(const i4v *)(xs + xs_off8(16 * mt + r, 4 * p + t));
     uint32_t zb[kRBW];
 #pragma unroll
-    for (int u = 0; u < kRBW; ++u) zb[u] = zbias((zn.zz[u] >> (8 * NH)) & 0xFF);
+    for (int u = 0; u < kRBW; ++u) zb[u] = zbias(zp_of(zn, u, NH));
     uint32_t d[kRBW][2 * B];
     i4v acc[kAR][kRBW];
     __builtin_amdgcn_sched_barrier(0);
-    tiles8<B, SH, NH>(std::make_integer_sequence<int, kMT>{}, Wc, Wn, sc, zb, xs, wpart, lane, d, X, acc, tot, bf, io,
+    tiles8<B, ZPK, SH, NH>(std::make_integer_sequence<int, kMT>{}, Wc, Wn, zs, zb, xs, wpart, lane, d, X, acc, tot, bf, io,
                       G, wv);
 }
 
@@ -337,7 +336,7 @@ __device__ __forceinline__ void step8(const i4v (&Wc)[kRBW][2], i4v (&Wn)[kRBW][
 // during step 2t - 2.  Waits: vmcnt(0) after even steps, vmcnt(weight DMAs) after odd ones.
 // Loads past the end are clamped to the last group or tile; what is unpacked from them is
 // discarded.
-template <int B>
+template <int B, bool ZPK>
 __device__ __forceinline__ void k_loop8(const Bufs &bf, uint8_t *__restrict__ xs0, uint8_t *__restrict__ xs1,
                                         uint8_t *__restrict__ ws0, uint8_t *__restrict__ ws1, int64_t KT, int64_t G,
                                         int wv, int lane, f4 (&tot)[kRBW][kMT])
@@ -347,34 +346,34 @@ __device__ __forceinline__ void k_loop8(const Bufs &bf, uint8_t *__restrict__ xs
     auto tclamp = [&](int64_t t) { return t < KT ? t : KT - 1; };
     uint8_t *w0 = ws0 + wv * (kRBW * WStage<B>::kBytes);
     uint8_t *w1 = ws1 + wv * (kRBW * WStage<B>::kBytes);
-    SZ z0, z1;
+    SZ<kGroup> z0{}, z1{};
     i4v Wa[kRBW][2], Wb[kRBW][2];
 
 #pragma unroll
     for (int it = 0; it < kDmaX; ++it) dma_x8(bf, 0, xs0, wv, it);
     dma_w<B>(bf, 0, w0, lane);
     dma_w<B>(bf, tclamp(1), w1, lane);
-    load_sz(bf, G, 0, lane, z0);
+    load_sz<B, kGroup, ZPK>(bf, G, 0, lane, z0);
     wait_and_sync<0>();
-    retired(z0, bf.zmid);
+    retired<B, kGroup, ZPK>(z0, bf, 0);
     unpack_group8<B, 0>(w0, z0, lane, Wa);
 
     for (int64_t kt = 0; kt < KT; kt += 2) {
         const int64_t g = 2 * kt;
-        const StepIO<0> s0{gclamp(g + 1), tclamp(kt + 1), xs1, nullptr, &z1};
-        step8<B, 0, 1>(Wa, Wb, z0.sc, z0, xs0, w0, lane, tot, bf, s0, G, wv);
+        const StepIO<0, kGroup> s0{gclamp(g + 1), tclamp(kt + 1), xs1, nullptr, &z1};
+        step8<B, ZPK, 0, 1>(Wa, Wb, z0, z0, xs0, w0, lane, tot, bf, s0, G, wv);
         wait_and_sync<0>();
-        retired(z1, bf.zmid);
-        const StepIO<1> s1{gclamp(g + 2), tclamp(kt + 2), xs0, w0, nullptr};
-        step8<B, 1, 0>(Wb, Wa, z0.sc, z1, xs1, w1, lane, tot, bf, s1, G, wv);
+        retired<B, kGroup, ZPK>(z1, bf, tclamp(kt + 1));
+        const StepIO<1, kGroup> s1{gclamp(g + 2), tclamp(kt + 2), xs0, w0, nullptr};
+        step8<B, ZPK, 1, 0>(Wb, Wa, z0, z1, xs1, w1, lane, tot, bf, s1, G, wv);
         wait_and_sync<kWOps<B>>();
         if (kt + 1 >= KT) break;
-        const StepIO<0> s2{gclamp(g + 3), tclamp(kt + 2), xs1, nullptr, &z0};
-        step8<B, 0, 1>(Wa, Wb, z1.sc, z1, xs0, w1, lane, tot, bf, s2, G, wv);
+        const StepIO<0, kGroup> s2{gclamp(g + 3), tclamp(kt + 2), xs1, nullptr, &z0};
+        step8<B, ZPK, 0, 1>(Wa, Wb, z1, z1, xs0, w1, lane, tot, bf, s2, G, wv);
         wait_and_sync<0>();
-        retired(z0, bf.zmid);
-        const StepIO<1> s3{gclamp(g + 4), tclamp(kt + 3), xs0, w1, nullptr};
-        step8<B, 1, 0>(Wb, Wa, z1.sc, z0, xs1, w0, lane, tot, bf, s3, G, wv);
+        retired<B, kGroup, ZPK>(z0, bf, tclamp(kt + 2));
+        const StepIO<1, kGroup> s3{gclamp(g + 4), tclamp(kt + 3), xs0, w1, nullptr};
+        step8<B, ZPK, 1, 0>(Wb, Wa, z1, z0, xs1, w0, lane, tot, bf, s3, G, wv);
         wait_and_sync<kWOps<B>>();
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA may land after the workgroup ends
@@ -395,10 +394,10 @@ __device__ __forceinline__ void plan8(int64_t b, int64_t NT, int64_t MB, int64_t
     }
 }
 
-template <int B>
+template <int B, bool ZPK>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_a8_kernel(
-    ExpertPtrs W, const int8_t *xq, const float *sx, int64_t m, int64_t n, int64_t k, uint32_t zmid, uint16_t *y,
-    int64_t ldy)
+    ExpertPtrs W, const int8_t *xq, const float *sx, int64_t m, int64_t n, int64_t k, uint32_t zmid, uint32_t zrow,
+    uint16_t *y, int64_t ldy)
 {
     __shared__ __attribute__((aligned(16))) Smem8<B> sm;
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -412,6 +411,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 
     Bufs bf;
     bf.zmid = zmid;
+    bf.zrow = zrow;
+    bf.kt0 = 0;
     bf.x = make_rsrc(xq, m * k);
 #pragma unroll
     for (int it = 0; it < kDmaX; ++it) {
@@ -426,7 +427,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         const bool in = rb < NB;
         bf.w[u] = make_rsrc(W.packed + rb * KT * (512 * B), in ? KT * (512 * B) : 0);
         bf.sc[u] = make_rsrc(W.scales + rb * kTileN * G, in ? kTileN * G * 2 : 0);
-        bf.zr[u] = make_rsrc(W.zeros + rb * kTileN * G, in && !zmid ? kTileN * G : 0);
+        const int64_t zstride = zrow ? zrow : G;  // zero-point bytes per weight row
+        bf.zr[u] = make_rsrc(W.zeros + rb * kTileN * zstride, in && !zmid ? kTileN * zstride : 0);
     }
 
     f4 tot[kRBW][kMT];
@@ -438,20 +440,22 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
             asm volatile("" : "+v"(tot[u][mt]));
         }
 
-    k_loop8<B>(bf, sm.xs[0], sm.xs[1], sm.ws[0], sm.ws[1], KT, G, wv, lane, tot);
+    k_loop8<B, ZPK>(bf, sm.xs[0], sm.xs[1], sm.ws[0], sm.ws[1], KT, G, wv, lane, tot);
 
+    // lane (t, r): activation rows 16 mt + 4 t + i of weight row rb * 16 + r
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt) {
-        const int64_t row = m0 + 16 * mt + r;
-        if (row >= m) continue;
-        const float s = sx[row];
 #pragma unroll
-        for (int u = 0; u < kRBW; ++u) {
-            const int64_t rb = rb0 + u;
-            if (rb >= NB) continue;
-            const f4 v = tot[u][mt];
-            uint16_t *yp = y + row * ldy + rb * kTileN + 4 * t;
-            *(u2 *)yp = (u2){pack_h2(v[0] * s, v[1] * s), pack_h2(v[2] * s, v[3] * s)};
+        for (int i = 0; i < 4; ++i) {
+            const int64_t row = m0 + 16 * mt + 4 * t + i;
+            if (row >= m) continue;
+            const float s = sx[row];
+#pragma unroll
+            for (int u = 0; u < kRBW; ++u) {
+                const int64_t rb = rb0 + u;
+                if (rb >= NB) continue;
+                y[row * ldy + rb * kTileN + r] = __builtin_bit_cast(uint16_t, (_Float16)(tot[u][mt][i] * s));
+            }
         }
     }
 }
@@ -459,17 +463,19 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 }  // namespace
 
 hipError_t launch_gemm_a8(int bits, const ExpertPtrs &w, const int8_t *xq, const float *sx, int64_t m, int64_t n,
-                          int64_t k, uint32_t zmid, uint16_t *y, int64_t ldy, hipStream_t st)
+                          int64_t k, uint32_t zmid, uint32_t zrow, uint16_t *y, int64_t ldy, hipStream_t st)
 {
     if (m < 1) return hipSuccess;
     const int64_t blocks = ((n + kNT - 1) / kNT) * ((m + kMRows - 1) / kMRows);
     const dim3 grid((unsigned)blocks), block(kWaves * 64);
-    switch (bits) {
-    case 2: hipLaunchKernelGGL(gemm_a8_kernel<2>, grid, block, 0, st, w, xq, sx, m, n, k, zmid, y, ldy); break;
-    case 3: hipLaunchKernelGGL(gemm_a8_kernel<3>, grid, block, 0, st, w, xq, sx, m, n, k, zmid, y, ldy); break;
-    case 4: hipLaunchKernelGGL(gemm_a8_kernel<4>, grid, block, 0, st, w, xq, sx, m, n, k, zmid, y, ldy); break;
-    case 5: hipLaunchKernelGGL(gemm_a8_kernel<5>, grid, block, 0, st, w, xq, sx, m, n, k, zmid, y, ldy); break;
-    case 6: hipLaunchKernelGGL(gemm_a8_kernel<6>, grid, block, 0, st, w, xq, sx, m, n, k, zmid, y, ldy); break;
+    switch (bits * 2 + (zrow ? 1 : 0)) {
+#define QP_A8_CASE(B, ZPK)                                                                                      \
+    case B * 2 + ZPK:                                                                                           \
+        hipLaunchKernelGGL((gemm_a8_kernel<B, ZPK>), grid, block, 0, st, w, xq, sx, m, n, k, zmid, zrow, y, ldy); \
+        break;
+        QP_A8_CASE(2, 0) QP_A8_CASE(2, 1) QP_A8_CASE(3, 0) QP_A8_CASE(3, 1) QP_A8_CASE(4, 0) QP_A8_CASE(4, 1)
+        QP_A8_CASE(5, 0) QP_A8_CASE(5, 1) QP_A8_CASE(6, 0) QP_A8_CASE(6, 1)
+#undef QP_A8_CASE
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -1,0 +1,8 @@
+// Prefill and grouped dequant-GEMM instantiations: groups of 64 with byte or implied zero points.
+#include "gemm_kernel.h"
+
+namespace qp {
+namespace gk {
+QP_GEMM_VARIANT(64, false)
+}  // namespace gk
+}  // namespace qp

@@ -90,6 +90,8 @@ struct GemmArgs {
     void *y;
     int64_t ldy;
     uint32_t zmid;  // 0: stored zero points; else the implied pair (2^(b-1) in both bytes)
+    uint32_t zrow;  // 0: one zero-point byte per group; else bytes per row of b-bit zero points
+    int32_t gs;     // group size: 128, 64 or 32
     int32_t ksplit;  // grouped fp32 rows: k in ksplit equal parts (0 or 1: whole k); part s
     int64_t ysplit;  //   writes its partial rows at y + s * ysplit floats
     uint16_t *xt;   // workspace (outliers only): x transposed, [k][ldxt]
@@ -104,7 +106,7 @@ hipError_t launch_grouped(int bits, int epilogue, int n_experts, const GemmArgs 
 hipError_t launch_act_quantize(const uint16_t *x, int64_t ldx, int64_t m, int64_t k, int8_t *xq, float *scales,
                                hipStream_t st);
 hipError_t launch_gemm_a8(int bits, const ExpertPtrs &w, const int8_t *xq, const float *sx, int64_t m, int64_t n,
-                          int64_t k, uint32_t zmid, uint16_t *y, int64_t ldy, hipStream_t st);
+                          int64_t k, uint32_t zmid, uint32_t zrow, uint16_t *y, int64_t ldy, hipStream_t st);
 
 hipError_t launch_moe_dispatch(const int32_t *ids, const float *w, int64_t tokens, int topk,
                                int n_experts, int32_t *offsets, int32_t *row_src,

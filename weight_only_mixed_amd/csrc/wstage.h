@@ -34,7 +34,9 @@ struct Bufs {
     rsrc_t w[kRBW];           // packed tiles of row block rb0 + u (empty past the last block)
     rsrc_t sc[kRBW], zr[kRBW];
     uint32_t xoff[kDmaXMax];  // this lane's source of LDS-DMA piece it (row offset + chunk)
-    uint32_t zmid;            // 0: stored zero points; else the implied pair used instead
+    uint32_t zmid;            // 0: stored zero points; else the implied zero point (low byte) used instead
+    uint32_t zrow;            // b-bit zero points: bytes per row
+    uint32_t kt0;             // first k-tile of this workgroup's k range (metadata is indexed from k = 0)
 };
 
 __device__ __forceinline__ void lds_dma16(rsrc_t r, uint8_t *lds, uint32_t voff, uint32_t soff)
@@ -81,49 +83,98 @@ __device__ __forceinline__ void read_chunk(const uint8_t *base, int lane, uint32
     }
 }
 
-// Scales and zero points of one k-tile (both groups) for this lane: the zero points of its
-// weight row r, the scales of the accumulator rows 4t + i.
+// Scales and zero points of one k-tile for this lane's weight rows: row r (lane % 16) of each
+// of its two row blocks.  The tile holds kNGT = 256 / GS groups; group q's fp16 scale is half
+// q % 2 of sc[u][q / 2], its zero point byte q % 4 of zz[u][q / 4].  b-bit zero points arrive as
+// the two words of the row's bit stream that hold the tile's fields and are expanded to bytes
+// by retired().
+template <int GS>
 struct SZ {
-    uint32_t zz[kRBW];
-    uint32_t sc[kRBW][4];
+    static constexpr int kNGT = kTileK / GS, kSW = kNGT / 2;
+    static_assert(GS == 32 || GS == 64 || GS == 128, "group size");
+    uint32_t zz[kRBW][2];
+    uint32_t sc[kRBW][kSW];    // as loaded: fp16 pairs
+    float scf[kRBW][kNGT];     // converted once per tile by retired()
 };
-constexpr int kSZOps = kRBW * 5;
+constexpr int kSZPer = 3;                // loads per row block: zero word 0, zero word 1, scales
+constexpr int kSZOps = kRBW * kSZPer;    // scale / zero-point loads per wave per k-tile
 
-__device__ __forceinline__ void load_sz(const Bufs &bf, int64_t G, int64_t kt, int lane, SZ &z)
+// First bit of k-tile kt's fields in a row of b-bit zero points, and whether they run into a
+// second 32-bit word.
+template <int B, int GS>
+__device__ __forceinline__ uint32_t zbit(int64_t kt) { return (uint32_t)(kt * SZ<GS>::kNGT * B); }
+template <int B, int GS>
+__device__ __forceinline__ bool zstraddles(int64_t kt) { return (zbit<B, GS>(kt) & 31) + SZ<GS>::kNGT * B > 32; }
+
+// Load p of kSZOps: row block p / 3, then its zero word 0, zero word 1 (the next four byte
+// zero points for g = 32; the second word of b-bit zero points that straddle one), the scales
+// (4, 8 or 16 bytes).  Each load writes one fixed word, so the metadata stays in registers.
+template <int B, int GS, bool ZPK>
+__device__ __forceinline__ void load_sz_piece(const Bufs &bf, int64_t G, int64_t ktl, int lane, SZ<GS> &z, int p)
 {
-    const int t = lane >> 4, r = lane & 15;
-    const uint32_t vz = (uint32_t)(r * G), vs = (uint32_t)(4 * t * G * 2);
-    const uint32_t zo = __builtin_amdgcn_readfirstlane((uint32_t)(2 * kt));
-#pragma unroll
-    for (int u = 0; u < kRBW; ++u) {
-        z.zz[u] = ld2(bf.zr[u], vz, zo);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            z.sc[u][i] = ld4(bf.sc[u], vs, __builtin_amdgcn_readfirstlane((uint32_t)((i * G + 2 * kt) * 2)));
+    const int r = lane & 15, u = p / kSZPer, j = p % kSZPer;
+    const int64_t kt = ktl + bf.kt0;
+    if (j == 0) {
+        if constexpr (ZPK)
+            z.zz[u][0] = ld4(bf.zr[u], (uint32_t)r * bf.zrow, uni(4 * (zbit<B, GS>(kt) >> 5)));
+        else if constexpr (GS == 32)
+            z.zz[u][0] = ld4(bf.zr[u], (uint32_t)(r * G), uni(8 * kt));
+        else if constexpr (GS == 64)
+            z.zz[u][0] = ld4(bf.zr[u], (uint32_t)(r * G), uni(4 * kt));
+        else
+            z.zz[u][0] = ld2(bf.zr[u], (uint32_t)(r * G), uni(2 * kt));
+    } else if (j == 1) {
+        if constexpr (ZPK) {
+            // the second word lies inside the row whenever the fields reach it
+            if (zstraddles<B, GS>(kt)) z.zz[u][1] = ld4(bf.zr[u], (uint32_t)r * bf.zrow, uni(4 * (zbit<B, GS>(kt) >> 5) + 4));
+        } else if constexpr (GS == 32) {
+            z.zz[u][1] = ld4(bf.zr[u], (uint32_t)(r * G), uni(8 * kt + 4));
+        }
+    } else {
+        if constexpr (GS == 32) {
+            const u4 v = ld16(bf.sc[u], (uint32_t)(r * G * 2), uni(16 * kt));
+            z.sc[u][0] = v[0];
+            z.sc[u][1] = v[1];
+            z.sc[u][2] = v[2];
+            z.sc[u][3] = v[3];
+        } else if constexpr (GS == 64) {
+            const u2 v = ld8(bf.sc[u], (uint32_t)(r * G * 2), uni(8 * kt));
+            z.sc[u][0] = v[0];
+            z.sc[u][1] = v[1];
+        } else {
+            z.sc[u][0] = ld4(bf.sc[u], (uint32_t)(r * G * 2), uni(4 * kt));
+        }
     }
+}
+
+template <int B, int GS, bool ZPK>
+__device__ __forceinline__ void load_sz(const Bufs &bf, int64_t G, int64_t kt, int lane, SZ<GS> &z)
+{
+#pragma unroll
+    for (int p = 0; p < kSZOps; ++p) load_sz_piece<B, GS, ZPK>(bf, G, kt, lane, z, p);
+}
+
+// Zero point and fp16 scale (as fp32) of group q (0 .. kNGT-1) of the tile, row block u.
+template <int GS>
+__device__ __forceinline__ uint32_t zp_of(const SZ<GS> &z, int u, int q)
+{
+    return (z.zz[u][q >> 2] >> (8 * (q & 3))) & 0xFF;
+}
+template <int GS>
+__device__ __forceinline__ float sc_of(const SZ<GS> &z, int u, int q)
+{
+    return z.scf[u][q];
 }
 
 // The loads one k-loop step issues for later steps: the activation DMA of group gx into
 // slot xdst, and on even steps (PAR 0) the scales and zero points of tile kt into z, on odd
 // steps (PAR 1) the weight DMA of tile kt into this wave's part wdst of a weight slot.
-template <int PAR>
+template <int PAR, int GS>
 struct StepIO {
     int64_t gx, kt;
     uint8_t *xdst, *wdst;
-    SZ *z;
+    SZ<GS> *z;
 };
-
-// Scale / zero-point load p of 2 x 5: the zero pair, then the four scale words of row block p / 5.
-__device__ __forceinline__ void load_sz_piece(const Bufs &bf, int64_t G, int64_t kt, int lane, SZ &z, int p)
-{
-    const int t = lane >> 4, r = lane & 15, u = p / 5, j = p % 5;
-    if (j == 0) {
-        z.zz[u] = ld2(bf.zr[u], (uint32_t)(r * G), __builtin_amdgcn_readfirstlane((uint32_t)(2 * kt)));
-    } else {
-        const int i = j - 1;
-        z.sc[u][i] = ld4(bf.sc[u], (uint32_t)(4 * t * G * 2), __builtin_amdgcn_readfirstlane((uint32_t)((i * G + 2 * kt) * 2)));
-    }
-}
 
 // Weight DMA piece p of kWOps<B>: row block p / kOps, then its 16-byte pieces and (odd B) the
 // two 4-byte words of the tail.
@@ -141,21 +192,46 @@ __device__ __forceinline__ void dma_w_piece(const Bufs &bf, int64_t kt, uint8_t 
     }
 }
 
-// After a wait that has retired this tile's scale / zero-point loads: hide their origin from
-// the compiler, which does not see the inline-asm wait and would otherwise wait for them again
-// at their first use, counting the weight DMA issued since (meant to stay in flight) as older.
-// Implied zero points (zmid != 0) replace the loaded ones (those loads read out of range).
-__device__ __forceinline__ void retired(SZ &z, uint32_t zmid)
+// After the wait that has retired the loads of k-tile kt's metadata: b-bit zero points (ZPK)
+// are expanded to one byte per group; otherwise the implied zero point is added, replicated to
+// every byte (0 for stored zero points; the loads of implied ones read out of range, as zeros).
+// The scales are converted to fp32 once, and the registers' origin is hidden from the
+// compiler, which does not see the inline-asm wait and would otherwise wait for the loads
+// again at their first use, counting the weight DMA issued since (meant to stay in flight) as
+// older.  Branch-free: a branch here splits the k loop into blocks the scheduler cannot
+// interleave across.
+template <int B, int GS, bool ZPK>
+__device__ __forceinline__ void retired(SZ<GS> &z, const Bufs &bf, int64_t ktl)
 {
-    if (zmid) {  // uniform
+    if constexpr (ZPK) {
+        const int64_t kt = ktl + bf.kt0;
+        const uint32_t sh = zbit<B, GS>(kt) & 31;
+        const bool two = zstraddles<B, GS>(kt);
 #pragma unroll
-        for (int u = 0; u < kRBW; ++u) z.zz[u] = zmid;
+        for (int u = 0; u < kRBW; ++u) {
+            const uint64_t v = ((uint64_t)(two ? z.zz[u][1] : 0u) << 32 | z.zz[u][0]) >> sh;
+            uint32_t w[2] = {0u, 0u};
+#pragma unroll
+            for (int q = 0; q < SZ<GS>::kNGT; ++q) w[q >> 2] |= (uint32_t)((v >> (q * B)) & ((1u << B) - 1)) << (8 * (q & 3));
+            z.zz[u][0] = w[0];
+            z.zz[u][1] = w[1];
+        }
+    } else {
+        const uint32_t rep = (bf.zmid & 0xFF) * 0x01010101u;
+#pragma unroll
+        for (int u = 0; u < kRBW; ++u) {
+            z.zz[u][0] += rep;
+            z.zz[u][1] += rep;
+        }
     }
 #pragma unroll
     for (int u = 0; u < kRBW; ++u) {
-        asm volatile("" : "+v"(z.zz[u]));
+        asm volatile("" : "+v"(z.zz[u][0]), "+v"(z.zz[u][1]));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(z.sc[u][i]));
+        for (int i = 0; i < SZ<GS>::kSW; ++i) asm volatile("" : "+v"(z.sc[u][i]));
+        // one conversion per group and tile (each scale multiplies four outputs per tile)
+#pragma unroll
+        for (int q = 0; q < SZ<GS>::kNGT; ++q) z.scf[u][q] = (q & 1) ? hi_h(z.sc[u][q >> 1]) : lo_h(z.sc[u][q >> 1]);
     }
 }
 
