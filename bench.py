@@ -460,6 +460,33 @@ def bench_prefill(q, torch, workloads, stream):
     return roof
 
 
+def bench_prefill_variants(q, torch, workloads, stream):
+    """The prefill GEMM (M=512, K=8192, N=28672, no outliers) for the metadata variants of the
+    mixed-bit page (s2.3): groups of 64 and 32, symmetric groups, zero points in b bits."""
+    dev = torch.device("cuda")
+    wp, _ = workloads.prefill_weights()
+    Mp, Kp, Np = workloads.PREFILL_M, workloads.PREFILL_K, workloads.PREFILL_N
+    xp = torch.from_numpy(workloads.prefill_activations().view(np.int16)).to(dev)
+    yp = torch.empty((Mp, Np), dtype=torch.int16, device=dev)
+    out = {}
+    for bits, g, sym, packed in ((4, 128, False, True), (4, 64, False, False), (2, 32, False, False),
+                                 (2, 32, False, True), (2, 32, True, False), (5, 64, False, True)):
+        d, wt = quantize_pack(q, torch, wp, bits, sym=sym, g=g)
+        z = wt["zeros"]
+        if packed:
+            d = q.desc(bits, Np, Kp, group_size=g, zero_mode=q.QP_ZERO_PACKED)
+            z = torch.empty(q.qp_zero_bytes(d), dtype=torch.uint8, device=dev)
+            q.qpack_pack_zeros(d, wt["zeros"], z)
+        h = q.weight(wt["packed"], wt["scales"], z)
+        ms = time_graph(torch, lambda i: q.qlinear_gemm(d, h, xp, Kp, Mp, yp, Np, None, 0), 10, stream)
+        tf = 2 * Mp * Np * Kp / (ms * 1e-3) / 1e12
+        key = f"b{bits}_g{g}" + ("_sym" if sym else "") + ("_bbit_zeros" if packed else "")
+        out[key] = dict(us=round(ms * 1e3, 2), TFLOPs=round(tf, 1), frac_mfma_peak=round(tf / MFMA_F16_PEAK_TFLOPS, 4))
+        del wt, h, z
+    del xp, yp
+    return out
+
+
 def bench_prefill_a8(q, torch, workloads, stream):
     """Integer-dot prefill (the W8A8 path): the prefill shape M=512, K=8192, N=28672 at 4 bits,
     g=128, on int8 activations (no outlier add-back: the held-out weights stay in their groups
@@ -683,6 +710,9 @@ def main():
         extra["roofline_prefill"] = bench_prefill(q, torch, workloads, stream)
         log("bench: integer-dot prefill (int8 activations) M=512 K=8192 N=28672 4-bit")
         extra["roofline_prefill_a8"] = bench_prefill_a8(q, torch, workloads, stream)
+        if not args.no_variants:
+            log("bench: prefill GEMM metadata variants (groups of 64/32, symmetric, b-bit zero points)")
+            extra["prefill_variants"] = bench_prefill_variants(q, torch, workloads, stream)
 
     if not args.no_sweep:
         log("bench: 4096x4096 sweep, bits 2/3/5/6 x M 1/4/8")
