@@ -85,6 +85,12 @@ def lib():
         L.or_act_layout.argtypes = [i64, i64, vp, vp, i32]
         L.or_linear_a8.restype = None
         L.or_linear_a8.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp]
+        L.or_e4m3_value.restype = dbl
+        L.or_e4m3_value.argtypes = [i32]
+        L.or_e4m3_ceil.restype = i32
+        L.or_e4m3_ceil.argtypes = [ctypes.c_float]
+        L.or_quantize_fp8.restype = i32
+        L.or_quantize_fp8.argtypes = [i64, i64, i32, i32, i32, vp, i64, vp, vp, vp, vp, vp, vp, i32, vp]
         L.or_zero_row_bytes.restype = i64
         L.or_zero_row_bytes.argtypes = [i64, i32]
         for name in ("or_pack_zeros", "or_unpack_zeros"):
@@ -327,6 +333,44 @@ def linear_a8(xq, sx, q: dict):
     lib().or_linear_a8(M, N, K, g, _p(xq), _p(_c(sx, np.float32)), _p(codes), _p(_c(q["scales"], np.uint16)),
                        _p(_c(q["zeros"], np.uint8)), _p(r))
     return r
+
+
+def e4m3_value(code: int) -> float:
+    return lib().or_e4m3_value(code)
+
+
+def e4m3_ceil(t: float) -> int:
+    return lib().or_e4m3_ceil(t)
+
+
+def quantize_fp8(w_fp16, bits: int, g: int = GROUP, sym: bool = False, fb_stride: int = 8):
+    """fp8 block scales with an fp16 fallback: W [N, K] fp16 -> dict(codes u8 [N,K], sc8 u8
+    [N,K/g] scale bytes, zeros u8 [N,K/g] (midpoints when sym), scales_f32 [N,K/g] stored scale
+    values, factors f32 [N], fb u16 [N, fb_stride], counts i32 [N], most, g, sym)."""
+    w = _bits16(w_fp16)
+    N, K = w.shape
+    G = K // g
+    out = dict(codes=np.zeros((N, K), np.uint8), sc8=np.zeros((N, G), np.uint8), zeros=np.zeros((N, G), np.uint8),
+               scales_f32=np.zeros((N, G), np.float32), factors=np.zeros(N, np.float32),
+               fb=np.zeros((N, fb_stride), np.uint16), counts=np.zeros(N, np.int32))
+    out["most"] = lib().or_quantize_fp8(N, K, bits, g, 1 if sym else 0, _p(w), K, _p(out["codes"]), _p(out["sc8"]),
+                                        _p(out["zeros"]), _p(out["scales_f32"]), _p(out["factors"]), _p(out["fb"]),
+                                        fb_stride, _p(out["counts"]))
+    out["g"], out["sym"] = g, sym
+    return out
+
+
+def dequant_fp8(qd) -> np.ndarray:
+    """fp64 W_hat = (q - zp) * stored scale for a quantize_fp8 result."""
+    g = qd["g"]
+    z = np.repeat(qd["zeros"].astype(np.float64), g, 1)
+    s = np.repeat(qd["scales_f32"].astype(np.float64), g, 1)
+    return (qd["codes"].astype(np.float64) - z) * s
+
+
+def linear_fp8(x_fp16, qd) -> np.ndarray:
+    """fp64 r = x * W_hat^T over the exactly dequantized fp8-scale weights (numpy matmul)."""
+    return np.asarray(x_fp16, np.float16).astype(np.float64) @ dequant_fp8(qd).T
 
 
 def swiglu_act(x_row_fp16, gate: dict, up: dict):

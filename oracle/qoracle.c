@@ -45,6 +45,14 @@
  *    an all-zero group gets scale 1.0 with every code at the midpoint;
  *  - zero points stored in b bits ([MB] s2.3): the same zero points as the affine groups,
  *    row n a little-endian stream of b-bit fields (LSB-first), rows padded to 32-bit words;
+ *  - fp8 block scales with an fp16 fallback ([MB] s2.3): E4M3 (sign, 4-bit exponent with
+ *    bias 7, 3-bit mantissa, no infinities, 0x7F NaN) times one fp32 factor per row,
+ *    F = (largest fp32 group scale of the row) * 2^-8 (exact: the largest group maps to 256);
+ *    a group's code is the smallest E4M3 value >= s32 / F, the stored scale F * value, and
+ *    groups with s32 / F below E4M3's normal range (2^-6) keep the fp16 scale of the fp16
+ *    path, marked by a code
+ *    with the sign bit set whose low 7 bits index the row's fallback list; all-zero groups
+ *    store code 0; codes and zero points are computed from the stored scale;
  *  - KV cache ([KV] s2.1-s2.2, s3.1): symmetric groups along the head dimension with
  *    qmax = 2^(b-1) - 1, an fp32 scale m / qmax, codes rint(x / s) clamped to
  *    [-qmax, qmax] and stored offset by 2^(b-1); an all-zero group stores scale 0;
@@ -268,6 +276,126 @@ int or_quantize(int64_t N, int64_t K, int bits, int g, int zero_mode,
     free(buf);
     free(held);
     return 0;
+}
+
+/* ------------------------------------------------------------------------------ */
+/* fp8 block scales with an fp16 fallback  ([MB] s2.3)                              */
+/* ------------------------------------------------------------------------------ */
+
+/* Value of an E4M3 byte (OCP 8-bit float, "FN" variant): sign bit, exponent bits 6..3 with
+ * bias 7, mantissa bits 2..0; exponent 0 is subnormal (mantissa/8 * 2^-6); 0x7F and 0xFF are
+ * NaN; there are no infinities (0x7E = 448 is the largest finite value). */
+double or_e4m3_value(int code)
+{
+    const int sign = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double mag = e == 0 ? (m / 8.0) * ldexp(1.0, -6) : (1.0 + m / 8.0) * ldexp(1.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+/* The smallest positive finite E4M3 code whose value is >= t (t > 0), or -1 if t > 448:
+ * a scan of the codes in increasing value. */
+int or_e4m3_ceil(float t)
+{
+    for (int c = 0x01; c <= 0x7E; ++c)
+        if (or_e4m3_value(c) >= (double)t) return c;
+    return -1;
+}
+
+/* One row of K weights in groups of g with fp8 scales.  Writes the codes (u8 [K]), the scale
+ * bytes (u8 [K/g]), the zero points (u8 [K/g]; midpoints for sym), the stored scale of each
+ * group as fp32 (scale_out [K/g]: F * E4M3 value, the fp16 fallback's value, or 0 for an
+ * all-zero group), the row factor F and up to fb_cap fallback fp16 scales; returns the
+ * number of fallback groups of the row. */
+int or_quantize_fp8_row(int64_t K, int bits, int g, int sym, const uint16_t *w, uint8_t *codes, uint8_t *sc8,
+                        uint8_t *zeros, float *scale_out, float *factor, uint16_t *fb, int fb_cap)
+{
+    const int qmax = (1 << bits) - 1, mid = 1 << (bits - 1);
+    const int64_t G = K / g;
+    float *s32 = (float *)malloc(sizeof(float) * (size_t)G);
+    float *lo = (float *)malloc(sizeof(float) * (size_t)G);
+    int *zero = (int *)malloc(sizeof(int) * (size_t)G);
+    float mx = 0.0f;
+    int any = 0;
+    /* the fp32 scale of every group, as in the fp16 path before its fp16 rounding */
+    for (int64_t gi = 0; gi < G; ++gi) {
+        const uint16_t *wg = w + gi * g;
+        float l = 0.0f, h = 0.0f, m = 0.0f;
+        for (int i = 0; i < g; ++i) {
+            const float v = (float)hv(wg[i]);
+            if (v < l) l = v;
+            if (v > h) h = v;
+            if (fabsf(v) > m) m = fabsf(v);
+        }
+        lo[gi] = l;
+        zero[gi] = sym ? (m == 0.0f) : (h == l);
+        if (zero[gi]) continue;
+        volatile float range = sym ? m + m : h - l;
+        volatile float s = range / (float)qmax;
+        s32[gi] = s;
+        if (!any || s > mx) mx = s;
+        any = 1;
+    }
+    volatile float F = any ? mx * 0.00390625f : 1.0f;  /* exact: times 2^-8 */
+    *factor = F;
+    int nfb = 0;
+    for (int64_t gi = 0; gi < G; ++gi) {
+        const uint16_t *wg = w + gi * g;
+        uint8_t *cg = codes + gi * g;
+        if (zero[gi]) {
+            sc8[gi] = 0;
+            scale_out[gi] = 0.0f;
+            zeros[gi] = (uint8_t)(sym ? mid : 0);
+            for (int i = 0; i < g; ++i) cg[i] = (uint8_t)(sym ? mid : 0);
+            continue;
+        }
+        volatile float t = s32[gi] / F;
+        const int c = (t >= 0.015625f) ? or_e4m3_ceil(t) : -1;
+        float sf;
+        if (c > 0) {
+            volatile float prod = F * (float)or_e4m3_value(c);
+            sf = prod;
+            sc8[gi] = (uint8_t)c;
+        } else {  /* below E4M3's normal range: the fp16 path's scale */
+            uint16_t sh = or_round_half((double)s32[gi]);
+            if ((sh & 0x7C00) == 0) sh = 0x0400;
+            sf = (float)or_half_value(sh);
+            if (nfb < fb_cap) fb[nfb] = sh;
+            sc8[gi] = (uint8_t)(0x80 | (nfb & 0x7F));
+            ++nfb;
+        }
+        scale_out[gi] = sf;
+        int zp = mid;
+        if (!sym) {
+            volatile float lo_over_s = lo[gi] / sf;
+            zp = clampi(-(int)rintf(lo_over_s), 0, qmax);
+        }
+        zeros[gi] = (uint8_t)zp;
+        for (int i = 0; i < g; ++i) {
+            volatile float q = (float)hv(wg[i]) / sf;
+            cg[i] = (uint8_t)clampi((int)rintf(q) + zp, 0, qmax);
+        }
+    }
+    free(s32);
+    free(lo);
+    free(zero);
+    return nfb;
+}
+
+/* Every row of W [N][K] (stride ldw); fb is [N][fb_stride]; counts [N] receives each row's
+ * number of fallback groups.  Returns the largest count. */
+int or_quantize_fp8(int64_t N, int64_t K, int bits, int g, int sym, const uint16_t *w, int64_t ldw, uint8_t *codes,
+                    uint8_t *sc8, uint8_t *zeros, float *scales, float *factors, uint16_t *fb, int fb_stride,
+                    int32_t *counts)
+{
+    const int64_t G = K / g;
+    int most = 0;
+    for (int64_t n = 0; n < N; ++n) {
+        counts[n] = or_quantize_fp8_row(K, bits, g, sym, w + n * ldw, codes + n * K, sc8 + n * G, zeros + n * G,
+                                        scales + n * G, factors + n, fb + n * fb_stride, fb_stride);
+        if (counts[n] > most) most = counts[n];
+    }
+    return most;
 }
 
 /* ------------------------------------------------------------------------------ */
