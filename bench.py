@@ -64,6 +64,43 @@ def quantize_pack(q, torch, w: np.ndarray, bits: int, frac: float = 0.0, sym: bo
     return d, dict(packed=packed, scales=scales, zeros=zeros, rowptr=rowptr, col=col, val=val, nnz=nnz)
 
 
+def quantize_pack_fp8(q, torch, w: np.ndarray, bits: int, g: int, sym: bool, fb_stride: int = 8):
+    """fp8 scales with an fp16 fallback (qpack_quantize_fp8), packed in the device layout."""
+    n, k = w.shape
+    dev = torch.device("cuda")
+    d = q.desc(bits, n, k, group_size=g, zero_mode=q.QP_ZERO_MIDPOINT if sym else q.QP_ZERO_STORED,
+               scale_format=q.QP_SCALE_FP8)
+    wd = torch.from_numpy(np.ascontiguousarray(w).view(np.int16)).to(dev)
+    codes = torch.empty((n, k), dtype=torch.uint8, device=dev)
+    wt = dict(sc8=torch.empty((n, k // g), dtype=torch.uint8, device=dev),
+              zeros=None if sym else torch.empty((n, k // g), dtype=torch.uint8, device=dev),
+              factors=torch.empty(n, dtype=torch.float32, device=dev),
+              fb=torch.zeros((n, fb_stride), dtype=torch.int16, device=dev))
+    counts = torch.empty(n, dtype=torch.int32, device=dev)
+    q.qpack_quantize_fp8(d, wd, k, codes, wt["sc8"], wt["zeros"], wt["factors"], wt["fb"], fb_stride, counts)
+    wt["packed"] = torch.empty(q.qp_packed_bytes(d), dtype=torch.uint8, device=dev)
+    q.qpack_pack(d, codes, wt["packed"])
+    torch.cuda.synchronize()
+    wt["fallbacks"] = int(counts.sum().item())
+    del wd, codes
+    return d, wt
+
+
+def gemv_line_fp8(q, torch, stream, d, wt, nbytes, x, m, y, ldy):
+    """gemv_line for a QP_SCALE_FP8 weight (its own clones for the >= 1 GiB rotation)."""
+    fb_stride = wt["fb"].shape[1]
+    keep = [{key: wt[key].clone() if wt[key] is not None else None for key in ("packed", "sc8", "zeros", "factors",
+                                                                            "fb")}
+            for _ in range(copies_for(nbytes))]
+    hs = [q.weight_fp8(c["packed"], c["sc8"], c["factors"], c["fb"], fb_stride, c["zeros"]) for c in keep]
+    k = d.k
+    ms = time_graph(torch, lambda i: q.qlinear_gemv(d, hs[i % len(hs)], x, k, m, y, ldy), 2 * len(hs), stream)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    del hs, keep
+    return dict(us=round(ms * 1e3, 3), GBps=round(gbps, 1), frac_hbm_peak=round(gbps / HBM_PEAK_GBS, 4),
+                bytes=nbytes)
+
+
 def weight_bytes(n: int, k: int, bits: int, nnz: int = 0, sym: bool = False, g: int = 128) -> int:
     """Algorithmic bytes a matmul must read for the weight: packed codes, fp16 scale and u8
     zero point per group of g (no zero point for symmetric groups), plus the outlier CSR
@@ -760,6 +797,21 @@ def main():
             pz[f"b{b}_g{g}"] = line
             del wz, zp
         extra["gemv_4096_packed_zeros_m1"] = pz
+        log("bench: 4096x4096 GEMV with fp8 scales (fp16 fallback), M=1 and 16")
+        f8 = {}
+        x16 = torch.from_numpy(workloads.activations_fp16(16, K, workloads.seed_for(2)).view(np.int16)).to(dev)
+        y16 = torch.empty((16, N), dtype=torch.int16, device=dev)
+        for b, g, sy in ((2, 32, True), (3, 64, True), (4, 128, False)):
+            d8, w8 = quantize_pack_fp8(q, torch, w2, b, g, sy)
+            # codes, one scale byte per group, zero-point bytes unless symmetric, one fp32 factor per row
+            b8 = N * K * b // 8 + (N * K // g) * (1 if sy else 2) + 4 * N
+            for m, x, y in ((1, x1, y1), (16, x16, y16)):
+                line = gemv_line_fp8(q, torch, stream, d8, w8, b8, x, m, y, N)
+                line["bits_per_weight"] = round(8 * b8 / (N * K), 4)
+                line["fallback_groups"] = w8["fallbacks"]
+                f8[f"b{b}_g{g}{'_sym' if sy else ''}_m{m}"] = line
+            del w8
+        extra["gemv_4096_fp8_scales"] = f8
     if not args.no_stack:
         log("bench: Llama-7B-shaped 32-layer decode stack at M=1")
         extra["stack_llama7b_m1"] = bench_stack(q, torch, workloads, stream)

@@ -98,22 +98,35 @@ enum {
  *                    occupies bits [g*b, g*b + b), padded to whole 32-bit words
  *                    (qp_zero_bytes(desc) bytes in all).  qpack_quantize writes u8 zero points
  *                    in this mode too; qpack_pack_zeros turns them into the packed form.  Read by
- *                    qlinear_gemv and qlinear_gemv_batch; the GEMM, grouped GEMM and MoE FFN
- *                    return QP_ERR_UNSUPPORTED. */
+ *                    every matmul. */
 enum { QP_ZERO_STORED = 0, QP_ZERO_MIDPOINT = 1, QP_ZERO_PACKED = 2 };
+
+/* Storage of the group scales (qp_weight_desc.scale_format).
+ *  QP_SCALE_FP16: one fp16 scale per group in qp_weight.scales.
+ *  QP_SCALE_FP8:  8-bit float scales with an fp16 fallback (mixed-bit page, s2.3: 2-bit groups
+ *                 of 32 at 2.25 bits per weight, the few blocks out of the fp8 range kept in
+ *                 fp16).  Group (n, g) has one byte in qp_weight.scales8 [n][k/g]:
+ *                  - bit 7 clear: an E4M3 value (OCP 8-bit float: 4-bit exponent, bias 7, 3-bit
+ *                    mantissa; 0x7F is NaN); the scale is row_factors[n] times that value;
+ *                  - bit 7 set: the scale is the fp16 fb_scales[n * fb_stride + (byte & 0x7F)].
+ *                 Written by qpack_quantize_fp8; read by qlinear_gemv (byte or implied zero
+ *                 points).  The other matmuls, qlinear_gemv_batch, qlinear_gemv_host and
+ *                 qp_blob_write return QP_ERR_UNSUPPORTED for it (qp_blob_bytes 0). */
+enum { QP_SCALE_FP16 = 0, QP_SCALE_FP8 = 1 };
 
 /* Shape and format of one quantized matrix W[n][k]. */
 typedef struct {
     int32_t bits;       /* 2, 3, 4, 5 or 6 */
     int32_t group_size; /* 32, 64 or 128 weights of consecutive k inside a row share a scale and
                            zero point (mixed-bit page, s2.3: small groups for the lowest bit
-                           widths).  32 and 64: qpack_quantize, qpack_pack/unpack, qlinear_gemv
-                           and qlinear_gemv_batch (one group size per batch); the GEMM, grouped
-                           GEMM and MoE FFN return QP_ERR_UNSUPPORTED for them. */
+                           widths).  Every call takes all three, except qlinear_gemm_a8 (128)
+                           and qlinear_gemv_batch (one group size per batch). */
     int32_t layout;     /* QP_LAYOUT_CANONICAL or QP_LAYOUT_DEVICE */
     int32_t zero_mode;  /* QP_ZERO_STORED, QP_ZERO_MIDPOINT or QP_ZERO_PACKED */
     int64_t n;          /* rows (output features) */
     int64_t k;          /* columns (input features), multiple of 128 */
+    int32_t scale_format; /* QP_SCALE_FP16 (0) or QP_SCALE_FP8 */
+    int32_t reserved;     /* 0 */
 } qp_weight_desc;
 
 /* Device buffers of one quantized matrix. */
@@ -127,6 +140,11 @@ typedef struct {
     const int32_t *csr_col;     /* [nnz] column k of each outlier, ascending within a row */
     const uint16_t *csr_val;    /* [nnz] fp16 value of each outlier */
     int64_t nnz;                /* number of outliers (0 if csr_rowptr is NULL) */
+    /* QP_SCALE_FP8 only (scales unused):                                                    */
+    const uint8_t *scales8;     /* [n][k/group_size] scale bytes, 4-byte aligned */
+    const float *row_factors;   /* [n] fp32 factor of each row's E4M3 scales */
+    const uint16_t *fb_scales;  /* [n][fb_stride] fp16 fallback scales (NULL if fb_stride is 0) */
+    int64_t fb_stride;          /* fallback slots per row, 0..128 */
 } qp_weight;
 
 /* ---- host-side accounting (no device work) ------------------------------------------ */
@@ -177,6 +195,29 @@ qp_status qpack_quantize(const qp_weight_desc *desc, const uint16_t *w, int64_t 
                          uint16_t *csr_val, int64_t csr_cap, int64_t *nnz_out,
                          void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * Group quantizer with fp8 scales (QP_SCALE_FP8; mixed-bit page, s2.3), no outliers.  Per row:
+ * every group's fp32 scale s32 as in qpack_quantize (before its fp16 rounding), the row factor
+ * F = (largest s32 of the row's non-zero groups) * 2^-8 (exact: that group maps to 256; 1.0 for
+ * an all-zero row), then per group t = s32 / F (IEEE fp32) and
+ *  - t >= 2^-6: byte = the smallest E4M3 value >= t (so the range still fits), stored scale
+ *    F * value (fp32);
+ *  - t < 2^-6 (below E4M3's normal range): byte = 0x80 | j for the row's j-th such group, the
+ *    stored scale is the fp16 scale qpack_quantize would give it (fb_scales[n][j]);
+ *  - an all-zero group: byte 0, codes at the zero point (0, or the midpoint).
+ * Zero points and codes then follow qpack_quantize's formulas with the stored scale.
+ *  desc     scale_format QP_SCALE_FP8, zero_mode QP_ZERO_STORED or QP_ZERO_MIDPOINT.
+ *  w, ldw, codes, zeros  as in qpack_quantize.
+ *  scales8  u8 [n][k/g]; row_factors float [n]; fb_scales u16 [n][fb_stride] (may be NULL when
+ *           fb_stride is 0); counts int32 [n] receives each row's number of fallback groups.
+ *           A row with more than fb_stride (<= 128) fallbacks keeps only the first fb_stride
+ *           (check counts; quantize again with a larger stride).  All device pointers.
+ * Bit-exact with the CPU reference.
+ */
+qp_status qpack_quantize_fp8(const qp_weight_desc *desc, const uint16_t *w, int64_t ldw, uint8_t *codes,
+                             uint8_t *scales8, uint8_t *zeros, float *row_factors, uint16_t *fb_scales,
+                             int64_t fb_stride, int32_t *counts, void *stream);
+
 /* codes u8 [n][k] (values < 2^bits) -> packed bytes in desc->layout
  * (qp_packed_bytes(desc) bytes, 16-byte aligned). */
 qp_status qpack_pack(const qp_weight_desc *desc, const uint8_t *codes, void *packed,
@@ -200,6 +241,10 @@ qp_status qpack_unpack(const qp_weight_desc *desc, const void *packed, uint8_t *
  *  x  fp16 [m][ldx] device, ldx >= k, ldx % 8 == 0, 16-byte aligned.
  *  y  fp16 [m][ldy] device, ldy >= n, ldy % 4 == 0, 8-byte aligned.
  *  The optional CSR of `w` is added in fp32 before the single fp16 rounding of y.
+ *  QP_SCALE_FP8: each group's fp32 sum is multiplied by its E4M3 value (a fallback group: by
+ *  its fp16 scale over the row factor) and the row's sum by the row factor, before the CSR.
+ *  A fallback byte 0x80 | j with j >= fb_stride is malformed; it reads the row's last slot
+ *  (0 when fb_stride is 0), so the call stays inside the buffers.
  * Returns QP_ERR_UNSUPPORTED for m > 16 (use qlinear_gemm).
  */
 qp_status qlinear_gemv(const qp_weight_desc *desc, const qp_weight *w, const uint16_t *x,

@@ -30,7 +30,7 @@ static uint32_t rnd()
 
 static qp_weight_desc desc(int bits, int64_t n, int64_t k, int layout = QP_LAYOUT_DEVICE, int g = 128, int zm = 0)
 {
-    qp_weight_desc d;
+    qp_weight_desc d{};
     d.bits = bits;
     d.group_size = g;
     d.layout = layout;

@@ -337,3 +337,54 @@ def test_int8_path_validation():
     assert q.qlinear_gemm_a8(d64, w, FAKE, FAKE, 4, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
     canon = q.desc(4, 256, 512, layout=q.QP_LAYOUT_CANONICAL)
     assert q.qlinear_gemm_a8(canon, w, FAKE, FAKE, 4, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
+
+
+def test_fp8_scale_validation():
+    """QP_SCALE_FP8 (8-bit float scales with an fp16 fallback, mixed-bit page s2.3): only the
+    fp8 quantizer writes it and only the GEMV reads it; every other call refuses it, and the
+    fp8 calls check their buffers, before any launch."""
+    ok = dict(stream=0, check=False)
+    f8 = q.desc(2, 256, 512, group_size=32, zero_mode=q.QP_ZERO_MIDPOINT, scale_format=q.QP_SCALE_FP8)
+    fp16 = q.desc(2, 256, 512, group_size=32, zero_mode=q.QP_ZERO_MIDPOINT)
+    assert q.qp_packed_bytes(q.desc(2, 256, 512, scale_format=7)) == 0
+    assert q.qp_packed_bytes(f8) == 256 * 512 // 4
+    assert q.qp_packed_bytes(q.desc(2, 256, 512, zero_mode=q.QP_ZERO_PACKED, scale_format=q.QP_SCALE_FP8)) == 0
+    # the fp8 quantizer
+    args = (FAKE, 512, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE)
+    assert q.qpack_quantize_fp8(fp16, *args, **ok) == q.QP_ERR_INVALID_ARG
+    assert q.qpack_quantize_fp8(f8, FAKE, 512, FAKE, None, FAKE, FAKE, FAKE, 8, FAKE, **ok) == q.QP_ERR_INVALID_ARG
+    assert q.qpack_quantize_fp8(f8, FAKE, 512, FAKE, FAKE, FAKE, FAKE, FAKE, 129, FAKE, **ok) == q.QP_ERR_INVALID_ARG
+    assert q.qpack_quantize_fp8(f8, FAKE, 512, FAKE, FAKE, FAKE, FAKE, None, 8, FAKE, **ok) == q.QP_ERR_INVALID_ARG
+    assert q.qpack_quantize_fp8(f8, FAKE, 510, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, **ok) == q.QP_ERR_INVALID_ARG
+    assert q.qpack_quantize_fp8(f8, FAKE, 512, FAKE, FAKE, FAKE, FAKE + 2, FAKE, 8, FAKE, **ok) == q.QP_ERR_INVALID_ARG
+    stored = q.desc(2, 256, 512, group_size=32, scale_format=q.QP_SCALE_FP8)
+    assert q.qpack_quantize_fp8(stored, FAKE, 512, FAKE, FAKE, None, FAKE, FAKE, 8, FAKE, **ok) == q.QP_ERR_INVALID_ARG
+    wide = q.desc(2, 16, 524416, layout=q.QP_LAYOUT_CANONICAL, group_size=32,
+                  scale_format=q.QP_SCALE_FP8)  # 16388 groups per row
+    assert q.qpack_quantize_fp8(wide, FAKE, 524416, *args[2:], **ok) == q.QP_ERR_UNSUPPORTED
+    st, _ = q.qpack_quantize(f8, FAKE, 512, 0.0, FAKE, FAKE, FAKE, **ok)
+    assert st == q.QP_ERR_UNSUPPORTED
+    # the GEMV checks the fp8 buffers
+    good = q.weight_fp8(FAKE, FAKE, FAKE, FAKE, 8)
+    assert q.qlinear_gemv(f8, q.weight_fp8(FAKE, None, FAKE, FAKE, 8), FAKE, 512, 1, FAKE, 256, **ok) == q.QP_ERR_INVALID_ARG
+    assert q.qlinear_gemv(f8, q.weight_fp8(FAKE, FAKE, None, FAKE, 8), FAKE, 512, 1, FAKE, 256, **ok) == q.QP_ERR_INVALID_ARG
+    assert q.qlinear_gemv(f8, q.weight_fp8(FAKE, FAKE, FAKE, None, 8), FAKE, 512, 1, FAKE, 256, **ok) == q.QP_ERR_INVALID_ARG
+    assert q.qlinear_gemv(f8, q.weight_fp8(FAKE, FAKE, FAKE, FAKE, 129), FAKE, 512, 1, FAKE, 256, **ok) == q.QP_ERR_INVALID_ARG
+    assert q.qlinear_gemv(f8, q.weight_fp8(FAKE, FAKE + 1, FAKE, FAKE, 8), FAKE, 512, 1, FAKE, 256, **ok) == q.QP_ERR_INVALID_ARG
+    assert q.qlinear_gemv(f8, good, FAKE, 512, 17, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
+    # every other matmul refuses fp8 scales
+    assert q.qlinear_gemv_batch([q.gemv_problem(f8, good, FAKE, 512, 1, FAKE, 256)], **ok) == q.QP_ERR_UNSUPPORTED
+    assert q.qlinear_gemm(f8, good, FAKE, 512, 64, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
+    assert q.qlinear_grouped_gemm(f8, [good], FAKE, 512, FAKE, FAKE, 10, 0, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
+    f8_128 = q.desc(4, 256, 512, zero_mode=q.QP_ZERO_MIDPOINT, scale_format=q.QP_SCALE_FP8)
+    assert q.qlinear_gemm_a8(f8_128, good, FAKE, FAKE, 4, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
+    gu = q.desc(4, 2 * 1024, 512, scale_format=q.QP_SCALE_FP8)
+    dn = q.desc(4, 512, 1024, scale_format=q.QP_SCALE_FP8)
+    assert q.qmoe_ffn(gu, [good] * 4, dn, [good] * 4, FAKE, 512, 8, FAKE, FAKE, 2, FAKE, 512, FAKE, 1 << 30,
+                      **ok) == q.QP_ERR_UNSUPPORTED
+    canon8 = q.desc(2, 256, 512, layout=q.QP_LAYOUT_CANONICAL, group_size=32, zero_mode=q.QP_ZERO_MIDPOINT,
+                    scale_format=q.QP_SCALE_FP8)
+    assert q.lib.qlinear_gemv_host(ctypes.byref(canon8), ctypes.byref(good), FAKE, 512, 1, FAKE, 256, 1) == \
+        q.QP_ERR_UNSUPPORTED
+    assert q.qp_blob_bytes(canon8, 0) == 0
+    assert q.lib.qp_blob_write(ctypes.byref(canon8), ctypes.byref(good), FAKE, 1 << 20) == q.QP_ERR_UNSUPPORTED

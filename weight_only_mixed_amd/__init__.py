@@ -27,19 +27,23 @@ QP_OK, QP_ERR_INVALID_ARG, QP_ERR_UNSUPPORTED, QP_ERR_DEVICE, QP_ERR_WORKSPACE =
 QP_LAYOUT_CANONICAL, QP_LAYOUT_DEVICE = 0, 1
 QP_EPI_NONE, QP_EPI_SWIGLU, QP_EPI_ROWS_F32 = 0, 1, 2
 QP_ZERO_STORED, QP_ZERO_MIDPOINT, QP_ZERO_PACKED = 0, 1, 2
+QP_SCALE_FP16, QP_SCALE_FP8 = 0, 1
 STATUS_NAMES = {0: "QP_OK", 1: "QP_ERR_INVALID_ARG", 2: "QP_ERR_UNSUPPORTED", 3: "QP_ERR_DEVICE",
                 4: "QP_ERR_WORKSPACE"}
 
 
 class qp_weight_desc(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("group_size", ctypes.c_int32), ("layout", ctypes.c_int32),
-                ("zero_mode", ctypes.c_int32), ("n", ctypes.c_int64), ("k", ctypes.c_int64)]
+                ("zero_mode", ctypes.c_int32), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("scale_format", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class qp_weight(ctypes.Structure):
     _fields_ = [("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p),
                 ("csr_rowptr", ctypes.c_void_p), ("csr_col", ctypes.c_void_p),
-                ("csr_val", ctypes.c_void_p), ("nnz", ctypes.c_int64)]
+                ("csr_val", ctypes.c_void_p), ("nnz", ctypes.c_int64),
+                ("scales8", ctypes.c_void_p), ("row_factors", ctypes.c_void_p), ("fb_scales", ctypes.c_void_p),
+                ("fb_stride", ctypes.c_int64)]
 
 
 class qkv_desc(ctypes.Structure):
@@ -69,6 +73,7 @@ _SIGS = {
     "qpack_quantize_workspace_bytes": (_sz, [_D, _dbl]),
     "qpack_quantize": (_i32, [_D, _vp, _i64, _dbl, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
                               ctypes.POINTER(_i64), _vp, _sz, _vp]),
+    "qpack_quantize_fp8": (_i32, [_D, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp]),
     "qpack_pack": (_i32, [_D, _vp, _vp, _vp]),
     "qpack_unpack": (_i32, [_D, _vp, _vp, _vp]),
     "qpack_pack_zeros": (_i32, [_D, _vp, _vp, _vp]),
@@ -137,12 +142,18 @@ def _check(fn, status, check):
 
 
 def desc(bits: int, n: int, k: int, layout: int = QP_LAYOUT_DEVICE, group_size: int = 128,
-         zero_mode: int = QP_ZERO_STORED):
-    return qp_weight_desc(bits, group_size, layout, zero_mode, n, k)
+         zero_mode: int = QP_ZERO_STORED, scale_format: int = QP_SCALE_FP16):
+    return qp_weight_desc(bits, group_size, layout, zero_mode, n, k, scale_format, 0)
 
 
 def weight(packed, scales, zeros, rowptr=None, col=None, val=None, nnz: int = 0):
     return qp_weight(_ptr(packed), _ptr(scales), _ptr(zeros), _ptr(rowptr), _ptr(col), _ptr(val), nnz)
+
+
+def weight_fp8(packed, scales8, row_factors, fb_scales, fb_stride: int, zeros=None):
+    """A QP_SCALE_FP8 weight (no outliers): scale bytes, row factors, fallback list."""
+    return qp_weight(_ptr(packed), None, _ptr(zeros), None, None, None, 0, _ptr(scales8), _ptr(row_factors),
+                     _ptr(fb_scales), fb_stride)
 
 
 # ---- host accounting ----------------------------------------------------------------
@@ -186,6 +197,13 @@ def qpack_quantize(d, w, ldw, outlier_frac, codes, scales, zeros, csr_rowptr=Non
                             ctypes.byref(nnz), _ptr(workspace), ws_bytes, _stream(stream))
     _check("qpack_quantize", st, check)
     return st, nnz.value
+
+
+def qpack_quantize_fp8(d, w, ldw, codes, scales8, zeros, row_factors, fb_scales, fb_stride, counts, stream=None,
+                       check=True):
+    st = lib.qpack_quantize_fp8(ctypes.byref(d), _ptr(w), ldw, _ptr(codes), _ptr(scales8), _ptr(zeros),
+                                _ptr(row_factors), _ptr(fb_scales), fb_stride, _ptr(counts), _stream(stream))
+    return _check("qpack_quantize_fp8", st, check)
 
 
 def qpack_pack(d, codes, packed, stream=None, check=True):

@@ -28,7 +28,7 @@ COMMON = [
 # The GEMV's matrix-core results feed vector fmas right away: with the VGPR form of MFMA
 # they are written where the fmas read them, instead of accumulation registers copied over
 # one by one (eight copies per k-tile in the 4-wave kernels).
-PER_FILE = {"quantize.hip": ["-ffp-contract=off"], "kvattn.hip": ["-ffp-contract=off", "-mllvm", "-amdgpu-mfma-vgpr-form=1"], "qmm_small.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+PER_FILE = {"quantize.hip": ["-ffp-contract=off"], "quant_fp8.hip": ["-ffp-contract=off"], "kvattn.hip": ["-ffp-contract=off", "-mllvm", "-amdgpu-mfma-vgpr-form=1"], "qmm_small.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:

@@ -68,6 +68,18 @@ static qp_status check_desc(const qp_weight_desc *d, bool need_device)
                     (long long)d->n, (long long)d->k);
     if (need_device && d->layout != QP_LAYOUT_DEVICE)
         return fail(QP_ERR_UNSUPPORTED, "matmuls read the device layout (pack with QP_LAYOUT_DEVICE)");
+    if (d->scale_format != QP_SCALE_FP16 && d->scale_format != QP_SCALE_FP8)
+        return fail(QP_ERR_INVALID_ARG, "scale_format=%d unknown", d->scale_format);
+    if (d->scale_format == QP_SCALE_FP8 && d->zero_mode == QP_ZERO_PACKED)
+        return fail(QP_ERR_UNSUPPORTED, "fp8 scales take byte or implied zero points");
+    return QP_OK;
+}
+
+// Calls that read only fp16 scales.
+static qp_status need_fp16_scales(const qp_weight_desc *d, const char *who)
+{
+    if (d->scale_format != QP_SCALE_FP16)
+        return fail(QP_ERR_UNSUPPORTED, "%s reads fp16 scales (fp8 scales: qpack_quantize_fp8, qlinear_gemv)", who);
     return QP_OK;
 }
 
@@ -75,7 +87,17 @@ static qp_status check_weight(const qp_weight_desc *d, const qp_weight *w, bool 
 {
     if (!w) return fail(QP_ERR_INVALID_ARG, "weight is NULL");
     if (!w->packed || !aligned(w->packed, 16)) return fail(QP_ERR_INVALID_ARG, "packed NULL or not 16-byte aligned");
-    if (!w->scales || !aligned(w->scales, 4)) return fail(QP_ERR_INVALID_ARG, "scales NULL or not 4-byte aligned");
+    if (d->scale_format == QP_SCALE_FP8) {
+        if (!w->scales8 || !aligned(w->scales8, 4)) return fail(QP_ERR_INVALID_ARG, "scales8 NULL or not 4-byte aligned");
+        if (!w->row_factors || !aligned(w->row_factors, 4))
+            return fail(QP_ERR_INVALID_ARG, "row_factors NULL or not 4-byte aligned");
+        if (w->fb_stride < 0 || w->fb_stride > 128)
+            return fail(QP_ERR_INVALID_ARG, "fb_stride=%lld not in 0..128", (long long)w->fb_stride);
+        if (w->fb_stride > 0 && (!w->fb_scales || !aligned(w->fb_scales, 2)))
+            return fail(QP_ERR_INVALID_ARG, "fb_scales NULL or not 2-byte aligned");
+    } else if (!w->scales || !aligned(w->scales, 4)) {
+        return fail(QP_ERR_INVALID_ARG, "scales NULL or not 4-byte aligned");
+    }
     if (d->zero_mode == QP_ZERO_STORED && (!w->zeros || !aligned(w->zeros, 2)))
         return fail(QP_ERR_INVALID_ARG, "zeros NULL or not 2-byte aligned");
     if (d->zero_mode == QP_ZERO_PACKED && (!w->zeros || !aligned(w->zeros, 4)))
@@ -206,6 +228,7 @@ qp_status qpack_quantize(const qp_weight_desc *d, const uint16_t *w, int64_t ldw
 {
     qp_status st = check_desc(d, false);
     if (st != QP_OK) return st;
+    if ((st = need_fp16_scales(d, "qpack_quantize")) != QP_OK) return st;
     if (!w || !aligned(w, 4)) return fail(QP_ERR_INVALID_ARG, "w NULL or not 4-byte aligned");
     if (ldw < d->k || ldw % 2 != 0) return fail(QP_ERR_INVALID_ARG, "ldw=%lld must be >= k and even", (long long)ldw);
     if (!codes || !aligned(codes, 2)) return fail(QP_ERR_INVALID_ARG, "codes NULL or not 2-byte aligned");
@@ -231,6 +254,33 @@ qp_status qpack_quantize(const qp_weight_desc *d, const uint16_t *w, int64_t ldw
     return device(launch_quantize(d->bits, d->zero_mode == QP_ZERO_MIDPOINT, w, ldw, d->n, d->k, d->group_size, kout, codes, scales,
                                   zeros, csr_rowptr, csr_col, csr_val, ws, S(stream)),
                   "qpack_quantize");
+}
+
+qp_status qpack_quantize_fp8(const qp_weight_desc *d, const uint16_t *w, int64_t ldw, uint8_t *codes,
+                             uint8_t *scales8, uint8_t *zeros, float *row_factors, uint16_t *fb_scales,
+                             int64_t fb_stride, int32_t *counts, void *stream)
+{
+    qp_status st = check_desc(d, false);
+    if (st != QP_OK) return st;
+    if (d->scale_format != QP_SCALE_FP8) return fail(QP_ERR_INVALID_ARG, "scale_format must be QP_SCALE_FP8");
+    if (!w || !aligned(w, 4)) return fail(QP_ERR_INVALID_ARG, "w NULL or not 4-byte aligned");
+    if (ldw < d->k || ldw % 2 != 0) return fail(QP_ERR_INVALID_ARG, "ldw=%lld must be >= k and even", (long long)ldw);
+    if (!codes || !aligned(codes, 2)) return fail(QP_ERR_INVALID_ARG, "codes NULL or not 2-byte aligned");
+    if (!scales8 || !row_factors || !counts) return fail(QP_ERR_INVALID_ARG, "scales8/row_factors/counts NULL");
+    if (!aligned(row_factors, 4) || !aligned(counts, 4))
+        return fail(QP_ERR_INVALID_ARG, "row_factors/counts not 4-byte aligned");
+    if (!zeros && d->zero_mode == QP_ZERO_STORED) return fail(QP_ERR_INVALID_ARG, "zeros NULL");
+    if (fb_stride < 0 || fb_stride > 128) return fail(QP_ERR_INVALID_ARG, "fb_stride=%lld not in 0..128", (long long)fb_stride);
+    if (fb_stride > 0 && (!fb_scales || !aligned(fb_scales, 2)))
+        return fail(QP_ERR_INVALID_ARG, "fb_scales NULL or not 2-byte aligned");
+    if (d->k / d->group_size > quantize_fp8_max_groups())
+        return fail(QP_ERR_UNSUPPORTED, "k/group_size=%lld above %lld groups per row", (long long)(d->k / d->group_size),
+                    (long long)quantize_fp8_max_groups());
+    if (d->n > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "n above 2^31 - 1 rows");
+    return device(launch_quantize_fp8(d->bits, d->zero_mode == QP_ZERO_MIDPOINT, w, ldw, d->n, d->k, d->group_size, codes,
+                                      scales8, d->zero_mode == QP_ZERO_MIDPOINT ? nullptr : zeros, row_factors,
+                                      fb_scales, fb_stride, counts, S(stream)),
+                  "qpack_quantize_fp8");
 }
 
 qp_status qpack_pack(const qp_weight_desc *d, const uint8_t *codes, void *packed, void *stream)
@@ -290,6 +340,12 @@ static qp_status gemv_problem(const qp_weight_desc *d, const qp_weight *w, const
     p->zmid = zero_pair(d);
     p->gs = d->group_size;
     p->zrow = d->zero_mode == QP_ZERO_PACKED ? (int32_t)zero_row_bytes(d) : 0;
+    if (d->scale_format == QP_SCALE_FP8) {
+        p->sc8 = w->scales8;
+        p->rowf = w->row_factors;
+        p->fb = w->fb_scales;
+        p->fb_stride = (int32_t)w->fb_stride;
+    }
     if (w->nnz > 0) {
         p->rowptr = w->csr_rowptr;
         p->col = w->csr_col;
@@ -327,6 +383,7 @@ qp_status qlinear_gemv_batch(const qp_gemv_problem *problems, int32_t count, voi
         const qp_gemv_problem &q = problems[i];
         qp_status st = gemv_problem(&q.desc, &q.w, q.x, q.ldx, q.m, q.y, q.ldy, &b.p[i]);
         if (st != QP_OK) return st;
+        if ((st = need_fp16_scales(&q.desc, "qlinear_gemv_batch")) != QP_OK) return st;
         if (b.p[i].gs != b.p[0].gs) return fail(QP_ERR_UNSUPPORTED, "one group size per batch");
         if ((b.p[i].zrow != 0) != (b.p[0].zrow != 0))
             return fail(QP_ERR_UNSUPPORTED, "packed and byte zero points in one batch");
@@ -351,6 +408,7 @@ qp_status qlinear_gemm(const qp_weight_desc *d, const qp_weight *w, const uint16
 {
     qp_status st = check_desc(d, true);
     if (st != QP_OK) return st;
+    if ((st = need_fp16_scales(d, "qlinear_gemm")) != QP_OK) return st;
     if ((st = check_weight(d, w, true)) != QP_OK) return st;
     if ((st = check_xy(d, x, ldx, m, y, ldy, d->n, 4)) != QP_OK) return st;
     if (m > (1LL << 24)) return fail(QP_ERR_INVALID_ARG, "m too large");
@@ -418,6 +476,7 @@ qp_status qlinear_grouped_gemm(const qp_weight_desc *d, const qp_weight *experts
 {
     qp_status st = check_desc(d, true);
     if (st != QP_OK) return st;
+    if ((st = need_fp16_scales(d, "qlinear_grouped_gemm")) != QP_OK) return st;
     if (!experts) return fail(QP_ERR_INVALID_ARG, "experts NULL");
     if (n_experts < 1 || n_experts > kMaxExperts) return fail(QP_ERR_INVALID_ARG, "n_experts=%d not in 1..64", n_experts);
     for (int e = 0; e < n_experts; ++e)
@@ -483,6 +542,7 @@ qp_status qmoe_ffn(const qp_weight_desc *dgu, const qp_weight *gate_up, const qp
     qp_status st;
     if ((st = check_desc(dgu, true)) != QP_OK) return st;
     if ((st = check_desc(dd, true)) != QP_OK) return st;
+    if ((st = need_fp16_scales(dgu, "qmoe_ffn")) != QP_OK || (st = need_fp16_scales(dd, "qmoe_ffn")) != QP_OK) return st;
     if (dgu->bits != dd->bits) return fail(QP_ERR_UNSUPPORTED, "gate/up and down must share the bit width");
     const int64_t d_model = dgu->k, d_ff = dgu->n / 2;
     if (dgu->n % 32 != 0 || dd->n != d_model || dd->k != d_ff)
@@ -659,6 +719,7 @@ qp_status qlinear_gemm_a8(const qp_weight_desc *d, const qp_weight *w, const int
 {
     qp_status st = check_desc(d, true);
     if (st != QP_OK) return st;
+    if ((st = need_fp16_scales(d, "qlinear_gemm_a8")) != QP_OK) return st;
     if (d->group_size != kGroup) return fail(QP_ERR_UNSUPPORTED, "the int8 GEMM is built for groups of 128");
     if ((st = check_weight(d, w, false)) != QP_OK) return st;
     if (w->nnz > 0) return fail(QP_ERR_UNSUPPORTED, "outliers are not applied on int8 activations");

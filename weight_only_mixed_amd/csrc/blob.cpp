@@ -93,7 +93,7 @@ struct Sections {
 // Section sizes and offsets, or false if the descriptor is not a valid weight.
 bool sections(const qp_weight_desc *d, int64_t nnz, Sections *s)
 {
-    if (nnz < 0) return false;
+    if (nnz < 0 || d->scale_format != QP_SCALE_FP16) return false;
     const size_t pb = qp_packed_bytes(d);
     if (pb == 0 || nnz > d->n * d->k) return false;  // a valid desc keeps n*k <= 2^40: no overflow below
     s->n_packed = pb;
@@ -133,6 +133,7 @@ qp_status qp_blob_write(const qp_weight_desc *d, const qp_weight *w, void *blob,
 {
     if (!d || !w || !blob) return qp::fail(QP_ERR_INVALID_ARG, "qp_blob_write: NULL argument");
     Sections s;
+    if (d->scale_format != QP_SCALE_FP16) return qp::fail(QP_ERR_UNSUPPORTED, "qp_blob_write: the blob holds fp16 scales");
     if (!sections(d, w->nnz, &s)) return qp::fail(QP_ERR_INVALID_ARG, "qp_blob_write: invalid descriptor or nnz");
     if (blob_bytes < s.total)
         return qp::fail(QP_ERR_WORKSPACE, "qp_blob_write: blob needs %zu bytes, got %zu", s.total, blob_bytes);
@@ -182,7 +183,7 @@ qp_status qp_blob_parse(const void *blob, size_t blob_bytes, qp_weight_desc *des
         return qp::fail(QP_ERR_UNSUPPORTED, "qp_blob_parse: version %u (only %u is known)", get_u32(b + 4), kVersion);
     if (get_u32(b + 8) != kHeader || get_u32(b + 28) != 0 || get_u32(b + 60) != 0)
         return qp::fail(QP_ERR_INVALID_ARG, "qp_blob_parse: bad header size or reserved fields");
-    qp_weight_desc d;
+    qp_weight_desc d{};
     d.bits = (int32_t)get_u32(b + 12);
     d.group_size = (int32_t)get_u32(b + 16);
     d.layout = (int32_t)get_u32(b + 20);

@@ -300,6 +300,7 @@ extern "C" qp_status qlinear_gemv_host(const qp_weight_desc *d, const qp_weight 
         return qp::fail(QP_ERR_UNSUPPORTED, "qlinear_gemv_host reads the canonical layout");
     if (d->zero_mode == QP_ZERO_PACKED)
         return qp::fail(QP_ERR_UNSUPPORTED, "qlinear_gemv_host reads byte or implied zero points");
+    if (d->scale_format != QP_SCALE_FP16) return qp::fail(QP_ERR_UNSUPPORTED, "qlinear_gemv_host reads fp16 scales");
     if (m < 1 || m > 8) return qp::fail(QP_ERR_UNSUPPORTED, "qlinear_gemv_host handles 1 <= m <= 8 (m=%lld)", (long long)m);
     if (ldx < d->k || ldy < d->n) return qp::fail(QP_ERR_INVALID_ARG, "qlinear_gemv_host: ldx < k or ldy < n");
     if (!w->packed || !w->scales || (d->zero_mode == QP_ZERO_STORED && !w->zeros))

@@ -9,6 +9,12 @@
 // fp16 scale in fp32 (mixed-bit page, s4.2).  The outlier CSR is added in fp32 before the one
 // fp16 rounding of y (70B page, s2).
 //
+// Scale and zero-point storage is a template mode (ZP): kMetaByte -- fp16 scales with byte
+// (or implied) zero points; kMetaPacked -- fp16 scales with b-bit zero points; kMetaFp8 --
+// E4M3 scale bytes times a per-row fp32 factor, with an fp16 fallback list (mixed-bit page,
+// s2.3), and byte (or implied) zero points.  fp8 groups are accumulated with their E4M3 value
+// and the row sum is multiplied by the row factor once, after the k reduction.
+//
 // Matrix-core fragment layout (A = 16 weight rows x 32 k, B = 32 k x 16 activation rows):
 // lane l = 16*t + r supplies row r of A and column r of B for k-slots 8t..8t+7 and receives
 // D[4t + i][r], i = 0..3 (weight row 4t+i, activation row r).
@@ -16,6 +22,8 @@
 #include "unpack.h"
 
 namespace qp {
+
+enum { kMetaByte = 0, kMetaPacked = 1, kMetaFp8 = 2 };
 
 // tot += sum over the tile's NG groups c of s_c * (A[j] . X[j] for the 8/NG blocks j of c),
 // groups kept apart and added in group order.  sc[i][c / 2] holds the fp16 scales of groups
@@ -39,6 +47,34 @@ __device__ __forceinline__ void mma_tile(const h8 *A, const h8 *X, const uint32_
             tot[i] = __builtin_fmaf((c & 1) ? hi_h(sc[i][c / 2]) : lo_h(sc[i][c / 2]), acc[c][i], tot[i]);
 }
 
+// As mma_tile, with the groups' scales as fp32 values: scf[i][c] for row 4t + i, group c.
+template <int NG>
+__device__ __forceinline__ void mma_tile_f(const h8 *A, const h8 *X, const float (&scf)[4][NG], f4 &tot)
+{
+    constexpr int JB = 8 / NG;
+    const f4 z = {0.f, 0.f, 0.f, 0.f};
+    f4 acc[NG];
+#pragma unroll
+    for (int c = 0; c < NG; ++c) acc[c] = mfma16(A[c * JB], X[c * JB], z);
+#pragma unroll
+    for (int jj = 1; jj < JB; ++jj)
+#pragma unroll
+        for (int c = 0; c < NG; ++c) acc[c] = mfma16(A[c * JB + jj], X[c * JB + jj], acc[c]);
+#pragma unroll
+    for (int c = 0; c < NG; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tot[i] = __builtin_fmaf(scf[i][c], acc[c][i], tot[i]);
+}
+
+// Two E4M3 bytes (the low or high half of w) as fp32.
+template <bool HI>
+__device__ __forceinline__ void e4m3_pair(uint32_t w, float &a, float &b)
+{
+    const auto v = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+    a = v[0];
+    b = v[1];
+}
+
 // ---- decode GEMV: one workgroup per 16-row block, NW waves take its k-tiles round-robin --
 //
 // Decode is latency- and VALU-bound at these sizes (a 4096 x 4096 layer is a few MB).  Every
@@ -54,7 +90,7 @@ __device__ __forceinline__ void mma_tile(const h8 *A, const h8 *X, const uint32_
 
 struct GemvBufs {
     rsrc_t w, sc, zr, x;
-    uint32_t zrow;  // bytes per row of b-bit zero points (ZP); 0 for byte zero points
+    uint32_t zrow;  // bytes per row of b-bit zero points (kMetaPacked); 0 otherwise
     uint32_t vw, vw8, vz, vs, vx;  // per-lane offsets
     int64_t G;
 };
@@ -65,16 +101,16 @@ struct GemvBufs {
 // NG = 8 one 16-byte DMA.  Zero points: NG = 2 the aligned 4-byte word holding the pair,
 // NG = 4 one 4-byte DMA, NG = 8 two (groups 0-3, 4-7); b-bit zero points (ZP) the 32-bit
 // words of the row's bit stream that cover the tile's NG fields (two, or three when
-// NG*B + 31 > 64).
-template <int B, int MX, int GS, int ZP = 0>
+// NG*B + 31 > 64).  fp8 scale bytes are staged as byte zero points are.
+template <int B, int MX, int GS, int ZP = kMetaByte>
 struct RingSlot {
     static constexpr int NG = kTileK / GS;
-    static constexpr int kScOps = NG == 4 ? 2 : 1;
-    static constexpr int kZrOps = ZP ? (NG * B + 62) / 32 : (NG == 8 ? 2 : 1);
+    static constexpr int kScOps = ZP == kMetaFp8 ? (NG == 8 ? 2 : 1) : (NG == 4 ? 2 : 1);
+    static constexpr int kZrOps = ZP == kMetaPacked ? (NG * B + 62) / 32 : (NG == 8 ? 2 : 1);
     static constexpr int kCodes = 512 * B;           // packed tile
     static constexpr int kX = kCodes;                 // activation rows, 512 B each, 2 per DMA
     static constexpr int kSc = kX + 1024 * MX;
-    static constexpr int kZr = kSc + (NG == 8 ? 1024 : 256 * kScOps);
+    static constexpr int kZr = kSc + (NG == 8 && ZP != kMetaFp8 ? 1024 : 256 * kScOps);
     static constexpr int kBytes = kZr + 256 * kZrOps;
     static constexpr int kLoads = B / 2 + 2 * (B & 1) + MX + kScOps + kZrOps;  // DMA instructions per tile
     static_assert(NG == 2 || NG == 4 || NG == 8, "groups of 128, 64 or 32");
@@ -108,7 +144,21 @@ __device__ __forceinline__ void ring_issue(const GemvBufs &bf, int64_t kt, int l
         dma16(bf.x, slot + S::kX + 1024 * q, (uint32_t)(row * ldx * 2) + xk + 16 * (lane & 31));
     }
     const uint32_t g0 = (uint32_t)(lane * bf.G + NG * kt);  // this lane's row, the tile's first group
-    if constexpr (ZP) {
+    if constexpr (ZP == kMetaFp8) {  // scale bytes, then zero points, each as byte zero points
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const rsrc_t &rs = e == 0 ? bf.sc : bf.zr;
+            uint8_t *dst = slot + (e == 0 ? S::kSc : S::kZr);
+            if constexpr (NG == 2) {
+                dma4(rs, dst, g0 & ~3u);
+            } else if constexpr (NG == 4) {
+                dma4(rs, dst, g0);
+            } else {
+                dma4(rs, dst, g0);
+                dma4(rs, dst + 256, g0 + 4);
+            }
+        }
+    } else if constexpr (ZP == kMetaPacked) {
         // the words of this lane's row stream from the one holding bit NG*kt*B on
         const uint32_t zo = lane * bf.zrow + 4 * (uint32_t)((NG * kt * B) >> 5);
 #pragma unroll
@@ -158,8 +208,11 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
     GemvBufs bf;
     bf.G = G;
     bf.w = make_rsrc(a.w.packed + rb * KT * (512 * B), KT * (512 * B));
-    bf.sc = make_rsrc(a.w.scales + rb * kTileN * G, kTileN * G * 2);
-    if constexpr (ZP) {
+    if constexpr (ZP == kMetaFp8)
+        bf.sc = make_rsrc(a.sc8 + rb * kTileN * G, kTileN * G);
+    else
+        bf.sc = make_rsrc(a.w.scales + rb * kTileN * G, kTileN * G * 2);
+    if constexpr (ZP == kMetaPacked) {
         bf.zrow = (uint32_t)a.zrow;
         bf.zr = make_rsrc(a.w.zeros + rb * kTileN * a.zrow, kTileN * a.zrow);
     } else {
@@ -177,6 +230,11 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
 #pragma unroll
     for (int j = 0; j < 8; ++j) X[j] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
     f4 tot = {0.f, 0.f, 0.f, 0.f};
+    float F[4] = {1.f, 1.f, 1.f, 1.f};  // fp8: the factors of rows 4t + i
+    if constexpr (ZP == kMetaFp8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) F[i] = a.rowf[rb * kTileN + 4 * t + i];
+    }
     // Tile i sits in slot i % 2 and the DMA of tile i+1 runs while tile i is consumed.  The two
     // slots are separate LDS arrays, named statically (the loop is unrolled by two), so the
     // compiler can tell that a slot's reads never overlap the DMA in flight into the other;
@@ -219,11 +277,59 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
         // scales of rows 4t..4t+3 (two groups per word) and zero points of row r
         uint32_t sc[4][NG / 2];
         uint32_t zw[NG == 8 ? 2 : 1];
-        if constexpr (NG == 2) {
+        float scf[4][NG];  // fp8: E4M3 values of rows 4t..4t+3
+        if constexpr (ZP == kMetaFp8) {
+            // scale bytes of row 4t+i: NG = 2 the pair inside the row's aligned word, else one
+            // word (NG = 4) or two (NG = 8) per row
+            uint32_t sw[4][NG == 8 ? 2 : 1];
+            uint32_t esc = 0;
+            if constexpr (NG == 2) {
+                const u4 v = *(const u4 *)(slot + S::kSc + 16 * t);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t par = (uint32_t)(((4 * t + i) * G + 2 * kt) & 3);
+                    sw[i][0] = (v[i] >> (8 * par)) & 0xFFFF;
+                    esc |= sw[i][0];
+                    e4m3_pair<false>(sw[i][0], scf[i][0], scf[i][1]);
+                }
+            } else {
+#pragma unroll
+                for (int h = 0; h < NG / 4; ++h) {
+                    const u4 v = *(const u4 *)(slot + S::kSc + 256 * h + 16 * t);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        sw[i][h] = v[i];
+                        esc |= v[i];
+                        e4m3_pair<false>(v[i], scf[i][4 * h], scf[i][4 * h + 1]);
+                        e4m3_pair<true>(v[i], scf[i][4 * h + 2], scf[i][4 * h + 3]);
+                    }
+                }
+            }
+            if (esc & 0x80808080u) {
+                // a fallback group (rare): its fp16 scale from the row's list, divided by the
+                // row factor that multiplies the row sum at the end; an index past the list
+                // (malformed bytes) reads its last entry, or 0 for an empty list
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int c = 0; c < NG; ++c) {
+                        const uint32_t b = (sw[i][c / 4] >> (8 * (c % 4))) & 0xFF;
+                        if (b & 0x80) {
+                            const int j = min((int)(b & 0x7F), a.fb_stride - 1);
+                            const int64_t row = rb * kTileN + 4 * t + i;
+                            scf[i][c] = j >= 0 ? h_f(a.fb[row * a.fb_stride + j]) / F[i] : 0.0f;
+                        }
+                    }
+            }
+            const uint32_t zpar = (uint32_t)((r * G + NG * kt) & 3);
+            if constexpr (NG == 2) zw[0] = *(const uint16_t *)(slot + S::kZr + 4 * r + zpar);
+            else zw[0] = *(const uint32_t *)(slot + S::kZr + 4 * r);
+            if constexpr (NG == 8) zw[1] = *(const uint32_t *)(slot + S::kZr + 256 + 4 * r);
+        } else if constexpr (NG == 2) {
             const u4 v = *(const u4 *)(slot + S::kSc + 16 * t);
 #pragma unroll
             for (int i = 0; i < 4; ++i) sc[i][0] = v[i];
-            if constexpr (!ZP) {
+            if constexpr (ZP == kMetaByte) {
                 const uint32_t zpar = (uint32_t)((r * G + 2 * kt) & 3);
                 zw[0] = *(const uint16_t *)(slot + S::kZr + 4 * r + zpar);
             }
@@ -234,7 +340,7 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
                 sc[i][0] = v0[i];
                 sc[i][1] = v1[i];
             }
-            if constexpr (!ZP) zw[0] = *(const uint32_t *)(slot + S::kZr + 4 * r);
+            if constexpr (ZP == kMetaByte) zw[0] = *(const uint32_t *)(slot + S::kZr + 4 * r);
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -244,13 +350,13 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
                 sc[i][2] = v[2];
                 sc[i][3] = v[3];
             }
-            if constexpr (!ZP) {
+            if constexpr (ZP == kMetaByte) {
                 zw[0] = *(const uint32_t *)(slot + S::kZr + 4 * r);
                 zw[1] = *(const uint32_t *)(slot + S::kZr + 256 + 4 * r);
             }
         }
         GroupConst<B> gc[NG];
-        if constexpr (ZP) {
+        if constexpr (ZP == kMetaPacked) {
             // fields c = 0 .. NG-1 at bits sh + c*B of the words fetched from the row stream
             uint32_t zp[3] = {0u, 0u, 0u};
 #pragma unroll
@@ -269,7 +375,10 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
         }
         h8 A[8];
         unpack_chunk_groups<B, NG>(d, gc, A);
-        mma_tile<NG>(A, X, sc, tot);
+        if constexpr (ZP == kMetaFp8)
+            mma_tile_f<NG>(A, X, scf, tot);
+        else
+            mma_tile<NG>(A, X, sc, tot);
     }
     wait_vm<0>();  // drain the tiles issued past the end before the workgroup's LDS is released
 
@@ -279,6 +388,10 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
     f4 s = red[0][lane];
 #pragma unroll
     for (int w = 1; w < NW; ++w) s += red[w][lane];
+    if constexpr (ZP == kMetaFp8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] *= F[i];
+    }
     if (a.rowptr) {
         const uint16_t *xrow = a.x + r * a.ldx;
 #pragma unroll
@@ -380,7 +493,8 @@ static hipError_t gemv_zp(const GemvProblem &a, hipStream_t st)
 
 hipError_t launch_gemv(const GemvProblem &a, hipStream_t st)
 {
-    return a.zrow ? gemv_zp<1>(a, st) : gemv_zp<0>(a, st);
+    if (a.sc8) return gemv_zp<kMetaFp8>(a, st);
+    return a.zrow ? gemv_zp<kMetaPacked>(a, st) : gemv_zp<kMetaByte>(a, st);
 }
 
 template <int MX, int GS, int ZP>
@@ -416,7 +530,7 @@ static hipError_t gemv_batch_zp(const GemvBatch &b, int64_t blocks, int m_max, h
 
 hipError_t launch_gemv_batch(const GemvBatch &b, int64_t blocks, int m_max, hipStream_t st)
 {
-    return b.p[0].zrow ? gemv_batch_zp<1>(b, blocks, m_max, st) : gemv_batch_zp<0>(b, blocks, m_max, st);
+    return b.p[0].zrow ? gemv_batch_zp<kMetaPacked>(b, blocks, m_max, st) : gemv_batch_zp<kMetaByte>(b, blocks, m_max, st);
 }
 
 }  // namespace qp

@@ -67,12 +67,22 @@ struct GemvProblem {
     int32_t gs;      // group size: 32, 64 or 128
     int32_t zrow;    // bytes per row of b-bit zero points (0: one byte per group)
     int64_t block0;  // batch: first workgroup of this problem
+    // fp8 scales (w.scales unused when sc8 is set): scale bytes [n][k/gs], row factors [n],
+    // fp16 fallback scales [n][fb_stride]
+    const uint8_t *sc8;
+    const float *rowf;
+    const uint16_t *fb;
+    int32_t fb_stride;
 };
 struct GemvBatch {
     GemvProblem p[kMaxGemvBatch];
     int32_t count;
 };
 hipError_t launch_gemv(const GemvProblem &p, hipStream_t st);
+int64_t quantize_fp8_max_groups();
+hipError_t launch_quantize_fp8(int bits, bool sym, const uint16_t *w, int64_t ldw, int64_t n, int64_t k, int gs,
+                               uint8_t *codes, uint8_t *sc8, uint8_t *zeros, float *factors, uint16_t *fb,
+                               int64_t fb_stride, int32_t *counts, hipStream_t st);
 hipError_t launch_gemv_batch(const GemvBatch &b, int64_t blocks, int m_max, hipStream_t st);
 
 // Dequant-GEMM on the matrix cores: a plain layer (ex[0], optional outliers) or a group of
