@@ -182,6 +182,13 @@ def measured_traffic(kernel: str):
     return None
 
 
+def launch_floor_us(torch, stream, reps: int = 200) -> float:
+    """Per-launch time of back-to-back dependent launches of a one-element fill kernel in one
+    graph, timed like the GEMV: what every launch costs before it reads a byte."""
+    t = torch.zeros(1, dtype=torch.int32, device="cuda")
+    return time_graph(torch, lambda i: t.zero_(), reps, stream) * 1e3
+
+
 def copy_gbps(torch, nbytes: int = 1 << 30, reps: int = 10) -> float:
     """Device-to-device copy bandwidth (read + write bytes / time) of torch's copy kernel."""
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -201,7 +208,9 @@ def copy_gbps(torch, nbytes: int = 1 << 30, reps: int = 10) -> float:
 
 def pmc_pass(q, torch, workloads):
     """A short eager sequence for counter collection: the headline 4-bit M=1 GEMV and every
-    (bits, M) GEMV of the sweep on four distinct weight copies each, the prefill GEMM twice (fp16 activations with
+    (bits, M) GEMV of the sweep on four distinct weight copies each, the four batched stages of
+    two Llama-7B stack layers (layer 5: 2-bit q/k/gate/up; layer 0: all 6-bit) on four copies
+    each, the prefill GEMM twice (fp16 activations with
     outliers, then int8 activations), decode attention over two copies of
     the 32K MHA quantized cache, and a 1 GiB copy twice (the copy is the calibration kernel:
     its bytes are known)."""
@@ -225,6 +234,26 @@ def pmc_pass(q, torch, workloads):
             for h in hs:
                 q.qlinear_gemv(d, h, x, K, m, y, N)
         torch.cuda.synchronize()
+    xs = {k: torch.from_numpy(workloads.activations_fp16(1, k, workloads.seed_for(3)).view(np.int16)).to(dev)
+          for k in (4096, 11008)}
+    for layer in (5, 0):
+        mats = {}
+        for nm in workloads.LLAMA_MATRICES:
+            n, k = workloads.STACK_SHAPES[nm]
+            b = workloads.stack_bits(layer, nm)
+            d, wt = quantize_pack(q, torch, workloads.weights_fp16(n, k, workloads.stack_matrix_seed(layer, nm)), b)
+            mats[nm] = (d, [clone_weight(torch, wt) for _ in range(4)], n, k)
+            del wt
+        ys = {nm: torch.empty((1, mats[nm][2]), dtype=torch.int16, device=dev) for nm in mats}
+        for stage in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+            for c in range(4):
+                q.qlinear_gemv_batch([q.gemv_problem(mats[nm][0], q.weight(mats[nm][1][c]["packed"],
+                                                                           mats[nm][1][c]["scales"],
+                                                                           mats[nm][1][c]["zeros"]),
+                                                     xs[mats[nm][3]], mats[nm][3], 1, ys[nm], mats[nm][2])
+                                      for nm in stage])
+            torch.cuda.synchronize()
+        del mats
     wp, _ = workloads.prefill_weights()
     dp, wt = quantize_pack(q, torch, wp, 4, workloads.PREFILL_OUTLIER_FRAC)
     hp = q.weight(wt["packed"], wt["scales"], wt["zeros"], wt["rowptr"], wt["col"], wt["val"], wt["nnz"])
@@ -739,6 +768,11 @@ def main():
                     frac=round(value / HBM_PEAK_GBS, 4), traffic=measured_traffic(kname),
                     kernel=kname, bytes_per_launch=step_bytes, avg_launch_us=round(ms_per_step * 1e3, 3))
     del g_full, g_rem
+    floor_us = launch_floor_us(torch, stream)
+    # the launch floor bounds a 4096x4096 launch: bytes / (floor + bytes at peak)
+    roofline["launch_floor_us"] = round(floor_us, 3)
+    roofline["frac_of_launch_bound"] = round(
+        value / (step_bytes / ((floor_us + step_bytes / HBM_PEAK_GBS / 1e3) * 1e-6) / 1e9), 4)
     extra = {"gemv_4096_4bit_m1_median5": gemv_line(q, torch, stream, d4, w4, step_bytes, x1, 1, y1, N)}
     del h4, keep4
 

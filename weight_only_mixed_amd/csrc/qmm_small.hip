@@ -417,12 +417,13 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvProblem a)
     gemv_block<B, NW, D, MX, GS, ZP>(a, blockIdx.x, &ring0[wv][0], &ring1[wv][0], red);
 }
 
-// Independent problems (mixed bit widths, one group size) in one launch: workgroup b serves
-// problem p with block0 <= b < block0 + n/16.  The ring slots are sized for 6-bit tiles.
-template <int NW, int D, int MX, int GS, int ZP>
+// Independent problems (mixed bit widths up to BM, one group size) in one launch: workgroup b
+// serves problem p with block0 <= b < block0 + n/16.  The ring slots are sized for BM-bit tiles
+// (smaller slots leave LDS for more workgroups per CU).
+template <int NW, int D, int MX, int GS, int ZP, int BM>
 __global__ __launch_bounds__(NW * 64) void gemv_batch_kernel(GemvBatch bt)
 {
-    constexpr int pitch = RingSlot<6, MX, GS, ZP>::kBytes;
+    constexpr int pitch = RingSlot<BM, MX, GS, ZP>::kBytes;
     __shared__ __attribute__((aligned(16))) uint8_t ring0[NW][pitch];
     __shared__ __attribute__((aligned(16))) uint8_t ring1[NW][pitch];
     __shared__ f4 red[NW][64];
@@ -437,10 +438,18 @@ __global__ __launch_bounds__(NW * 64) void gemv_batch_kernel(GemvBatch bt)
     uint8_t *s0 = &ring0[wv][0], *s1 = &ring1[wv][0];
     switch (a.bits) {
     case 2: gemv_block<2, NW, D, MX, GS, ZP>(a, rb, s0, s1, red); break;
-    case 3: gemv_block<3, NW, D, MX, GS, ZP>(a, rb, s0, s1, red); break;
-    case 4: gemv_block<4, NW, D, MX, GS, ZP>(a, rb, s0, s1, red); break;
-    case 5: gemv_block<5, NW, D, MX, GS, ZP>(a, rb, s0, s1, red); break;
-    default: gemv_block<6, NW, D, MX, GS, ZP>(a, rb, s0, s1, red); break;
+    case 3:
+        if constexpr (BM >= 3) gemv_block<3, NW, D, MX, GS, ZP>(a, rb, s0, s1, red);
+        break;
+    case 4:
+        if constexpr (BM >= 4) gemv_block<4, NW, D, MX, GS, ZP>(a, rb, s0, s1, red);
+        break;
+    case 5:
+        if constexpr (BM >= 5) gemv_block<5, NW, D, MX, GS, ZP>(a, rb, s0, s1, red);
+        break;
+    default:
+        if constexpr (BM >= 6) gemv_block<6, NW, D, MX, GS, ZP>(a, rb, s0, s1, red);
+        break;
     }
 }
 
@@ -497,40 +506,52 @@ hipError_t launch_gemv(const GemvProblem &a, hipStream_t st)
     return a.zrow ? gemv_zp<kMetaPacked>(a, st) : gemv_zp<kMetaByte>(a, st);
 }
 
-template <int MX, int GS, int ZP>
+template <int MX, int GS, int ZP, int BM>
 static hipError_t gemv_batch_mx(const GemvBatch &b, int64_t blocks, hipStream_t st)
 {
     if constexpr (MX >= 4) {
-        hipLaunchKernelGGL((gemv_batch_kernel<4, 2, MX, GS, ZP>), dim3((unsigned)blocks), dim3(256), 0, st, b);
+        hipLaunchKernelGGL((gemv_batch_kernel<4, 2, MX, GS, ZP, BM>), dim3((unsigned)blocks), dim3(256), 0, st, b);
     } else {
         if (blocks >= 512)
-            hipLaunchKernelGGL((gemv_batch_kernel<4, 2, MX, GS, ZP>), dim3((unsigned)blocks), dim3(256), 0, st, b);
+            hipLaunchKernelGGL((gemv_batch_kernel<4, 2, MX, GS, ZP, BM>), dim3((unsigned)blocks), dim3(256), 0, st, b);
         else
-            hipLaunchKernelGGL((gemv_batch_kernel<8, 2, MX, GS, ZP>), dim3((unsigned)blocks), dim3(512), 0, st, b);
+            hipLaunchKernelGGL((gemv_batch_kernel<8, 2, MX, GS, ZP, BM>), dim3((unsigned)blocks), dim3(512), 0, st, b);
     }
     return hipGetLastError();
 }
 
-template <int GS, int ZP>
+template <int GS, int ZP, int BM>
 static hipError_t gemv_batch_gs(const GemvBatch &b, int64_t blocks, int m_max, hipStream_t st)
 {
-    if (m_max <= 2) return gemv_batch_mx<1, GS, ZP>(b, blocks, st);
-    if (m_max <= 4) return gemv_batch_mx<2, GS, ZP>(b, blocks, st);
-    if (m_max <= 8) return gemv_batch_mx<4, GS, ZP>(b, blocks, st);
-    return gemv_batch_mx<8, GS, ZP>(b, blocks, st);
+    if (m_max <= 2) return gemv_batch_mx<1, GS, ZP, BM>(b, blocks, st);
+    if (m_max <= 4) return gemv_batch_mx<2, GS, ZP, BM>(b, blocks, st);
+    if (m_max <= 8) return gemv_batch_mx<4, GS, ZP, BM>(b, blocks, st);
+    return gemv_batch_mx<8, GS, ZP, BM>(b, blocks, st);
 }
 
-template <int ZP>
+template <int ZP, int BM>
 static hipError_t gemv_batch_zp(const GemvBatch &b, int64_t blocks, int m_max, hipStream_t st)
 {
-    if (b.p[0].gs == 32) return gemv_batch_gs<32, ZP>(b, blocks, m_max, st);
-    if (b.p[0].gs == 64) return gemv_batch_gs<64, ZP>(b, blocks, m_max, st);
-    return gemv_batch_gs<128, ZP>(b, blocks, m_max, st);
+    if (b.p[0].gs == 32) return gemv_batch_gs<32, ZP, BM>(b, blocks, m_max, st);
+    if (b.p[0].gs == 64) return gemv_batch_gs<64, ZP, BM>(b, blocks, m_max, st);
+    return gemv_batch_gs<128, ZP, BM>(b, blocks, m_max, st);
 }
 
+template <int BM>
+static hipError_t gemv_batch_bm(const GemvBatch &b, int64_t blocks, int m_max, hipStream_t st)
+{
+    return b.p[0].zrow ? gemv_batch_zp<kMetaPacked, BM>(b, blocks, m_max, st)
+                       : gemv_batch_zp<kMetaByte, BM>(b, blocks, m_max, st);
+}
+
+// Ring slots sized for the widest problem of the batch: 2, 4 or 6 bits.
 hipError_t launch_gemv_batch(const GemvBatch &b, int64_t blocks, int m_max, hipStream_t st)
 {
-    return b.p[0].zrow ? gemv_batch_zp<kMetaPacked>(b, blocks, m_max, st) : gemv_batch_zp<kMetaByte>(b, blocks, m_max, st);
+    int bm = 2;
+    for (int i = 0; i < b.count; ++i) bm = b.p[i].bits > bm ? b.p[i].bits : bm;
+    if (bm <= 2) return gemv_batch_bm<2>(b, blocks, m_max, st);
+    if (bm <= 4) return gemv_batch_bm<4>(b, blocks, m_max, st);
+    return gemv_batch_bm<6>(b, blocks, m_max, st);
 }
 
 }  // namespace qp
