@@ -140,7 +140,7 @@ typedef struct {
     const int32_t *csr_col;     /* [nnz] column k of each outlier, ascending within a row */
     const uint16_t *csr_val;    /* [nnz] fp16 value of each outlier */
     int64_t nnz;                /* number of outliers (0 if csr_rowptr is NULL) */
-    /* QP_SCALE_FP8 only (scales unused):                                                    */
+    /* QP_SCALE_FP8 only (scales unused; no outlier CSR: csr_rowptr NULL, nnz 0):          */
     const uint8_t *scales8;     /* [n][k/group_size] scale bytes, 4-byte aligned */
     const float *row_factors;   /* [n] fp32 factor of each row's E4M3 scales */
     const uint16_t *fb_scales;  /* [n][fb_stride] fp16 fallback scales (NULL if fb_stride is 0) */

@@ -372,6 +372,9 @@ def test_fp8_scale_validation():
     assert q.qlinear_gemv(f8, q.weight_fp8(FAKE, FAKE, FAKE, FAKE, 129), FAKE, 512, 1, FAKE, 256, **ok) == q.QP_ERR_INVALID_ARG
     assert q.qlinear_gemv(f8, q.weight_fp8(FAKE, FAKE + 1, FAKE, FAKE, 8), FAKE, 512, 1, FAKE, 256, **ok) == q.QP_ERR_INVALID_ARG
     assert q.qlinear_gemv(f8, good, FAKE, 512, 17, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
+    with_csr = q.weight_fp8(FAKE, FAKE, FAKE, FAKE, 8)
+    with_csr.csr_rowptr, with_csr.csr_col, with_csr.csr_val, with_csr.nnz = FAKE, FAKE, FAKE, 5
+    assert q.qlinear_gemv(f8, with_csr, FAKE, 512, 1, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
     # every other matmul refuses fp8 scales
     assert q.qlinear_gemv_batch([q.gemv_problem(f8, good, FAKE, 512, 1, FAKE, 256)], **ok) == q.QP_ERR_UNSUPPORTED
     assert q.qlinear_gemm(f8, good, FAKE, 512, 64, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED

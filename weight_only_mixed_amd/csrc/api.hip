@@ -95,6 +95,8 @@ static qp_status check_weight(const qp_weight_desc *d, const qp_weight *w, bool 
             return fail(QP_ERR_INVALID_ARG, "fb_stride=%lld not in 0..128", (long long)w->fb_stride);
         if (w->fb_stride > 0 && (!w->fb_scales || !aligned(w->fb_scales, 2)))
             return fail(QP_ERR_INVALID_ARG, "fb_scales NULL or not 2-byte aligned");
+        if (w->nnz != 0 || w->csr_rowptr)
+            return fail(QP_ERR_UNSUPPORTED, "fp8-scale weights carry no outlier CSR (qpack_quantize_fp8 holds none out)");
     } else if (!w->scales || !aligned(w->scales, 4)) {
         return fail(QP_ERR_INVALID_ARG, "scales NULL or not 4-byte aligned");
     }
