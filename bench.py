@@ -528,7 +528,8 @@ def bench_prefill(q, torch, workloads, stream):
 
 def bench_prefill_variants(q, torch, workloads, stream):
     """The prefill GEMM (M=512, K=8192, N=28672, no outliers) for the metadata variants of the
-    mixed-bit page (s2.3): groups of 64 and 32, symmetric groups, zero points in b bits."""
+    mixed-bit page (s2.3): groups of 64 and 32, symmetric groups, zero points in b bits, fp8
+    scales with an fp16 fallback."""
     dev = torch.device("cuda")
     wp, _ = workloads.prefill_weights()
     Mp, Kp, Np = workloads.PREFILL_M, workloads.PREFILL_K, workloads.PREFILL_N
@@ -549,6 +550,15 @@ def bench_prefill_variants(q, torch, workloads, stream):
         key = f"b{bits}_g{g}" + ("_sym" if sym else "") + ("_bbit_zeros" if packed else "")
         out[key] = dict(us=round(ms * 1e3, 2), TFLOPs=round(tf, 1), frac_mfma_peak=round(tf / MFMA_F16_PEAK_TFLOPS, 4))
         del wt, h, z
+    for bits, g, sym in ((2, 32, True), (4, 128, False)):  # fp8 scales with an fp16 fallback
+        d, wt = quantize_pack_fp8(q, torch, wp, bits, g, sym)
+        h = q.weight_fp8(wt["packed"], wt["sc8"], wt["factors"], wt["fb"], wt["fb"].shape[1], wt["zeros"])
+        ms = time_graph(torch, lambda i: q.qlinear_gemm(d, h, xp, Kp, Mp, yp, Np, None, 0), 10, stream)
+        tf = 2 * Mp * Np * Kp / (ms * 1e-3) / 1e12
+        out[f"b{bits}_g{g}" + ("_sym" if sym else "") + "_fp8_scales"] = dict(
+            us=round(ms * 1e3, 2), TFLOPs=round(tf, 1), frac_mfma_peak=round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+            fallback_groups=wt["fallbacks"])
+        del wt, h
     del xp, yp
     return out
 

@@ -109,9 +109,10 @@ enum { QP_ZERO_STORED = 0, QP_ZERO_MIDPOINT = 1, QP_ZERO_PACKED = 2 };
  *                  - bit 7 clear: an E4M3 value (OCP 8-bit float: 4-bit exponent, bias 7, 3-bit
  *                    mantissa; 0x7F is NaN); the scale is row_factors[n] times that value;
  *                  - bit 7 set: the scale is the fp16 fb_scales[n * fb_stride + (byte & 0x7F)].
- *                 Written by qpack_quantize_fp8; read by qlinear_gemv (byte or implied zero
- *                 points).  The other matmuls, qlinear_gemv_batch, qlinear_gemv_host and
- *                 qp_blob_write return QP_ERR_UNSUPPORTED for it (qp_blob_bytes 0). */
+ *                 Written by qpack_quantize_fp8; read by qlinear_gemv and qlinear_gemm (byte or
+ *                 implied zero points).  The grouped GEMM, the MoE FFN, qlinear_gemm_a8,
+ *                 qlinear_gemv_batch, qlinear_gemv_host and qp_blob_write return
+ *                 QP_ERR_UNSUPPORTED for it (qp_blob_bytes 0). */
 enum { QP_SCALE_FP16 = 0, QP_SCALE_FP8 = 1 };
 
 /* Shape and format of one quantized matrix W[n][k]. */
@@ -270,9 +271,11 @@ qp_status qlinear_gemv_batch(const qp_gemv_problem *problems, int32_t count, voi
 
 /*
  * Prefill dequant-GEMM for any m >= 1 (tuned for m >= 64): same operands and result as
- * qlinear_gemv, for every group size (32, 64, 128) and zero mode.  Tiles of the packed
- * weight are unpacked in registers and fed to fp16 matrix cores with fp32 accumulation;
- * scales are applied per group in fp32.
+ * qlinear_gemv, for every group size (32, 64, 128), zero mode and scale format.  Tiles of the
+ * packed weight are unpacked in registers and fed to fp16 matrix cores with fp32 accumulation;
+ * scales are applied per group in fp32 (QP_SCALE_FP8: the row factor times the E4M3 value,
+ * rounded once in fp32 as the quantizer stores it, or the fallback's fp16 scale; a fallback
+ * index past the list reads its last slot, 0 for an empty list).
  *  workspace/ws_bytes  device scratch of at least qlinear_gemm_workspace_bytes(desc, m,
  *           w->nnz) bytes, 16-byte aligned, only needed when w carries outliers (NULL/0
  *           otherwise).  It holds x transposed (k * ldt fp16) and the fp32 outlier partial

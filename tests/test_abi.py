@@ -341,8 +341,8 @@ def test_int8_path_validation():
 
 def test_fp8_scale_validation():
     """QP_SCALE_FP8 (8-bit float scales with an fp16 fallback, mixed-bit page s2.3): only the
-    fp8 quantizer writes it and only the GEMV reads it; every other call refuses it, and the
-    fp8 calls check their buffers, before any launch."""
+    fp8 quantizer writes it and only the GEMV and the layer GEMM read it; every other call
+    refuses it, and the fp8 calls check their buffers, before any launch."""
     ok = dict(stream=0, check=False)
     f8 = q.desc(2, 256, 512, group_size=32, zero_mode=q.QP_ZERO_MIDPOINT, scale_format=q.QP_SCALE_FP8)
     fp16 = q.desc(2, 256, 512, group_size=32, zero_mode=q.QP_ZERO_MIDPOINT)
@@ -377,7 +377,10 @@ def test_fp8_scale_validation():
     assert q.qlinear_gemv(f8, with_csr, FAKE, 512, 1, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
     # every other matmul refuses fp8 scales
     assert q.qlinear_gemv_batch([q.gemv_problem(f8, good, FAKE, 512, 1, FAKE, 256)], **ok) == q.QP_ERR_UNSUPPORTED
-    assert q.qlinear_gemm(f8, good, FAKE, 512, 64, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
+    # the layer GEMM reads them too (validation only here: a malformed weight is refused)
+    assert q.qlinear_gemm(f8, q.weight_fp8(FAKE, None, FAKE, FAKE, 8), FAKE, 512, 64, FAKE, 256, **ok) == \
+        q.QP_ERR_INVALID_ARG
+    assert q.qlinear_gemm(f8, with_csr, FAKE, 512, 64, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
     assert q.qlinear_grouped_gemm(f8, [good], FAKE, 512, FAKE, FAKE, 10, 0, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
     f8_128 = q.desc(4, 256, 512, zero_mode=q.QP_ZERO_MIDPOINT, scale_format=q.QP_SCALE_FP8)
     assert q.qlinear_gemm_a8(f8_128, good, FAKE, FAKE, 4, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED

@@ -157,3 +157,110 @@ def test_gemv_fp8_layer_4096(m):
     r = oracle.linear_fp8(x, oracle.quantize_fp8(w, 2, 32, sym=True))
     y = gemv(GpuWeightFp8(w, 2, 32, True), x)
     assert rel_err(y, r) <= TOL, report(y, r)
+
+
+@pytest.mark.parametrize("m", (1, 2, 9, 16))
+def test_gemv_fp8_single_tile_and_block(m):
+    """The smallest shapes: one 16-row block and one 256-k tile (k = 256), every group size,
+    fallbacks in the last group of a row."""
+    for g in (32, 64, 128):
+        w = workloads.weights_fp16(16, 256, 2500 + g)
+        w[3, :g] *= np.float16(400.0)
+        w[3, 256 - g:] = (w[3, 256 - g:].astype(np.float32) * 0.01).astype(np.float16)
+        x = workloads.activations_fp16(m, 256, 2500 + g)
+        qd = oracle.quantize_fp8(w, 4, g, sym=False)
+        assert qd["counts"][3] >= 1 and qd["sc8"][3, -1] >= 0x80
+        y = gemv(GpuWeightFp8(w, 4, g, False), x)
+        r = oracle.linear_fp8(x, qd)
+        assert rel_err(y, r) <= TOL, report(y, r)
+
+
+def test_gemv_fp8_without_fallback_list():
+    """fb_stride = 0 (no list passed): weights without fallbacks run unchanged."""
+    w = workloads.weights_fp16(64, 1024, 2600)
+    x = workloads.activations_fp16(4, 1024, 2600)
+    qd = oracle.quantize_fp8(w, 3, 64, sym=True, fb_stride=0)
+    assert qd["counts"].sum() == 0
+    y = gemv(GpuWeightFp8(w, 3, 64, True, fb_stride=0), x)
+    r = oracle.linear_fp8(x, qd)
+    assert rel_err(y, r) <= TOL, report(y, r)
+
+
+def test_gemv_fp8_fallback_index_past_the_list_reads_the_last_slot():
+    """A row with more fallbacks than slots: bytes 0x80 | j with j >= fb_stride are malformed;
+    the GEMV reads the row's last slot for them, so the output equals the oracle's product with
+    those groups' scales replaced by that slot's (and stays inside the buffers)."""
+    g, n, k, m = 32, 16, 512, 3
+    w = workloads.weights_fp16(n, k, 2700, std=0.002)
+    w[5, :g] = workloads.weights_fp16(1, g, 2701, std=100.0)  # row 5: 15 fallbacks, 4 slots
+    x = workloads.activations_fp16(m, k, 2700)
+    x[:, :g] = 0
+    qd = oracle.quantize_fp8(w, 4, g, sym=False, fb_stride=4)
+    assert qd["counts"][5] == k // g - 1
+    fb_last = np.float32(oracle.half_value(int(qd["fb"][5, 3])))
+    sc = qd["scales_f32"].copy()
+    for gi in range(k // g):
+        b = int(qd["sc8"][5, gi])
+        if b & 0x80 and (b & 0x7F) >= 4:
+            sc[5, gi] = fb_last
+    r = oracle.linear_fp8(x, dict(qd, scales_f32=sc))
+    y = gemv(GpuWeightFp8(w, 4, g, False, fb_stride=4), x)
+    assert rel_err(y, r) <= TOL, report(y, r)
+
+
+def gemm(gw: GpuWeightFp8, x: np.ndarray) -> np.ndarray:
+    torch, q = gpu()
+    m, k = x.shape
+    y = torch.empty((m, gw.n), dtype=torch.int16, device="cuda")
+    q.qlinear_gemm(gw.desc, gw.handle(), to_dev_fp16(x), k, m, y, gw.n, None, 0)
+    torch.cuda.synchronize()
+    return from_dev_fp16(y)
+
+
+@pytest.mark.parametrize("g", (32, 64, 128))
+@pytest.mark.parametrize("bits", (2, 3, 4, 5, 6))
+@pytest.mark.parametrize("m", (17, 130))
+def test_gemm_fp8(g, bits, m):
+    """The prefill GEMM on fp8 scales: a partial last weight tile (n = 560), a ragged activation
+    block (m = 17) or a full one plus a ragged one (m = 130), fallback groups in five rows,
+    affine and symmetric groups."""
+    n, k = 560, 1536
+    for sym in (False, True):
+        print(f"gemm fp8 g={g} bits={bits} m={m} sym={sym}", flush=True)
+        w = workloads.weights_fp16(n, k, 2800 + bits + g)
+        plant_fallbacks(w, g, 2800 + bits, rows=(0, 5, 300, 513, 559))
+        x = workloads.activations_fp16(m, k, 2800 + bits)
+        qd = oracle.quantize_fp8(w, bits, g, sym=sym)
+        assert qd["counts"][300] == 3
+        y = gemm(GpuWeightFp8(w, bits, g, sym), x)
+        r = oracle.linear_fp8(x, qd)
+        assert rel_err(y, r) <= TOL, report(y, r)
+
+
+@pytest.mark.parametrize("g", (32, 128))
+def test_gemm_fp8_fallback_groups_alone(g):
+    """Even rows whose outputs come from fallback groups only (x zero over their one large
+    group), through the GEMM's fallback path."""
+    n, k, m = 256, 1024, 64
+    w = workloads.weights_fp16(n, k, 2900 + g, std=0.002)
+    w[0::2, :g] = workloads.weights_fp16(n // 2, g, 2901, std=100.0)
+    x = workloads.activations_fp16(m, k, 2900 + g)
+    x[:, :g] = 0
+    G = k // g
+    qd = oracle.quantize_fp8(w, 4, g, sym=False, fb_stride=G)
+    assert (qd["counts"][0::2] == G - 1).all()
+    y = gemm(GpuWeightFp8(w, 4, g, False, fb_stride=G), x)
+    r = oracle.linear_fp8(x, qd)
+    assert rel_err(y[:, 0::2], r[:, 0::2]) <= TOL, report(y[:, 0::2], r[:, 0::2])
+    assert rel_err(y, r) <= TOL, report(y, r)
+
+
+def test_gemm_fp8_layer_4096_prefill():
+    """The 4096 x 4096 layer at the page's 2.25-bit setting (2-bit symmetric groups of 32, fp8
+    scales), M = 512: every output against the oracle."""
+    w = workloads.layer_weights(2)
+    x = workloads.activations_fp16(512, 4096, workloads.seed_for(2))
+    qd = oracle.quantize_fp8(w, 2, 32, sym=True)
+    y = gemm(GpuWeightFp8(w, 2, 32, True), x)
+    r = oracle.linear_fp8(x, qd)
+    assert rel_err(y, r) <= TOL, report(y, r)

@@ -79,7 +79,7 @@ static qp_status check_desc(const qp_weight_desc *d, bool need_device)
 static qp_status need_fp16_scales(const qp_weight_desc *d, const char *who)
 {
     if (d->scale_format != QP_SCALE_FP16)
-        return fail(QP_ERR_UNSUPPORTED, "%s reads fp16 scales (fp8 scales: qpack_quantize_fp8, qlinear_gemv)", who);
+        return fail(QP_ERR_UNSUPPORTED, "%s reads fp16 scales (fp8 scales: qpack_quantize_fp8, qlinear_gemv, qlinear_gemm)", who);
     return QP_OK;
 }
 
@@ -410,7 +410,6 @@ qp_status qlinear_gemm(const qp_weight_desc *d, const qp_weight *w, const uint16
 {
     qp_status st = check_desc(d, true);
     if (st != QP_OK) return st;
-    if ((st = need_fp16_scales(d, "qlinear_gemm")) != QP_OK) return st;
     if ((st = check_weight(d, w, true)) != QP_OK) return st;
     if ((st = check_xy(d, x, ldx, m, y, ldy, d->n, 4)) != QP_OK) return st;
     if (m > (1LL << 24)) return fail(QP_ERR_INVALID_ARG, "m too large");
@@ -421,6 +420,12 @@ qp_status qlinear_gemm(const qp_weight_desc *d, const qp_weight *w, const uint16
     a.zmid = zero_pair(d);
     a.gs = d->group_size;
     a.zrow = d->zero_mode == QP_ZERO_PACKED ? (uint32_t)zero_row_bytes(d) : 0u;
+    if (d->scale_format == QP_SCALE_FP8) {  // check_weight has refused an outlier CSR
+        a.sc8 = w->scales8;
+        a.rowf = w->row_factors;
+        a.fb = w->fb_scales;
+        a.fb_stride = (int32_t)w->fb_stride;
+    }
     if (w->nnz > 0) {
         if (prod_over(d->k, gemm_xt_ld(m), 2, 0x7FFFFFFFLL) || prod_over(d->n, gemm_xt_ld(m), 4, 0x7FFFFFFFLL))
             return fail(QP_ERR_UNSUPPORTED, "m*k or m*n too large for the outlier add-back");

@@ -11,6 +11,9 @@ QP_GEMM_VARIANT_EXTERN(32, false)
 QP_GEMM_VARIANT_EXTERN(128, true)
 QP_GEMM_VARIANT_EXTERN(64, true)
 QP_GEMM_VARIANT_EXTERN(32, true)
+QP_GEMM_VARIANT_EXTERN(128, 2)
+QP_GEMM_VARIANT_EXTERN(64, 2)
+QP_GEMM_VARIANT_EXTERN(32, 2)
 }  // namespace gk
 
 // Position of activation row 16 mt + 4 t + i (of a 128-row block) in the transposed layouts:
@@ -89,7 +92,7 @@ __global__ __launch_bounds__(256) void outlier_spmm_kernel(const int32_t *rowptr
 
 int64_t gemm_xt_ld(int64_t m) { return (m + gk::GeoLayer::kMRows - 1) / gk::GeoLayer::kMRows * gk::GeoLayer::kMRows; }
 
-template <bool ZPK>
+template <int ZPK>
 static hipError_t gemm_zp(int bits, bool outl, const GemmArgs &a, hipStream_t st)
 {
     switch (a.gs) {
@@ -108,7 +111,9 @@ hipError_t launch_gemm(int bits, const GemmArgs &a, hipStream_t st)
         hipLaunchKernelGGL(outlier_spmm_kernel, dim3((unsigned)((a.n + 3) / 4), (unsigned)((a.ldxt + 511) / 512)),
                            dim3(256), 0, st, a.rowptr, a.col, a.val, a.xt, a.n, a.ldxt, a.spart);
     }
-    return a.zrow ? gemm_zp<true>(bits, a.rowptr != nullptr, a, st) : gemm_zp<false>(bits, a.rowptr != nullptr, a, st);
+    if (a.sc8) return gemm_zp<gk::kZpFp8>(bits, a.rowptr != nullptr, a, st);
+    return a.zrow ? gemm_zp<gk::kZpPacked>(bits, a.rowptr != nullptr, a, st)
+                  : gemm_zp<gk::kZpByte>(bits, a.rowptr != nullptr, a, st);
 }
 
 template <bool ZPK>

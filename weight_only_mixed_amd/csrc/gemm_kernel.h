@@ -121,7 +121,7 @@ __device__ __forceinline__ void dma_x_piece(const Bufs &bf, int64_t g, uint8_t *
 // steps, after every activation piece, so the end-of-step wait can leave them in flight).
 // Issuing everything at the start of a step instead stalls all eight waves together while
 // the address unit works through about 48 KB.
-template <int B, typename GE, int GS, bool ZPK, int PAR, int NMT, int MT>
+template <int B, typename GE, int GS, int ZPK, int PAR, int NMT, int MT>
 __device__ __forceinline__ void issue_tile(const Bufs &bf, const StepIO<PAR, GS> &io, int64_t G, int wv, int lane)
 {
     static_assert(NMT == GE::kMT && GE::kDmaX == NMT / 2, "one activation piece per tile of the first half");
@@ -139,7 +139,7 @@ __device__ __forceinline__ void issue_tile(const Bufs &bf, const StepIO<PAR, GS>
 }
 
 // All of a step's loads at once (ragged steps, whose tile count is not known at compile time).
-template <int B, typename GE, int GS, bool ZPK, int PAR>
+template <int B, typename GE, int GS, int ZPK, int PAR>
 __device__ __forceinline__ void issue_all(const Bufs &bf, const StepIO<PAR, GS> &io, int64_t G, int wv, int lane,
                                           int nmt)
 {
@@ -274,7 +274,7 @@ __device__ __forceinline__ void tile_units(std::integer_sequence<int, C...>, con
 // matrix-core units of tile MT (each scaling the unit before it), and a share of the next
 // group's unpack (its eight blocks spread evenly over the NMT tiles; row block 1's chunk is
 // read at tile NMT/2), interleaved so every wave keeps its matrix core and vector ALU busy.
-template <int B, typename GE, int GS, bool ZPK, int SH, int NH, int NMT, int MT>
+template <int B, typename GE, int GS, int ZPK, int SH, int NH, int NMT, int MT>
 __device__ __forceinline__ void full_tile(const h8 (&Acur)[kRBW][4], h8 (&Anxt)[kRBW][4], const SZ<GS> &zs,
                                           const SZ<GS> &zn, const GroupConst<B> (&gc)[kRBW], const uint8_t *xs,
                                           const uint8_t *wpart, int lane, uint32_t (&d)[2 * B], h8 (&X)[kXR][4],
@@ -304,7 +304,7 @@ __device__ __forceinline__ void full_tile(const h8 (&Acur)[kRBW][4], h8 (&Anxt)[
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int B, typename GE, int GS, bool ZPK, int SH, int NH, int NMT, int... MT>
+template <int B, typename GE, int GS, int ZPK, int SH, int NH, int NMT, int... MT>
 __device__ __forceinline__ void full_tiles(std::integer_sequence<int, MT...>, const h8 (&Acur)[kRBW][4],
                                            h8 (&Anxt)[kRBW][4], const SZ<GS> &zs, const SZ<GS> &zn,
                                            const GroupConst<B> (&gc)[kRBW], const uint8_t *xs, const uint8_t *wpart,
@@ -345,7 +345,7 @@ __device__ __forceinline__ void ragged_tile(std::integer_sequence<int, C...>, co
 // are issued (a step that unpacks a first group, NH = 0, is an odd step).  NMT > 0: the first
 // NMT 16-row activation tiles all hold rows; NMT == 0: nmt tiles hold rows (ragged), the loads
 // are issued at once and the next group is unpacked first.
-template <int B, typename GE, int GS, bool ZPK, int SH, int NH, int NMT>
+template <int B, typename GE, int GS, int ZPK, int SH, int NH, int NMT>
 __device__ __forceinline__ void group_step(const h8 (&Acur)[kRBW][4], h8 (&Anxt)[kRBW][4], const SZ<GS> &zs,
                                            const SZ<GS> &zn, const uint8_t *xs, const uint8_t *wpart, int lane,
                                            int nmt, f4 (&tot)[kRBW][GE::kMT], const Bufs &bf,
@@ -418,7 +418,7 @@ __device__ __forceinline__ void group_step(const h8 (&Acur)[kRBW][4], h8 (&Anxt)
 //  vmcnt(weight DMAs) after steps 2t+1.  Loads past the end are clamped to the last group or
 //  tile and land in slots that are not read again; the A operands unpacked from them are
 //  discarded.
-template <int B, typename GE, int GS, bool ZPK, int NMT>
+template <int B, typename GE, int GS, int ZPK, int NMT>
 //  The four slots reach the loop as restrict pointers: that tells the compiler that reads of
 //  one slot never touch a DMA in flight into another.  Without it (slots at run-time offsets
 //  in one array) it waits for every outstanding load, the weight DMA meant to run a step and a
@@ -516,7 +516,7 @@ __device__ __forceinline__ void plan_tile(const TilePlan &p, int64_t b, int64_t 
 // NMT > 0: every workgroup's first NMT 16-row activation tiles hold rows; NMT == 0: a ragged
 // workgroup (the last activation rows of a layer, or an expert's rows), tiles past its rows
 // are skipped.
-template <int B, int MODE, int NMT, typename GE, int GS, bool ZPK>
+template <int B, int MODE, int NMT, typename GE, int GS, int ZPK>
 __global__ __launch_bounds__(GE::kWaves * 64) __attribute__((amdgpu_waves_per_eu(GE::kWavesPerEU, GE::kWavesPerEU))) void gemm_kernel(
     GemmArgs a, TilePlan plan)
 {
@@ -575,6 +575,10 @@ __global__ __launch_bounds__(GE::kWaves * 64) __attribute__((amdgpu_waves_per_eu
     bf.zmid = a.zmid;
     bf.zrow = a.zrow;
     bf.kt0 = (uint32_t)kt0;
+    bf.rowf = make_rsrc(a.rowf, a.rowf ? a.n * 4 : 0);
+    bf.row0 = (uint32_t)(rb0 * kTileN);
+    bf.fb = make_rsrc(a.fb, a.fb ? a.n * a.fb_stride * 2 : 0);
+    bf.fbs = a.fb_stride;
     const int64_t zstride = a.zrow ? a.zrow : G;  // zero-point bytes per weight row
     // Activation rows are gathered per lane: the DMA source of a row past the workgroup's
     // rows lies past the buffer's range and reads zeros.
@@ -595,7 +599,10 @@ __global__ __launch_bounds__(GE::kWaves * 64) __attribute__((amdgpu_waves_per_eu
         // tiles kt0 .. kt0 + KTp - 1 of the block; scales and zero points are read from their
         // rows' starts (bf.kt0 offsets the tile index)
         bf.w[u] = make_rsrc(W.packed + (rb * KT + kt0) * (512 * B), in ? KTp * (512 * B) : 0);
-        bf.sc[u] = make_rsrc(W.scales + rb * kTileN * G, in ? kTileN * G * 2 : 0);
+        if constexpr (ZPK == kZpFp8)  // scale bytes
+            bf.sc[u] = make_rsrc(a.sc8 + rb * kTileN * G, in ? kTileN * G : 0);
+        else
+            bf.sc[u] = make_rsrc(W.scales + rb * kTileN * G, in ? kTileN * G * 2 : 0);
         bf.zr[u] = make_rsrc(W.zeros + rb * kTileN * zstride, in && !a.zmid ? kTileN * zstride : 0);
     }
 
@@ -635,13 +642,16 @@ __global__ __launch_bounds__(GE::kWaves * 64) __attribute__((amdgpu_waves_per_eu
     for (int u = 0; u < kRBW; ++u) {
         const int64_t rb = rb0 + u;
         if (rb >= NB) continue;
+        float rowf = 1.0f;  // fp8 scales: the weight row's factor
+        if constexpr (ZPK == kZpFp8) rowf = a.rowf[rb * kTileN + r];
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int64_t row = m0 + 16 * mt + 4 * t + i;
                 if (row >= mend) continue;
-                const float v = tot[u][mt][i];
+                float v = tot[u][mt][i];
+                if constexpr (ZPK == kZpFp8) v *= rowf;
                 if constexpr (MODE == kGroupRowsF32) {
                     ((float *)a.y)[(int64_t)blockIdx.z * a.ysplit + row * a.ldy + rb * kTileN + r] = v;
                 } else if constexpr (MODE == kGroupSwiglu) {
@@ -669,7 +679,7 @@ static inline TilePlan one_rect(int32_t nt0, int32_t nnt, int32_t m0, int32_t mt
 }
 
 // Whole 128-row activation tiles in one launch, a ragged last tile in another.
-template <int B, int MODE, int GS, bool ZPK>
+template <int B, int MODE, int GS, int ZPK>
 void gemm_launch(const GemmArgs &a, hipStream_t st)
 {
     using GE = GeoLayer;
@@ -685,16 +695,28 @@ void gemm_launch(const GemmArgs &a, hipStream_t st)
 
 // The layer GEMM for one group size and zero-point form (outl: accumulators seeded from the
 // outlier partial, which the caller has computed).
-template <int GS, bool ZPK>
+template <int GS, int ZPK>
 hipError_t gemm_main(int bits, bool outl, const GemmArgs &a, hipStream_t st)
 {
-    switch (bits) {
-    case 2: outl ? gemm_launch<2, kOutl, GS, ZPK>(a, st) : gemm_launch<2, kPlain, GS, ZPK>(a, st); break;
-    case 3: outl ? gemm_launch<3, kOutl, GS, ZPK>(a, st) : gemm_launch<3, kPlain, GS, ZPK>(a, st); break;
-    case 4: outl ? gemm_launch<4, kOutl, GS, ZPK>(a, st) : gemm_launch<4, kPlain, GS, ZPK>(a, st); break;
-    case 5: outl ? gemm_launch<5, kOutl, GS, ZPK>(a, st) : gemm_launch<5, kPlain, GS, ZPK>(a, st); break;
-    case 6: outl ? gemm_launch<6, kOutl, GS, ZPK>(a, st) : gemm_launch<6, kPlain, GS, ZPK>(a, st); break;
-    default: return hipErrorInvalidValue;
+    if constexpr (ZPK == kZpFp8) {  // fp8-scale weights carry no outliers
+        if (outl) return hipErrorInvalidValue;
+        switch (bits) {
+        case 2: gemm_launch<2, kPlain, GS, ZPK>(a, st); break;
+        case 3: gemm_launch<3, kPlain, GS, ZPK>(a, st); break;
+        case 4: gemm_launch<4, kPlain, GS, ZPK>(a, st); break;
+        case 5: gemm_launch<5, kPlain, GS, ZPK>(a, st); break;
+        case 6: gemm_launch<6, kPlain, GS, ZPK>(a, st); break;
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (bits) {
+        case 2: outl ? gemm_launch<2, kOutl, GS, ZPK>(a, st) : gemm_launch<2, kPlain, GS, ZPK>(a, st); break;
+        case 3: outl ? gemm_launch<3, kOutl, GS, ZPK>(a, st) : gemm_launch<3, kPlain, GS, ZPK>(a, st); break;
+        case 4: outl ? gemm_launch<4, kOutl, GS, ZPK>(a, st) : gemm_launch<4, kPlain, GS, ZPK>(a, st); break;
+        case 5: outl ? gemm_launch<5, kOutl, GS, ZPK>(a, st) : gemm_launch<5, kPlain, GS, ZPK>(a, st); break;
+        case 6: outl ? gemm_launch<6, kOutl, GS, ZPK>(a, st) : gemm_launch<6, kPlain, GS, ZPK>(a, st); break;
+        default: return hipErrorInvalidValue;
+        }
     }
     return hipGetLastError();
 }
@@ -705,7 +727,7 @@ hipError_t gemm_main(int bits, bool outl, const GemmArgs &a, hipStream_t st)
 // and the surplus workgroups return at once.  With at most 32 rows per expert on average the
 // small geometry runs (three 4-wave workgroups per CU instead of one 8-wave one), else the
 // layer's.
-template <int B, int MODE, typename GE, int GS, bool ZPK>
+template <int B, int MODE, typename GE, int GS, int ZPK>
 hipError_t grouped_geo(int n_experts, const GemmArgs &a, hipStream_t st)
 {
     constexpr int64_t T = GE::kMRows;
@@ -718,13 +740,13 @@ hipError_t grouped_geo(int n_experts, const GemmArgs &a, hipStream_t st)
                        dim3(GE::kWaves * 64), 0, st, a, plan);
     return hipGetLastError();
 }
-template <int B, int MODE, int GS, bool ZPK>
+template <int B, int MODE, int GS, int ZPK>
 hipError_t grouped_mode(int n_experts, const GemmArgs &a, hipStream_t st)
 {
     if (a.m <= (int64_t)GeoExperts::kMRows * n_experts) return grouped_geo<B, MODE, GeoExperts, GS, ZPK>(n_experts, a, st);
     return grouped_geo<B, MODE, GeoLayer, GS, ZPK>(n_experts, a, st);
 }
-template <int B, int GS, bool ZPK>
+template <int B, int GS, int ZPK>
 hipError_t grouped_bits(int epilogue, int n_experts, const GemmArgs &a, hipStream_t st)
 {
     switch (epilogue) {
@@ -734,15 +756,17 @@ hipError_t grouped_bits(int epilogue, int n_experts, const GemmArgs &a, hipStrea
     }
     return hipErrorInvalidValue;
 }
-template <int GS, bool ZPK>
+template <int GS, int ZPK>
 hipError_t grouped_main(int bits, int epilogue, int n_experts, const GemmArgs &a, hipStream_t st)
 {
-    switch (bits) {
-    case 2: return grouped_bits<2, GS, ZPK>(epilogue, n_experts, a, st);
-    case 3: return grouped_bits<3, GS, ZPK>(epilogue, n_experts, a, st);
-    case 4: return grouped_bits<4, GS, ZPK>(epilogue, n_experts, a, st);
-    case 5: return grouped_bits<5, GS, ZPK>(epilogue, n_experts, a, st);
-    case 6: return grouped_bits<6, GS, ZPK>(epilogue, n_experts, a, st);
+    if constexpr (ZPK != kZpFp8) {  // fp8 scales: the layer GEMM only
+        switch (bits) {
+        case 2: return grouped_bits<2, GS, ZPK>(epilogue, n_experts, a, st);
+        case 3: return grouped_bits<3, GS, ZPK>(epilogue, n_experts, a, st);
+        case 4: return grouped_bits<4, GS, ZPK>(epilogue, n_experts, a, st);
+        case 5: return grouped_bits<5, GS, ZPK>(epilogue, n_experts, a, st);
+        case 6: return grouped_bits<6, GS, ZPK>(epilogue, n_experts, a, st);
+        }
     }
     return hipErrorInvalidValue;
 }

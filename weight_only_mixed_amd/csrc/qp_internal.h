@@ -104,6 +104,11 @@ struct GemmArgs {
     int32_t gs;     // group size: 128, 64 or 32
     int32_t ksplit;  // grouped fp32 rows: k in ksplit equal parts (0 or 1: whole k); part s
     int64_t ysplit;  //   writes its partial rows at y + s * ysplit floats
+    // fp8 scales (layer GEMM only): scale bytes [n][k/gs], row factors [n], fallbacks [n][fb_stride]
+    const uint8_t *sc8;
+    const float *rowf;
+    const uint16_t *fb;
+    int32_t fb_stride;
     uint16_t *xt;   // workspace (outliers only): x transposed, [k][ldxt]
     float *spart;   // workspace (outliers only): fp32 outlier partial, [n][ldxt]
     int64_t ldxt;

@@ -37,7 +37,17 @@ struct Bufs {
     uint32_t zmid;            // 0: stored zero points; else the implied zero point (low byte) used instead
     uint32_t zrow;            // b-bit zero points: bytes per row
     uint32_t kt0;             // first k-tile of this workgroup's k range (metadata is indexed from k = 0)
+    // fp8 scales (ZPK == kZpFp8): row factors [n] and fp16 fallback lists [n][fbs] (buffer
+    // ranges), the wave's first weight row
+    rsrc_t rowf, fb;
+    int32_t fbs;              // fallback slots per row
+    uint32_t row0;
 };
+
+// Metadata forms (template parameter ZPK): fp16 scales with byte (or implied) zero points,
+// fp16 scales with b-bit zero points, E4M3 scale bytes (times a row factor, fp16 fallback
+// list) with byte (or implied) zero points.
+enum { kZpByte = 0, kZpPacked = 1, kZpFp8 = 2 };
 
 __device__ __forceinline__ void lds_dma16(rsrc_t r, uint8_t *lds, uint32_t voff, uint32_t soff)
 {
@@ -109,13 +119,13 @@ __device__ __forceinline__ bool zstraddles(int64_t kt) { return (zbit<B, GS>(kt)
 // Load p of kSZOps: row block p / 3, then its zero word 0, zero word 1 (the next four byte
 // zero points for g = 32; the second word of b-bit zero points that straddle one), the scales
 // (4, 8 or 16 bytes).  Each load writes one fixed word, so the metadata stays in registers.
-template <int B, int GS, bool ZPK>
+template <int B, int GS, int ZPK>
 __device__ __forceinline__ void load_sz_piece(const Bufs &bf, int64_t G, int64_t ktl, int lane, SZ<GS> &z, int p)
 {
     const int r = lane & 15, u = p / kSZPer, j = p % kSZPer;
     const int64_t kt = ktl + bf.kt0;
     if (j == 0) {
-        if constexpr (ZPK)
+        if constexpr (ZPK == kZpPacked)
             z.zz[u][0] = ld4(bf.zr[u], (uint32_t)r * bf.zrow, uni(4 * (zbit<B, GS>(kt) >> 5)));
         else if constexpr (GS == 32)
             z.zz[u][0] = ld4(bf.zr[u], (uint32_t)(r * G), uni(8 * kt));
@@ -124,11 +134,21 @@ __device__ __forceinline__ void load_sz_piece(const Bufs &bf, int64_t G, int64_t
         else
             z.zz[u][0] = ld2(bf.zr[u], (uint32_t)(r * G), uni(2 * kt));
     } else if (j == 1) {
-        if constexpr (ZPK) {
+        if constexpr (ZPK == kZpPacked) {
             // the second word lies inside the row whenever the fields reach it
             if (zstraddles<B, GS>(kt)) z.zz[u][1] = ld4(bf.zr[u], (uint32_t)r * bf.zrow, uni(4 * (zbit<B, GS>(kt) >> 5) + 4));
         } else if constexpr (GS == 32) {
             z.zz[u][1] = ld4(bf.zr[u], (uint32_t)(r * G), uni(8 * kt + 4));
+        }
+    } else if constexpr (ZPK == kZpFp8) {  // one scale byte per group
+        if constexpr (GS == 32) {
+            const u2 v = ld8(bf.sc[u], (uint32_t)(r * G), uni(8 * kt));
+            z.sc[u][0] = v[0];
+            z.sc[u][1] = v[1];
+        } else if constexpr (GS == 64) {
+            z.sc[u][0] = ld4(bf.sc[u], (uint32_t)(r * G), uni(4 * kt));
+        } else {
+            z.sc[u][0] = ld2(bf.sc[u], (uint32_t)(r * G), uni(2 * kt));
         }
     } else {
         if constexpr (GS == 32) {
@@ -147,7 +167,7 @@ __device__ __forceinline__ void load_sz_piece(const Bufs &bf, int64_t G, int64_t
     }
 }
 
-template <int B, int GS, bool ZPK>
+template <int B, int GS, int ZPK>
 __device__ __forceinline__ void load_sz(const Bufs &bf, int64_t G, int64_t kt, int lane, SZ<GS> &z)
 {
 #pragma unroll
@@ -200,10 +220,10 @@ __device__ __forceinline__ void dma_w_piece(const Bufs &bf, int64_t kt, uint8_t 
 // again at their first use, counting the weight DMA issued since (meant to stay in flight) as
 // older.  Branch-free: a branch here splits the k loop into blocks the scheduler cannot
 // interleave across.
-template <int B, int GS, bool ZPK>
+template <int B, int GS, int ZPK>
 __device__ __forceinline__ void retired(SZ<GS> &z, const Bufs &bf, int64_t ktl)
 {
-    if constexpr (ZPK) {
+    if constexpr (ZPK == kZpPacked) {
         const int64_t kt = ktl + bf.kt0;
         const uint32_t sh = zbit<B, GS>(kt) & 31;
         const bool two = zstraddles<B, GS>(kt);
@@ -227,11 +247,42 @@ __device__ __forceinline__ void retired(SZ<GS> &z, const Bufs &bf, int64_t ktl)
 #pragma unroll
     for (int u = 0; u < kRBW; ++u) {
         asm volatile("" : "+v"(z.zz[u][0]), "+v"(z.zz[u][1]));
+        // scale words holding data: fp16 pairs, or four E4M3 bytes per word
+        constexpr int kWords = ZPK == kZpFp8 ? (SZ<GS>::kNGT + 3) / 4 : SZ<GS>::kSW;
 #pragma unroll
-        for (int i = 0; i < SZ<GS>::kSW; ++i) asm volatile("" : "+v"(z.sc[u][i]));
+        for (int i = 0; i < kWords; ++i) asm volatile("" : "+v"(z.sc[u][i]));
         // one conversion per group and tile (each scale multiplies four outputs per tile)
+        if constexpr (ZPK == kZpFp8) {
+            // two E4M3 bytes per conversion (the row factor multiplies the row's sums once, in
+            // the epilogue); a byte with bit 7 set (rare) takes the fp16 scale from the row's
+            // fallback list over the row factor instead, its index clamped to the list
+            uint32_t esc = 0;
 #pragma unroll
-        for (int q = 0; q < SZ<GS>::kNGT; ++q) z.scf[u][q] = (q & 1) ? hi_h(z.sc[u][q >> 1]) : lo_h(z.sc[u][q >> 1]);
+            for (int q = 0; q < SZ<GS>::kNGT; q += 2) {
+                const uint32_t w = z.sc[u][q >> 2];
+                const auto v = (q & 2) ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true)
+                                       : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+                z.scf[u][q] = v[0];
+                z.scf[u][q + 1] = v[1];
+                esc |= w;
+            }
+            if (esc & 0x80808080u) {
+                const uint32_t row = bf.row0 + u * kTileN + (threadIdx.x & 15);
+#pragma unroll
+                for (int q = 0; q < SZ<GS>::kNGT; ++q) {
+                    const uint32_t b = (z.sc[u][q >> 2] >> (8 * (q & 3))) & 0xFF;
+                    if (b & 0x80) {
+                        const int j = min((int)(b & 0x7F), bf.fbs - 1);
+                        z.scf[u][q] = j >= 0 ? h_f(ld2(bf.fb, 2 * (row * (uint32_t)bf.fbs + (uint32_t)j))) *
+                                                   __builtin_amdgcn_rcpf(as_f(ld4(bf.rowf, 4 * row)))
+                                             : 0.0f;
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < SZ<GS>::kNGT; ++q) z.scf[u][q] = (q & 1) ? hi_h(z.sc[u][q >> 1]) : lo_h(z.sc[u][q >> 1]);
+        }
     }
 }
 
