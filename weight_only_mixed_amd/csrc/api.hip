@@ -456,6 +456,7 @@ static qp_status grouped_launch(const qp_weight_desc *d, const qp_weight *expert
                                 const int32_t *expert_offsets, int64_t rows, int32_t epilogue, void *y,
                                 int64_t ldy, int32_t ksplit, int64_t ysplit, void *stream)
 {
+    if ((d->n + 127) / 128 > 65535) return fail(QP_ERR_UNSUPPORTED, "grouped matmuls take n <= 8388480");
     GemmArgs a{};
     for (int e = 0; e < n_experts; ++e)
         a.ex[e] = {(const uint8_t *)experts[e].packed, experts[e].scales, experts[e].zeros};
