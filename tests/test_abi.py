@@ -193,6 +193,17 @@ def test_grouped_and_moe_validation():
                       stream=0, check=False) == q.QP_ERR_WORKSPACE
 
 
+def test_grouped_rejects_more_row_tiles_than_the_grid_holds():
+    """The grouped launch's second grid dimension counts 32-row tiles of routed rows: more than
+    65535 of them is refused before any launch."""
+    d = q.desc(4, 256, 256)
+    w = q.weight(FAKE, FAKE, FAKE)
+    rows = 65536 * 32
+    assert q.qlinear_grouped_gemm(d, [w], FAKE, 256, FAKE, FAKE, rows, q.QP_EPI_NONE, FAKE, 256, stream=0,
+                                  check=False) == q.QP_ERR_UNSUPPORTED
+    assert "65535" in q.last_error()
+
+
 def test_moe_ffn_rejects_intermediate_beyond_2gib():
     """The fp16 intermediate [tokens*topk][d_ff] is read through one 2 GiB buffer range: 65536
     routed rows at d_ff = 16384 (2 GiB exactly) must be refused before any launch."""

@@ -456,7 +456,9 @@ static qp_status grouped_launch(const qp_weight_desc *d, const qp_weight *expert
                                 const int32_t *expert_offsets, int64_t rows, int32_t epilogue, void *y,
                                 int64_t ldy, int32_t ksplit, int64_t ysplit, void *stream)
 {
-    if ((d->n + 127) / 128 > 65535) return fail(QP_ERR_UNSUPPORTED, "grouped matmuls take n <= 8388480");
+    // the launch's second grid dimension counts the occupied 32-row tiles (at most 65535)
+    if ((rows + (int64_t)n_experts * 31) / 32 > 65535)
+        return fail(QP_ERR_UNSUPPORTED, "grouped matmuls take at most 65535 32-row tiles of routed rows");
     GemmArgs a{};
     for (int e = 0; e < n_experts; ++e)
         a.ex[e] = {(const uint8_t *)experts[e].packed, experts[e].scales, experts[e].zeros};

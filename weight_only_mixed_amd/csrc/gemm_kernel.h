@@ -736,6 +736,7 @@ hipError_t grouped_geo(int n_experts, const GemmArgs &a, hipStream_t st)
     TilePlan plan{};
     plan.experts = n_experts;
     const unsigned parts = MODE == kGroupRowsF32 && a.ksplit > 1 ? (unsigned)a.ksplit : 1u;
+    if (items > 65535) return hipErrorInvalidValue;  // refused by the caller's validation
     hipLaunchKernelGGL((gemm_kernel<B, MODE, 0, GE, GS, ZPK>), dim3((unsigned)n_tiles, (unsigned)items, parts),
                        dim3(GE::kWaves * 64), 0, st, a, plan);
     return hipGetLastError();
