@@ -645,6 +645,26 @@ def bench_host_gemv(q, workloads, K, N):
         dt = float(np.median(times))
         out[f"b{bits}_m1"] = dict(us=round(dt * 1e6, 1), GBps=round(nb / dt / 1e9, 2), bytes=nb, copies=len(hs))
         del copies, hs
+    out["isa"] = q.qlinear_gemv_host_isa()
+    if out["isa"] == "avx512vbmi":  # the AVX2 path beside it, on the 4-bit layer
+        os.environ["QPACK_HOST_AVX2"] = "1"
+        try:
+            r = oracle.quantize(w, 4)
+            p_, s_, z_ = (np.ascontiguousarray(a) for a in (oracle.pack_canonical(r["codes"], 4), r["scales"], r["zeros"]))
+            h = q.qp_weight(p_.ctypes.data, s_.ctypes.data, z_.ctypes.data, None, None, None, 0)
+            d = q.desc(4, N, K, q.QP_LAYOUT_CANONICAL)
+            copies = [(p_.copy(), s_.copy(), z_.copy()) for _ in range(copies_for(p_.nbytes))]
+            hs = [q.qp_weight(a.ctypes.data, b.ctypes.data, c.ctypes.data, None, None, None, 0) for a, b, c in copies]
+            for h in hs[:4]:
+                q.qlinear_gemv_host(d, h, x, K, 1, y, N)
+            t = time.perf_counter()
+            for h in hs:
+                q.qlinear_gemv_host(d, h, x, K, 1, y, N)
+            dt = (time.perf_counter() - t) / len(hs)
+            out["b4_m1_avx2"] = dict(us=round(dt * 1e6, 1), GBps=round(p_.nbytes / dt / 1e9, 2))
+            del copies, hs
+        finally:
+            del os.environ["QPACK_HOST_AVX2"]
     out["threads"] = max(1, (os.cpu_count() or 2) - 1)
     out["host_read_GBps"] = round(host_read_gbps(), 2)
     return out

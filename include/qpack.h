@@ -497,11 +497,18 @@ qp_status qattn_decode_noalloc(const qkv_desc *desc, const uint16_t *q, const vo
  *  w        HOST pointers: packed canonical rows, scales, zeros, optional CSR.
  *  x, y     HOST fp16 [m][ldx] and [m][ldy]; 1 <= m <= 8.
  *  threads  worker threads (OpenMP); 0 = the machine's processors minus one.
- * Uses AVX2/FMA/F16C when the CPU has them, else a portable loop with the same arithmetic.
+ * Three code paths, chosen at run time from the CPU's features: AVX-512 with byte permutes
+ * (F, BW, VL, VBMI: 16 codes per 512-bit vector, each decoded straight to the fp32 value
+ * 1 + q/2^b), else AVX2/FMA/F16C (8 codes per 256-bit vector), else a portable loop.  They
+ * sum in different orders (fp32 results agree to rounding, not bit for bit).  The environment
+ * variables QPACK_HOST_AVX2 and QPACK_HOST_PORTABLE force the lesser paths.
  * Synchronous; allocates nothing.
  */
 qp_status qlinear_gemv_host(const qp_weight_desc *desc, const qp_weight *w, const uint16_t *x, int64_t ldx,
                             int64_t m, uint16_t *y, int64_t ldy, int32_t threads);
+/* The path qlinear_gemv_host takes on this host now: "avx512vbmi", "avx2" or "portable"
+ * (a static string). */
+const char *qlinear_gemv_host_isa(void);
 
 /*
  * Serialized packed weight (HOST memory): a self-describing little-endian byte string holding

@@ -1,8 +1,8 @@
 """Host fused unpack + multiply-accumulate GEMV (qlinear_gemv_host, the CPU half of a CPU/GPU
 layer split, mixed-bit page s4.1/s4.3) against the oracle's fp64 linear layer, within the
 floored relative tolerance of the GPU matmuls: every width, group sizes 128/64/32, byte and
-implied zero points, 1-8 activation rows, outliers, ragged row counts, the vector path and
-the portable path.  CPU only."""
+implied zero points, 1-8 activation rows, outliers, ragged row counts, and each of the three
+paths (AVX-512 with byte permutes where the host has it, AVX2, portable).  CPU only."""
 import os
 
 import numpy as np
@@ -61,6 +61,27 @@ def test_full_layer_4096_and_thread_counts():
     assert rel_err(y1, r) <= TOL, report(y1, r)
     y0, _ = run_host(w, 4, x, threads=0)
     assert np.array_equal(y0, y1)  # rows are independent: the thread count changes nothing
+
+
+@pytest.mark.parametrize("bits", (2, 3, 4, 5, 6))
+def test_avx2_path(monkeypatch, bits):
+    monkeypatch.setenv("QPACK_HOST_AVX2", "1")
+    w = workloads.weights_fp16(36, 512, 930 + bits)
+    workloads.plant_outliers(w, 0.004, 930 + bits)
+    x = workloads.activations_fp16(3, 512, 931)
+    y, r = run_host(w, bits, x, g=64 if bits == 5 else 128, frac=0.004)
+    assert rel_err(y, r) <= TOL, report(y, r)
+
+
+def test_path_query(monkeypatch):
+    monkeypatch.delenv("QPACK_HOST_AVX2", raising=False)
+    monkeypatch.delenv("QPACK_HOST_PORTABLE", raising=False)
+    best = q.qlinear_gemv_host_isa()
+    assert best in ("avx512vbmi", "avx2", "portable")
+    monkeypatch.setenv("QPACK_HOST_AVX2", "1")
+    assert q.qlinear_gemv_host_isa() == ("portable" if best == "portable" else "avx2")
+    monkeypatch.setenv("QPACK_HOST_PORTABLE", "1")
+    assert q.qlinear_gemv_host_isa() == "portable"
 
 
 def test_portable_path(monkeypatch):

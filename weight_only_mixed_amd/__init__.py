@@ -96,6 +96,7 @@ _SIGS = {
     "qattn_decode": (_i32, [_KD, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _sz, _vp]),
     "qattn_decode_noalloc": (_i32, [_KD, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp]),
     "qlinear_gemv_host": (_i32, [_D, _W, _vp, _i64, _i64, _vp, _i64, _i32]),
+    "qlinear_gemv_host_isa": (ctypes.c_char_p, []),
     "qp_blob_bytes": (_sz, [_D, _i64]),
     "qp_blob_write": (_i32, [_D, _W, _vp, _sz]),
     "qp_blob_parse": (_i32, [_vp, _sz, _D, ctypes.POINTER(_i64), ctypes.POINTER(_sz)]),
@@ -324,6 +325,11 @@ def qlinear_gemv_host(d, w, x, ldx, m, y, ldy, threads: int = 0, check=True):
     addr = lambda a: a if isinstance(a, int) else a.ctypes.data
     return _check("qlinear_gemv_host", lib.qlinear_gemv_host(ctypes.byref(d), ctypes.byref(w), addr(x), ldx, m,
                                                              addr(y), ldy, threads), check)
+
+
+def qlinear_gemv_host_isa() -> str:
+    """The vector path qlinear_gemv_host takes on this host: "avx512vbmi", "avx2" or "portable"."""
+    return lib.qlinear_gemv_host_isa().decode()
 
 
 def qp_blob_bytes(d, nnz: int = 0) -> int:

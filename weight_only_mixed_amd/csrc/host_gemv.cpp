@@ -10,6 +10,8 @@
 //    canonical page units) come from one 16-byte broadcast load, one byte shuffle that puts
 //    the 4 bytes holding code i into 32-bit lane i, one per-lane variable shift and one mask --
 //    the same four instructions for every width, straddling 3- and 5-bit fields included;
+//    on CPUs with AVX-512 VBMI the same idea on 512-bit vectors: a byte permute, a variable
+//    left shift and one ternary-logic op decode 16 codes straight to the fp32 values 1 + q/2^b;
 //  * fp32 accumulation with the scale applied in fp32 (s4.2);
 //  * software prefetch four cache lines ahead on every row stream (s4.3: distance 4);
 //  * worker threads one fewer than the cores by default, leaving one for the scheduling side
@@ -270,13 +272,128 @@ QP_AVX2 void rows_avx2(const HostArgs &a, int64_t r0, int64_t r1)
     }
 }
 
-// The vector path when the CPU has AVX2, FMA and F16C, unless QPACK_HOST_PORTABLE is set in the
-// environment (which selects the portable loop, e.g. to test it on a vector-capable host).
-bool use_avx2()
+// ---- AVX-512 path (byte permutes of VBMI) -------------------------------------------------
+#define QP_AVX512 __attribute__((target("avx512f,avx512bw,avx512vl,avx512vbmi,fma,f16c")))
+//
+// 32 codes (four 8-k blocks, 4b bytes) come from one masked load (it cannot fault past the end
+// of the buffer); for each half of 16, one byte permute puts the 4 bytes holding code i into
+// 32-bit lane i, one variable left shift moves the code to mantissa bits [23 - b, 23), and one
+// ternary-logic op keeps those bits and sets the exponent of 1.0: the lane holds 1 + q / 2^b
+// as fp32, exactly, with no integer-to-float conversion.  Per group,
+// sum_k x_k (q_k - zp) = 2^b (sum_k x_k (1 + q_k / 2^b)) - (2^b + zp) sum_k x_k.
+
+struct Unpacker512 {
+    __m512i perm[2], shl, keep;
+};
+
+QP_AVX512 Unpacker512 make_unpacker512(int b)
 {
-    static const bool cpu = __builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma") &&
-                            __builtin_cpu_supports("f16c");
-    return cpu && !getenv("QPACK_HOST_PORTABLE");
+    alignas(64) uint8_t pm[2][64];
+    alignas(64) int32_t sv[16];
+    for (int h = 0; h < 2; ++h)
+        for (int i = 0; i < 16; ++i) {
+            const int code = 16 * h + i, byte0 = (b * code) / 8;
+            for (int j = 0; j < 4; ++j) pm[h][4 * i + j] = (uint8_t)(byte0 + j < 64 ? byte0 + j : 63);
+        }
+    for (int i = 0; i < 16; ++i) sv[i] = 23 - b - (b * i) % 8;  // 16 b is a multiple of 8: both halves alike
+    Unpacker512 u;
+    u.perm[0] = _mm512_load_si512((const void *)pm[0]);
+    u.perm[1] = _mm512_load_si512((const void *)pm[1]);
+    u.shl = _mm512_load_si512((const void *)sv);
+    u.keep = _mm512_set1_epi32(((1 << b) - 1) << (23 - b));
+    return u;
+}
+
+// R rows [r0, r0+R) with M activation rows.
+template <int R, int M>
+QP_AVX512 void rows_avx512_tile(const HostArgs &a, int64_t r0, const Unpacker512 &u)
+{
+    const int b = a.bits, steps = (int)(a.gs / 32);  // 32-code steps per group
+    const __mmask64 lm = (__mmask64)((1ull << (4 * b)) - 1);
+    const __m512i one = _mm512_set1_epi32(0x3F800000);
+    const __m512 vpw = _mm512_set1_ps((float)(1 << b));
+    const uint8_t *p = a.w + r0 * (a.k * b / 8);  // the R rows are consecutive: one stream per row
+    const int64_t rb = a.k * b / 8;
+    const uint16_t *sc = a.scales + r0 * a.G;
+    const uint8_t *zp8 = a.zeros ? a.zeros + r0 * a.G : nullptr;
+    __m512 tot[R][M];
+    for (int i = 0; i < R; ++i)
+        for (int mm = 0; mm < M; ++mm) tot[i][mm] = _mm512_setzero_ps();
+    const uint16_t *xk = a.x;
+    for (int64_t g = 0; g < a.G; ++g) {
+        __m512 acc[R][M], xs[M];
+        for (int mm = 0; mm < M; ++mm) xs[mm] = _mm512_setzero_ps();
+        for (int i = 0; i < R; ++i)
+            for (int mm = 0; mm < M; ++mm) acc[i][mm] = _mm512_setzero_ps();
+        for (int st = 0; st < steps; ++st, xk += 32, p += 4 * b) {
+            __m512 xv[2][M];
+            for (int mm = 0; mm < M; ++mm)
+                for (int h = 0; h < 2; ++h) {
+                    xv[h][mm] = _mm512_cvtph_ps(_mm256_loadu_si256((const __m256i *)(xk + mm * a.ldx + 16 * h)));
+                    xs[mm] = _mm512_add_ps(xs[mm], xv[h][mm]);
+                }
+            for (int i = 0; i < R; ++i) {
+                _mm_prefetch((const char *)(p + i * rb + 4 * 64), _MM_HINT_T0);
+                const __m512i v = _mm512_maskz_loadu_epi8(lm, p + i * rb);
+                for (int h = 0; h < 2; ++h) {
+                    const __m512i f = _mm512_sllv_epi32(_mm512_permutexvar_epi8(u.perm[h], v), u.shl);
+                    const __m512 wq = _mm512_castsi512_ps(_mm512_ternarylogic_epi32(f, u.keep, one, 0xEA));
+                    for (int mm = 0; mm < M; ++mm) acc[i][mm] = _mm512_fmadd_ps(xv[h][mm], wq, acc[i][mm]);
+                }
+            }
+        }
+        for (int i = 0; i < R; ++i) {
+            const float s = _cvtsh_ss(sc[i * a.G + g]);
+            const float zp = (float)(zp8 ? zp8[i * a.G + g] : a.zmid);
+            const __m512 vs = _mm512_set1_ps(s), vnc = _mm512_set1_ps(-((float)(1 << b) + zp));
+            for (int mm = 0; mm < M; ++mm)
+                tot[i][mm] = _mm512_fmadd_ps(vs, _mm512_fmadd_ps(vpw, acc[i][mm], _mm512_mul_ps(vnc, xs[mm])), tot[i][mm]);
+        }
+    }
+    for (int i = 0; i < R; ++i) {
+        float acc1[8];
+        for (int mm = 0; mm < M; ++mm) acc1[mm] = _mm512_reduce_add_ps(tot[i][mm]);
+        finish_row(a, r0 + i, acc1);
+    }
+}
+
+template <int M>
+QP_AVX512 void rows_avx512_m(const HostArgs &a, int64_t r0, int64_t r1, const Unpacker512 &u)
+{
+    constexpr int R = M == 1 ? 4 : M == 2 ? 2 : 1;
+    int64_t r = r0;
+    for (; r + R <= r1; r += R) rows_avx512_tile<R, M>(a, r, u);
+    for (; r < r1; ++r) rows_avx512_tile<1, M>(a, r, u);
+}
+
+QP_AVX512 void rows_avx512(const HostArgs &a, int64_t r0, int64_t r1)
+{
+    const Unpacker512 u = make_unpacker512(a.bits);
+    switch (a.m) {
+    case 1: rows_avx512_m<1>(a, r0, r1, u); break;
+    case 2: rows_avx512_m<2>(a, r0, r1, u); break;
+    case 3: rows_avx512_m<3>(a, r0, r1, u); break;
+    case 4: rows_avx512_m<4>(a, r0, r1, u); break;
+    case 5: rows_avx512_m<5>(a, r0, r1, u); break;
+    case 6: rows_avx512_m<6>(a, r0, r1, u); break;
+    case 7: rows_avx512_m<7>(a, r0, r1, u); break;
+    default: rows_avx512_m<8>(a, r0, r1, u); break;
+    }
+}
+
+// The vector path: AVX-512 (with VBMI) when the CPU has it, else AVX2 with FMA and F16C.
+// QPACK_HOST_PORTABLE in the environment selects the portable loop and QPACK_HOST_AVX2 the AVX2
+// one (to test them on a host that has more).
+enum Path { kPortable, kAvx2, kAvx512 };
+Path host_path()
+{
+    static const bool avx2 = __builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma") &&
+                             __builtin_cpu_supports("f16c");
+    static const bool avx512 = avx2 && __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
+                               __builtin_cpu_supports("avx512vl") && __builtin_cpu_supports("avx512vbmi");
+    if (getenv("QPACK_HOST_PORTABLE") || !avx2) return kPortable;
+    if (avx512 && !getenv("QPACK_HOST_AVX2")) return kAvx512;
+    return kAvx2;
 }
 
 int default_threads()
@@ -290,6 +407,15 @@ int default_threads()
 }
 
 }  // namespace
+
+extern "C" const char *qlinear_gemv_host_isa(void)
+{
+    switch (host_path()) {
+    case kAvx512: return "avx512vbmi";
+    case kAvx2: return "avx2";
+    default: return "portable";
+    }
+}
 
 extern "C" qp_status qlinear_gemv_host(const qp_weight_desc *d, const qp_weight *w, const uint16_t *x, int64_t ldx,
                                        int64_t m, uint16_t *y, int64_t ldy, int32_t threads)
@@ -328,13 +454,15 @@ extern "C" qp_status qlinear_gemv_host(const qp_weight_desc *d, const qp_weight 
     a.bits = d->bits;
     a.total_bytes = (int64_t)qp_packed_bytes(d);
     const int nt = threads > 0 ? threads : default_threads();
-    const bool avx = use_avx2();
+    const Path path = host_path();
     // Rows in chunks of 16 (a multiple of every row tile), spread over the threads.
     const int64_t chunks = (a.n + 15) / 16;
 #pragma omp parallel for num_threads(nt) schedule(static)
     for (int64_t c = 0; c < chunks; ++c) {
         const int64_t r0 = 16 * c, r1 = r0 + 16 < a.n ? r0 + 16 : a.n;
-        if (avx)
+        if (path == kAvx512)
+            rows_avx512(a, r0, r1);
+        else if (path == kAvx2)
             rows_avx2(a, r0, r1);
         else
             rows_scalar(a, r0, r1);
