@@ -109,10 +109,11 @@ enum { QP_ZERO_STORED = 0, QP_ZERO_MIDPOINT = 1, QP_ZERO_PACKED = 2 };
  *                  - bit 7 clear: an E4M3 value (OCP 8-bit float: 4-bit exponent, bias 7, 3-bit
  *                    mantissa; 0x7F is NaN); the scale is row_factors[n] times that value;
  *                  - bit 7 set: the scale is the fp16 fb_scales[n * fb_stride + (byte & 0x7F)].
- *                 Written by qpack_quantize_fp8; read by qlinear_gemv and qlinear_gemm (byte or
- *                 implied zero points).  The grouped GEMM, the MoE FFN, qlinear_gemm_a8,
- *                 qlinear_gemv_batch, qlinear_gemv_host and qp_blob_write return
- *                 QP_ERR_UNSUPPORTED for it (qp_blob_bytes 0). */
+ *                 Written by qpack_quantize_fp8; read by qlinear_gemv, qlinear_gemm,
+ *                 qlinear_grouped_gemm and qmoe_ffn (byte or implied zero points; every expert
+ *                 of a grouped call brings its own scale bytes, row factors and fallback list).
+ *                 qlinear_gemm_a8, qlinear_gemv_batch, qlinear_gemv_host and qp_blob_write
+ *                 return QP_ERR_UNSUPPORTED for it (qp_blob_bytes 0). */
 enum { QP_SCALE_FP16 = 0, QP_SCALE_FP8 = 1 };
 
 /* Shape and format of one quantized matrix W[n][k]. */

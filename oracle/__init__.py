@@ -373,6 +373,30 @@ def linear_fp8(x_fp16, qd) -> np.ndarray:
     return np.asarray(x_fp16, np.float16).astype(np.float64) @ dequant_fp8(qd).T
 
 
+def swiglu_act_fp8(x_rows_fp16, gate: dict, up: dict) -> np.ndarray:
+    """fp64 silu(What_gate x) * (What_up x) for token rows over fp8-scale weights (quantize_fp8
+    dicts), before the fp16 rounding ([MoE] s4.2 expert FFN gate/up; silu(v) = v / (1 + e^-v))."""
+    gv, uv = linear_fp8(x_rows_fp16, gate), linear_fp8(x_rows_fp16, up)
+    return gv / (1.0 + np.exp(-gv)) * uv
+
+
+def moe_ffn_fp8(x_fp16, ids, wts, gate: list, up: list, down: list) -> np.ndarray:
+    """fp64 routed-expert FFN over fp8-scale experts, the same definition as moe_ffn: per token,
+    sum over its top-k experts of routing weight * What_down fp16(silu(gate) * up)
+    ([MoE] s4.2: routing weights as given, not renormalised)."""
+    x = np.asarray(x_fp16, np.float16)
+    ids = np.asarray(ids)
+    wts = np.asarray(wts, np.float32)
+    T = x.shape[0]
+    r = np.zeros((T, down[0]["codes"].shape[0]), np.float64)
+    for t in range(T):
+        for j in range(ids.shape[1]):
+            e = int(ids[t, j])
+            a = swiglu_act_fp8(x[t:t + 1], gate[e], up[e]).astype(np.float16)
+            r[t] += float(wts[t, j]) * linear_fp8(a, down[e])[0]
+    return r
+
+
 def swiglu_act(x_row_fp16, gate: dict, up: dict):
     """fp64 silu(What_gate x) * (What_up x) for one token row, before fp16 rounding."""
     xt = _bits16(x_row_fp16).ravel()

@@ -352,8 +352,9 @@ def test_int8_path_validation():
 
 def test_fp8_scale_validation():
     """QP_SCALE_FP8 (8-bit float scales with an fp16 fallback, mixed-bit page s2.3): only the
-    fp8 quantizer writes it and only the GEMV and the layer GEMM read it; every other call
-    refuses it, and the fp8 calls check their buffers, before any launch."""
+    fp8 quantizer writes it and the GEMV, the layer GEMM, the grouped GEMM and the expert FFN
+    read it; every other call refuses it, and the fp8 calls check their buffers, before any
+    launch (no call here gets past validation: every weight or shape is malformed)."""
     ok = dict(stream=0, check=False)
     f8 = q.desc(2, 256, 512, group_size=32, zero_mode=q.QP_ZERO_MIDPOINT, scale_format=q.QP_SCALE_FP8)
     fp16 = q.desc(2, 256, 512, group_size=32, zero_mode=q.QP_ZERO_MIDPOINT)
@@ -386,19 +387,26 @@ def test_fp8_scale_validation():
     with_csr = q.weight_fp8(FAKE, FAKE, FAKE, FAKE, 8)
     with_csr.csr_rowptr, with_csr.csr_col, with_csr.csr_val, with_csr.nnz = FAKE, FAKE, FAKE, 5
     assert q.qlinear_gemv(f8, with_csr, FAKE, 512, 1, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
-    # every other matmul refuses fp8 scales
+    # the batched GEMV refuses fp8 scales
     assert q.qlinear_gemv_batch([q.gemv_problem(f8, good, FAKE, 512, 1, FAKE, 256)], **ok) == q.QP_ERR_UNSUPPORTED
     # the layer GEMM reads them too (validation only here: a malformed weight is refused)
     assert q.qlinear_gemm(f8, q.weight_fp8(FAKE, None, FAKE, FAKE, 8), FAKE, 512, 64, FAKE, 256, **ok) == \
         q.QP_ERR_INVALID_ARG
     assert q.qlinear_gemm(f8, with_csr, FAKE, 512, 64, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
-    assert q.qlinear_grouped_gemm(f8, [good], FAKE, 512, FAKE, FAKE, 10, 0, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
+    # the grouped GEMM and the expert FFN check every expert's fp8 buffers
+    bad = q.weight_fp8(FAKE, None, FAKE, FAKE, 8)
+    assert q.qlinear_grouped_gemm(f8, [good, bad], FAKE, 512, FAKE, FAKE, 10, 0, FAKE, 256, **ok) == q.QP_ERR_INVALID_ARG
+    assert q.qlinear_grouped_gemm(f8, [good, q.weight_fp8(FAKE, FAKE, FAKE, FAKE, 129)], FAKE, 512, FAKE, FAKE, 10, 0,
+                                  FAKE, 256, **ok) == q.QP_ERR_INVALID_ARG
+    assert q.qlinear_grouped_gemm(f8, [with_csr], FAKE, 512, FAKE, FAKE, 10, 0, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
     f8_128 = q.desc(4, 256, 512, zero_mode=q.QP_ZERO_MIDPOINT, scale_format=q.QP_SCALE_FP8)
     assert q.qlinear_gemm_a8(f8_128, good, FAKE, FAKE, 4, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
     gu = q.desc(4, 2 * 1024, 512, scale_format=q.QP_SCALE_FP8)
     dn = q.desc(4, 512, 1024, scale_format=q.QP_SCALE_FP8)
-    assert q.qmoe_ffn(gu, [good] * 4, dn, [good] * 4, FAKE, 512, 8, FAKE, FAKE, 2, FAKE, 512, FAKE, 1 << 30,
-                      **ok) == q.QP_ERR_UNSUPPORTED
+    assert q.qmoe_ffn(gu, [good] * 4, dn, [good] * 3 + [bad], FAKE, 512, 8, FAKE, FAKE, 2, FAKE, 512, FAKE, 1 << 30,
+                      **ok) == q.QP_ERR_INVALID_ARG
+    assert q.qmoe_ffn(gu, [good] * 3 + [bad], dn, [good] * 4, FAKE, 512, 8, FAKE, FAKE, 2, FAKE, 512, FAKE, 1 << 30,
+                      **ok) == q.QP_ERR_INVALID_ARG
     canon8 = q.desc(2, 256, 512, layout=q.QP_LAYOUT_CANONICAL, group_size=32, zero_mode=q.QP_ZERO_MIDPOINT,
                     scale_format=q.QP_SCALE_FP8)
     assert q.lib.qlinear_gemv_host(ctypes.byref(canon8), ctypes.byref(good), FAKE, 512, 1, FAKE, 256, 1) == \

@@ -137,3 +137,25 @@ def test_all_zero_rows_and_groups():
         mid = 8 if sym else 0
         assert (q["codes"][0] == mid).all() and (q["codes"][1, :192] == mid).all()
         assert list(q["sc8"][1, :3]) == [0, 0, 0] and q["sc8"][1, 3] == 0x78
+
+
+def test_moe_ffn_fp8_equals_the_fp16_ffn_on_equal_scales():
+    """The fp8-scale expert FFN (numpy) against the C oracle's FFN: with every stored scale an
+    fp16 value (the fp16 path's own quantization, its scales carried as fp32), both compute
+    the same definition, so the two agree to fp64 rounding."""
+    E, D, F, T = 3, 128, 256, 6
+    x = workloads.activations_fp16(T, D, 70)
+    ids = np.array([[0, 2], [1, 0], [2, 1], [2, 0], [0, 1], [1, 2]], np.int32)
+    wts = np.array([[0.7, 0.3], [0.5, 0.25], [1.0, 0.125], [0.6, 0.4], [0.9, 0.1], [0.2, 0.8]], np.float32)
+    q16 = [[oracle.quantize(m, 4) for m in workloads.moe_expert(e, D, F, 71)] for e in range(E)]
+    as8 = lambda d: dict(codes=d["codes"], zeros=d["zeros"], g=128,
+                         scales_f32=d["scales"].view(np.float16).astype(np.float32))
+    r16 = oracle.moe_ffn(x, ids, wts, *[[q16[e][i] for e in range(E)] for i in range(3)])
+    r8 = oracle.moe_ffn_fp8(x, ids, wts, *[[as8(q16[e][i]) for e in range(E)] for i in range(3)])
+    rms = np.sqrt(np.mean(r16 * r16))
+    assert rms > 0 and np.abs(r8 - r16).max() <= 1e-12 * rms
+    # one token through one expert with weight 1 is silu(gate) * up rounded to fp16, then down
+    g, u, dn = (as8(d) for d in q16[1])
+    a = oracle.swiglu_act_fp8(x[:1], g, u).astype(np.float16)
+    one = oracle.moe_ffn_fp8(x[:1], np.array([[1]], np.int32), np.array([[1.0]], np.float32), [g] * E, [u] * E, [dn] * E)
+    assert np.array_equal(one, oracle.linear_fp8(a, dn))

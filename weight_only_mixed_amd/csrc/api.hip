@@ -79,8 +79,21 @@ static qp_status check_desc(const qp_weight_desc *d, bool need_device)
 static qp_status need_fp16_scales(const qp_weight_desc *d, const char *who)
 {
     if (d->scale_format != QP_SCALE_FP16)
-        return fail(QP_ERR_UNSUPPORTED, "%s reads fp16 scales (fp8 scales: qpack_quantize_fp8, qlinear_gemv, qlinear_gemm)", who);
+        return fail(QP_ERR_UNSUPPORTED,
+                    "%s reads fp16 scales (fp8 scales: qpack_quantize_fp8, qlinear_gemv, qlinear_gemm, "
+                    "qlinear_grouped_gemm, qmoe_ffn)",
+                    who);
     return QP_OK;
+}
+
+// The kernels' view of a validated weight: with fp8 scales, `scales` carries the scale bytes
+// and the row factors and fallback list ride along.
+static ExpertPtrs weight_ptrs(const qp_weight_desc *d, const qp_weight *w)
+{
+    if (d->scale_format == QP_SCALE_FP8)
+        return {(const uint8_t *)w->packed, (const uint16_t *)w->scales8, w->zeros, w->row_factors,
+                w->fb_stride > 0 ? w->fb_scales : nullptr, (int32_t)w->fb_stride};
+    return {(const uint8_t *)w->packed, w->scales, w->zeros, nullptr, nullptr, 0};
 }
 
 static qp_status check_weight(const qp_weight_desc *d, const qp_weight *w, bool allow_csr)
@@ -338,16 +351,11 @@ static qp_status gemv_problem(const qp_weight_desc *d, const qp_weight *w, const
     if (m > 16) return fail(QP_ERR_UNSUPPORTED, "gemv handles m <= 16 (m=%lld); use qlinear_gemm", (long long)m);
     if (prod_over(m, ldx, 2, 0x7FFFFFFFLL)) return fail(QP_ERR_UNSUPPORTED, "x larger than 2 GiB");
     *p = GemvProblem{};
-    p->w = {(const uint8_t *)w->packed, w->scales, w->zeros};
+    p->w = weight_ptrs(d, w);
+    p->fp8 = d->scale_format == QP_SCALE_FP8;
     p->zmid = zero_pair(d);
     p->gs = d->group_size;
     p->zrow = d->zero_mode == QP_ZERO_PACKED ? (int32_t)zero_row_bytes(d) : 0;
-    if (d->scale_format == QP_SCALE_FP8) {
-        p->sc8 = w->scales8;
-        p->rowf = w->row_factors;
-        p->fb = w->fb_scales;
-        p->fb_stride = (int32_t)w->fb_stride;
-    }
     if (w->nnz > 0) {
         p->rowptr = w->csr_rowptr;
         p->col = w->csr_col;
@@ -416,16 +424,11 @@ qp_status qlinear_gemm(const qp_weight_desc *d, const qp_weight *w, const uint16
     if (prod_over(m, ldx, 2, 0x7FFFFFFFLL)) return fail(QP_ERR_UNSUPPORTED, "x larger than 2 GiB");
     if ((int64_t)qp_packed_bytes(d) > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "packed weight larger than 2 GiB");
     GemmArgs a{};
-    a.ex[0] = {(const uint8_t *)w->packed, w->scales, w->zeros};
+    a.ex[0] = weight_ptrs(d, w);
+    a.fp8 = d->scale_format == QP_SCALE_FP8;  // check_weight has refused an outlier CSR with it
     a.zmid = zero_pair(d);
     a.gs = d->group_size;
     a.zrow = d->zero_mode == QP_ZERO_PACKED ? (uint32_t)zero_row_bytes(d) : 0u;
-    if (d->scale_format == QP_SCALE_FP8) {  // check_weight has refused an outlier CSR
-        a.sc8 = w->scales8;
-        a.rowf = w->row_factors;
-        a.fb = w->fb_scales;
-        a.fb_stride = (int32_t)w->fb_stride;
-    }
     if (w->nnz > 0) {
         if (prod_over(d->k, gemm_xt_ld(m), 2, 0x7FFFFFFFLL) || prod_over(d->n, gemm_xt_ld(m), 4, 0x7FFFFFFFLL))
             return fail(QP_ERR_UNSUPPORTED, "m*k or m*n too large for the outlier add-back");
@@ -460,8 +463,8 @@ static qp_status grouped_launch(const qp_weight_desc *d, const qp_weight *expert
     if ((rows + (int64_t)n_experts * 31) / 32 > 65535)
         return fail(QP_ERR_UNSUPPORTED, "grouped matmuls take at most 65535 32-row tiles of routed rows");
     GemmArgs a{};
-    for (int e = 0; e < n_experts; ++e)
-        a.ex[e] = {(const uint8_t *)experts[e].packed, experts[e].scales, experts[e].zeros};
+    for (int e = 0; e < n_experts; ++e) a.ex[e] = weight_ptrs(d, &experts[e]);
+    a.fp8 = d->scale_format == QP_SCALE_FP8;
     a.zmid = zero_pair(d);
     a.gs = d->group_size;
     a.zrow = d->zero_mode == QP_ZERO_PACKED ? (uint32_t)zero_row_bytes(d) : 0u;
@@ -486,7 +489,6 @@ qp_status qlinear_grouped_gemm(const qp_weight_desc *d, const qp_weight *experts
 {
     qp_status st = check_desc(d, true);
     if (st != QP_OK) return st;
-    if ((st = need_fp16_scales(d, "qlinear_grouped_gemm")) != QP_OK) return st;
     if (!experts) return fail(QP_ERR_INVALID_ARG, "experts NULL");
     if (n_experts < 1 || n_experts > kMaxExperts) return fail(QP_ERR_INVALID_ARG, "n_experts=%d not in 1..64", n_experts);
     for (int e = 0; e < n_experts; ++e)
@@ -552,7 +554,6 @@ qp_status qmoe_ffn(const qp_weight_desc *dgu, const qp_weight *gate_up, const qp
     qp_status st;
     if ((st = check_desc(dgu, true)) != QP_OK) return st;
     if ((st = check_desc(dd, true)) != QP_OK) return st;
-    if ((st = need_fp16_scales(dgu, "qmoe_ffn")) != QP_OK || (st = need_fp16_scales(dd, "qmoe_ffn")) != QP_OK) return st;
     if (dgu->bits != dd->bits) return fail(QP_ERR_UNSUPPORTED, "gate/up and down must share the bit width");
     const int64_t d_model = dgu->k, d_ff = dgu->n / 2;
     if (dgu->n % 32 != 0 || dd->n != d_model || dd->k != d_ff)

@@ -5,15 +5,15 @@
 
 namespace qp {
 namespace gk {
-QP_GEMM_VARIANT(128, false)
-QP_GEMM_VARIANT_EXTERN(64, false)
-QP_GEMM_VARIANT_EXTERN(32, false)
-QP_GEMM_VARIANT_EXTERN(128, true)
-QP_GEMM_VARIANT_EXTERN(64, true)
-QP_GEMM_VARIANT_EXTERN(32, true)
-QP_GEMM_VARIANT_EXTERN(128, 2)
-QP_GEMM_VARIANT_EXTERN(64, 2)
-QP_GEMM_VARIANT_EXTERN(32, 2)
+QP_GEMM_VARIANT(128, kZpByte)
+QP_GEMM_VARIANT_EXTERN(64, kZpByte)
+QP_GEMM_VARIANT_EXTERN(32, kZpByte)
+QP_GEMM_VARIANT_EXTERN(128, kZpPacked)
+QP_GEMM_VARIANT_EXTERN(64, kZpPacked)
+QP_GEMM_VARIANT_EXTERN(32, kZpPacked)
+QP_GEMM_VARIANT_EXTERN(128, kZpFp8)
+QP_GEMM_VARIANT_EXTERN(64, kZpFp8)
+QP_GEMM_VARIANT_EXTERN(32, kZpFp8)
 }  // namespace gk
 
 // Position of activation row 16 mt + 4 t + i (of a 128-row block) in the transposed layouts:
@@ -111,12 +111,12 @@ hipError_t launch_gemm(int bits, const GemmArgs &a, hipStream_t st)
         hipLaunchKernelGGL(outlier_spmm_kernel, dim3((unsigned)((a.n + 3) / 4), (unsigned)((a.ldxt + 511) / 512)),
                            dim3(256), 0, st, a.rowptr, a.col, a.val, a.xt, a.n, a.ldxt, a.spart);
     }
-    if (a.sc8) return gemm_zp<gk::kZpFp8>(bits, a.rowptr != nullptr, a, st);
+    if (a.fp8) return gemm_zp<gk::kZpFp8>(bits, a.rowptr != nullptr, a, st);
     return a.zrow ? gemm_zp<gk::kZpPacked>(bits, a.rowptr != nullptr, a, st)
                   : gemm_zp<gk::kZpByte>(bits, a.rowptr != nullptr, a, st);
 }
 
-template <bool ZPK>
+template <int ZPK>
 static hipError_t grouped_zp(int bits, int epilogue, int n_experts, const GemmArgs &a, hipStream_t st)
 {
     switch (a.gs) {
@@ -130,7 +130,9 @@ static hipError_t grouped_zp(int bits, int epilogue, int n_experts, const GemmAr
 hipError_t launch_grouped(int bits, int epilogue, int n_experts, const GemmArgs &a, hipStream_t st)
 {
     if (a.m < 1) return hipSuccess;
-    return a.zrow ? grouped_zp<true>(bits, epilogue, n_experts, a, st) : grouped_zp<false>(bits, epilogue, n_experts, a, st);
+    if (a.fp8) return grouped_zp<gk::kZpFp8>(bits, epilogue, n_experts, a, st);
+    return a.zrow ? grouped_zp<gk::kZpPacked>(bits, epilogue, n_experts, a, st)
+                  : grouped_zp<gk::kZpByte>(bits, epilogue, n_experts, a, st);
 }
 
 }  // namespace qp

@@ -3,6 +3,6 @@
 
 namespace qp {
 namespace gk {
-QP_GEMM_VARIANT(64, false)
+QP_GEMM_VARIANT(64, kZpByte)
 }  // namespace gk
 }  // namespace qp

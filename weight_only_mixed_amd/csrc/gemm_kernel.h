@@ -495,6 +495,8 @@ struct TilePlan {
     int32_t mh;       // activation rows per tile
     int32_t experts;  // grouped: entries of the offsets table, minus one
 };
+// Both travel as kernel arguments: keep them within 4 KB.
+static_assert(sizeof(GemmArgs) + sizeof(TilePlan) <= 4096, "kernel arguments over 4 KB");
 
 __device__ __forceinline__ void plan_tile(const TilePlan &p, int64_t b, int64_t &nt, int64_t &m0)
 {
@@ -575,10 +577,10 @@ __global__ __launch_bounds__(GE::kWaves * 64) __attribute__((amdgpu_waves_per_eu
     bf.zmid = a.zmid;
     bf.zrow = a.zrow;
     bf.kt0 = (uint32_t)kt0;
-    bf.rowf = make_rsrc(a.rowf, a.rowf ? a.n * 4 : 0);
+    bf.rowf = make_rsrc(W.rowf, W.rowf ? a.n * 4 : 0);
     bf.row0 = (uint32_t)(rb0 * kTileN);
-    bf.fb = make_rsrc(a.fb, a.fb ? a.n * a.fb_stride * 2 : 0);
-    bf.fbs = a.fb_stride;
+    bf.fb = make_rsrc(W.fb, W.fb ? a.n * W.fb_stride * 2 : 0);
+    bf.fbs = W.fb_stride;
     const int64_t zstride = a.zrow ? a.zrow : G;  // zero-point bytes per weight row
     // Activation rows are gathered per lane: the DMA source of a row past the workgroup's
     // rows lies past the buffer's range and reads zeros.
@@ -600,7 +602,7 @@ __global__ __launch_bounds__(GE::kWaves * 64) __attribute__((amdgpu_waves_per_eu
         // rows' starts (bf.kt0 offsets the tile index)
         bf.w[u] = make_rsrc(W.packed + (rb * KT + kt0) * (512 * B), in ? KTp * (512 * B) : 0);
         if constexpr (ZPK == kZpFp8)  // scale bytes
-            bf.sc[u] = make_rsrc(a.sc8 + rb * kTileN * G, in ? kTileN * G : 0);
+            bf.sc[u] = make_rsrc((const uint8_t *)W.scales + rb * kTileN * G, in ? kTileN * G : 0);
         else
             bf.sc[u] = make_rsrc(W.scales + rb * kTileN * G, in ? kTileN * G * 2 : 0);
         bf.zr[u] = make_rsrc(W.zeros + rb * kTileN * zstride, in && !a.zmid ? kTileN * zstride : 0);
@@ -638,12 +640,17 @@ __global__ __launch_bounds__(GE::kWaves * 64) __attribute__((amdgpu_waves_per_eu
 
     // epilogue: lane (t, r) holds, per row block u and tile mt, activation rows 16 mt + 4 t + i
     // of weight row rb * 16 + r (sixteen lanes store 16 consecutive outputs of a row)
+    float rowf[kRBW];  // fp8 scales: each row block's weight-row factor (1 otherwise)
+#pragma unroll
+    for (int u = 0; u < kRBW; ++u) {
+        rowf[u] = 1.0f;
+        if constexpr (ZPK == kZpFp8)
+            if (rb0 + u < NB) rowf[u] = W.rowf[(rb0 + u) * kTileN + r];
+    }
 #pragma unroll
     for (int u = 0; u < kRBW; ++u) {
         const int64_t rb = rb0 + u;
         if (rb >= NB) continue;
-        float rowf = 1.0f;  // fp8 scales: the weight row's factor
-        if constexpr (ZPK == kZpFp8) rowf = a.rowf[rb * kTileN + r];
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
 #pragma unroll
@@ -651,13 +658,14 @@ __global__ __launch_bounds__(GE::kWaves * 64) __attribute__((amdgpu_waves_per_eu
                 const int64_t row = m0 + 16 * mt + 4 * t + i;
                 if (row >= mend) continue;
                 float v = tot[u][mt][i];
-                if constexpr (ZPK == kZpFp8) v *= rowf;
+                if constexpr (ZPK == kZpFp8) v *= rowf[u];
                 if constexpr (MODE == kGroupRowsF32) {
                     ((float *)a.y)[(int64_t)blockIdx.z * a.ysplit + row * a.ldy + rb * kTileN + r] = v;
                 } else if constexpr (MODE == kGroupSwiglu) {
                     // row blocks 2j (gate) and 2j+1 (up) of a wave: output feature 16 j + r
                     if (u == 1) {
-                        const float gt = tot[0][mt][i];
+                        float gt = tot[0][mt][i];
+                        if constexpr (ZPK == kZpFp8) gt *= rowf[0];
                         const float o = gt / (1.0f + expf(-gt)) * v;
                         ((uint16_t *)a.y)[row * a.ldy + (rb / 2) * kTileN + r] = __builtin_bit_cast(uint16_t, (_Float16)o);
                     }
@@ -760,22 +768,22 @@ hipError_t grouped_bits(int epilogue, int n_experts, const GemmArgs &a, hipStrea
 template <int GS, int ZPK>
 hipError_t grouped_main(int bits, int epilogue, int n_experts, const GemmArgs &a, hipStream_t st)
 {
-    if constexpr (ZPK != kZpFp8) {  // fp8 scales: the layer GEMM only
-        switch (bits) {
-        case 2: return grouped_bits<2, GS, ZPK>(epilogue, n_experts, a, st);
-        case 3: return grouped_bits<3, GS, ZPK>(epilogue, n_experts, a, st);
-        case 4: return grouped_bits<4, GS, ZPK>(epilogue, n_experts, a, st);
-        case 5: return grouped_bits<5, GS, ZPK>(epilogue, n_experts, a, st);
-        case 6: return grouped_bits<6, GS, ZPK>(epilogue, n_experts, a, st);
-        }
+    switch (bits) {
+    case 2: return grouped_bits<2, GS, ZPK>(epilogue, n_experts, a, st);
+    case 3: return grouped_bits<3, GS, ZPK>(epilogue, n_experts, a, st);
+    case 4: return grouped_bits<4, GS, ZPK>(epilogue, n_experts, a, st);
+    case 5: return grouped_bits<5, GS, ZPK>(epilogue, n_experts, a, st);
+    case 6: return grouped_bits<6, GS, ZPK>(epilogue, n_experts, a, st);
     }
     return hipErrorInvalidValue;
 }
 
-// Each variant is instantiated in one translation unit (they compile in parallel).
-#define QP_GEMM_VARIANT(GS, ZPK)                                                                      \
-    template hipError_t gemm_main<GS, ZPK>(int, bool, const GemmArgs &, hipStream_t);                 \
+// Each variant is instantiated in one translation unit (they compile in parallel); the layer
+// and grouped halves of a variant can also go to translation units of their own.
+#define QP_GEMM_LAYER(GS, ZPK) template hipError_t gemm_main<GS, ZPK>(int, bool, const GemmArgs &, hipStream_t);
+#define QP_GEMM_GROUPED(GS, ZPK) \
     template hipError_t grouped_main<GS, ZPK>(int, int, int, const GemmArgs &, hipStream_t);
+#define QP_GEMM_VARIANT(GS, ZPK) QP_GEMM_LAYER(GS, ZPK) QP_GEMM_GROUPED(GS, ZPK)
 #define QP_GEMM_VARIANT_EXTERN(GS, ZPK)                                                               \
     extern template hipError_t gemm_main<GS, ZPK>(int, bool, const GemmArgs &, hipStream_t);          \
     extern template hipError_t grouped_main<GS, ZPK>(int, int, int, const GemmArgs &, hipStream_t);

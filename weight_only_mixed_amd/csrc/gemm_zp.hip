@@ -3,8 +3,8 @@
 
 namespace qp {
 namespace gk {
-QP_GEMM_VARIANT(128, true)
-QP_GEMM_VARIANT(64, true)
-QP_GEMM_VARIANT(32, true)
+QP_GEMM_VARIANT(128, kZpPacked)
+QP_GEMM_VARIANT(64, kZpPacked)
+QP_GEMM_VARIANT(32, kZpPacked)
 }  // namespace gk
 }  // namespace qp

@@ -209,7 +209,7 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
     bf.G = G;
     bf.w = make_rsrc(a.w.packed + rb * KT * (512 * B), KT * (512 * B));
     if constexpr (ZP == kMetaFp8)
-        bf.sc = make_rsrc(a.sc8 + rb * kTileN * G, kTileN * G);
+        bf.sc = make_rsrc((const uint8_t *)a.w.scales + rb * kTileN * G, kTileN * G);
     else
         bf.sc = make_rsrc(a.w.scales + rb * kTileN * G, kTileN * G * 2);
     if constexpr (ZP == kMetaPacked) {
@@ -233,7 +233,7 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
     float F[4] = {1.f, 1.f, 1.f, 1.f};  // fp8: the factors of rows 4t + i
     if constexpr (ZP == kMetaFp8) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) F[i] = a.rowf[rb * kTileN + 4 * t + i];
+        for (int i = 0; i < 4; ++i) F[i] = a.w.rowf[rb * kTileN + 4 * t + i];
     }
     // Tile i sits in slot i % 2 and the DMA of tile i+1 runs while tile i is consumed.  The two
     // slots are separate LDS arrays, named statically (the loop is unrolled by two), so the
@@ -315,9 +315,9 @@ __device__ __forceinline__ void gemv_block(const GemvProblem &a, int64_t rb, uin
                     for (int c = 0; c < NG; ++c) {
                         const uint32_t b = (sw[i][c / 4] >> (8 * (c % 4))) & 0xFF;
                         if (b & 0x80) {
-                            const int j = min((int)(b & 0x7F), a.fb_stride - 1);
+                            const int j = min((int)(b & 0x7F), a.w.fb_stride - 1);
                             const int64_t row = rb * kTileN + 4 * t + i;
-                            scf[i][c] = j >= 0 ? h_f(a.fb[row * a.fb_stride + j]) / F[i] : 0.0f;
+                            scf[i][c] = j >= 0 ? h_f(a.w.fb[row * a.w.fb_stride + j]) / F[i] : 0.0f;
                         }
                     }
             }
@@ -502,7 +502,7 @@ static hipError_t gemv_zp(const GemvProblem &a, hipStream_t st)
 
 hipError_t launch_gemv(const GemvProblem &a, hipStream_t st)
 {
-    if (a.sc8) return gemv_zp<kMetaFp8>(a, st);
+    if (a.fp8) return gemv_zp<kMetaFp8>(a, st);
     return a.zrow ? gemv_zp<kMetaPacked>(a, st) : gemv_zp<kMetaByte>(a, st);
 }
 

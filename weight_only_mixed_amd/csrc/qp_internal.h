@@ -45,10 +45,16 @@ hipError_t launch_unpack(int bits, int layout, const uint8_t *in, int64_t n, int
 hipError_t launch_pack_zeros(int bits, const uint8_t *zeros, int64_t n, int64_t G, int64_t row_bytes,
                              uint8_t *out, hipStream_t st);
 
+// One quantized weight's device buffers.  With fp8 scales, `scales` holds the E4M3 scale
+// bytes [n][k/gs] (read as bytes), rowf the fp32 row factors [n] and fb the fp16 fallback
+// scales [n][fb_stride] (null with fb_stride 0); with fp16 scales rowf and fb are null.
 struct ExpertPtrs {
     const uint8_t *packed;
     const uint16_t *scales;
     const uint8_t *zeros;
+    const float *rowf;
+    const uint16_t *fb;
+    int32_t fb_stride;
 };
 // One decode GEMV problem, and a batch of independent ones run in a single launch.
 constexpr int kMaxGemvBatch = 8;
@@ -67,12 +73,7 @@ struct GemvProblem {
     int32_t gs;      // group size: 32, 64 or 128
     int32_t zrow;    // bytes per row of b-bit zero points (0: one byte per group)
     int64_t block0;  // batch: first workgroup of this problem
-    // fp8 scales (w.scales unused when sc8 is set): scale bytes [n][k/gs], row factors [n],
-    // fp16 fallback scales [n][fb_stride]
-    const uint8_t *sc8;
-    const float *rowf;
-    const uint16_t *fb;
-    int32_t fb_stride;
+    int32_t fp8;     // 1: E4M3 scales (w.scales holds the bytes, w.rowf and w.fb are set)
 };
 struct GemvBatch {
     GemvProblem p[kMaxGemvBatch];
@@ -104,11 +105,7 @@ struct GemmArgs {
     int32_t gs;     // group size: 128, 64 or 32
     int32_t ksplit;  // grouped fp32 rows: k in ksplit equal parts (0 or 1: whole k); part s
     int64_t ysplit;  //   writes its partial rows at y + s * ysplit floats
-    // fp8 scales (layer GEMM only): scale bytes [n][k/gs], row factors [n], fallbacks [n][fb_stride]
-    const uint8_t *sc8;
-    const float *rowf;
-    const uint16_t *fb;
-    int32_t fb_stride;
+    int32_t fp8;    // 1: E4M3 scales for every expert (ex[e].scales holds the bytes)
     uint16_t *xt;   // workspace (outliers only): x transposed, [k][ldxt]
     float *spart;   // workspace (outliers only): fp32 outlier partial, [n][ldxt]
     int64_t ldxt;
