@@ -109,11 +109,11 @@ enum { QP_ZERO_STORED = 0, QP_ZERO_MIDPOINT = 1, QP_ZERO_PACKED = 2 };
  *                  - bit 7 clear: an E4M3 value (OCP 8-bit float: 4-bit exponent, bias 7, 3-bit
  *                    mantissa; 0x7F is NaN); the scale is row_factors[n] times that value;
  *                  - bit 7 set: the scale is the fp16 fb_scales[n * fb_stride + (byte & 0x7F)].
- *                 Written by qpack_quantize_fp8; read by qlinear_gemv, qlinear_gemm,
- *                 qlinear_grouped_gemm and qmoe_ffn (byte or implied zero points; every expert
- *                 of a grouped call brings its own scale bytes, row factors and fallback list).
- *                 qlinear_gemm_a8, qlinear_gemv_batch, qlinear_gemv_host and qp_blob_write
- *                 return QP_ERR_UNSUPPORTED for it (qp_blob_bytes 0). */
+ *                 Written by qpack_quantize_fp8; read by qlinear_gemv, qlinear_gemv_batch (one
+ *                 scale format per batch), qlinear_gemm, qlinear_grouped_gemm and qmoe_ffn
+ *                 (byte or implied zero points; every problem or expert brings its own scale
+ *                 bytes, row factors and fallback list).  qlinear_gemm_a8, qlinear_gemv_host
+ *                 and qp_blob_write return QP_ERR_UNSUPPORTED for it (qp_blob_bytes 0). */
 enum { QP_SCALE_FP16 = 0, QP_SCALE_FP8 = 1 };
 
 /* Shape and format of one quantized matrix W[n][k]. */
@@ -257,7 +257,9 @@ qp_status qlinear_gemv(const qp_weight_desc *desc, const qp_weight *w, const uin
  * projections that read the same activations, each at its own bit width (the mixed-bit page
  * assigns bit widths per projection, s2.2).  Each problem has the operands and result of
  * qlinear_gemv and is validated the same way; `problems` is a HOST array of 1..8 entries.
- * Outputs must not overlap (not checked).  Returns the first failing problem's status.
+ * All problems share the group size, the zero-point storage (bytes or implied, or b-bit) and
+ * the scale format (QP_ERR_UNSUPPORTED otherwise).  Outputs must not overlap (not checked).
+ * Returns the first failing problem's status.
  */
 typedef struct {
     qp_weight_desc desc;

@@ -352,7 +352,7 @@ def test_int8_path_validation():
 
 def test_fp8_scale_validation():
     """QP_SCALE_FP8 (8-bit float scales with an fp16 fallback, mixed-bit page s2.3): only the
-    fp8 quantizer writes it and the GEMV, the layer GEMM, the grouped GEMM and the expert FFN
+    fp8 quantizer writes it and the GEMVs, the layer GEMM, the grouped GEMM and the expert FFN
     read it; every other call refuses it, and the fp8 calls check their buffers, before any
     launch (no call here gets past validation: every weight or shape is malformed)."""
     ok = dict(stream=0, check=False)
@@ -378,6 +378,7 @@ def test_fp8_scale_validation():
     assert st == q.QP_ERR_UNSUPPORTED
     # the GEMV checks the fp8 buffers
     good = q.weight_fp8(FAKE, FAKE, FAKE, FAKE, 8)
+    bad = q.weight_fp8(FAKE, None, FAKE, FAKE, 8)
     assert q.qlinear_gemv(f8, q.weight_fp8(FAKE, None, FAKE, FAKE, 8), FAKE, 512, 1, FAKE, 256, **ok) == q.QP_ERR_INVALID_ARG
     assert q.qlinear_gemv(f8, q.weight_fp8(FAKE, FAKE, None, FAKE, 8), FAKE, 512, 1, FAKE, 256, **ok) == q.QP_ERR_INVALID_ARG
     assert q.qlinear_gemv(f8, q.weight_fp8(FAKE, FAKE, FAKE, None, 8), FAKE, 512, 1, FAKE, 256, **ok) == q.QP_ERR_INVALID_ARG
@@ -387,14 +388,18 @@ def test_fp8_scale_validation():
     with_csr = q.weight_fp8(FAKE, FAKE, FAKE, FAKE, 8)
     with_csr.csr_rowptr, with_csr.csr_col, with_csr.csr_val, with_csr.nnz = FAKE, FAKE, FAKE, 5
     assert q.qlinear_gemv(f8, with_csr, FAKE, 512, 1, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
-    # the batched GEMV refuses fp8 scales
-    assert q.qlinear_gemv_batch([q.gemv_problem(f8, good, FAKE, 512, 1, FAKE, 256)], **ok) == q.QP_ERR_UNSUPPORTED
+    # the batched GEMV checks every problem's fp8 buffers and takes one scale format per batch
+    assert q.qlinear_gemv_batch([q.gemv_problem(f8, good, FAKE, 512, 1, FAKE, 256),
+                                 q.gemv_problem(f8, bad, FAKE, 512, 1, FAKE, 256)], **ok) == q.QP_ERR_INVALID_ARG
+    f16 = q.desc(2, 256, 512, group_size=32, zero_mode=q.QP_ZERO_MIDPOINT)
+    w16 = q.qp_weight(FAKE, FAKE, None, None, None, None, 0)
+    assert q.qlinear_gemv_batch([q.gemv_problem(f8, good, FAKE, 512, 1, FAKE, 256),
+                                 q.gemv_problem(f16, w16, FAKE, 512, 1, FAKE, 256)], **ok) == q.QP_ERR_UNSUPPORTED
     # the layer GEMM reads them too (validation only here: a malformed weight is refused)
     assert q.qlinear_gemm(f8, q.weight_fp8(FAKE, None, FAKE, FAKE, 8), FAKE, 512, 64, FAKE, 256, **ok) == \
         q.QP_ERR_INVALID_ARG
     assert q.qlinear_gemm(f8, with_csr, FAKE, 512, 64, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
     # the grouped GEMM and the expert FFN check every expert's fp8 buffers
-    bad = q.weight_fp8(FAKE, None, FAKE, FAKE, 8)
     assert q.qlinear_grouped_gemm(f8, [good, bad], FAKE, 512, FAKE, FAKE, 10, 0, FAKE, 256, **ok) == q.QP_ERR_INVALID_ARG
     assert q.qlinear_grouped_gemm(f8, [good, q.weight_fp8(FAKE, FAKE, FAKE, FAKE, 129)], FAKE, 512, FAKE, FAKE, 10, 0,
                                   FAKE, 256, **ok) == q.QP_ERR_INVALID_ARG

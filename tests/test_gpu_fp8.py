@@ -264,3 +264,28 @@ def test_gemm_fp8_layer_4096_prefill():
     y = gemm(GpuWeightFp8(w, 2, 32, True), x)
     r = oracle.linear_fp8(x, qd)
     assert rel_err(y, r) <= TOL, report(y, r)
+
+
+@pytest.mark.parametrize("g", (32, 128))
+@pytest.mark.parametrize("m", (1, 5))
+def test_gemv_batch_fp8(g, m):
+    """Independent fp8-scale problems of 2, 4 and 6 bits (and widths, fallback groups planted)
+    in one qlinear_gemv_batch launch: each output against the oracle's product."""
+    torch, q = gpu()
+    k = 1024
+    shapes = ((2, 192), (4, 64), (6, 320), (2, 16))
+    ws, ys, refs = [], [], []
+    x = workloads.activations_fp16(m, k, 3200 + g)
+    xd = to_dev_fp16(x)
+    for i, (bits, n) in enumerate(shapes):
+        w = workloads.weights_fp16(n, k, 3200 + 7 * i + bits)
+        plant_fallbacks(w, g, 3300 + i, rows=(0, n - 1), per_row=2)
+        qd = oracle.quantize_fp8(w, bits, g, sym=(i % 2 == 1))
+        ws.append(GpuWeightFp8(w, bits, g, i % 2 == 1))
+        ys.append(torch.empty((m, n), dtype=torch.int16, device="cuda"))
+        refs.append(oracle.linear_fp8(x, qd))
+    q.qlinear_gemv_batch([q.gemv_problem(gw.desc, gw.handle(), xd, k, m, y, gw.n) for gw, y in zip(ws, ys)])
+    torch.cuda.synchronize()
+    for (bits, n), y, r in zip(shapes, ys, refs):
+        yh = from_dev_fp16(y)
+        assert rel_err(yh, r) <= TOL, (bits, n, report(yh, r))

@@ -80,8 +80,8 @@ static qp_status need_fp16_scales(const qp_weight_desc *d, const char *who)
 {
     if (d->scale_format != QP_SCALE_FP16)
         return fail(QP_ERR_UNSUPPORTED,
-                    "%s reads fp16 scales (fp8 scales: qpack_quantize_fp8, qlinear_gemv, qlinear_gemm, "
-                    "qlinear_grouped_gemm, qmoe_ffn)",
+                    "%s reads fp16 scales (fp8 scales: qpack_quantize_fp8, qlinear_gemv, qlinear_gemv_batch, "
+                    "qlinear_gemm, qlinear_grouped_gemm, qmoe_ffn)",
                     who);
     return QP_OK;
 }
@@ -393,8 +393,8 @@ qp_status qlinear_gemv_batch(const qp_gemv_problem *problems, int32_t count, voi
         const qp_gemv_problem &q = problems[i];
         qp_status st = gemv_problem(&q.desc, &q.w, q.x, q.ldx, q.m, q.y, q.ldy, &b.p[i]);
         if (st != QP_OK) return st;
-        if ((st = need_fp16_scales(&q.desc, "qlinear_gemv_batch")) != QP_OK) return st;
         if (b.p[i].gs != b.p[0].gs) return fail(QP_ERR_UNSUPPORTED, "one group size per batch");
+        if (b.p[i].fp8 != b.p[0].fp8) return fail(QP_ERR_UNSUPPORTED, "fp16 and fp8 scales in one batch");
         if ((b.p[i].zrow != 0) != (b.p[0].zrow != 0))
             return fail(QP_ERR_UNSUPPORTED, "packed and byte zero points in one batch");
         b.p[i].block0 = blocks;

@@ -540,6 +540,7 @@ static hipError_t gemv_batch_zp(const GemvBatch &b, int64_t blocks, int m_max, h
 template <int BM>
 static hipError_t gemv_batch_bm(const GemvBatch &b, int64_t blocks, int m_max, hipStream_t st)
 {
+    if (b.p[0].fp8) return gemv_batch_zp<kMetaFp8, BM>(b, blocks, m_max, st);
     return b.p[0].zrow ? gemv_batch_zp<kMetaPacked, BM>(b, blocks, m_max, st)
                        : gemv_batch_zp<kMetaByte, BM>(b, blocks, m_max, st);
 }
