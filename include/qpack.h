@@ -110,9 +110,9 @@ enum { QP_ZERO_STORED = 0, QP_ZERO_MIDPOINT = 1, QP_ZERO_PACKED = 2 };
  *                    mantissa; 0x7F is NaN); the scale is row_factors[n] times that value;
  *                  - bit 7 set: the scale is the fp16 fb_scales[n * fb_stride + (byte & 0x7F)].
  *                 Written by qpack_quantize_fp8; read by qlinear_gemv, qlinear_gemv_batch (one
- *                 scale format per batch), qlinear_gemm, qlinear_grouped_gemm and qmoe_ffn
- *                 (byte or implied zero points; every problem or expert brings its own scale
- *                 bytes, row factors and fallback list).  qlinear_gemm_a8, qlinear_gemv_host
+ *                 scale format per batch), qlinear_gemm, qlinear_grouped_gemm, qmoe_ffn and
+ *                 qlinear_gemv_host (byte or implied zero points; every problem or expert
+ *                 brings its own scale bytes, row factors and fallback list).  qlinear_gemm_a8
  *                 and qp_blob_write return QP_ERR_UNSUPPORTED for it (qp_blob_bytes 0). */
 enum { QP_SCALE_FP16 = 0, QP_SCALE_FP8 = 1 };
 
@@ -496,8 +496,10 @@ qp_status qattn_decode_noalloc(const qkv_desc *desc, const uint16_t *q, const vo
  *                     + sum_{CSR row n} x[m][k] * val )
  * accumulated in fp32 (each group's partial, then its scale, then the outliers, in fp32).
  *  desc     canonical layout (QP_LAYOUT_CANONICAL), groups of 32/64/128, byte or implied zero
- *           points (QP_ZERO_STORED / QP_ZERO_MIDPOINT).
- *  w        HOST pointers: packed canonical rows, scales, zeros, optional CSR.
+ *           points (QP_ZERO_STORED / QP_ZERO_MIDPOINT), fp16 or fp8 scales (a group's fp8
+ *           scale is the row factor times its E4M3 value in fp32, or its fp16 fallback).
+ *  w        HOST pointers: packed canonical rows, scales (or scales8, row_factors and the
+ *           fallback list), zeros, optional CSR (fp16 scales only).
  *  x, y     HOST fp16 [m][ldx] and [m][ldy]; 1 <= m <= 8.
  *  threads  worker threads (OpenMP); 0 = the machine's processors minus one.
  * Three code paths, chosen at run time from the CPU's features: AVX-512 with byte permutes

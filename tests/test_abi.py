@@ -352,9 +352,9 @@ def test_int8_path_validation():
 
 def test_fp8_scale_validation():
     """QP_SCALE_FP8 (8-bit float scales with an fp16 fallback, mixed-bit page s2.3): only the
-    fp8 quantizer writes it and the GEMVs, the layer GEMM, the grouped GEMM and the expert FFN
-    read it; every other call refuses it, and the fp8 calls check their buffers, before any
-    launch (no call here gets past validation: every weight or shape is malformed)."""
+    fp8 quantizer writes it; the GEMVs (device and host), the layer GEMM, the grouped GEMM and
+    the expert FFN read it; the other calls refuse it, and the fp8 calls check their buffers
+    before any launch (no call here gets past validation: every weight or shape is malformed)."""
     ok = dict(stream=0, check=False)
     f8 = q.desc(2, 256, 512, group_size=32, zero_mode=q.QP_ZERO_MIDPOINT, scale_format=q.QP_SCALE_FP8)
     fp16 = q.desc(2, 256, 512, group_size=32, zero_mode=q.QP_ZERO_MIDPOINT)
@@ -414,7 +414,12 @@ def test_fp8_scale_validation():
                       **ok) == q.QP_ERR_INVALID_ARG
     canon8 = q.desc(2, 256, 512, layout=q.QP_LAYOUT_CANONICAL, group_size=32, zero_mode=q.QP_ZERO_MIDPOINT,
                     scale_format=q.QP_SCALE_FP8)
-    assert q.lib.qlinear_gemv_host(ctypes.byref(canon8), ctypes.byref(good), FAKE, 512, 1, FAKE, 256, 1) == \
+    # the host GEMV reads fp8 scales too (validation only here: every weight is malformed)
+    assert q.lib.qlinear_gemv_host(ctypes.byref(canon8), ctypes.byref(bad), FAKE, 512, 1, FAKE, 256, 1) == \
+        q.QP_ERR_INVALID_ARG
+    assert q.lib.qlinear_gemv_host(ctypes.byref(canon8), ctypes.byref(q.weight_fp8(FAKE, FAKE, FAKE, None, 8)), FAKE,
+                                   512, 1, FAKE, 256, 1) == q.QP_ERR_INVALID_ARG
+    assert q.lib.qlinear_gemv_host(ctypes.byref(canon8), ctypes.byref(with_csr), FAKE, 512, 1, FAKE, 256, 1) == \
         q.QP_ERR_UNSUPPORTED
     assert q.qp_blob_bytes(canon8, 0) == 0
     assert q.lib.qp_blob_write(ctypes.byref(canon8), ctypes.byref(good), FAKE, 1 << 20) == q.QP_ERR_UNSUPPORTED

@@ -104,3 +104,67 @@ def test_rejections():
     d = q.desc(4, 64, 512, q.QP_LAYOUT_CANONICAL)
     assert q.qlinear_gemv_host(d, wh, x, 512, 9, y, 64, check=False) == q.QP_ERR_UNSUPPORTED  # m > 8
     assert q.qlinear_gemv_host(d, wh, x, 500, 1, y, 64, check=False) == q.QP_ERR_INVALID_ARG  # ldx < k
+
+
+def shrink_groups(w: np.ndarray, g: int, row: int, groups):
+    """Scale groups of one row by 2^-16: they fall outside E4M3's range below the row's
+    largest scale and take fp16 fallback scales."""
+    for c in groups:
+        w[row, c * g:(c + 1) * g] = (w[row, c * g:(c + 1) * g].astype(np.float32) * 2.0 ** -16).astype(np.float16)
+
+
+def run_host_fp8(w, bits, x, g, sym, fb_stride=8):
+    n, k = w.shape
+    m = x.shape[0]
+    qd = oracle.quantize_fp8(w, bits, g, sym=sym, fb_stride=fb_stride)
+    packed = np.ascontiguousarray(oracle.pack_canonical(qd["codes"], bits))
+    sc8, fac = np.ascontiguousarray(qd["sc8"]), np.ascontiguousarray(qd["factors"])
+    fb = np.ascontiguousarray(qd["fb"]) if fb_stride else None
+    zeros = None if sym else np.ascontiguousarray(qd["zeros"])
+    wh = q.weight_fp8(packed.ctypes.data, sc8.ctypes.data, fac.ctypes.data, fb.ctypes.data if fb is not None else None,
+                      fb_stride, zeros.ctypes.data if zeros is not None else None)
+    d = q.desc(bits, n, k, q.QP_LAYOUT_CANONICAL, group_size=g,
+               zero_mode=q.QP_ZERO_MIDPOINT if sym else q.QP_ZERO_STORED, scale_format=q.QP_SCALE_FP8)
+    y = np.zeros((m, n), np.uint16)
+    q.qlinear_gemv_host(d, wh, np.ascontiguousarray(x).view(np.uint16), k, m, y, n, 0)
+    return y.view(np.float16).astype(np.float64), oracle.linear_fp8(x, qd), qd
+
+
+@pytest.mark.parametrize("path", ("best", "avx2", "portable"))
+@pytest.mark.parametrize("bits,g,sym", ((2, 32, True), (3, 64, False), (4, 128, False), (5, 32, True), (6, 64, False)))
+def test_fp8_scales(monkeypatch, path, bits, g, sym):
+    """fp8 scales with fallback groups on every path: each group's scale is the row factor
+    times its E4M3 value, or its fp16 fallback."""
+    monkeypatch.delenv("QPACK_HOST_AVX2", raising=False)
+    monkeypatch.delenv("QPACK_HOST_PORTABLE", raising=False)
+    if path == "avx2":
+        monkeypatch.setenv("QPACK_HOST_AVX2", "1")
+    elif path == "portable":
+        monkeypatch.setenv("QPACK_HOST_PORTABLE", "1")
+    w = workloads.weights_fp16(40, 512, 940 + bits)
+    shrink_groups(w, g, 0, (1, 3))
+    shrink_groups(w, g, 21, (0,))
+    x = workloads.activations_fp16(3, 512, 941)
+    y, r, qd = run_host_fp8(w, bits, x, g, sym)
+    assert qd["counts"][0] == 2 and qd["counts"][21] == 1
+    assert rel_err(y, r) <= TOL, report(y, r)
+
+
+def test_fp8_fallback_index_past_the_list():
+    """More fallback groups than slots: bytes naming a slot past the list read its last slot
+    (as the GPU paths do); without a list they read scale 0."""
+    g, k = 32, 512
+    w = workloads.weights_fp16(16, k, 950, std=0.002)
+    w[5, :g] = workloads.weights_fp16(1, g, 951, std=100.0)  # row 5: 15 fallbacks
+    x = workloads.activations_fp16(2, k, 952)
+    x[:, :g] = 0
+    y, _, qd = run_host_fp8(w, 4, x, g, False, fb_stride=4)
+    assert qd["counts"][5] == k // g - 1
+    sc = qd["scales_f32"].copy()
+    last = np.float32(oracle.half_value(int(qd["fb"][5, 3])))
+    for gi in range(k // g):
+        b = int(qd["sc8"][5, gi])
+        if b & 0x80 and (b & 0x7F) >= 4:
+            sc[5, gi] = last
+    r = oracle.linear_fp8(x, dict(qd, scales_f32=sc))
+    assert rel_err(y, r) <= TOL, report(y, r)

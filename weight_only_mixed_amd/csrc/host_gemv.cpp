@@ -20,6 +20,7 @@
 // - zp * sum_k x_k, and the lane-wise sums of x are accumulated beside the products, so the
 // inner loop is shuffle, shift, and, convert, and one fma per activation row.
 #include <immintrin.h>
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -91,7 +92,11 @@ uint16_t float_to_half(float v)
 
 struct HostArgs {
     const uint8_t *w;        // canonical packed rows, k*b/8 bytes each
-    const uint16_t *scales;  // [n][G]
+    const uint16_t *scales;  // [n][G] fp16 scales, or null with fp8 scales:
+    const uint8_t *sc8;      //   [n][G] scale bytes (E4M3 value, or 0x80 | fallback index)
+    const float *rowf;       //   [n] row factors
+    const uint16_t *fb;      //   [n][fbs] fp16 fallback scales
+    int32_t fbs;
     const uint8_t *zeros;    // [n][G], or null (implied midpoint zmid)
     uint32_t zmid;
     const int32_t *rowptr;
@@ -104,6 +109,35 @@ struct HostArgs {
     int bits;
     int64_t total_bytes;  // n * k * b / 8
 };
+
+// Value of an E4M3 byte (OCP 8-bit float: sign, 4-bit exponent with bias 7, 3-bit mantissa;
+// exponent 0 holds the subnormals man * 2^-9; 0x7F and 0xFF are NaN).
+float e4m3_value(uint32_t b)
+{
+    const uint32_t e = (b >> 3) & 15, man = b & 7;
+    float v;
+    if (e == 15 && man == 7)
+        v = __builtin_nanf("");
+    else if (e == 0)
+        v = (float)man * 0x1p-9f;
+    else
+        v = ldexpf(1.0f + (float)man * 0.125f, (int)e - 7);
+    return (b & 0x80) ? -v : v;
+}
+
+// The fp32 scale of group g of row r: the fp16 scale, or with fp8 scales the row factor
+// times the byte's E4M3 value (the stored scale, one fp32 product), or for a byte with bit 7
+// set the fp16 fallback it indexes (clamped to the row's list; 0 without one).
+inline float group_scale(const HostArgs &a, int64_t r, int64_t g)
+{
+    if (!a.sc8) return half_to_float(a.scales[r * a.G + g]);
+    const uint32_t b = a.sc8[r * a.G + g];
+    if (b & 0x80) {
+        const int j = (int)(b & 0x7F) < a.fbs - 1 ? (int)(b & 0x7F) : a.fbs - 1;
+        return j >= 0 ? half_to_float(a.fb[r * a.fbs + j]) : 0.0f;
+    }
+    return a.rowf[r] * e4m3_value(b);
+}
 
 // Outliers of row r added in fp32, then the one fp16 rounding.
 void finish_row(const HostArgs &a, int64_t r, const float *acc)
@@ -127,7 +161,7 @@ void rows_scalar(const HostArgs &a, int64_t r0, int64_t r1)
         for (int64_t mm = 0; mm < a.m; ++mm) acc[mm] = 0.f;
         const uint8_t *row = a.w + r * rb;
         for (int64_t g = 0; g < a.G; ++g) {
-            const float s = half_to_float(a.scales[r * a.G + g]);
+            const float s = group_scale(a, r, g);
             const float zp = (float)(a.zeros ? a.zeros[r * a.G + g] : a.zmid);
             for (int64_t mm = 0; mm < a.m; ++mm) {
                 float sq = 0.f, sx = 0.f;
@@ -234,7 +268,7 @@ QP_AVX2 void rows_avx2_tile(const HostArgs &a, int64_t r0, const Unpacker &u)
         }
         for (int i = 0; i < R; ++i) {
             const int64_t r = r0 + i;
-            const float s = half_to_float(a.scales[r * a.G + g]);
+            const float s = group_scale(a, r, g);
             const float zp = (float)(a.zeros ? a.zeros[r * a.G + g] : a.zmid);
             const __m256 vs = _mm256_set1_ps(s), vnz = _mm256_set1_ps(-zp);
             for (int mm = 0; mm < M; ++mm)
@@ -314,7 +348,6 @@ QP_AVX512 void rows_avx512_tile(const HostArgs &a, int64_t r0, const Unpacker512
     const __m512 vpw = _mm512_set1_ps((float)(1 << b));
     const uint8_t *p = a.w + r0 * (a.k * b / 8);  // the R rows are consecutive: one stream per row
     const int64_t rb = a.k * b / 8;
-    const uint16_t *sc = a.scales + r0 * a.G;
     const uint8_t *zp8 = a.zeros ? a.zeros + r0 * a.G : nullptr;
     __m512 tot[R][M];
     for (int i = 0; i < R; ++i)
@@ -343,7 +376,7 @@ QP_AVX512 void rows_avx512_tile(const HostArgs &a, int64_t r0, const Unpacker512
             }
         }
         for (int i = 0; i < R; ++i) {
-            const float s = _cvtsh_ss(sc[i * a.G + g]);
+            const float s = group_scale(a, r0 + i, g);
             const float zp = (float)(zp8 ? zp8[i * a.G + g] : a.zmid);
             const __m512 vs = _mm512_set1_ps(s), vnc = _mm512_set1_ps(-((float)(1 << b) + zp));
             for (int mm = 0; mm < M; ++mm)
@@ -426,17 +459,28 @@ extern "C" qp_status qlinear_gemv_host(const qp_weight_desc *d, const qp_weight 
         return qp::fail(QP_ERR_UNSUPPORTED, "qlinear_gemv_host reads the canonical layout");
     if (d->zero_mode == QP_ZERO_PACKED)
         return qp::fail(QP_ERR_UNSUPPORTED, "qlinear_gemv_host reads byte or implied zero points");
-    if (d->scale_format != QP_SCALE_FP16) return qp::fail(QP_ERR_UNSUPPORTED, "qlinear_gemv_host reads fp16 scales");
     if (m < 1 || m > 8) return qp::fail(QP_ERR_UNSUPPORTED, "qlinear_gemv_host handles 1 <= m <= 8 (m=%lld)", (long long)m);
     if (ldx < d->k || ldy < d->n) return qp::fail(QP_ERR_INVALID_ARG, "qlinear_gemv_host: ldx < k or ldy < n");
-    if (!w->packed || !w->scales || (d->zero_mode == QP_ZERO_STORED && !w->zeros))
+    const bool fp8 = d->scale_format == QP_SCALE_FP8;
+    if (!w->packed || (!fp8 && !w->scales) || (d->zero_mode == QP_ZERO_STORED && !w->zeros))
         return qp::fail(QP_ERR_INVALID_ARG, "qlinear_gemv_host: packed/scales/zeros NULL");
+    if (fp8) {
+        if (!w->scales8 || !w->row_factors) return qp::fail(QP_ERR_INVALID_ARG, "qlinear_gemv_host: scales8/row_factors NULL");
+        if (w->fb_stride < 0 || w->fb_stride > 128 || (w->fb_stride > 0 && !w->fb_scales))
+            return qp::fail(QP_ERR_INVALID_ARG, "qlinear_gemv_host: bad fallback list");
+        if (w->nnz != 0 || w->csr_rowptr)
+            return qp::fail(QP_ERR_UNSUPPORTED, "qlinear_gemv_host: fp8-scale weights carry no outlier CSR");
+    }
     if (w->nnz < 0 || (w->nnz > 0 && (!w->csr_rowptr || !w->csr_col || !w->csr_val)))
         return qp::fail(QP_ERR_INVALID_ARG, "qlinear_gemv_host: bad outlier CSR");
     if (threads < 0) return qp::fail(QP_ERR_INVALID_ARG, "qlinear_gemv_host: threads < 0");
     HostArgs a;
     a.w = (const uint8_t *)w->packed;
-    a.scales = w->scales;
+    a.scales = fp8 ? nullptr : w->scales;
+    a.sc8 = fp8 ? w->scales8 : nullptr;
+    a.rowf = fp8 ? w->row_factors : nullptr;
+    a.fb = fp8 && w->fb_stride > 0 ? w->fb_scales : nullptr;
+    a.fbs = fp8 ? (int32_t)w->fb_stride : 0;
     a.zeros = d->zero_mode == QP_ZERO_STORED ? w->zeros : nullptr;
     a.zmid = 1u << (d->bits - 1);
     a.rowptr = w->nnz > 0 ? w->csr_rowptr : nullptr;

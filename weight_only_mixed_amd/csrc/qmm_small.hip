@@ -77,7 +77,8 @@ __device__ __forceinline__ void e4m3_pair(uint32_t w, float &a, float &b)
 
 // ---- decode GEMV: one workgroup per 16-row block, NW waves take its k-tiles round-robin --
 //
-// Decode is latency- and VALU-bound at these sizes (a 4096 x 4096 layer is a few MB).  Every
+// Decode is bound by the launch and the latency of each wave's few tiles at these sizes (a
+// 4096 x 4096 layer is a few MB), not by bandwidth or vector work.  Every
 // operand of a k-tile -- packed codes, the activation rows, scales and zero points -- is
 // copied HBM -> LDS by buffer-to-LDS DMA into a per-wave ring of D slots, issued D-1 tiles
 // ahead, so bytes in flight cost no registers and a CU holds many waves.  Each DMA reads at
@@ -91,7 +92,6 @@ __device__ __forceinline__ void e4m3_pair(uint32_t w, float &a, float &b)
 struct GemvBufs {
     rsrc_t w, sc, zr, x;
     uint32_t zrow;  // bytes per row of b-bit zero points (kMetaPacked); 0 otherwise
-    uint32_t vw, vw8, vz, vs, vx;  // per-lane offsets
     int64_t G;
 };
 
