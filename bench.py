@@ -526,6 +526,28 @@ def bench_prefill(q, torch, workloads, stream):
     return roof
 
 
+def bench_gemv_large(q, torch, workloads, stream):
+    """Decode GEMV on the prefill case's 70B-style FFN weight (N=28672, K=8192, 4-bit g=128, no
+    outliers: 124 MB with its metadata) at M = 1 and 8, over a >= 1 GiB rotation: the kernel's
+    streaming rate once one launch carries enough bytes to hide the launch and its first
+    fetches."""
+    dev = torch.device("cuda")
+    wp, _ = workloads.prefill_weights()
+    dp, wt = quantize_pack(q, torch, wp, 4)
+    del wp
+    N, K = workloads.PREFILL_N, workloads.PREFILL_K
+    nb = weight_bytes(N, K, 4)
+    out = {}
+    for m in (1, 8):
+        x = torch.from_numpy(workloads.activations_fp16(m, K, workloads.seed_for(4)).view(np.int16)).to(dev)
+        y = torch.empty((m, N), dtype=torch.int16, device=dev)
+        line = gemv_line(q, torch, stream, dp, wt, nb, x, m, y, N)
+        line["kernel"] = gemv_kernel_name(4, m, N)
+        out[f"n{N}_k{K}_b4_m{m}"] = line
+    del wt
+    return out
+
+
 def bench_prefill_variants(q, torch, workloads, stream):
     """The prefill GEMM (M=512, K=8192, N=28672, no outliers) for the metadata variants of the
     mixed-bit page (s2.3): groups of 64 and 32, symmetric groups, zero points in b bits, fp8
@@ -809,6 +831,8 @@ def main():
     if not args.no_prefill:
         log("bench: prefill GEMM M=512 K=8192 N=28672 4-bit + 0.1% outliers")
         extra["roofline_prefill"] = bench_prefill(q, torch, workloads, stream)
+        log("bench: decode GEMV on the same 28672x8192 4-bit weight, M=1 and 8")
+        extra["gemv_large_70b_ffn"] = bench_gemv_large(q, torch, workloads, stream)
         log("bench: integer-dot prefill (int8 activations) M=512 K=8192 N=28672 4-bit")
         extra["roofline_prefill_a8"] = bench_prefill_a8(q, torch, workloads, stream)
         if not args.no_variants:
