@@ -509,6 +509,25 @@ def bench_prefill(q, torch, workloads, stream):
     wsp = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
     ms = time_graph(torch, lambda i: q.qlinear_gemm(dp, hp, xp, Kp, Mp, yp, Np, wsp, wsb), 10, stream)
     ms_dense = time_graph(torch, lambda i: q.qlinear_gemm(dp, hd, xp, Kp, Mp, yp, Np, None, 0), 10, stream)
+    # one GPU's share under 8-way column parallelism: the first N/8 rows of the same quantized
+    # weight with their outliers; with the split workspace (k in parts) and without
+    ns = Np // 8
+    ds = q.desc(4, ns, Kp, q.QP_LAYOUT_DEVICE)
+    nnz_s = int(wt["rowptr"][ns].item())
+    hs = q.weight(wt["packed"], wt["scales"], wt["zeros"], wt["rowptr"], wt["col"], wt["val"], nnz_s)
+    ys = torch.empty((Mp, ns), dtype=torch.int16, device=dev)
+    wsb_s = q.qlinear_gemm_workspace_bytes(ds, Mp, nnz_s)
+    wsb_o = (2 * Kp + 4 * ns) * ((Mp + 127) // 128 * 128)  # the outlier part alone: no split
+    ws_s = torch.empty(wsb_s, dtype=torch.uint8, device=dev)
+    ms_s = time_graph(torch, lambda i: q.qlinear_gemm(ds, hs, xp, Kp, Mp, ys, ns, ws_s, wsb_s), 10, stream)
+    ms_u = time_graph(torch, lambda i: q.qlinear_gemm(ds, hs, xp, Kp, Mp, ys, ns, ws_s, wsb_o), 10, stream)
+    fl_s = 2 * Mp * ns * Kp + 2 * Mp * nnz_s
+    shard = dict(shape=dict(m=Mp, k=Kp, n=ns, nnz=nnz_s), k_parts=(wsb_s - wsb_o) // (4 * Mp * ns) if wsb_s > wsb_o else 1,
+                 us=round(ms_s * 1e3, 2), TFLOPs=round(fl_s / (ms_s * 1e-3) / 1e12, 1),
+                 frac_mfma_peak=round(fl_s / (ms_s * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                 unsplit_us=round(ms_u * 1e3, 2),
+                 unsplit_TFLOPs=round(fl_s / (ms_u * 1e-3) / 1e12, 1))
+    del ws_s, ys
     dense_flops = 2 * Mp * Np * Kp
     flops = dense_flops + 2 * Mp * wt["nnz"]
     tf = flops / (ms * 1e-3) / 1e12
@@ -522,7 +541,7 @@ def bench_prefill(q, torch, workloads, stream):
                 dense_kernel_alone=dict(achieved=round(tf_dense, 1), frac=round(tf_dense / MFMA_F16_PEAK_TFLOPS, 4),
                                         avg_launch_us=round(ms_dense * 1e3, 2), flops_per_launch=dense_flops,
                                         kernel="qp::gemm_kernel<4, 0, 8> (no outliers)"),
-                weight_bytes=wbytes)
+                weight_bytes=wbytes, tp8_shard=shard)
     return roof
 
 

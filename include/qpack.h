@@ -279,10 +279,15 @@ qp_status qlinear_gemv_batch(const qp_gemv_problem *problems, int32_t count, voi
  * scales are applied per group in fp32 (QP_SCALE_FP8: the row factor times the E4M3 value,
  * rounded once in fp32 as the quantizer stores it, or the fallback's fp16 scale; a fallback
  * index past the list reads its last slot, 0 for an empty list).
- *  workspace/ws_bytes  device scratch of at least qlinear_gemm_workspace_bytes(desc, m,
- *           w->nnz) bytes, 16-byte aligned, only needed when w carries outliers (NULL/0
- *           otherwise).  It holds x transposed (k * ldt fp16) and the fp32 outlier partial
- *           (n * ldt floats), ldt = m rounded up to 128: (2k + 4n) * ldt bytes.
+ *  workspace/ws_bytes  device scratch, 16-byte aligned; qlinear_gemm_workspace_bytes(desc, m,
+ *           w->nnz) bytes (0 for a dense weight whose output fills the GPU: NULL/0 then).
+ *           Parts, in order: with outliers, x transposed (k * ldt fp16) and the fp32 outlier
+ *           partial (n * ldt floats), ldt = m rounded up to 128, i.e. (2k + 4n) * ldt bytes
+ *           (required); then, for shapes whose 256 x 128 output tiles fill at most half of
+ *           the GPU's 256 CUs, the fp32 partials of S = 2, 4 or 8 k parts (4 * S * m * n bytes,
+ *           at the next multiple of 256): with them the GEMM splits k into S parts and a
+ *           second pass sums the parts (in part order) and the outlier partial before the one
+ *           fp16 rounding.  A workspace without that part runs the GEMM unsplit.
  *  Limits: x, the packed weight, and each workspace part under 2 GiB.
  */
 size_t qlinear_gemm_workspace_bytes(const qp_weight_desc *desc, int64_t m, int64_t nnz);

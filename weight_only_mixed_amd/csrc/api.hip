@@ -405,12 +405,28 @@ qp_status qlinear_gemv_batch(const qp_gemv_problem *problems, int32_t count, voi
     return device(launch_gemv_batch(b, blocks, m_max, S(stream)), "qlinear_gemv_batch");
 }
 
-size_t qlinear_gemm_workspace_bytes(const qp_weight_desc *d, int64_t m, int64_t nnz)
+// Workspace of qlinear_gemm: the outlier add-back's x^T and fp32 partial (nnz > 0), then the
+// fp32 partials of a k-split GEMM (when its output tiles would leave most CUs idle).
+static size_t gemm_outlier_bytes(const qp_weight_desc *d, int64_t m, int64_t nnz)
 {
-    if (check_desc(d, false) != QP_OK || m < 1 || m > (1LL << 24) || nnz <= 0) return 0;
+    if (nnz <= 0) return 0;
     const int64_t per = d->k * 2 + d->n * 4;  // n*k <= 2^40 keeps this far from overflow
     if (prod_over(per, gemm_xt_ld(m), 1, 1LL << 62)) return 0;
     return (size_t)(per * gemm_xt_ld(m));
+}
+static size_t gemm_split_bytes(const qp_weight_desc *d, int64_t m)
+{
+    const int s = gemm_split_parts(m, d->n, d->k);
+    if (s < 2 || prod_over(m, d->n, 4 * s, 1LL << 40)) return 0;
+    return (size_t)(4 * s * m * d->n);
+}
+
+size_t qlinear_gemm_workspace_bytes(const qp_weight_desc *d, int64_t m, int64_t nnz)
+{
+    if (check_desc(d, false) != QP_OK || m < 1 || m > (1LL << 24)) return 0;
+    const size_t o = gemm_outlier_bytes(d, m, nnz);
+    const size_t sp = gemm_split_bytes(d, m);
+    return sp ? (o + 255) / 256 * 256 + sp : o;
 }
 
 qp_status qlinear_gemm(const qp_weight_desc *d, const qp_weight *w, const uint16_t *x, int64_t ldx, int64_t m,
@@ -429,18 +445,26 @@ qp_status qlinear_gemm(const qp_weight_desc *d, const qp_weight *w, const uint16
     a.zmid = zero_pair(d);
     a.gs = d->group_size;
     a.zrow = d->zero_mode == QP_ZERO_PACKED ? (uint32_t)zero_row_bytes(d) : 0u;
+    const size_t need_o = gemm_outlier_bytes(d, m, w->nnz);
     if (w->nnz > 0) {
         if (prod_over(d->k, gemm_xt_ld(m), 2, 0x7FFFFFFFLL) || prod_over(d->n, gemm_xt_ld(m), 4, 0x7FFFFFFFLL))
             return fail(QP_ERR_UNSUPPORTED, "m*k or m*n too large for the outlier add-back");
-        const size_t need = qlinear_gemm_workspace_bytes(d, m, w->nnz);
-        if (!workspace || ws_bytes < need || !aligned(workspace, 16))
-            return fail(QP_ERR_WORKSPACE, "outlier add-back needs %zu bytes of workspace (16-byte aligned)", need);
+        if (!workspace || ws_bytes < need_o || !aligned(workspace, 16))
+            return fail(QP_ERR_WORKSPACE, "outlier add-back needs %zu bytes of workspace (16-byte aligned)", need_o);
         a.rowptr = w->csr_rowptr;
         a.col = w->csr_col;
         a.val = w->csr_val;
         a.ldxt = gemm_xt_ld(m);
         a.xt = (uint16_t *)workspace;
         a.spart = (float *)((uint8_t *)workspace + d->k * a.ldxt * 2);
+    }
+    // A workspace large enough for the k-split partials as well turns the split on (a shape
+    // whose output tiles leave most CUs idle); without one the GEMM runs unsplit.
+    const size_t need_s = gemm_split_bytes(d, m);
+    const size_t off_s = (need_o + 255) / 256 * 256;
+    if (need_s && workspace && aligned(workspace, 16) && ws_bytes >= off_s + need_s) {
+        a.ksplit = gemm_split_parts(m, d->n, d->k);
+        a.parts = (float *)((uint8_t *)workspace + off_s);
     }
     a.x = x;
     a.ldx = ldx;

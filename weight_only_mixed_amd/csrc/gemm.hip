@@ -92,6 +92,32 @@ __global__ __launch_bounds__(256) void outlier_spmm_kernel(const int32_t *rowptr
 
 int64_t gemm_xt_ld(int64_t m) { return (m + gk::GeoLayer::kMRows - 1) / gk::GeoLayer::kMRows * gk::GeoLayer::kMRows; }
 
+// Split k when the output tiles fill at most half of the CUs: double the parts while the
+// workgroups stay within one per CU and each part keeps whole 512-k tile pairs (at most 8).
+int gemm_split_parts(int64_t m, int64_t n, int64_t k)
+{
+    constexpr int64_t kCUs = 256;
+    const int64_t tiles = (n + gk::GeoLayer::kNT - 1) / gk::GeoLayer::kNT * ((m + gk::GeoLayer::kMRows - 1) / gk::GeoLayer::kMRows);
+    int s = 1;
+    while (s < 8 && tiles * 2 * s <= kCUs && k % (512 * 2 * s) == 0) s *= 2;
+    return s;
+}
+
+// The split GEMM's reduction: y[r][c] = fp16(sum of the ksplit fp32 partials in part order),
+// rounded once (the first part started from the outlier partial).  Four outputs per thread.
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float *parts, int32_t nparts, int64_t pstride,
+                                                           int64_t m, int64_t n, uint16_t *y, int64_t ldy)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (row, 4-column) index
+    const int64_t q = n / 4;
+    if (i >= m * q) return;
+    const int64_t row = i / q, c = 4 * (i % q);
+    f4 acc = *(const f4 *)(parts + row * n + c);
+    for (int32_t s = 1; s < nparts; ++s) acc += *(const f4 *)(parts + s * pstride + row * n + c);
+    uint16_t *dst = y + row * ldy + c;
+    *(u2 *)dst = (u2){pack_h2(acc[0], acc[1]), pack_h2(acc[2], acc[3])};
+}
+
 template <int ZPK>
 static hipError_t gemm_zp(int bits, bool outl, const GemmArgs &a, hipStream_t st)
 {
@@ -110,6 +136,23 @@ hipError_t launch_gemm(int bits, const GemmArgs &a, hipStream_t st)
                            st, a.x, a.ldx, a.m, a.k, a.xt, a.ldxt);
         hipLaunchKernelGGL(outlier_spmm_kernel, dim3((unsigned)((a.n + 3) / 4), (unsigned)((a.ldxt + 511) / 512)),
                            dim3(256), 0, st, a.rowptr, a.col, a.val, a.xt, a.n, a.ldxt, a.spart);
+    }
+    if (a.ksplit > 1) {
+        // k parts into fp32 partial rows (the first seeded from the outlier partial), then one
+        // pass sums them
+        GemmArgs g = a;
+        if (!a.rowptr) g.spart = nullptr;
+        g.y = a.parts;
+        g.ldy = a.n;
+        g.ysplit = a.m * a.n;
+        hipError_t e = a.fp8    ? gemm_zp<gk::kZpFp8>(bits, false, g, st)
+                       : a.zrow ? gemm_zp<gk::kZpPacked>(bits, false, g, st)
+                                : gemm_zp<gk::kZpByte>(bits, false, g, st);
+        if (e != hipSuccess) return e;
+        const int64_t items = a.m * (a.n / 4);
+        hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st, a.parts,
+                           a.ksplit, a.m * a.n, a.m, a.n, (uint16_t *)a.y, a.ldy);
+        return hipGetLastError();
     }
     if (a.fp8) return gemm_zp<gk::kZpFp8>(bits, a.rowptr != nullptr, a, st);
     return a.zrow ? gemm_zp<gk::kZpPacked>(bits, a.rowptr != nullptr, a, st)

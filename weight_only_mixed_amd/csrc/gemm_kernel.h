@@ -477,9 +477,9 @@ __device__ __forceinline__ void k_loop(const Bufs &bf, uint8_t *__restrict__ xs0
 }
 
 
-// Kernel modes: a plain layer, the same with outliers, or routed experts with one of the three
-// grouped epilogues.
-enum { kPlain = 0, kOutl = 1, kGroupNone = 2, kGroupSwiglu = 3, kGroupRowsF32 = 4 };
+// Kernel modes: a plain layer, the same with outliers, routed experts with one of the three
+// grouped epilogues, or a plain layer split into k parts writing fp32 partial rows.
+enum { kPlain = 0, kOutl = 1, kGroupNone = 2, kGroupSwiglu = 3, kGroupRowsF32 = 4, kSplitF32 = 5 };
 
 // Workgroup -> (weight tile, activation rows) of a plain layer: up to two rectangles of
 // weight tiles [nt0, nt0 + nnt) x activation tiles of mh rows starting at row m0, numbered
@@ -522,15 +522,16 @@ template <int B, int MODE, int NMT, typename GE, int GS, int ZPK>
 __global__ __launch_bounds__(GE::kWaves * 64) __attribute__((amdgpu_waves_per_eu(GE::kWavesPerEU, GE::kWavesPerEU))) void gemm_kernel(
     GemmArgs a, TilePlan plan)
 {
-    constexpr bool OUTL = MODE == kOutl, GROUPED = MODE >= kGroupNone;
+    constexpr bool OUTL = MODE == kOutl, GROUPED = MODE >= kGroupNone && MODE <= kGroupRowsF32;
+    constexpr bool KSPLIT = MODE == kGroupRowsF32 || MODE == kSplitF32;
     constexpr int kMT = GE::kMT, kMRows = GE::kMRows;
     __shared__ __attribute__((aligned(16))) Smem<B, GE> sm;
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t = lane >> 4, r = lane & 15;
     const int64_t KT = a.k / kTileK, G = a.k / GS;  // G: groups per weight row
-    // k range: all of k, or part blockIdx.z of a.ksplit equal parts (grouped fp32 rows)
+    // k range: all of k, or part blockIdx.z of a.ksplit equal parts (fp32 rows)
     int64_t kt0 = 0, KTp = KT;
-    if constexpr (MODE == kGroupRowsF32) {
+    if constexpr (KSPLIT) {
         if (a.ksplit > 1) {
             KTp = KT / a.ksplit;
             kt0 = (int64_t)blockIdx.z * KTp;
@@ -609,22 +610,30 @@ __global__ __launch_bounds__(GE::kWaves * 64) __attribute__((amdgpu_waves_per_eu
     }
 
     f4 tot[kRBW][kMT];
-    if constexpr (OUTL) {
+    // the outlier partial seeds the accumulators of an outlier layer, and of the first k part
+    // of a split one (the parts are summed afterwards)
+    bool seed = false;
+    if constexpr (OUTL) seed = true;
+    if constexpr (MODE == kSplitF32) seed = blockIdx.z == 0 && a.spart != nullptr;
+    if constexpr (OUTL || MODE == kSplitF32) {
         static_assert(kMT == 8, "the outlier partial's layout holds eight tiles per position block");
-        // accumulators start from the outlier partial S^T (rows past n read as zeros): inside
-        // each 128-row block, activation row 16 mt + 4 t + i sits at position 32 t + 4 mt + i,
-        // so a lane's tot[u][0..7] are 32 consecutive floats of weight row rb * 16 + r
-        const rsrc_t sr = make_rsrc(a.spart, a.n * a.ldxt * 4);
+        if (seed) {
+            // accumulators start from S^T (rows past n read as zeros): inside each 128-row
+            // block, activation row 16 mt + 4 t + i sits at position 32 t + 4 mt + i, so a
+            // lane's tot[u][0..7] are 32 consecutive floats of weight row rb * 16 + r
+            const rsrc_t sr = make_rsrc(a.spart, a.n * a.ldxt * 4);
 #pragma unroll
-        for (int u = 0; u < kRBW; ++u) {
-            const uint32_t off = (uint32_t)((((rb0 + u) * kTileN + r) * a.ldxt + m0 + 32 * t) * 4);
+            for (int u = 0; u < kRBW; ++u) {
+                const uint32_t off = (uint32_t)((((rb0 + u) * kTileN + r) * a.ldxt + m0 + 32 * t) * 4);
 #pragma unroll
-            for (int mt = 0; mt < kMT; ++mt) {
-                const u4 v = ld16(sr, off + 16 * mt);
-                tot[u][mt] = (f4){as_f(v[0]), as_f(v[1]), as_f(v[2]), as_f(v[3])};
+                for (int mt = 0; mt < kMT; ++mt) {
+                    const u4 v = ld16(sr, off + 16 * mt);
+                    tot[u][mt] = (f4){as_f(v[0]), as_f(v[1]), as_f(v[2]), as_f(v[3])};
+                }
             }
         }
-    } else {
+    }
+    if (!seed) {
 #pragma unroll
         for (int u = 0; u < kRBW; ++u)
 #pragma unroll
@@ -659,7 +668,7 @@ __global__ __launch_bounds__(GE::kWaves * 64) __attribute__((amdgpu_waves_per_eu
                 if (row >= mend) continue;
                 float v = tot[u][mt][i];
                 if constexpr (ZPK == kZpFp8) v *= rowf[u];
-                if constexpr (MODE == kGroupRowsF32) {
+                if constexpr (KSPLIT) {
                     ((float *)a.y)[(int64_t)blockIdx.z * a.ysplit + row * a.ldy + rb * kTileN + r] = v;
                 } else if constexpr (MODE == kGroupSwiglu) {
                     // row blocks 2j (gate) and 2j+1 (up) of a wave: output feature 16 j + r
@@ -686,18 +695,20 @@ static inline TilePlan one_rect(int32_t nt0, int32_t nnt, int32_t m0, int32_t mt
     return p;
 }
 
-// Whole 128-row activation tiles in one launch, a ragged last tile in another.
+// Whole 128-row activation tiles in one launch, a ragged last tile in another (kSplitF32: each
+// with a.ksplit k parts as the grid's third dimension).
 template <int B, int MODE, int GS, int ZPK>
 void gemm_launch(const GemmArgs &a, hipStream_t st)
 {
     using GE = GeoLayer;
     const int32_t NT = (int32_t)((a.n + GE::kNT - 1) / GE::kNT), F = (int32_t)(a.m / GE::kMRows);
+    const unsigned parts = MODE == kSplitF32 ? (unsigned)a.ksplit : 1u;
     const dim3 block(GE::kWaves * 64);
     if (F > 0)
-        hipLaunchKernelGGL((gemm_kernel<B, MODE, GE::kMT, GE, GS, ZPK>), dim3((unsigned)((int64_t)NT * F)), block, 0,
-                           st, a, one_rect(0, NT, 0, F, GE::kMRows));
+        hipLaunchKernelGGL((gemm_kernel<B, MODE, GE::kMT, GE, GS, ZPK>), dim3((unsigned)((int64_t)NT * F), 1, parts),
+                           block, 0, st, a, one_rect(0, NT, 0, F, GE::kMRows));
     if (a.m % GE::kMRows)
-        hipLaunchKernelGGL((gemm_kernel<B, MODE, 0, GE, GS, ZPK>), dim3((unsigned)NT), block, 0, st, a,
+        hipLaunchKernelGGL((gemm_kernel<B, MODE, 0, GE, GS, ZPK>), dim3((unsigned)NT, 1, parts), block, 0, st, a,
                            one_rect(0, NT, F * GE::kMRows, 1, GE::kMRows));
 }
 
@@ -706,7 +717,16 @@ void gemm_launch(const GemmArgs &a, hipStream_t st)
 template <int GS, int ZPK>
 hipError_t gemm_main(int bits, bool outl, const GemmArgs &a, hipStream_t st)
 {
-    if constexpr (ZPK == kZpFp8) {  // fp8-scale weights carry no outliers
+    if (a.ksplit > 1) {  // k parts into fp32 partial rows (the caller sums them, outliers included)
+        switch (bits) {
+        case 2: gemm_launch<2, kSplitF32, GS, ZPK>(a, st); break;
+        case 3: gemm_launch<3, kSplitF32, GS, ZPK>(a, st); break;
+        case 4: gemm_launch<4, kSplitF32, GS, ZPK>(a, st); break;
+        case 5: gemm_launch<5, kSplitF32, GS, ZPK>(a, st); break;
+        case 6: gemm_launch<6, kSplitF32, GS, ZPK>(a, st); break;
+        default: return hipErrorInvalidValue;
+        }
+    } else if constexpr (ZPK == kZpFp8) {  // fp8-scale weights carry no outliers
         if (outl) return hipErrorInvalidValue;
         switch (bits) {
         case 2: gemm_launch<2, kPlain, GS, ZPK>(a, st); break;

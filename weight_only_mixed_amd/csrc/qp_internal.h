@@ -103,14 +103,19 @@ struct GemmArgs {
     uint32_t zmid;  // 0: stored zero points; else the implied pair (2^(b-1) in both bytes)
     uint32_t zrow;  // 0: one zero-point byte per group; else bytes per row of b-bit zero points
     int32_t gs;     // group size: 128, 64 or 32
-    int32_t ksplit;  // grouped fp32 rows: k in ksplit equal parts (0 or 1: whole k); part s
-    int64_t ysplit;  //   writes its partial rows at y + s * ysplit floats
+    int32_t ksplit;  // fp32 rows: k in ksplit equal parts (0 or 1: whole k); part s writes its
+    int64_t ysplit;  //   partial rows at y + s * ysplit floats (grouped), or at parts + s * ysplit
+                     //   (the layer GEMM, summed into y by the split reduction)
+    float *parts;    // layer GEMM with ksplit > 1: workspace of ksplit fp32 [m][n] partials
     int32_t fp8;    // 1: E4M3 scales for every expert (ex[e].scales holds the bytes)
     uint16_t *xt;   // workspace (outliers only): x transposed, [k][ldxt]
     float *spart;   // workspace (outliers only): fp32 outlier partial, [n][ldxt]
     int64_t ldxt;
 };
 int64_t gemm_xt_ld(int64_t m);
+// k parts the layer GEMM splits into for an m x n output with k columns (1: no split): enough
+// to give the GPU's CUs a workgroup each when the output tiles alone leave most idle.
+int gemm_split_parts(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm(int bits, const GemmArgs &a, hipStream_t st);
 hipError_t launch_grouped(int bits, int epilogue, int n_experts, const GemmArgs &a, hipStream_t st);
 
