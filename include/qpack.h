@@ -110,10 +110,10 @@ enum { QP_ZERO_STORED = 0, QP_ZERO_MIDPOINT = 1, QP_ZERO_PACKED = 2 };
  *                    mantissa; 0x7F is NaN); the scale is row_factors[n] times that value;
  *                  - bit 7 set: the scale is the fp16 fb_scales[n * fb_stride + (byte & 0x7F)].
  *                 Written by qpack_quantize_fp8; read by qlinear_gemv, qlinear_gemv_batch (one
- *                 scale format per batch), qlinear_gemm, qlinear_grouped_gemm, qmoe_ffn and
- *                 qlinear_gemv_host (byte or implied zero points; every problem or expert
- *                 brings its own scale bytes, row factors and fallback list).  qlinear_gemm_a8
- *                 and qp_blob_write return QP_ERR_UNSUPPORTED for it (qp_blob_bytes 0). */
+ *                 scale format per batch), qlinear_gemm, qlinear_gemm_a8, qlinear_grouped_gemm,
+ *                 qmoe_ffn and qlinear_gemv_host (byte or implied zero points; every problem or
+ *                 expert brings its own scale bytes, row factors and fallback list).
+ *                 qp_blob_write returns QP_ERR_UNSUPPORTED for it (qp_blob_bytes 0). */
 enum { QP_SCALE_FP16 = 0, QP_SCALE_FP8 = 1 };
 
 /* Shape and format of one quantized matrix W[n][k]. */
@@ -318,7 +318,9 @@ qp_status qact_quantize(const uint16_t *x, int64_t ldx, int64_t m, int64_t k, in
  * codes unpacked to 8-bit integers, integer dot products, the scale applied in fp32):
  *     y[m][n] = fp16( x_scales[m] * sum_g s[n][g] * sum_{k in g} xq[m][k] * (q[n][k] - zp[n][g]) )
  * with each group's integer sum exact (int32) and the sum over groups in fp32.
- *  desc     QP_LAYOUT_DEVICE, group_size 128, any zero mode (stored, implied midpoint, b-bit).
+ *  desc     QP_LAYOUT_DEVICE, group_size 128, any zero mode (stored, implied midpoint, b-bit),
+ *           fp16 or fp8 scales (fp8: each group's fp32 sum times its E4M3 value, the row
+ *           factor once per output, or the fallback's fp16 scale).
  *  w        no outliers (w->nnz must be 0: the held-out weights are defined against the fp16
  *           activations; use qlinear_gemm for them).
  *  xq, x_scales  from qact_quantize (xq 16-byte aligned, m * k < 2^31).

@@ -335,6 +335,19 @@ def linear_a8(xq, sx, q: dict):
     return r
 
 
+def linear_a8_fp8(xq, sx, qd) -> np.ndarray:
+    """fp64 r = s_x * sum_g s_w * (integer group dot products of xq with q - zp) over a
+    quantize_fp8 result (its stored fp32 scales), the definition linear_a8 computes."""
+    xq = np.asarray(xq, np.int64)
+    M, K = xq.shape
+    g = qd["g"]
+    dq = qd["codes"].astype(np.int64) - np.repeat(qd["zeros"].astype(np.int64), g, 1)
+    N, G = dq.shape[0], K // g
+    isum = np.einsum("mgk,ngk->mng", xq.reshape(M, G, g), dq.reshape(N, G, g))  # exact integers
+    r = (isum.astype(np.float64) * qd["scales_f32"].astype(np.float64)[None]).sum(2)
+    return r * np.asarray(sx, np.float64)[:, None]
+
+
 def e4m3_value(code: int) -> float:
     return lib().or_e4m3_value(code)
 

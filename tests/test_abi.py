@@ -352,9 +352,10 @@ def test_int8_path_validation():
 
 def test_fp8_scale_validation():
     """QP_SCALE_FP8 (8-bit float scales with an fp16 fallback, mixed-bit page s2.3): only the
-    fp8 quantizer writes it; the GEMVs (device and host), the layer GEMM, the grouped GEMM and
-    the expert FFN read it; the other calls refuse it, and the fp8 calls check their buffers
-    before any launch (no call here gets past validation: every weight or shape is malformed)."""
+    fp8 quantizer writes it; the GEMVs (device and host), the layer GEMM, the int8-activation
+    GEMM, the grouped GEMM and the expert FFN read it; the blob refuses it, and the fp8 calls
+    check their buffers before any launch (no call here gets past validation: every weight or
+    shape is malformed)."""
     ok = dict(stream=0, check=False)
     f8 = q.desc(2, 256, 512, group_size=32, zero_mode=q.QP_ZERO_MIDPOINT, scale_format=q.QP_SCALE_FP8)
     fp16 = q.desc(2, 256, 512, group_size=32, zero_mode=q.QP_ZERO_MIDPOINT)
@@ -405,7 +406,8 @@ def test_fp8_scale_validation():
                                   FAKE, 256, **ok) == q.QP_ERR_INVALID_ARG
     assert q.qlinear_grouped_gemm(f8, [with_csr], FAKE, 512, FAKE, FAKE, 10, 0, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
     f8_128 = q.desc(4, 256, 512, zero_mode=q.QP_ZERO_MIDPOINT, scale_format=q.QP_SCALE_FP8)
-    assert q.qlinear_gemm_a8(f8_128, good, FAKE, FAKE, 4, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
+    assert q.qlinear_gemm_a8(f8_128, bad, FAKE, FAKE, 4, FAKE, 256, **ok) == q.QP_ERR_INVALID_ARG
+    assert q.qlinear_gemm_a8(f8_128, with_csr, FAKE, FAKE, 4, FAKE, 256, **ok) == q.QP_ERR_UNSUPPORTED
     gu = q.desc(4, 2 * 1024, 512, scale_format=q.QP_SCALE_FP8)
     dn = q.desc(4, 512, 1024, scale_format=q.QP_SCALE_FP8)
     assert q.qmoe_ffn(gu, [good] * 4, dn, [good] * 3 + [bad], FAKE, 512, 8, FAKE, FAKE, 2, FAKE, 512, FAKE, 1 << 30,

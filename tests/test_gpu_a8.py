@@ -124,3 +124,29 @@ def test_gemm_a8_prefill_full_sampled():
     got = y[:, ns]
     assert rel_err(got, r) <= TOL, report(got, r)
     assert np.isfinite(y).all()
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("sym", (False, True))
+def test_gemm_a8_fp8_scales(bits, sym):
+    """fp8 group scales with fallback groups on int8 activations: the integer group sums
+    scaled by the E4M3 values (or the fallback's fp16 scale) and the row factor, against the
+    oracle's integer-dot product over the same weights; a partial last weight tile and a
+    ragged activation block."""
+    from test_gpu_fp8 import GpuWeightFp8, plant_fallbacks
+    torch, q = gpu()
+    n, k, m = 560, 1536, 130
+    w = workloads.weights_fp16(n, k, 960 + bits)
+    plant_fallbacks(w, 128, 960 + bits, rows=(0, 300, 559))
+    x = workloads.activations_fp16(m, k, 961 + bits)
+    xq, sx = act_quantize_gpu(x)
+    rq, rs = oracle.act_quantize(x)
+    qd = oracle.quantize_fp8(w, bits, 128, sym=sym)
+    assert qd["counts"][300] == 3
+    g = GpuWeightFp8(w, bits, 128, sym)
+    y = torch.empty((m, n), dtype=torch.int16, device="cuda")
+    q.qlinear_gemm_a8(g.desc, g.handle(), xq, sx, m, y, n)
+    torch.cuda.synchronize()
+    got = from_dev_fp16(y)
+    r = oracle.linear_a8_fp8(rq, rs, qd)
+    assert rel_err(got, r) <= TOL, report(got, r)

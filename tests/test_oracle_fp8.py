@@ -159,3 +159,17 @@ def test_moe_ffn_fp8_equals_the_fp16_ffn_on_equal_scales():
     a = oracle.swiglu_act_fp8(x[:1], g, u).astype(np.float16)
     one = oracle.moe_ffn_fp8(x[:1], np.array([[1]], np.int32), np.array([[1.0]], np.float32), [g] * E, [u] * E, [dn] * E)
     assert np.array_equal(one, oracle.linear_fp8(a, dn))
+
+
+def test_linear_a8_fp8_equals_the_c_integer_dot_on_equal_scales():
+    """The int8-activation product over fp8-scale weights (numpy) against the C oracle's
+    integer-dot product when every stored scale is an fp16 value: same definition, same
+    integer group sums, so the two agree to fp64 rounding."""
+    w = workloads.weights_fp16(48, 512, 80)
+    x = workloads.activations_fp16(5, 512, 81)
+    xq, sx = oracle.act_quantize(x)
+    q16 = oracle.quantize(w, 3)
+    as8 = dict(codes=q16["codes"], zeros=q16["zeros"], g=128, scales_f32=q16["scales"].view(np.float16).astype(np.float32))
+    r16 = oracle.linear_a8(xq, sx, q16)
+    r8 = oracle.linear_a8_fp8(xq, sx, as8)
+    assert np.abs(r8 - r16).max() <= 1e-12 * np.abs(r16).max()

@@ -80,8 +80,7 @@ static qp_status need_fp16_scales(const qp_weight_desc *d, const char *who)
 {
     if (d->scale_format != QP_SCALE_FP16)
         return fail(QP_ERR_UNSUPPORTED,
-                    "%s reads fp16 scales (fp8 scales: qpack_quantize_fp8, qlinear_gemv, qlinear_gemv_batch, "
-                    "qlinear_gemm, qlinear_grouped_gemm, qmoe_ffn)",
+                    "%s reads fp16 scales (fp8 scales: qpack_quantize_fp8 writes them, every matmul reads them)",
                     who);
     return QP_OK;
 }
@@ -754,7 +753,6 @@ qp_status qlinear_gemm_a8(const qp_weight_desc *d, const qp_weight *w, const int
 {
     qp_status st = check_desc(d, true);
     if (st != QP_OK) return st;
-    if ((st = need_fp16_scales(d, "qlinear_gemm_a8")) != QP_OK) return st;
     if (d->group_size != kGroup) return fail(QP_ERR_UNSUPPORTED, "the int8 GEMM is built for groups of 128");
     if ((st = check_weight(d, w, false)) != QP_OK) return st;
     if (w->nnz > 0) return fail(QP_ERR_UNSUPPORTED, "outliers are not applied on int8 activations");
@@ -765,9 +763,10 @@ qp_status qlinear_gemm_a8(const qp_weight_desc *d, const qp_weight *w, const int
     if (m < 1) return fail(QP_ERR_INVALID_ARG, "m=%lld must be >= 1", (long long)m);
     if (prod_over(m, d->k, 1, 0x7FFFFFFFLL)) return fail(QP_ERR_UNSUPPORTED, "xq larger than 2 GiB");
     if ((int64_t)qp_packed_bytes(d) > 0x7FFFFFFFLL) return fail(QP_ERR_UNSUPPORTED, "packed weight larger than 2 GiB");
-    const ExpertPtrs ep{(const uint8_t *)w->packed, w->scales, w->zeros};
+    const ExpertPtrs ep = weight_ptrs(d, w);
     const uint32_t zrow = d->zero_mode == QP_ZERO_PACKED ? (uint32_t)zero_row_bytes(d) : 0u;
-    return device(launch_gemm_a8(d->bits, ep, xq, x_scales, m, d->n, d->k, zero_pair(d), zrow, y, ldy, S(stream)),
+    return device(launch_gemm_a8(d->bits, ep, d->scale_format == QP_SCALE_FP8, xq, x_scales, m, d->n, d->k, zero_pair(d),
+                                 zrow, y, ldy, S(stream)),
                   "qlinear_gemm_a8");
 }
 

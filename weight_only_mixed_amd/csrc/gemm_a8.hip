@@ -240,7 +240,7 @@ __device__ __forceinline__ void scale8(const SZ<kGroup> &zs, const i4v (&acc)[kR
 // tiles; scales and zero points (even steps) with the first half; the weight DMA (odd steps)
 // with the second half, after every activation piece, so the end-of-step wait can leave it in
 // flight.
-template <int B, bool ZPK, int PAR, int MT>
+template <int B, int ZPK, int PAR, int MT>
 __device__ __forceinline__ void issue_tile8(const Bufs &bf, const StepIO<PAR, kGroup> &io, int64_t G, int wv, int lane)
 {
     if constexpr (MT < kDmaX) dma_x8(bf, io.gx, io.xdst, wv, MT);
@@ -261,7 +261,7 @@ constexpr int kLag = 1, kAR = kLag + 1;  // integer sums are scaled one tile lat
 // Activation tile MT of a step: its fragment reads for tile MT + 2, the matrix-core chains of
 // tile MT (two K = 64 steps per row block, from zero), the scaling of tile MT - 2's integer
 // sums (their matrix-core ops finished a tile ago) and a share of the next group's unpack.
-template <int B, bool ZPK, int SH, int NH, int MT>
+template <int B, int ZPK, int SH, int NH, int MT>
 __device__ __forceinline__ void tile8(const i4v (&Wc)[kRBW][2], i4v (&Wn)[kRBW][2], const SZ<kGroup> &zs,
                                       const uint32_t (&zb)[kRBW], const uint8_t *xs, const uint8_t *wpart, int lane,
                                       uint32_t (&d)[kRBW][2 * B], i4v (&X)[kXR][2], i4v (&acc)[kAR][kRBW],
@@ -296,7 +296,7 @@ __device__ __forceinline__ void tile8(const i4v (&Wc)[kRBW][2], i4v (&Wn)[kRBW][
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int B, bool ZPK, int SH, int NH, int... MT>
+template <int B, int ZPK, int SH, int NH, int... MT>
 __device__ __forceinline__ void tiles8(std::integer_sequence<int, MT...>, const i4v (&Wc)[kRBW][2], i4v (&Wn)[kRBW][2],
                                        const SZ<kGroup> &zs, const uint32_t (&zb)[kRBW], const uint8_t *xs,
                                        const uint8_t *wpart, int lane, uint32_t (&d)[kRBW][2 * B], i4v (&X)[kXR][2],
@@ -309,7 +309,7 @@ __device__ __forceinline__ void tiles8(std::integer_sequence<int, MT...>, const 
 // One 128-k group step: Wc times the activation tile of this group (slot xs), scale half SH;
 // meanwhile the next group (half NH of staged tile wpart, zero points zn) is unpacked into Wn
 // and the loads io are issued.
-template <int B, bool ZPK, int SH, int NH>
+template <int B, int ZPK, int SH, int NH>
 __device__ __forceinline__ void step8(const i4v (&Wc)[kRBW][2], i4v (&Wn)[kRBW][2], const SZ<kGroup> &zs,
                                       const SZ<kGroup> &zn, const uint8_t *xs, const uint8_t *wpart, int lane,
                                       f4 (&tot)[kRBW][kMT], const Bufs &bf, const StepIO<NH ^ 1, kGroup> &io, int64_t G, int wv)
@@ -336,7 +336,7 @@ __device__ __forceinline__ void step8(const i4v (&Wc)[kRBW][2], i4v (&Wn)[kRBW][
 // during step 2t - 2.  Waits: vmcnt(0) after even steps, vmcnt(weight DMAs) after odd ones.
 // Loads past the end are clamped to the last group or tile; what is unpacked from them is
 // discarded.
-template <int B, bool ZPK>
+template <int B, int ZPK>
 __device__ __forceinline__ void k_loop8(const Bufs &bf, uint8_t *__restrict__ xs0, uint8_t *__restrict__ xs1,
                                         uint8_t *__restrict__ ws0, uint8_t *__restrict__ ws1, int64_t KT, int64_t G,
                                         int wv, int lane, f4 (&tot)[kRBW][kMT])
@@ -394,7 +394,7 @@ __device__ __forceinline__ void plan8(int64_t b, int64_t NT, int64_t MB, int64_t
     }
 }
 
-template <int B, bool ZPK>
+template <int B, int ZPK>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_a8_kernel(
     ExpertPtrs W, const int8_t *xq, const float *sx, int64_t m, int64_t n, int64_t k, uint32_t zmid, uint32_t zrow,
     uint16_t *y, int64_t ldy)
@@ -414,6 +414,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     bf.zrow = zrow;
     bf.kt0 = 0;
     bf.x = make_rsrc(xq, m * k);
+    bf.rowf = make_rsrc(W.rowf, W.rowf ? n * 4 : 0);
+    bf.row0 = (uint32_t)(rb0 * kTileN);
+    bf.fb = make_rsrc(W.fb, W.fb ? n * W.fb_stride * 2 : 0);
+    bf.fbs = W.fb_stride;
 #pragma unroll
     for (int it = 0; it < kDmaX; ++it) {
         const int row = 8 * (kDmaX * wv + it) + (lane >> 3);
@@ -426,7 +430,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
         const int64_t rb = rb0 + u;
         const bool in = rb < NB;
         bf.w[u] = make_rsrc(W.packed + rb * KT * (512 * B), in ? KT * (512 * B) : 0);
-        bf.sc[u] = make_rsrc(W.scales + rb * kTileN * G, in ? kTileN * G * 2 : 0);
+        if constexpr (ZPK == kZpFp8)  // scale bytes
+            bf.sc[u] = make_rsrc((const uint8_t *)W.scales + rb * kTileN * G, in ? kTileN * G : 0);
+        else
+            bf.sc[u] = make_rsrc(W.scales + rb * kTileN * G, in ? kTileN * G * 2 : 0);
         const int64_t zstride = zrow ? zrow : G;  // zero-point bytes per weight row
         bf.zr[u] = make_rsrc(W.zeros + rb * kTileN * zstride, in && !zmid ? kTileN * zstride : 0);
     }
@@ -443,6 +450,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     k_loop8<B, ZPK>(bf, sm.xs[0], sm.xs[1], sm.ws[0], sm.ws[1], KT, G, wv, lane, tot);
 
     // lane (t, r): activation rows 16 mt + 4 t + i of weight row rb * 16 + r
+    float rowf[kRBW];  // fp8 scales: each row block's weight-row factor (1 otherwise)
+#pragma unroll
+    for (int u = 0; u < kRBW; ++u) {
+        rowf[u] = 1.0f;
+        if constexpr (ZPK == kZpFp8)
+            if (rb0 + u < NB) rowf[u] = W.rowf[(rb0 + u) * kTileN + r];
+    }
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt) {
 #pragma unroll
@@ -454,7 +468,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
             for (int u = 0; u < kRBW; ++u) {
                 const int64_t rb = rb0 + u;
                 if (rb >= NB) continue;
-                y[row * ldy + rb * kTileN + r] = __builtin_bit_cast(uint16_t, (_Float16)(tot[u][mt][i] * s));
+                float v = tot[u][mt][i];
+                if constexpr (ZPK == kZpFp8) v *= rowf[u];
+                y[row * ldy + rb * kTileN + r] = __builtin_bit_cast(uint16_t, (_Float16)(v * s));
             }
         }
     }
@@ -462,19 +478,23 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
 
 }  // namespace
 
-hipError_t launch_gemm_a8(int bits, const ExpertPtrs &w, const int8_t *xq, const float *sx, int64_t m, int64_t n,
-                          int64_t k, uint32_t zmid, uint32_t zrow, uint16_t *y, int64_t ldy, hipStream_t st)
+hipError_t launch_gemm_a8(int bits, const ExpertPtrs &w, bool fp8, const int8_t *xq, const float *sx, int64_t m,
+                          int64_t n, int64_t k, uint32_t zmid, uint32_t zrow, uint16_t *y, int64_t ldy, hipStream_t st)
 {
     if (m < 1) return hipSuccess;
     const int64_t blocks = ((n + kNT - 1) / kNT) * ((m + kMRows - 1) / kMRows);
     const dim3 grid((unsigned)blocks), block(kWaves * 64);
-    switch (bits * 2 + (zrow ? 1 : 0)) {
+    const int zpk = fp8 ? kZpFp8 : zrow ? kZpPacked : kZpByte;
+    switch (bits * 3 + zpk) {
 #define QP_A8_CASE(B, ZPK)                                                                                      \
-    case B * 2 + ZPK:                                                                                           \
+    case B * 3 + ZPK:                                                                                           \
         hipLaunchKernelGGL((gemm_a8_kernel<B, ZPK>), grid, block, 0, st, w, xq, sx, m, n, k, zmid, zrow, y, ldy); \
         break;
-        QP_A8_CASE(2, 0) QP_A8_CASE(2, 1) QP_A8_CASE(3, 0) QP_A8_CASE(3, 1) QP_A8_CASE(4, 0) QP_A8_CASE(4, 1)
-        QP_A8_CASE(5, 0) QP_A8_CASE(5, 1) QP_A8_CASE(6, 0) QP_A8_CASE(6, 1)
+        QP_A8_CASE(2, kZpByte) QP_A8_CASE(2, kZpPacked) QP_A8_CASE(2, kZpFp8)
+        QP_A8_CASE(3, kZpByte) QP_A8_CASE(3, kZpPacked) QP_A8_CASE(3, kZpFp8)
+        QP_A8_CASE(4, kZpByte) QP_A8_CASE(4, kZpPacked) QP_A8_CASE(4, kZpFp8)
+        QP_A8_CASE(5, kZpByte) QP_A8_CASE(5, kZpPacked) QP_A8_CASE(5, kZpFp8)
+        QP_A8_CASE(6, kZpByte) QP_A8_CASE(6, kZpPacked) QP_A8_CASE(6, kZpFp8)
 #undef QP_A8_CASE
     default: return hipErrorInvalidValue;
     }

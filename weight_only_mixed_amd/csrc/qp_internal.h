@@ -122,8 +122,8 @@ hipError_t launch_grouped(int bits, int epilogue, int n_experts, const GemmArgs 
 // Integer-dot path: per-token int8 activations (storage map of qpack.h) and the GEMM on them.
 hipError_t launch_act_quantize(const uint16_t *x, int64_t ldx, int64_t m, int64_t k, int8_t *xq, float *scales,
                                hipStream_t st);
-hipError_t launch_gemm_a8(int bits, const ExpertPtrs &w, const int8_t *xq, const float *sx, int64_t m, int64_t n,
-                          int64_t k, uint32_t zmid, uint32_t zrow, uint16_t *y, int64_t ldy, hipStream_t st);
+hipError_t launch_gemm_a8(int bits, const ExpertPtrs &w, bool fp8, const int8_t *xq, const float *sx, int64_t m,
+                          int64_t n, int64_t k, uint32_t zmid, uint32_t zrow, uint16_t *y, int64_t ldy, hipStream_t st);
 
 hipError_t launch_moe_dispatch(const int32_t *ids, const float *w, int64_t tokens, int topk,
                                int n_experts, int32_t *offsets, int32_t *row_src,
