@@ -3,38 +3,13 @@
 // the tokens routed to it and their top-k expert ids; results return per token).
 //
 // Dispatch is one workgroup: expert sizes by LDS atomics, an exclusive scan for the offsets,
-// then a stable placement (token order, then choice order) by one block scan per expert over
-// chunks of 1024 choices.  Combine sums a token's choices in choice order in fp32 (no atomics),
+// then a stable placement (token order, then choice order) over chunks of 1024 choices: a
+// choice's rank is its position among its wave's choices of the same expert (one ballot per
+// expert) plus the counts of the chunk's earlier waves and of the earlier chunks.  Combine sums a token's choices in choice order in fp32 (no atomics),
 // so results are deterministic.
 #include "qp_internal.h"
 
 namespace qp {
-
-__device__ int block_excl_scan_1024(int v, int *lds, int *total)
-{
-    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-    int x = v;
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    if (lane == 63) lds[wv] = x;
-    __syncthreads();
-    if (t == 0) {
-        int a = 0;
-        for (int i = 0; i < 16; ++i) {
-            const int c = lds[i];
-            lds[i] = a;
-            a += c;
-        }
-        lds[16] = a;
-    }
-    __syncthreads();
-    const int res = lds[wv] + x - v;
-    *total = lds[16];
-    __syncthreads();
-    return res;
-}
 
 __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t *ids, const float *w,
                                                         int total, int topk, int n_experts,
@@ -42,7 +17,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t *ids, cons
                                                         float *row_weight, int32_t *token_rows)
 {
     __shared__ int cnt[kMaxExperts], base[kMaxExperts + 1], run[kMaxExperts];
-    __shared__ int lds[17];
+    __shared__ int wcnt[16][kMaxExperts];  // per-wave counts of the current chunk
     const int t = threadIdx.x;
     if (t < kMaxExperts) cnt[t] = 0;
     __syncthreads();
@@ -62,23 +37,41 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t *ids, cons
     }
     __syncthreads();
     if (t <= n_experts) offsets[t] = base[t];
+    const int lane = t & 63, wv = t >> 6;
     for (int c0 = 0; c0 < total; c0 += 1024) {
         const int i = c0 + t;
         const int e_i = i < total ? ids[i] : -1;
-        int pos = -1;
+        const bool ok = e_i >= 0 && e_i < n_experts;
+        // this choice's rank among the wave's choices of the same expert, and the wave's count
+        // of each expert (one ballot per expert, no barrier)
+        int rank = 0;
         for (int e = 0; e < n_experts; ++e) {
-            int tot;
-            const int rk = block_excl_scan_1024(e_i == e ? 1 : 0, lds, &tot);
-            if (e_i == e) pos = base[e] + run[e] + rk;
-            __syncthreads();
-            if (t == 0) run[e] += tot;
-            __syncthreads();
+            const uint64_t mask = __ballot(ok && e_i == e);
+            if (ok && e_i == e) rank = __popcll(mask & ((1ull << lane) - 1));
+            if (lane == 0) wcnt[wv][e] = __popcll(mask);
         }
-        if (i < total && pos < 0) token_rows[i] = -1;
-        if (i < total && pos >= 0) {
-            row_src[pos] = i / topk;
-            row_weight[pos] = w[i];
-            token_rows[i] = pos;
+        __syncthreads();
+        int pos = -1;
+        if (ok) {  // after the expert's earlier chunks and this chunk's earlier waves
+            int before = 0;
+            for (int w2 = 0; w2 < wv; ++w2) before += wcnt[w2][e_i];
+            pos = base[e_i] + run[e_i] + before + rank;
+        }
+        __syncthreads();
+        if (t < n_experts) {
+            int c = 0;
+            for (int w2 = 0; w2 < 16; ++w2) c += wcnt[w2][t];
+            run[t] += c;
+        }
+        __syncthreads();
+        if (i < total) {
+            if (pos < 0) {
+                token_rows[i] = -1;
+            } else {
+                row_src[pos] = i / topk;
+                row_weight[pos] = w[i];
+                token_rows[i] = pos;
+            }
         }
     }
 }
