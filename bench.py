@@ -140,6 +140,7 @@ def time_graph(torch, fn, reps: int, stream, trials: int = 5, warm_ms: float = 5
 
 
 ROTATION_BYTES = 1 << 30
+CALLS = 100  # calls per timed graph replay for the compute-bound lines
 
 
 def copies_for(nbytes: int, min_bytes: int = ROTATION_BYTES) -> int:
@@ -377,7 +378,7 @@ def bench_stack(q, torch, workloads, stream, reps: int = 20):
                 GBps_one_launch_per_matrix=round(total / (us_each * 1e-6) / 1e9, 1))
 
 
-def bench_moe(q, torch, workloads, stream, reps: int = 20):
+def bench_moe(q, torch, workloads, stream, reps: int = CALLS):
     """Routed-expert FFN: 16 experts x (gate, up 14336x4096; down 4096x14336), 4-bit, 128 tokens
     top-2 with Zipf(1.1) routing, one qmoe_ffn call.  One quantized template per matrix kind,
     cloned per expert (1.48 GB of expert weights); gate and up rows interleaved per 16-row block
@@ -507,8 +508,8 @@ def bench_prefill(q, torch, workloads, stream):
     yp = torch.empty((Mp, Np), dtype=torch.int16, device=dev)
     wsb = q.qlinear_gemm_workspace_bytes(dp, Mp, wt["nnz"])
     wsp = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
-    ms = time_graph(torch, lambda i: q.qlinear_gemm(dp, hp, xp, Kp, Mp, yp, Np, wsp, wsb), 10, stream)
-    ms_dense = time_graph(torch, lambda i: q.qlinear_gemm(dp, hd, xp, Kp, Mp, yp, Np, None, 0), 10, stream)
+    ms = time_graph(torch, lambda i: q.qlinear_gemm(dp, hp, xp, Kp, Mp, yp, Np, wsp, wsb), CALLS, stream)
+    ms_dense = time_graph(torch, lambda i: q.qlinear_gemm(dp, hd, xp, Kp, Mp, yp, Np, None, 0), CALLS, stream)
     # one GPU's share under 8-way column parallelism: the first N/8 rows of the same quantized
     # weight with their outliers; with the split workspace (k in parts) and without
     ns = Np // 8
@@ -519,8 +520,8 @@ def bench_prefill(q, torch, workloads, stream):
     wsb_s = q.qlinear_gemm_workspace_bytes(ds, Mp, nnz_s)
     wsb_o = (2 * Kp + 4 * ns) * ((Mp + 127) // 128 * 128)  # the outlier part alone: no split
     ws_s = torch.empty(wsb_s, dtype=torch.uint8, device=dev)
-    ms_s = time_graph(torch, lambda i: q.qlinear_gemm(ds, hs, xp, Kp, Mp, ys, ns, ws_s, wsb_s), 10, stream)
-    ms_u = time_graph(torch, lambda i: q.qlinear_gemm(ds, hs, xp, Kp, Mp, ys, ns, ws_s, wsb_o), 10, stream)
+    ms_s = time_graph(torch, lambda i: q.qlinear_gemm(ds, hs, xp, Kp, Mp, ys, ns, ws_s, wsb_s), CALLS, stream)
+    ms_u = time_graph(torch, lambda i: q.qlinear_gemm(ds, hs, xp, Kp, Mp, ys, ns, ws_s, wsb_o), CALLS, stream)
     fl_s = 2 * Mp * ns * Kp + 2 * Mp * nnz_s
     shard = dict(shape=dict(m=Mp, k=Kp, n=ns, nnz=nnz_s), k_parts=(wsb_s - wsb_o) // (4 * Mp * ns) if wsb_s > wsb_o else 1,
                  us=round(ms_s * 1e3, 2), TFLOPs=round(fl_s / (ms_s * 1e-3) / 1e12, 1),
@@ -586,7 +587,7 @@ def bench_prefill_variants(q, torch, workloads, stream):
             z = torch.empty(q.qp_zero_bytes(d), dtype=torch.uint8, device=dev)
             q.qpack_pack_zeros(d, wt["zeros"], z)
         h = q.weight(wt["packed"], wt["scales"], z)
-        ms = time_graph(torch, lambda i: q.qlinear_gemm(d, h, xp, Kp, Mp, yp, Np, None, 0), 10, stream)
+        ms = time_graph(torch, lambda i: q.qlinear_gemm(d, h, xp, Kp, Mp, yp, Np, None, 0), CALLS, stream)
         tf = 2 * Mp * Np * Kp / (ms * 1e-3) / 1e12
         key = f"b{bits}_g{g}" + ("_sym" if sym else "") + ("_bbit_zeros" if packed else "")
         out[key] = dict(us=round(ms * 1e3, 2), TFLOPs=round(tf, 1), frac_mfma_peak=round(tf / MFMA_F16_PEAK_TFLOPS, 4))
@@ -594,7 +595,7 @@ def bench_prefill_variants(q, torch, workloads, stream):
     for bits, g, sym in ((2, 32, True), (4, 128, False)):  # fp8 scales with an fp16 fallback
         d, wt = quantize_pack_fp8(q, torch, wp, bits, g, sym)
         h = q.weight_fp8(wt["packed"], wt["sc8"], wt["factors"], wt["fb"], wt["fb"].shape[1], wt["zeros"])
-        ms = time_graph(torch, lambda i: q.qlinear_gemm(d, h, xp, Kp, Mp, yp, Np, None, 0), 10, stream)
+        ms = time_graph(torch, lambda i: q.qlinear_gemm(d, h, xp, Kp, Mp, yp, Np, None, 0), CALLS, stream)
         tf = 2 * Mp * Np * Kp / (ms * 1e-3) / 1e12
         out[f"b{bits}_g{g}" + ("_sym" if sym else "") + "_fp8_scales"] = dict(
             us=round(ms * 1e3, 2), TFLOPs=round(tf, 1), frac_mfma_peak=round(tf / MFMA_F16_PEAK_TFLOPS, 4),
@@ -621,14 +622,14 @@ def bench_prefill_a8(q, torch, workloads, stream):
     sx = torch.empty(Mp, dtype=torch.float32, device=dev)
     yp = torch.empty((Mp, Np), dtype=torch.int16, device=dev)
     q.qact_quantize(xp, Kp, Mp, Kp, xq, sx)
-    ms_gemm = time_graph(torch, lambda i: q.qlinear_gemm_a8(dp, h, xq, sx, Mp, yp, Np), 10, stream)
+    ms_gemm = time_graph(torch, lambda i: q.qlinear_gemm_a8(dp, h, xq, sx, Mp, yp, Np), CALLS, stream)
 
     def e2e(i):
         q.qact_quantize(xp, Kp, Mp, Kp, xq, sx)
         q.qlinear_gemm_a8(dp, h, xq, sx, Mp, yp, Np)
 
-    ms_e2e = time_graph(torch, e2e, 10, stream)
-    ms_act = time_graph(torch, lambda i: q.qact_quantize(xp, Kp, Mp, Kp, xq, sx), 50, stream)
+    ms_e2e = time_graph(torch, e2e, CALLS, stream)
+    ms_act = time_graph(torch, lambda i: q.qact_quantize(xp, Kp, Mp, Kp, xq, sx), CALLS, stream)
     ops = 2 * Mp * Np * Kp
     tops = ops / (ms_gemm * 1e-3) / 1e12
     tops_e2e = ops / (ms_e2e * 1e-3) / 1e12

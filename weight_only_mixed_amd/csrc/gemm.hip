@@ -55,34 +55,51 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t *x, int64
     }
 }
 
-// Outlier partial: S^T[n][p] = sum over the outliers (n, c, v) of v * x^T[c][p], in fp32 (one
-// wave per weight row, each lane 8 consecutive positions p of a 512-position chunk).  Eight
-// entries are gathered per step so their loads are in flight together.
+// Outlier partial: S^T[n][p] = sum over the outliers (n, c, v) of v * x^T[c][p], in fp32.  A
+// wave takes eight weight rows and one 64-position chunk: lane (8 j + q) sums row 8 w + j over
+// positions 8 q .. 8 q + 7 of the chunk.  Per step the eight lanes of a row load sixteen of its
+// entries (two each) and pass them round, so all sixteen 16-byte gathers are in flight behind
+// one index load.  Work items (chunk, 32-row group) run chunk-major and each XCD (workgroup b on
+// XCD b % 8) takes a contiguous eighth of them, so an XCD gathers from about one chunk of x^T at
+// a time (k rows of 128 bytes: L2-resident) rather than from all of it.
 __global__ __launch_bounds__(256) void outlier_spmm_kernel(const int32_t *rowptr, const int32_t *col,
                                                            const uint16_t *val, const uint16_t *xt, int64_t n,
-                                                           int64_t ldxt, float *spart)
+                                                           int64_t k, int64_t ldxt, int64_t per_xcd, float *spart)
 {
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + wv;
-    const int64_t p = (int64_t)blockIdx.y * 512 + 8 * lane;
-    if (row >= n || p >= ldxt) return;
+    const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    const int64_t groups = (n + 31) / 32, chunk = item / groups;
+    if (chunk >= ldxt / 64) return;
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane & 7;
+    const int64_t row = (item % groups) * 32 + 8 * wv + (lane >> 3);
+    if (row >= n) return;  // whole eight-lane row groups: the exchanges below stay inside one
+    const int64_t p = chunk * 64 + 8 * q;
+    const rsrc_t xr = make_rsrc(xt, k * ldxt * 2);  // (under 2 GiB) a column index outside k reads zeros
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const int64_t e0 = rowptr[row], e1 = rowptr[row + 1];
-    for (int64_t e = e0; e < e1; e += 8) {
-        u4 xv[8];
-        float v[8];
+    for (int64_t e = e0; e < e1; e += 16) {
+        int32_t c2[2];
+        uint32_t v2[2];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const bool ok = e + j < e1;
-            v[j] = ok ? h_f(val[e + j]) : 0.f;
-            xv[j] = ok ? *(const u4 *)(xt + (int64_t)col[e + j] * ldxt + p) : (u4){0u, 0u, 0u, 0u};
+        for (int h = 0; h < 2; ++h) {
+            const bool ok = e + 8 * h + q < e1;
+            c2[h] = ok ? col[e + 8 * h + q] : -1;
+            v2[h] = ok ? val[e + 8 * h + q] : 0u;
+        }
+        u4 xv[16];
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int src = (lane & ~7) | (j & 7);
+            const int32_t c = __shfl(c2[j >> 3], src);
+            v[j] = h_f((uint16_t)__shfl((int)v2[j >> 3], src));
+            xv[j] = ld16(xr, (uint64_t)c < (uint64_t)k ? (uint32_t)(((int64_t)c * ldxt + p) * 2) : 0x80000000u);
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 16; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc[2 * q] = __builtin_fmaf(lo_h(xv[j][q]), v[j], acc[2 * q]);
-                acc[2 * q + 1] = __builtin_fmaf(hi_h(xv[j][q]), v[j], acc[2 * q + 1]);
+            for (int u = 0; u < 4; ++u) {
+                acc[2 * u] = __builtin_fmaf(lo_h(xv[j][u]), v[j], acc[2 * u]);
+                acc[2 * u + 1] = __builtin_fmaf(hi_h(xv[j][u]), v[j], acc[2 * u + 1]);
             }
     }
     f4 *dst = (f4 *)(spart + row * ldxt + p);
@@ -134,8 +151,9 @@ hipError_t launch_gemm(int bits, const GemmArgs &a, hipStream_t st)
     if (a.rowptr) {
         hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)((a.k + 63) / 64), (unsigned)(a.ldxt / 128)), dim3(256), 0,
                            st, a.x, a.ldx, a.m, a.k, a.xt, a.ldxt);
-        hipLaunchKernelGGL(outlier_spmm_kernel, dim3((unsigned)((a.n + 3) / 4), (unsigned)((a.ldxt + 511) / 512)),
-                           dim3(256), 0, st, a.rowptr, a.col, a.val, a.xt, a.n, a.ldxt, a.spart);
+        const int64_t per_xcd = ((a.n + 31) / 32 * (a.ldxt / 64) + 7) / 8;
+        hipLaunchKernelGGL(outlier_spmm_kernel, dim3((unsigned)(8 * per_xcd)), dim3(256), 0, st, a.rowptr, a.col,
+                           a.val, a.xt, a.n, a.k, a.ldxt, per_xcd, a.spart);
     }
     if (a.ksplit > 1) {
         // k parts into fp32 partial rows (the first seeded from the outlier partial), then one
