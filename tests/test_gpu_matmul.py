@@ -174,3 +174,26 @@ def test_gemm_prefill_full_sampled():
     got = y[np.ix_(ms, ns)]
     assert rel_err(got, r) <= TOL, report(got, r)
     assert np.isfinite(y).all()
+
+
+@pytest.mark.parametrize("k", (1024, 4096))
+def test_gemm_outlier_heavy_rows(k):
+    """Rows holding 17, 33 and 40 outliers (the sparse partial's multi-step rows), a weight of
+    784 rows (its last 32-row group half full) and m = 70 (one ragged 128-row block of x^T, two
+    64-position chunks); k = 4096 also takes the k-split path (the first part seeded)."""
+    n, m, frac = 784, 70, 0.004
+    w = workloads.weights_fp16(n, k, 4400 + k)
+    workloads.plant_outliers(w, 0.003, 4400 + k)
+    rng = np.random.default_rng(4401 + k)
+    for row, cnt in ((5, 40), (6, 17), (n - 1, 33)):
+        cols = rng.choice(k, size=cnt, replace=False)
+        w[row, cols] = (rng.uniform(6.0, 8.0, cnt) * rng.choice((-1.0, 1.0), cnt)).astype(np.float16)
+    ref_q = oracle.quantize(w, 4, frac)
+    counts = np.diff(ref_q["rowptr"])
+    assert counts[5] >= 40 and counts[6] >= 17 and counts[n - 1] >= 33, counts[[5, 6, n - 1]]
+    x = workloads.activations_fp16(m, k, 4402 + k)
+    r = oracle.linear(x, ref_q)
+    g = GpuWeight(w, 4, frac)
+    assert g.nnz == int(ref_q["rowptr"][-1])
+    y = run_linear("qlinear_gemm", g, x)
+    assert rel_err(y, r) <= TOL, report(y, r)
